@@ -1,0 +1,228 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) forward layer core of Gated DeltaNet.
+ *
+ * The layer core is three stages, each a hand-written HIP kernel, plus a call
+ * that runs all three on one stream:
+ *
+ *   gdn_prologue_fwd    concatenated depthwise causal conv + SiLU over the
+ *                       q|k|v channels, beta = sigmoid(b) and the log-decay
+ *                       g = -exp(A_log) * softplus(a + dt_bias)
+ *   gdn_chunk_rule_fwd  chunked gated delta rule (chunks of 64 tokens) with
+ *                       q/k L2 normalisation folded in and the GQA head map
+ *   gdn_gated_norm_fwd  output RMSNorm, materialised in the activation dtype,
+ *                       then the FP32 SiLU-gate multiply
+ *   gdn_layer_fwd       the three stages in order, in a caller workspace
+ *
+ * Sources (web pages):
+ *   [P1] Megatron-LM pull request "perf(gated_delta_net): fold q/k L2-norm
+ *        into the gated_delta_rule kernel" - sections What, Why.
+ *   [P2] Megatron Core developer guide "GDN Elementwise Fusion" - option
+ *        table, "Post-GDR requirements", "Execution and numerical behavior".
+ *   [P3] flash-linear-attention pull request fusing GatedDeltaNet's q/k/v
+ *        short convolutions - Summary, Why, Risk / scope.
+ *   The recurrence is not printed on the pages; it is the gated delta rule of
+ *   Gated DeltaNet (Yang, Kautz and Hatamizadeh, ICLR 2025):
+ *       S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *       o_t = scale * S_t q_t,   S is dv x dk, FP32.
+ *
+ * Conventions shared by every call
+ *   - Tensors are described by gdn_tensor: a DEVICE pointer, a dtype, a shape
+ *     and strides counted in elements. Strides may be arbitrary (views are
+ *     read in place, never copied) except that the innermost (channel /
+ *     head-dim) stride must be 1. Outputs that this ABI calls "contiguous"
+ *     must have row-major strides.
+ *   - All memory is owned by the caller. The library never allocates, frees
+ *     or synchronises; every call only enqueues kernels on `stream` (a
+ *     hipStream_t; NULL is the legacy default stream) and returns.
+ *   - Every argument is checked from host metadata alone (shapes, strides,
+ *     dtypes, pointer alignment and overlap) before anything is launched, so
+ *     a call that returns an error has had no effect ([P2] Post-GDR
+ *     requirements: unsupported inputs are rejected on every call, without a
+ *     device synchronisation and without a silent fallback). Device contents
+ *     (e.g. cu_seqlens values) are not validated.
+ *   - An optional tensor is passed as a NULL descriptor pointer.
+ *   - Calls are re-entrant and may run concurrently on different streams.
+ *   - On error, gdn_last_error() returns a message for the calling thread.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_MAX_DIMS 5
+
+typedef enum gdn_dtype {
+  GDN_F32 = 0,
+  GDN_BF16 = 1,
+  GDN_F16 = 2,
+  GDN_I32 = 3
+} gdn_dtype;
+
+typedef struct gdn_tensor {
+  void *data;                    /* device pointer */
+  int32_t dtype;                 /* gdn_dtype */
+  int32_t ndim;                  /* 1 .. GDN_MAX_DIMS */
+  int64_t shape[GDN_MAX_DIMS];
+  int64_t stride[GDN_MAX_DIMS];  /* in elements */
+} gdn_tensor;
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_VALUE = 1,  /* shape/dtype/stride mismatch, empty input,
+                                 non-power-of-two head dim, Hv % Hqk != 0,
+                                 inner stride != 1, output overlapping an
+                                 input, workspace too small */
+  GDN_ERR_NOT_SUPPORTED = 2,  /* valid but not built: head dims outside the
+                                 instantiated set, misaligned vectors */
+  GDN_ERR_LAUNCH = 3          /* the HIP runtime refused a launch */
+} gdn_status;
+
+/* Head geometry: Hqk query/key heads of dimension dk, Hv value heads of
+ * dimension dv. Hv must be a multiple of Hqk; value head h reads query/key
+ * head h / (Hv / Hqk) ([P1] Why: normalisation is per head, so head
+ * replication leaves the result unchanged). Supported: dk in {64, 128, 256},
+ * dv in {64, 128, 256, 512}. */
+typedef struct gdn_dims {
+  int64_t Hqk, dk, Hv, dv;
+} gdn_dims;
+
+/* Message describing the last error on the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* Library version string. */
+const char *gdn_version(void);
+
+/*
+ * gdn_prologue_fwd - [P3] Summary/Why; [P2] option table ("causal
+ * convolution, SiLU, layout transforms, Q/K L2 normalization, head expansion,
+ * beta and decay preparation").
+ *
+ * One depthwise causal conv1d of 4 taps over the concatenated channels
+ * c in [0, C), C = 2*Hqk*dk + Hv*dv, ordered q | k | v:
+ *     y[t, c] = bias[c] + sum_{j=0..3} w[c, j] * x[t - 3 + j, c]
+ *     qkv[t, c] = silu(y[t, c])  (computed in FP32, stored in the act dtype)
+ * with zero history before the start of every sequence. The conv is
+ * depthwise, so this equals three separate q, k and v convolutions.
+ * Also, per token and value head:
+ *     beta = sigmoid(b),  g = -exp(A_log[h]) * softplus(a + dt_bias[h])
+ * stored in FP32.
+ *
+ *   x_q, x_k   [B, T, Hqk*dk] act dtype (F32/BF16/F16), any strides, inner 1
+ *   x_v        [B, T, Hv*dv]  act dtype
+ *   conv_w     [C, 4] act dtype or F32, contiguous
+ *   conv_b     [C] act dtype or F32, or NULL
+ *   a, b       [B, T, Hv] act dtype, any strides, inner 1
+ *   A_log, dt_bias [Hv] F32
+ *   cu_seqlens [N+1] I32 or NULL. NULL: each of the B rows is one sequence.
+ *              Given: B must be 1 and sequence n is tokens
+ *              [cu_seqlens[n], cu_seqlens[n+1]) of the row; the offsets must
+ *              be non-decreasing with cu_seqlens[0] = 0, cu_seqlens[N] = T
+ *              (caller's contract, not checked).
+ *   caller_l2norm  0: q/k stored as conv outputs (the in-kernel route).
+ *              1: q and k are additionally L2-normalised per head over dk
+ *              (x / sqrt(sum x^2 + l2_eps)) before being stored (the
+ *              caller-side route of [P1]).
+ *   out_qkv    [B, T, C] act dtype, contiguous; q, k, v are its channel
+ *              ranges [0, Hqk*dk), [Hqk*dk, 2*Hqk*dk), [2*Hqk*dk, C), head h
+ *              at offset h*d inside its range.
+ *   out_g, out_beta [B, T, Hv] F32, contiguous.
+ */
+gdn_status gdn_prologue_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
+                            const gdn_tensor *x_v, const gdn_tensor *conv_w,
+                            const gdn_tensor *conv_b, const gdn_tensor *a,
+                            const gdn_tensor *b, const gdn_tensor *A_log,
+                            const gdn_tensor *dt_bias,
+                            const gdn_tensor *cu_seqlens, const gdn_dims *dims,
+                            int32_t caller_l2norm, float l2_eps,
+                            const gdn_tensor *out_qkv, const gdn_tensor *out_g,
+                            const gdn_tensor *out_beta, void *stream);
+
+/*
+ * gdn_chunk_rule_fwd - the gated delta rule over chunks of 64 tokens ([P3]
+ * Benchmark: FLA's chunk mode; [P1] What: q/k normalisation inside the
+ * recurrence kernel). Per (sequence, value head h), starting from the given
+ * initial state (or zero):
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ * where, with use_qk_l2norm_in_kernel = 1, q and k are first replaced by
+ * x / sqrt(sum x^2 + l2_eps) over dk ([P1] Why: eps 1e-6 on both routes;
+ * 0 is a no-op). Arithmetic: FP32 state and accumulation; MFMA operands in
+ * the act dtype (FP32 MFMA for F32 inputs).
+ *
+ *   q, k       [B, T, Hqk, dk] act dtype, any strides, inner 1
+ *   v          [B, T, Hv, dv]  act dtype, any strides, inner 1
+ *   g, beta    [B, T, Hv] F32, any strides
+ *   cu_seqlens [N+1] I32 or NULL (as in gdn_prologue_fwd); state and
+ *              chunking restart at every sequence boundary
+ *   initial_state [N, Hv, dv, dk] F32 contiguous, or NULL (zero state)
+ *   out_o      [B, T, Hv, dv] act dtype, any strides, inner 1
+ *   final_state   [N, Hv, dv, dk] F32 contiguous, or NULL; may alias
+ *              initial_state (each state is read before it is written)
+ * N = B without cu_seqlens.
+ */
+gdn_status gdn_chunk_rule_fwd(const gdn_tensor *q, const gdn_tensor *k,
+                              const gdn_tensor *v, const gdn_tensor *g,
+                              const gdn_tensor *beta, float scale,
+                              int32_t use_qk_l2norm_in_kernel, float l2_eps,
+                              const gdn_tensor *cu_seqlens,
+                              const gdn_tensor *initial_state,
+                              const gdn_tensor *out_o,
+                              const gdn_tensor *final_state, void *stream);
+
+/*
+ * gdn_gated_norm_fwd - [P2] option table (output RMSNorm and SiLU gating),
+ * Post-GDR requirements and Execution and numerical behavior. Per
+ * (token, head) row of length dv:
+ *     r   = 1 / sqrt(mean(o^2) + eps)
+ *     y   = round_act(o * r * weight)          (RMSNorm in the act dtype)
+ *     out = round_act(float(y) * silu(float(gate)))   (FP32 gate multiply)
+ *
+ *   o       [B, T, H, dv] F32/BF16/F16, any strides, inner 1, nonempty,
+ *           dv a power of two
+ *   gate    [B, T, H, dv] o's dtype or F32, any strides (separate batch and
+ *           sequence strides, e.g. a view into a projection buffer), inner 1
+ *   weight  [dv] F32/BF16/F16, contiguous
+ *   out     [B, T, H, dv] o's dtype, contiguous
+ */
+gdn_status gdn_gated_norm_fwd(const gdn_tensor *o, const gdn_tensor *gate,
+                              const gdn_tensor *weight, float eps,
+                              const gdn_tensor *out, void *stream);
+
+/* Bytes of workspace gdn_layer_fwd needs for B*T tokens (a multiple of 256):
+ * qkv [B,T,C] act dtype, g and beta [B,T,Hv] F32, o [B,T,Hv,dv] act dtype,
+ * each 256-byte aligned. Returns 0 for invalid arguments. */
+size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, const gdn_dims *dims,
+                                 int32_t act_dtype);
+
+/*
+ * gdn_layer_fwd - the layer core ([P2] Execution: the pre-recurrence stage,
+ * the recurrence and the gated norm; the output projection is not part of
+ * it). Runs gdn_prologue_fwd (caller_l2norm = 0), gdn_chunk_rule_fwd on the
+ * q/k/v channel views of its output, and gdn_gated_norm_fwd, on one stream.
+ * Arguments are those of the three stages; `workspace` is device memory of
+ * at least gdn_layer_workspace_bytes(...) bytes, 256-byte aligned, owned by
+ * the caller and not used by any other call until this call's work on
+ * `stream` is done. `out` is [B, T, Hv, dv] act dtype, contiguous.
+ */
+gdn_status gdn_layer_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
+                         const gdn_tensor *x_v, const gdn_tensor *conv_w,
+                         const gdn_tensor *conv_b, const gdn_tensor *a,
+                         const gdn_tensor *b, const gdn_tensor *A_log,
+                         const gdn_tensor *dt_bias, const gdn_tensor *gate,
+                         const gdn_tensor *norm_w,
+                         const gdn_tensor *cu_seqlens, const gdn_dims *dims,
+                         float scale, int32_t use_qk_l2norm_in_kernel,
+                         float l2_eps, float rms_eps, void *workspace,
+                         size_t workspace_bytes, const gdn_tensor *out,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,518 @@
+// C ABI of the GDN layer core: argument validation from host metadata only,
+// launch planning, and the composition of the three stages.
+//
+// Validation follows the Megatron Core "GDN Elementwise Fusion" guide (Post-
+// GDR requirements): every call checks its inputs from tensor metadata, with
+// no device synchronisation, and rejects what it does not support with an
+// error instead of falling back to another path. Nothing here touches the
+// device before all checks have passed, so a rejected call has no effect.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+gdn_status fail(gdn_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+int64_t elem_size(int32_t dt) {
+  switch (dt) {
+    case GDN_F32: return 4;
+    case GDN_BF16: return 2;
+    case GDN_F16: return 2;
+    case GDN_I32: return 4;
+  }
+  return 0;
+}
+
+const char *dt_name(int32_t dt) {
+  switch (dt) {
+    case GDN_F32: return "F32";
+    case GDN_BF16: return "BF16";
+    case GDN_F16: return "F16";
+    case GDN_I32: return "I32";
+  }
+  return "?";
+}
+
+bool is_act(int32_t dt) { return dt == GDN_F32 || dt == GDN_BF16 || dt == GDN_F16; }
+
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Byte range [lo, hi) covered by a tensor with non-negative strides.
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range range_of(const gdn_tensor *t) {
+  int64_t last = 0;
+  for (int i = 0; i < t->ndim; ++i) {
+    if (t->shape[i] == 0) return {0, 0};
+    last += (t->shape[i] - 1) * t->stride[i];
+  }
+  const uintptr_t lo = (uintptr_t)t->data;
+  return {lo, lo + (uintptr_t)((last + 1) * elem_size(t->dtype))};
+}
+
+bool overlaps(const gdn_tensor *a, const gdn_tensor *b) {
+  if (!a || !b) return false;
+  const Range x = range_of(a), y = range_of(b);
+  if (x.lo == x.hi || y.lo == y.hi) return false;
+  return x.lo < y.hi && y.lo < x.hi;
+}
+
+// Basic descriptor sanity: non-null, data non-null, rank, dtype, shape.
+gdn_status check(const gdn_tensor *t, const char *name, int ndim, const int64_t *shape) {
+  if (!t) return fail(GDN_ERR_INVALID_VALUE, "%s: descriptor is NULL", name);
+  if (t->ndim != ndim)
+    return fail(GDN_ERR_INVALID_VALUE, "%s: expected %d dims, got %d", name, ndim, t->ndim);
+  if (!elem_size(t->dtype)) return fail(GDN_ERR_INVALID_VALUE, "%s: unknown dtype %d", name, t->dtype);
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] != shape[i])
+      return fail(GDN_ERR_INVALID_VALUE, "%s: dim %d is %lld, expected %lld", name, i,
+                  (long long)t->shape[i], (long long)shape[i]);
+    if (t->stride[i] < 0) return fail(GDN_ERR_INVALID_VALUE, "%s: negative stride", name);
+  }
+  if (!t->data) return fail(GDN_ERR_INVALID_VALUE, "%s: data pointer is NULL", name);
+  if ((uintptr_t)t->data % (uintptr_t)elem_size(t->dtype))
+    return fail(GDN_ERR_INVALID_VALUE, "%s: data not aligned to its element size", name);
+  return GDN_OK;
+}
+
+gdn_status check_dtype(const gdn_tensor *t, const char *name, int32_t want) {
+  if (t->dtype != want)
+    return fail(GDN_ERR_INVALID_VALUE, "%s: dtype %s, expected %s", name, dt_name(t->dtype), dt_name(want));
+  return GDN_OK;
+}
+
+gdn_status check_inner(const gdn_tensor *t, const char *name) {
+  if (t->shape[t->ndim - 1] > 1 && t->stride[t->ndim - 1] != 1)
+    return fail(GDN_ERR_INVALID_VALUE, "%s: innermost stride must be 1", name);
+  return GDN_OK;
+}
+
+bool contiguous(const gdn_tensor *t) {
+  int64_t expect = 1;
+  for (int i = t->ndim - 1; i >= 0; --i) {
+    if (t->shape[i] != 1 && t->stride[i] != expect) return false;
+    expect *= t->shape[i];
+  }
+  return true;
+}
+
+gdn_status check_contig(const gdn_tensor *t, const char *name) {
+  if (!contiguous(t)) return fail(GDN_ERR_INVALID_VALUE, "%s: must be contiguous", name);
+  return GDN_OK;
+}
+
+// Largest power-of-two byte alignment (<= 16) shared by the base address and
+// every stride (in bytes) of the leading `nd` dims.
+int row_align(const gdn_tensor *t, int nd) {
+  uint64_t acc = (uint64_t)(uintptr_t)t->data;
+  const int64_t es = elem_size(t->dtype);
+  for (int i = 0; i < nd; ++i)
+    if (t->shape[i] > 1) acc |= (uint64_t)(t->stride[i] * es);
+  return gdn::align_of_host(acc);
+}
+
+#define TRY(x)                        \
+  do {                                \
+    gdn_status _st = (x);             \
+    if (_st != GDN_OK) return _st;    \
+  } while (0)
+
+gdn_status check_dims(const gdn_dims *d) {
+  if (!d) return fail(GDN_ERR_INVALID_VALUE, "dims is NULL");
+  if (d->Hqk <= 0 || d->dk <= 0 || d->Hv <= 0 || d->dv <= 0)
+    return fail(GDN_ERR_INVALID_VALUE, "dims must be positive");
+  if (d->Hv % d->Hqk)
+    return fail(GDN_ERR_INVALID_VALUE, "Hv (%lld) must be a multiple of Hqk (%lld)", (long long)d->Hv,
+                (long long)d->Hqk);
+  if (!pow2(d->dk) || !pow2(d->dv))
+    return fail(GDN_ERR_INVALID_VALUE, "head dims must be powers of two (dk=%lld, dv=%lld)",
+                (long long)d->dk, (long long)d->dv);
+  return GDN_OK;
+}
+
+gdn_status check_cu(const gdn_tensor *cu, int64_t B, int64_t *n_seqs) {
+  if (!cu) {
+    *n_seqs = B;
+    return GDN_OK;
+  }
+  if (cu->ndim != 1 || cu->shape[0] < 2)
+    return fail(GDN_ERR_INVALID_VALUE, "cu_seqlens: expected shape [N+1] with N >= 1");
+  TRY(check(cu, "cu_seqlens", 1, cu->shape));
+  TRY(check_dtype(cu, "cu_seqlens", GDN_I32));
+  TRY(check_contig(cu, "cu_seqlens"));
+  if (B != 1) return fail(GDN_ERR_INVALID_VALUE, "cu_seqlens requires B == 1 (got B=%lld)", (long long)B);
+  *n_seqs = cu->shape[0] - 1;
+  return GDN_OK;
+}
+
+gdn_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return GDN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Planning of each stage (validation + argument packing, no device calls).
+// ---------------------------------------------------------------------------
+gdn_status plan_prologue(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
+                         const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *a,
+                         const gdn_tensor *b, const gdn_tensor *A_log, const gdn_tensor *dt_bias,
+                         const gdn_tensor *cu_seqlens, const gdn_dims *dims, int32_t caller_l2norm,
+                         float l2_eps, const gdn_tensor *out_qkv, const gdn_tensor *out_g,
+                         const gdn_tensor *out_beta, gdn::PrologueArgs *P) {
+  TRY(check_dims(dims));
+  if (!x_q) return fail(GDN_ERR_INVALID_VALUE, "x_q: descriptor is NULL");
+  if (x_q->ndim != 3) return fail(GDN_ERR_INVALID_VALUE, "x_q: expected [B, T, Hqk*dk]");
+  const int64_t B = x_q->shape[0], T = x_q->shape[1];
+  const int64_t nq = dims->Hqk * dims->dk, nv = dims->Hv * dims->dv, C = 2 * nq + nv;
+  const int64_t sq[3] = {B, T, nq}, sv[3] = {B, T, nv}, sw[2] = {C, 4}, sc[1] = {C};
+  const int64_t sab[3] = {B, T, dims->Hv}, sh[1] = {dims->Hv}, so[3] = {B, T, C};
+  if (B * T == 0) return fail(GDN_ERR_INVALID_VALUE, "empty input (B*T == 0)");
+  TRY(check(x_q, "x_q", 3, sq));
+  const int32_t act = x_q->dtype;
+  if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "x_q: dtype must be F32, BF16 or F16");
+  TRY(check(x_k, "x_k", 3, sq));
+  TRY(check(x_v, "x_v", 3, sv));
+  TRY(check_dtype(x_k, "x_k", act));
+  TRY(check_dtype(x_v, "x_v", act));
+  TRY(check_inner(x_q, "x_q"));
+  TRY(check_inner(x_k, "x_k"));
+  TRY(check_inner(x_v, "x_v"));
+  TRY(check(conv_w, "conv_w", 2, sw));
+  if (conv_w->dtype != act && conv_w->dtype != GDN_F32)
+    return fail(GDN_ERR_INVALID_VALUE, "conv_w: dtype must be the activation dtype or F32");
+  TRY(check_contig(conv_w, "conv_w"));
+  if (conv_b) {
+    TRY(check(conv_b, "conv_b", 1, sc));
+    if (conv_b->dtype != act && conv_b->dtype != GDN_F32)
+      return fail(GDN_ERR_INVALID_VALUE, "conv_b: dtype must be the activation dtype or F32");
+    TRY(check_contig(conv_b, "conv_b"));
+  }
+  TRY(check(a, "a", 3, sab));
+  TRY(check(b, "b", 3, sab));
+  TRY(check_dtype(a, "a", act));
+  TRY(check_dtype(b, "b", act));
+  TRY(check(A_log, "A_log", 1, sh));
+  TRY(check(dt_bias, "dt_bias", 1, sh));
+  TRY(check_dtype(A_log, "A_log", GDN_F32));
+  TRY(check_dtype(dt_bias, "dt_bias", GDN_F32));
+  TRY(check_contig(A_log, "A_log"));
+  TRY(check_contig(dt_bias, "dt_bias"));
+  int64_t n_seqs = 0;
+  TRY(check_cu(cu_seqlens, B, &n_seqs));
+  TRY(check(out_qkv, "out_qkv", 3, so));
+  TRY(check_dtype(out_qkv, "out_qkv", act));
+  TRY(check_contig(out_qkv, "out_qkv"));
+  TRY(check(out_g, "out_g", 3, sab));
+  TRY(check(out_beta, "out_beta", 3, sab));
+  TRY(check_dtype(out_g, "out_g", GDN_F32));
+  TRY(check_dtype(out_beta, "out_beta", GDN_F32));
+  TRY(check_contig(out_g, "out_g"));
+  TRY(check_contig(out_beta, "out_beta"));
+  const gdn_tensor *ins[] = {x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens};
+  const gdn_tensor *outs[] = {out_qkv, out_g, out_beta};
+  for (auto *o : outs)
+    for (auto *i : ins)
+      if (overlaps(o, i)) return fail(GDN_ERR_INVALID_VALUE, "an output overlaps an input");
+  if (overlaps(out_qkv, out_g) || overlaps(out_qkv, out_beta) || overlaps(out_g, out_beta))
+    return fail(GDN_ERR_INVALID_VALUE, "outputs overlap each other");
+  if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps)) return fail(GDN_ERR_INVALID_VALUE, "l2_eps must be finite and >= 0");
+
+  const int64_t es = elem_size(act);
+  int al = 16;
+  for (const gdn_tensor *x : {x_q, x_k, x_v}) {
+    const int r = row_align(x, 2);
+    al = r < al ? r : al;
+  }
+  int vec = (int)(al / es);
+  if (vec > 8) vec = 8;
+  while (vec > 1 && (nq % vec || nv % vec)) vec >>= 1;
+  if (vec < 1) return fail(GDN_ERR_INVALID_VALUE, "x: misaligned rows");
+  if (caller_l2norm && (dims->dk % vec || dims->dk / vec > 64))
+    return fail(GDN_ERR_NOT_SUPPORTED,
+                "caller-side L2 norm needs rows aligned to at least %lld bytes", (long long)(dims->dk / 64 * es));
+
+  if (B > 65535 || (C + 255) / 256 + 1 > 65535 || (T + 63) / 64 > 0x7fffffff)
+    return fail(GDN_ERR_NOT_SUPPORTED, "prologue: grid too large (B=%lld, T=%lld, C=%lld)", (long long)B,
+                (long long)T, (long long)C);
+
+  gdn::PrologueArgs &p = *P;
+  memset(&p, 0, sizeof p);
+  p.xq = x_q->data; p.xk = x_k->data; p.xv = x_v->data;
+  p.sxq_b = x_q->stride[0]; p.sxq_t = x_q->stride[1];
+  p.sxk_b = x_k->stride[0]; p.sxk_t = x_k->stride[1];
+  p.sxv_b = x_v->stride[0]; p.sxv_t = x_v->stride[1];
+  p.conv_w = conv_w->data; p.w_dtype = conv_w->dtype;
+  p.conv_b = conv_b ? conv_b->data : nullptr; p.b_dtype = conv_b ? conv_b->dtype : act;
+  p.a = a->data; p.b = b->data;
+  p.sa_b = a->stride[0]; p.sa_t = a->stride[1]; p.sa_h = a->stride[2];
+  p.sb_b = b->stride[0]; p.sb_t = b->stride[1]; p.sb_h = b->stride[2];
+  p.A_log = static_cast<const float *>(A_log->data);
+  p.dt_bias = static_cast<const float *>(dt_bias->data);
+  p.cu_seqlens = cu_seqlens ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
+  p.n_seqs = n_seqs;
+  p.B = B; p.T = T; p.Hqk = dims->Hqk; p.dk = dims->dk; p.Hv = dims->Hv; p.dv = dims->dv; p.C = C;
+  p.act = act; p.vec = vec; p.caller_l2norm = caller_l2norm ? 1 : 0; p.l2_eps = l2_eps;
+  p.qkv = out_qkv->data;
+  p.g = static_cast<float *>(out_g->data);
+  p.beta = static_cast<float *>(out_beta->data);
+  return GDN_OK;
+}
+
+gdn_status plan_chunk(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, const gdn_tensor *g,
+                      const gdn_tensor *beta, float scale, int32_t use_l2, float l2_eps,
+                      const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state, const gdn_tensor *out_o,
+                      const gdn_tensor *final_state, gdn::ChunkArgs *P) {
+  if (!q || q->ndim != 4) return fail(GDN_ERR_INVALID_VALUE, "q: expected [B, T, Hqk, dk]");
+  if (!v || v->ndim != 4) return fail(GDN_ERR_INVALID_VALUE, "v: expected [B, T, Hv, dv]");
+  const int64_t B = q->shape[0], T = q->shape[1], Hqk = q->shape[2], dk = q->shape[3];
+  const int64_t Hv = v->shape[2], dv = v->shape[3];
+  if (B * T == 0) return fail(GDN_ERR_INVALID_VALUE, "empty input (B*T == 0)");
+  const gdn_dims d = {Hqk, dk, Hv, dv};
+  TRY(check_dims(&d));
+  const int64_t sq[4] = {B, T, Hqk, dk}, svv[4] = {B, T, Hv, dv}, sg[3] = {B, T, Hv};
+  TRY(check(q, "q", 4, sq));
+  const int32_t act = q->dtype;
+  if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "q: dtype must be F32, BF16 or F16");
+  TRY(check(k, "k", 4, sq));
+  TRY(check(v, "v", 4, svv));
+  TRY(check_dtype(k, "k", act));
+  TRY(check_dtype(v, "v", act));
+  TRY(check_inner(q, "q"));
+  TRY(check_inner(k, "k"));
+  TRY(check_inner(v, "v"));
+  TRY(check(g, "g", 3, sg));
+  TRY(check(beta, "beta", 3, sg));
+  TRY(check_dtype(g, "g", GDN_F32));
+  TRY(check_dtype(beta, "beta", GDN_F32));
+  int64_t n_seqs = 0;
+  TRY(check_cu(cu_seqlens, B, &n_seqs));
+  const int64_t ss[4] = {n_seqs, Hv, dv, dk};
+  if (initial_state) {
+    TRY(check(initial_state, "initial_state", 4, ss));
+    TRY(check_dtype(initial_state, "initial_state", GDN_F32));
+    TRY(check_contig(initial_state, "initial_state"));
+  }
+  if (final_state) {
+    TRY(check(final_state, "final_state", 4, ss));
+    TRY(check_dtype(final_state, "final_state", GDN_F32));
+    TRY(check_contig(final_state, "final_state"));
+  }
+  TRY(check(out_o, "out_o", 4, svv));
+  TRY(check_dtype(out_o, "out_o", act));
+  TRY(check_inner(out_o, "out_o"));
+  if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_VALUE, "scale must be finite");
+  if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps)) return fail(GDN_ERR_INVALID_VALUE, "l2_eps must be finite and >= 0");
+  const gdn_tensor *ins[] = {q, k, v, g, beta, cu_seqlens, initial_state};
+  for (auto *i : ins) {
+    if (overlaps(out_o, i)) return fail(GDN_ERR_INVALID_VALUE, "out_o overlaps an input");
+    if (i != initial_state && overlaps(final_state, i))
+      return fail(GDN_ERR_INVALID_VALUE, "final_state overlaps an input");
+  }
+  if (overlaps(out_o, final_state)) return fail(GDN_ERR_INVALID_VALUE, "out_o overlaps final_state");
+  if (initial_state && final_state && overlaps(initial_state, final_state) &&
+      initial_state->data != final_state->data)
+    return fail(GDN_ERR_INVALID_VALUE, "final_state partially overlaps initial_state");
+  if (!gdn::chunk_rule_supported(dk, act) || dv % 16)
+    return fail(GDN_ERR_NOT_SUPPORTED, "chunk rule: dk=%lld dv=%lld %s is not instantiated", (long long)dk,
+                (long long)dv, dt_name(act));
+  if (n_seqs > 65535 || Hv > 65535)
+    return fail(GDN_ERR_NOT_SUPPORTED, "chunk rule: at most 65535 sequences and heads");
+  const int64_t es = elem_size(act);
+  if (row_align(q, 3) < 16 || row_align(k, 3) < 16)
+    return fail(GDN_ERR_NOT_SUPPORTED, "q/k rows must be 16-byte aligned");
+  if (row_align(v, 3) < 4 * es) return fail(GDN_ERR_NOT_SUPPORTED, "v rows must be %lld-byte aligned", (long long)(4 * es));
+
+  gdn::ChunkArgs &p = *P;
+  memset(&p, 0, sizeof p);
+  p.q = q->data; p.k = k->data; p.v = v->data;
+  p.sq_b = q->stride[0]; p.sq_t = q->stride[1]; p.sq_h = q->stride[2];
+  p.sk_b = k->stride[0]; p.sk_t = k->stride[1]; p.sk_h = k->stride[2];
+  p.sv_b = v->stride[0]; p.sv_t = v->stride[1]; p.sv_h = v->stride[2];
+  p.g = static_cast<const float *>(g->data);
+  p.beta = static_cast<const float *>(beta->data);
+  p.sg_b = g->stride[0]; p.sg_t = g->stride[1]; p.sg_h = g->stride[2];
+  p.sbt_b = beta->stride[0]; p.sbt_t = beta->stride[1]; p.sbt_h = beta->stride[2];
+  p.cu_seqlens = cu_seqlens ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
+  p.n_seqs = n_seqs;
+  p.init_state = initial_state ? static_cast<const float *>(initial_state->data) : nullptr;
+  p.final_state = final_state ? static_cast<float *>(final_state->data) : nullptr;
+  p.o = out_o->data;
+  p.so_b = out_o->stride[0]; p.so_t = out_o->stride[1]; p.so_h = out_o->stride[2];
+  p.B = B; p.T = T; p.Hqk = Hqk; p.dk = dk; p.Hv = Hv; p.dv = dv;
+  p.act = act; p.use_l2 = use_l2 ? 1 : 0; p.l2_eps = l2_eps; p.scale = scale;
+  return GDN_OK;
+}
+
+gdn_status plan_norm(const gdn_tensor *o, const gdn_tensor *gate, const gdn_tensor *weight, float eps,
+                     const gdn_tensor *out, gdn::NormArgs *P) {
+  if (!o || o->ndim != 4) return fail(GDN_ERR_INVALID_VALUE, "o: expected [B, T, H, dv]");
+  const int64_t B = o->shape[0], T = o->shape[1], H = o->shape[2], dv = o->shape[3];
+  if (B * T * H * dv == 0) return fail(GDN_ERR_INVALID_VALUE, "o: empty tensor");
+  if (!pow2(dv)) return fail(GDN_ERR_INVALID_VALUE, "head dim %lld is not a power of two", (long long)dv);
+  const int64_t so[4] = {B, T, H, dv}, sw[1] = {dv};
+  TRY(check(o, "o", 4, so));
+  const int32_t act = o->dtype;
+  if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "o: dtype must be F32, BF16 or F16");
+  TRY(check_inner(o, "o"));
+  TRY(check(gate, "gate", 4, so));
+  if (gate->dtype != act && gate->dtype != GDN_F32)
+    return fail(GDN_ERR_INVALID_VALUE, "gate: dtype must be o's dtype or F32");
+  TRY(check_inner(gate, "gate"));
+  TRY(check(weight, "weight", 1, sw));
+  if (!is_act(weight->dtype)) return fail(GDN_ERR_INVALID_VALUE, "weight: dtype must be F32, BF16 or F16");
+  TRY(check_contig(weight, "weight"));
+  TRY(check(out, "out", 4, so));
+  TRY(check_dtype(out, "out", act));
+  TRY(check_contig(out, "out"));
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(GDN_ERR_INVALID_VALUE, "eps must be finite and >= 0");
+  if (overlaps(out, o) || overlaps(out, gate) || overlaps(out, weight))
+    return fail(GDN_ERR_INVALID_VALUE, "out overlaps an input");
+  if (dv < 64 || dv > 512)
+    return fail(GDN_ERR_NOT_SUPPORTED, "gated norm: head dim %lld is not instantiated (64..512)", (long long)dv);
+  if ((uintptr_t)weight->data % 16 || (uintptr_t)out->data % 16)
+    return fail(GDN_ERR_NOT_SUPPORTED, "weight and out must be 16-byte aligned");
+  gdn::NormArgs &p = *P;
+  memset(&p, 0, sizeof p);
+  p.o = o->data; p.so_b = o->stride[0]; p.so_t = o->stride[1]; p.so_h = o->stride[2];
+  p.gate = gate->data; p.sg_b = gate->stride[0]; p.sg_t = gate->stride[1]; p.sg_h = gate->stride[2];
+  p.w = weight->data; p.out = out->data;
+  p.B = B; p.T = T; p.H = H; p.dv = dv;
+  p.act = act; p.gate_dtype = gate->dtype; p.w_dtype = weight->dtype;
+  p.o_align = row_align(o, 3);
+  p.gate_align = row_align(gate, 3);
+  p.eps = eps;
+  return GDN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_last_error(void) { return g_error.c_str(); }
+
+const char *gdn_version(void) { return "gdn-mi355x 0.1.0 (gfx950)"; }
+
+gdn_status gdn_prologue_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
+                            const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *a,
+                            const gdn_tensor *b, const gdn_tensor *A_log, const gdn_tensor *dt_bias,
+                            const gdn_tensor *cu_seqlens, const gdn_dims *dims, int32_t caller_l2norm,
+                            float l2_eps, const gdn_tensor *out_qkv, const gdn_tensor *out_g,
+                            const gdn_tensor *out_beta, void *stream) {
+  g_error.clear();
+  gdn::PrologueArgs P;
+  TRY(plan_prologue(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, dims, caller_l2norm,
+                    l2_eps, out_qkv, out_g, out_beta, &P));
+  return launched(gdn::launch_prologue(P, (hipStream_t)stream), "prologue");
+}
+
+gdn_status gdn_chunk_rule_fwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                              const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                              int32_t use_qk_l2norm_in_kernel, float l2_eps, const gdn_tensor *cu_seqlens,
+                              const gdn_tensor *initial_state, const gdn_tensor *out_o,
+                              const gdn_tensor *final_state, void *stream) {
+  g_error.clear();
+  gdn::ChunkArgs P;
+  TRY(plan_chunk(q, k, v, g, beta, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, initial_state, out_o,
+                 final_state, &P));
+  return launched(gdn::launch_chunk_rule(P, (hipStream_t)stream), "chunk rule");
+}
+
+gdn_status gdn_gated_norm_fwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_tensor *weight, float eps,
+                              const gdn_tensor *out, void *stream) {
+  g_error.clear();
+  gdn::NormArgs P;
+  TRY(plan_norm(o, gate, weight, eps, out, &P));
+  return launched(gdn::launch_gated_norm(P, (hipStream_t)stream), "gated norm");
+}
+
+size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, const gdn_dims *dims, int32_t act_dtype) {
+  if (!dims || B < 0 || T < 0 || !is_act(act_dtype)) return 0;
+  if (dims->Hqk <= 0 || dims->dk <= 0 || dims->Hv <= 0 || dims->dv <= 0) return 0;
+  const size_t es = (size_t)elem_size(act_dtype), n = (size_t)(B * T);
+  const size_t C = (size_t)(2 * dims->Hqk * dims->dk + dims->Hv * dims->dv);
+  return align256(n * C * es) + 2 * align256(n * (size_t)dims->Hv * 4) +
+         align256(n * (size_t)(dims->Hv * dims->dv) * es);
+}
+
+gdn_status gdn_layer_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
+                         const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *a,
+                         const gdn_tensor *b, const gdn_tensor *A_log, const gdn_tensor *dt_bias,
+                         const gdn_tensor *gate, const gdn_tensor *norm_w, const gdn_tensor *cu_seqlens,
+                         const gdn_dims *dims, float scale, int32_t use_qk_l2norm_in_kernel, float l2_eps,
+                         float rms_eps, void *workspace, size_t workspace_bytes, const gdn_tensor *out,
+                         void *stream) {
+  g_error.clear();
+  TRY(check_dims(dims));
+  if (!x_q || x_q->ndim != 3) return fail(GDN_ERR_INVALID_VALUE, "x_q: expected [B, T, Hqk*dk]");
+  const int64_t B = x_q->shape[0], T = x_q->shape[1];
+  const int32_t act = x_q->dtype;
+  if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "x_q: dtype must be F32, BF16 or F16");
+  const size_t need = gdn_layer_workspace_bytes(B, T, dims, act);
+  if (!workspace) return fail(GDN_ERR_INVALID_VALUE, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(GDN_ERR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  if ((uintptr_t)workspace % 256) return fail(GDN_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+
+  const int64_t Hqk = dims->Hqk, dk = dims->dk, Hv = dims->Hv, dv = dims->dv;
+  const int64_t nq = Hqk * dk, C = 2 * nq + Hv * dv, es = elem_size(act);
+  char *ws = static_cast<char *>(workspace);
+  const size_t n = (size_t)(B * T);
+  gdn_tensor qkv = {ws, act, 3, {B, T, C}, {T * C, C, 1}};
+  ws += align256(n * (size_t)C * (size_t)es);
+  gdn_tensor gt = {ws, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
+  ws += align256(n * (size_t)Hv * 4);
+  gdn_tensor bt = {ws, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
+  ws += align256(n * (size_t)Hv * 4);
+  gdn_tensor ot = {ws, act, 4, {B, T, Hv, dv}, {T * Hv * dv, Hv * dv, dv, 1}};
+  char *qkv_base = static_cast<char *>(qkv.data);
+  gdn_tensor qv = {qkv_base, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor kv = {qkv_base + nq * es, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor vv = {qkv_base + 2 * nq * es, act, 4, {B, T, Hv, dv}, {T * C, C, dv, 1}};
+  gdn_tensor wsd = {workspace, GDN_BF16, 1, {(int64_t)(need / 2)}, {1}};
+
+  // Plan all three stages before launching anything.
+  gdn::PrologueArgs PP;
+  gdn::ChunkArgs PC;
+  gdn::NormArgs PN;
+  TRY(plan_prologue(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, dims, 0, l2_eps, &qkv, &gt,
+                    &bt, &PP));
+  TRY(plan_chunk(&qv, &kv, &vv, &gt, &bt, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, nullptr, &ot,
+                 nullptr, &PC));
+  TRY(plan_norm(&ot, gate, norm_w, rms_eps, out, &PN));
+  if (out->dtype != act) return fail(GDN_ERR_INVALID_VALUE, "out: dtype must be the activation dtype");
+  const gdn_tensor *ins[] = {x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens};
+  for (auto *i : ins)
+    if (overlaps(&wsd, i)) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps an input");
+  if (overlaps(&wsd, out)) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps out");
+  for (auto *i : ins)
+    if (overlaps(out, i)) return fail(GDN_ERR_INVALID_VALUE, "out overlaps an input");
+
+  hipStream_t s = (hipStream_t)stream;
+  TRY(launched(gdn::launch_prologue(PP, s), "prologue"));
+  TRY(launched(gdn::launch_chunk_rule(PC, s), "chunk rule"));
+  return launched(gdn::launch_gated_norm(PN, s), "gated norm");
+}
+
+}  // extern "C"

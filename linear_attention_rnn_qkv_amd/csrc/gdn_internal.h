@@ -1,0 +1,80 @@
+// Internal launch descriptors shared by the C-ABI layer (gdn_api.cpp) and the
+// kernel translation units. Plain structs of device pointers, sizes and
+// element strides, filled by the host after validation.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace gdn {
+
+enum Dt : int32_t { kF32 = 0, kBF16 = 1, kF16 = 2, kI32 = 3 };
+
+struct PrologueArgs {
+  // Inputs. Strides in elements; the channel/head stride is 1.
+  const void *xq, *xk, *xv;
+  int64_t sxq_b, sxq_t, sxk_b, sxk_t, sxv_b, sxv_t;
+  const void *conv_w;  // [C, 4] contiguous
+  const void *conv_b;  // [C] or null
+  int32_t w_dtype, b_dtype;
+  const void *a, *b;   // [B, T, Hv]
+  int64_t sa_b, sa_t, sa_h, sb_b, sb_t, sb_h;
+  const float *A_log, *dt_bias;
+  const int32_t *cu_seqlens;  // null => dense
+  int64_t n_seqs;
+  // Geometry.
+  int64_t B, T, Hqk, dk, Hv, dv, C;
+  int32_t act;           // Dt
+  int32_t vec;           // elements per vector access of x (1, 2, 4 or 8)
+  int32_t caller_l2norm;
+  float l2_eps;
+  // Outputs (contiguous).
+  void *qkv;             // [B, T, C]
+  float *g, *beta;       // [B, T, Hv]
+};
+
+struct ChunkArgs {
+  const void *q, *k, *v;
+  int64_t sq_b, sq_t, sq_h, sk_b, sk_t, sk_h, sv_b, sv_t, sv_h;
+  const float *g, *beta;
+  int64_t sg_b, sg_t, sg_h, sbt_b, sbt_t, sbt_h;
+  const int32_t *cu_seqlens;  // null => dense
+  int64_t n_seqs;             // B when dense
+  const float *init_state;    // [N, Hv, dv, dk] or null
+  float *final_state;         // [N, Hv, dv, dk] or null
+  void *o;
+  int64_t so_b, so_t, so_h;
+  int64_t B, T, Hqk, dk, Hv, dv;
+  int32_t act;
+  int32_t use_l2;
+  float l2_eps, scale;
+};
+
+struct NormArgs {
+  const void *o;
+  int64_t so_b, so_t, so_h;
+  const void *gate;
+  int64_t sg_b, sg_t, sg_h;
+  const void *w;
+  void *out;  // contiguous
+  int64_t B, T, H, dv;
+  int32_t act, gate_dtype, w_dtype;
+  int32_t o_align, gate_align;  // bytes guaranteed for every row start
+  float eps;
+};
+
+// Each returns the HIP error of the launch (hipSuccess if queued).
+hipError_t launch_prologue(const PrologueArgs &a, hipStream_t s);
+hipError_t launch_chunk_rule(const ChunkArgs &a, hipStream_t s);
+hipError_t launch_gated_norm(const NormArgs &a, hipStream_t s);
+
+// Host-side capability query used by validation (no device calls).
+bool chunk_rule_supported(int64_t dk, int32_t act);
+
+// Largest power-of-two alignment (bytes, <= 16) of an address or stride set.
+inline int align_of_host(uint64_t addr) {
+  int a = 16;
+  while (a > 1 && (addr % (uint64_t)a) != 0) a >>= 1;
+  return a;
+}
+
+}  // namespace gdn

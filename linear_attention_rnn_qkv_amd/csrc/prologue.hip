@@ -1,0 +1,207 @@
+// Pre-recurrence prologue: one depthwise causal conv1d (4 taps) + SiLU over
+// the concatenated q|k|v channels, and beta / log-decay preparation.
+//
+// flash-linear-attention pull request fusing GatedDeltaNet's q/k/v short
+// convolutions (Summary, Why): the three depthwise convolutions share kernel
+// size and activation and mix no channels, so one convolution over the
+// channel-concatenated projections with concatenated weights (and bias) is
+// the same computation at one launch. Here the concatenation costs no copy:
+// the kernel reads the three (possibly strided) projection views in place and
+// writes one [B, T, C] buffer whose channel ranges are q, k and v.
+// Megatron Core "GDN Elementwise Fusion" (option table) lists the same
+// prologue operations plus beta and decay preparation; the formulas used for
+// those are beta = sigmoid(b) and g = -exp(A_log) * softplus(a + dt_bias)
+// (Gated DeltaNet's parameterisation; the pages do not print them).
+//
+// Layout and schedule (HBM-bound): a thread owns VEC consecutive channels and
+// walks a tile of 64 tokens, keeping the three previous inputs in registers,
+// so each input element is read once (plus a 3-token halo per tile) and each
+// output written once with VEC-wide coalesced accesses. History is zero
+// before every sequence start: batch rows are sequences; with cu_seqlens the
+// thread finds the boundaries inside its tile from the offsets. One extra
+// block column per token tile computes beta and g for all value heads.
+#include <limits.h>
+
+#include "device_common.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;   // tokens per block
+constexpr int kUnroll = 4;  // tokens loaded ahead per step
+
+template <typename TW>
+__device__ __forceinline__ float ld_param(const void *p, int64_t i) {
+  return f(static_cast<const TW *>(p)[i]);
+}
+
+__device__ __forceinline__ float ld_any(const void *p, int32_t dt, int64_t i) {
+  if (dt == kF32) return ld_param<float>(p, i);
+  if (dt == kBF16) return ld_param<bf16>(p, i);
+  return ld_param<f16>(p, i);
+}
+
+template <typename T>
+__device__ void beta_g_tile(const PrologueArgs &p, int64_t b, int64_t t0, int64_t t1) {
+  const T *pa = static_cast<const T *>(p.a);
+  const T *pb = static_cast<const T *>(p.b);
+  const int64_t n = (t1 - t0) * p.Hv;
+  for (int64_t i = threadIdx.x; i < n; i += kThreads) {
+    const int64_t t = t0 + i / p.Hv, h = i % p.Hv;
+    const float bb = f(pb[b * p.sb_b + t * p.sb_t + h * p.sb_h]);
+    const float aa = f(pa[b * p.sa_b + t * p.sa_t + h * p.sa_h]);
+    const float x = aa + p.dt_bias[h];
+    const float sp = x > 20.f ? x : log1pf(expf(x));
+    const int64_t o = (b * p.T + t) * p.Hv + h;
+    p.beta[o] = 1.0f / (1.0f + expf(-bb));
+    p.g[o] = -expf(p.A_log[h]) * sp;
+  }
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs p) {
+  const int64_t b = blockIdx.z;
+  const int64_t t0 = (int64_t)blockIdx.x * kTile;
+  const int64_t t1 = t0 + kTile < p.T ? t0 + kTile : p.T;
+  if ((int)blockIdx.y == (int)gridDim.y - 1) {
+    beta_g_tile<T>(p, b, t0, t1);
+    return;
+  }
+  const int64_t c0 = ((int64_t)blockIdx.y * kThreads + threadIdx.x) * VEC;
+  const bool active = c0 < p.C;
+  const int64_t nq = p.Hqk * p.dk;
+
+  // Source view for this thread's channels.
+  const T *src;
+  int64_t st;
+  if (c0 < nq) {
+    src = static_cast<const T *>(p.xq) + b * p.sxq_b + c0;
+    st = p.sxq_t;
+  } else if (c0 < 2 * nq) {
+    src = static_cast<const T *>(p.xk) + b * p.sxk_b + (c0 - nq);
+    st = p.sxk_t;
+  } else {
+    src = static_cast<const T *>(p.xv) + b * p.sxv_b + (c0 - 2 * nq);
+    st = p.sxv_t;
+  }
+  constexpr int AL = VEC * (int)sizeof(T);
+
+  float w[VEC][4], bias[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[i][j] = active ? ld_any(p.conv_w, p.w_dtype, (c0 + i) * 4 + j) : 0.f;
+    bias[i] = (active && p.conv_b) ? ld_any(p.conv_b, p.b_dtype, c0 + i) : 0.f;
+  }
+
+  // Sequence containing t0, and the next boundary after it.
+  int64_t bos = 0, next = LLONG_MAX, idx = 0;
+  const int32_t *cu = p.cu_seqlens;
+  if (cu) {
+    int64_t lo = 0, hi = p.n_seqs;  // invariant: cu[lo] <= t0
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (cu[mid] <= t0) lo = mid; else hi = mid;
+    }
+    bos = cu[lo];
+    idx = lo + 1;
+    next = idx <= p.n_seqs ? cu[idx] : LLONG_MAX;
+  }
+
+  float h1[VEC], h2[VEC], h3[VEC];  // inputs at t-1, t-2, t-3
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) h1[i] = h2[i] = h3[i] = 0.f;
+  if (active && t0 - 1 >= bos) load_vec<T, VEC>(src + (t0 - 1) * st, AL, h1);
+  if (active && t0 - 2 >= bos) load_vec<T, VEC>(src + (t0 - 2) * st, AL, h2);
+  if (active && t0 - 3 >= bos) load_vec<T, VEC>(src + (t0 - 3) * st, AL, h3);
+
+  const bool l2 = p.caller_l2norm && c0 < 2 * nq;
+  const int group = (int)(p.dk / VEC);  // lanes per q/k head
+  T *dst = static_cast<T *>(p.qkv) + b * p.T * p.C + c0;
+
+  for (int64_t tb = t0; tb < t1; tb += kUnroll) {
+    float xs[kUnroll][VEC];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (active && tb + u < t1) {
+        load_vec<T, VEC>(src + (tb + u) * st, AL, xs[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) xs[u][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t t = tb + u;
+      if (t >= t1) break;
+      if (t == next) {  // a new sequence starts: drop the history
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) h1[i] = h2[i] = h3[i] = 0.f;
+        while (idx <= p.n_seqs && cu[idx] <= t) ++idx;
+        next = idx <= p.n_seqs ? cu[idx] : LLONG_MAX;
+      }
+      float z[VEC];
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const float y = bias[i] + w[i][0] * h3[i] + w[i][1] * h2[i] + w[i][2] * h1[i] + w[i][3] * xs[u][i];
+        z[i] = silu(y);
+        ss += z[i] * z[i];
+      }
+      if (p.caller_l2norm) {  // block-uniform: every lane joins the shuffles
+        for (int off = group >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if (l2) {
+          const float r = rsqrtf(ss + p.l2_eps);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) z[i] *= r;
+        }
+      }
+      if (active) store_vec<T, VEC>(dst + t * p.C, z);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        h3[i] = h2[i];
+        h2[i] = h1[i];
+        h1[i] = xs[u][i];
+      }
+    }
+  }
+}
+
+template <typename T, int VEC>
+hipError_t launch_vec(const PrologueArgs &a, hipStream_t s) {
+  const int64_t per_block = (int64_t)kThreads * VEC;
+  const int64_t cblocks = (a.C + per_block - 1) / per_block;
+  const int64_t tblocks = (a.T + kTile - 1) / kTile;
+  dim3 grid((unsigned)tblocks, (unsigned)(cblocks + 1), (unsigned)a.B);
+  hipLaunchKernelGGL((prologue_kernel<T, VEC>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const PrologueArgs &a, hipStream_t s) {
+  switch (a.vec) {
+    case 1: return launch_vec<T, 1>(a, s);
+    case 2: return launch_vec<T, 2>(a, s);
+    case 4: return launch_vec<T, 4>(a, s);
+    case 8:
+      if constexpr (sizeof(T) == 2) return launch_vec<T, 8>(a, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_prologue(const PrologueArgs &a, hipStream_t s) {
+  if (a.B * a.T == 0) return hipSuccess;
+  switch (a.act) {
+    case kF32: return launch_t<float>(a, s);
+    case kBF16: return launch_t<bf16>(a, s);
+    case kF16: return launch_t<f16>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -1,0 +1,193 @@
+"""Thin ctypes binding of ``libgdn.so`` (the C ABI in ``include/gdn.h``).
+
+Argument marshalling only: torch tensors are turned into ``gdn_tensor``
+descriptors (device pointer, dtype, shape, element strides), outputs the
+caller does not pass are allocated with torch, and the call is enqueued on
+torch's current HIP stream. Every step of the computation runs in the HIP
+kernels of the library; there is no other path. If the library is missing the
+import of any function here raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID_VALUE, GDN_ERR_NOT_SUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
+DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2, torch.int32: 3}
+_NAMES = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+
+
+class GdnTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 5), ("stride", ctypes.c_int64 * 5)]
+
+
+class GdnDims(ctypes.Structure):
+    _fields_ = [("Hqk", ctypes.c_int64), ("dk", ctypes.c_int64), ("Hv", ctypes.c_int64),
+                ("dv", ctypes.c_int64)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[gdn status {status}] {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m linear_attention_rnn_qkv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(GdnTensor)
+        vp, f32, i32 = ctypes.c_void_p, ctypes.c_float, ctypes.c_int32
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_version.restype = ctypes.c_char_p
+        L.gdn_prologue_fwd.argtypes = [P] * 10 + [ctypes.POINTER(GdnDims), i32, f32, P, P, P, vp]
+        L.gdn_chunk_rule_fwd.argtypes = [P, P, P, P, P, f32, i32, f32, P, P, P, P, vp]
+        L.gdn_gated_norm_fwd.argtypes = [P, P, P, f32, P, vp]
+        L.gdn_layer_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.POINTER(GdnDims), i32]
+        L.gdn_layer_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_layer_fwd.argtypes = ([P] * 12 + [ctypes.POINTER(GdnDims), f32, i32, f32, f32, vp,
+                                                ctypes.c_size_t, P, vp])
+        for name in ("gdn_prologue_fwd", "gdn_chunk_rule_fwd", "gdn_gated_norm_fwd", "gdn_layer_fwd"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def desc(t: Optional[torch.Tensor]):
+    """gdn_tensor descriptor of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if t.dtype not in DTYPE:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() > 5:
+        raise ValueError("at most 5 dims")
+    d = GdnTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else 0
+    d.dtype = DTYPE[t.dtype]
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _p(d):
+    return None if d is None else ctypes.byref(d)
+
+
+def dims_of(Hqk: int, dk: int, Hv: int, dv: int) -> GdnDims:
+    return GdnDims(Hqk, dk, Hv, dv)
+
+
+def _stream(t: torch.Tensor):
+    if t.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, lib().gdn_last_error().decode())
+
+
+def gdn_last_error() -> str:
+    return lib().gdn_last_error().decode()
+
+
+def gdn_version() -> str:
+    return lib().gdn_version().decode()
+
+
+def gdn_prologue_fwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens,
+                     dims: Sequence[int], caller_l2norm: bool = False, l2_eps: float = 1e-6,
+                     out_qkv=None, out_g=None, out_beta=None):
+    """Concatenated causal conv + SiLU and beta/g. Returns (qkv, g, beta)."""
+    Hqk, dk, Hv, dv = dims
+    B, T = x_q.shape[0], x_q.shape[1]
+    C = 2 * Hqk * dk + Hv * dv
+    dev = x_q.device
+    if out_qkv is None:
+        out_qkv = torch.empty((B, T, C), dtype=x_q.dtype, device=dev)
+    if out_g is None:
+        out_g = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+    if out_beta is None:
+        out_beta = torch.empty((B, T, Hv), dtype=torch.float32, device=dev)
+    D = [desc(t) for t in (x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens)]
+    O = [desc(t) for t in (out_qkv, out_g, out_beta)]
+    gd = dims_of(Hqk, dk, Hv, dv)
+    _check(lib().gdn_prologue_fwd(*[_p(d) for d in D], ctypes.byref(gd), int(bool(caller_l2norm)),
+                                  float(l2_eps), *[_p(d) for d in O], _stream(x_q)))
+    return out_qkv, out_g, out_beta
+
+
+def gdn_chunk_rule_fwd(q, k, v, g, beta, scale: float, use_qk_l2norm_in_kernel: bool = True,
+                       l2_eps: float = 1e-6, cu_seqlens=None, initial_state=None, out_o=None,
+                       output_final_state: bool = False, final_state=None):
+    """Chunked gated delta rule. Returns (o, final_state or None)."""
+    B, T, Hv, dv = v.shape
+    dk = q.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    if out_o is None:
+        out_o = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, Hv, dv, dk), dtype=torch.float32, device=q.device)
+    D = [desc(t) for t in (q, k, v, g, beta)]
+    E = [desc(t) for t in (cu_seqlens, initial_state, out_o, final_state)]
+    _check(lib().gdn_chunk_rule_fwd(*[_p(d) for d in D], float(scale),
+                                    int(bool(use_qk_l2norm_in_kernel)), float(l2_eps),
+                                    *[_p(d) for d in E], _stream(q)))
+    return out_o, final_state
+
+
+def gdn_gated_norm_fwd(o, gate, weight, eps: float = 1e-5, out=None):
+    """RMSNorm (act dtype) then FP32 SiLU gate. Returns out (contiguous)."""
+    if out is None:
+        out = torch.empty(o.shape, dtype=o.dtype, device=o.device)
+    D = [desc(t) for t in (o, gate, weight)]
+    _check(lib().gdn_gated_norm_fwd(*[_p(d) for d in D], float(eps), _p(desc(out)), _stream(o)))
+    return out
+
+
+def gdn_layer_workspace_bytes(B: int, T: int, dims: Sequence[int], dtype: torch.dtype) -> int:
+    gd = dims_of(*dims)
+    return int(lib().gdn_layer_workspace_bytes(int(B), int(T), ctypes.byref(gd), DTYPE[dtype]))
+
+
+def gdn_layer_fwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens,
+                  dims: Sequence[int], scale: float, use_qk_l2norm_in_kernel: bool = True,
+                  l2_eps: float = 1e-6, rms_eps: float = 1e-5, workspace=None, out=None):
+    """The layer core (prologue -> chunk rule -> gated norm). Returns out."""
+    Hqk, dk, Hv, dv = dims
+    B, T = x_q.shape[0], x_q.shape[1]
+    nbytes = gdn_layer_workspace_bytes(B, T, dims, x_q.dtype)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_q.device)
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=x_q.dtype, device=x_q.device)
+    D = [desc(t) for t in (x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w,
+                           cu_seqlens)]
+    gd = dims_of(Hqk, dk, Hv, dv)
+    _check(lib().gdn_layer_fwd(*[_p(d) for d in D], ctypes.byref(gd), float(scale),
+                               int(bool(use_qk_l2norm_in_kernel)), float(l2_eps), float(rms_eps),
+                               ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+                               _p(desc(out)), _stream(x_q)))
+    return out
+
+
+def dtype_name(t: torch.dtype) -> str:
+    return _NAMES[t]

@@ -18,8 +18,12 @@ the long-context grouped-query shapes of the Megatron pull requests):
 Value distributions (all workloads): pre-conv q/k/v, gate, a and b ~ N(0, 1);
 conv weight ~ U(-0.5, 0.5), shape [C, 4], no bias; A_log = log U(1, 16);
 dt_bias ~ N(0, 0.1); RMSNorm weight ~ 1 + N(0, 0.02). Draws are made in
-float32 with ``numpy.random.default_rng(42 + id)`` in a fixed order and cast
-to each tensor's dtype with round-to-nearest-even (torch's conversion).
+float32 from ``numpy.random.SeedSequence(42 + id)``: tensor number i (in a
+fixed order) uses child i of that sequence, and large tensors are drawn in
+blocks of rows, block j from child j of the tensor's sequence, so that blocks
+can be drawn on several threads with a result that does not depend on the
+thread count. Values are cast to each tensor's dtype with round-to-nearest-
+even (torch's conversion).
 Workload 1 draws one projection buffer [2, 2048, 9228] laid out
 [q 1536 | k 1536 | v 3072 | gate 3072 | b 6 | a 6] and hands out strided views
 into it (row pitch 18456 bytes, 8 mod 16). Workload 4 draws its 64 sequence
@@ -27,7 +31,9 @@ lengths from ``default_rng(42).integers(1, 4097, size=64)``.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
+import os
 from dataclasses import dataclass
 from typing import Optional, Tuple
 
@@ -97,7 +103,47 @@ def spec(cfg: int) -> Spec:
 
 
 def _cast(x: np.ndarray, dtype: str, device) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device).to(TORCH_DTYPE[dtype])
+    return torch.from_numpy(np.ascontiguousarray(x)).to(TORCH_DTYPE[dtype]).to(device=device)
+
+
+_BLOCK = 1 << 20  # values per independently seeded block
+
+
+class _Draws:
+    """Tensor-by-tensor draws from one SeedSequence (see module docstring)."""
+
+    def __init__(self, seed: int):
+        self.seq = np.random.SeedSequence(seed)
+        self.n = 0
+
+    def _next(self) -> np.random.SeedSequence:
+        child = self.seq.spawn(1)[0]
+        self.n += 1
+        return child
+
+    def normal(self, shape) -> np.ndarray:
+        seq = self._next()
+        shape = tuple(int(x) for x in shape)
+        total = int(np.prod(shape)) if shape else 1
+        out = np.empty(total, dtype=np.float32)
+        nblk = max(1, (total + _BLOCK - 1) // _BLOCK)
+        kids = seq.spawn(nblk)
+
+        def fill(j):
+            lo, hi = j * _BLOCK, min(total, (j + 1) * _BLOCK)
+            np.random.default_rng(kids[j]).standard_normal(hi - lo, dtype=np.float32, out=out[lo:hi])
+
+        workers = min(nblk, max(1, min(16, os.cpu_count() or 1)))
+        if workers == 1:
+            for j in range(nblk):
+                fill(j)
+        else:
+            with cf.ThreadPoolExecutor(workers) as ex:
+                list(ex.map(fill, range(nblk)))
+        return out.reshape(shape)
+
+    def rng(self) -> np.random.Generator:
+        return np.random.default_rng(self._next())
 
 
 def make_inputs(s: Spec, device="cpu", dt_bias_override=None) -> dict:
@@ -109,13 +155,13 @@ def make_inputs(s: Spec, device="cpu", dt_bias_override=None) -> dict:
     A_log, dt_bias [Hv] (f32), norm_w [dv], cu_seqlens (int32 [N+1] or None).
     ``dt_bias_override`` replaces the dt_bias draw (stress sets).
     """
-    rng = np.random.default_rng(s.seed)
+    dr = _Draws(s.seed)
     B, T = s.B, s.T
     nq, nv = s.Hqk * s.dk, s.Hv * s.dv
     out = {}
     if s.gate_in_proj:
         width = 2 * nq + 2 * nv + 2 * s.Hv
-        proj = _cast(rng.standard_normal((B, T, width), dtype=np.float32), s.act, device)
+        proj = _cast(dr.normal((B, T, width)), s.act, device)
         o = 0
         out["x_q"] = proj[..., o:o + nq]; o += nq
         out["x_k"] = proj[..., o:o + nq]; o += nq
@@ -125,14 +171,15 @@ def make_inputs(s: Spec, device="cpu", dt_bias_override=None) -> dict:
         out["a"] = proj[..., o:o + s.Hv]; o += s.Hv
         out["proj"] = proj
     else:
-        out["x_q"] = _cast(rng.standard_normal((B, T, nq), dtype=np.float32), s.act, device)
-        out["x_k"] = _cast(rng.standard_normal((B, T, nq), dtype=np.float32), s.act, device)
-        out["x_v"] = _cast(rng.standard_normal((B, T, nv), dtype=np.float32), s.act, device)
-        out["gate"] = _cast(rng.standard_normal((B, T, s.Hv, s.dv), dtype=np.float32),
+        out["x_q"] = _cast(dr.normal((B, T, nq)), s.act, device)
+        out["x_k"] = _cast(dr.normal((B, T, nq)), s.act, device)
+        out["x_v"] = _cast(dr.normal((B, T, nv)), s.act, device)
+        out["gate"] = _cast(dr.normal((B, T, s.Hv, s.dv)),
                             s.gate_dtype, device)
-        out["b"] = _cast(rng.standard_normal((B, T, s.Hv), dtype=np.float32), s.act, device)
-        out["a"] = _cast(rng.standard_normal((B, T, s.Hv), dtype=np.float32), s.act, device)
+        out["b"] = _cast(dr.normal((B, T, s.Hv)), s.act, device)
+        out["a"] = _cast(dr.normal((B, T, s.Hv)), s.act, device)
         out["proj"] = None
+    rng = dr.rng()
     out["conv_w"] = _cast(rng.uniform(-0.5, 0.5, (s.C, s.K)).astype(np.float32), s.act, device)
     out["conv_b"] = None
     out["A_log"] = _cast(np.log(rng.uniform(1.0, 16.0, s.Hv)).astype(np.float32), "f32", device)
@@ -164,3 +211,14 @@ def to_f64(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
     if t is None:
         return None
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def randn(shape, dtype: str, seed: int, device="cpu") -> torch.Tensor:
+    """Seeded N(0, 1) draws of ``shape`` cast to ``dtype`` (stand-alone stage
+    inputs, e.g. a recurrence output fed to the gated norm on its own)."""
+    return _cast(_Draws(seed).normal(shape), dtype, device)
+
+
+def uniform(shape, lo: float, hi: float, seed: int) -> np.ndarray:
+    """Seeded U(lo, hi) float64 draws (stress sets of the recurrence)."""
+    return np.random.default_rng(seed).uniform(lo, hi, shape)

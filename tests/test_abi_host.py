@@ -1,0 +1,156 @@
+"""Host-only tests of the C ABI: the library loads, exports every function the
+header declares, sizes the workspace, and rejects invalid arguments from
+metadata alone (no device work, so these run without a GPU). The descriptors
+here point at host memory; every call is expected to fail validation before
+anything is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from linear_attention_rnn_qkv_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED = gdn.GDN_ERR_INVALID_VALUE, gdn.GDN_ERR_NOT_SUPPORTED
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    names = set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", hdr))
+    assert names == {"gdn_last_error", "gdn_version", "gdn_prologue_fwd", "gdn_chunk_rule_fwd",
+                     "gdn_gated_norm_fwd", "gdn_layer_workspace_bytes", "gdn_layer_fwd"}
+    L = gdn.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gfx950" in gdn.gdn_version()
+
+
+def test_workspace_bytes():
+    def a256(x):
+        return (x + 255) // 256 * 256
+    B, T, dims = 2, 1000, (6, 256, 6, 512)
+    C = 2 * 6 * 256 + 6 * 512
+    expect = a256(B * T * C * 2) + 2 * a256(B * T * 6 * 4) + a256(B * T * 6 * 512 * 2)
+    assert gdn.gdn_layer_workspace_bytes(B, T, dims, torch.bfloat16) == expect
+    assert gdn.gdn_layer_workspace_bytes(B, T, (0, 64, 1, 64), torch.bfloat16) == 0
+
+
+def _expect(status, fragment, fn, *args, **kw):
+    with pytest.raises(gdn.GdnError) as e:
+        fn(*args, **kw)
+    assert e.value.status == status, str(e.value)
+    assert fragment in str(e.value), str(e.value)
+
+
+def _prologue_inputs(B=1, T=8, Hqk=2, dk=64, Hv=4, dv=64, dt=torch.bfloat16):
+    nq, nv = Hqk * dk, Hv * dv
+    C = 2 * nq + nv
+    z = lambda *s, d=dt: torch.zeros(*s, dtype=d)  # noqa: E731
+    return dict(x_q=z(B, T, nq), x_k=z(B, T, nq), x_v=z(B, T, nv), conv_w=z(C, 4), conv_b=None,
+                a=z(B, T, Hv), b=z(B, T, Hv), A_log=z(Hv, d=torch.float32),
+                dt_bias=z(Hv, d=torch.float32), cu_seqlens=None, dims=(Hqk, dk, Hv, dv))
+
+
+def _pro(**over):
+    kw = _prologue_inputs()
+    kw.update(over)
+    return gdn.gdn_prologue_fwd(**kw)
+
+
+def test_prologue_rejections():
+    x = _prologue_inputs()
+    _expect(INVALID, "empty", gdn.gdn_prologue_fwd, **{**_prologue_inputs(T=0)})
+    _expect(INVALID, "multiple of Hqk", _pro, dims=(3, 64, 4, 64))
+    _expect(INVALID, "powers of two", _pro, dims=(2, 48, 4, 64))
+    _expect(INVALID, "x_k: dtype", _pro, x_k=x["x_k"].half())
+    _expect(INVALID, "innermost stride", _pro, x_q=torch.zeros(1, 8, 256, dtype=torch.bfloat16)[..., ::2])
+    _expect(INVALID, "A_log: dtype", _pro, A_log=torch.zeros(4, dtype=torch.bfloat16))
+    _expect(INVALID, "conv_w: dim 0", _pro, conv_w=torch.zeros(100, 4, dtype=torch.bfloat16))
+    _expect(INVALID, "requires B == 1", gdn.gdn_prologue_fwd,
+            **{**_prologue_inputs(B=2), "cu_seqlens": torch.tensor([0, 8], dtype=torch.int32)})
+    _expect(INVALID, "cu_seqlens: dtype", _pro, cu_seqlens=torch.tensor([0, 8], dtype=torch.float32))
+    C = 2 * 128 + 256
+    qkv_nc = torch.zeros(1, 8, 2 * C, dtype=torch.bfloat16)[..., :C]
+    _expect(INVALID, "out_qkv: must be contiguous", _pro, out_qkv=qkv_nc)
+    buf = torch.zeros(1, 8, C, dtype=torch.bfloat16)
+    _expect(INVALID, "overlaps", _pro, x_q=buf[..., :128], out_qkv=buf)
+    _expect(INVALID, "descriptor is NULL", _pro, b=None)
+
+
+def _chunk_inputs(B=1, T=8, Hqk=2, dk=64, Hv=4, dv=64, dt=torch.bfloat16):
+    z = lambda *s, d=dt: torch.zeros(*s, dtype=d)  # noqa: E731
+    return dict(q=z(B, T, Hqk, dk), k=z(B, T, Hqk, dk), v=z(B, T, Hv, dv),
+                g=z(B, T, Hv, d=torch.float32), beta=z(B, T, Hv, d=torch.float32), scale=0.125)
+
+
+def _chk(**over):
+    kw = _chunk_inputs()
+    kw.update(over)
+    return gdn.gdn_chunk_rule_fwd(**kw)
+
+
+def test_chunk_rule_rejections():
+    _expect(INVALID, "empty", gdn.gdn_chunk_rule_fwd, **_chunk_inputs(T=0))
+    _expect(UNSUPPORTED, "not instantiated", gdn.gdn_chunk_rule_fwd, **_chunk_inputs(dk=32))
+    _expect(UNSUPPORTED, "not instantiated", gdn.gdn_chunk_rule_fwd, **_chunk_inputs(dk=256, dt=torch.float32))
+    _expect(INVALID, "multiple of Hqk", gdn.gdn_chunk_rule_fwd, **_chunk_inputs(Hqk=3, Hv=4))
+    _expect(INVALID, "initial_state: dim", _chk, initial_state=torch.zeros(1, 4, 64, 32))
+    _expect(INVALID, "g: dtype", _chk, g=torch.zeros(1, 8, 4, dtype=torch.bfloat16))
+    _expect(INVALID, "scale", _chk, scale=float("inf"))
+    qbuf = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    _expect(INVALID, "out_o overlaps", _chk, q=qbuf, out_o=qbuf.view(1, 8, 1, 128)[..., :64]
+            .expand(1, 8, 4, 64))
+    raw = torch.zeros(1 * 8 * 2 * 64 + 1, dtype=torch.bfloat16)
+    q_mis = raw[1:].view(1, 8, 2, 64)
+    _expect(UNSUPPORTED, "16-byte aligned", _chk, q=q_mis)
+
+
+def _norm_inputs(B=1, T=4, H=2, dv=64, dt=torch.bfloat16, gdt=None, wdt=None):
+    return dict(o=torch.zeros(B, T, H, dv, dtype=dt), gate=torch.zeros(B, T, H, dv, dtype=gdt or dt),
+                weight=torch.ones(dv, dtype=wdt or dt))
+
+
+def _nrm(**over):
+    kw = _norm_inputs()
+    kw.update(over)
+    return gdn.gdn_gated_norm_fwd(**kw)
+
+
+def test_gated_norm_rejections():
+    # Megatron Core "GDN Elementwise Fusion", Post-GDR requirements: nonempty
+    # output, matching gate shape, power-of-two head dim, gate in the
+    # activation dtype or FP32, contiguous weight of length head_dim.
+    _expect(INVALID, "empty", gdn.gdn_gated_norm_fwd, **_norm_inputs(T=0))
+    _expect(INVALID, "power of two", gdn.gdn_gated_norm_fwd, **_norm_inputs(dv=96))
+    _expect(UNSUPPORTED, "not instantiated", gdn.gdn_gated_norm_fwd, **_norm_inputs(dv=32))
+    _expect(INVALID, "gate: dim", _nrm, gate=torch.zeros(1, 4, 3, 64, dtype=torch.bfloat16))
+    _expect(INVALID, "gate: dtype", _nrm, gate=torch.zeros(1, 4, 2, 64, dtype=torch.float16))
+    _expect(INVALID, "weight: must be contiguous", _nrm, weight=torch.ones(128, dtype=torch.bfloat16)[::2])
+    _expect(INVALID, "weight: dim", _nrm, weight=torch.ones(32, dtype=torch.bfloat16))
+    _expect(INVALID, "out: must be contiguous", _nrm,
+            out=torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)[..., :64])
+    _expect(INVALID, "out: dtype", _nrm, out=torch.zeros(1, 4, 2, 64, dtype=torch.float32))
+    o = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    _expect(INVALID, "overlaps", _nrm, o=o, out=o)
+
+
+def test_layer_rejections():
+    x = _prologue_inputs()
+    kw = dict(x, gate=torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16),
+              norm_w=torch.ones(64, dtype=torch.bfloat16), scale=0.125)
+    small = torch.zeros(256, dtype=torch.uint8)
+    _expect(INVALID, "workspace too small", gdn.gdn_layer_fwd, **kw, workspace=small)
+    n = gdn.gdn_layer_workspace_bytes(1, 8, (2, 64, 4, 64), torch.bfloat16)
+    big = torch.zeros(n + 512, dtype=torch.uint8)
+    off = (-big.data_ptr()) % 256
+    mis = big[off + 8: off + 8 + n]
+    _expect(INVALID, "256-byte aligned", gdn.gdn_layer_fwd, **kw, workspace=mis)
+
+
+def test_error_message_is_per_call():
+    with pytest.raises(gdn.GdnError):
+        _nrm(o=torch.zeros(1, 0, 2, 64, dtype=torch.bfloat16))
+    assert "empty" in gdn.gdn_last_error()
