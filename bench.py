@@ -1,0 +1,243 @@
+"""Benchmark of the GDN layer-core forward on one MI355X.
+
+One step = one pass of the whole layer core (prologue -> chunked gated delta
+rule -> gated RMSNorm) over one batch of synthetic input resident in HBM.
+Default workload: long-bf16-T131072 (B=1, 131072 tokens, 16 q/k heads of 128,
+32 value heads of 128, chunk 64), the configuration the roofline fractions of
+the stages are defined on. ``--config 0..4`` selects another workload.
+
+Prints one JSON line: whole-job tokens/s, per-stage times and roofline
+fractions measured with HIP events on the stream the kernels run on, the
+dominant kernel's roofline, and the FP64 CPU oracle timed on a bounded sample
+of the same workload on this machine's host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN layer-core fwd tokens/s at 1 GPU; % of HBM BW / MFMA peak per stage"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+CHUNK = 64
+
+
+def stage_work(s) -> dict:
+    """Algorithmic bytes / flops per token of each stage (no recompute)."""
+    e = {"f32": 4, "bf16": 2, "f16": 2}[s.act]
+    eg = {"f32": 4, "bf16": 2, "f16": 2}[s.gate_dtype]
+    C = s.C
+    return {
+        # read x (C channels) and a, b; write qkv (C) and g, beta (FP32)
+        "prologue_bytes": 2 * C * e + 2 * s.Hv * e + 8 * s.Hv,
+        # read q, k, v, g, beta; write o
+        "chunk_bytes": (2 * s.Hqk * s.dk + 2 * s.Hv * s.dv) * e + 8 * s.Hv,
+        "chunk_flops": s.Hv * (6 * CHUNK * s.dk + 4 * CHUNK * s.dv + 6 * s.dk * s.dv),
+        # read o and gate, write out
+        "norm_bytes": s.Hv * s.dv * (2 * e + eg),
+    }
+
+
+def cpu_baseline(cfg: int, s, budget_s: float) -> dict:
+    """The FP64 oracle (as it stands) on a prefix of the workload's tokens."""
+    import numpy as np
+
+    from linear_attention_rnn_qkv_amd import synth
+    from oracle import gdn as O
+
+    threads = O.default_threads()
+    # calibrate on a short prefix, then run a prefix sized to the budget
+    def run(ntok):
+        sub = s.replace(T=ntok, B=1, lengths=None)
+        x = synth.make_inputs(sub)
+        f = synth.to_f64
+        t0 = time.perf_counter()
+        O.layer(f(x["x_q"]), f(x["x_k"]), f(x["x_v"]), f(x["conv_w"]), None, f(x["a"]), f(x["b"]),
+                f(x["A_log"]), f(x["dt_bias"]), f(x["gate"]), f(x["norm_w"]), Hqk=s.Hqk, dk=s.dk,
+                Hv=s.Hv, dv=s.dv, act=s.act, scale=s.dk ** -0.5, threads=threads)
+        return time.perf_counter() - t0
+
+    t_cal = run(256)
+    ntok = int(min(s.T, max(256, 256 * budget_s / max(t_cal, 1e-3))))
+    ntok = max(256, ntok // 64 * 64)
+    dt = run(ntok)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {ntok} tokens of one sequence of workload {s.name}, all {s.Hv} value "
+                      f"heads, whole layer core (FP64 C recurrence + NumPy stages), {dt:.1f} s",
+            "cpu": cpu}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the layer core "
+              "shards by heads or sequences without a collective, which is not built here.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from linear_attention_rnn_qkv_amd import gdn, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    s = synth.spec(args.config)
+    print(f"[bench] workload {args.config} {s.name}: generating inputs", file=sys.stderr, flush=True)
+    x = synth.make_inputs(s)
+    d = {}
+    for k, v in x.items():
+        d[k] = v.cuda() if isinstance(v, torch.Tensor) else v
+    if x.get("proj") is not None:
+        proj = x["proj"].cuda()
+        for k in ("x_q", "x_k", "x_v", "gate", "b", "a"):
+            v = x[k]
+            d[k] = proj.as_strided(v.shape, v.stride(), v.storage_offset() - x["proj"].storage_offset())
+    del x
+    dims = (s.Hqk, s.dk, s.Hv, s.dv)
+    scale = s.dk ** -0.5
+    dt = synth.TORCH_DTYPE[s.act]
+    ws = torch.empty(gdn.gdn_layer_workspace_bytes(s.B, s.T, dims, dt), dtype=torch.uint8, device="cuda")
+    out = torch.empty((s.B, s.T, s.Hv, s.dv), dtype=dt, device="cuda")
+    # stage buffers for the per-stage timing loop (same kernels, same shapes)
+    qkv = torch.empty((s.B, s.T, s.C), dtype=dt, device="cuda")
+    g = torch.empty((s.B, s.T, s.Hv), dtype=torch.float32, device="cuda")
+    beta = torch.empty_like(g)
+    o = torch.empty((s.B, s.T, s.Hv, s.dv), dtype=dt, device="cuda")
+    nq = s.Hqk * s.dk
+    qv = qkv[..., :nq].unflatten(-1, (s.Hqk, s.dk))
+    kv = qkv[..., nq:2 * nq].unflatten(-1, (s.Hqk, s.dk))
+    vv = qkv[..., 2 * nq:].unflatten(-1, (s.Hv, s.dv))
+
+    def layer():
+        gdn.gdn_layer_fwd(d["x_q"], d["x_k"], d["x_v"], d["conv_w"], None, d["a"], d["b"], d["A_log"],
+                          d["dt_bias"], d["gate"], d["norm_w"], d["cu_seqlens"], dims, scale, workspace=ws,
+                          out=out)
+
+    def prologue():
+        gdn.gdn_prologue_fwd(d["x_q"], d["x_k"], d["x_v"], d["conv_w"], None, d["a"], d["b"], d["A_log"],
+                             d["dt_bias"], d["cu_seqlens"], dims, out_qkv=qkv, out_g=g, out_beta=beta)
+
+    def chunk():
+        gdn.gdn_chunk_rule_fwd(qv, kv, vv, g, beta, scale, True, 1e-6, d["cu_seqlens"], out_o=o)
+
+    def norm():
+        gdn.gdn_gated_norm_fwd(o, d["gate"], d["norm_w"], 1e-5, out=out)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        layer()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps of the layer core.
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        layer()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # Per-stage durations: the same three kernels, one event between each.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        e = evs[i]
+        e[0].record(stream)
+        prologue()
+        e[1].record(stream)
+        chunk()
+        e[2].record(stream)
+        norm()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t_pro = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_chk = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    t_nrm = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    w = stage_work(s)
+    ntok = s.tokens
+    pb, cb, cf, nb = (w["prologue_bytes"] * ntok, w["chunk_bytes"] * ntok, w["chunk_flops"] * ntok,
+                      w["norm_bytes"] * ntok)
+    mfma_peak = MFMA_PEAK_TFLOPS[s.act]
+
+    def gbs(b, t_ms):
+        return b / (t_ms * 1e-3) / 1e9
+
+    stages = {
+        "prologue": {"kernel": "prologue_kernel", "ms": t_pro, "bytes": pb, "GB/s": gbs(pb, t_pro),
+                     "hbm_frac": gbs(pb, t_pro) / HBM_PEAK_GBS},
+        "chunk_rule": {"kernel": "chunk_rule_kernel", "ms": t_chk, "bytes": cb, "flops": cf,
+                       "GB/s": gbs(cb, t_chk), "hbm_frac": gbs(cb, t_chk) / HBM_PEAK_GBS,
+                       "TFLOP/s": cf / (t_chk * 1e-3) / 1e12,
+                       "mfma_frac": cf / (t_chk * 1e-3) / 1e12 / mfma_peak},
+        "gated_norm": {"kernel": "gated_norm_kernel", "ms": t_nrm, "bytes": nb, "GB/s": gbs(nb, t_nrm),
+                       "hbm_frac": gbs(nb, t_nrm) / HBM_PEAK_GBS},
+    }
+    # dominant kernel and the roof that bounds it in the ideal
+    dom = max(stages, key=lambda k: stages[k]["ms"])
+    st = stages[dom]
+    if dom == "chunk_rule" and cf / (mfma_peak * 1e12) > cb / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": st["TFLOP/s"], "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": st["mfma_frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": st["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": st["hbm_frac"]}
+    roof["kernel"] = st["kernel"]
+    roof["traffic"] = None
+
+    result = {
+        "metric": METRIC,
+        "value": ntok / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.act,
+        "data": "synthetic",
+        "config": {"workload": s.name, "B": s.B, "T": s.T, "tokens": ntok, "Hqk": s.Hqk, "dk": s.dk,
+                   "Hv": s.Hv, "dv": s.dv, "chunk": CHUNK, "conv_taps": 4, "parallelism": "single GPU"},
+        "roofline": roof,
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(args.config, s, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
