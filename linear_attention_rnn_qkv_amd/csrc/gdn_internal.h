@@ -70,6 +70,10 @@ hipError_t launch_gated_norm(const NormArgs &a, hipStream_t s);
 // Host-side capability query used by validation (no device calls).
 bool chunk_rule_supported(int64_t dk, int32_t act);
 
+// The wavefront-pipelined chunk kernel (16-bit inputs, dk 64 or 128).
+bool chunk_rule_v2_supported(int64_t dk, int32_t act);
+hipError_t launch_chunk_rule_v2(const ChunkArgs &a, hipStream_t s);
+
 // Largest power-of-two alignment (bytes, <= 16) of an address or stride set.
 inline int align_of_host(uint64_t addr) {
   int a = 16;
