@@ -15,29 +15,32 @@
 // q and k are used raw (exactly as stored); the norms enter as row factors.
 //
 // One workgroup = (sequence, value head, 16 rows of dv), four wavefronts with
-// fixed roles, one barrier per step. At step s:
-//   wave 0  state(s):   K S^T, R, the triangular solve by 16 x 16 blocks
-//                       (diagonal inverses from wave 3, -A blocks from wave 1),
-//                       the state update; S lives in MFMA accumulators.
-//   wave 1  prep(s+2):  loads k, g, beta; norms, gamma and row factors; K K^T
-//                       -> A (FP32 diagonal blocks, act-dtype -A blocks);
-//                       stores the k rows for waves 0 and 2.
-//   wave 2  prep(s+1):  loads q and the v slice; norms; Q K^T -> P.
-//   wave 3  inv(s+1):   (I + A_bb)^-1 of the four diagonal blocks (FP32
-//                       forward substitution, one lane per column);
-//           out(s-1):   Q S^T and P Vn -> o.
-// Every hand-off crosses at least one barrier; ring buffers in LDS are sized
-// so that no slot is written while another wave reads it.
+// fixed roles and one barrier per step. At step s:
+//   wave 0  state(s):  K S^T, R, the triangular solve by 16 x 16 blocks, the
+//                      state update; S lives in MFMA accumulators.
+//   wave 1  prep(s+1): K K^T -> 1/|k| (its diagonal) and A; the four
+//                      16 x 16 diagonal inverses (FP32, right-looking
+//                      substitution, one lane per column); -A blocks.
+//   wave 2  loads:     g, beta of chunk s+3 and their per-row factors (gamma
+//                      scan, exponentials); then streams the k tile of chunk
+//                      s+3 and the q, v tiles of chunk s+2 from HBM straight
+//                      into LDS rings (global_load_lds, no registers). Copies
+//                      issued at step s have retired before barrier s+2, which
+//                      publishes them: a step of latency is hidden.
+//   wave 3  out(s):    Q S^T and P^T = K Q^T for chunk s (P^T accumulators are
+//                      exactly the A operands of P Vn); finishes o(s-1) with
+//                      Vn(s-1) from wave 0.
+// Ring sizes make sure no slot is overwritten while another wave reads it.
 //
 // Operand layouts. With v_mfma_f32_16x16x32, lane l = 16 g + c supplies 8 k
 // values; an accumulator tile holds rows 4 g + i (i < 4) of column c. Two
 // accumulator tiles (rows 16 t .. 16 t + 15, t = 2q, 2q + 1) therefore form
-// one B operand whose k slots are {32q + 4g + i} then {32q + 16 + 4g + i}.
-// Every matrix used against such an operand is stored in LDS with its k
-// columns permuted to that order (pcol below), so one 16-byte read yields a
-// matching A fragment. The state update contracts K over chunk rows; its A
-// fragments come straight from the row-major k tile through two
-// ds_read_b64_tr_b16 transposing reads.
+// one B operand whose k slots are {32q + 4g + i} then {32q + 16 + 4g + i},
+// and every A operand used against it is read in that k order (two 8-byte
+// LDS reads). q/k tiles are stored row-major with the 16-byte chunks of each
+// row XOR-swizzled by the row index, which keeps these reads and the
+// ds_read_b64_tr_b16 transposing reads (K^T fragments of the state update)
+// free of bank conflicts.
 #include "device_common.h"
 #include "gdn_internal.h"
 
@@ -52,6 +55,7 @@ typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 template <typename T> struct M2;
 template <> struct M2<bf16> {
@@ -79,45 +83,52 @@ template <> struct M2<f16> {
   static __device__ __forceinline__ f4 as_f4(v4 x) { return x; }
 };
 
-// Storage column of logical column x inside rows whose k order is permuted
-// per 32-block: logical 4a + i -> 8a + i, logical 16 + 4a + i -> 8a + 4 + i.
-__device__ __forceinline__ int pcol(int x) {
-  const int xi = x & 31;
-  return (x & ~31) + ((xi & 15) >> 2) * 8 + ((xi >> 4) << 2) + (xi & 3);
-}
-
-enum { F_GAM = 0, F_BETA, F_RK, F_RQ, F_A, F_CW, F_BQ, F_MISC, F_N };
+enum { F_GAM = 0, F_BETA, F_EG, F_ECG, F_RK, F_MISC, F_N };
 
 template <typename T, int DK>
-struct Lds2 {
-  static constexpr int LDK = DK + 8;  // k rows (dk columns, permuted)
-  static constexpr int LDP = BT + 8;  // P rows (chunk columns, permuted)
-  static constexpr int LDV = BT + 8;  // V^T rows
-  alignas(16) T k[3][BT * LDK];
-  alignas(16) T p[3][BT * LDP];
-  alignas(16) T vt[2][DVT * LDV];
-  alignas(16) T ao[3][6][256];        // -A_ij, i > j, row-major 16 x 16
-  alignas(16) T tii[2][4][256];       // (I + A_bb)^-1, row-major 16 x 16
-  alignas(16) T sfrag[2][64 * (DK / 4)];
-  alignas(16) T wfrag[2][64 * 16];
-  alignas(16) float ad[3][4][256];    // A_bb, FP32, row-major 16 x 16
-  alignas(16) float fac[4][F_N][BT];  // per-row factors of a chunk
+struct Lds3 {
+  static constexpr int RB = DK * 2;    // bytes per q/k row
+  static constexpr int CPR = RB / 16;  // 16-byte chunks per row
+  static constexpr int TILE = BT * RB;
+  alignas(16) unsigned char k[4][TILE];  // k rows of chunk c in slot c % 4
+  alignas(16) unsigned char q[3][TILE];  // q rows of chunk c in slot c % 3
+  alignas(16) T v[3][BT * DVT];          // v slice, row-major [64][16]
+  alignas(16) float adt[4][256];         // A_bb, FP32, column-major (wave 1 only)
+  alignas(16) T ao[2][6][256];           // -A_ij (i > j), row-major 16 x 16
+  alignas(16) T tii[2][4][256];          // (I + A_bb)^-1, row-major 16 x 16
+  alignas(16) T sfrag[2][64 * (DK / 4)]; // state fragments per lane
+  alignas(16) T wfrag[2][64 * 16];       // Vn fragments per lane
+  alignas(16) float fac[4][F_N][BT];     // per-row factors of chunk c, slot c % 4
 };
 
 __device__ __forceinline__ int off_idx(int i, int j) { return i * (i - 1) / 2 + j; }
 
-// Workgroup barrier for LDS hand-offs only. Waves exchange data through LDS
-// alone, so each wave waits for its own LDS accesses (lgkmcnt 0) and then
-// meets the others; outstanding global loads (prefetches for later steps) and
-// stores (outputs) stay in flight across the barrier. The memory clobber keeps
-// the compiler from moving LDS accesses across it.
+// Workgroup barrier for LDS hand-offs only: each wave waits for its own LDS
+// accesses (lgkmcnt 0) and meets the others; global stores stay in flight.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Keeps the global loads issued above it (prefetches for the next step) from
-// being scheduled below it, so they are in flight during this step's work.
-__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+// Orders LDS accesses of the lanes of one wavefront: stores issued before it
+// are complete, and the compiler moves no LDS access across it. Needed where
+// lanes read what other lanes of the same wave stored (the per-thread memory
+// model lets the compiler hoist such a read above the other lanes' stores).
+__device__ __forceinline__ void lds_fence_wave() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Asynchronous global -> LDS copy of 16 bytes per lane (gfx950
+// global_load_lds_dwordx4): lane i's bytes land at `lds + 16 i`. The compiler
+// sets M0 and keeps the wait state an LDS DMA needs after an M0 write.
+__device__ __forceinline__ void g2l16(const void *gptr, unsigned char *lds) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)(lds_u8 *)lds, 16, 0, 0);
+}
+// s_waitcnt vmcnt(N) for a count known only at run time (one of few values).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <typename T>
 __device__ __forceinline__ typename M2<T>::f8 cat8(typename M2<T>::v4 a, typename M2<T>::v4 b) {
@@ -129,55 +140,33 @@ __device__ __forceinline__ typename M2<T>::v4 cvt4(f32x4 x) {
   return __builtin_convertvector(x, typename M2<T>::v4);
 }
 
-// Rows [0, nr) of a chunk (row stride st, elements, nr >= 1) into fragments
-// with the permuted k order: fr[mt][p] = row 16 mt + c, k slots 32p + 4g + i
-// and 32p + 16 + 4g + i. Rows beyond nr repeat row nr - 1 (in bounds, no
-// branches, no use of the data at issue time). Such padding rows are inert:
-// their beta and g are zero, so their rows of A, R and Vn vanish, a padding
-// column only meets valid rows above the diagonal (masked), and their
-// outputs are not stored.
-template <typename T, int KT>
-__device__ __forceinline__ void load_rows(typename M2<T>::f8 (&fr)[4][KT], const T *base, int64_t st,
-                                          int nr, int g, int c) {
-  using f8 = typename M2<T>::f8;
-  struct Pair {
-    uint2 lo, hi;
-  };
+// A/B fragment from a q/k tile: `off` is the lane's byte offset of row
+// 16 mt + c, k-step pp, half h (see FragOffsets).
+template <typename T>
+__device__ __forceinline__ typename M2<T>::f8 frag_at(const unsigned char *tile, int off0, int off1) {
+  using v4 = typename M2<T>::v4;
+  return cat8<T>(*reinterpret_cast<const v4 *>(tile + off0), *reinterpret_cast<const v4 *>(tile + off1));
+}
+
+// Sum of squares of 8 packed 16-bit values (two-element dot products).
+template <typename T>
+__device__ __forceinline__ float sumsq8(typename M2<T>::f8 x, float acc) {
+  if constexpr (sizeof(T) == 2 && __is_same(T, bf16)) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = 16 * mt + c;
-    const T *rp = base + (int64_t)(row < nr ? row : nr - 1) * st;
+    for (int j = 0; j < 4; ++j) {
+      const b2 v = {x[2 * j], x[2 * j + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+    }
+  } else {
+    typedef __attribute__((ext_vector_type(2))) _Float16 h2;
 #pragma unroll
-    for (int pp = 0; pp < KT; ++pp) {
-      Pair v;
-      v.lo = *reinterpret_cast<const uint2 *>(rp + 32 * pp + 4 * g);
-      v.hi = *reinterpret_cast<const uint2 *>(rp + 32 * pp + 16 + 4 * g);
-      fr[mt][pp] = __builtin_bit_cast(f8, v);
+    for (int j = 0; j < 4; ++j) {
+      const h2 v = {x[2 * j], x[2 * j + 1]};
+      acc = __builtin_amdgcn_fdot2(v, v, acc, false);
     }
   }
-}
-
-// Row sums of squares of fragments (row 16 mt + c), summed over the 4 groups.
-template <typename T, int KT>
-__device__ __forceinline__ void row_sumsq(const typename M2<T>::f8 (&fr)[4][KT], float (&ss)[4]) {
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    float s = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < KT; ++pp)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = f(fr[mt][pp][j]);
-        s += x * x;
-      }
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
-    ss[mt] = s;
-  }
-}
-
-__device__ __forceinline__ float pick4(const float (&v)[4], int i) {
-  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+  return acc;
 }
 
 template <typename T, int DK>
@@ -186,12 +175,12 @@ __global__ __launch_bounds__(kThreads) void chunk_rule_v2_kernel(ChunkArgs p) {
   using f8 = typename MF::f8;
   using f4 = typename MF::f4;
   using v4 = typename MF::v4;
-  using SM = Lds2<T, DK>;
+  using SM = Lds3<T, DK>;
   constexpr int KT = DK / 32;  // k-steps over dk
   constexpr int NT = DK / 16;  // 16-row tiles of dk
-  constexpr int LDK = SM::LDK, LDP = SM::LDP, LDV = SM::LDV;
   constexpr int SF = DK / 4;   // state-fragment elements per lane
-  typedef f8 Frags[4][KT];
+  constexpr int RB = SM::RB, CPR = SM::CPR;
+  constexpr int NI = SM::TILE / 1024;  // 1 KB global_load_lds rounds per tile
   __shared__ SM sm;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -229,53 +218,69 @@ __global__ __launch_bounds__(kThreads) void chunk_rule_v2_kernel(ChunkArgs p) {
     const int64_t r = L - (int64_t)ch * BT;
     return (int)(r < BT ? r : BT);
   };
-  // Steps s = -2 .. Nc; every wave runs them all (one barrier each). Roles
-  // with prefetched operands alternate between two register buffers so that
-  // the loads for the next step land directly where that step reads them.
-  auto run_steps = [&](auto &&step) {
-    int s = -2;
-    for (; s + 1 <= Nc; s += 2) {
-      step(s, 0);
-      step(s + 1, 1);
-    }
-    if (s <= Nc) step(s, 0);
-  };
-
+  // Per-lane byte offsets inside a swizzled q/k tile (XOR of the 16-byte
+  // chunk index with the row's low bits; rows 16 mt + c share c's bits):
+  // fragment of row 16 mt + c, k-step pp, half h  ->  fo[pp][h] + mt * 16 RB.
+  int fo[KT][2];
+#pragma unroll
+  for (int pp = 0; pp < KT; ++pp)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      fo[pp][hh] = c * RB + (((4 * pp + (g >> 1) + 2 * hh) ^ (c & (CPR - 1))) << 4) + 8 * (g & 1);
+  // Steps s = -3 .. Nc, one barrier each, in every wave.
   if (wave == 0) {
     // ---------------------------------------------------------------- state
-    // S[mt][i] = S[dv row c][dk 16 mt + 4 g + i], FP32 accumulators.
+    // S[mt][i] = S[dv row c][dk 16 mt + 4 g + i], FP32 accumulators; Sf are
+    // the act-dtype B fragments of S for the next K S^T.
     f32x4 S[NT];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         S[mt][i] = p.init_state ? p.init_state[st_base + (int64_t)c * DK + 16 * mt + 4 * g + i] : 0.f;
-    run_steps([&](int s, int) {
+    f8 Sf[KT];
+#pragma unroll
+    for (int pp = 0; pp < KT; ++pp) {
+      Sf[pp] = cat8<T>(cvt4<T>(S[2 * pp]), cvt4<T>(S[2 * pp + 1]));
+      *reinterpret_cast<f8 *>(&sm.sfrag[0][lane * SF + 8 * pp]) = Sf[pp];
+    }
+    // transposing-read offsets: row 32 q + 16 hh + 4 g + (c >> 2), columns
+    // 16 mt + 4 (c & 3) .. + 3  ->  trb + trc[mt] + (32 q + 16 hh) RB
+    const int yrow = (4 * g + (c >> 2)) & (CPR - 1);
+    const int trb = (4 * g + (c >> 2)) * RB + 8 * (c & 1);
+    int trc[NT];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) trc[mt] = trb + (((2 * mt + ((c & 3) >> 1)) ^ yrow) << 4);
+    for (int s = -3; s <= Nc; ++s) {
       lds_barrier();
-      if (s < 0 || s >= Nc) return;
-      const int k3 = s % 3, k2 = s & 1, k4 = s & 3;
-      const T *kt = sm.k[k3];
-      const float *fa = &sm.fac[k4][0][0];
+      if (s < 0 || s >= Nc) continue;
+      const unsigned char *kt = sm.k[s & 3];
+      const int s2 = s & 1;
+      const float *fa = &sm.fac[s & 3][0][0];
       // operands that do not depend on S: read them all first
-      Frags kf;
+      f8 kf[4][KT];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int pp = 0; pp < KT; ++pp)
-          kf[mt][pp] = *reinterpret_cast<const f8 *>(&kt[(16 * mt + c) * LDK + 32 * pp + 8 * g]);
-      v4 vv[4];
-      f32x4 be[4], aa[4], cw[4];
+          kf[mt][pp] = frag_at<T>(kt + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+      f32x4 be[4], aa[4], cw[4], vv[4];
+      const T *vt = sm.v[s % 3];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int r0 = 16 * mt + 4 * g;
-        vv[mt] = *reinterpret_cast<const v4 *>(&sm.vt[k2][c * LDV + r0]);
         be[mt] = *reinterpret_cast<const f32x4 *>(&fa[F_BETA * BT + r0]);
-        aa[mt] = *reinterpret_cast<const f32x4 *>(&fa[F_A * BT + r0]);
-        cw[mt] = *reinterpret_cast<const f32x4 *>(&fa[F_CW * BT + r0]);
+        const f32x4 eg = *reinterpret_cast<const f32x4 *>(&fa[F_EG * BT + r0]);
+        const f32x4 ecg = *reinterpret_cast<const f32x4 *>(&fa[F_ECG * BT + r0]);
+        const f32x4 rk = *reinterpret_cast<const f32x4 *>(&fa[F_RK * BT + r0]);
+        aa[mt] = be[mt] * eg * rk;
+        cw[mt] = ecg * rk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[mt][i] = f(vt[(r0 + i) * DVT + c]);
       }
       const float eC = fa[F_MISC * BT];
-      const T *ti = sm.tii[k2][0];
-      const T *ao = sm.ao[k3][0];
+      const T *ti = sm.tii[s2][0];
+      const T *ao = sm.ao[s2][0];
       f4 tf[4], af[6];
 #pragma unroll
       for (int b = 0; b < 4; ++b) tf[b] = *reinterpret_cast<const f4 *>(&ti[b * 256 + c * 16 + 4 * g]);
@@ -284,23 +289,15 @@ __global__ __launch_bounds__(kThreads) void chunk_rule_v2_kernel(ChunkArgs p) {
       // A fragments of K^T for the state update (transposing reads)
       f8 kt8[NT][2];
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt) {
-        const int colst = pcol(16 * mt + 4 * (c & 3));
+      for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const T *a1 = &kt[(32 * q + 4 * g + (c >> 2)) * LDK + colst];
-          const T *a2 = &kt[(32 * q + 16 + 4 * g + (c >> 2)) * LDK + colst];
-          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<T *>(a1));
-          const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<T *>(a2));
+          const unsigned char *a1 = kt + trc[mt] + (32 * q) * RB;
+          const unsigned char *a2 = kt + trc[mt] + (32 * q + 16) * RB;
+          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(a1));
+          const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(a2));
           kt8[mt][q] = cat8<T>(__builtin_bit_cast(v4, r1), __builtin_bit_cast(v4, r2));
         }
-      }
-      // state fragments (also handed to the output wave)
-      f8 Sf[KT];
-#pragma unroll
-      for (int pp = 0; pp < KT; ++pp) Sf[pp] = cat8<T>(cvt4<T>(S[2 * pp]), cvt4<T>(S[2 * pp + 1]));
-#pragma unroll
-      for (int pp = 0; pp < KT; ++pp) *reinterpret_cast<f8 *>(&sm.sfrag[k2][lane * SF + 8 * pp]) = Sf[pp];
       // Y = K S^T (four independent accumulators)
       f32x4 Y[4];
 #pragma unroll
@@ -311,9 +308,7 @@ __global__ __launch_bounds__(kThreads) void chunk_rule_v2_kernel(ChunkArgs p) {
         for (int mt = 0; mt < 4; ++mt) Y[mt] = MF::k32(kf[mt][pp], Sf[pp], Y[mt]);
       f32x4 R[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) R[mt][i] = be[mt][i] * f(vv[mt][i]) - aa[mt][i] * Y[mt][i];
+      for (int mt = 0; mt < 4; ++mt) R[mt] = be[mt] * vv[mt] - aa[mt] * Y[mt];
       // Vn = (I + A)^-1 R by 16-row blocks
       const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
       f32x4 W[4];
@@ -325,10 +320,11 @@ __global__ __launch_bounds__(kThreads) void chunk_rule_v2_kernel(ChunkArgs p) {
         for (int j = 0; j < i; ++j) x = MF::k16(af[off_idx(i, j)], MF::as_f4(cvt4<T>(W[j])), x);
         W[i] = MF::k16(tf[i], MF::as_f4(cvt4<T>(x)), zero4);
       }
-      f8 Bw[2], Wf[2];
+      f8 Bw[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        Wf[q] = cat8<T>(cvt4<T>(W[2 * q]), cvt4<T>(W[2 * q + 1]));
+        const f8 wf = cat8<T>(cvt4<T>(W[2 * q]), cvt4<T>(W[2 * q + 1]));
+        *reinterpret_cast<f8 *>(&sm.wfrag[s2][lane * 16 + 8 * q]) = wf;
         Bw[q] = cat8<T>(cvt4<T>(cw[2 * q] * W[2 * q]), cvt4<T>(cw[2 * q + 1] * W[2 * q + 1]));
       }
 #pragma unroll
@@ -338,8 +334,11 @@ __global__ __launch_bounds__(kThreads) void chunk_rule_v2_kernel(ChunkArgs p) {
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) S[mt] = MF::k32(kt8[mt][q], Bw[q], S[mt]);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) *reinterpret_cast<f8 *>(&sm.wfrag[k2][lane * 16 + 8 * q]) = Wf[q];
-    });
+      for (int pp = 0; pp < KT; ++pp) {
+        Sf[pp] = cat8<T>(cvt4<T>(S[2 * pp]), cvt4<T>(S[2 * pp + 1]));
+        *reinterpret_cast<f8 *>(&sm.sfrag[s2 ^ 1][lane * SF + 8 * pp]) = Sf[pp];
+      }
+    }
     if (p.final_state) {
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
@@ -347,54 +346,21 @@ __global__ __launch_bounds__(kThreads) void chunk_rule_v2_kernel(ChunkArgs p) {
         for (int i = 0; i < 4; ++i) p.final_state[st_base + (int64_t)c * DK + 16 * mt + 4 * g + i] = S[mt][i];
     }
   } else if (wave == 1) {
-    // --------------------------------------------------------- prep(s + 2): k
-    Frags kbuf[2];
-    float gbuf[2], bbuf[2];
-    auto load_k = [&](int ch, int slot) {
-      const int nr = rows_of(ch);
-      const int64_t t0 = (int64_t)ch * BT;
-      load_rows<T, KT>(kbuf[slot], kb + t0 * p.sk_t, p.sk_t, nr, g, c);
-      const int lr = lane < nr ? lane : nr - 1;
-      gbuf[slot] = gb[(t0 + lr) * p.sg_t];  // rows >= nr are zeroed at use
-      bbuf[slot] = bb[(t0 + lr) * p.sbt_t];
-    };
-    if (Nc > 0) load_k(0, 0);
-    run_steps([&](int s, int par) {
+    // ----------------------------------------------------------- prep(s + 1)
+    for (int s = -3; s <= Nc; ++s) {
       lds_barrier();
-      const int ch = s + 2;
-      if (ch >= Nc) return;
-      if (ch + 1 < Nc) load_k(ch + 1, par ^ 1);
-      issue_fence();
-      Frags &cur = kbuf[par];
-      const bool live = lane < rows_of(ch);
-      const float bv = live ? bbuf[par] : 0.f;
-      const int k3 = ch % 3, k4 = ch & 3;
-      float ss[4], rk[4];
-      row_sumsq<T, KT>(cur, ss);
+      const int ch = s + 1;
+      if (ch < 0 || ch >= Nc) continue;
+      const int c2 = ch & 1;
+      const unsigned char *kt = sm.k[ch & 3];
+      float *fa = &sm.fac[ch & 3][0][0];
+      f8 kf[4][KT];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) rk[mt] = p.use_l2 ? rsqrtf(ss[mt] + p.l2_eps) : 1.f;
-      float gam = live ? gbuf[par] : 0.f;
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(gam, off, 64);
-        if (lane >= off) gam += o;
-      }
-      const float gC = __shfl(gam, 63, 64);
-      const float rko = pick4(rk, g);  // row `lane`
-      // factors of the rows this lane's accumulators hold (16 mi + 4 g + i)
-      // and of its columns (16 ni + c)
-      float gR[4][4], bR[4][4], kR[4][4], gCol[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mi + 4 * g + i;
-          gR[mi][i] = __shfl(gam, r, 64);
-          bR[mi][i] = __shfl(bv, r, 64);
-          kR[mi][i] = __shfl(rk[mi], 4 * g + i, 64);
-        }
-        gCol[mi] = __shfl(gam, 16 * mi + c, 64);
-      }
+        for (int pp = 0; pp < KT; ++pp)
+          kf[mt][pp] = frag_at<T>(kt + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+      // K K^T, lower tiles
       f32x4 acc[10];
 #pragma unroll
       for (int t = 0; t < 10; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -404,211 +370,262 @@ __global__ __launch_bounds__(kThreads) void chunk_rule_v2_kernel(ChunkArgs p) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-          for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(cur[mi][pp], cur[ni][pp], acc[t]);
+          for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(kf[mi][pp], kf[ni][pp], acc[t]);
       }
-      float *fa = &sm.fac[k4][0][0];
-      fa[F_GAM * BT + lane] = gam;
-      fa[F_BETA * BT + lane] = bv;
-      fa[F_RK * BT + lane] = rko;
-      fa[F_A * BT + lane] = bv * fast_exp(gam) * rko;
-      fa[F_CW * BT + lane] = fast_exp(gC - gam) * rko;
-      if (lane == 0) fa[F_MISC * BT] = fast_exp(gC);
-      T *kt = sm.k[k3];
+      // 1/|k| from the diagonal of K K^T: lane (g, c) with c >> 2 == g holds
+      // |k_{16 mi + c}|^2 in element c & 3 of diagonal tile mi.
+      if ((c >> 2) == g) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int pp = 0; pp < KT; ++pp)
-          *reinterpret_cast<f8 *>(&kt[(16 * mt + c) * LDK + 32 * pp + 8 * g]) = cur[mt][pp];
-      int t = 0;
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni <= mi; ++ni, ++t) {
-          const int col = 16 * ni + c;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mi + 4 * g + i;
-            const float av =
-                col < r ? bR[mi][i] * fast_exp(fminf(gR[mi][i] - gCol[ni], 0.f)) * kR[mi][i] * rk[ni] * acc[t][i]
-                        : 0.f;
-            if (mi == ni) sm.ad[k3][mi][(4 * g + i) * 16 + c] = av;
-            else sm.ao[k3][off_idx(mi, ni)][(4 * g + i) * 16 + c] = to<T>(-av);
-          }
+        for (int mi = 0; mi < 4; ++mi) {
+          const f32x4 d = acc[mi * (mi + 1) / 2 + mi];
+          const int e = c & 3;
+          const float sq = e == 0 ? d[0] : e == 1 ? d[1] : e == 2 ? d[2] : d[3];
+          fa[F_RK * BT + 16 * mi + c] = p.use_l2 ? rsqrtf(sq + p.l2_eps) : 1.f;
         }
-    });
-  } else if (wave == 2) {
-    // ------------------------------------------------------ prep(s + 1): q, v
-    Frags qbuf[2];
-    uint2 vbuf[2][4];
-    auto load_q = [&](int ch, int slot) {
-      const int nr = rows_of(ch);
-      const int64_t t0 = (int64_t)ch * BT;
-      load_rows<T, KT>(qbuf[slot], qb + t0 * p.sq_t, p.sq_t, nr, g, c);
-      const int lr = lane < nr ? lane : nr - 1;
-      const T *vr = vb + (t0 + lr) * p.sv_t;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vbuf[slot][i] = *reinterpret_cast<const uint2 *>(vr + 4 * i);
-    };
-    run_steps([&](int s, int par) {
-      lds_barrier();
-      const int ch = s + 1;
-      if (ch >= Nc) return;
-      if (ch + 1 < Nc) load_q(ch + 1, par ^ 1);
-      issue_fence();
-      if (ch < 0) return;
-      Frags &cur = qbuf[par];
-      const int k3 = ch % 3, k2 = ch & 1, k4 = ch & 3;
-      float *fa = &sm.fac[k4][0][0];
-      const T *kt = sm.k[k3];
-      // LDS operands first: k fragments, gamma and 1/|k| of rows and columns
-      Frags kf;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int pp = 0; pp < KT; ++pp)
-          kf[mt][pp] = *reinterpret_cast<const f8 *>(&kt[(16 * mt + c) * LDK + 32 * pp + 8 * g]);
-      f32x4 gR[4];
+      }
+      lds_fence_wave();
+      f32x4 gR[4], bR[4], kR[4];
       float gCol[4], kCol[4];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         gR[mi] = *reinterpret_cast<const f32x4 *>(&fa[F_GAM * BT + 16 * mi + 4 * g]);
+        bR[mi] = *reinterpret_cast<const f32x4 *>(&fa[F_BETA * BT + 16 * mi + 4 * g]);
+        kR[mi] = *reinterpret_cast<const f32x4 *>(&fa[F_RK * BT + 16 * mi + 4 * g]);
         gCol[mi] = fa[F_GAM * BT + 16 * mi + c];
         kCol[mi] = fa[F_RK * BT + 16 * mi + c];
       }
-      const float gOwn = fa[F_GAM * BT + lane];
-      float ss[4], rq[4];
-      row_sumsq<T, KT>(cur, ss);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) rq[mt] = p.use_l2 ? rsqrtf(ss[mt] + p.l2_eps) : 1.f;
-      float qR[4][4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qR[mi][i] = __shfl(rq[mi], 4 * g + i, 64);
-      f32x4 acc[10];
-#pragma unroll
-      for (int t = 0; t < 10; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int pp = 0; pp < KT; ++pp) {
-        int t = 0;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(cur[mi][pp], kf[ni][pp], acc[t]);
-      }
-      // writes: v slice (transposed), factors, P
-      {
-        T vv[16];
-        __builtin_memcpy(vv, vbuf[par], sizeof vv);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sm.vt[k2][j * LDV + lane] = vv[j];
-      }
-      const float rqo = pick4(rq, g);
-      fa[F_RQ * BT + lane] = rqo;
-      fa[F_BQ * BT + lane] = p.scale * fast_exp(gOwn) * rqo;
-      T *pm = sm.p[k3];
+      T *ao = sm.ao[c2][0];
       int t = 0;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < 4; ++mi) {
+        const f32x4 rowf = bR[mi] * kR[mi];
 #pragma unroll
         for (int ni = 0; ni <= mi; ++ni, ++t) {
           const int col = 16 * ni + c;
-          const int pc = pcol(col);
+          f32x4 av;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 16 * mi + 4 * g + i;
-            const float pv =
-                col <= r ? p.scale * fast_exp(fminf(gR[mi][i] - gCol[ni], 0.f)) * qR[mi][i] * kCol[ni] * acc[t][i]
-                         : 0.f;
-            pm[r * LDP + pc] = to<T>(pv);
+            const float e = fast_exp(gR[mi][i] - gCol[ni]);
+            av[i] = col < r ? rowf[i] * kCol[ni] * e * acc[t][i] : 0.f;
+          }
+          if (mi == ni) {
+            *reinterpret_cast<f32x4 *>(&sm.adt[mi][c * 16 + 4 * g]) = av;  // column-major
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ao[off_idx(mi, ni) * 256 + (4 * g + i) * 16 + c] = to<T>(-av[i]);
           }
         }
-      // upper tiles read by the 32-wide k steps: (0, 1) and (2, 3)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pm[(4 * g + i) * LDP + pcol(16 + c)] = to<T>(0.f);
-        pm[(32 + 4 * g + i) * LDP + pcol(48 + c)] = to<T>(0.f);
       }
-    });
-  } else {
-    // -------------------------------------------- inv(s + 1), out(s - 1)
-    Frags qbuf[2];
-    run_steps([&](int s, int par) {
-      lds_barrier();
-      if (s >= 0 && s < Nc)
-        load_rows<T, KT>(qbuf[par ^ 1], qb + (int64_t)s * BT * p.sq_t, p.sq_t, rows_of(s), g, c);
-      issue_fence();
-      const int ci = s + 1;
-      if (ci >= 0 && ci < Nc) {
-        // forward substitution, lane = (block g, column c); rows read as
-        // float4 vectors, four rows at a time
-        const float *ad = sm.ad[ci % 3][g];
+      // (I + A_bb)^-1, lane = (block g, column c): right-looking substitution
+      lds_fence_wave();
+      {
+        const float *adb = sm.adt[g];
         float x[16];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          f32x4 arow[4][4];
+        for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
+        for (int i = 0; i < 15; ++i) {
+          f32x4 col4[4];
 #pragma unroll
-            for (int v = 0; v <= rb; ++v)
-              arow[rr][v] = *reinterpret_cast<const f32x4 *>(&ad[(4 * rb + rr) * 16 + 4 * v]);
+          for (int v = (i + 1) >> 2; v < 4; ++v) col4[v] = *reinterpret_cast<const f32x4 *>(&adb[i * 16 + 4 * v]);
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int r = 4 * rb + rr;
-            float acc = r == c ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 0; i < r; ++i) acc -= arow[rr][i >> 2][i & 3] * x[i];
-            x[r] = acc;
-          }
+          for (int r = i + 1; r < 16; ++r) x[r] -= col4[r >> 2][r & 3] * x[i];
         }
-        T *ti = sm.tii[ci & 1][g];
+        T *ti = sm.tii[c2][g];
 #pragma unroll
         for (int r = 0; r < 16; ++r) ti[r * 16 + c] = to<T>(x[r]);
       }
+    }
+  } else if (wave == 2) {
+    // --------------------------------------------------- loads and factors
+    for (int s = -3; s <= Nc; ++s) {
+      lds_barrier();
+      // factors of chunk s + 3 first: its g and beta come through ordinary
+      // loads, whose wait also retires the tile copies issued one step ago
+      const int cf = s + 3;
+      if (cf < Nc) {
+        const bool live = lane < rows_of(cf);
+        const int64_t t = (int64_t)cf * BT + (live ? lane : 0);
+        float gam = gb[t * p.sg_t];
+        float bv = bb[t * p.sbt_t];
+        gam = live ? gam : 0.f;
+        bv = live ? bv : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float o = __shfl_up(gam, off, 64);
+          if (lane >= off) gam += o;
+        }
+        const float gC = __shfl(gam, 63, 64);
+        float *fa = &sm.fac[cf & 3][0][0];
+        fa[F_GAM * BT + lane] = gam;
+        fa[F_BETA * BT + lane] = bv;
+        fa[F_EG * BT + lane] = fast_exp(gam);
+        fa[F_ECG * BT + lane] = fast_exp(gC - gam);
+        if (lane == 0) fa[F_MISC * BT] = fast_exp(gC);
+      }
+      // tile copies of the previous step must have landed before the next
+      // barrier publishes them
+      wait_vm<0>();
+      const int ck = s + 3;  // k
+      if (ck < Nc) {
+        const int nr = rows_of(ck);
+        const int64_t t0 = (int64_t)ck * BT;
+        unsigned char *base = sm.k[ck & 3];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int b = 1024 * i + 16 * lane;
+          const int r = b / RB, jp = (b % RB) >> 4;
+          const int j = jp ^ (r & (CPR - 1));
+          const int rr = r < nr ? r : nr - 1;
+          g2l16(kb + (t0 + rr) * p.sk_t + 8 * j, base + 1024 * i);
+        }
+      }
+      const int cq = s + 2;  // q, v
+      if (cq >= 0 && cq < Nc) {
+        const int nr = rows_of(cq);
+        const int64_t t0 = (int64_t)cq * BT;
+        const int sl = cq % 3;
+        unsigned char *base = sm.q[sl];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int b = 1024 * i + 16 * lane;
+          const int r = b / RB, jp = (b % RB) >> 4;
+          const int j = jp ^ (r & (CPR - 1));
+          const int rr = r < nr ? r : nr - 1;
+          g2l16(qb + (t0 + rr) * p.sq_t + 8 * j, base + 1024 * i);
+        }
+        unsigned char *vbase = reinterpret_cast<unsigned char *>(sm.v[sl]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = 32 * i + (lane >> 1);
+          const int rr = r < nr ? r : nr - 1;
+          g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane & 1), vbase + 1024 * i);
+        }
+      }
+    }
+    wait_vm<0>();
+  } else {
+    // ------------------------------------------------- out(s), o(s - 1)
+    f32x4 Zc[4];
+    f8 Pf[6];
+    for (int s = -3; s <= Nc; ++s) {
+      lds_barrier();
       const int co = s - 1;
-      if (co < 0 || co >= Nc) return;
-      Frags &cur = qbuf[par];  // q rows of chunk co, loaded one step ago
-      const int k3 = co % 3, k2 = co & 1, k4 = co & 3;
-      const int nr = rows_of(co);
-      const float *fa = &sm.fac[k4][0][0];
-      const T *pm = sm.p[k3];
-      f8 Sf[KT], Wf[2], pf[6];
-      f32x4 bq[4];
+      if (co >= 0 && co < Nc) {
+        const int nr = rows_of(co);
+        f8 Wf[2];
 #pragma unroll
-      for (int pp = 0; pp < KT; ++pp) Sf[pp] = *reinterpret_cast<const f8 *>(&sm.sfrag[k2][lane * SF + 8 * pp]);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) Wf[q] = *reinterpret_cast<const f8 *>(&sm.wfrag[k2][lane * 16 + 8 * q]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) bq[mt] = *reinterpret_cast<const f32x4 *>(&fa[F_BQ * BT + 16 * mt + 4 * g]);
-      {
+        for (int q = 0; q < 2; ++q) Wf[q] = *reinterpret_cast<const f8 *>(&sm.wfrag[co & 1][lane * 16 + 8 * q]);
+        T *orow = ob + (int64_t)co * BT * p.so_t;
         int t = 0;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 o = Zc[mt];
 #pragma unroll
-          for (int q = 0; q <= mt / 2; ++q, ++t)
-            pf[t] = *reinterpret_cast<const f8 *>(&pm[(16 * mt + c) * LDP + 32 * q + 8 * g]);
+          for (int q = 0; q <= mt / 2; ++q, ++t) o = MF::k32(Pf[t], Wf[q], o);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mt + 4 * g + i;
+            if (r < nr) orow[(int64_t)r * p.so_t + c] = to<T>(o[i]);
+          }
+        }
       }
+      if (s < 0 || s >= Nc) continue;
+      const unsigned char *qt = sm.q[s % 3];
+      const unsigned char *kt = sm.k[s & 3];
+      const float *fa = &sm.fac[s & 3][0][0];
+      f8 qf[4][KT], kf[4][KT], Sf[KT];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int pp = 0; pp < KT; ++pp) {
+          qf[mt][pp] = frag_at<T>(qt + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+          kf[mt][pp] = frag_at<T>(kt + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+        }
+#pragma unroll
+      for (int pp = 0; pp < KT; ++pp) Sf[pp] = *reinterpret_cast<const f8 *>(&sm.sfrag[s & 1][lane * SF + 8 * pp]);
+      f32x4 gRow[4], egRow[4], kK[4];
+      float gC4[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        gRow[m] = *reinterpret_cast<const f32x4 *>(&fa[F_GAM * BT + 16 * m + 4 * g]);
+        egRow[m] = *reinterpret_cast<const f32x4 *>(&fa[F_EG * BT + 16 * m + 4 * g]);
+        kK[m] = *reinterpret_cast<const f32x4 *>(&fa[F_RK * BT + 16 * m + 4 * g]);
+        gC4[m] = fa[F_GAM * BT + 16 * m + c];
+      }
+      // 1/|q| of rows 16 mt + c
+      float rq[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        float ssq = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < KT; ++pp) ssq = sumsq8<T>(qf[mt][pp], ssq);
+        ssq += __shfl_xor(ssq, 16, 64);
+        ssq += __shfl_xor(ssq, 32, 64);
+        rq[mt] = p.use_l2 ? rsqrtf(ssq + p.l2_eps) : 1.f;
+      }
+      // Z = Q S^T, scaled by scale exp(gamma_r) rq_r (rows 16 mt + 4 g + i)
       f32x4 z[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) z[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int pp = 0; pp < KT; ++pp)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) z[mt] = MF::k32(cur[mt][pp], Sf[pp], z[mt]);
-      T *orow = ob + (int64_t)co * BT * p.so_t;
-      int t = 0;
+        for (int mt = 0; mt < 4; ++mt) z[mt] = MF::k32(qf[mt][pp], Sf[pp], z[mt]);
+      // P^T tiles (ni <= mi): lane holds q_{16 mi + c} . k_{16 ni + 4 g + i}
+      f32x4 pt[10];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 o = bq[mt] * z[mt];
+      for (int t = 0; t < 10; ++t) pt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q <= mt / 2; ++q, ++t) o = MF::k32(pf[t], Wf[q], o);
+      for (int pp = 0; pp < KT; ++pp) {
+        int t = 0;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni <= mi; ++ni, ++t) pt[t] = MF::k32(kf[ni][pp], qf[mi][pp], pt[t]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * g + i;
-          if (r < nr) orow[(int64_t)r * p.so_t + c] = to<T>(o[i]);
+          const float rqr = __shfl(rq[mt], 4 * g + i, 64);
+          Zc[mt][i] = p.scale * egRow[mt][i] * rqr * z[mt][i];
+        }
+      // P[r, i] = scale exp(gamma_r - gamma_i) rq_r rk_i (q_r . k_i), i <= r,
+      // r = 16 mi + c, i = 16 ni + 4 g + j; packed as A fragments of P Vn.
+      f32x4 pv[10];
+      {
+        int t = 0;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const float rowf = p.scale * rq[mi];
+#pragma unroll
+          for (int ni = 0; ni <= mi; ++ni, ++t) {
+            const int r = 16 * mi + c;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = 16 * ni + 4 * g + j;
+              const float e = fast_exp(gC4[mi] - gRow[ni][j]);
+              pv[t][j] = i <= r ? rowf * kK[ni][j] * e * pt[t][j] : 0.f;
+            }
+          }
         }
       }
-    });
+      auto tix = [](int mi, int ni) { return mi * (mi + 1) / 2 + ni; };
+      const v4 z4 = cvt4<T>(f32x4{0.f, 0.f, 0.f, 0.f});
+      {
+        int t = 0;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int q = 0; q <= mt / 2; ++q, ++t) {
+            const v4 lo = cvt4<T>(pv[tix(mt, 2 * q)]);
+            const v4 hi = (2 * q + 1 <= mt) ? cvt4<T>(pv[tix(mt, 2 * q + 1)]) : z4;
+            Pf[t] = cat8<T>(lo, hi);
+          }
+      }
+    }
   }
 }
 

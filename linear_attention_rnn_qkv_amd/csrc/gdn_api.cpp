@@ -360,6 +360,7 @@ gdn_status plan_chunk(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor
   p.so_b = out_o->stride[0]; p.so_t = out_o->stride[1]; p.so_h = out_o->stride[2];
   p.B = B; p.T = T; p.Hqk = Hqk; p.dk = dk; p.Hv = Hv; p.dv = dv;
   p.act = act; p.use_l2 = use_l2 ? 1 : 0; p.l2_eps = l2_eps; p.scale = scale;
+  p.rows16 = row_align(v, 3) >= 16 ? 1 : 0;
   return GDN_OK;
 }
 

@@ -46,6 +46,7 @@ struct ChunkArgs {
   int64_t B, T, Hqk, dk, Hv, dv;
   int32_t act;
   int32_t use_l2;
+  int32_t rows16;  // q, k and v rows are all 16-byte aligned
   float l2_eps, scale;
 };
 
