@@ -87,6 +87,80 @@ __device__ __forceinline__ void store_vec(T *__restrict__ p, const float (&v)[N]
   }
 }
 
+// Streaming (non-temporal) variants for data touched exactly once: the
+// accesses bypass the cache retention that would otherwise evict useful lines
+// (measured: a 16 B/lane copy streams ~10% faster this way on gfx950).
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+
+// Raw copy of N elements to registers; 16-byte non-temporal loads when the
+// size and alignment allow, else the widest plain access `align` allows.
+template <typename T, int N>
+__device__ __forceinline__ void load_raw_nt(const T *__restrict__ p, int align, T (&out)[N]) {
+  constexpr int BYTES = N * (int)sizeof(T);
+  const char *src = reinterpret_cast<const char *>(p);
+  char *dst = reinterpret_cast<char *>(out);
+  if constexpr (BYTES % 16 == 0) {
+    if (align >= 16) {
+#pragma unroll
+      for (int c = 0; c < BYTES / 16; ++c) {
+        const u32x4_nt u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(src + 16 * c));
+        __builtin_memcpy(dst + 16 * c, &u, 16);
+      }
+      return;
+    }
+  }
+  if constexpr (BYTES % 8 == 0) {
+    if (align >= 8) {
+#pragma unroll
+      for (int c = 0; c < BYTES / 8; ++c) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(src + 8 * c);
+        __builtin_memcpy(dst + 8 * c, &u, 8);
+      }
+      return;
+    }
+  }
+  if constexpr (BYTES % 4 == 0) {
+    if (align >= 4) {
+#pragma unroll
+      for (int c = 0; c < BYTES / 4; ++c) {
+        const uint32_t u = *reinterpret_cast<const uint32_t *>(src + 4 * c);
+        __builtin_memcpy(dst + 4 * c, &u, 4);
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = p[i];
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void load_vec_nt(const T *__restrict__ p, int align, float (&out)[N]) {
+  T tmp[N];
+  load_raw_nt<T, N>(p, align, tmp);
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = f(tmp[i]);
+}
+
+// Store N floats as T at p (aligned to min(16, N * sizeof(T)) bytes);
+// non-temporal when the size is a multiple of 16 bytes.
+template <typename T, int N>
+__device__ __forceinline__ void store_vec_nt(T *__restrict__ p, const float (&v)[N]) {
+  constexpr int BYTES = N * (int)sizeof(T);
+  if constexpr (BYTES % 16 == 0) {
+    T tmp[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) tmp[i] = to<T>(v[i]);
+#pragma unroll
+    for (int c = 0; c < BYTES / 16; ++c) {
+      u32x4_nt u;
+      __builtin_memcpy(&u, reinterpret_cast<const char *>(tmp) + 16 * c, 16);
+      __builtin_nontemporal_store(u, reinterpret_cast<u32x4_nt *>(p) + c);
+    }
+  } else {
+    store_vec<T, N>(p, v);
+  }
+}
+
 // Round a float through T and back (the materialisation of a T value).
 template <typename T> __device__ __forceinline__ float round_through(float x) {
   return f(to<T>(x));
@@ -94,9 +168,10 @@ template <typename T> __device__ __forceinline__ float round_through(float x) {
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
-// x * sigmoid(x); for very negative x, exp(-x) overflows to inf and the
-// quotient is -0, the correctly signed limit.
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// x * sigmoid(x) as x * rcp(1 + exp(-x)) (hardware reciprocal, ~1 ulp,
+// instead of a full IEEE division); for very negative x, exp(-x) overflows to
+// inf, the reciprocal is 0 and the result is -0, the correctly signed limit.
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Sum over aligned groups of W lanes (W a power of two <= 64).
 template <int W> __device__ __forceinline__ float group_sum(float v) {

@@ -16,8 +16,9 @@
 //
 // Memory-bound: each row is read once (o, gate) and written once (out). A row
 // is handled by dv/8 lanes holding 8 elements each; the sum of squares is a
-// butterfly reduction inside that lane group. Each lane handles ROWS rows so
-// that several independent 16-byte loads are in flight per lane.
+// butterfly reduction inside that lane group. Each lane handles two rows so
+// that four independent 16-byte loads are in flight per lane; o, gate and out
+// are streamed with non-temporal accesses (each byte is touched once).
 #include "device_common.h"
 #include "gdn_internal.h"
 
@@ -48,9 +49,9 @@ __global__ __launch_bounds__(kThreads) void gated_norm_kernel(NormArgs p) {
     rows[u] = row;
     if (row < nrows) {
       const int64_t h = row % p.H, bt = row / p.H, t = bt % p.T, b = bt / p.T;
-      load_vec<T, E>(static_cast<const T *>(p.o) + b * p.so_b + t * p.so_t + h * p.so_h + c0,
+      load_vec_nt<T, E>(static_cast<const T *>(p.o) + b * p.so_b + t * p.so_t + h * p.so_h + c0,
                      p.o_align, ov[u]);
-      load_vec<TG, E>(static_cast<const TG *>(p.gate) + b * p.sg_b + t * p.sg_t + h * p.sg_h + c0,
+      load_vec_nt<TG, E>(static_cast<const TG *>(p.gate) + b * p.sg_b + t * p.sg_t + h * p.sg_h + c0,
                       p.gate_align, gv[u]);
     } else {
 #pragma unroll
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void gated_norm_kernel(NormArgs p) {
       const float y = round_through<T>(ov[u][i] * r * w[i]);
       res[i] = y * silu(gv[u][i]);
     }
-    if (rows[u] < nrows) store_vec<T, E>(static_cast<T *>(p.out) + rows[u] * DV + c0, res);
+    if (rows[u] < nrows) store_vec_nt<T, E>(static_cast<T *>(p.out) + rows[u] * DV + c0, res);
   }
 }
 

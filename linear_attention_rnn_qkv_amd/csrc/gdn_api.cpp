@@ -251,7 +251,7 @@ gdn_status plan_prologue(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn
     return fail(GDN_ERR_NOT_SUPPORTED,
                 "caller-side L2 norm needs rows aligned to at least %lld bytes", (long long)(dims->dk / 64 * es));
 
-  if (B > 65535 || (C + 255) / 256 + 1 > 65535 || (T + 63) / 64 > 0x7fffffff)
+  if (B > 65535 || (C + 255) / 256 + 1 > 65535 || (T + 127) / 128 > 0x7fffffff)
     return fail(GDN_ERR_NOT_SUPPORTED, "prologue: grid too large (B=%lld, T=%lld, C=%lld)", (long long)B,
                 (long long)T, (long long)C);
 
@@ -262,6 +262,7 @@ gdn_status plan_prologue(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn
   p.sxk_b = x_k->stride[0]; p.sxk_t = x_k->stride[1];
   p.sxv_b = x_v->stride[0]; p.sxv_t = x_v->stride[1];
   p.conv_w = conv_w->data; p.w_dtype = conv_w->dtype;
+  p.w_align = gdn::align_of_host((uint64_t)(uintptr_t)conv_w->data);
   p.conv_b = conv_b ? conv_b->data : nullptr; p.b_dtype = conv_b ? conv_b->dtype : act;
   p.a = a->data; p.b = b->data;
   p.sa_b = a->stride[0]; p.sa_t = a->stride[1]; p.sa_h = a->stride[2];

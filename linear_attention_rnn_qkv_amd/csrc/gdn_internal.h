@@ -16,6 +16,7 @@ struct PrologueArgs {
   const void *conv_w;  // [C, 4] contiguous
   const void *conv_b;  // [C] or null
   int32_t w_dtype, b_dtype;
+  int32_t w_align;     // bytes conv_w's base address is aligned to (<= 16)
   const void *a, *b;   // [B, T, Hv]
   int64_t sa_b, sa_t, sa_h, sb_b, sb_t, sb_h;
   const float *A_log, *dt_bias;

@@ -14,12 +14,17 @@
 // (Gated DeltaNet's parameterisation; the pages do not print them).
 //
 // Layout and schedule (HBM-bound): a thread owns VEC consecutive channels and
-// walks a tile of 64 tokens, keeping the three previous inputs in registers,
-// so each input element is read once (plus a 3-token halo per tile) and each
-// output written once with VEC-wide coalesced accesses. History is zero
+// walks a tile of 128 tokens in batches of 8, double-buffered so the next
+// batch's loads (raw packed vectors) are in flight during the arithmetic of
+// the current one, convolving each batch over a register window that holds
+// the three
+// previous inputs in registers, so each input element is read once (plus a
+// 3-token halo per tile) and each output written once with VEC-wide
+// coalesced accesses. History is zero
 // before every sequence start: batch rows are sequences; with cu_seqlens the
-// thread finds the boundaries inside its tile from the offsets. One extra
-// block column per token tile computes beta and g for all value heads.
+// thread finds the boundaries inside its tile from the offsets. The blocks
+// of the first channel column also compute beta and g for all value heads of
+// their tile.
 #include <limits.h>
 
 #include "device_common.h"
@@ -29,8 +34,8 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 64;   // tokens per block
-constexpr int kUnroll = 4;  // tokens loaded ahead per step
+constexpr int kTile = 128;  // tokens per block
+constexpr int kUnroll = 8;   // tokens per load batch
 
 template <typename TW>
 __device__ __forceinline__ float ld_param(const void *p, int64_t i) {
@@ -41,6 +46,15 @@ __device__ __forceinline__ float ld_any(const void *p, int32_t dt, int64_t i) {
   if (dt == kF32) return ld_param<float>(p, i);
   if (dt == kBF16) return ld_param<bf16>(p, i);
   return ld_param<f16>(p, i);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// silu(y) from y2 = y * log2(e): y * sigmoid(y) = y2 / (log2(e) * (1 + 2^-y2)).
+// (Convolving with weights pre-scaled by log2(e) saves the scaling of the
+// exponent's argument.) For y2 -> -inf the reciprocal is 0 and the result -0.
+__device__ __forceinline__ float silu_log2(float y2) {
+  return y2 * __builtin_amdgcn_rcpf(__builtin_fmaf(kLog2e, __builtin_amdgcn_exp2f(-y2), kLog2e));
 }
 
 template <typename T>
@@ -62,38 +76,53 @@ __device__ void beta_g_tile(const PrologueArgs &p, int64_t b, int64_t t0, int64_
 
 template <typename T, int VEC>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs p) {
+  // Consecutive blocks cover consecutive token tiles of one channel block.
+  const int cb = (int)blockIdx.y;
   const int64_t b = blockIdx.z;
   const int64_t t0 = (int64_t)blockIdx.x * kTile;
   const int64_t t1 = t0 + kTile < p.T ? t0 + kTile : p.T;
-  if ((int)blockIdx.y == (int)gridDim.y - 1) {
-    beta_g_tile<T>(p, b, t0, t1);
-    return;
-  }
-  const int64_t c0 = ((int64_t)blockIdx.y * kThreads + threadIdx.x) * VEC;
+  const int64_t c0 = ((int64_t)cb * kThreads + threadIdx.x) * VEC;
   const bool active = c0 < p.C;
   const int64_t nq = p.Hqk * p.dk;
 
-  // Source view for this thread's channels.
+  // Source view for this thread's channels (lanes past C read the last
+  // channels and store nothing, so every lane issues the same loads).
+  const int64_t cl = active ? c0 : p.C - VEC;
   const T *src;
   int64_t st;
-  if (c0 < nq) {
-    src = static_cast<const T *>(p.xq) + b * p.sxq_b + c0;
+  if (cl < nq) {
+    src = static_cast<const T *>(p.xq) + b * p.sxq_b + cl;
     st = p.sxq_t;
-  } else if (c0 < 2 * nq) {
-    src = static_cast<const T *>(p.xk) + b * p.sxk_b + (c0 - nq);
+  } else if (cl < 2 * nq) {
+    src = static_cast<const T *>(p.xk) + b * p.sxk_b + (cl - nq);
     st = p.sxk_t;
   } else {
-    src = static_cast<const T *>(p.xv) + b * p.sxv_b + (c0 - 2 * nq);
+    src = static_cast<const T *>(p.xv) + b * p.sxv_b + (cl - 2 * nq);
     st = p.sxv_t;
   }
   constexpr int AL = VEC * (int)sizeof(T);
 
+  // The thread's taps are 4*VEC consecutive weights: vector loads.
   float w[VEC][4], bias[VEC];
+  {
+    float wf[4 * VEC];
+    if (!active) {
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) {
+      for (int i = 0; i < 4 * VEC; ++i) wf[i] = 0.f;
+    } else if (p.w_dtype == kF32) {
+      load_vec<float, 4 * VEC>(static_cast<const float *>(p.conv_w) + c0 * 4, align_of(16 * VEC) < p.w_align
+                               ? align_of(16 * VEC) : p.w_align, wf);
+    } else {
+      load_vec<T, 4 * VEC>(static_cast<const T *>(p.conv_w) + c0 * 4,
+                           align_of(8 * VEC) < p.w_align ? align_of(8 * VEC) : p.w_align, wf);
+    }
+    // taps and bias pre-scaled by log2(e): the convolution yields y * log2(e)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[i][j] = active ? ld_any(p.conv_w, p.w_dtype, (c0 + i) * 4 + j) : 0.f;
-    bias[i] = (active && p.conv_b) ? ld_any(p.conv_b, p.b_dtype, c0 + i) : 0.f;
+    for (int i = 0; i < VEC; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[i][j] = wf[4 * i + j] * kLog2e;
+      bias[i] = (active && p.conv_b) ? ld_any(p.conv_b, p.b_dtype, c0 + i) * kLog2e : 0.f;
+    }
   }
 
   // Sequence containing t0, and the next boundary after it.
@@ -110,27 +139,70 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs p) {
     next = idx <= p.n_seqs ? cu[idx] : LLONG_MAX;
   }
 
-  float h1[VEC], h2[VEC], h3[VEC];  // inputs at t-1, t-2, t-3
+  // Inputs at t0-1, t0-2, t0-3 (zero before the sequence start). The loads
+  // are unconditional (clamped rows) so they overlap the first batch's.
+  float h1[VEC], h2[VEC], h3[VEC];
+  {
+    const int64_t r1 = t0 - 1 >= 0 ? t0 - 1 : 0, r2 = t0 - 2 >= 0 ? t0 - 2 : 0, r3 = t0 - 3 >= 0 ? t0 - 3 : 0;
+    load_vec<T, VEC>(src + r1 * st, AL, h1);
+    load_vec<T, VEC>(src + r2 * st, AL, h2);
+    load_vec<T, VEC>(src + r3 * st, AL, h3);
+    const bool v1 = t0 - 1 >= bos, v2 = t0 - 2 >= bos, v3 = t0 - 3 >= bos;
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) h1[i] = h2[i] = h3[i] = 0.f;
-  if (active && t0 - 1 >= bos) load_vec<T, VEC>(src + (t0 - 1) * st, AL, h1);
-  if (active && t0 - 2 >= bos) load_vec<T, VEC>(src + (t0 - 2) * st, AL, h2);
-  if (active && t0 - 3 >= bos) load_vec<T, VEC>(src + (t0 - 3) * st, AL, h3);
+    for (int i = 0; i < VEC; ++i) {
+      h1[i] = v1 ? h1[i] : 0.f;
+      h2[i] = v2 ? h2[i] : 0.f;
+      h3[i] = v3 ? h3[i] : 0.f;
+    }
+  }
 
   const bool l2 = p.caller_l2norm && c0 < 2 * nq;
   const int group = (int)(p.dk / VEC);  // lanes per q/k head
   T *dst = static_cast<T *>(p.qkv) + b * p.T * p.C + c0;
 
-  for (int64_t tb = t0; tb < t1; tb += kUnroll) {
-    float xs[kUnroll][VEC];
+  // Batches of kUnroll tokens. Loads are unconditional (rows past the tile
+  // end read the tile's last row, results unused) so the compiler can count
+  // the outstanding loads exactly.
+  auto load_batch = [&](int64_t tb, T (&raw)[kUnroll][VEC]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if (active && tb + u < t1) {
-        load_vec<T, VEC>(src + (tb + u) * st, AL, xs[u]);
-      } else {
+      const int64_t t = tb + u < t1 ? tb + u : t1 - 1;
+      load_raw_nt<T, VEC>(src + t * st, AL, raw[u]);
+    }
+  };
+  auto emit = [&](int64_t t, float (&z)[VEC]) {
+    if (p.caller_l2norm) {  // block-uniform: every lane joins the shuffles
+      float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) xs[u][i] = 0.f;
+      for (int i = 0; i < VEC; ++i) ss += z[i] * z[i];
+      for (int off = group >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      if (l2) {
+        const float r = rsqrtf(ss + p.l2_eps);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) z[i] *= r;
       }
+    }
+    if (active && t < t1) store_vec_nt<T, VEC>(dst + t * p.C, z);
+  };
+  auto compute_batch = [&](int64_t tb, const T (&raw)[kUnroll][VEC]) {
+    if (next >= tb + kUnroll) {
+      // No sequence starts inside the batch: a rolling 4-input window per
+      // channel over the fully unrolled batch (registers are renamed, not
+      // moved).
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float z[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float x = f(raw[u][i]);
+          z[i] = silu_log2(bias[i] + w[i][0] * h3[i] + w[i][1] * h2[i] + w[i][2] * h1[i] + w[i][3] * x);
+          h3[i] = h2[i];
+          h2[i] = h1[i];
+          h1[i] = x;
+        }
+        emit(tb + u, z);
+      }
+      return;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -143,30 +215,44 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs p) {
         next = idx <= p.n_seqs ? cu[idx] : LLONG_MAX;
       }
       float z[VEC];
-      float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
-        const float y = bias[i] + w[i][0] * h3[i] + w[i][1] * h2[i] + w[i][2] * h1[i] + w[i][3] * xs[u][i];
-        z[i] = silu(y);
-        ss += z[i] * z[i];
+        const float x = f(raw[u][i]);
+        z[i] = silu_log2(bias[i] + w[i][0] * h3[i] + w[i][1] * h2[i] + w[i][2] * h1[i] + w[i][3] * x);
       }
-      if (p.caller_l2norm) {  // block-uniform: every lane joins the shuffles
-        for (int off = group >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-        if (l2) {
-          const float r = rsqrtf(ss + p.l2_eps);
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) z[i] *= r;
-        }
-      }
-      if (active) store_vec<T, VEC>(dst + t * p.C, z);
+      emit(t, z);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         h3[i] = h2[i];
         h2[i] = h1[i];
-        h1[i] = xs[u][i];
+        h1[i] = f(raw[u][i]);
       }
     }
+  };
+  T ra[kUnroll][VEC], rb[kUnroll][VEC];
+  if (t1 - t0 == kTile) {
+    // Full tile: double-buffered with a fixed trip count, the loads of batch
+    // i + 1 in flight during the arithmetic of batch i.
+    constexpr int kPairs = kTile / (2 * kUnroll);
+    load_batch(t0, ra);
+    int64_t tb = t0;
+    for (int i = 0; i < kPairs - 1; ++i, tb += 2 * kUnroll) {
+      load_batch(tb + kUnroll, rb);
+      compute_batch(tb, ra);
+      load_batch(tb + 2 * kUnroll, ra);
+      compute_batch(tb + kUnroll, rb);
+    }
+    load_batch(tb + kUnroll, rb);
+    compute_batch(tb, ra);
+    compute_batch(tb + kUnroll, rb);
+  } else {
+    for (int64_t tb = t0; tb < t1; tb += kUnroll) {
+      load_batch(tb, ra);
+      compute_batch(tb, ra);
+    }
   }
+  // beta and g of the tile's tokens, by the first channel block
+  if (cb == 0) beta_g_tile<T>(p, b, t0, t1);
 }
 
 template <typename T, int VEC>
@@ -174,7 +260,7 @@ hipError_t launch_vec(const PrologueArgs &a, hipStream_t s) {
   const int64_t per_block = (int64_t)kThreads * VEC;
   const int64_t cblocks = (a.C + per_block - 1) / per_block;
   const int64_t tblocks = (a.T + kTile - 1) / kTile;
-  dim3 grid((unsigned)tblocks, (unsigned)(cblocks + 1), (unsigned)a.B);
+  dim3 grid((unsigned)tblocks, (unsigned)cblocks, (unsigned)a.B);
   hipLaunchKernelGGL((prologue_kernel<T, VEC>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
