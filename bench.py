@@ -83,6 +83,45 @@ def cpu_baseline(cfg: int, s, budget_s: float) -> dict:
             "cpu": cpu}
 
 
+COPY_BYTES = 1 << 30
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    workload, if it was taken on the kernel's current sources; else None."""
+    from linear_attention_rnn_qkv_amd import profile_summary as ps
+
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic.{workload}.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if kernel not in ps.KERNELS or rec.get("source_hash") != ps.source_hash(kernel):
+        return None
+    return rec["bytes"]
+
+
+def calibrate_copy(reps: int) -> int:
+    """A plain device copy of COPY_BYTES, `reps` times: its byte counters per
+    dispatch (which must read COPY_BYTES fetched and written) calibrate the
+    HBM traffic counters of the kernels."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"calibration": "device copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "ms": ms, "GB/s": 2 * COPY_BYTES / (ms * 1e-3) / 1e9}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +130,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the layer core "
@@ -106,6 +147,8 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        return calibrate_copy(args.steps)
     s = synth.spec(args.config)
     print(f"[bench] workload {args.config} {s.name}: generating inputs", file=sys.stderr, flush=True)
     x = synth.make_inputs(s)
@@ -190,10 +233,12 @@ def main() -> int:
     def gbs(b, t_ms):
         return b / (t_ms * 1e-3) / 1e9
 
+    chunk_kernel = ("chunk_rule_v2_kernel" if s.act in ("bf16", "f16") and s.dk in (64, 128)
+                    else "chunk_rule_kernel")
     stages = {
         "prologue": {"kernel": "prologue_kernel", "ms": t_pro, "bytes": pb, "GB/s": gbs(pb, t_pro),
                      "hbm_frac": gbs(pb, t_pro) / HBM_PEAK_GBS},
-        "chunk_rule": {"kernel": "chunk_rule_kernel", "ms": t_chk, "bytes": cb, "flops": cf,
+        "chunk_rule": {"kernel": chunk_kernel, "ms": t_chk, "bytes": cb, "flops": cf,
                        "GB/s": gbs(cb, t_chk), "hbm_frac": gbs(cb, t_chk) / HBM_PEAK_GBS,
                        "TFLOP/s": cf / (t_chk * 1e-3) / 1e12,
                        "mfma_frac": cf / (t_chk * 1e-3) / 1e12 / mfma_peak},
@@ -210,7 +255,9 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": st["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": st["hbm_frac"]}
     roof["kernel"] = st["kernel"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(s.name, st["kernel"])
+    for v in stages.values():
+        v["traffic"] = measured_traffic(s.name, v["kernel"])
 
     result = {
         "metric": METRIC,

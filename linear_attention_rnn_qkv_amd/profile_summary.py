@@ -1,0 +1,150 @@
+"""Summaries of rocprofv3 runs of bench.py, and the source fingerprints that
+tie measured HBM traffic to the kernel code it was measured on.
+
+Usage (after the rocprofv3 runs listed in the summaries it writes):
+
+    python -m linear_attention_rnn_qkv_amd.profile_summary \\
+        --workload long-bf16-T131072 --trace DIR_kt --fetch DIR_f --write DIR_w \\
+        --copy-fetch DIR_cf --copy-write DIR_cw --out profiles/
+
+DIR_* are rocprofv3 ``-d`` output directories (CSV format). The copy runs are
+``bench.py --calibrate-copy``: a plain device copy of exactly 1 GiB read and
+1 GiB written per dispatch, whose FETCH_SIZE / WRITE_SIZE readings give the
+factor from counter KiB to bytes.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+COPY_BYTES = 1 << 30
+
+# kernel symbol fragment -> (short name, sources its machine code is built from)
+KERNELS = {
+    "chunk_rule_v2_kernel": ("chunk_rule_v2_kernel", ["chunk_rule_v2.hip", "device_common.h", "gdn_internal.h"]),
+    "chunk_rule_kernel": ("chunk_rule_kernel", ["chunk_rule.hip", "device_common.h", "gdn_internal.h"]),
+    "prologue_kernel": ("prologue_kernel", ["prologue.hip", "device_common.h", "gdn_internal.h"]),
+    "gated_norm_kernel": ("gated_norm_kernel", ["gated_norm.hip", "device_common.h", "gdn_internal.h"]),
+}
+
+
+def short_name(symbol: str) -> str | None:
+    for frag, (name, _) in KERNELS.items():
+        if frag + "I" in symbol or symbol.endswith(frag):
+            return name
+    return None
+
+
+def source_hash(kernel: str) -> str:
+    """SHA-256 (first 16 hex digits) of the sources a kernel is built from."""
+    h = hashlib.sha256()
+    for f in KERNELS[kernel][1]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _csv(d: str, suffix: str) -> list[dict]:
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def kernel_stats(d: str) -> dict:
+    out = {}
+    for r in _csv(d, "_kernel_stats.csv"):
+        n = short_name(r["Name"])
+        if n:
+            out[n] = {"symbol": r["Name"], "calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                      "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+    return out
+
+
+def counter_per_dispatch(d: str, counter: str) -> dict:
+    """Mean counter value (KiB) per dispatch, per kernel (short name or symbol)."""
+    acc: dict[str, list[float]] = {}
+    for r in _csv(d, "_counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        n = short_name(r["Kernel_Name"]) or r["Kernel_Name"]
+        acc.setdefault(n, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--copy-fetch", required=True)
+    ap.add_argument("--copy-write", required=True)
+    ap.add_argument("--algorithmic", default="{}",
+                    help='JSON {kernel: algorithmic bytes per launch} for the comparison column')
+    ap.add_argument("--commands", default="", help="text block with the exact commands that were run")
+    ap.add_argument("--out", default="profiles")
+    a = ap.parse_args()
+
+    stats = kernel_stats(a.trace)
+    fetch = counter_per_dispatch(a.fetch, "FETCH_SIZE")
+    write = counter_per_dispatch(a.write, "WRITE_SIZE")
+    cf = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE")
+    cw = counter_per_dispatch(a.copy_write, "WRITE_SIZE")
+    copy_key = [k for k in cf if "copyBuffer" in k or "copy" in k.lower()]
+    if not copy_key:
+        raise SystemExit("no copy kernel in the calibration runs")
+    kf = COPY_BYTES / (cf[copy_key[0]] * 1024.0)  # bytes per counted byte, fetch
+    kw = COPY_BYTES / (cw[copy_key[0]] * 1024.0)
+    algo = json.loads(a.algorithmic)
+
+    traffic = {"workload": a.workload, "fetch_factor": kf, "write_factor": kw,
+               "copy_counters_kib": {"FETCH_SIZE": cf[copy_key[0]], "WRITE_SIZE": cw[copy_key[0]]},
+               "kernels": {}}
+    for k in sorted(set(fetch) & set(write)):
+        if k not in KERNELS:
+            continue
+        rb, wb = fetch[k] * 1024.0 * kf, write[k] * 1024.0 * kw
+        traffic["kernels"][k] = {"source_hash": source_hash(k), "read_bytes": rb, "write_bytes": wb,
+                                 "bytes": rb + wb, "FETCH_SIZE_kib": fetch[k], "WRITE_SIZE_kib": write[k]}
+    os.makedirs(a.out, exist_ok=True)
+    with open(os.path.join(a.out, f"hbm_traffic.{a.workload}.json"), "w") as fh:
+        json.dump(traffic, fh, indent=1)
+
+    lines = [f"# Kernel durations and HBM traffic, workload {a.workload}", ""]
+    if a.commands:
+        lines += ["Commands (run from the repository root on one MI355X):", "", "```", a.commands.strip(), "```", ""]
+    lines += ["## rocprofv3 --kernel-trace --stats", "",
+              "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
+    for k, v in sorted(stats.items(), key=lambda kv: -kv[1]["avg_us"]):
+        lines.append(f"| {k} | {v['calls']} | {v['avg_us']:.1f} | {v['min_us']:.1f} | {v['max_us']:.1f} |")
+    lines += ["", "## HBM bytes per launch (rocprofv3 --pmc, one counter per run)", "",
+              f"Calibration: a 1 GiB device copy reads FETCH_SIZE = {cf[copy_key[0]]:.0f} KiB and "
+              f"WRITE_SIZE = {cw[copy_key[0]]:.0f} KiB per dispatch, so bytes = FETCH_SIZE x 1024 x "
+              f"{kf:.4f} and WRITE_SIZE x 1024 x {kw:.4f}.", "",
+              "| kernel | source hash | read GB | write GB | total GB | algorithmic GB | ratio |",
+              "|---|---|---|---|---|---|---|"]
+    for k, v in traffic["kernels"].items():
+        al = algo.get(k)
+        ratio = f"{v['bytes'] / al:.3f}" if al else "-"
+        alt = f"{al / 1e9:.3f}" if al else "-"
+        lines.append(f"| {k} | {v['source_hash']} | {v['read_bytes'] / 1e9:.3f} | {v['write_bytes'] / 1e9:.3f} | "
+                     f"{v['bytes'] / 1e9:.3f} | {alt} | {ratio} |")
+    with open(os.path.join(a.out, f"layer_core_kernels.{a.workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())
