@@ -87,19 +87,24 @@ COPY_BYTES = 1 << 30
 
 
 def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of this
-    workload, if it was taken on the kernel's current sources; else None."""
+    """HBM bytes per launch (summed over the '+'-joined kernels of a stage) from
+    the committed rocprofv3 counter summary of this workload, if it was taken
+    on the kernels' current sources; else None."""
     from linear_attention_rnn_qkv_amd import profile_summary as ps
 
     path = os.path.join(ROOT, "profiles", f"hbm_traffic.{workload}.json")
     try:
         with open(path) as fh:
-            rec = json.load(fh)["kernels"][kernel]
+            recs = json.load(fh)["kernels"]
     except (OSError, KeyError, ValueError):
         return None
-    if kernel not in ps.KERNELS or rec.get("source_hash") != ps.source_hash(kernel):
-        return None
-    return rec["bytes"]
+    total = 0.0
+    for k in kernel.split("+"):
+        rec = recs.get(k)
+        if rec is None or k not in ps.KERNELS or rec.get("source_hash") != ps.source_hash(k):
+            return None
+        total += rec["bytes"]
+    return total
 
 
 def calibrate_copy(reps: int) -> int:
@@ -164,7 +169,10 @@ def main() -> int:
     dims = (s.Hqk, s.dk, s.Hv, s.dv)
     scale = s.dk ** -0.5
     dt = synth.TORCH_DTYPE[s.act]
-    ws = torch.empty(gdn.gdn_layer_workspace_bytes(s.B, s.T, dims, dt), dtype=torch.uint8, device="cuda")
+    n_seqs = 0 if d["cu_seqlens"] is None else d["cu_seqlens"].shape[0] - 1
+    ws = torch.empty(gdn.gdn_layer_workspace_bytes(s.B, s.T, dims, dt, n_seqs), dtype=torch.uint8, device="cuda")
+    cws_bytes = gdn.gdn_chunk_rule_workspace_bytes(s.B, s.T, dims, dt, n_seqs)
+    cws = torch.empty(cws_bytes, dtype=torch.uint8, device="cuda") if cws_bytes else None
     out = torch.empty((s.B, s.T, s.Hv, s.dv), dtype=dt, device="cuda")
     # stage buffers for the per-stage timing loop (same kernels, same shapes)
     qkv = torch.empty((s.B, s.T, s.C), dtype=dt, device="cuda")
@@ -186,7 +194,7 @@ def main() -> int:
                              d["dt_bias"], d["cu_seqlens"], dims, out_qkv=qkv, out_g=g, out_beta=beta)
 
     def chunk():
-        gdn.gdn_chunk_rule_fwd(qv, kv, vv, g, beta, scale, True, 1e-6, d["cu_seqlens"], out_o=o)
+        gdn.gdn_chunk_rule_fwd(qv, kv, vv, g, beta, scale, True, 1e-6, d["cu_seqlens"], out_o=o, workspace=cws)
 
     def norm():
         gdn.gdn_gated_norm_fwd(o, d["gate"], d["norm_w"], 1e-5, out=out)
@@ -233,8 +241,9 @@ def main() -> int:
     def gbs(b, t_ms):
         return b / (t_ms * 1e-3) / 1e9
 
-    chunk_kernel = ("chunk_rule_v2_kernel" if s.act in ("bf16", "f16") and s.dk in (64, 128)
-                    else "chunk_rule_kernel")
+    # the chunk stage: chunk prep + chunk state (two launches) where a workspace
+    # applies, else the single recurrence kernel
+    chunk_kernel = ("chunk_prep_kernel+chunk_state_kernel" if cws is not None else "chunk_rule_kernel")
     stages = {
         "prologue": {"kernel": "prologue_kernel", "ms": t_pro, "bytes": pb, "GB/s": gbs(pb, t_pro),
                      "hbm_frac": gbs(pb, t_pro) / HBM_PEAK_GBS},

@@ -163,6 +163,17 @@ gdn_status gdn_prologue_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
  *   out_o      [B, T, Hv, dv] act dtype, any strides, inner 1
  *   final_state   [N, Hv, dv, dk] F32 contiguous, or NULL; may alias
  *              initial_state (each state is read before it is written)
+ *   workspace  device memory of gdn_chunk_rule_workspace_bytes(...) bytes,
+ *              256-byte aligned, or NULL. With a workspace, BF16/FP16 inputs
+ *              with dk 64 or 128 and 16-byte aligned rows run as two kernels:
+ *              a chunk prep that is parallel over (chunk, value head) and
+ *              writes T = (I + A)^-1, P and row factors of every chunk to the
+ *              workspace, then the serial state pass. Without one (or where
+ *              that path does not apply) a single kernel does both. The
+ *              results agree to rounding. A workspace smaller than required
+ *              is an error; the memory must not overlap any tensor argument
+ *              and must not be used by any other call until this call's work
+ *              on `stream` is done.
  * N = B without cu_seqlens.
  */
 gdn_status gdn_chunk_rule_fwd(const gdn_tensor *q, const gdn_tensor *k,
@@ -172,7 +183,16 @@ gdn_status gdn_chunk_rule_fwd(const gdn_tensor *q, const gdn_tensor *k,
                               const gdn_tensor *cu_seqlens,
                               const gdn_tensor *initial_state,
                               const gdn_tensor *out_o,
-                              const gdn_tensor *final_state, void *stream);
+                              const gdn_tensor *final_state, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Bytes of chunk workspace for B*T tokens (n_seqs = number of packed
+ * sequences with cu_seqlens, 0 without): 4*(N+1) rounded to 256, plus
+ * (ceil(T/64) + n_seqs, or B*ceil(T/64)) * Hv records of 14336 bytes.
+ * Returns 0 where the two-kernel path does not apply (F32 inputs, dk 256)
+ * and for invalid arguments. */
+size_t gdn_chunk_rule_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs,
+                                      const gdn_dims *dims, int32_t act_dtype);
 
 /*
  * gdn_gated_norm_fwd - [P2] option table (output RMSNorm and SiLU gating),
@@ -195,9 +215,11 @@ gdn_status gdn_gated_norm_fwd(const gdn_tensor *o, const gdn_tensor *gate,
 
 /* Bytes of workspace gdn_layer_fwd needs for B*T tokens (a multiple of 256):
  * qkv [B,T,C] act dtype, g and beta [B,T,Hv] F32, o [B,T,Hv,dv] act dtype,
- * each 256-byte aligned. Returns 0 for invalid arguments. */
-size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, const gdn_dims *dims,
-                                 int32_t act_dtype);
+ * each 256-byte aligned, then the chunk workspace
+ * (gdn_chunk_rule_workspace_bytes). n_seqs: number of packed sequences when
+ * cu_seqlens is given, else 0. Returns 0 for invalid arguments. */
+size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs,
+                                 const gdn_dims *dims, int32_t act_dtype);
 
 /*
  * gdn_layer_fwd - the layer core ([P2] Execution: the pre-recurrence stage,

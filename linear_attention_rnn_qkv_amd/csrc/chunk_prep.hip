@@ -1,0 +1,380 @@
+// Chunk prep: the state-independent half of the chunked gated delta rule,
+// fully parallel over (chunk, value head). For a chunk of 64 rows, with
+// gamma = cumsum(g) inside the chunk and rk, rq the inverse L2 norms of the
+// k and q rows (folded into the kernel as in the Megatron-LM pull request
+// "fold q/k L2-norm into the gated_delta_rule kernel", section What):
+//
+//   A[r,i] = beta_r exp(gamma_r - gamma_i) rk_r rk_i (k_r . k_i),   i < r
+//   T      = (I + A)^-1                        (unit lower triangular)
+//   P[r,i] = scale exp(gamma_r - gamma_i) rq_r rk_i (q_r . k_i),    i <= r
+//   aa = beta e^gamma rk,  cw = e^(gamma_C - gamma) rk,  zc = scale e^gamma rq
+//
+// which the chunk-state kernel consumes as
+//   Vn = T (beta (.) V) - T (aa (.) (K S0^T)),   O = zc (.) (Q S0^T) + P Vn,
+//   S  = e^gamma_C S0 + K^T (cw (.) Vn).
+// This is the WY/UT form of the delta rule (Yang et al., NeurIPS 2024) with
+// the gating of Gated DeltaNet (ICLR 2025); only non-positive exponents are
+// evaluated. T is computed in FP32: the four 16 x 16 diagonal blocks by
+// forward substitution, then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj block
+// column by block column. Results go to the caller's workspace in MFMA
+// operand order (layout in gdn_internal.h).
+//
+// One workgroup (four wavefronts) per (chunk, value head); q/k/v of the GQA
+// group are read in place. Packed sequences: a one-block kernel first turns
+// cu_seqlens into chunk offsets.
+#include "gdn_internal.h"
+#include "mfma_tiles.h"
+
+namespace gdn {
+namespace {
+
+constexpr int BT = 64;
+constexpr int kPrepThreads = 256;
+
+// cu_chunks[n] = sum over sequences m < n of ceil(len_m / 64).
+__global__ __launch_bounds__(256) void chunk_index_kernel(const int32_t *__restrict__ cu, int64_t n,
+                                                          int32_t *__restrict__ cuc) {
+  __shared__ int32_t part[256];
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 255) / 256;
+  const int64_t b = tid * per, e = b + per < n ? b + per : n;
+  int32_t sum = 0;
+  for (int64_t i = b; i < e; ++i) sum += (cu[i + 1] - cu[i] + BT - 1) / BT;
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t acc = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int32_t x = part[i];
+      part[i] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+  int32_t acc = part[tid];
+  for (int64_t i = b; i < e; ++i) {
+    cuc[i] = acc;
+    acc += (cu[i + 1] - cu[i] + BT - 1) / BT;
+  }
+  if (b < e && e == n) cuc[n] = acc;
+  if (n == 0 && tid == 0) cuc[0] = 0;
+}
+
+enum { P_GAM = 0, P_BT, P_EG, P_ECG, P_RK, P_RQ, P_N };
+
+template <int DK>
+struct PrepLds {
+  static constexpr int RB = DK * 2;    // bytes per q/k row (16-bit elements)
+  static constexpr int CPR = RB / 16;  // 16-byte chunks per row
+  static constexpr int TILE = BT * RB;
+  struct Mats {                        // lower 16 x 16 blocks, FP32, column-major
+    float a[10][256];                  //   a[blk][col * 16 + row] = A block
+    float t[10][256];                  //   same for T
+    float x[4][256];                   //   per-wave scratch
+  };
+  alignas(16) unsigned char k[TILE];
+  union alignas(16) {
+    unsigned char q[TILE];             // q rows, dead after the P^T product
+    Mats m;
+  } u;
+  alignas(16) float fac[P_N][BT];
+  float eC;
+};
+
+__device__ __forceinline__ int blk(int mi, int ni) { return mi * (mi + 1) / 2 + ni; }
+
+template <typename T, int DK>
+__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
+  using MF = M2<T>;
+  using f8 = typename MF::f8;
+  using v4 = typename MF::v4;
+  using SM = PrepLds<DK>;
+  constexpr int KT = DK / 32;
+  constexpr int RB = SM::RB, CPR = SM::CPR;
+  __shared__ SM sm;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t gc = blockIdx.x;
+  const int64_t h = blockIdx.y;
+  const int64_t hk = h / (p.Hv / p.Hqk);
+  int64_t ch, bos, L, brow;
+  if (p.cu_seqlens) {
+    const int32_t *cuc = p.cu_chunks;
+    if (gc >= cuc[p.n_seqs]) return;  // whole block: past the last chunk
+    int64_t lo = 0, hi = p.n_seqs;    // cuc[lo] <= gc < cuc[hi]
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (cuc[mid] <= gc) lo = mid; else hi = mid;
+    }
+    ch = gc - cuc[lo];
+    bos = p.cu_seqlens[lo];
+    L = p.cu_seqlens[lo + 1] - bos;
+    brow = 0;
+  } else {
+    const int64_t nc = (p.T + BT - 1) / BT;
+    brow = gc / nc;
+    ch = gc % nc;
+    bos = 0;
+    L = p.T;
+  }
+  const int64_t t0 = bos + ch * BT;
+  const int nr = (int)(L - ch * BT < BT ? L - ch * BT : BT);
+  const T *qb = static_cast<const T *>(p.q) + brow * p.sq_b + hk * p.sq_h + t0 * p.sq_t;
+  const T *kb = static_cast<const T *>(p.k) + brow * p.sk_b + hk * p.sk_h + t0 * p.sk_t;
+  unsigned char *rec = p.ws_rec + (gc * p.Hv + h) * kRecBytes;
+
+  // 1. k and q tiles, rows past the chunk repeat its last row (their beta
+  //    and g are zero, which makes them inert).
+  for (int i = threadIdx.x; i < BT * CPR; i += kPrepThreads) {
+    const int r = i / CPR, jp = i % CPR;
+    const int j = jp ^ (r & (CPR - 1));
+    const int rr = r < nr ? r : nr - 1;
+    *reinterpret_cast<uint4 *>(sm.k + r * RB + jp * 16) =
+        *reinterpret_cast<const uint4 *>(kb + (int64_t)rr * p.sk_t + 8 * j);
+    *reinterpret_cast<uint4 *>(sm.u.q + r * RB + jp * 16) =
+        *reinterpret_cast<const uint4 *>(qb + (int64_t)rr * p.sq_t + 8 * j);
+  }
+  __syncthreads();
+
+  int fo[KT][2];
+#pragma unroll
+  for (int pp = 0; pp < KT; ++pp)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      fo[pp][hh] = c * RB + (((4 * pp + (g >> 1) + 2 * hh) ^ (c & (CPR - 1))) << 4) + 8 * (g & 1);
+
+  // 2. K K^T (wave 0), P^T = K Q^T (wave 1), gamma and decay factors (wave 2)
+  f32x4 acc[10];
+#pragma unroll
+  for (int t = 0; t < 10; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (wave == 0) {
+    f8 kf[4][KT];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int pp = 0; pp < KT; ++pp) kf[mt][pp] = frag_at<T>(sm.k + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+#pragma unroll
+    for (int pp = 0; pp < KT; ++pp) {
+      int t = 0;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(kf[mi][pp], kf[ni][pp], acc[t]);
+    }
+    // 1/|k| from the diagonal: lane (g, c) with c / 4 == g holds |k_{16 mi + c}|^2
+    if ((c >> 2) == g) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const f32x4 d = acc[blk(mi, mi)];
+        const int e = c & 3;
+        const float sq = e == 0 ? d[0] : e == 1 ? d[1] : e == 2 ? d[2] : d[3];
+        sm.fac[P_RK][16 * mi + c] = p.use_l2 ? rsqrtf(sq + p.l2_eps) : 1.f;
+      }
+    }
+  } else if (wave == 1) {
+    f8 kf[4][KT], qf[4][KT];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int pp = 0; pp < KT; ++pp) {
+        kf[mt][pp] = frag_at<T>(sm.k + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+        qf[mt][pp] = frag_at<T>(sm.u.q + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+      }
+    // lane (g, c) of tile (mi, ni): q_{16 mi + c} . k_{16 ni + 4 g + j}
+#pragma unroll
+    for (int pp = 0; pp < KT; ++pp) {
+      int t = 0;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(kf[ni][pp], qf[mi][pp], acc[t]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      float ssq = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < KT; ++pp) ssq = sumsq8<T>(qf[mt][pp], ssq);
+      ssq += __shfl_xor(ssq, 16, 64);
+      ssq += __shfl_xor(ssq, 32, 64);
+      if (g == 0) sm.fac[P_RQ][16 * mt + c] = p.use_l2 ? rsqrtf(ssq + p.l2_eps) : 1.f;
+    }
+  } else if (wave == 2) {
+    const float *gp = p.g + brow * p.sg_b + h * p.sg_h + t0 * p.sg_t;
+    const float *bp = p.beta + brow * p.sbt_b + h * p.sbt_h + t0 * p.sbt_t;
+    const bool live = lane < nr;
+    float gam = live ? gp[(int64_t)lane * p.sg_t] : 0.f;
+    const float bv = live ? bp[(int64_t)lane * p.sbt_t] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(gam, off, 64);
+      if (lane >= off) gam += o;
+    }
+    const float gC = __shfl(gam, 63, 64);
+    sm.fac[P_GAM][lane] = gam;
+    sm.fac[P_BT][lane] = bv;
+    sm.fac[P_EG][lane] = fast_exp(gam);
+    sm.fac[P_ECG][lane] = fast_exp(gC - gam);
+    if (lane == 0) sm.eC = fast_exp(gC);
+  }
+  __syncthreads();  // the q tile is dead from here on (its space holds A, T)
+
+  // 3. A blocks (wave 0), P fragments (wave 1), row factors (wave 2)
+  if (wave == 0) {
+    int t = 0;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      f32x4 rowf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mi + 4 * g + i;
+        rowf[i] = sm.fac[P_BT][r] * sm.fac[P_RK][r];
+      }
+#pragma unroll
+      for (int ni = 0; ni <= mi; ++ni, ++t) {
+        const int col = 16 * ni + c;
+        const float kc = sm.fac[P_RK][col], gcol = sm.fac[P_GAM][col];
+        f32x4 av;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mi + 4 * g + i;
+          const float e = fast_exp(sm.fac[P_GAM][r] - gcol);
+          av[i] = col < r ? rowf[i] * kc * e * acc[t][i] : 0.f;
+        }
+        *reinterpret_cast<f32x4 *>(&sm.u.m.a[t][c * 16 + 4 * g]) = av;  // column c, rows 4g..
+      }
+    }
+  } else if (wave == 1) {
+    f32x4 pv[10];
+    int t = 0;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = 16 * mi + c;
+      const float rowf = p.scale * sm.fac[P_RQ][r], gr = sm.fac[P_GAM][r];
+#pragma unroll
+      for (int ni = 0; ni <= mi; ++ni, ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * ni + 4 * g + j;
+          const float e = fast_exp(gr - sm.fac[P_GAM][i]);
+          pv[t][j] = i <= r ? rowf * sm.fac[P_RK][i] * e * acc[t][j] : 0.f;
+        }
+      }
+    }
+    const v4 z4 = cvt4<T>(f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+      const int mt = f < 4 ? f : f - 2, q = f < 4 ? 0 : 1;
+      const v4 lo = cvt4<T>(pv[blk(mt, 2 * q)]);
+      const v4 hi = (2 * q + 1 <= mt) ? cvt4<T>(pv[blk(mt, 2 * q + 1)]) : z4;
+      *reinterpret_cast<f8 *>(rec + kRecP + f * 1024 + lane * 16) = cat8<T>(lo, hi);
+    }
+  } else if (wave == 2) {
+    float *rf = reinterpret_cast<float *>(rec + kRecF);
+    const float bt = sm.fac[P_BT][lane], eg = sm.fac[P_EG][lane], rk = sm.fac[P_RK][lane];
+    rf[0 * BT + lane] = bt * eg * rk;                            // aa
+    rf[1 * BT + lane] = sm.fac[P_ECG][lane] * rk;                // cw
+    rf[2 * BT + lane] = p.scale * eg * sm.fac[P_RQ][lane];       // zc
+    rf[3 * BT + lane] = bt;                                      // beta
+    if (lane == 0) rf[4 * BT] = sm.eC;
+  }
+  __syncthreads();
+
+  // 4. T = (I + A)^-1. Diagonal blocks: wave j, lane c < 16 solves column c
+  //    of (I + A_jj) x = e_c by forward substitution in FP32.
+  {
+    const int j = wave;
+    const float *ab = sm.u.m.a[blk(j, j)];
+    if (lane < 16) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = r == lane ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < 15; ++i) {
+        f32x4 col4[4];
+#pragma unroll
+        for (int v = (i + 1) >> 2; v < 4; ++v) col4[v] = *reinterpret_cast<const f32x4 *>(&ab[i * 16 + 4 * v]);
+#pragma unroll
+        for (int r = i + 1; r < 16; ++r) x[r] -= col4[r >> 2][r & 3] * x[i];
+      }
+      float *tb = sm.u.m.t[blk(j, j)];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        *reinterpret_cast<f32x4 *>(&tb[lane * 16 + 4 * v]) = f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
+    }
+  }
+  __syncthreads();
+  //    Off-diagonal blocks: wave j owns block column j; lane (g, c) computes
+  //    rows 4g..4g+3 of column c of each 16 x 16 block.
+  {
+    const int j = wave;
+    float *xs = sm.u.m.x[j];
+    for (int i = j + 1; i < 4; ++i) {
+      // X = sum_{k=j}^{i-1} A_ik T_kj
+      f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+      for (int k = j; k < i; ++k) {
+        const float *ab = sm.u.m.a[blk(i, k)];
+        const float *tb = sm.u.m.t[blk(k, j)];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&ab[m * 16 + 4 * g]);  // A[4g..4g+3][m]
+          const float tm = tb[c * 16 + m];                                        // T[m][c]
+          xv += a4 * tm;
+        }
+      }
+      *reinterpret_cast<f32x4 *>(&xs[c * 16 + 4 * g]) = xv;
+      lds_fence_wave();
+      // T_ij = -T_ii X
+      const float *ti = sm.u.m.t[blk(i, i)];
+      f32x4 tv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&ti[m * 16 + 4 * g]);  // T_ii[4g..][m]
+        tv -= t4 * xs[c * 16 + m];
+      }
+      *reinterpret_cast<f32x4 *>(&sm.u.m.t[blk(i, j)][c * 16 + 4 * g]) = tv;
+      lds_fence_wave();
+    }
+  }
+  __syncthreads();
+
+  // 5. T fragments to the record: wave w writes fragments w and w + 4.
+  for (int f = wave; f < 6; f += 4) {
+    const int mt = f < 4 ? f : f - 2, q = f < 4 ? 0 : 1;
+    f32x4 lo, hi;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int nb = 2 * q + hh;  // block column
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (nb <= mt) {
+        const float *tb = sm.u.m.t[blk(mt, nb)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = tb[(4 * g + i) * 16 + c];  // T[row c][col 4g + i]
+      }
+      if (hh == 0) lo = v; else hi = v;
+    }
+    *reinterpret_cast<f8 *>(rec + kRecT + f * 1024 + lane * 16) = cat8<T>(cvt4<T>(lo), cvt4<T>(hi));
+  }
+}
+
+template <typename T, int DK>
+hipError_t launch_prep(const ChunkArgs &a, hipStream_t s) {
+  if (a.cu_seqlens) {
+    hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.n_seqs, a.cu_chunks);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((unsigned)a.chunk_bound, (unsigned)a.Hv);
+  hipLaunchKernelGGL((chunk_prep_kernel<T, DK>), grid, dim3(kPrepThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_prep(const ChunkArgs &a, hipStream_t s) {
+  if (a.act == kBF16) return a.dk == 64 ? launch_prep<bf16, 64>(a, s) : launch_prep<bf16, 128>(a, s);
+  if (a.act == kF16) return a.dk == 64 ? launch_prep<f16, 64>(a, s) : launch_prep<f16, 128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

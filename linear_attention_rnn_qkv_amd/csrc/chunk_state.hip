@@ -1,0 +1,340 @@
+// Chunk state: the state-dependent half of the chunked gated delta rule,
+// serial over the chunks of a sequence. With the per-chunk record written by
+// the chunk-prep kernel (T = (I + A)^-1, P and row factors aa, cw, zc, beta,
+// e^{gamma_C}; see chunk_prep.hip), a chunk of 64 rows entering with state S0
+// (dv x dk, FP32) gives
+//
+//   U  = T (beta (.) V),   X = K S0^T,   Vn = U - T (aa (.) X)
+//   O  = zc (.) (Q S0^T) + P Vn
+//   S  = e^{gamma_C} S0 + K^T (cw (.) Vn)
+//
+// (the WY/UT form of the gated delta rule; q and k are used raw, their
+// inverse norms are inside the factors).
+//
+// One workgroup = (sequence, value head, 16 rows of dv) with three
+// wavefronts and one barrier per step s:
+//   wave 0  chain(s): U, X, Vn, the state update; S lives in MFMA
+//           accumulators; Vn and the next S are handed over as fragments.
+//   wave 1  out(s):   Q S0^T for chunk s and, with Vn(s - 1), finishes and
+//                     stores o(s - 1).
+//   wave 2  loads:    streams the k, q, v tiles and the record of chunk s + 2
+//                     into three-slot LDS rings (global_load_lds); the copies
+//                     of a step are complete before the barrier that ends the
+//                     next step, so two steps of latency are hidden.
+#include "gdn_internal.h"
+#include "mfma_tiles.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kStateThreads = 192;
+constexpr int BT = 64;
+constexpr int DVT = 16;
+
+template <typename T, int DK>
+struct StateLds {
+  static constexpr int RB = DK * 2;
+  static constexpr int CPR = RB / 16;
+  static constexpr int TILE = BT * RB;
+  alignas(16) unsigned char k[3][TILE];      // k rows of chunk c in slot c % 3 (swizzled)
+  alignas(16) unsigned char q[3][TILE];      // q rows
+  alignas(16) T v[3][BT * DVT];              // v slice, row-major [64][16]
+  alignas(16) unsigned char rec[3][kRecBytes];
+  alignas(16) T sfrag[2][64 * (DK / 4)];     // state fragments per lane
+  alignas(16) T wfrag[2][64 * 16];           // Vn fragments per lane
+};
+
+// fragment index of (row tile mt, k pair q) in a record matrix
+__device__ __forceinline__ constexpr int frag_id(int mt, int q) { return q == 0 ? mt : 2 + mt; }
+
+template <typename T, int DK>
+__global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p) {
+  using MF = M2<T>;
+  using f8 = typename MF::f8;
+  using v4 = typename MF::v4;
+  using SM = StateLds<T, DK>;
+  constexpr int KT = DK / 32;
+  constexpr int NT = DK / 16;
+  constexpr int SF = DK / 4;
+  constexpr int RB = SM::RB, CPR = SM::CPR;
+  constexpr int NI = SM::TILE / 1024;          // 1 KB copies per q/k tile
+  constexpr int NR = (int)(kRecBytes / 1024);  // 1 KB copies per record
+  constexpr int NLOAD = 2 * NI + 2 + NR;       // copies per step
+  static_assert(NLOAD <= 63, "vmcnt range");
+  __shared__ SM sm;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  // The dv slices of one head (which read the same q/k tiles and records) are
+  // placed on one XCD so that they share its L2.
+  const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
+  const int64_t j0 = (lid % ntile) * DVT;
+  const int64_t h = (lid / ntile) % gridDim.y;
+  const int64_t n = lid / (ntile * gridDim.y);
+  const int64_t hk = h / (p.Hv / p.Hqk);
+  int64_t bos, eos, brow, cbase;
+  if (p.cu_seqlens) {
+    bos = p.cu_seqlens[n];
+    eos = p.cu_seqlens[n + 1];
+    brow = 0;
+    cbase = p.cu_chunks[n];
+  } else {
+    bos = 0;
+    eos = p.T;
+    brow = n;
+    cbase = n * ((p.T + BT - 1) / BT);
+  }
+  const int64_t L = eos - bos;
+  const int Nc = (int)((L + BT - 1) / BT);
+  const T *qb = static_cast<const T *>(p.q) + brow * p.sq_b + hk * p.sq_h + bos * p.sq_t;
+  const T *kb = static_cast<const T *>(p.k) + brow * p.sk_b + hk * p.sk_h + bos * p.sk_t;
+  const T *vb = static_cast<const T *>(p.v) + brow * p.sv_b + h * p.sv_h + j0 + bos * p.sv_t;
+  T *ob = static_cast<T *>(p.o) + brow * p.so_b + h * p.so_h + j0 + bos * p.so_t;
+  const unsigned char *recb = p.ws_rec + (cbase * p.Hv + h) * kRecBytes;
+  const int64_t rec_stride = p.Hv * kRecBytes;
+  const int64_t st_base = ((n * p.Hv + h) * p.dv + j0) * DK;
+  auto rows_of = [&](int ch) -> int {
+    const int64_t r = L - (int64_t)ch * BT;
+    return (int)(r < BT ? r : BT);
+  };
+  int fo[KT][2];
+#pragma unroll
+  for (int pp = 0; pp < KT; ++pp)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      fo[pp][hh] = c * RB + (((4 * pp + (g >> 1) + 2 * hh) ^ (c & (CPR - 1))) << 4) + 8 * (g & 1);
+
+  // Steps s = -2 .. Nc, one barrier each, in every wave.
+  if (wave == 0) {
+    // ---------------------------------------------------------------- chain
+    f32x4 S[NT];  // S[mt][i] = S[dv row c][dk 16 mt + 4 g + i]
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[mt][i] = p.init_state ? p.init_state[st_base + (int64_t)c * DK + 16 * mt + 4 * g + i] : 0.f;
+    f8 Sf[KT];
+#pragma unroll
+    for (int pp = 0; pp < KT; ++pp) {
+      Sf[pp] = cat8<T>(cvt4<T>(S[2 * pp]), cvt4<T>(S[2 * pp + 1]));
+      *reinterpret_cast<f8 *>(&sm.sfrag[0][lane * SF + 8 * pp]) = Sf[pp];
+    }
+    // transposing-read offsets (K^T fragments of the state update)
+    const int yrow = (4 * g + (c >> 2)) & (CPR - 1);
+    const int trb = (4 * g + (c >> 2)) * RB + 8 * (c & 1);
+    int trc[NT];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) trc[mt] = trb + (((2 * mt + ((c & 3) >> 1)) ^ yrow) << 4);
+    for (int s = -2; s <= Nc; ++s) {
+      lds_barrier();
+      if (s < 0 || s >= Nc) continue;
+      const int sl = s % 3;
+      const unsigned char *kt = sm.k[sl];
+      const unsigned char *rec = sm.rec[sl];
+      const float *fa = reinterpret_cast<const float *>(rec + kRecF);
+      const T *vt = sm.v[sl];
+      f8 Tf[6];
+#pragma unroll
+      for (int f = 0; f < 6; ++f) Tf[f] = *reinterpret_cast<const f8 *>(rec + kRecT + f * 1024 + lane * 16);
+      f8 kf[4][KT];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int pp = 0; pp < KT; ++pp) kf[mt][pp] = frag_at<T>(kt + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+      f32x4 aa[4], cw[4], bt[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int r0 = 16 * mt + 4 * g;
+        aa[mt] = *reinterpret_cast<const f32x4 *>(&fa[0 * BT + r0]);
+        cw[mt] = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + r0]);
+        bt[mt] = *reinterpret_cast<const f32x4 *>(&fa[3 * BT + r0]);
+      }
+      const float eC = fa[4 * BT];
+      // B operands of U = T (beta (.) V): rows 32 q + 16 hh + 4 g + i, column c
+      f8 Bv[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo[i] = f(vt[(32 * q + 4 * g + i) * DVT + c]);
+          hi[i] = f(vt[(32 * q + 16 + 4 * g + i) * DVT + c]);
+        }
+        Bv[q] = cat8<T>(cvt4<T>(bt[2 * q] * lo), cvt4<T>(bt[2 * q + 1] * hi));
+      }
+      f8 kt8[NT][2];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const unsigned char *a1 = kt + trc[mt] + (32 * q) * RB;
+          const unsigned char *a2 = kt + trc[mt] + (32 * q + 16) * RB;
+          const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(a1));
+          const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(a2));
+          kt8[mt][q] = cat8<T>(__builtin_bit_cast(v4, r1), __builtin_bit_cast(v4, r2));
+        }
+      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+      // X = K S0^T
+      f32x4 X[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) X[mt] = zero4;
+#pragma unroll
+      for (int pp = 0; pp < KT; ++pp)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) X[mt] = MF::k32(kf[mt][pp], Sf[pp], X[mt]);
+      // U = T (beta (.) V), independent of S
+      f32x4 U[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        U[mt] = MF::k32(Tf[frag_id(mt, 0)], Bv[0], zero4);
+        if (mt >= 2) U[mt] = MF::k32(Tf[frag_id(mt, 1)], Bv[1], U[mt]);
+      }
+      // Vn = U - T (aa (.) X)
+      f8 Rf[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) Rf[q] = cat8<T>(cvt4<T>(aa[2 * q] * X[2 * q]), cvt4<T>(aa[2 * q + 1] * X[2 * q + 1]));
+      f32x4 Vn[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 y = MF::k32(Tf[frag_id(mt, 0)], Rf[0], zero4);
+        if (mt >= 2) y = MF::k32(Tf[frag_id(mt, 1)], Rf[1], y);
+        Vn[mt] = U[mt] - y;
+      }
+      f8 Bw[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        *reinterpret_cast<f8 *>(&sm.wfrag[s & 1][lane * 16 + 8 * q]) =
+            cat8<T>(cvt4<T>(Vn[2 * q]), cvt4<T>(Vn[2 * q + 1]));
+        Bw[q] = cat8<T>(cvt4<T>(cw[2 * q] * Vn[2 * q]), cvt4<T>(cw[2 * q + 1] * Vn[2 * q + 1]));
+      }
+      // S = e^{gamma_C} S0 + K^T (cw (.) Vn)
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) S[mt] = S[mt] * eC;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) S[mt] = MF::k32(kt8[mt][q], Bw[q], S[mt]);
+#pragma unroll
+      for (int pp = 0; pp < KT; ++pp) {
+        Sf[pp] = cat8<T>(cvt4<T>(S[2 * pp]), cvt4<T>(S[2 * pp + 1]));
+        *reinterpret_cast<f8 *>(&sm.sfrag[(s & 1) ^ 1][lane * SF + 8 * pp]) = Sf[pp];
+      }
+    }
+    if (p.final_state) {
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p.final_state[st_base + (int64_t)c * DK + 16 * mt + 4 * g + i] = S[mt][i];
+    }
+  } else if (wave == 1) {
+    // ------------------------------------------------- out(s), o(s - 1)
+    f32x4 Zc[4];
+    f8 Pf[6];
+    for (int s = -2; s <= Nc; ++s) {
+      lds_barrier();
+      const int co = s - 1;
+      if (co >= 0 && co < Nc) {
+        const int nr = rows_of(co);
+        f8 Wf[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) Wf[q] = *reinterpret_cast<const f8 *>(&sm.wfrag[co & 1][lane * 16 + 8 * q]);
+        T *orow = ob + (int64_t)co * BT * p.so_t;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 o = MF::k32(Pf[frag_id(mt, 0)], Wf[0], Zc[mt]);
+          if (mt >= 2) o = MF::k32(Pf[frag_id(mt, 1)], Wf[1], o);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mt + 4 * g + i;
+            if (r < nr) orow[(int64_t)r * p.so_t + c] = to<T>(o[i]);
+          }
+        }
+      }
+      if (s < 0 || s >= Nc) continue;
+      const int sl = s % 3;
+      const unsigned char *qt = sm.q[sl];
+      const unsigned char *rec = sm.rec[sl];
+      const float *fa = reinterpret_cast<const float *>(rec + kRecF);
+      f8 qf[4][KT], Sf[KT];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int pp = 0; pp < KT; ++pp) qf[mt][pp] = frag_at<T>(qt + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+#pragma unroll
+      for (int pp = 0; pp < KT; ++pp) Sf[pp] = *reinterpret_cast<const f8 *>(&sm.sfrag[s & 1][lane * SF + 8 * pp]);
+#pragma unroll
+      for (int f = 0; f < 6; ++f) Pf[f] = *reinterpret_cast<const f8 *>(rec + kRecP + f * 1024 + lane * 16);
+      f32x4 z[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) z[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pp = 0; pp < KT; ++pp)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) z[mt] = MF::k32(qf[mt][pp], Sf[pp], z[mt]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) Zc[mt] = *reinterpret_cast<const f32x4 *>(&fa[2 * BT + 16 * mt + 4 * g]) * z[mt];
+    }
+  } else {
+    // ------------------------------------------------------------- loads
+    for (int s = -2; s <= Nc; ++s) {
+      lds_barrier();
+      const int cl = s + 2;
+      const bool issue = cl < Nc;
+      if (issue) {
+        const int nr = rows_of(cl);
+        const int64_t t0 = (int64_t)cl * BT;
+        const int sl = cl % 3;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int b = 1024 * i + 16 * lane;
+          const int r = b / RB, jp = (b % RB) >> 4;
+          const int j = jp ^ (r & (CPR - 1));
+          const int rr = r < nr ? r : nr - 1;
+          g2l16(kb + (t0 + rr) * p.sk_t + 8 * j, sm.k[sl] + 1024 * i);
+          g2l16(qb + (t0 + rr) * p.sq_t + 8 * j, sm.q[sl] + 1024 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = 32 * i + (lane >> 1);
+          const int rr = r < nr ? r : nr - 1;
+          g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane & 1), reinterpret_cast<unsigned char *>(sm.v[sl]) + 1024 * i);
+        }
+        const unsigned char *rg = recb + (int64_t)cl * rec_stride;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * i);
+      }
+      // The copies of the previous step must be complete before the next
+      // barrier publishes them; this step's stay in flight.
+      if (issue) wait_vm<NLOAD>(); else wait_vm<0>();
+    }
+  }
+}
+
+template <typename T, int DK>
+hipError_t launch_dk(const ChunkArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)(a.dv / DVT), (unsigned)a.Hv, (unsigned)a.n_seqs);
+  hipLaunchKernelGGL((chunk_state_kernel<T, DK>), grid, dim3(kStateThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_prep(const ChunkArgs &a, hipStream_t s);
+
+bool chunk_split_supported(int64_t dk, int32_t act) {
+  return (act == kBF16 || act == kF16) && (dk == 64 || dk == 128);
+}
+
+hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s) {
+  if (a.n_seqs == 0 || a.dv == 0) return hipSuccess;
+  if (!a.ws_rec || (a.cu_seqlens && !a.cu_chunks)) return hipErrorInvalidValue;
+  hipError_t e = launch_chunk_prep(a, s);
+  if (e != hipSuccess) return e;
+  if (a.act == kBF16) return a.dk == 64 ? launch_dk<bf16, 64>(a, s) : launch_dk<bf16, 128>(a, s);
+  if (a.act == kF16) return a.dk == 64 ? launch_dk<f16, 64>(a, s) : launch_dk<f16, 128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

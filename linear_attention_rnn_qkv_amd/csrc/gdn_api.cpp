@@ -408,6 +408,37 @@ gdn_status plan_norm(const gdn_tensor *o, const gdn_tensor *gate, const gdn_tens
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace of the two-kernel chunk path: chunk offsets of packed sequences,
+// then one record per (chunk, value head). 0 when that path does not apply.
+int64_t chunk_bound_of(int64_t B, int64_t T, int64_t n_seqs) {
+  const int64_t nc = (T + 63) / 64;
+  return n_seqs > 0 ? nc + n_seqs : B * nc;
+}
+size_t chunk_ws_bytes(int64_t B, int64_t T, int64_t n_seqs, int64_t dk, int64_t Hv, int64_t dv, int32_t act) {
+  if (!gdn::chunk_split_supported(dk, act) || dv % 16) return 0;
+  const int64_t N = n_seqs > 0 ? n_seqs : B;
+  return align256((size_t)(N + 1) * 4) + (size_t)chunk_bound_of(B, T, n_seqs) * (size_t)Hv * (size_t)gdn::kRecBytes;
+}
+
+// Attach a caller workspace to a planned chunk call (validated, no launch).
+gdn_status attach_chunk_ws(gdn::ChunkArgs *p, void *ws, size_t ws_bytes) {
+  p->ws_rec = nullptr;
+  p->cu_chunks = nullptr;
+  p->chunk_bound = 0;
+  if (!ws) return GDN_OK;
+  if (!gdn::chunk_split_supported(p->dk, p->act) || !p->rows16 || p->dv % 16) return GDN_OK;  // not used
+  const int64_t ns = p->cu_seqlens ? p->n_seqs : 0;
+  const size_t need = chunk_ws_bytes(p->B, p->T, ns, p->dk, p->Hv, p->dv, p->act);
+  if (ws_bytes < need)
+    return fail(GDN_ERR_INVALID_VALUE, "chunk workspace too small: %zu < %zu bytes", ws_bytes, need);
+  if ((uintptr_t)ws % 256) return fail(GDN_ERR_INVALID_VALUE, "chunk workspace must be 256-byte aligned");
+  char *w = static_cast<char *>(ws);
+  p->cu_chunks = reinterpret_cast<int32_t *>(w);
+  p->ws_rec = reinterpret_cast<unsigned char *>(w + align256((size_t)(p->n_seqs + 1) * 4));
+  p->chunk_bound = chunk_bound_of(p->B, p->T, ns);
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -433,12 +464,27 @@ gdn_status gdn_chunk_rule_fwd(const gdn_tensor *q, const gdn_tensor *k, const gd
                               const gdn_tensor *g, const gdn_tensor *beta, float scale,
                               int32_t use_qk_l2norm_in_kernel, float l2_eps, const gdn_tensor *cu_seqlens,
                               const gdn_tensor *initial_state, const gdn_tensor *out_o,
-                              const gdn_tensor *final_state, void *stream) {
+                              const gdn_tensor *final_state, void *workspace, size_t workspace_bytes,
+                              void *stream) {
   g_error.clear();
   gdn::ChunkArgs P;
   TRY(plan_chunk(q, k, v, g, beta, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, initial_state, out_o,
                  final_state, &P));
+  TRY(attach_chunk_ws(&P, workspace, workspace_bytes));
+  if (P.ws_rec) {
+    const gdn_tensor wsd = {workspace, GDN_BF16, 1, {(int64_t)(workspace_bytes / 2)}, {1}};
+    const gdn_tensor *all[] = {q, k, v, g, beta, cu_seqlens, initial_state, out_o, final_state};
+    for (auto *t : all)
+      if (overlaps(&wsd, t)) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps a tensor argument");
+  }
   return launched(gdn::launch_chunk_rule(P, (hipStream_t)stream), "chunk rule");
+}
+
+size_t gdn_chunk_rule_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *dims,
+                                      int32_t act_dtype) {
+  if (!dims || B < 0 || T < 0 || n_seqs < 0 || !is_act(act_dtype)) return 0;
+  if (dims->Hqk <= 0 || dims->dk <= 0 || dims->Hv <= 0 || dims->dv <= 0) return 0;
+  return chunk_ws_bytes(B, T, n_seqs, dims->dk, dims->Hv, dims->dv, act_dtype);
 }
 
 gdn_status gdn_gated_norm_fwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_tensor *weight, float eps,
@@ -449,13 +495,15 @@ gdn_status gdn_gated_norm_fwd(const gdn_tensor *o, const gdn_tensor *gate, const
   return launched(gdn::launch_gated_norm(P, (hipStream_t)stream), "gated norm");
 }
 
-size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, const gdn_dims *dims, int32_t act_dtype) {
-  if (!dims || B < 0 || T < 0 || !is_act(act_dtype)) return 0;
+size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *dims,
+                                 int32_t act_dtype) {
+  if (!dims || B < 0 || T < 0 || n_seqs < 0 || !is_act(act_dtype)) return 0;
   if (dims->Hqk <= 0 || dims->dk <= 0 || dims->Hv <= 0 || dims->dv <= 0) return 0;
   const size_t es = (size_t)elem_size(act_dtype), n = (size_t)(B * T);
   const size_t C = (size_t)(2 * dims->Hqk * dims->dk + dims->Hv * dims->dv);
   return align256(n * C * es) + 2 * align256(n * (size_t)dims->Hv * 4) +
-         align256(n * (size_t)(dims->Hv * dims->dv) * es);
+         align256(n * (size_t)(dims->Hv * dims->dv) * es) +
+         chunk_ws_bytes(B, T, n_seqs, dims->dk, dims->Hv, dims->dv, act_dtype);
 }
 
 gdn_status gdn_layer_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
@@ -471,7 +519,13 @@ gdn_status gdn_layer_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn
   const int64_t B = x_q->shape[0], T = x_q->shape[1];
   const int32_t act = x_q->dtype;
   if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "x_q: dtype must be F32, BF16 or F16");
-  const size_t need = gdn_layer_workspace_bytes(B, T, dims, act);
+  int64_t n_seqs = 0;
+  if (cu_seqlens) {
+    if (cu_seqlens->ndim != 1 || cu_seqlens->shape[0] < 1)
+      return fail(GDN_ERR_INVALID_VALUE, "cu_seqlens: expected [N+1]");
+    n_seqs = cu_seqlens->shape[0] - 1;
+  }
+  const size_t need = gdn_layer_workspace_bytes(B, T, n_seqs, dims, act);
   if (!workspace) return fail(GDN_ERR_INVALID_VALUE, "workspace is NULL");
   if (workspace_bytes < need)
     return fail(GDN_ERR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
@@ -488,6 +542,8 @@ gdn_status gdn_layer_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn
   gdn_tensor bt = {ws, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
   ws += align256(n * (size_t)Hv * 4);
   gdn_tensor ot = {ws, act, 4, {B, T, Hv, dv}, {T * Hv * dv, Hv * dv, dv, 1}};
+  ws += align256(n * (size_t)(Hv * dv) * (size_t)es);
+  const size_t chunk_ws = chunk_ws_bytes(B, T, n_seqs, dk, Hv, dv, act);
   char *qkv_base = static_cast<char *>(qkv.data);
   gdn_tensor qv = {qkv_base, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
   gdn_tensor kv = {qkv_base + nq * es, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
@@ -502,6 +558,7 @@ gdn_status gdn_layer_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn
                     &bt, &PP));
   TRY(plan_chunk(&qv, &kv, &vv, &gt, &bt, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, nullptr, &ot,
                  nullptr, &PC));
+  TRY(attach_chunk_ws(&PC, chunk_ws ? ws : nullptr, chunk_ws));
   TRY(plan_norm(&ot, gate, norm_w, rms_eps, out, &PN));
   if (out->dtype != act) return fail(GDN_ERR_INVALID_VALUE, "out: dtype must be the activation dtype");
   const gdn_tensor *ins[] = {x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens};

@@ -49,7 +49,22 @@ struct ChunkArgs {
   int32_t use_l2;
   int32_t rows16;  // q, k and v rows are all 16-byte aligned
   float l2_eps, scale;
+  // Two-kernel path (chunk prep + chunk state): caller workspace.
+  unsigned char *ws_rec;  // [chunk_bound, Hv] records of kRecBytes, or null
+  int32_t *cu_chunks;     // [n_seqs + 1] chunk offsets of packed sequences
+  int64_t chunk_bound;    // number of record rows (>= total chunks)
 };
+
+// Per-(chunk, value head) record that the chunk-prep kernel writes and the
+// chunk-state kernel reads (16-bit activations). The 64 x 64 matrices are
+// stored as six MFMA A-operand fragments (lane l's 16 bytes at l * 16 within
+// each 1 KB fragment), fragment f = (row tile mt, k pair q) in the order
+// (0,0) (1,0) (2,0) (3,0) (2,1) (3,1); element e of lane 16 g + c is
+// M[16 mt + c][32 q + 16 (e / 4) + 4 g + e % 4].
+constexpr int64_t kRecT = 0;        // T = (I + A)^-1, activation dtype
+constexpr int64_t kRecP = 6144;     // P (scaled, decayed, masked q.k), act dtype
+constexpr int64_t kRecF = 12288;    // FP32 row factors [4][64]: aa, cw, zc, beta; then e^{gamma_C}
+constexpr int64_t kRecBytes = 14336;
 
 struct NormArgs {
   const void *o;
@@ -75,6 +90,11 @@ bool chunk_rule_supported(int64_t dk, int32_t act);
 // The wavefront-pipelined chunk kernel (16-bit inputs, dk 64 or 128).
 bool chunk_rule_v2_supported(int64_t dk, int32_t act);
 hipError_t launch_chunk_rule_v2(const ChunkArgs &a, hipStream_t s);
+
+// Two-kernel path: chunk prep (parallel over chunks and heads) then chunk
+// state (serial over chunks). Needs a.ws_rec / a.cu_chunks.
+bool chunk_split_supported(int64_t dk, int32_t act);
+hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s);
 
 // Largest power-of-two alignment (bytes, <= 16) of an address or stride set.
 inline int align_of_host(uint64_t addr) {

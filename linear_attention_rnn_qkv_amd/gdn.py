@@ -55,9 +55,12 @@ def lib() -> ctypes.CDLL:
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_version.restype = ctypes.c_char_p
         L.gdn_prologue_fwd.argtypes = [P] * 10 + [ctypes.POINTER(GdnDims), i32, f32, P, P, P, vp]
-        L.gdn_chunk_rule_fwd.argtypes = [P, P, P, P, P, f32, i32, f32, P, P, P, P, vp]
+        L.gdn_chunk_rule_fwd.argtypes = [P, P, P, P, P, f32, i32, f32, P, P, P, P, vp, ctypes.c_size_t, vp]
+        L.gdn_chunk_rule_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                     ctypes.POINTER(GdnDims), i32]
+        L.gdn_chunk_rule_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_gated_norm_fwd.argtypes = [P, P, P, f32, P, vp]
-        L.gdn_layer_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64,
+        L.gdn_layer_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                 ctypes.POINTER(GdnDims), i32]
         L.gdn_layer_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_layer_fwd.argtypes = ([P] * 12 + [ctypes.POINTER(GdnDims), f32, i32, f32, f32, vp,
@@ -135,22 +138,38 @@ def gdn_prologue_fwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seq
     return out_qkv, out_g, out_beta
 
 
+def gdn_chunk_rule_workspace_bytes(B: int, T: int, dims: Sequence[int], dtype: torch.dtype,
+                                   n_seqs: int = 0) -> int:
+    gd = dims_of(*dims)
+    return int(lib().gdn_chunk_rule_workspace_bytes(int(B), int(T), int(n_seqs), ctypes.byref(gd), DTYPE[dtype]))
+
+
 def gdn_chunk_rule_fwd(q, k, v, g, beta, scale: float, use_qk_l2norm_in_kernel: bool = True,
                        l2_eps: float = 1e-6, cu_seqlens=None, initial_state=None, out_o=None,
-                       output_final_state: bool = False, final_state=None):
-    """Chunked gated delta rule. Returns (o, final_state or None)."""
+                       output_final_state: bool = False, final_state=None, workspace="auto"):
+    """Chunked gated delta rule. Returns (o, final_state or None).
+
+    workspace: "auto" allocates the chunk workspace (two-kernel path where it
+    applies), None passes none (single-kernel path), or a uint8 device tensor
+    of at least gdn_chunk_rule_workspace_bytes(...) bytes."""
     B, T, Hv, dv = v.shape
-    dk = q.shape[3]
+    Hqk, dk = q.shape[2], q.shape[3]
     N = B if cu_seqlens is None else cu_seqlens.shape[0] - 1
     if out_o is None:
         out_o = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
     if output_final_state and final_state is None:
         final_state = torch.empty((N, Hv, dv, dk), dtype=torch.float32, device=q.device)
+    if isinstance(workspace, str):
+        nb = gdn_chunk_rule_workspace_bytes(B, T, (Hqk, dk, Hv, dv), q.dtype,
+                                            0 if cu_seqlens is None else N)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+    wptr = ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0)
+    wlen = ctypes.c_size_t(workspace.numel() if workspace is not None else 0)
     D = [desc(t) for t in (q, k, v, g, beta)]
     E = [desc(t) for t in (cu_seqlens, initial_state, out_o, final_state)]
     _check(lib().gdn_chunk_rule_fwd(*[_p(d) for d in D], float(scale),
                                     int(bool(use_qk_l2norm_in_kernel)), float(l2_eps),
-                                    *[_p(d) for d in E], _stream(q)))
+                                    *[_p(d) for d in E], wptr, wlen, _stream(q)))
     return out_o, final_state
 
 
@@ -163,9 +182,10 @@ def gdn_gated_norm_fwd(o, gate, weight, eps: float = 1e-5, out=None):
     return out
 
 
-def gdn_layer_workspace_bytes(B: int, T: int, dims: Sequence[int], dtype: torch.dtype) -> int:
+def gdn_layer_workspace_bytes(B: int, T: int, dims: Sequence[int], dtype: torch.dtype,
+                              n_seqs: int = 0) -> int:
     gd = dims_of(*dims)
-    return int(lib().gdn_layer_workspace_bytes(int(B), int(T), ctypes.byref(gd), DTYPE[dtype]))
+    return int(lib().gdn_layer_workspace_bytes(int(B), int(T), int(n_seqs), ctypes.byref(gd), DTYPE[dtype]))
 
 
 def gdn_layer_fwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens,
@@ -174,7 +194,8 @@ def gdn_layer_fwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, nor
     """The layer core (prologue -> chunk rule -> gated norm). Returns out."""
     Hqk, dk, Hv, dv = dims
     B, T = x_q.shape[0], x_q.shape[1]
-    nbytes = gdn_layer_workspace_bytes(B, T, dims, x_q.dtype)
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    nbytes = gdn_layer_workspace_bytes(B, T, dims, x_q.dtype, n_seqs)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_q.device)
     if out is None:

@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol():
     hdr = open(os.path.join(ROOT, "include", "gdn.h")).read()
     names = set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", hdr))
     assert names == {"gdn_last_error", "gdn_version", "gdn_prologue_fwd", "gdn_chunk_rule_fwd",
-                     "gdn_gated_norm_fwd", "gdn_layer_workspace_bytes", "gdn_layer_fwd"}
+                     "gdn_chunk_rule_workspace_bytes", "gdn_gated_norm_fwd", "gdn_layer_workspace_bytes",
+                     "gdn_layer_fwd"}
     L = gdn.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -34,8 +35,19 @@ def test_workspace_bytes():
     B, T, dims = 2, 1000, (6, 256, 6, 512)
     C = 2 * 6 * 256 + 6 * 512
     expect = a256(B * T * C * 2) + 2 * a256(B * T * 6 * 4) + a256(B * T * 6 * 512 * 2)
+    # dk = 256: the single-kernel recurrence, no chunk workspace
+    assert gdn.gdn_chunk_rule_workspace_bytes(B, T, dims, torch.bfloat16) == 0
     assert gdn.gdn_layer_workspace_bytes(B, T, dims, torch.bfloat16) == expect
     assert gdn.gdn_layer_workspace_bytes(B, T, (0, 64, 1, 64), torch.bfloat16) == 0
+    # dk = 128 BF16: chunk offsets, then one 14336-byte record per (chunk, value head)
+    d2 = (16, 128, 32, 128)
+    rec = 14336
+    assert gdn.gdn_chunk_rule_workspace_bytes(B, T, d2, torch.bfloat16) == a256((B + 1) * 4) + B * 16 * 32 * rec
+    assert gdn.gdn_chunk_rule_workspace_bytes(1, T, d2, torch.float16, n_seqs=5) == a256(6 * 4) + (16 + 5) * 32 * rec
+    assert gdn.gdn_chunk_rule_workspace_bytes(B, T, d2, torch.float32) == 0
+    C2 = 2 * 16 * 128 + 32 * 128
+    base = a256(B * T * C2 * 2) + 2 * a256(B * T * 32 * 4) + a256(B * T * 32 * 128 * 2)
+    assert gdn.gdn_layer_workspace_bytes(B, T, d2, torch.bfloat16) == base + a256((B + 1) * 4) + B * 16 * 32 * rec
 
 
 def _expect(status, fragment, fn, *args, **kw):
@@ -106,6 +118,18 @@ def test_chunk_rule_rejections():
     raw = torch.zeros(1 * 8 * 2 * 64 + 1, dtype=torch.bfloat16)
     q_mis = raw[1:].view(1, 8, 2, 64)
     _expect(UNSUPPORTED, "16-byte aligned", _chk, q=q_mis)
+    # chunk workspace: too small, misaligned, overlapping an argument
+    n = gdn.gdn_chunk_rule_workspace_bytes(1, 8, (2, 64, 4, 64), torch.bfloat16)
+    assert n > 0
+    _expect(INVALID, "chunk workspace too small", _chk, workspace=torch.zeros(n - 256, dtype=torch.uint8))
+    big = torch.zeros(n + 512, dtype=torch.uint8)
+    off = (-big.data_ptr()) % 256
+    _expect(INVALID, "256-byte aligned", _chk, workspace=big[off + 16: off + 16 + n])
+    buf = torch.zeros(n + 4096, dtype=torch.uint8)
+    off = (-buf.data_ptr()) % 256
+    ws = buf[off: off + n]
+    o_in_ws = ws[:8 * 4 * 64 * 2].view(torch.bfloat16).view(1, 8, 4, 64)
+    _expect(INVALID, "workspace overlaps", _chk, workspace=ws, out_o=o_in_ws)
 
 
 def _norm_inputs(B=1, T=4, H=2, dv=64, dt=torch.bfloat16, gdt=None, wdt=None):

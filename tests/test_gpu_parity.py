@@ -33,6 +33,9 @@ SMALL = [
     ("varlen-fp16-8seq", 4, {"lengths": (1, 63, 64, 65, 130, 2, 3, 200)}),
 ]
 IDS = [c[0] for c in SMALL]
+# The recurrence runs as two kernels (chunk prep + chunk state) when given a
+# workspace, as one kernel without; every recurrence test runs both.
+PATHS = {"split": "auto", "fused": None}
 
 
 def _spec(cfg, over):
@@ -93,8 +96,9 @@ def test_prologue_caller_side_l2norm(name, cfg, over):
 # ---------------------------------------------------------------------------
 # Chunk rule
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("name,cfg,over", SMALL, ids=IDS)
-def test_chunk_rule_parity(name, cfg, over):
+def test_chunk_rule_parity(name, cfg, over, path):
     s = _spec(cfg, over)
     x = synth.make_inputs(s)
     qkv, g, beta = H.oracle_prologue(x, s)
@@ -102,7 +106,7 @@ def test_chunk_rule_parity(name, cfg, over):
     cu = H.cu_of(x)
     qd, kd, vd, gd, bd, cud = _gpu_stage_inputs(s, qkv, g, beta, cu)
     for scale in (s.dk ** -0.5, 1.0):
-        o, _ = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, scale, True, 1e-6, cud)
+        o, _ = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, scale, True, 1e-6, cud, workspace=PATHS[path])
         torch.cuda.synchronize()
         ro, _ = O.gated_delta_rule(q, k, v, g, beta, scale=scale, cu_seqlens=cu)
         H.assert_close(f64(o), O.round_to(ro, s.act), TAU[s.act], f"o (scale {scale:g})")
@@ -115,8 +119,9 @@ def _stress_inputs(cfg, over, seed, dt_bias=None):
     return s, x, qkv, g, beta
 
 
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("act_cfg", [0, 3])
-def test_chunk_rule_state_in_out_slow_decay(act_cfg):
+def test_chunk_rule_state_in_out_slow_decay(act_cfg, path):
     # Stress set S1: dt_bias spread from -12 to 0 across heads, so some heads
     # keep their state for many chunks; a random initial state; final state out.
     over = {"T": 300, "Hqk": 2, "Hv": 4} if act_cfg == 3 else {"T": 200}
@@ -126,7 +131,9 @@ def test_chunk_rule_state_in_out_slow_decay(act_cfg):
     qd, kd, vd, gd, bd, _ = _gpu_stage_inputs(s, qkv, g, beta, None)
     S0 = synth.randn((s.B, s.Hv, s.dv, s.dk), "f32", 77).cuda() * 0.5
     scale = s.dk ** -0.5
-    o, fin = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, scale, True, 1e-6, None, S0, output_final_state=True)
+    ws = PATHS[path]
+    o, fin = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, scale, True, 1e-6, None, S0, output_final_state=True,
+                                    workspace=ws)
     torch.cuda.synchronize()
     ro, rfin = O.gated_delta_rule(q, k, v, g, beta, scale=scale, initial_state=f64(S0), output_final_state=True)
     tau = TAU[s.act]
@@ -135,16 +142,17 @@ def test_chunk_rule_state_in_out_slow_decay(act_cfg):
     # state hand-off at a point inside a chunk equals one run
     cut = 137
     o1, f1 = gdn.gdn_chunk_rule_fwd(qd[:, :cut], kd[:, :cut], vd[:, :cut], gd[:, :cut], bd[:, :cut], scale, True,
-                                    1e-6, None, S0, output_final_state=True)
+                                    1e-6, None, S0, output_final_state=True, workspace=ws)
     o2, f2 = gdn.gdn_chunk_rule_fwd(qd[:, cut:], kd[:, cut:], vd[:, cut:], gd[:, cut:], bd[:, cut:], scale, True,
-                                    1e-6, None, f1, output_final_state=True)
+                                    1e-6, None, f1, output_final_state=True, workspace=ws)
     torch.cuda.synchronize()
     H.assert_close(f64(torch.cat([o1, o2], 1)), O.round_to(ro, s.act), tau, "o (hand-off)")
     H.assert_close(f64(f2), rfin, tau, "final state (hand-off)")
 
 
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("cfg", [0, 3])
-def test_chunk_rule_no_decay(cfg):
+def test_chunk_rule_no_decay(cfg, path):
     # Stress set S2: g = 0 and beta ~ U(0, 1): nothing decays, so every chunk
     # boundary carries the full state.
     over = {"T": 260, "Hqk": 2, "Hv": 4} if cfg == 3 else {"T": 260}
@@ -153,7 +161,8 @@ def test_chunk_rule_no_decay(cfg):
     g = np.zeros((s.B, s.T, s.Hv))
     beta = O.round_to(synth.uniform((s.B, s.T, s.Hv), 0.0, 1.0, 5), "f32")
     qd, kd, vd, gd, bd, _ = _gpu_stage_inputs(s, qkv, g, beta, None)
-    o, fin = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.125, True, 1e-6, None, output_final_state=True)
+    o, fin = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.125, True, 1e-6, None, output_final_state=True,
+                                    workspace=PATHS[path])
     torch.cuda.synchronize()
     ro, rfin = O.gated_delta_rule(q, k, v, g, beta, scale=0.125, output_final_state=True)
     H.assert_close(f64(o), O.round_to(ro, s.act), TAU[s.act], "o")
@@ -180,29 +189,33 @@ def test_chunk_rule_orthonormal_keys_retrieve_values():
     H.assert_close(f64(o)[0, :, 0], exp, 1e-4, "retrieved values")
 
 
-def test_chunk_rule_gqa_map_equals_replication_bitwise():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_chunk_rule_gqa_map_equals_replication_bitwise(path):
     s, x, qkv, g, beta = _stress_inputs(3, {"T": 150}, 0)
     qd, kd, vd, gd, bd, _ = _gpu_stage_inputs(s, qkv, g, beta, None)
     G = s.Hv // s.Hqk
-    o1, _ = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.1, True, 1e-6)
+    ws = PATHS[path]
+    o1, _ = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.1, True, 1e-6, workspace=ws)
     o2, _ = gdn.gdn_chunk_rule_fwd(qd.repeat_interleave(G, 2).contiguous(), kd.repeat_interleave(G, 2).contiguous(),
-                                   vd, gd, bd, 0.1, True, 1e-6)
+                                   vd, gd, bd, 0.1, True, 1e-6, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
 
 
-def test_chunk_rule_deterministic_and_varlen_equals_separate_calls():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_chunk_rule_deterministic_and_varlen_equals_separate_calls(path):
     s, x, qkv, g, beta = _stress_inputs(4, {"lengths": (5, 64, 100, 1, 77)}, 0)
     cu = H.cu_of(x)
     qd, kd, vd, gd, bd, cud = _gpu_stage_inputs(s, qkv, g, beta, cu)
-    o1, f1 = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.2, True, 1e-6, cud, output_final_state=True)
-    o2, f2 = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.2, True, 1e-6, cud, output_final_state=True)
+    ws = PATHS[path]
+    o1, f1 = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.2, True, 1e-6, cud, output_final_state=True, workspace=ws)
+    o2, f2 = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.2, True, 1e-6, cud, output_final_state=True, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
     for i in range(len(cu) - 1):
         a, b = int(cu[i]), int(cu[i + 1])
         oi, fi = gdn.gdn_chunk_rule_fwd(qd[:, a:b], kd[:, a:b], vd[:, a:b], gd[:, a:b], bd[:, a:b], 0.2, True, 1e-6,
-                                        output_final_state=True)
+                                        output_final_state=True, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(oi, o1[:, a:b]), i
         assert torch.equal(fi[0], f1[i]), i
