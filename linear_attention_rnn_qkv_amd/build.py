@@ -20,7 +20,11 @@ SOURCES = ["gdn_api.cpp", "prologue.hip", "chunk_rule.hip", "chunk_rule_v2.hip",
            "chunk_state.hip", "gated_norm.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          # no packed-FP32 instructions in generated device code
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA sources and results in VGPRs (gfx950 has no separate
+         # accumulator file requirement): avoids AGPR<->VGPR copies around
+         # every VALU use of an accumulator
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -16,7 +16,7 @@
 // the gating of Gated DeltaNet (ICLR 2025); only non-positive exponents are
 // evaluated. T is computed in FP32: the four 16 x 16 diagonal blocks by
 // forward substitution, then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj block
-// column by block column. Results go to the caller's workspace in MFMA
+// column by block column on the FP32 MFMA. Results go to the caller's workspace in MFMA
 // operand order (layout in gdn_internal.h).
 //
 // One workgroup (four wavefronts) per (chunk, value head); q/k/v of the GQA
@@ -304,8 +304,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
     }
   }
   __syncthreads();
-  //    Off-diagonal blocks: wave j owns block column j; lane (g, c) computes
-  //    rows 4g..4g+3 of column c of each 16 x 16 block.
+  //    Off-diagonal blocks: wave j owns block column j. 16 x 16 x 16 products
+  //    on the FP32 MFMA (16x16x4: lane 16 g + c supplies A[c][4 kk + g] and
+  //    B[4 kk + g][c]; the result lane holds rows 4 g .. 4 g + 3 of column c).
   {
     const int j = wave;
     float *xs = sm.u.m.x[j];
@@ -316,11 +317,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
         const float *ab = sm.u.m.a[blk(i, k)];
         const float *tb = sm.u.m.t[blk(k, j)];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&ab[m * 16 + 4 * g]);  // A[4g..4g+3][m]
-          const float tm = tb[c * 16 + m];                                        // T[m][c]
-          xv += a4 * tm;
-        }
+        for (int kk = 0; kk < 4; ++kk)
+          xv = __builtin_amdgcn_mfma_f32_16x16x4f32(ab[(4 * kk + g) * 16 + c], tb[c * 16 + 4 * kk + g], xv, 0, 0, 0);
       }
       *reinterpret_cast<f32x4 *>(&xs[c * 16 + 4 * g]) = xv;
       lds_fence_wave();
@@ -328,11 +326,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
       const float *ti = sm.u.m.t[blk(i, i)];
       f32x4 tv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&ti[m * 16 + 4 * g]);  // T_ii[4g..][m]
-        tv -= t4 * xs[c * 16 + m];
-      }
-      *reinterpret_cast<f32x4 *>(&sm.u.m.t[blk(i, j)][c * 16 + 4 * g]) = tv;
+      for (int kk = 0; kk < 4; ++kk)
+        tv = __builtin_amdgcn_mfma_f32_16x16x4f32(ti[(4 * kk + g) * 16 + c], xs[c * 16 + 4 * kk + g], tv, 0, 0, 0);
+      *reinterpret_cast<f32x4 *>(&sm.u.m.t[blk(i, j)][c * 16 + 4 * g]) = -tv;
       lds_fence_wave();
     }
   }
