@@ -7,10 +7,11 @@
 //   A[r,i] = beta_r exp(gamma_r - gamma_i) rk_r rk_i (k_r . k_i),   i < r
 //   T      = (I + A)^-1                        (unit lower triangular)
 //   P[r,i] = scale exp(gamma_r - gamma_i) rq_r rk_i (q_r . k_i),    i <= r
-//   aa = beta e^gamma rk,  cw = e^(gamma_C - gamma) rk,  zc = scale e^gamma rq
+//   T' = T diag(beta),  aa = e^gamma rk,  cw = e^(gamma_C - gamma) rk,
+//   zc = scale e^gamma rq
 //
 // which the chunk-state kernel consumes as
-//   Vn = T (beta (.) V) - T (aa (.) (K S0^T)),   O = zc (.) (Q S0^T) + P Vn,
+//   Vn = T' V - T' (aa (.) (K S0^T)),   O = zc (.) (Q S0^T) + P Vn,
 //   S  = e^gamma_C S0 + K^T (cw (.) Vn).
 // This is the WY/UT form of the delta rule (Yang et al., NeurIPS 2024) with
 // the gating of Gated DeltaNet (ICLR 2025); only non-positive exponents are
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
   } else if (wave == 2) {
     float *rf = reinterpret_cast<float *>(rec + kRecF);
     const float bt = sm.fac[P_BT][lane], eg = sm.fac[P_EG][lane], rk = sm.fac[P_RK][lane];
-    rf[0 * BT + lane] = bt * eg * rk;                            // aa
+    rf[0 * BT + lane] = eg * rk;                                 // aa (beta is in T')
     rf[1 * BT + lane] = sm.fac[P_ECG][lane] * rk;                // cw
     rf[2 * BT + lane] = p.scale * eg * sm.fac[P_RQ][lane];       // zc
     rf[3 * BT + lane] = bt;                                      // beta
@@ -334,7 +335,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
   }
   __syncthreads();
 
-  // 5. T fragments to the record: wave w writes fragments w and w + 4.
+  // 5. T' = T diag(beta) fragments to the record: wave w writes fragments w
+  //    and w + 4.
   for (int f = wave; f < 6; f += 4) {
     const int mt = f < 4 ? f : f - 2, q = f < 4 ? 0 : 1;
     f32x4 lo, hi;
@@ -345,7 +347,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
       if (nb <= mt) {
         const float *tb = sm.u.m.t[blk(mt, nb)];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = tb[(4 * g + i) * 16 + c];  // T[row c][col 4g + i]
+        for (int i = 0; i < 4; ++i)  // T[row c][col 4g + i] beta_col
+          v[i] = tb[(4 * g + i) * 16 + c] * sm.fac[P_BT][16 * nb + 4 * g + i];
       }
       if (hh == 0) lo = v; else hi = v;
     }

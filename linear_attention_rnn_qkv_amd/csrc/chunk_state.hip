@@ -1,12 +1,12 @@
 // Chunk state: the state-dependent half of the chunked gated delta rule,
 // serial over the chunks of a sequence. With the per-chunk record written by
-// the chunk-prep kernel (T = (I + A)^-1, P and row factors aa, cw, zc, beta,
-// e^{gamma_C}; see chunk_prep.hip), a chunk of 64 rows entering with state S0
-// (dv x dk, FP32) gives
+// the chunk-prep kernel (T' = (I + A)^-1 diag(beta), P and row factors aa,
+// cw, zc, e^{gamma_C}; see chunk_prep.hip), a chunk of 64 rows entering with
+// state S0 (dv x dk, FP32) gives
 //
-//   U  = T (beta (.) V),   X = K S0^T,   Vn = U - T (aa (.) X)
-//   O  = zc (.) (Q S0^T) + P Vn
-//   S  = e^{gamma_C} S0 + K^T (cw (.) Vn)
+//   X = K S0^T,   Vn = T' V - T' (aa (.) X)
+//   O = zc (.) (Q S0^T) + P Vn          (computed transposed, O^T)
+//   S = e^{gamma_C} S0 + K^T (cw (.) Vn)
 //
 // (the WY/UT form of the gated delta rule; q and k are used raw, their
 // inverse norms are inside the factors).
@@ -15,8 +15,9 @@
 // wavefronts and one barrier per step s:
 //   wave 0  chain(s): U, X, Vn, the state update; S lives in MFMA
 //           accumulators; Vn and the next S are handed over as fragments.
-//   wave 1  out(s):   Q S0^T for chunk s and, with Vn(s - 1), finishes and
-//                     stores o(s - 1).
+//   wave 1  out(s):   (Q S0^T)^T for chunk s and, with Vn(s - 1), finishes
+//                     o(s - 1) transposed, so that each lane stores 4
+//                     consecutive dv values of a row (8-byte stores).
 //   wave 2  loads:    streams the k, q, v tiles and the record of chunk s + 2
 //                     into three-slot LDS rings (global_load_lds); the copies
 //                     of a step are complete before the barrier that ends the
@@ -127,6 +128,10 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
     int trc[NT];
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) trc[mt] = trb + (((2 * mt + ((c & 3) >> 1)) ^ yrow) << 4);
+    // V fragments (B operand of T' V) by transposing reads of the [64][16]
+    // v tile: lane 16 g + L reads the 4 values of row 4 g + L / 4 starting at
+    // column 4 (L % 4); lane c then holds V[t0 .. t0 + 3][c].
+    const int vtr = (4 * g + (c >> 2)) * (DVT * 2) + 8 * (c & 3);
     for (int s = -2; s <= Nc; ++s) {
       lds_barrier();
       if (s < 0 || s >= Nc) continue;
@@ -143,26 +148,23 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int pp = 0; pp < KT; ++pp) kf[mt][pp] = frag_at<T>(kt + mt * 16 * RB, fo[pp][0], fo[pp][1]);
-      f32x4 aa[4], cw[4], bt[4];
+      f32x4 aa[4], cw[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int r0 = 16 * mt + 4 * g;
         aa[mt] = *reinterpret_cast<const f32x4 *>(&fa[0 * BT + r0]);
         cw[mt] = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + r0]);
-        bt[mt] = *reinterpret_cast<const f32x4 *>(&fa[3 * BT + r0]);
       }
       const float eC = fa[4 * BT];
-      // B operands of U = T (beta (.) V): rows 32 q + 16 hh + 4 g + i, column c
+      // B operands of T' V: rows 32 q + 16 hh + 4 g + i, column c
       f8 Bv[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        f32x4 lo, hi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo[i] = f(vt[(32 * q + 4 * g + i) * DVT + c]);
-          hi[i] = f(vt[(32 * q + 16 + 4 * g + i) * DVT + c]);
-        }
-        Bv[q] = cat8<T>(cvt4<T>(bt[2 * q] * lo), cvt4<T>(bt[2 * q + 1] * hi));
+        const unsigned char *vb8 = reinterpret_cast<const unsigned char *>(vt) + vtr + 32 * q * (DVT * 2);
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb8));
+        const s16x4 r1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb8 + 16 * DVT * 2));
+        Bv[q] = cat8<T>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
       }
       f8 kt8[NT][2];
 #pragma unroll
@@ -184,14 +186,14 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
       for (int pp = 0; pp < KT; ++pp)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) X[mt] = MF::k32(kf[mt][pp], Sf[pp], X[mt]);
-      // U = T (beta (.) V), independent of S
+      // U = T' V, independent of S
       f32x4 U[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         U[mt] = MF::k32(Tf[frag_id(mt, 0)], Bv[0], zero4);
         if (mt >= 2) U[mt] = MF::k32(Tf[frag_id(mt, 1)], Bv[1], U[mt]);
       }
-      // Vn = U - T (aa (.) X)
+      // Vn = U - T' (aa (.) X)
       f8 Rf[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) Rf[q] = cat8<T>(cvt4<T>(aa[2 * q] * X[2 * q]), cvt4<T>(aa[2 * q + 1] * X[2 * q + 1]));
@@ -241,15 +243,13 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
 #pragma unroll
         for (int q = 0; q < 2; ++q) Wf[q] = *reinterpret_cast<const f8 *>(&sm.wfrag[co & 1][lane * 16 + 8 * q]);
         T *orow = ob + (int64_t)co * BT * p.so_t;
+        // O^T = Zc^T + Vn^T P^T: lane (g, c) holds o[16 mt + c][4 g .. 4 g + 3]
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          f32x4 o = MF::k32(Pf[frag_id(mt, 0)], Wf[0], Zc[mt]);
-          if (mt >= 2) o = MF::k32(Pf[frag_id(mt, 1)], Wf[1], o);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mt + 4 * g + i;
-            if (r < nr) orow[(int64_t)r * p.so_t + c] = to<T>(o[i]);
-          }
+          f32x4 o = MF::k32(Wf[0], Pf[frag_id(mt, 0)], Zc[mt]);
+          if (mt >= 2) o = MF::k32(Wf[1], Pf[frag_id(mt, 1)], o);
+          const int r = 16 * mt + c;
+          if (r < nr) *reinterpret_cast<v4 *>(orow + (int64_t)r * p.so_t + 4 * g) = cvt4<T>(o);
         }
       }
       if (s < 0 || s >= Nc) continue;
@@ -269,12 +269,13 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
       f32x4 z[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) z[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // Z^T = S0 Q^T: lane (g, c) holds Z[16 mt + c][dv 4 g + i]
 #pragma unroll
       for (int pp = 0; pp < KT; ++pp)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) z[mt] = MF::k32(qf[mt][pp], Sf[pp], z[mt]);
+        for (int mt = 0; mt < 4; ++mt) z[mt] = MF::k32(Sf[pp], qf[mt][pp], z[mt]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) Zc[mt] = *reinterpret_cast<const f32x4 *>(&fa[2 * BT + 16 * mt + 4 * g]) * z[mt];
+      for (int mt = 0; mt < 4; ++mt) Zc[mt] = z[mt] * fa[2 * BT + 16 * mt + c];
     }
   } else {
     // ------------------------------------------------------------- loads

@@ -362,6 +362,7 @@ gdn_status plan_chunk(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor
   p.B = B; p.T = T; p.Hqk = Hqk; p.dk = dk; p.Hv = Hv; p.dv = dv;
   p.act = act; p.use_l2 = use_l2 ? 1 : 0; p.l2_eps = l2_eps; p.scale = scale;
   p.rows16 = row_align(v, 3) >= 16 ? 1 : 0;
+  p.o8 = row_align(out_o, 3) >= 8 ? 1 : 0;
   return GDN_OK;
 }
 
@@ -426,7 +427,7 @@ gdn_status attach_chunk_ws(gdn::ChunkArgs *p, void *ws, size_t ws_bytes) {
   p->cu_chunks = nullptr;
   p->chunk_bound = 0;
   if (!ws) return GDN_OK;
-  if (!gdn::chunk_split_supported(p->dk, p->act) || !p->rows16 || p->dv % 16) return GDN_OK;  // not used
+  if (!gdn::chunk_split_supported(p->dk, p->act) || !p->rows16 || !p->o8 || p->dv % 16) return GDN_OK;  // not used
   const int64_t ns = p->cu_seqlens ? p->n_seqs : 0;
   const size_t need = chunk_ws_bytes(p->B, p->T, ns, p->dk, p->Hv, p->dv, p->act);
   if (ws_bytes < need)

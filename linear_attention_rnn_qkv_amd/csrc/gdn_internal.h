@@ -48,6 +48,7 @@ struct ChunkArgs {
   int32_t act;
   int32_t use_l2;
   int32_t rows16;  // q, k and v rows are all 16-byte aligned
+  int32_t o8;      // o rows are 8-byte aligned
   float l2_eps, scale;
   // Two-kernel path (chunk prep + chunk state): caller workspace.
   unsigned char *ws_rec;  // [chunk_bound, Hv] records of kRecBytes, or null
@@ -61,7 +62,7 @@ struct ChunkArgs {
 // each 1 KB fragment), fragment f = (row tile mt, k pair q) in the order
 // (0,0) (1,0) (2,0) (3,0) (2,1) (3,1); element e of lane 16 g + c is
 // M[16 mt + c][32 q + 16 (e / 4) + 4 g + e % 4].
-constexpr int64_t kRecT = 0;        // T = (I + A)^-1, activation dtype
+constexpr int64_t kRecT = 0;        // T' = (I + A)^-1 diag(beta), activation dtype
 constexpr int64_t kRecP = 6144;     // P (scaled, decayed, masked q.k), act dtype
 constexpr int64_t kRecF = 12288;    // FP32 row factors [4][64]: aa, cw, zc, beta; then e^{gamma_C}
 constexpr int64_t kRecBytes = 14336;
