@@ -48,6 +48,20 @@ struct StateLds {
 // fragment index of (row tile mt, k pair q) in a record matrix
 __device__ __forceinline__ constexpr int frag_id(int mt, int q) { return q == 0 ? mt : 2 + mt; }
 
+template <int N> struct Slot { static constexpr int v = N; };
+
+// Runs body(s, Slot<s mod 3>) for s = -2 .. last in order: the ring slot of
+// chunk s is a compile-time constant in every call, so LDS addresses are
+// loop-invariant.
+template <typename F>
+__device__ __forceinline__ void for_steps(int last, F &&body) {
+  for (int base = -3; base <= last; base += 3) {
+    if (base >= -2) body(base, Slot<0>{});
+    if (base + 1 >= -2 && base + 1 <= last) body(base + 1, Slot<1>{});
+    if (base + 2 <= last) body(base + 2, Slot<2>{});
+  }
+}
+
 template <typename T, int DK>
 __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p) {
   using MF = M2<T>;
@@ -132,10 +146,10 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
     // v tile: lane 16 g + L reads the 4 values of row 4 g + L / 4 starting at
     // column 4 (L % 4); lane c then holds V[t0 .. t0 + 3][c].
     const int vtr = (4 * g + (c >> 2)) * (DVT * 2) + 8 * (c & 3);
-    for (int s = -2; s <= Nc; ++s) {
+    for_steps(Nc, [&](int s, auto SL) {
       lds_barrier();
-      if (s < 0 || s >= Nc) continue;
-      const int sl = s % 3;
+      if (s < 0 || s >= Nc) return;
+      constexpr int sl = decltype(SL)::v;
       const unsigned char *kt = sm.k[sl];
       const unsigned char *rec = sm.rec[sl];
       const float *fa = reinterpret_cast<const float *>(rec + kRecF);
@@ -223,7 +237,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
         Sf[pp] = cat8<T>(cvt4<T>(S[2 * pp]), cvt4<T>(S[2 * pp + 1]));
         *reinterpret_cast<f8 *>(&sm.sfrag[(s & 1) ^ 1][lane * SF + 8 * pp]) = Sf[pp];
       }
-    }
+    });
     if (p.final_state) {
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
@@ -234,7 +248,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
     // ------------------------------------------------- out(s), o(s - 1)
     f32x4 Zc[4];
     f8 Pf[6];
-    for (int s = -2; s <= Nc; ++s) {
+    for_steps(Nc, [&](int s, auto SL) {
       lds_barrier();
       const int co = s - 1;
       if (co >= 0 && co < Nc) {
@@ -252,8 +266,8 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
           if (r < nr) *reinterpret_cast<v4 *>(orow + (int64_t)r * p.so_t + 4 * g) = cvt4<T>(o);
         }
       }
-      if (s < 0 || s >= Nc) continue;
-      const int sl = s % 3;
+      if (s < 0 || s >= Nc) return;
+      constexpr int sl = decltype(SL)::v;
       const unsigned char *qt = sm.q[sl];
       const unsigned char *rec = sm.rec[sl];
       const float *fa = reinterpret_cast<const float *>(rec + kRecF);
@@ -276,31 +290,60 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
         for (int mt = 0; mt < 4; ++mt) z[mt] = MF::k32(Sf[pp], qf[mt][pp], z[mt]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) Zc[mt] = z[mt] * fa[2 * BT + 16 * mt + c];
-    }
+    });
   } else {
     // ------------------------------------------------------------- loads
-    for (int s = -2; s <= Nc; ++s) {
+    // Per-lane byte offsets of the copies inside a chunk (rows of the q/k
+    // tiles with the XOR swizzle, v half rows, record bytes); a full chunk is
+    // then a block-uniform base plus these, with no per-step address math.
+    uint32_t koff[NI], qoff[NI], voff[2];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int b = 1024 * i + 16 * lane;
+      const int r = b / RB, jp = (b % RB) >> 4;
+      const int j = jp ^ (r & (CPR - 1));
+      koff[i] = (uint32_t)(((int64_t)r * p.sk_t + 8 * j) * (int64_t)sizeof(T));
+      qoff[i] = (uint32_t)(((int64_t)r * p.sq_t + 8 * j) * (int64_t)sizeof(T));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      voff[i] = (uint32_t)(((int64_t)(32 * i + (lane >> 1)) * p.sv_t + 8 * (lane & 1)) * (int64_t)sizeof(T));
+    for_steps(Nc, [&](int s, auto SL) {
       lds_barrier();
+      constexpr int sl = (decltype(SL)::v + 2) % 3;  // slot of chunk s + 2
       const int cl = s + 2;
       const bool issue = cl < Nc;
       if (issue) {
         const int nr = rows_of(cl);
         const int64_t t0 = (int64_t)cl * BT;
-        const int sl = cl % 3;
+        if (nr == BT) {
+          const unsigned char *kg = reinterpret_cast<const unsigned char *>(kb + t0 * p.sk_t);
+          const unsigned char *qg = reinterpret_cast<const unsigned char *>(qb + t0 * p.sq_t);
+          const unsigned char *vg = reinterpret_cast<const unsigned char *>(vb + t0 * p.sv_t);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int b = 1024 * i + 16 * lane;
-          const int r = b / RB, jp = (b % RB) >> 4;
-          const int j = jp ^ (r & (CPR - 1));
-          const int rr = r < nr ? r : nr - 1;
-          g2l16(kb + (t0 + rr) * p.sk_t + 8 * j, sm.k[sl] + 1024 * i);
-          g2l16(qb + (t0 + rr) * p.sq_t + 8 * j, sm.q[sl] + 1024 * i);
-        }
+          for (int i = 0; i < NI; ++i) {
+            g2l16(kg + koff[i], sm.k[sl] + 1024 * i);
+            g2l16(qg + qoff[i], sm.q[sl] + 1024 * i);
+          }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = 32 * i + (lane >> 1);
-          const int rr = r < nr ? r : nr - 1;
-          g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane & 1), reinterpret_cast<unsigned char *>(sm.v[sl]) + 1024 * i);
+          for (int i = 0; i < 2; ++i) g2l16(vg + voff[i], reinterpret_cast<unsigned char *>(sm.v[sl]) + 1024 * i);
+        } else {
+          // last, partial chunk: rows past its end repeat its last row
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            const int b = 1024 * i + 16 * lane;
+            const int r = b / RB, jp = (b % RB) >> 4;
+            const int j = jp ^ (r & (CPR - 1));
+            const int rr = r < nr ? r : nr - 1;
+            g2l16(kb + (t0 + rr) * p.sk_t + 8 * j, sm.k[sl] + 1024 * i);
+            g2l16(qb + (t0 + rr) * p.sq_t + 8 * j, sm.q[sl] + 1024 * i);
+          }
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int r = 32 * i + (lane >> 1);
+            const int rr = r < nr ? r : nr - 1;
+            g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane & 1), reinterpret_cast<unsigned char *>(sm.v[sl]) + 1024 * i);
+          }
         }
         const unsigned char *rg = recb + (int64_t)cl * rec_stride;
 #pragma unroll
@@ -309,7 +352,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
       // The copies of the previous step must be complete before the next
       // barrier publishes them; this step's stay in flight.
       if (issue) wait_vm<NLOAD>(); else wait_vm<0>();
-    }
+    });
   }
 }
 
