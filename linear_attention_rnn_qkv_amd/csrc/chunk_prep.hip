@@ -73,9 +73,12 @@ struct PrepLds {
     float t[10][256];                  //   same for T
     float x[4][256];                   //   per-wave scratch
   };
-  alignas(16) unsigned char k[TILE];
+  struct Tiles {
+    unsigned char k[TILE];
+    unsigned char q[TILE];
+  };
   union alignas(16) {
-    unsigned char q[TILE];             // q rows, dead after the P^T product
+    Tiles x;                           // k and q rows, dead after the products
     Mats m;
   } u;
   alignas(16) float fac[P_N][BT];
@@ -85,7 +88,8 @@ struct PrepLds {
 __device__ __forceinline__ int blk(int mi, int ni) { return mi * (mi + 1) / 2 + ni; }
 
 template <typename T, int DK>
-__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
+__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
+    ChunkArgs p) {
   using MF = M2<T>;
   using f8 = typename MF::f8;
   using v4 = typename MF::v4;
@@ -131,9 +135,9 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
     const int r = i / CPR, jp = i % CPR;
     const int j = jp ^ (r & (CPR - 1));
     const int rr = r < nr ? r : nr - 1;
-    *reinterpret_cast<uint4 *>(sm.k + r * RB + jp * 16) =
+    *reinterpret_cast<uint4 *>(sm.u.x.k + r * RB + jp * 16) =
         *reinterpret_cast<const uint4 *>(kb + (int64_t)rr * p.sk_t + 8 * j);
-    *reinterpret_cast<uint4 *>(sm.u.q + r * RB + jp * 16) =
+    *reinterpret_cast<uint4 *>(sm.u.x.q + r * RB + jp * 16) =
         *reinterpret_cast<const uint4 *>(qb + (int64_t)rr * p.sq_t + 8 * j);
   }
   __syncthreads();
@@ -150,18 +154,16 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
 #pragma unroll
   for (int t = 0; t < 10; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (wave == 0) {
-    f8 kf[4][KT];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int pp = 0; pp < KT; ++pp) kf[mt][pp] = frag_at<T>(sm.k + mt * 16 * RB, fo[pp][0], fo[pp][1]);
-#pragma unroll
+#pragma unroll 2  // a full unroll hoists every fragment load: 150 VGPRs at DK = 128
     for (int pp = 0; pp < KT; ++pp) {
+      f8 kf[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) kf[mt] = frag_at<T>(sm.u.x.k + mt * 16 * RB, fo[pp][0], fo[pp][1]);
       int t = 0;
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(kf[mi][pp], kf[ni][pp], acc[t]);
+        for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(kf[mi], kf[ni], acc[t]);
     }
     // 1/|k| from the diagonal: lane (g, c) with c / 4 == g holds |k_{16 mi + c}|^2
     if ((c >> 2) == g) {
@@ -174,28 +176,26 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
       }
     }
   } else if (wave == 1) {
-    f8 kf[4][KT], qf[4][KT];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int pp = 0; pp < KT; ++pp) {
-        kf[mt][pp] = frag_at<T>(sm.k + mt * 16 * RB, fo[pp][0], fo[pp][1]);
-        qf[mt][pp] = frag_at<T>(sm.u.q + mt * 16 * RB, fo[pp][0], fo[pp][1]);
-      }
     // lane (g, c) of tile (mi, ni): q_{16 mi + c} . k_{16 ni + 4 g + j}
-#pragma unroll
+    float ssqs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2  // a full unroll hoists every fragment load: 150 VGPRs at DK = 128
     for (int pp = 0; pp < KT; ++pp) {
+      f8 kf[4], qf[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        kf[mt] = frag_at<T>(sm.u.x.k + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+        qf[mt] = frag_at<T>(sm.u.x.q + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+        ssqs[mt] = sumsq8<T>(qf[mt], ssqs[mt]);
+      }
       int t = 0;
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(kf[ni][pp], qf[mi][pp], acc[t]);
+        for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(kf[ni], qf[mi], acc[t]);
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      float ssq = 0.f;
-#pragma unroll
-      for (int pp = 0; pp < KT; ++pp) ssq = sumsq8<T>(qf[mt][pp], ssq);
+      float ssq = ssqs[mt];
       ssq += __shfl_xor(ssq, 16, 64);
       ssq += __shfl_xor(ssq, 32, 64);
       if (g == 0) sm.fac[P_RQ][16 * mt + c] = p.use_l2 ? rsqrtf(ssq + p.l2_eps) : 1.f;
@@ -246,28 +246,26 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(ChunkArgs p) {
       }
     }
   } else if (wave == 1) {
-    f32x4 pv[10];
-    int t = 0;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    // P^T tile (mi, ni), lane (g, c): row r = 16 mi + c, key i = 16 ni + 4 g + j
+    auto ptile = [&](int mi, int ni) -> f32x4 {
       const int r = 16 * mi + c;
       const float rowf = p.scale * sm.fac[P_RQ][r], gr = sm.fac[P_GAM][r];
+      const f32x4 a = acc[blk(mi, ni)];
+      f32x4 pv;
 #pragma unroll
-      for (int ni = 0; ni <= mi; ++ni, ++t) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 16 * ni + 4 * g + j;
-          const float e = fast_exp(gr - sm.fac[P_GAM][i]);
-          pv[t][j] = i <= r ? rowf * sm.fac[P_RK][i] * e * acc[t][j] : 0.f;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int i = 16 * ni + 4 * g + j;
+        const float e = fast_exp(gr - sm.fac[P_GAM][i]);
+        pv[j] = i <= r ? rowf * sm.fac[P_RK][i] * e * a[j] : 0.f;
       }
-    }
+      return pv;
+    };
     const v4 z4 = cvt4<T>(f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int f = 0; f < 6; ++f) {
       const int mt = f < 4 ? f : f - 2, q = f < 4 ? 0 : 1;
-      const v4 lo = cvt4<T>(pv[blk(mt, 2 * q)]);
-      const v4 hi = (2 * q + 1 <= mt) ? cvt4<T>(pv[blk(mt, 2 * q + 1)]) : z4;
+      const v4 lo = cvt4<T>(ptile(mt, 2 * q));
+      const v4 hi = (2 * q + 1 <= mt) ? cvt4<T>(ptile(mt, 2 * q + 1)) : z4;
       *reinterpret_cast<f8 *>(rec + kRecP + f * 1024 + lane * 16) = cat8<T>(lo, hi);
     }
   } else if (wave == 2) {
