@@ -11,14 +11,14 @@
 // (the WY/UT form of the gated delta rule; q and k are used raw, their
 // inverse norms are inside the factors).
 //
-// One workgroup = (sequence, value head, 16 rows of dv) with three
+// One workgroup = (sequence, value head, 16 rows of dv) with eight
 // wavefronts and one barrier per step s:
 //   wave 0  chain(s): U, X, Vn, the state update; S lives in MFMA
 //           accumulators; Vn and the next S are handed over as fragments.
 //   wave 1  out(s):   (Q S0^T)^T for chunk s and, with Vn(s - 1), finishes
 //                     o(s - 1) transposed, so that each lane stores 4
 //                     consecutive dv values of a row (8-byte stores).
-//   wave 2  loads:    streams the k, q, v tiles and the record of chunk s + 2
+//   waves 2-7 loads:  stream the k, q, v tiles and the record of chunk s + 2
 //                     into three-slot LDS rings (global_load_lds); the copies
 //                     of a step are complete before the barrier that ends the
 //                     next step, so two steps of latency are hidden.
@@ -28,7 +28,7 @@
 namespace gdn {
 namespace {
 
-constexpr int kStateThreads = 192;
+constexpr int kStateThreads = 512;
 constexpr int BT = 64;
 constexpr int DVT = 16;
 
@@ -44,6 +44,24 @@ struct StateLds {
   alignas(16) T sfrag[2][64 * (DK / 4)];     // state fragments per lane
   alignas(16) T wfrag[2][64 * 16];           // Vn fragments per lane
 };
+
+// The dk axis of the state tiles is permuted so that every MFMA operand
+// fragment over dk is one contiguous 16-byte run: accumulator tile mt = 2 pp + h,
+// row 4 g + i holds dk 32 pp + 8 g + 4 h + i. The state fragment of k step pp
+// (tiles 2 pp and 2 pp + 1 side by side) then covers dk 32 pp + 8 g .. + 7 in
+// lane group g, matching one 16-byte read of a k or q row.
+__device__ __forceinline__ constexpr int dk_of(int mt, int r) {
+  return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3);
+}
+
+// XOR swizzle of the 16-byte units of a q/k tile row. It keeps the row reads
+// of the fragments (16 rows, one unit) and the transposing reads of the
+// state update (4 rows x 4 units per 16 lanes) free of bank conflicts.
+template <int DK>
+__device__ __forceinline__ constexpr int kswz(int r) {
+  if constexpr (DK == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 // fragment index of (row tile mt, k pair q) in a record matrix
 __device__ __forceinline__ constexpr int frag_id(int mt, int q) { return q == 0 ? mt : 2 + mt; }
@@ -71,11 +89,10 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
   constexpr int KT = DK / 32;
   constexpr int NT = DK / 16;
   constexpr int SF = DK / 4;
-  constexpr int RB = SM::RB, CPR = SM::CPR;
+  constexpr int RB = SM::RB;
   constexpr int NI = SM::TILE / 1024;          // 1 KB copies per q/k tile
   constexpr int NR = (int)(kRecBytes / 1024);  // 1 KB copies per record
-  constexpr int NLOAD = 2 * NI + 2 + NR;       // copies per step
-  static_assert(NLOAD <= 63, "vmcnt range");
+  static_assert(NI % 2 == 0 && NR % 2 == 0 && NI / 2 <= 31 && NR / 2 + 1 <= 31, "copy split");
   __shared__ SM sm;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -114,34 +131,33 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
     const int64_t r = L - (int64_t)ch * BT;
     return (int)(r < BT ? r : BT);
   };
-  int fo[KT][2];
+  int fo[KT];  // row c of a 16-row tile, dk 32 pp + 8 g .. + 7
 #pragma unroll
-  for (int pp = 0; pp < KT; ++pp)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      fo[pp][hh] = c * RB + (((4 * pp + (g >> 1) + 2 * hh) ^ (c & (CPR - 1))) << 4) + 8 * (g & 1);
+  for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
 
   // Steps s = -2 .. Nc, one barrier each, in every wave.
   if (wave == 0) {
     // ---------------------------------------------------------------- chain
-    f32x4 S[NT];  // S[mt][i] = S[dv row c][dk 16 mt + 4 g + i]
+    f32x4 S[NT];  // S[mt][i] = S[dv row c][dk dk_of(mt, 4 g + i)]
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S[mt][i] = p.init_state ? p.init_state[st_base + (int64_t)c * DK + 16 * mt + 4 * g + i] : 0.f;
+        S[mt][i] = p.init_state ? p.init_state[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] : 0.f;
     f8 Sf[KT];
 #pragma unroll
     for (int pp = 0; pp < KT; ++pp) {
       Sf[pp] = cat8<T>(cvt4<T>(S[2 * pp]), cvt4<T>(S[2 * pp + 1]));
       *reinterpret_cast<f8 *>(&sm.sfrag[0][lane * SF + 8 * pp]) = Sf[pp];
     }
-    // transposing-read offsets (K^T fragments of the state update)
-    const int yrow = (4 * g + (c >> 2)) & (CPR - 1);
-    const int trb = (4 * g + (c >> 2)) * RB + 8 * (c & 1);
+    // transposing-read offsets (K^T fragments of the state update): lane
+    // 16 g + c addresses row 4 g + c / 4 at dk dk_of(mt, 4 (c % 4)) .. + 3, so
+    // that lane c of the group receives dk dk_of(mt, c) of rows 4 g .. 4 g + 3
+    const int yrow = 4 * g + (c >> 2);
     int trc[NT];
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) trc[mt] = trb + (((2 * mt + ((c & 3) >> 1)) ^ yrow) << 4);
+    for (int mt = 0; mt < NT; ++mt)
+      trc[mt] = yrow * RB + (((4 * (mt >> 1) + (c & 3)) ^ kswz<DK>(yrow)) << 4) + 8 * (mt & 1);
     // V fragments (B operand of T' V) by transposing reads of the [64][16]
     // v tile: lane 16 g + L reads the 4 values of row 4 g + L / 4 starting at
     // column 4 (L % 4); lane c then holds V[t0 .. t0 + 3][c].
@@ -161,7 +177,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int pp = 0; pp < KT; ++pp) kf[mt][pp] = frag_at<T>(kt + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+        for (int pp = 0; pp < KT; ++pp) kf[mt][pp] = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
       f32x4 aa[4], cw[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -242,7 +258,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p.final_state[st_base + (int64_t)c * DK + 16 * mt + 4 * g + i] = S[mt][i];
+        for (int i = 0; i < 4; ++i) p.final_state[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] = S[mt][i];
     }
   } else if (wave == 1) {
     // ------------------------------------------------- out(s), o(s - 1)
@@ -275,7 +291,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int pp = 0; pp < KT; ++pp) qf[mt][pp] = frag_at<T>(qt + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+        for (int pp = 0; pp < KT; ++pp) qf[mt][pp] = *reinterpret_cast<const f8 *>(qt + mt * 16 * RB + fo[pp]);
 #pragma unroll
       for (int pp = 0; pp < KT; ++pp) Sf[pp] = *reinterpret_cast<const f8 *>(&sm.sfrag[s & 1][lane * SF + 8 * pp]);
 #pragma unroll
@@ -293,66 +309,84 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
     });
   } else {
     // ------------------------------------------------------------- loads
-    // Per-lane byte offsets of the copies inside a chunk (rows of the q/k
-    // tiles with the XOR swizzle, v half rows, record bytes); a full chunk is
-    // then a block-uniform base plus these, with no per-step address math.
-    uint32_t koff[NI], qoff[NI], voff[2];
+    // Six loader waves with at most 8 copies each per step: waves 2, 3 copy
+    // the halves of the k tile, waves 4, 5 those of the q tile, waves 6, 7
+    // the halves of the record and of the v slice. Spreading the copies over
+    // many waves keeps more of them in flight per CU.
+    const int role = wave - 2;
+    if (role < 4) {
+      constexpr int NH = NI / 2;
+      const bool isk = role < 2;
+      const int i0 = (role & 1) * NH;
+      const int64_t st = isk ? p.sk_t : p.sq_t;
+      const T *xb = isk ? kb : qb;
+      // per-lane byte offsets of the copies inside a full chunk (rows of the
+      // tile with the XOR swizzle): a block-uniform base plus these
+      uint32_t xoff[NH];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int b = 1024 * i + 16 * lane;
-      const int r = b / RB, jp = (b % RB) >> 4;
-      const int j = jp ^ (r & (CPR - 1));
-      koff[i] = (uint32_t)(((int64_t)r * p.sk_t + 8 * j) * (int64_t)sizeof(T));
-      qoff[i] = (uint32_t)(((int64_t)r * p.sq_t + 8 * j) * (int64_t)sizeof(T));
-    }
+      for (int i = 0; i < NH; ++i) {
+        const int b = 1024 * (i0 + i) + 16 * lane;
+        const int r = b / RB, jp = (b % RB) >> 4;
+        const int j = jp ^ kswz<DK>(r);
+        xoff[i] = (uint32_t)(((int64_t)r * st + 8 * j) * (int64_t)sizeof(T));
+      }
+      for_steps(Nc, [&](int s, auto SL) {
+        lds_barrier();
+        constexpr int sl = (decltype(SL)::v + 2) % 3;  // slot of chunk s + 2
+        const int cl = s + 2;
+        const bool issue = cl < Nc;
+        unsigned char *xt = (isk ? sm.k[sl] : sm.q[sl]) + 1024 * i0;
+        if (issue) {
+          const int nr = rows_of(cl);
+          const int64_t t0 = (int64_t)cl * BT;
+          if (nr == BT) {
+            const unsigned char *xg = reinterpret_cast<const unsigned char *>(xb + t0 * st);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      voff[i] = (uint32_t)(((int64_t)(32 * i + (lane >> 1)) * p.sv_t + 8 * (lane & 1)) * (int64_t)sizeof(T));
-    for_steps(Nc, [&](int s, auto SL) {
-      lds_barrier();
-      constexpr int sl = (decltype(SL)::v + 2) % 3;  // slot of chunk s + 2
-      const int cl = s + 2;
-      const bool issue = cl < Nc;
-      if (issue) {
-        const int nr = rows_of(cl);
-        const int64_t t0 = (int64_t)cl * BT;
-        if (nr == BT) {
-          const unsigned char *kg = reinterpret_cast<const unsigned char *>(kb + t0 * p.sk_t);
-          const unsigned char *qg = reinterpret_cast<const unsigned char *>(qb + t0 * p.sq_t);
-          const unsigned char *vg = reinterpret_cast<const unsigned char *>(vb + t0 * p.sv_t);
+            for (int i = 0; i < NH; ++i) g2l16(xg + xoff[i], xt + 1024 * i);
+          } else {
+            // last, partial chunk: rows past its end repeat its last row
 #pragma unroll
-          for (int i = 0; i < NI; ++i) {
-            g2l16(kg + koff[i], sm.k[sl] + 1024 * i);
-            g2l16(qg + qoff[i], sm.q[sl] + 1024 * i);
-          }
-#pragma unroll
-          for (int i = 0; i < 2; ++i) g2l16(vg + voff[i], reinterpret_cast<unsigned char *>(sm.v[sl]) + 1024 * i);
-        } else {
-          // last, partial chunk: rows past its end repeat its last row
-#pragma unroll
-          for (int i = 0; i < NI; ++i) {
-            const int b = 1024 * i + 16 * lane;
-            const int r = b / RB, jp = (b % RB) >> 4;
-            const int j = jp ^ (r & (CPR - 1));
-            const int rr = r < nr ? r : nr - 1;
-            g2l16(kb + (t0 + rr) * p.sk_t + 8 * j, sm.k[sl] + 1024 * i);
-            g2l16(qb + (t0 + rr) * p.sq_t + 8 * j, sm.q[sl] + 1024 * i);
-          }
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int r = 32 * i + (lane >> 1);
-            const int rr = r < nr ? r : nr - 1;
-            g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane & 1), reinterpret_cast<unsigned char *>(sm.v[sl]) + 1024 * i);
+            for (int i = 0; i < NH; ++i) {
+              const int b = 1024 * (i0 + i) + 16 * lane;
+              const int r = b / RB, jp = (b % RB) >> 4;
+              const int j = jp ^ kswz<DK>(r);
+              const int rr = r < nr ? r : nr - 1;
+              g2l16(xb + (t0 + rr) * st + 8 * j, xt + 1024 * i);
+            }
           }
         }
-        const unsigned char *rg = recb + (int64_t)cl * rec_stride;
+        // The copies of the previous step must be complete before the next
+        // barrier publishes them; this step's stay in flight.
+        if (issue) wait_vm<NH>(); else wait_vm<0>();
+      });
+    } else {
+      constexpr int NRH = NR / 2;
+      const int half = role - 4;
+      const uint32_t voff =
+          (uint32_t)(((int64_t)(32 * half + (lane >> 1)) * p.sv_t + 8 * (lane & 1)) * (int64_t)sizeof(T));
+      for_steps(Nc, [&](int s, auto SL) {
+        lds_barrier();
+        constexpr int sl = (decltype(SL)::v + 2) % 3;
+        const int cl = s + 2;
+        const bool issue = cl < Nc;
+        if (issue) {
+          const int nr = rows_of(cl);
+          const int64_t t0 = (int64_t)cl * BT;
+          const unsigned char *rg = recb + (int64_t)cl * rec_stride + 1024 * NRH * half;
 #pragma unroll
-        for (int i = 0; i < NR; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * i);
-      }
-      // The copies of the previous step must be complete before the next
-      // barrier publishes them; this step's stay in flight.
-      if (issue) wait_vm<NLOAD>(); else wait_vm<0>();
-    });
+          for (int i = 0; i < NRH; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * (NRH * half + i));
+          unsigned char *vt = reinterpret_cast<unsigned char *>(sm.v[sl]) + 1024 * half;
+          if (nr == BT) {
+            g2l16(reinterpret_cast<const unsigned char *>(vb + t0 * p.sv_t) + voff, vt);
+          } else {
+            const int r = 32 * half + (lane >> 1);
+            const int rr = r < nr ? r : nr - 1;
+            g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane & 1), vt);
+          }
+        }
+        if (issue) wait_vm<NRH + 1>(); else wait_vm<0>();
+      });
+    }
   }
 }
 

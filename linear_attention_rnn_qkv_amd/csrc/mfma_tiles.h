@@ -69,7 +69,12 @@ __device__ __forceinline__ void lds_fence_wave() {
 __device__ __forceinline__ void g2l16(const void *gptr, unsigned char *lds) {
   __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)(lds_u8 *)lds, 16, 0, 0);
 }
-// s_waitcnt vmcnt(N) for a count known only at run time (one of few values).
+// 4 bytes per lane from global memory into LDS (lane i writes lds + 4 i).
+__device__ __forceinline__ void g2l4(const void *gptr, unsigned char *lds) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)(lds_u8 *)lds, 4, 0, 0);
+}
+// s_waitcnt vmcnt(N): returns once at most N vector memory operations of this
+// wave are outstanding (they complete in issue order).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
