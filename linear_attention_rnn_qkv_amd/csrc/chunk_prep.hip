@@ -20,9 +20,10 @@
 // column by block column on the FP32 MFMA. Results go to the caller's workspace in MFMA
 // operand order (layout in gdn_internal.h).
 //
-// One workgroup (four wavefronts) per (chunk, value head); q/k/v of the GQA
-// group are read in place. Packed sequences: a one-block kernel first turns
-// cu_seqlens into chunk offsets.
+// One workgroup per (chunk, NV value heads of one GQA group), four wavefronts
+// per value head: the NV heads share the q/k tiles, which are read once (NV = 2
+// when the group size is even). Packed sequences: a one-block kernel first
+// turns cu_seqlens into chunk offsets.
 #include "gdn_internal.h"
 #include "mfma_tiles.h"
 
@@ -30,7 +31,7 @@ namespace gdn {
 namespace {
 
 constexpr int BT = 64;
-constexpr int kPrepThreads = 256;
+constexpr int kPrepThreads = 256;  // per value head
 
 // cu_chunks[n] = sum over sequences m < n of ceil(len_m / 64).
 __global__ __launch_bounds__(256) void chunk_index_kernel(const int32_t *__restrict__ cu, int64_t n,
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(256) void chunk_index_kernel(const int32_t *__restr
 
 enum { P_GAM = 0, P_BT, P_EG, P_ECG, P_RK, P_RQ, P_N };
 
-template <int DK>
+template <int DK, int NV>
 struct PrepLds {
   static constexpr int RB = DK * 2;    // bytes per q/k row (16-bit elements)
   static constexpr int CPR = RB / 16;  // 16-byte chunks per row
@@ -79,30 +80,32 @@ struct PrepLds {
   };
   union alignas(16) {
     Tiles x;                           // k and q rows, dead after the products
-    Mats m;
+    Mats m[NV];                        // per value head
   } u;
-  alignas(16) float fac[P_N][BT];
-  float eC;
+  alignas(16) float fac[NV][P_N][BT];
+  float eC[NV];
 };
 
 __device__ __forceinline__ int blk(int mi, int ni) { return mi * (mi + 1) / 2 + ni; }
 
-template <typename T, int DK>
-__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
+template <typename T, int DK, int NV>
+__global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_eu(6))) void chunk_prep_kernel(
     ChunkArgs p) {
   using MF = M2<T>;
   using f8 = typename MF::f8;
   using v4 = typename MF::v4;
-  using SM = PrepLds<DK>;
+  using SM = PrepLds<DK, NV>;
   constexpr int KT = DK / 32;
   constexpr int RB = SM::RB, CPR = SM::CPR;
   __shared__ SM sm;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, hv = threadIdx.x >> 8, wave = (threadIdx.x >> 6) & 3;
   const int g = lane >> 4, c = lane & 15;
   const int64_t gc = blockIdx.x;
-  const int64_t h = blockIdx.y;
+  const int64_t h = blockIdx.y * NV + hv;
   const int64_t hk = h / (p.Hv / p.Hqk);
+  float(&fac)[P_N][BT] = sm.fac[hv];
+  typename SM::Mats &mm = sm.u.m[hv];
   int64_t ch, bos, L, brow;
   if (p.cu_seqlens) {
     const int32_t *cuc = p.cu_chunks;
@@ -129,36 +132,57 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
   const T *kb = static_cast<const T *>(p.k) + brow * p.sk_b + hk * p.sk_h + t0 * p.sk_t;
   unsigned char *rec = p.ws_rec + (gc * p.Hv + h) * kRecBytes;
 
+  // g and beta of the chunk (wave 2 of each head), issued first so that their
+  // latency overlaps the tile loads
+  const float *gp = p.g + brow * p.sg_b + h * p.sg_h + t0 * p.sg_t;
+  const float *bp = p.beta + brow * p.sbt_b + h * p.sbt_h + t0 * p.sbt_t;
+  float graw = 0.f, braw = 0.f;
+  if (wave == 2) {
+    const int64_t li = lane < nr ? lane : nr - 1;
+    graw = gp[li * p.sg_t];
+    braw = bp[li * p.sbt_t];
+  }
+
   // 1. k and q tiles, rows past the chunk repeat its last row (their beta
-  //    and g are zero, which makes them inert).
-  for (int i = threadIdx.x; i < BT * CPR; i += kPrepThreads) {
+  //    and g are zero, which makes them inert). All loads are issued before
+  //    the first LDS write.
+  constexpr int NLD = BT * CPR / (kPrepThreads * NV);
+  static_assert(NLD * kPrepThreads * NV == BT * CPR, "tile split");
+  uint4 kr[NLD], qr[NLD];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int i = threadIdx.x + u * kPrepThreads * NV;
     const int r = i / CPR, jp = i % CPR;
-    const int j = jp ^ (r & (CPR - 1));
+    const int j = jp ^ kswz<DK>(r);
     const int rr = r < nr ? r : nr - 1;
-    *reinterpret_cast<uint4 *>(sm.u.x.k + r * RB + jp * 16) =
-        *reinterpret_cast<const uint4 *>(kb + (int64_t)rr * p.sk_t + 8 * j);
-    *reinterpret_cast<uint4 *>(sm.u.x.q + r * RB + jp * 16) =
-        *reinterpret_cast<const uint4 *>(qb + (int64_t)rr * p.sq_t + 8 * j);
+    kr[u] = *reinterpret_cast<const uint4 *>(kb + (int64_t)rr * p.sk_t + 8 * j);
+    qr[u] = *reinterpret_cast<const uint4 *>(qb + (int64_t)rr * p.sq_t + 8 * j);
+  }
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int i = threadIdx.x + u * kPrepThreads * NV;
+    const int r = i / CPR, jp = i % CPR;
+    *reinterpret_cast<uint4 *>(sm.u.x.k + r * RB + jp * 16) = kr[u];
+    *reinterpret_cast<uint4 *>(sm.u.x.q + r * RB + jp * 16) = qr[u];
   }
   __syncthreads();
 
-  int fo[KT][2];
+  // Fragments over dk: lane group g of k step pp holds dk 32 pp + 8 g .. + 7 of
+  // row c (one 16-byte read); both operands of the products use this order.
+  int fo[KT];
 #pragma unroll
-  for (int pp = 0; pp < KT; ++pp)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      fo[pp][hh] = c * RB + (((4 * pp + (g >> 1) + 2 * hh) ^ (c & (CPR - 1))) << 4) + 8 * (g & 1);
+  for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
 
   // 2. K K^T (wave 0), P^T = K Q^T (wave 1), gamma and decay factors (wave 2)
   f32x4 acc[10];
 #pragma unroll
   for (int t = 0; t < 10; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (wave == 0) {
-#pragma unroll 2  // a full unroll hoists every fragment load: 150 VGPRs at DK = 128
+#pragma unroll 1  // unrolling hoists the fragment loads of later k steps (VGPRs)
     for (int pp = 0; pp < KT; ++pp) {
       f8 kf[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) kf[mt] = frag_at<T>(sm.u.x.k + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+      for (int mt = 0; mt < 4; ++mt) kf[mt] = *reinterpret_cast<const f8 *>(sm.u.x.k + mt * 16 * RB + fo[pp]);
       int t = 0;
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
@@ -172,19 +196,19 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
         const f32x4 d = acc[blk(mi, mi)];
         const int e = c & 3;
         const float sq = e == 0 ? d[0] : e == 1 ? d[1] : e == 2 ? d[2] : d[3];
-        sm.fac[P_RK][16 * mi + c] = p.use_l2 ? rsqrtf(sq + p.l2_eps) : 1.f;
+        fac[P_RK][16 * mi + c] = p.use_l2 ? rsqrtf(sq + p.l2_eps) : 1.f;
       }
     }
   } else if (wave == 1) {
     // lane (g, c) of tile (mi, ni): q_{16 mi + c} . k_{16 ni + 4 g + j}
     float ssqs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2  // a full unroll hoists every fragment load: 150 VGPRs at DK = 128
+#pragma unroll 1  // unrolling hoists the fragment loads of later k steps (VGPRs)
     for (int pp = 0; pp < KT; ++pp) {
       f8 kf[4], qf[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        kf[mt] = frag_at<T>(sm.u.x.k + mt * 16 * RB, fo[pp][0], fo[pp][1]);
-        qf[mt] = frag_at<T>(sm.u.x.q + mt * 16 * RB, fo[pp][0], fo[pp][1]);
+        kf[mt] = *reinterpret_cast<const f8 *>(sm.u.x.k + mt * 16 * RB + fo[pp]);
+        qf[mt] = *reinterpret_cast<const f8 *>(sm.u.x.q + mt * 16 * RB + fo[pp]);
         ssqs[mt] = sumsq8<T>(qf[mt], ssqs[mt]);
       }
       int t = 0;
@@ -198,25 +222,23 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
       float ssq = ssqs[mt];
       ssq += __shfl_xor(ssq, 16, 64);
       ssq += __shfl_xor(ssq, 32, 64);
-      if (g == 0) sm.fac[P_RQ][16 * mt + c] = p.use_l2 ? rsqrtf(ssq + p.l2_eps) : 1.f;
+      if (g == 0) fac[P_RQ][16 * mt + c] = p.use_l2 ? rsqrtf(ssq + p.l2_eps) : 1.f;
     }
   } else if (wave == 2) {
-    const float *gp = p.g + brow * p.sg_b + h * p.sg_h + t0 * p.sg_t;
-    const float *bp = p.beta + brow * p.sbt_b + h * p.sbt_h + t0 * p.sbt_t;
     const bool live = lane < nr;
-    float gam = live ? gp[(int64_t)lane * p.sg_t] : 0.f;
-    const float bv = live ? bp[(int64_t)lane * p.sbt_t] : 0.f;
+    float gam = live ? graw : 0.f;
+    const float bv = live ? braw : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float o = __shfl_up(gam, off, 64);
       if (lane >= off) gam += o;
     }
     const float gC = __shfl(gam, 63, 64);
-    sm.fac[P_GAM][lane] = gam;
-    sm.fac[P_BT][lane] = bv;
-    sm.fac[P_EG][lane] = fast_exp(gam);
-    sm.fac[P_ECG][lane] = fast_exp(gC - gam);
-    if (lane == 0) sm.eC = fast_exp(gC);
+    fac[P_GAM][lane] = gam;
+    fac[P_BT][lane] = bv;
+    fac[P_EG][lane] = fast_exp(gam);
+    fac[P_ECG][lane] = fast_exp(gC - gam);
+    if (lane == 0) sm.eC[hv] = fast_exp(gC);
   }
   __syncthreads();  // the q tile is dead from here on (its space holds A, T)
 
@@ -229,34 +251,34 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mi + 4 * g + i;
-        rowf[i] = sm.fac[P_BT][r] * sm.fac[P_RK][r];
+        rowf[i] = fac[P_BT][r] * fac[P_RK][r];
       }
 #pragma unroll
       for (int ni = 0; ni <= mi; ++ni, ++t) {
         const int col = 16 * ni + c;
-        const float kc = sm.fac[P_RK][col], gcol = sm.fac[P_GAM][col];
+        const float kc = fac[P_RK][col], gcol = fac[P_GAM][col];
         f32x4 av;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * mi + 4 * g + i;
-          const float e = fast_exp(sm.fac[P_GAM][r] - gcol);
+          const float e = fast_exp(fac[P_GAM][r] - gcol);
           av[i] = col < r ? rowf[i] * kc * e * acc[t][i] : 0.f;
         }
-        *reinterpret_cast<f32x4 *>(&sm.u.m.a[t][c * 16 + 4 * g]) = av;  // column c, rows 4g..
+        *reinterpret_cast<f32x4 *>(&mm.a[t][c * 16 + 4 * g]) = av;  // column c, rows 4g..
       }
     }
   } else if (wave == 1) {
     // P^T tile (mi, ni), lane (g, c): row r = 16 mi + c, key i = 16 ni + 4 g + j
     auto ptile = [&](int mi, int ni) -> f32x4 {
       const int r = 16 * mi + c;
-      const float rowf = p.scale * sm.fac[P_RQ][r], gr = sm.fac[P_GAM][r];
+      const float rowf = p.scale * fac[P_RQ][r], gr = fac[P_GAM][r];
       const f32x4 a = acc[blk(mi, ni)];
       f32x4 pv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 16 * ni + 4 * g + j;
-        const float e = fast_exp(gr - sm.fac[P_GAM][i]);
-        pv[j] = i <= r ? rowf * sm.fac[P_RK][i] * e * a[j] : 0.f;
+        const float e = fast_exp(gr - fac[P_GAM][i]);
+        pv[j] = i <= r ? rowf * fac[P_RK][i] * e * a[j] : 0.f;
       }
       return pv;
     };
@@ -270,12 +292,12 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
     }
   } else if (wave == 2) {
     float *rf = reinterpret_cast<float *>(rec + kRecF);
-    const float bt = sm.fac[P_BT][lane], eg = sm.fac[P_EG][lane], rk = sm.fac[P_RK][lane];
+    const float bt = fac[P_BT][lane], eg = fac[P_EG][lane], rk = fac[P_RK][lane];
     rf[0 * BT + lane] = eg * rk;                                 // aa (beta is in T')
-    rf[1 * BT + lane] = sm.fac[P_ECG][lane] * rk;                // cw
-    rf[2 * BT + lane] = p.scale * eg * sm.fac[P_RQ][lane];       // zc
+    rf[1 * BT + lane] = fac[P_ECG][lane] * rk;                // cw
+    rf[2 * BT + lane] = p.scale * eg * fac[P_RQ][lane];       // zc
     rf[3 * BT + lane] = bt;                                      // beta
-    if (lane == 0) rf[4 * BT] = sm.eC;
+    if (lane == 0) rf[4 * BT] = sm.eC[hv];
   }
   __syncthreads();
 
@@ -283,7 +305,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
   //    of (I + A_jj) x = e_c by forward substitution in FP32.
   {
     const int j = wave;
-    const float *ab = sm.u.m.a[blk(j, j)];
+    const float *ab = mm.a[blk(j, j)];
     if (lane < 16) {
       float x[16];
 #pragma unroll
@@ -296,7 +318,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 #pragma unroll
         for (int r = i + 1; r < 16; ++r) x[r] -= col4[r >> 2][r & 3] * x[i];
       }
-      float *tb = sm.u.m.t[blk(j, j)];
+      float *tb = mm.t[blk(j, j)];
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         *reinterpret_cast<f32x4 *>(&tb[lane * 16 + 4 * v]) = f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
@@ -308,13 +330,13 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
   //    B[4 kk + g][c]; the result lane holds rows 4 g .. 4 g + 3 of column c).
   {
     const int j = wave;
-    float *xs = sm.u.m.x[j];
+    float *xs = mm.x[j];
     for (int i = j + 1; i < 4; ++i) {
       // X = sum_{k=j}^{i-1} A_ik T_kj
       f32x4 xv = {0.f, 0.f, 0.f, 0.f};
       for (int k = j; k < i; ++k) {
-        const float *ab = sm.u.m.a[blk(i, k)];
-        const float *tb = sm.u.m.t[blk(k, j)];
+        const float *ab = mm.a[blk(i, k)];
+        const float *tb = mm.t[blk(k, j)];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           xv = __builtin_amdgcn_mfma_f32_16x16x4f32(ab[(4 * kk + g) * 16 + c], tb[c * 16 + 4 * kk + g], xv, 0, 0, 0);
@@ -322,12 +344,12 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
       *reinterpret_cast<f32x4 *>(&xs[c * 16 + 4 * g]) = xv;
       lds_fence_wave();
       // T_ij = -T_ii X
-      const float *ti = sm.u.m.t[blk(i, i)];
+      const float *ti = mm.t[blk(i, i)];
       f32x4 tv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         tv = __builtin_amdgcn_mfma_f32_16x16x4f32(ti[(4 * kk + g) * 16 + c], xs[c * 16 + 4 * kk + g], tv, 0, 0, 0);
-      *reinterpret_cast<f32x4 *>(&sm.u.m.t[blk(i, j)][c * 16 + 4 * g]) = -tv;
+      *reinterpret_cast<f32x4 *>(&mm.t[blk(i, j)][c * 16 + 4 * g]) = -tv;
       lds_fence_wave();
     }
   }
@@ -343,10 +365,10 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
       const int nb = 2 * q + hh;  // block column
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (nb <= mt) {
-        const float *tb = sm.u.m.t[blk(mt, nb)];
+        const float *tb = mm.t[blk(mt, nb)];
 #pragma unroll
         for (int i = 0; i < 4; ++i)  // T[row c][col 4g + i] beta_col
-          v[i] = tb[(4 * g + i) * 16 + c] * sm.fac[P_BT][16 * nb + 4 * g + i];
+          v[i] = tb[(4 * g + i) * 16 + c] * fac[P_BT][16 * nb + 4 * g + i];
       }
       if (hh == 0) lo = v; else hi = v;
     }
@@ -356,13 +378,18 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(
 
 template <typename T, int DK>
 hipError_t launch_prep(const ChunkArgs &a, hipStream_t s) {
+  const bool pair = (a.Hv / a.Hqk) % 2 == 0;
   if (a.cu_seqlens) {
     hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, s, a.cu_seqlens, a.n_seqs, a.cu_chunks);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 grid((unsigned)a.chunk_bound, (unsigned)a.Hv);
-  hipLaunchKernelGGL((chunk_prep_kernel<T, DK>), grid, dim3(kPrepThreads), 0, s, a);
+  if (pair)
+    hipLaunchKernelGGL((chunk_prep_kernel<T, DK, 2>), dim3((unsigned)a.chunk_bound, (unsigned)(a.Hv / 2)),
+                       dim3(2 * kPrepThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((chunk_prep_kernel<T, DK, 1>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hv),
+                       dim3(kPrepThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -54,15 +54,6 @@ __device__ __forceinline__ constexpr int dk_of(int mt, int r) {
   return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3);
 }
 
-// XOR swizzle of the 16-byte units of a q/k tile row. It keeps the row reads
-// of the fragments (16 rows, one unit) and the transposing reads of the
-// state update (4 rows x 4 units per 16 lanes) free of bank conflicts.
-template <int DK>
-__device__ __forceinline__ constexpr int kswz(int r) {
-  if constexpr (DK == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
 // fragment index of (row tile mt, k pair q) in a record matrix
 __device__ __forceinline__ constexpr int frag_id(int mt, int q) { return q == 0 ? mt : 2 + mt; }
 

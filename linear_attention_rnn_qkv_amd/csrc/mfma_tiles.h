@@ -69,10 +69,15 @@ __device__ __forceinline__ void lds_fence_wave() {
 __device__ __forceinline__ void g2l16(const void *gptr, unsigned char *lds) {
   __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)(lds_u8 *)lds, 16, 0, 0);
 }
-// 4 bytes per lane from global memory into LDS (lane i writes lds + 4 i).
-__device__ __forceinline__ void g2l4(const void *gptr, unsigned char *lds) {
-  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)(lds_u8 *)lds, 4, 0, 0);
+// XOR swizzle of the 16-byte units of a q/k tile row (DK 16-bit values per
+// row). It keeps 16-byte fragment reads of 16 consecutive rows and
+// transposing reads of 4 rows x 4 units per 16 lanes free of bank conflicts.
+template <int DK>
+__device__ __forceinline__ constexpr int kswz(int r) {
+  if constexpr (DK == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
+
 // s_waitcnt vmcnt(N): returns once at most N vector memory operations of this
 // wave are outstanding (they complete in issue order).
 template <int N>

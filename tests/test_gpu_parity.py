@@ -169,6 +169,26 @@ def test_chunk_rule_no_decay(cfg, path):
     H.assert_close(f64(fin), rfin, TAU[s.act], "final state")
 
 
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("dk,hqk,hv", [(64, 2, 8), (128, 4, 4), (64, 3, 3)], ids=["dk64-G4", "dk128-G1", "dk64-G1"])
+def test_chunk_rule_head_dims_and_group_sizes(dk, hqk, hv, path):
+    # The two-kernel path has separate code for dk 64 and 128 and for odd and
+    # even GQA group sizes; each is checked against the oracle with a state in
+    # and out.
+    over = {"T": 300, "Hqk": hqk, "Hv": hv, "dk": dk}
+    s, x, qkv, g, beta = _stress_inputs(3, over, 0)
+    q, k, v = H.split_qkv(qkv, s)
+    qd, kd, vd, gd, bd, _ = _gpu_stage_inputs(s, qkv, g, beta, None)
+    S0 = synth.randn((s.B, s.Hv, s.dv, s.dk), "f32", 78).cuda() * 0.5
+    scale = s.dk ** -0.5
+    o, fin = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, scale, True, 1e-6, None, S0, output_final_state=True,
+                                    workspace=PATHS[path])
+    torch.cuda.synchronize()
+    ro, rfin = O.gated_delta_rule(q, k, v, g, beta, scale=scale, initial_state=f64(S0), output_final_state=True)
+    H.assert_close(f64(o), O.round_to(ro, s.act), TAU[s.act], "o")
+    H.assert_close(f64(fin), rfin, TAU[s.act], "final state")
+
+
 def test_chunk_rule_orthonormal_keys_retrieve_values():
     # Stress set S3 in FP32: g = 0, beta = 1 writes of orthonormal keys in the
     # first chunk, then beta = 0 reads in the second chunk with q = k_j must
