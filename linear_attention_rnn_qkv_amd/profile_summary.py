@@ -133,13 +133,24 @@ def main() -> int:
               "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
     for k, v in sorted(stats.items(), key=lambda kv: -kv[1]["avg_us"]):
         lines.append(f"| {k} | {v['calls']} | {v['avg_us']:.1f} | {v['min_us']:.1f} | {v['max_us']:.1f} |")
+    # stages of several launches ('+'-joined names): the sum of their averages
+    for key in algo:
+        parts = key.split("+")
+        if len(parts) > 1 and all(q in stats for q in parts):
+            lines.append(f"| {key} (sum) | - | {sum(stats[q]['avg_us'] for q in parts):.1f} | - | - |")
     lines += ["", "## HBM bytes per launch (rocprofv3 --pmc, one counter per run)", "",
               f"Calibration: a 1 GiB device copy reads FETCH_SIZE = {cf[copy_key[0]]:.0f} KiB and "
               f"WRITE_SIZE = {cw[copy_key[0]]:.0f} KiB per dispatch, so bytes = FETCH_SIZE x 1024 x "
               f"{kf:.4f} and WRITE_SIZE x 1024 x {kw:.4f}.", "",
               "| kernel | source hash | read GB | write GB | total GB | algorithmic GB | ratio |",
               "|---|---|---|---|---|---|---|"]
-    for k, v in traffic["kernels"].items():
+    rows = dict(traffic["kernels"])
+    for key in algo:
+        parts = key.split("+")
+        if len(parts) > 1 and all(q in rows for q in parts):
+            rows[key] = {"source_hash": "+".join(rows[q]["source_hash"][:6] for q in parts),
+                         **{f: sum(rows[q][f] for q in parts) for f in ("read_bytes", "write_bytes", "bytes")}}
+    for k, v in rows.items():
         al = algo.get(k)
         ratio = f"{v['bytes'] / al:.3f}" if al else "-"
         alt = f"{al / 1e9:.3f}" if al else "-"
