@@ -189,6 +189,39 @@ def test_chunk_rule_head_dims_and_group_sizes(dk, hqk, hv, path):
     H.assert_close(f64(fin), rfin, TAU[s.act], "final state")
 
 
+@pytest.mark.parametrize("path", list(PATHS))
+def test_chunk_rule_empty_and_one_token_sequences(path):
+    # Packed sequences of length 0 and 1 next to partial and full chunks: an
+    # empty sequence hands its initial state through unchanged.
+    s, x, qkv, g, beta = _stress_inputs(4, {"lengths": (0, 70, 0, 1, 64), "Hqk": 2, "Hv": 4}, 0)
+    q, k, v = H.split_qkv(qkv, s)
+    cu = H.cu_of(x)
+    qd, kd, vd, gd, bd, cud = _gpu_stage_inputs(s, qkv, g, beta, cu)
+    S0 = synth.randn((len(cu) - 1, s.Hv, s.dv, s.dk), "f32", 79).cuda() * 0.5
+    o, fin = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.1, True, 1e-6, cud, S0, output_final_state=True,
+                                    workspace=PATHS[path])
+    torch.cuda.synchronize()
+    ro, rfin = O.gated_delta_rule(q, k, v, g, beta, scale=0.1, cu_seqlens=cu, initial_state=f64(S0),
+                                  output_final_state=True)
+    H.assert_close(f64(o), O.round_to(ro, s.act), TAU[s.act], "o")
+    H.assert_close(f64(fin), rfin, TAU[s.act], "final state")
+    assert torch.equal(fin[0], S0[0]) and torch.equal(fin[2], S0[2])
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("T", [1, 63, 65])
+def test_chunk_rule_short_sequences(T, path):
+    s, x, qkv, g, beta = _stress_inputs(3, {"T": T, "Hqk": 2, "Hv": 4}, 0)
+    q, k, v = H.split_qkv(qkv, s)
+    qd, kd, vd, gd, bd, _ = _gpu_stage_inputs(s, qkv, g, beta, None)
+    o, fin = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.1, True, 1e-6, output_final_state=True,
+                                    workspace=PATHS[path])
+    torch.cuda.synchronize()
+    ro, rfin = O.gated_delta_rule(q, k, v, g, beta, scale=0.1, output_final_state=True)
+    H.assert_close(f64(o), O.round_to(ro, s.act), TAU[s.act], "o")
+    H.assert_close(f64(fin), rfin, TAU[s.act], "final state")
+
+
 def test_chunk_rule_orthonormal_keys_retrieve_values():
     # Stress set S3 in FP32: g = 0, beta = 1 writes of orthonormal keys in the
     # first chunk, then beta = 0 reads in the second chunk with q = k_j must
