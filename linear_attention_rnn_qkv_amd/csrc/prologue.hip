@@ -14,17 +14,15 @@
 // (Gated DeltaNet's parameterisation; the pages do not print them).
 //
 // Layout and schedule (HBM-bound): a thread owns VEC consecutive channels and
-// walks a tile of 128 tokens in batches of 8, double-buffered so the next
-// batch's loads (raw packed vectors) are in flight during the arithmetic of
-// the current one, convolving each batch over a register window that holds
-// the three
-// previous inputs in registers, so each input element is read once (plus a
-// 3-token halo per tile) and each output written once with VEC-wide
-// coalesced accesses. History is zero
-// before every sequence start: batch rows are sequences; with cu_seqlens the
-// thread finds the boundaries inside its tile from the offsets. The blocks
-// of the first channel column also compute beta and g for all value heads of
-// their tile.
+// walks a tile of 128 tokens in batches of 8, double-buffered so that the
+// next batch's loads (raw packed vectors) are in flight during the arithmetic
+// of the current one. It convolves over a window that keeps the three previous
+// inputs in registers, so each input element is read once (plus a 3-token halo
+// per tile) and each output is written once, with VEC-wide coalesced accesses.
+// History is zero before every sequence start: batch rows are sequences; with
+// cu_seqlens the thread finds the boundaries inside its tile from the offsets.
+// The blocks of a token tile also compute beta and g of its tokens, each an
+// equal share of the (token, head) pairs.
 #include <limits.h>
 
 #include "device_common.h"
@@ -57,12 +55,12 @@ __device__ __forceinline__ float silu_log2(float y2) {
   return y2 * __builtin_amdgcn_rcpf(__builtin_fmaf(kLog2e, __builtin_amdgcn_exp2f(-y2), kLog2e));
 }
 
+// beta and g of the tile's (token, head) pairs [lo, hi) in token-major order
 template <typename T>
-__device__ void beta_g_tile(const PrologueArgs &p, int64_t b, int64_t t0, int64_t t1) {
+__device__ void beta_g_tile(const PrologueArgs &p, int64_t b, int64_t t0, int64_t lo, int64_t hi) {
   const T *pa = static_cast<const T *>(p.a);
   const T *pb = static_cast<const T *>(p.b);
-  const int64_t n = (t1 - t0) * p.Hv;
-  for (int64_t i = threadIdx.x; i < n; i += kThreads) {
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) {
     const int64_t t = t0 + i / p.Hv, h = i % p.Hv;
     const float bb = f(pb[b * p.sb_b + t * p.sb_t + h * p.sb_h]);
     const float aa = f(pa[b * p.sa_b + t * p.sa_t + h * p.sa_h]);
@@ -251,8 +249,11 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs p) {
       compute_batch(tb, ra);
     }
   }
-  // beta and g of the tile's tokens, by the first channel block
-  if (cb == 0) beta_g_tile<T>(p, b, t0, t1);
+  // beta and g of the tile's tokens, split evenly over its channel blocks
+  {
+    const int64_t n = (t1 - t0) * p.Hv, ncb = gridDim.y;
+    beta_g_tile<T>(p, b, t0, n * cb / ncb, n * (cb + 1) / ncb);
+  }
 }
 
 template <typename T, int VEC>
