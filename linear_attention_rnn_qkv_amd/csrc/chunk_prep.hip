@@ -16,14 +16,17 @@
 // This is the WY/UT form of the delta rule (Yang et al., NeurIPS 2024) with
 // the gating of Gated DeltaNet (ICLR 2025); only non-positive exponents are
 // evaluated. T is computed in FP32: the four 16 x 16 diagonal blocks by
-// forward substitution, then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj block
-// column by block column on the FP32 MFMA. Results go to the caller's workspace in MFMA
-// operand order (layout in gdn_internal.h).
+// forward substitution, then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, one
+// block column per wave, on the FP32 MFMA with the column's blocks kept in
+// registers. Results go to the caller's workspace in MFMA operand order
+// (layout in gdn_internal.h).
 //
 // One workgroup per (chunk, NV value heads of one GQA group), four wavefronts
 // per value head: the NV heads share the q/k tiles, which are read once (NV = 2
 // when the group size is even). Packed sequences: a one-block kernel first
 // turns cu_seqlens into chunk offsets.
+#include <type_traits>
+
 #include "gdn_internal.h"
 #include "mfma_tiles.h"
 
@@ -72,7 +75,6 @@ struct PrepLds {
   struct Mats {                        // lower 16 x 16 blocks, FP32, column-major
     float a[10][256];                  //   a[blk][col * 16 + row] = A block
     float t[10][256];                  //   same for T
-    float x[4][256];                   //   per-wave scratch
   };
   struct Tiles {
     unsigned char k[TILE];
@@ -242,43 +244,59 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
   }
   __syncthreads();  // the q tile is dead from here on (its space holds A, T)
 
-  // 3. A blocks (wave 0), P fragments (wave 1), row factors (wave 2)
+  // 3. A blocks (wave 0), P fragments (wave 1), row factors (wave 2). The
+  //    row and column factors are read once as vectors; every exponential is
+  //    evaluated (with its argument clamped to <= 0, exact where the mask keeps
+  //    it since gamma is non-increasing) and masked by a select, so the
+  //    epilogues have no branches.
   if (wave == 0) {
+    // lane (g, c) of tile (mi, ni): rows r = 16 mi + 4 g + i, column 16 ni + c
+    float gcol[4], kcol[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      gcol[m] = fac[P_GAM][16 * m + c];
+      kcol[m] = fac[P_RK][16 * m + c];
+    }
     int t = 0;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-      f32x4 rowf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mi + 4 * g + i;
-        rowf[i] = fac[P_BT][r] * fac[P_RK][r];
-      }
+      const f32x4 gr = *reinterpret_cast<const f32x4 *>(&fac[P_GAM][16 * mi + 4 * g]);
+      const f32x4 br = *reinterpret_cast<const f32x4 *>(&fac[P_BT][16 * mi + 4 * g]) *
+                       *reinterpret_cast<const f32x4 *>(&fac[P_RK][16 * mi + 4 * g]);
 #pragma unroll
       for (int ni = 0; ni <= mi; ++ni, ++t) {
         const int col = 16 * ni + c;
-        const float kc = fac[P_RK][col], gcol = fac[P_GAM][col];
         f32x4 av;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * mi + 4 * g + i;
-          const float e = fast_exp(fac[P_GAM][r] - gcol);
-          av[i] = col < r ? rowf[i] * kc * e * acc[t][i] : 0.f;
+          const float e = fast_exp(fminf(gr[i] - gcol[ni], 0.f));
+          const float x = br[i] * kcol[ni] * e * acc[t][i];
+          av[i] = col < r ? x : 0.f;
         }
         *reinterpret_cast<f32x4 *>(&mm.a[t][c * 16 + 4 * g]) = av;  // column c, rows 4g..
       }
     }
   } else if (wave == 1) {
     // P^T tile (mi, ni), lane (g, c): row r = 16 mi + c, key i = 16 ni + 4 g + j
+    float grow[4], qrow[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      grow[m] = fac[P_GAM][16 * m + c];
+      qrow[m] = p.scale * fac[P_RQ][16 * m + c];
+    }
     auto ptile = [&](int mi, int ni) -> f32x4 {
       const int r = 16 * mi + c;
-      const float rowf = p.scale * fac[P_RQ][r], gr = fac[P_GAM][r];
       const f32x4 a = acc[blk(mi, ni)];
+      const f32x4 gk = *reinterpret_cast<const f32x4 *>(&fac[P_GAM][16 * ni + 4 * g]);
+      const f32x4 rkk = *reinterpret_cast<const f32x4 *>(&fac[P_RK][16 * ni + 4 * g]);
       f32x4 pv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 16 * ni + 4 * g + j;
-        const float e = fast_exp(gr - fac[P_GAM][i]);
-        pv[j] = i <= r ? rowf * fac[P_RK][i] * e * a[j] : 0.f;
+        const float e = fast_exp(fminf(grow[mi] - gk[j], 0.f));
+        const float x = qrow[mi] * rkk[j] * e * a[j];
+        pv[j] = i <= r ? x : 0.f;
       }
       return pv;
     };
@@ -325,32 +343,47 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
     }
   }
   __syncthreads();
-  //    Off-diagonal blocks: wave j owns block column j. 16 x 16 x 16 products
-  //    on the FP32 MFMA (16x16x4: lane 16 g + c supplies A[c][4 kk + g] and
-  //    B[4 kk + g][c]; the result lane holds rows 4 g .. 4 g + 3 of column c).
+  //    Off-diagonal blocks: wave j owns block column j and computes, for
+  //    i = j + 1 .. 3, T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj on the FP32 MFMA
+  //    (16x16x4). The k index of MFMA kk in lane group g is 4 g + kk, so a
+  //    16 x 16 accumulator (lane (g, c) holds rows 4 g .. 4 g + 3 of column c)
+  //    is directly the B operand of the next product: X and the T_kj of this
+  //    column stay in registers, and only A blocks and the diagonal T blocks
+  //    (phase 4) are read from LDS.
   {
-    const int j = wave;
-    float *xs = mm.x[j];
-    for (int i = j + 1; i < 4; ++i) {
-      // X = sum_{k=j}^{i-1} A_ik T_kj
-      f32x4 xv = {0.f, 0.f, 0.f, 0.f};
-      for (int k = j; k < i; ++k) {
-        const float *ab = mm.a[blk(i, k)];
-        const float *tb = mm.t[blk(k, j)];
+    auto column = [&](auto jt) {
+      constexpr int J = decltype(jt)::value;
+      if constexpr (J < 3) {
+        // B operand T_JJ[4 g + kk][c]: column-major, four consecutive floats
+        const f32x4 tjj = *reinterpret_cast<const f32x4 *>(&mm.t[blk(J, J)][c * 16 + 4 * g]);
+        f32x4 tk[4];  // T_kJ, k > J
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          xv = __builtin_amdgcn_mfma_f32_16x16x4f32(ab[(4 * kk + g) * 16 + c], tb[c * 16 + 4 * kk + g], xv, 0, 0, 0);
+        for (int i = J + 1; i < 4; ++i) {
+          f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = J; k < i; ++k) {
+            const float *ab = mm.a[blk(i, k)];
+            const f32x4 bk = k == J ? tjj : tk[k];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+              xv = __builtin_amdgcn_mfma_f32_16x16x4f32(ab[(4 * g + kk) * 16 + c], bk[kk], xv, 0, 0, 0);
+          }
+          const float *ti = mm.t[blk(i, i)];
+          f32x4 tv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            tv = __builtin_amdgcn_mfma_f32_16x16x4f32(ti[(4 * g + kk) * 16 + c], xv[kk], tv, 0, 0, 0);
+          tk[i] = -tv;
+        }
+#pragma unroll
+        for (int i = J + 1; i < 4; ++i) *reinterpret_cast<f32x4 *>(&mm.t[blk(i, J)][c * 16 + 4 * g]) = tk[i];
       }
-      *reinterpret_cast<f32x4 *>(&xs[c * 16 + 4 * g]) = xv;
-      lds_fence_wave();
-      // T_ij = -T_ii X
-      const float *ti = mm.t[blk(i, i)];
-      f32x4 tv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        tv = __builtin_amdgcn_mfma_f32_16x16x4f32(ti[(4 * kk + g) * 16 + c], xs[c * 16 + 4 * kk + g], tv, 0, 0, 0);
-      *reinterpret_cast<f32x4 *>(&mm.t[blk(i, j)][c * 16 + 4 * g]) = -tv;
-      lds_fence_wave();
+    };
+    switch (wave) {
+      case 0: column(std::integral_constant<int, 0>{}); break;
+      case 1: column(std::integral_constant<int, 1>{}); break;
+      case 2: column(std::integral_constant<int, 2>{}); break;
+      default: break;
     }
   }
   __syncthreads();
