@@ -73,8 +73,9 @@ struct PrepLds {
   static constexpr int CPR = RB / 16;  // 16-byte chunks per row
   static constexpr int TILE = BT * RB;
   struct Mats {                        // lower 16 x 16 blocks, FP32, column-major
-    float a[10][256];                  //   a[blk][col * 16 + row] = A block
-    float t[10][256];                  //   same for T
+    float a[10][256];                  //   a[blk][col * 16 + row] = A block; the
+                                       //   off-diagonal T blocks replace it
+    float t[4][256];                   //   diagonal T blocks
   };
   struct Tiles {
     unsigned char k[TILE];
@@ -91,7 +92,7 @@ struct PrepLds {
 __device__ __forceinline__ int blk(int mi, int ni) { return mi * (mi + 1) / 2 + ni; }
 
 template <typename T, int DK, int NV>
-__global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_eu(6))) void chunk_prep_kernel(
+__global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_eu(NV == 2 ? 8 : 6))) void chunk_prep_kernel(
     ChunkArgs p) {
   using MF = M2<T>;
   using f8 = typename MF::f8;
@@ -134,12 +135,14 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
   const T *kb = static_cast<const T *>(p.k) + brow * p.sk_b + hk * p.sk_h + t0 * p.sk_t;
   unsigned char *rec = p.ws_rec + (gc * p.Hv + h) * kRecBytes;
 
-  // g and beta of the chunk (wave 2 of each head), issued first so that their
-  // latency overlaps the tile loads
-  const float *gp = p.g + brow * p.sg_b + h * p.sg_h + t0 * p.sg_t;
-  const float *bp = p.beta + brow * p.sbt_b + h * p.sbt_h + t0 * p.sbt_t;
+  // g and beta of value head hv' of the block, loaded by workgroup wave hv'
+  // and issued first so that their latency overlaps the tile loads
+  const int wid = threadIdx.x >> 6;
   float graw = 0.f, braw = 0.f;
-  if (wave == 2) {
+  if (wid < NV) {
+    const int64_t hs = blockIdx.y * NV + wid;
+    const float *gp = p.g + brow * p.sg_b + hs * p.sg_h + t0 * p.sg_t;
+    const float *bp = p.beta + brow * p.sbt_b + hs * p.sbt_h + t0 * p.sbt_t;
     const int64_t li = lane < nr ? lane : nr - 1;
     graw = gp[li * p.sg_t];
     braw = bp[li * p.sbt_t];
@@ -175,58 +178,95 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
 #pragma unroll
   for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
 
-  // 2. K K^T (wave 0), P^T = K Q^T (wave 1), gamma and decay factors (wave 2)
-  f32x4 acc[10];
+  // 2. The lower 16 x 16 tiles of K K^T and of P^T = K Q^T, which the NV
+  //    value heads share, are computed once per workgroup in eight groups of
+  //    tiles: Gram / q-form x {(0,0) (1,0) (1,1)}, {(2,0) (2,1) (2,2)},
+  //    {(3,0) (3,1)}, {(3,2) (3,3)}; wave w takes groups w and w + 4 NV.
+  //    1/|k| comes from the diagonal Gram tiles, 1/|q| from the q fragments.
+  //    Waves 0 .. NV - 1 also scan gamma of their value head.
+  // Gram tile (mi, ni): lane (g, c) holds k_{16 mi + 4 g + j} . k_{16 ni + c};
+  // q-form tile: q_{16 mi + c} . k_{16 ni + 4 g + j}.
+  constexpr int NW = 4 * NV;
+  constexpr int NGW = (8 + NW - 1) / NW;  // groups per wave
+  f32x4 acc[NGW][3];
+  // tile list of group sub: sub 0: (0,0) (1,0) (1,1); sub 1: (2,0) (2,1) (2,2);
+  // sub 2: (3,0) (3,1); sub 3: (3,2) (3,3)
+  auto tile_mi = [](int sub, int t) { return sub == 0 ? (t == 0 ? 0 : 1) : sub == 1 ? 2 : 3; };
+  auto tile_ni = [](int sub, int t) { return sub == 0 ? (t == 0 ? 0 : t - 1) : sub == 1 ? t : sub == 2 ? t : 2 + t; };
+  auto products = [&](auto sub_t, auto qform_t, f32x4(&ac)[3]) {
+    constexpr int SUB = decltype(sub_t)::value;
+    constexpr bool QF = decltype(qform_t)::value;
+    constexpr int NTL = SUB < 2 ? 3 : 2;
+    constexpr int MLO = SUB == 0 ? 0 : SUB == 1 ? 2 : 3, MHI = SUB == 0 ? 1 : SUB == 1 ? 2 : 3;
 #pragma unroll
-  for (int t = 0; t < 10; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (wave == 0) {
+    for (int t = 0; t < 3; ++t) ac[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float ssq[2] = {0.f, 0.f};
 #pragma unroll 1  // unrolling hoists the fragment loads of later k steps (VGPRs)
     for (int pp = 0; pp < KT; ++pp) {
-      f8 kf[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) kf[mt] = *reinterpret_cast<const f8 *>(sm.u.x.k + mt * 16 * RB + fo[pp]);
-      int t = 0;
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(kf[mi], kf[ni], acc[t]);
-    }
-    // 1/|k| from the diagonal: lane (g, c) with c / 4 == g holds |k_{16 mi + c}|^2
-    if ((c >> 2) == g) {
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const f32x4 d = acc[blk(mi, mi)];
-        const int e = c & 3;
-        const float sq = e == 0 ? d[0] : e == 1 ? d[1] : e == 2 ? d[2] : d[3];
-        fac[P_RK][16 * mi + c] = p.use_l2 ? rsqrtf(sq + p.l2_eps) : 1.f;
-      }
-    }
-  } else if (wave == 1) {
-    // lane (g, c) of tile (mi, ni): q_{16 mi + c} . k_{16 ni + 4 g + j}
-    float ssqs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1  // unrolling hoists the fragment loads of later k steps (VGPRs)
-    for (int pp = 0; pp < KT; ++pp) {
-      f8 kf[4], qf[4];
+      f8 kf[4], qf[2];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        kf[mt] = *reinterpret_cast<const f8 *>(sm.u.x.k + mt * 16 * RB + fo[pp]);
-        qf[mt] = *reinterpret_cast<const f8 *>(sm.u.x.q + mt * 16 * RB + fo[pp]);
-        ssqs[mt] = sumsq8<T>(qf[mt], ssqs[mt]);
+        bool used = false;
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) used |= tile_ni(SUB, t) == mt || (!QF && tile_mi(SUB, t) == mt);
+        if (used) kf[mt] = *reinterpret_cast<const f8 *>(sm.u.x.k + mt * 16 * RB + fo[pp]);
       }
-      int t = 0;
+      if constexpr (QF) {
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+        for (int m = MLO; m <= MHI; ++m) {
+          qf[m - MLO] = *reinterpret_cast<const f8 *>(sm.u.x.q + m * 16 * RB + fo[pp]);
+          ssq[m - MLO] = sumsq8<T>(qf[m - MLO], ssq[m - MLO]);
+        }
+      }
 #pragma unroll
-        for (int ni = 0; ni <= mi; ++ni, ++t) acc[t] = MF::k32(kf[ni], qf[mi], acc[t]);
+      for (int t = 0; t < NTL; ++t) {
+        const int mi = tile_mi(SUB, t), ni = tile_ni(SUB, t);
+        if constexpr (QF) ac[t] = MF::k32(kf[ni], qf[mi - MLO], ac[t]);
+        else ac[t] = MF::k32(kf[mi], kf[ni], ac[t]);
+      }
     }
+    if constexpr (QF) {
+      if constexpr (SUB != 3) {  // sub 3 shares row 3 with sub 2
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      float ssq = ssqs[mt];
-      ssq += __shfl_xor(ssq, 16, 64);
-      ssq += __shfl_xor(ssq, 32, 64);
-      if (g == 0) fac[P_RQ][16 * mt + c] = p.use_l2 ? rsqrtf(ssq + p.l2_eps) : 1.f;
+        for (int m = MLO; m <= MHI; ++m) {
+          float sq = ssq[m - MLO];
+          sq += __shfl_xor(sq, 16, 64);
+          sq += __shfl_xor(sq, 32, 64);
+          const float rq = p.use_l2 ? rsqrtf(sq + p.l2_eps) : 1.f;
+          if (g == 0)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) sm.fac[v][P_RQ][16 * m + c] = rq;
+        }
+      }
+    } else if ((c >> 2) == g) {
+      // lane (g, c) with c / 4 == g holds |k_{16 mi + c}|^2 in a diagonal tile
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        const int mi = tile_mi(SUB, t), ni = tile_ni(SUB, t);
+        if (mi != ni) continue;
+        const int e = c & 3;
+        const float sq = e == 0 ? ac[t][0] : e == 1 ? ac[t][1] : e == 2 ? ac[t][2] : ac[t][3];
+        const float rk = p.use_l2 ? rsqrtf(sq + p.l2_eps) : 1.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) sm.fac[v][P_RK][16 * mi + c] = rk;
+      }
     }
-  } else if (wave == 2) {
+  };
+  auto group = [&](int gid, auto fn) {
+    switch (gid) {
+      case 0: fn(std::integral_constant<int, 0>{}, std::false_type{}); break;
+      case 1: fn(std::integral_constant<int, 1>{}, std::false_type{}); break;
+      case 2: fn(std::integral_constant<int, 2>{}, std::false_type{}); break;
+      case 3: fn(std::integral_constant<int, 3>{}, std::false_type{}); break;
+      case 4: fn(std::integral_constant<int, 0>{}, std::true_type{}); break;
+      case 5: fn(std::integral_constant<int, 1>{}, std::true_type{}); break;
+      case 6: fn(std::integral_constant<int, 2>{}, std::true_type{}); break;
+      case 7: fn(std::integral_constant<int, 3>{}, std::true_type{}); break;
+      default: break;
+    }
+  };
+  if (wid < NV) {
+    float(&fv)[P_N][BT] = sm.fac[wid];
     const bool live = lane < nr;
     float gam = live ? graw : 0.f;
     const float bv = live ? braw : 0.f;
@@ -236,86 +276,101 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
       if (lane >= off) gam += o;
     }
     const float gC = __shfl(gam, 63, 64);
-    fac[P_GAM][lane] = gam;
-    fac[P_BT][lane] = bv;
-    fac[P_EG][lane] = fast_exp(gam);
-    fac[P_ECG][lane] = fast_exp(gC - gam);
-    if (lane == 0) sm.eC[hv] = fast_exp(gC);
+    fv[P_GAM][lane] = gam;
+    fv[P_BT][lane] = bv;
+    fv[P_EG][lane] = fast_exp(gam);
+    fv[P_ECG][lane] = fast_exp(gC - gam);
+    if (lane == 0) sm.eC[wid] = fast_exp(gC);
   }
-  __syncthreads();  // the q tile is dead from here on (its space holds A, T)
+#pragma unroll
+  for (int u = 0; u < NGW; ++u)
+    group(wid + u * NW, [&](auto sub_t, auto qform_t) { products(sub_t, qform_t, acc[u]); });
+  __syncthreads();  // the q/k tiles are dead from here on (their space holds A, T)
 
-  // 3. A blocks (wave 0), P fragments (wave 1), row factors (wave 2). The
-  //    row and column factors are read once as vectors; every exponential is
-  //    evaluated (with its argument clamped to <= 0, exact where the mask keeps
-  //    it since gamma is non-increasing) and masked by a select, so the
-  //    epilogues have no branches.
-  if (wave == 0) {
-    // lane (g, c) of tile (mi, ni): rows r = 16 mi + 4 g + i, column 16 ni + c
-    float gcol[4], kcol[4];
+  // 3. For every value head of the block: A blocks (Gram groups) and P
+  //    fragments (q-form groups) of the tiles each wave holds; the row
+  //    factors to the record (wave hv'). The row and column factors are read
+  //    once as vectors; every exponential is evaluated (with its argument
+  //    clamped to <= 0, exact where the mask keeps it since gamma is
+  //    non-increasing) and masked by a select, so the epilogues have no
+  //    branches.
+  auto epilogue = [&](auto sub_t, auto qform_t, const f32x4(&ac)[3], int v) {
+    constexpr int SUB = decltype(sub_t)::value;
+    constexpr bool QF = decltype(qform_t)::value;
+    constexpr int NTL = SUB < 2 ? 3 : 2;
+    const float(&fv)[P_N][BT] = sm.fac[v];
+    if constexpr (!QF) {
+      // lane (g, c) of tile (mi, ni): rows r = 16 mi + 4 g + i, column 16 ni + c
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      gcol[m] = fac[P_GAM][16 * m + c];
-      kcol[m] = fac[P_RK][16 * m + c];
-    }
-    int t = 0;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const f32x4 gr = *reinterpret_cast<const f32x4 *>(&fac[P_GAM][16 * mi + 4 * g]);
-      const f32x4 br = *reinterpret_cast<const f32x4 *>(&fac[P_BT][16 * mi + 4 * g]) *
-                       *reinterpret_cast<const f32x4 *>(&fac[P_RK][16 * mi + 4 * g]);
-#pragma unroll
-      for (int ni = 0; ni <= mi; ++ni, ++t) {
+      for (int t = 0; t < NTL; ++t) {
+        const int mi = tile_mi(SUB, t), ni = tile_ni(SUB, t);
         const int col = 16 * ni + c;
+        const float gcol = fv[P_GAM][col], kcol = fv[P_RK][col];
+        const f32x4 gr = *reinterpret_cast<const f32x4 *>(&fv[P_GAM][16 * mi + 4 * g]);
+        const f32x4 br = *reinterpret_cast<const f32x4 *>(&fv[P_BT][16 * mi + 4 * g]) *
+                         *reinterpret_cast<const f32x4 *>(&fv[P_RK][16 * mi + 4 * g]);
         f32x4 av;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * mi + 4 * g + i;
-          const float e = fast_exp(fminf(gr[i] - gcol[ni], 0.f));
-          const float x = br[i] * kcol[ni] * e * acc[t][i];
+          const float e = fast_exp(fminf(gr[i] - gcol, 0.f));
+          const float x = br[i] * kcol * e * ac[t][i];
           av[i] = col < r ? x : 0.f;
         }
-        *reinterpret_cast<f32x4 *>(&mm.a[t][c * 16 + 4 * g]) = av;  // column c, rows 4g..
+        *reinterpret_cast<f32x4 *>(&sm.u.m[v].a[blk(mi, ni)][c * 16 + 4 * g]) = av;  // column c, rows 4g..
+      }
+    } else {
+      // P fragment f = (mt, q) = cat(tile (mt, 2 q), tile (mt, 2 q + 1)); lane
+      // (g, c) of tile (mi, ni): query row r = 16 mi + c, key i = 16 ni + 4 g + j.
+      unsigned char *rv = p.ws_rec + (gc * p.Hv + blockIdx.y * NV + v) * kRecBytes;
+      f32x4 pv[3];
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) {
+        const int mi = tile_mi(SUB, t), ni = tile_ni(SUB, t);
+        const int r = 16 * mi + c;
+        const float grow = fv[P_GAM][r], srq = p.scale * fv[P_RQ][r];
+        const f32x4 gk = *reinterpret_cast<const f32x4 *>(&fv[P_GAM][16 * ni + 4 * g]);
+        const f32x4 rkk = *reinterpret_cast<const f32x4 *>(&fv[P_RK][16 * ni + 4 * g]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * ni + 4 * g + j;
+          const float e = fast_exp(fminf(grow - gk[j], 0.f));
+          const float x = srq * rkk[j] * e * ac[t][j];
+          pv[t][j] = i <= r ? x : 0.f;
+        }
+      }
+      const v4 z4 = cvt4<T>(f32x4{0.f, 0.f, 0.f, 0.f});
+      auto put = [&](int f, const v4 &lo, const v4 &hi) {
+        *reinterpret_cast<f8 *>(rv + kRecP + f * 1024 + lane * 16) = cat8<T>(lo, hi);
+      };
+      if constexpr (SUB == 0) {
+        put(0, cvt4<T>(pv[0]), z4);                   // f0 = (0,0) | 0
+        put(1, cvt4<T>(pv[1]), cvt4<T>(pv[2]));       // f1 = (1,0) | (1,1)
+      } else if constexpr (SUB == 1) {
+        put(2, cvt4<T>(pv[0]), cvt4<T>(pv[1]));       // f2 = (2,0) | (2,1)
+        put(4, cvt4<T>(pv[2]), z4);                   // f4 = (2,2) | 0
+      } else if constexpr (SUB == 2) {
+        put(3, cvt4<T>(pv[0]), cvt4<T>(pv[1]));       // f3 = (3,0) | (3,1)
+      } else {
+        put(5, cvt4<T>(pv[0]), cvt4<T>(pv[1]));       // f5 = (3,2) | (3,3)
       }
     }
-  } else if (wave == 1) {
-    // P^T tile (mi, ni), lane (g, c): row r = 16 mi + c, key i = 16 ni + 4 g + j
-    float grow[4], qrow[4];
+  };
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      grow[m] = fac[P_GAM][16 * m + c];
-      qrow[m] = p.scale * fac[P_RQ][16 * m + c];
-    }
-    auto ptile = [&](int mi, int ni) -> f32x4 {
-      const int r = 16 * mi + c;
-      const f32x4 a = acc[blk(mi, ni)];
-      const f32x4 gk = *reinterpret_cast<const f32x4 *>(&fac[P_GAM][16 * ni + 4 * g]);
-      const f32x4 rkk = *reinterpret_cast<const f32x4 *>(&fac[P_RK][16 * ni + 4 * g]);
-      f32x4 pv;
+  for (int u = 0; u < NGW; ++u)
+    group(wid + u * NW, [&](auto sub_t, auto qform_t) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 16 * ni + 4 * g + j;
-        const float e = fast_exp(fminf(grow[mi] - gk[j], 0.f));
-        const float x = qrow[mi] * rkk[j] * e * a[j];
-        pv[j] = i <= r ? x : 0.f;
-      }
-      return pv;
-    };
-    const v4 z4 = cvt4<T>(f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-    for (int f = 0; f < 6; ++f) {
-      const int mt = f < 4 ? f : f - 2, q = f < 4 ? 0 : 1;
-      const v4 lo = cvt4<T>(ptile(mt, 2 * q));
-      const v4 hi = (2 * q + 1 <= mt) ? cvt4<T>(ptile(mt, 2 * q + 1)) : z4;
-      *reinterpret_cast<f8 *>(rec + kRecP + f * 1024 + lane * 16) = cat8<T>(lo, hi);
-    }
-  } else if (wave == 2) {
-    float *rf = reinterpret_cast<float *>(rec + kRecF);
-    const float bt = fac[P_BT][lane], eg = fac[P_EG][lane], rk = fac[P_RK][lane];
-    rf[0 * BT + lane] = eg * rk;                                 // aa (beta is in T')
-    rf[1 * BT + lane] = fac[P_ECG][lane] * rk;                // cw
-    rf[2 * BT + lane] = p.scale * eg * fac[P_RQ][lane];       // zc
-    rf[3 * BT + lane] = bt;                                      // beta
-    if (lane == 0) rf[4 * BT] = sm.eC[hv];
+      for (int v = 0; v < NV; ++v) epilogue(sub_t, qform_t, acc[u], v);
+    });
+  if (wid < NV) {
+    const float(&fv)[P_N][BT] = sm.fac[wid];
+    float *rf = reinterpret_cast<float *>(p.ws_rec + (gc * p.Hv + blockIdx.y * NV + wid) * kRecBytes + kRecF);
+    const float eg = fv[P_EG][lane], rk = fv[P_RK][lane];
+    rf[0 * BT + lane] = eg * rk;                          // aa (beta is in T')
+    rf[1 * BT + lane] = fv[P_ECG][lane] * rk;             // cw
+    rf[2 * BT + lane] = p.scale * eg * fv[P_RQ][lane];    // zc
+    rf[3 * BT + lane] = fv[P_BT][lane];                   // beta
+    if (lane == 0) rf[4 * BT] = sm.eC[wid];
   }
   __syncthreads();
 
@@ -336,7 +391,7 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
 #pragma unroll
         for (int r = i + 1; r < 16; ++r) x[r] -= col4[r >> 2][r & 3] * x[i];
       }
-      float *tb = mm.t[blk(j, j)];
+      float *tb = mm.t[j];
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         *reinterpret_cast<f32x4 *>(&tb[lane * 16 + 4 * v]) = f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
@@ -348,43 +403,52 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
   //    (16x16x4). The k index of MFMA kk in lane group g is 4 g + kk, so a
   //    16 x 16 accumulator (lane (g, c) holds rows 4 g .. 4 g + 3 of column c)
   //    is directly the B operand of the next product: X and the T_kj of this
-  //    column stay in registers, and only A blocks and the diagonal T blocks
-  //    (phase 4) are read from LDS.
+  //    column stay in registers. The A blocks and diagonal T blocks it needs
+  //    are read into registers first; after a barrier the off-diagonal T
+  //    blocks are written over the A blocks.
   {
-    auto column = [&](auto jt) {
+    f32x4 tjj;           // B operand T_JJ[4 g + kk][c] (column-major, four consecutive floats)
+    float aop[4][4][4];  // A_ik[c][4 g + kk] for i > k >= J
+    float tio[4][4];     // T_ii[c][4 g + kk] for i > J
+    auto load = [&](auto jt) {
       constexpr int J = decltype(jt)::value;
-      if constexpr (J < 3) {
-        // B operand T_JJ[4 g + kk][c]: column-major, four consecutive floats
-        const f32x4 tjj = *reinterpret_cast<const f32x4 *>(&mm.t[blk(J, J)][c * 16 + 4 * g]);
-        f32x4 tk[4];  // T_kJ, k > J
+      tjj = *reinterpret_cast<const f32x4 *>(&mm.t[J][c * 16 + 4 * g]);
 #pragma unroll
-        for (int i = J + 1; i < 4; ++i) {
-          f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+      for (int i = J + 1; i < 4; ++i) {
 #pragma unroll
-          for (int k = J; k < i; ++k) {
-            const float *ab = mm.a[blk(i, k)];
-            const f32x4 bk = k == J ? tjj : tk[k];
+        for (int kk = 0; kk < 4; ++kk) tio[i][kk] = mm.t[i][(4 * g + kk) * 16 + c];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-              xv = __builtin_amdgcn_mfma_f32_16x16x4f32(ab[(4 * g + kk) * 16 + c], bk[kk], xv, 0, 0, 0);
-          }
-          const float *ti = mm.t[blk(i, i)];
-          f32x4 tv = {0.f, 0.f, 0.f, 0.f};
+        for (int k = J; k < i; ++k)
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            tv = __builtin_amdgcn_mfma_f32_16x16x4f32(ti[(4 * g + kk) * 16 + c], xv[kk], tv, 0, 0, 0);
-          tk[i] = -tv;
-        }
-#pragma unroll
-        for (int i = J + 1; i < 4; ++i) *reinterpret_cast<f32x4 *>(&mm.t[blk(i, J)][c * 16 + 4 * g]) = tk[i];
+          for (int kk = 0; kk < 4; ++kk) aop[i][k][kk] = mm.a[blk(i, k)][(4 * g + kk) * 16 + c];
       }
     };
-    switch (wave) {
-      case 0: column(std::integral_constant<int, 0>{}); break;
-      case 1: column(std::integral_constant<int, 1>{}); break;
-      case 2: column(std::integral_constant<int, 2>{}); break;
-      default: break;
-    }
+    auto solve = [&](auto jt) {
+      constexpr int J = decltype(jt)::value;
+      f32x4 tk[4];  // T_kJ, k > J
+#pragma unroll
+      for (int i = J + 1; i < 4; ++i) {
+        f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = J; k < i; ++k) {
+          const f32x4 bk = k == J ? tjj : tk[k];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) xv = __builtin_amdgcn_mfma_f32_16x16x4f32(aop[i][k][kk], bk[kk], xv, 0, 0, 0);
+        }
+        f32x4 tv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) tv = __builtin_amdgcn_mfma_f32_16x16x4f32(tio[i][kk], xv[kk], tv, 0, 0, 0);
+        tk[i] = -tv;
+      }
+#pragma unroll
+      for (int i = J + 1; i < 4; ++i) *reinterpret_cast<f32x4 *>(&mm.a[blk(i, J)][c * 16 + 4 * g]) = tk[i];
+    };
+    using J0 = std::integral_constant<int, 0>;
+    using J1 = std::integral_constant<int, 1>;
+    using J2 = std::integral_constant<int, 2>;
+    if (wave == 0) load(J0{}); else if (wave == 1) load(J1{}); else if (wave == 2) load(J2{});
+    __syncthreads();  // every A operand is in registers: T may replace A
+    if (wave == 0) solve(J0{}); else if (wave == 1) solve(J1{}); else if (wave == 2) solve(J2{});
   }
   __syncthreads();
 
@@ -398,7 +462,7 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
       const int nb = 2 * q + hh;  // block column
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (nb <= mt) {
-        const float *tb = mm.t[blk(mt, nb)];
+        const float *tb = nb == mt ? mm.t[mt] : mm.a[blk(mt, nb)];
 #pragma unroll
         for (int i = 0; i < 4; ++i)  // T[row c][col 4g + i] beta_col
           v[i] = tb[(4 * g + i) * 16 + c] * fac[P_BT][16 * nb + 4 * g + i];
