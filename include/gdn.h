@@ -12,6 +12,8 @@
  *   gdn_gated_norm_fwd  output RMSNorm, materialised in the activation dtype,
  *                       then the FP32 SiLU-gate multiply
  *   gdn_layer_fwd       the three stages in order, in a caller workspace
+ *   gdn_decode_fwd      one recurrent step per sequence (conv cache and FP32
+ *                       state updated in place), all stages in one kernel
  *
  * Sources (web pages):
  *   [P1] Megatron-LM pull request "perf(gated_delta_net): fold q/k L2-norm
@@ -242,6 +244,52 @@ gdn_status gdn_layer_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
                          float l2_eps, float rms_eps, void *workspace,
                          size_t workspace_bytes, const gdn_tensor *out,
                          void *stream);
+
+/*
+ * gdn_decode_fwd - one recurrent decode step of the layer core: a new token
+ * for each of N independent sequences, each carrying a conv cache and a
+ * state. It is the recurrent form of the same layer (the gated delta rule of
+ * Gated DeltaNet for one token, the conv of [P3] Summary at the newest token,
+ * the gated norm of [P2] Execution and numerical behavior). Per sequence n:
+ *     window = (cache[n, 0], cache[n, 1], cache[n, 2], x[n])  per channel
+ *     z      = round_act(silu(bias + sum_j conv_w[:, j] * window[j]))
+ *     cache[n] <- (window[1], window[2], window[3])   (exact copies)
+ *     beta, g as in gdn_prologue_fwd; q, k L2-normalised if requested
+ *     S[n, h] <- e^g S (I - beta k k^T) + beta v k^T;  o = scale S q
+ *     out[n, h] = gdn_gated_norm_fwd of round_act(o)
+ * A sequence that starts from a zero cache and a zero state and takes T
+ * steps produces what gdn_layer_fwd produces for those T tokens, and its
+ * state is gdn_chunk_rule_fwd's final state.
+ *
+ *   x_q, x_k     [N, Hqk*dk] F32/BF16/F16 (the activation dtype), row stride
+ *                free, inner 1
+ *   x_v          [N, Hv*dv] act dtype, inner 1
+ *   conv_w       [C, 4] act dtype or F32, contiguous, C = 2 Hqk dk + Hv dv
+ *   conv_b       [C] act dtype or F32, contiguous, or NULL
+ *   conv_state   [N, 3, C] act dtype, inner 1: the last three inputs of every
+ *                channel, oldest first (zeros for a fresh sequence). Read and
+ *                updated in place.
+ *   a, b         [N, Hv] act dtype, inner 1
+ *   A_log, dt_bias [Hv] F32, contiguous
+ *   state        [N, Hv, dv, dk] F32, contiguous, 16-byte aligned (zeros for
+ *                a fresh sequence). Read and updated in place.
+ *   gate         [N, Hv, dv] act dtype or F32, inner 1
+ *   norm_w       [dv] F32/BF16/F16, contiguous
+ *   out          [N, Hv, dv] act dtype, contiguous
+ * conv_state, state and out must not overlap one another or any input.
+ * Supported: dk in {64, 128, 256}, 64 <= dv <= 512, Hv / Hqk <= 64,
+ * (Hv / Hqk) * dv <= 8192, N <= 65535 (else GDN_ERR_NOT_SUPPORTED).
+ */
+gdn_status gdn_decode_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
+                          const gdn_tensor *x_v, const gdn_tensor *conv_w,
+                          const gdn_tensor *conv_b,
+                          const gdn_tensor *conv_state, const gdn_tensor *a,
+                          const gdn_tensor *b, const gdn_tensor *A_log,
+                          const gdn_tensor *dt_bias, const gdn_tensor *state,
+                          const gdn_dims *dims, float scale,
+                          int32_t use_qk_l2norm_in_kernel, float l2_eps,
+                          const gdn_tensor *gate, const gdn_tensor *norm_w,
+                          float rms_eps, const gdn_tensor *out, void *stream);
 
 #ifdef __cplusplus
 }

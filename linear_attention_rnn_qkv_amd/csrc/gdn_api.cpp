@@ -407,6 +407,107 @@ gdn_status plan_norm(const gdn_tensor *o, const gdn_tensor *gate, const gdn_tens
   return GDN_OK;
 }
 
+gdn_status plan_decode(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
+                       const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *conv_state,
+                       const gdn_tensor *a, const gdn_tensor *b, const gdn_tensor *A_log,
+                       const gdn_tensor *dt_bias, const gdn_tensor *state, const gdn_tensor *gate,
+                       const gdn_tensor *norm_w, const gdn_dims *dims, float scale, int32_t use_l2, float l2_eps,
+                       float rms_eps, const gdn_tensor *out, gdn::DecodeArgs *P) {
+  TRY(check_dims(dims));
+  if (!x_q) return fail(GDN_ERR_INVALID_VALUE, "x_q: descriptor is NULL");
+  if (x_q->ndim != 2) return fail(GDN_ERR_INVALID_VALUE, "x_q: expected [N, Hqk*dk]");
+  const int64_t N = x_q->shape[0], Hv = dims->Hv, dv = dims->dv, dk = dims->dk;
+  const int64_t nq = dims->Hqk * dk, nv = Hv * dv, C = 2 * nq + nv;
+  if (N == 0) return fail(GDN_ERR_INVALID_VALUE, "empty input (N == 0)");
+  const int64_t sq[2] = {N, nq}, sv[2] = {N, nv}, sw[2] = {C, 4}, sc[1] = {C}, scs[3] = {N, 3, C};
+  const int64_t sab[2] = {N, Hv}, sh[1] = {Hv}, sst[4] = {N, Hv, dv, dk}, so[3] = {N, Hv, dv}, sn[1] = {dv};
+  TRY(check(x_q, "x_q", 2, sq));
+  const int32_t act = x_q->dtype;
+  if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "x_q: dtype must be F32, BF16 or F16");
+  TRY(check(x_k, "x_k", 2, sq));
+  TRY(check(x_v, "x_v", 2, sv));
+  TRY(check_dtype(x_k, "x_k", act));
+  TRY(check_dtype(x_v, "x_v", act));
+  TRY(check_inner(x_q, "x_q"));
+  TRY(check_inner(x_k, "x_k"));
+  TRY(check_inner(x_v, "x_v"));
+  TRY(check(conv_w, "conv_w", 2, sw));
+  if (conv_w->dtype != act && conv_w->dtype != GDN_F32)
+    return fail(GDN_ERR_INVALID_VALUE, "conv_w: dtype must be the activation dtype or F32");
+  TRY(check_contig(conv_w, "conv_w"));
+  if (conv_b) {
+    TRY(check(conv_b, "conv_b", 1, sc));
+    if (conv_b->dtype != act && conv_b->dtype != GDN_F32)
+      return fail(GDN_ERR_INVALID_VALUE, "conv_b: dtype must be the activation dtype or F32");
+    TRY(check_contig(conv_b, "conv_b"));
+  }
+  TRY(check(conv_state, "conv_state", 3, scs));
+  TRY(check_dtype(conv_state, "conv_state", act));
+  TRY(check_inner(conv_state, "conv_state"));
+  TRY(check(a, "a", 2, sab));
+  TRY(check(b, "b", 2, sab));
+  TRY(check_dtype(a, "a", act));
+  TRY(check_dtype(b, "b", act));
+  TRY(check_inner(a, "a"));
+  TRY(check_inner(b, "b"));
+  TRY(check(A_log, "A_log", 1, sh));
+  TRY(check(dt_bias, "dt_bias", 1, sh));
+  TRY(check_dtype(A_log, "A_log", GDN_F32));
+  TRY(check_dtype(dt_bias, "dt_bias", GDN_F32));
+  TRY(check_contig(A_log, "A_log"));
+  TRY(check_contig(dt_bias, "dt_bias"));
+  TRY(check(state, "state", 4, sst));
+  TRY(check_dtype(state, "state", GDN_F32));
+  TRY(check_contig(state, "state"));
+  TRY(check(gate, "gate", 3, so));
+  if (gate->dtype != act && gate->dtype != GDN_F32)
+    return fail(GDN_ERR_INVALID_VALUE, "gate: dtype must be the activation dtype or F32");
+  TRY(check_inner(gate, "gate"));
+  TRY(check(norm_w, "norm_w", 1, sn));
+  if (!is_act(norm_w->dtype)) return fail(GDN_ERR_INVALID_VALUE, "norm_w: dtype must be F32, BF16 or F16");
+  TRY(check_contig(norm_w, "norm_w"));
+  TRY(check(out, "out", 3, so));
+  TRY(check_dtype(out, "out", act));
+  TRY(check_contig(out, "out"));
+  if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps)) return fail(GDN_ERR_INVALID_VALUE, "l2_eps must be finite and >= 0");
+  if (!(rms_eps >= 0.f) || !std::isfinite(rms_eps))
+    return fail(GDN_ERR_INVALID_VALUE, "rms_eps must be finite and >= 0");
+  if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_VALUE, "scale must be finite");
+  // conv_state and state are updated in place; nothing else may alias them or out
+  const gdn_tensor *ins[] = {x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w};
+  const gdn_tensor *outs[] = {conv_state, state, out};
+  for (auto *o : outs)
+    for (auto *i : ins)
+      if (overlaps(o, i)) return fail(GDN_ERR_INVALID_VALUE, "an output or cache overlaps an input");
+  if (overlaps(conv_state, state) || overlaps(conv_state, out) || overlaps(state, out))
+    return fail(GDN_ERR_INVALID_VALUE, "conv_state, state and out must not overlap");
+  const int64_t G = Hv / dims->Hqk;
+  if (!gdn::decode_supported(dk, G, dv))
+    return fail(GDN_ERR_NOT_SUPPORTED, "decode: dk %lld, dv %lld, group size %lld not instantiated", (long long)dk,
+                (long long)dv, (long long)G);
+  if ((uintptr_t)state->data % 16) return fail(GDN_ERR_NOT_SUPPORTED, "state must be 16-byte aligned");
+  if (N > 65535 || dims->Hqk > 0x7fffffff) return fail(GDN_ERR_NOT_SUPPORTED, "decode: grid too large");
+
+  gdn::DecodeArgs &p = *P;
+  memset(&p, 0, sizeof p);
+  p.xq = x_q->data; p.xk = x_k->data; p.xv = x_v->data;
+  p.sxq = x_q->stride[0]; p.sxk = x_k->stride[0]; p.sxv = x_v->stride[0];
+  p.conv_w = conv_w->data; p.w_dtype = conv_w->dtype;
+  p.conv_b = conv_b ? conv_b->data : nullptr; p.b_dtype = conv_b ? conv_b->dtype : act;
+  p.conv_state = conv_state->data; p.scs_n = conv_state->stride[0]; p.scs_t = conv_state->stride[1];
+  p.a = a->data; p.b = b->data; p.sa = a->stride[0]; p.sb = b->stride[0];
+  p.A_log = static_cast<const float *>(A_log->data);
+  p.dt_bias = static_cast<const float *>(dt_bias->data);
+  p.state = static_cast<float *>(state->data);
+  p.gate = gate->data; p.sgate_n = gate->stride[0]; p.sgate_h = gate->stride[1]; p.gate_dtype = gate->dtype;
+  p.norm_w = norm_w->data; p.nw_dtype = norm_w->dtype;
+  p.out = out->data;
+  p.N = N; p.Hqk = dims->Hqk; p.dk = dk; p.Hv = Hv; p.dv = dv;
+  p.act = act; p.use_l2 = use_l2 ? 1 : 0;
+  p.scale = scale; p.l2_eps = l2_eps; p.rms_eps = rms_eps;
+  return GDN_OK;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace of the two-kernel chunk path: chunk offsets of packed sequences,
@@ -494,6 +595,19 @@ gdn_status gdn_gated_norm_fwd(const gdn_tensor *o, const gdn_tensor *gate, const
   gdn::NormArgs P;
   TRY(plan_norm(o, gate, weight, eps, out, &P));
   return launched(gdn::launch_gated_norm(P, (hipStream_t)stream), "gated norm");
+}
+
+gdn_status gdn_decode_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
+                          const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *conv_state,
+                          const gdn_tensor *a, const gdn_tensor *b, const gdn_tensor *A_log,
+                          const gdn_tensor *dt_bias, const gdn_tensor *state, const gdn_dims *dims, float scale,
+                          int32_t use_qk_l2norm_in_kernel, float l2_eps, const gdn_tensor *gate,
+                          const gdn_tensor *norm_w, float rms_eps, const gdn_tensor *out, void *stream) {
+  g_error.clear();
+  gdn::DecodeArgs p;
+  TRY(plan_decode(x_q, x_k, x_v, conv_w, conv_b, conv_state, a, b, A_log, dt_bias, state, gate, norm_w, dims,
+                  scale, use_qk_l2norm_in_kernel, l2_eps, rms_eps, out, &p));
+  return launched(gdn::launch_decode(p, static_cast<hipStream_t>(stream)), "decode");
 }
 
 size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *dims,

@@ -80,10 +80,36 @@ struct NormArgs {
   float eps;
 };
 
+// One decode step (a new token per sequence, conv cache and state updated in
+// place).
+struct DecodeArgs {
+  const void *xq, *xk, *xv;     // [N, Hqk*dk], [N, Hqk*dk], [N, Hv*dv], act dtype
+  int64_t sxq, sxk, sxv;        // row strides
+  const void *conv_w;           // [C, 4] act dtype or F32, contiguous
+  const void *conv_b;           // [C] or null
+  int32_t w_dtype, b_dtype;
+  void *conv_state;             // [N, 3, C] act dtype, inner stride 1; oldest input first
+  int64_t scs_n, scs_t;
+  const void *a, *b;            // [N, Hv] act dtype
+  int64_t sa, sb;
+  const float *A_log, *dt_bias; // [Hv]
+  float *state;                 // [N, Hv, dv, dk] F32, contiguous
+  const void *gate;             // [N, Hv, dv] act dtype or F32, inner stride 1
+  int64_t sgate_n, sgate_h;
+  int32_t gate_dtype, nw_dtype;
+  const void *norm_w;           // [dv], contiguous
+  void *out;                    // [N, Hv, dv] act dtype, contiguous
+  int64_t N, Hqk, dk, Hv, dv;
+  int32_t act, use_l2;
+  float scale, l2_eps, rms_eps;
+};
+
 // Each returns the HIP error of the launch (hipSuccess if queued).
 hipError_t launch_prologue(const PrologueArgs &a, hipStream_t s);
 hipError_t launch_chunk_rule(const ChunkArgs &a, hipStream_t s);
 hipError_t launch_gated_norm(const NormArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+bool decode_supported(int64_t dk, int64_t G, int64_t dv);
 
 // Host-side capability query used by validation (no device calls).
 bool chunk_rule_supported(int64_t dk, int32_t act);

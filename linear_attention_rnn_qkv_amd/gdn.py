@@ -65,7 +65,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_layer_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_layer_fwd.argtypes = ([P] * 12 + [ctypes.POINTER(GdnDims), f32, i32, f32, f32, vp,
                                                 ctypes.c_size_t, P, vp])
-        for name in ("gdn_prologue_fwd", "gdn_chunk_rule_fwd", "gdn_gated_norm_fwd", "gdn_layer_fwd"):
+        L.gdn_decode_fwd.argtypes = ([P] * 11 + [ctypes.POINTER(GdnDims), f32, i32, f32, P, P, f32, P, vp])
+        for name in ("gdn_prologue_fwd", "gdn_chunk_rule_fwd", "gdn_gated_norm_fwd", "gdn_layer_fwd",
+                     "gdn_decode_fwd"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -207,6 +209,23 @@ def gdn_layer_fwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, nor
                                int(bool(use_qk_l2norm_in_kernel)), float(l2_eps), float(rms_eps),
                                ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
                                _p(desc(out)), _stream(x_q)))
+    return out
+
+
+def gdn_decode_fwd(x_q, x_k, x_v, conv_w, conv_b, conv_state, a, b, A_log, dt_bias, state, gate,
+                   norm_w, dims: Sequence[int], scale: float, use_qk_l2norm_in_kernel: bool = True,
+                   l2_eps: float = 1e-6, rms_eps: float = 1e-5, out=None):
+    """One decode step; conv_state [N,3,C] and state [N,Hv,dv,dk] are updated
+    in place. Returns out [N, Hv, dv]."""
+    Hqk, dk, Hv, dv = dims
+    N = x_q.shape[0]
+    if out is None:
+        out = torch.empty((N, Hv, dv), dtype=x_q.dtype, device=x_q.device)
+    D = [desc(t) for t in (x_q, x_k, x_v, conv_w, conv_b, conv_state, a, b, A_log, dt_bias, state)]
+    gd = dims_of(Hqk, dk, Hv, dv)
+    _check(lib().gdn_decode_fwd(*[_p(d) for d in D], ctypes.byref(gd), float(scale),
+                                int(bool(use_qk_l2norm_in_kernel)), float(l2_eps), _p(desc(gate)),
+                                _p(desc(norm_w)), float(rms_eps), _p(desc(out)), _stream(x_q)))
     return out
 
 

@@ -18,10 +18,14 @@ Parity status of each function (what pins it; the pins live in
 * ``gated_rmsnorm``     - library rms_norm and silu, gate 0, scale invariance.
 * ``layer``             - composition of the above; concatenated conv equals
                           three separate convs end to end.
+* ``decode_step``       - T steps from a zero cache and state equal ``layer``
+                          over the T tokens (every output, and the final state
+                          of ``gated_delta_rule``); the cache shift is exact;
+                          a closed form for one step from a nonzero state.
 
 No function is "parity unpinned", but the absolute values of the layer have no
 printed worked example on the pages to check against.
 """
-from .gdn import (beta_and_g, build, causal_conv_silu, default_threads,  # noqa: F401
-                  gated_delta_rule, gated_rmsnorm, l2norm, layer, round_to, silu,
+from .gdn import (beta_and_g, build, causal_conv_silu, decode_step,  # noqa: F401
+                  default_threads, gated_delta_rule, gated_rmsnorm, l2norm, layer, round_to, silu,
                   softplus)

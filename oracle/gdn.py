@@ -313,3 +313,60 @@ def layer(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, *,
     if return_stages:
         return out, dict(qkv=qkv, g=g, beta=beta, o=o)
     return out
+
+
+# --------------------------------------------------------------------------
+# Recurrent decode: one new token per sequence with a conv cache and a state.
+# --------------------------------------------------------------------------
+def decode_step(x_q, x_k, x_v, conv_w, conv_b, conv_state, a, b, A_log, dt_bias,
+                state, gate, norm_w, *, Hqk, dk, Hv, dv, act, scale,
+                use_qk_l2norm=True, l2_eps=1e-6, rms_eps=1e-5):
+    """One token of the layer core for each of N independent sequences.
+
+    The recurrent form of the same layer (Gated DeltaNet's gated delta rule,
+    one token; the conv of P3 Summary evaluated at the newest token; the gated
+    norm of P2 Execution and numerical behavior). Reading of the cache: the
+    conv keeps the last K-1 = 3 inputs of every channel, oldest first, in the
+    activation dtype; a fresh sequence has a zero cache and a zero state, so T
+    steps from zero reproduce ``layer`` over those T tokens.
+
+    x_q, x_k [N, Hqk*dk]; x_v [N, Hv*dv]; conv_w [C, 4]; conv_state [N, 3, C];
+    a, b [N, Hv]; state [N, Hv, dv, dk] (FP32 values); gate [N, Hv, dv].
+    Returns (out [N, Hv, dv] float64 values of ``act``, the new conv cache
+    [N, 3, C], the new state [N, Hv, dv, dk] float64, not rounded).
+    """
+    x = np.concatenate([np.asarray(x_q, np.float64), np.asarray(x_k, np.float64),
+                        np.asarray(x_v, np.float64)], axis=-1)  # [N, C]
+    cache = np.asarray(conv_state, np.float64)
+    N, C = x.shape
+    w = np.asarray(conv_w, np.float64)
+    # the window of the newest token: three cached inputs then the new one;
+    # tap j multiplies window entry j
+    window = np.concatenate([cache, x[:, None, :]], axis=1)  # [N, 4, C]
+    y = np.einsum("njc,cj->nc", window, w)
+    if conv_b is not None:
+        y = y + np.asarray(conv_b, np.float64)[None, :]
+    z = round_to(silu(y), act)
+    new_cache = window[:, 1:, :].copy()
+    nq = Hqk * dk
+    q = z[:, :nq].reshape(N, Hqk, dk)
+    k = z[:, nq:2 * nq].reshape(N, Hqk, dk)
+    v = z[:, 2 * nq:].reshape(N, Hv, dv)
+    beta, g = beta_and_g(b, a, A_log, dt_bias)
+    beta = round_to(beta, "f32")
+    g = round_to(g, "f32")
+    if use_qk_l2norm:
+        q, k = l2norm(q, l2_eps), l2norm(k, l2_eps)
+    G = Hv // Hqk
+    S = np.array(state, dtype=np.float64, copy=True)
+    o = np.zeros((N, Hv, dv))
+    for n in range(N):
+        for h in range(Hv):
+            kk, qq = k[n, h // G], q[n, h // G]
+            # S_t = e^g S_{t-1} (I - beta k k^T) + beta v k^T;  o = scale S_t q
+            Sd = np.exp(g[n, h]) * S[n, h]
+            S[n, h] = Sd - beta[n, h] * np.outer(Sd @ kk, kk) + beta[n, h] * np.outer(v[n, h], kk)
+            o[n, h] = scale * (S[n, h] @ qq)
+    o = round_to(o, act)
+    out = gated_rmsnorm(o, gate, norm_w, rms_eps, act)
+    return out, new_cache, S

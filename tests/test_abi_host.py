@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol():
     names = set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", hdr))
     assert names == {"gdn_last_error", "gdn_version", "gdn_prologue_fwd", "gdn_chunk_rule_fwd",
                      "gdn_chunk_rule_workspace_bytes", "gdn_gated_norm_fwd", "gdn_layer_workspace_bytes",
-                     "gdn_layer_fwd"}
+                     "gdn_layer_fwd", "gdn_decode_fwd"}
     L = gdn.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -172,6 +172,51 @@ def test_layer_rejections():
     off = (-big.data_ptr()) % 256
     mis = big[off + 8: off + 8 + n]
     _expect(INVALID, "256-byte aligned", gdn.gdn_layer_fwd, **kw, workspace=mis)
+
+
+def _decode_inputs(N=3, Hqk=2, dk=64, Hv=4, dv=64, dt=torch.bfloat16):
+    nq, nv = Hqk * dk, Hv * dv
+    C = 2 * nq + nv
+    z = lambda *s, d=dt: torch.zeros(*s, dtype=d)  # noqa: E731
+    return dict(x_q=z(N, nq), x_k=z(N, nq), x_v=z(N, nv), conv_w=z(C, 4), conv_b=None,
+                conv_state=z(N, 3, C), a=z(N, Hv), b=z(N, Hv), A_log=z(Hv, d=torch.float32),
+                dt_bias=z(Hv, d=torch.float32), state=z(N, Hv, dv, dk, d=torch.float32),
+                gate=z(N, Hv, dv), norm_w=z(dv), dims=(Hqk, dk, Hv, dv), scale=0.125)
+
+
+def _dec(**over):
+    kw = _decode_inputs()
+    kw.update(over)
+    return gdn.gdn_decode_fwd(**kw)
+
+
+def test_decode_rejections():
+    x = _decode_inputs()
+    _expect(INVALID, "empty", gdn.gdn_decode_fwd, **_decode_inputs(N=0))
+    _expect(INVALID, "multiple of Hqk", _dec, dims=(3, 64, 4, 64))
+    _expect(UNSUPPORTED, "not instantiated", gdn.gdn_decode_fwd, **_decode_inputs(dk=32))
+    _expect(UNSUPPORTED, "not instantiated", gdn.gdn_decode_fwd, **_decode_inputs(dv=32))
+    _expect(UNSUPPORTED, "not instantiated", gdn.gdn_decode_fwd, **_decode_inputs(Hqk=1, Hv=128))
+    _expect(INVALID, "conv_state: dim", _dec, conv_state=torch.zeros(3, 4, 512, dtype=torch.bfloat16))
+    _expect(INVALID, "conv_state: dtype", _dec, conv_state=x["conv_state"].float())
+    _expect(INVALID, "state: dtype", _dec, state=x["state"].bfloat16())
+    _expect(INVALID, "state: must be contiguous", _dec,
+            state=torch.zeros(3, 4, 64, 128, dtype=torch.float32)[..., :64])
+    _expect(INVALID, "x_k: dtype", _dec, x_k=x["x_k"].half())
+    _expect(INVALID, "gate: dtype", _dec, gate=x["gate"].half())
+    _expect(INVALID, "out: must be contiguous", _dec,
+            out=torch.zeros(3, 4, 128, dtype=torch.bfloat16)[..., :64])
+    _expect(INVALID, "A_log: dtype", _dec, A_log=x["A_log"].bfloat16())
+    _expect(INVALID, "l2_eps", _dec, l2_eps=float("nan"))
+    _expect(INVALID, "overlaps", _dec, gate=x["gate"], out=x["gate"])
+    buf = torch.zeros(3 * 3 * 512, dtype=torch.bfloat16)
+    _expect(INVALID, "overlaps", _dec, conv_state=buf.view(3, 3, 512), x_v=buf[:768].view(3, 256))
+    st = x["state"]
+    _expect(INVALID, "must not overlap", _dec, state=st, conv_state=st.view(torch.bfloat16).view(-1)[:3 * 3 * 512]
+            .view(3, 3, 512))
+    big = torch.zeros(3 * 4 * 64 * 64 + 4, dtype=torch.float32)
+    off = (-big.data_ptr() // 4) % 4
+    _expect(UNSUPPORTED, "16-byte aligned", _dec, state=big[off + 1: off + 1 + 3 * 4 * 64 * 64].view(3, 4, 64, 64))
 
 
 def test_error_message_is_per_call():

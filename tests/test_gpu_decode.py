@@ -1,0 +1,144 @@
+"""GPU parity of the recurrent decode step (gdn_decode_fwd) through the C ABI.
+
+One step from a random conv cache and a random FP32 state against the FP64
+oracle's ``decode_step`` (output and new state within the dtype's tolerance,
+new conv cache bit-exact: it is a pure shift of stored values), and T steps
+from a zero cache and state against the prefill layer core on the same T
+tokens, both the oracle's and the GPU's own (outputs), and against the chunk
+rule's final state.
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_rnn_qkv_amd import gdn, synth
+from oracle import gdn as O
+from . import _gdn_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+TAU = H.TAU
+f64 = H.f64
+
+
+def _dims(s):
+    return (s.Hqk, s.dk, s.Hv, s.dv)
+
+
+def _step_inputs(s, seed):
+    """Inputs of one token per sequence (N = s.B), plus a random cache and
+    state. Token inputs keep the layout of the workload (views into one
+    projection buffer where it has one)."""
+    x = H.to_dev(synth.make_inputs(s.replace(T=1)))
+    tok = {k: x[k][:, 0] for k in ("x_q", "x_k", "x_v", "a", "b", "gate")}
+    dt = synth.TORCH_DTYPE[s.act]
+    cache = synth.randn((s.B, 3, s.C), s.act, seed).cuda()
+    state = (0.5 * synth.randn((s.B, s.Hv, s.dv, s.dk), "f32", seed + 1)).cuda()
+    return x, tok, cache, state, dt
+
+
+def _oracle_step(x, tok, cache, state, s, scale, use_l2=True):
+    return O.decode_step(f64(tok["x_q"]), f64(tok["x_k"]), f64(tok["x_v"]), f64(x["conv_w"]),
+                         f64(x["conv_b"]), f64(cache), f64(tok["a"]), f64(tok["b"]), f64(x["A_log"]),
+                         f64(x["dt_bias"]), f64(state), f64(tok["gate"]), f64(x["norm_w"]), Hqk=s.Hqk,
+                         dk=s.dk, Hv=s.Hv, dv=s.dv, act=s.act, scale=scale, use_qk_l2norm=use_l2)
+
+
+def _gpu_step(x, tok, cache, state, s, scale, use_l2=True):
+    return gdn.gdn_decode_fwd(tok["x_q"], tok["x_k"], tok["x_v"], x["conv_w"], x["conv_b"], cache,
+                              tok["a"], tok["b"], x["A_log"], x["dt_bias"], state, tok["gate"],
+                              x["norm_w"], _dims(s), scale, use_qk_l2norm_in_kernel=use_l2)
+
+
+def _expected_cache(cache, tok):
+    xc = torch.cat([tok["x_q"], tok["x_k"], tok["x_v"]], -1)
+    return torch.cat([cache[:, 1:], xc[:, None]], 1)
+
+
+STEP = [
+    ("tiny-fp32-N5", 0, {"B": 5}),
+    ("bf16-hd256-dv512-strided-N3", 1, {"B": 3}),
+    ("gqa-bf16-fp32gate-N16", 2, {"B": 16}),
+    ("gqa-bf16-N64", 3, {"B": 64}),
+    ("fp16-N7", 4, {"B": 7, "lengths": None}),
+    ("dk64-G8-N4", 2, {"B": 4, "Hqk": 2, "dk": 64, "Hv": 16, "dv": 256}),
+    ("max-group-G64-N2", 2, {"B": 2, "Hqk": 1, "dk": 128, "Hv": 64, "dv": 128}),
+    ("dv512-G16-N2", 3, {"B": 2, "Hqk": 1, "dk": 256, "Hv": 16, "dv": 512}),
+]
+
+
+@pytest.mark.parametrize("name,cfg,over", STEP, ids=[c[0] for c in STEP])
+def test_decode_step_parity(name, cfg, over):
+    s = synth.spec(cfg).replace(**over)
+    x, tok, cache, state, _ = _step_inputs(s, 100 + cfg)
+    scale = s.dk ** -0.5
+    ref_out, ref_cache, ref_state = _oracle_step(x, tok, cache, state, s, scale)
+    want_cache = _expected_cache(cache, tok)
+    out = _gpu_step(x, tok, cache, state, s, scale)
+    torch.cuda.synchronize()
+    H.assert_close(f64(out), ref_out, TAU[s.act], "out")
+    H.assert_close(f64(state), ref_state, TAU[s.act], "state")
+    assert torch.equal(cache, want_cache), "conv cache is not the exact shift"
+    np.testing.assert_array_equal(f64(cache), ref_cache)
+
+
+def test_decode_step_without_in_kernel_l2():
+    s = synth.spec(2).replace(B=8)
+    x, tok, cache, state, _ = _step_inputs(s, 7)
+    ref_out, _, ref_state = _oracle_step(x, tok, cache, state, s, 0.05, use_l2=False)
+    out = _gpu_step(x, tok, cache, state, s, 0.05, use_l2=False)
+    torch.cuda.synchronize()
+    H.assert_close(f64(out), ref_out, TAU[s.act], "out")
+    H.assert_close(f64(state), ref_state, TAU[s.act], "state")
+
+
+@pytest.mark.parametrize("cfg,over", [(0, {"B": 2, "T": 70}), (1, {"B": 2, "T": 67}),
+                                      (2, {"B": 3, "T": 130, "Hqk": 4, "Hv": 8})],
+                         ids=["fp32-T70", "bf16-hd256-T67", "gqa-bf16-T130"])
+def test_decode_steps_equal_prefill(cfg, over):
+    """T steps from zero reproduce the prefill layer core token by token and
+    end in the chunk rule's final state."""
+    s = synth.spec(cfg).replace(**over)
+    x = H.to_dev(synth.make_inputs(s))
+    scale = s.dk ** -0.5
+    tau = TAU[s.act]
+    dt = synth.TORCH_DTYPE[s.act]
+    cache = torch.zeros((s.B, 3, s.C), dtype=dt, device="cuda")
+    state = torch.zeros((s.B, s.Hv, s.dv, s.dk), dtype=torch.float32, device="cuda")
+    outs = []
+    for t in range(s.T):
+        tok = {k: x[k][:, t] for k in ("x_q", "x_k", "x_v", "a", "b", "gate")}
+        outs.append(_gpu_step(x, tok, cache, state, s, scale))
+    dec = torch.stack(outs, 1)
+    pre = gdn.gdn_layer_fwd(x["x_q"], x["x_k"], x["x_v"], x["conv_w"], x["conv_b"], x["a"], x["b"],
+                            x["A_log"], x["dt_bias"], x["gate"], x["norm_w"], None, _dims(s), scale)
+    qkv, g, beta = gdn.gdn_prologue_fwd(x["x_q"], x["x_k"], x["x_v"], x["conv_w"], x["conv_b"], x["a"],
+                                        x["b"], x["A_log"], x["dt_bias"], None, _dims(s))
+    nq = s.Hqk * s.dk
+    q = qkv[..., :nq].unflatten(-1, (s.Hqk, s.dk))
+    k = qkv[..., nq:2 * nq].unflatten(-1, (s.Hqk, s.dk))
+    v = qkv[..., 2 * nq:].unflatten(-1, (s.Hv, s.dv))
+    _, fin = gdn.gdn_chunk_rule_fwd(q, k, v, g, beta, scale, output_final_state=True)
+    torch.cuda.synchronize()
+    ref = H.oracle_layer(x, s, scale)
+    H.assert_close(f64(dec), ref, tau, "decode vs oracle layer")
+    H.assert_close(f64(dec), f64(pre), tau, "decode vs GPU layer")
+    H.assert_close(f64(state), f64(fin), tau, "decode state vs chunk rule final state")
+    xc = torch.cat([x["x_q"], x["x_k"], x["x_v"]], -1)
+    assert torch.equal(cache, xc[:, s.T - 3:].contiguous())
+
+
+def test_decode_rows_are_independent_and_deterministic():
+    s = synth.spec(3).replace(B=6)
+    x, tok, cache, state, _ = _step_inputs(s, 11)
+    c1, s1 = cache.clone(), state.clone()
+    out = _gpu_step(x, tok, c1, s1, s, 0.1)
+    c2, s2 = cache.clone(), state.clone()
+    out2 = _gpu_step(x, tok, c2, s2, s, 0.1)
+    assert torch.equal(out, out2) and torch.equal(s1, s2) and torch.equal(c1, c2)
+    # one row at a time gives the same bits
+    for n in (0, 5):
+        t1 = {k: v[n:n + 1] for k, v in tok.items()}
+        cn, sn = cache[n:n + 1].clone(), state[n:n + 1].clone()
+        on = _gpu_step(x, t1, cn, sn, s, 0.1)
+        assert torch.equal(on[0], out[n]) and torch.equal(sn[0], s1[n]) and torch.equal(cn[0], c1[n])

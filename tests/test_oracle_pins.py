@@ -15,6 +15,7 @@ import pytest
 import torch
 import torch.nn.functional as F
 
+from linear_attention_rnn_qkv_amd import synth
 from oracle import gdn as O
 from oracle.chunked import chunked_gated_delta_rule
 
@@ -374,3 +375,76 @@ def test_layer_concatenated_prologue_equals_separate_route():
            for n, a, b in (("x_q", 0, nq), ("x_k", nq, 2 * nq), ("x_v", 2 * nq, s.C))]
     np.testing.assert_array_equal(st["qkv"], np.concatenate(sep, -1))
     assert np.all(np.isfinite(out)) and out.shape == (1, 40, s.Hv, s.dv)
+
+
+# ----------------------------------------------------------------------------
+# Recurrent decode
+# ----------------------------------------------------------------------------
+def _decode_run(x, s, T, scale):
+    """T decode steps from a zero cache and state over the tokens of x."""
+    f = synth.to_f64
+    B = s.B
+    cache = np.zeros((B, 3, s.C))
+    S = np.zeros((B, s.Hv, s.dv, s.dk))
+    outs, caches = [], []
+    for t in range(T):
+        o, cache, S = O.decode_step(
+            f(x["x_q"])[:, t], f(x["x_k"])[:, t], f(x["x_v"])[:, t], f(x["conv_w"]), None, cache,
+            f(x["a"])[:, t], f(x["b"])[:, t], f(x["A_log"]), f(x["dt_bias"]), S, f(x["gate"])[:, t],
+            f(x["norm_w"]), Hqk=s.Hqk, dk=s.dk, Hv=s.Hv, dv=s.dv, act=s.act, scale=scale)
+        outs.append(o)
+        caches.append(cache)
+    return np.stack(outs, 1), caches, S
+
+
+def test_decode_steps_from_zero_equal_the_layer():
+    # The recurrent form and the sequence form of the same layer: token t of
+    # the layer's output equals the t-th decode step; the final state equals
+    # the recurrence's final state (conv lags, tap order, gates, GQA map and
+    # every rounding point are exercised by the comparison).
+    s = synth.spec(0).replace(B=2, T=11, Hqk=2, dk=8, Hv=4, dv=6, act="bf16", gate_dtype="bf16",
+                              w_dtype="bf16")
+    x = synth.make_inputs(s)
+    f = synth.to_f64
+    scale = 0.3
+    got, caches, S = _decode_run(x, s, s.T, scale)
+    ref, st = O.layer(f(x["x_q"]), f(x["x_k"]), f(x["x_v"]), f(x["conv_w"]), None, f(x["a"]),
+                      f(x["b"]), f(x["A_log"]), f(x["dt_bias"]), f(x["gate"]), f(x["norm_w"]),
+                      Hqk=s.Hqk, dk=s.dk, Hv=s.Hv, dv=s.dv, act=s.act, scale=scale,
+                      return_stages=True)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    q, k, v = (a.reshape(s.B, s.T, -1, d) for a, d in
+               ((st["qkv"][..., :16], s.dk), (st["qkv"][..., 16:32], s.dk), (st["qkv"][..., 32:], s.dv)))
+    _, fin = O.gated_delta_rule(q, k, v, st["g"], st["beta"], scale=scale, output_final_state=True)
+    np.testing.assert_allclose(S, fin, rtol=1e-10, atol=1e-12)
+    # the cache after step t holds inputs t-2, t-1, t exactly (zeros before the start)
+    xc = np.concatenate([f(x["x_q"]), f(x["x_k"]), f(x["x_v"])], -1)
+    pad = np.concatenate([np.zeros((s.B, 2, s.C)), xc], 1)
+    for t in (0, 1, 5, s.T - 1):
+        np.testing.assert_array_equal(caches[t], pad[:, t:t + 3])
+
+
+def test_decode_unit_write_strength_overwrites_the_value_at_the_key():
+    # With beta = 1 and no decay the delta rule replaces what the state held
+    # at the (unit) key by the new value, whatever the state was: S_new k = v.
+    rng = np.random.default_rng(5)
+    Hqk, dk, Hv, dv = 1, 8, 2, 5
+    C = 2 * Hqk * dk + Hv * dv
+    xq, xk, xv = rng.normal(size=(1, dk)), rng.normal(size=(1, dk)), rng.normal(size=(1, Hv * dv))
+    w = rng.uniform(-0.5, 0.5, (C, 4))
+    cache = rng.normal(size=(1, 3, C))
+    S0 = rng.normal(size=(1, Hv, dv, dk))
+    b = np.full((1, Hv), 60.0)           # sigmoid(60) == 1 in float64
+    a = np.zeros((1, Hv))
+    A_log = np.full(Hv, -80.0)           # exp(-80) softplus(0): decay e^g == 1 in float64
+    out, _, S = O.decode_step(xq, xk, xv, w, None, cache, a, b, A_log, np.zeros(Hv), S0,
+                              np.zeros((1, Hv, dv)), np.ones(dv), Hqk=Hqk, dk=dk, Hv=Hv, dv=dv,
+                              act="f64", scale=1.0, l2_eps=0.0)
+    win = np.concatenate([cache[0], np.concatenate([xq, xk, xv], -1)], 0)  # [4, C]
+    z = O.silu(np.sum(win.T * w, axis=1))
+    kh = z[dk:2 * dk] / np.sqrt(np.sum(z[dk:2 * dk] ** 2))
+    for h in range(Hv):
+        np.testing.assert_allclose(S[0, h] @ kh, z[2 * dk + h * dv: 2 * dk + (h + 1) * dv],
+                                   rtol=1e-12, atol=1e-12)
+        assert np.max(np.abs(S0[0, h] @ kh - S[0, h] @ kh)) > 0.1  # the old content was replaced
+    np.testing.assert_array_equal(out, 0.0)  # gate 0: silu(0) = 0
