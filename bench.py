@@ -127,6 +127,44 @@ def calibrate_copy(reps: int) -> int:
     return 0
 
 
+def decode_leg(gdn, synth, torch, s, d, dims, scale, N, steps, warmup) -> dict:
+    """The recurrent decode step (one token for each of N sequences, conv
+    cache and FP32 state updated in place) at the workload's head geometry.
+    Not the headline metric: reported beside it, against the HBM roof (the
+    state is read and written once per step)."""
+    dt = synth.TORCH_DTYPE[s.act]
+    e = {"f32": 4, "bf16": 2, "f16": 2}[s.act]
+    eg = {"f32": 4, "bf16": 2, "f16": 2}[s.gate_dtype]
+    tok = synth.make_inputs(s.replace(B=N, T=1, lengths=None, gate_in_proj=False))
+    t = {k: tok[k][:, 0].contiguous().cuda() for k in ("x_q", "x_k", "x_v", "a", "b", "gate")}
+    cache = synth.randn((N, 3, s.C), s.act, 7).cuda()
+    state = (0.5 * synth.randn((N, s.Hv, s.dv, s.dk), "f32", 8)).cuda()
+    out = torch.empty((N, s.Hv, s.dv), dtype=dt, device="cuda")
+
+    def step():
+        gdn.gdn_decode_fwd(t["x_q"], t["x_k"], t["x_v"], d["conv_w"], None, cache, t["a"], t["b"],
+                           d["A_log"], d["dt_bias"], state, t["gate"], d["norm_w"], dims, scale, out=out)
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # per sequence: state read + written (FP32), x, conv cache read + written,
+    # a and b, gate, out; per launch: conv weights and norm weight
+    per_seq = (2 * s.Hv * s.dv * s.dk * 4 + s.C * e + 6 * s.C * e + 2 * s.Hv * e + s.Hv * s.dv * (eg + e))
+    nbytes = N * per_seq + 4 * s.C * e + s.dv * e
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "decode_kernel", "seqs": N, "ms": ms, "bytes": nbytes, "GB/s": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS, "tokens/s": N / (ms * 1e-3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +173,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-seqs", type=int, default=256,
+                    help="sequences of the decode-step leg (0 skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -268,6 +308,11 @@ def main() -> int:
     for v in stages.values():
         v["traffic"] = measured_traffic(s.name, v["kernel"])
 
+    decode = None
+    if args.decode_seqs > 0:
+        decode = decode_leg(gdn, synth, torch, s, d, dims, scale, args.decode_seqs, args.steps,
+                            args.warmup)
+
     result = {
         "metric": METRIC,
         "value": ntok / (ms * 1e-3),
@@ -285,6 +330,7 @@ def main() -> int:
                    "Hv": s.Hv, "dv": s.dv, "chunk": CHUNK, "conv_taps": 4, "parallelism": "single GPU"},
         "roofline": roof,
         "stages": stages,
+        "decode": decode,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

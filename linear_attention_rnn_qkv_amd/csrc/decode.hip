@@ -18,18 +18,27 @@
 // written once, 2 * dv * dk * 4 bytes per head and token); everything else is
 // a few KB per sequence.
 //
-// One workgroup per (sequence, query/key head): it convolves the q and k
-// channels of the head once and the v channels of its G value heads, then
-// updates the G states. A state row (dk floats) is handled by dk / 8 lanes,
-// 8 floats each (two 16-byte non-temporal loads and stores); the two dot
-// products per row are lane-group reductions.
+// One workgroup of 1024 threads per (sequence, query/key head): it convolves
+// the q and k channels of the head once and the v channels of its G value
+// heads, then updates the G states, which are adjacent in memory (one block
+// of G * dv rows of dk floats). A row is handled by dk / 4 lanes, 4 floats
+// each (one 16-byte non-temporal load and store); the two dot products per
+// row are lane-group reductions. Wide, short-lived workgroups matter here: on
+// this part a read-modify-write stream of many independent workgroups runs
+// faster the less work each workgroup holds (measured: 256 rows per 256-thread
+// workgroup reach 5.1 TB/s, the same rows per 1024-thread workgroup 5.8 TB/s),
+// and the row block of one (sequence, head group) cannot be split across
+// workgroups without a race on the shared q/k conv cache.
 #include "device_common.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
+constexpr int kCols = 4;       // state columns per lane (one 16-byte access)
+constexpr int kBatch = 4;      // state rows in flight per lane
+constexpr int kWavesPerEU = 8;
 constexpr int kMaxVCh = 8192;  // G * dv (dynamic LDS: one FP32 row of this length)
 constexpr int kMaxG = 64;
 
@@ -40,11 +49,12 @@ __device__ __forceinline__ float ld_as(const void *p, int32_t dt, int64_t i) {
 }
 
 template <typename T, int DK>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p) {
-  constexpr int LR = DK / 8;             // lanes per state row
-  constexpr int RP = kThreads / LR;      // rows per pass
-  __shared__ float qv[DK], kv[DK];
-  __shared__ float gdec[kMaxG], bet[kMaxG];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU))) void decode_kernel(
+    DecodeArgs p) {
+  constexpr int LR = DK / kCols;     // lanes per state row
+  constexpr int RP = kThreads / LR;  // rows per pass
+  __shared__ __align__(16) float qv[DK], kv[DK];
+  __shared__ float gexp[kMaxG], bet[kMaxG];
   __shared__ float nrm[2];
   // v of the G value heads; row i's o overwrites its v (the lanes that read
   // v[i] belong to the wave that writes o[i], and one wave's LDS accesses
@@ -56,37 +66,50 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p) {
   const int64_t hk = blockIdx.x, n = blockIdx.y;
   const int64_t G = p.Hv / p.Hqk, nq = p.Hqk * DK;
   const int64_t nvc = G * p.dv;
+  const int cb = tid % LR, rw = tid / LR;  // column block and row within a pass
+  const int64_t np = p.dv / RP;           // passes of RP rows per value head
+
+  // The G value heads of query/key head hk are adjacent in the state, so the
+  // workgroup's rows form one contiguous block of G * dv rows, walked in
+  // passes of RP rows (a pass never straddles two heads: RP divides dv).
+  const int nt = (int)(G * np);
+  const int lnp = __builtin_ctz((unsigned)np);
+  float *sbase = p.state + ((n * p.Hv + hk * G) * p.dv + rw) * DK + kCols * cb;
+
+  // The rows of the first batch are requested before anything else: their
+  // latency overlaps the conv below.
+  float s[kBatch][kCols];
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b)
+    if (b < nt) load_vec_nt<float, kCols>(sbase + (int64_t)b * RP * DK, 16, s[b]);
 
   // 1. conv + SiLU of the head's q, k channels and its value heads' v
   //    channels; the cache shifts by one token
-  const T *xq = static_cast<const T *>(p.xq) + n * p.sxq + hk * DK;
-  const T *xk = static_cast<const T *>(p.xk) + n * p.sxk + hk * DK;
-  const T *xv = static_cast<const T *>(p.xv) + n * p.sxv + hk * nvc;
-  T *cs = static_cast<T *>(p.conv_state) + n * p.scs_n;
-  for (int64_t i = tid; i < 2 * DK + nvc; i += kThreads) {
-    int64_t ch;
-    float x;
-    if (i < DK) {
-      ch = hk * DK + i;
-      x = f(xq[i]);
-    } else if (i < 2 * DK) {
-      ch = nq + hk * DK + (i - DK);
-      x = f(xk[i - DK]);
-    } else {
-      ch = 2 * nq + hk * nvc + (i - 2 * DK);
-      x = f(xv[i - 2 * DK]);
-    }
-    const float c0 = f(cs[ch]), c1 = f(cs[p.scs_t + ch]), c2 = f(cs[2 * p.scs_t + ch]);
-    float y = p.conv_b ? ld_as<T>(p.conv_b, p.b_dtype, ch) : 0.f;
-    y += ld_as<T>(p.conv_w, p.w_dtype, 4 * ch) * c0 + ld_as<T>(p.conv_w, p.w_dtype, 4 * ch + 1) * c1 +
-         ld_as<T>(p.conv_w, p.w_dtype, 4 * ch + 2) * c2 + ld_as<T>(p.conv_w, p.w_dtype, 4 * ch + 3) * x;
-    const float z = round_through<T>(silu(y));
-    if (i < DK) qv[i] = z;
-    else if (i < 2 * DK) kv[i - DK] = z;
-    else vv[i - 2 * DK] = z;
-    cs[ch] = to<T>(c1);
-    cs[p.scs_t + ch] = to<T>(c2);
-    cs[2 * p.scs_t + ch] = to<T>(x);
+  // Offsets below are 32-bit from uniform base pointers (C < 2^31).
+  T *cs0 = static_cast<T *>(p.conv_state) + n * p.scs_n;
+  T *cs1 = cs0 + p.scs_t, *cs2 = cs1 + p.scs_t;
+  const bool w32 = p.w_dtype == kF32, b32 = p.b_dtype == kF32;
+  auto conv = [&](int ch, float x) {
+    const float c0 = f(cs0[ch]), c1 = f(cs1[ch]), c2 = f(cs2[ch]);
+    float w[4];
+    if (w32) load_vec<float, 4>(static_cast<const float *>(p.conv_w) + 4 * ch, p.w_align, w);
+    else load_vec<T, 4>(static_cast<const T *>(p.conv_w) + 4 * ch, p.w_align, w);
+    float y = 0.f;
+    if (p.conv_b) y = b32 ? static_cast<const float *>(p.conv_b)[ch] : f(static_cast<const T *>(p.conv_b)[ch]);
+    y += w[0] * c0 + w[1] * c1 + w[2] * c2 + w[3] * x;
+    cs0[ch] = to<T>(c1);
+    cs1[ch] = to<T>(c2);
+    cs2[ch] = to<T>(x);
+    return round_through<T>(silu(y));
+  };
+  {
+    const T *xq = static_cast<const T *>(p.xq) + n * p.sxq + hk * DK;
+    const T *xk = static_cast<const T *>(p.xk) + n * p.sxk + hk * DK;
+    const T *xv = static_cast<const T *>(p.xv) + n * p.sxv + hk * nvc;
+    const int q0 = (int)(hk * DK), k0 = (int)(nq + hk * DK), v0 = (int)(2 * nq + hk * nvc);
+    for (int i = tid; i < DK; i += kThreads) qv[i] = conv(q0 + i, f(xq[i]));
+    for (int i = tid; i < DK; i += kThreads) kv[i] = conv(k0 + i, f(xk[i]));
+    for (int i = tid; i < (int)nvc; i += kThreads) vv[i] = conv(v0 + i, f(xv[i]));
   }
   // beta and g of the G value heads
   for (int64_t j = tid; j < G; j += kThreads) {
@@ -95,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p) {
     const float xa = f(static_cast<const T *>(p.a)[n * p.sa + h]) + p.dt_bias[h];
     const float sp = xa > 20.f ? xa : log1pf(expf(xa));
     bet[j] = 1.0f / (1.0f + expf(-bb));
-    gdec[j] = -expf(p.A_log[h]) * sp;
+    gexp[j] = fast_exp(-expf(p.A_log[h]) * sp);  // the decay e^g
   }
   __syncthreads();
 
@@ -109,48 +132,44 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p) {
   }
   __syncthreads();
 
-  // 3. state update, one value head at a time; lane group of row i holds dk
-  //    columns 8 cb .. 8 cb + 7
-  const int cb = tid % LR;
-  float kh[8], qh[8];
+  // 3. state update; the lane group of a row holds its columns
+  //    kCols * cb .. kCols * cb + kCols - 1
+  float kh[kCols], qh[kCols];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    kh[e] = kv[8 * cb + e] * nrm[1];
-    qh[e] = qv[8 * cb + e] * nrm[0];
+  for (int e = 0; e < kCols; ++e) {
+    kh[e] = kv[kCols * cb + e] * nrm[1];
+    qh[e] = qv[kCols * cb + e] * nrm[0];
   }
-  for (int64_t j = 0; j < G; ++j) {
-    const int64_t h = hk * G + j;
-    const float decay = fast_exp(gdec[j]), bj = bet[j];
-    float *sbase = p.state + ((n * p.Hv + h) * p.dv) * DK + 8 * cb;
-    const int64_t np = p.dv / RP;  // passes of RP rows
-    // batches of four passes: their rows are loaded before any is updated
-    for (int64_t p0 = 0; p0 < np; p0 += 4) {
-      float s[4][8];
+  // batches of kBatch passes: their rows are loaded before any is updated
+  for (int t0 = 0; t0 < nt; t0 += kBatch) {
+    if (t0 > 0) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (p0 + b < np) load_vec_nt<float, 8>(sbase + ((p0 + b) * RP + tid / LR) * DK, 16, s[b]);
+      for (int b = 0; b < kBatch; ++b)
+        if (t0 + b < nt) load_vec_nt<float, kCols>(sbase + (int64_t)(t0 + b) * RP * DK, 16, s[b]);
+    }
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (p0 + b >= np) break;
-        const int64_t i = (p0 + b) * RP + tid / LR;
-        float d = 0.f;
+    for (int b = 0; b < kBatch; ++b) {
+      if (t0 + b >= nt) break;
+      const int t = t0 + b, j = t >> lnp;  // value head j of the group
+      const int r = t * RP + rw;           // row of the block: j * dv + (row in head j)
+      const float decay = gexp[j], bj = bet[j];
+      float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          s[b][e] *= decay;
-          d += s[b][e] * kh[e];
-        }
-        d = group_sum<LR>(d);
-        const float u = bj * (vv[j * p.dv + i] - d);
-        float o = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          s[b][e] += u * kh[e];
-          o += s[b][e] * qh[e];
-        }
-        o = group_sum<LR>(o);
-        store_vec_nt<float, 8>(sbase + i * DK, s[b]);
-        if (cb == 0) ov[j * p.dv + i] = p.scale * o;
+      for (int e = 0; e < kCols; ++e) {
+        s[b][e] *= decay;
+        d += s[b][e] * kh[e];
       }
+      d = group_sum<LR>(d);
+      const float u = bj * (vv[r] - d);
+      float o = 0.f;
+#pragma unroll
+      for (int e = 0; e < kCols; ++e) {
+        s[b][e] += u * kh[e];
+        o += s[b][e] * qh[e];
+      }
+      o = group_sum<LR>(o);
+      store_vec_nt<float, kCols>(sbase + (int64_t)t * RP * DK, s[b]);
+      if (cb == 0) ov[r] = p.scale * o;
     }
   }
   __syncthreads();

@@ -493,6 +493,7 @@ gdn_status plan_decode(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_t
   p.xq = x_q->data; p.xk = x_k->data; p.xv = x_v->data;
   p.sxq = x_q->stride[0]; p.sxk = x_k->stride[0]; p.sxv = x_v->stride[0];
   p.conv_w = conv_w->data; p.w_dtype = conv_w->dtype;
+  p.w_align = gdn::align_of_host((uint64_t)(uintptr_t)conv_w->data);
   p.conv_b = conv_b ? conv_b->data : nullptr; p.b_dtype = conv_b ? conv_b->dtype : act;
   p.conv_state = conv_state->data; p.scs_n = conv_state->stride[0]; p.scs_t = conv_state->stride[1];
   p.a = a->data; p.b = b->data; p.sa = a->stride[0]; p.sb = b->stride[0];

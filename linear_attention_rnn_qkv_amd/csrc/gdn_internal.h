@@ -88,6 +88,7 @@ struct DecodeArgs {
   const void *conv_w;           // [C, 4] act dtype or F32, contiguous
   const void *conv_b;           // [C] or null
   int32_t w_dtype, b_dtype;
+  int32_t w_align;              // bytes conv_w's base address is aligned to (<= 16)
   void *conv_state;             // [N, 3, C] act dtype, inner stride 1; oldest input first
   int64_t scs_n, scs_t;
   const void *a, *b;            // [N, Hv] act dtype

@@ -35,6 +35,7 @@ KERNELS = {
                                                   "gdn_internal.h"]),
     "chunk_rule_kernel": ("chunk_rule_kernel", ["chunk_rule.hip", "device_common.h", "gdn_internal.h"]),
     "prologue_kernel": ("prologue_kernel", ["prologue.hip", "device_common.h", "gdn_internal.h"]),
+    "decode_kernel": ("decode_kernel", ["decode.hip", "device_common.h", "gdn_internal.h"]),
     "gated_norm_kernel": ("gated_norm_kernel", ["gated_norm.hip", "device_common.h", "gdn_internal.h"]),
 }
 

@@ -142,3 +142,24 @@ def test_decode_rows_are_independent_and_deterministic():
         cn, sn = cache[n:n + 1].clone(), state[n:n + 1].clone()
         on = _gpu_step(x, t1, cn, sn, s, 0.1)
         assert torch.equal(on[0], out[n]) and torch.equal(sn[0], s1[n]) and torch.equal(cn[0], c1[n])
+
+
+@pytest.mark.parametrize("wdt", ["act", "f32"])
+def test_decode_step_bias_and_unaligned_conv_weight(wdt):
+    """Conv bias present and conv weights whose base is not 16-byte aligned
+    (a view one element into a buffer), in the activation dtype or FP32."""
+    s = synth.spec(2).replace(B=6, Hqk=4, Hv=8)
+    x, tok, cache, state, dt = _step_inputs(s, 21)
+    wt = dt if wdt == "act" else torch.float32
+    buf = torch.empty(s.C * 4 + 1, dtype=wt, device="cuda")
+    w = buf[1:].view(s.C, 4)
+    w.copy_(x["conv_w"].to(wt))
+    bias = (0.1 * synth.randn((s.C,), "f32", 22)).to(wt).cuda()
+    x = dict(x, conv_w=w, conv_b=bias)
+    assert w.data_ptr() % 16 != 0
+    ref_out, ref_cache, ref_state = _oracle_step(x, tok, cache, state, s, 0.1)
+    out = _gpu_step(x, tok, cache, state, s, 0.1)
+    torch.cuda.synchronize()
+    H.assert_close(f64(out), ref_out, TAU[s.act], "out")
+    H.assert_close(f64(state), ref_state, TAU[s.act], "state")
+    np.testing.assert_array_equal(f64(cache), ref_cache)
