@@ -165,6 +165,76 @@ def decode_leg(gdn, synth, torch, s, d, dims, scale, N, steps, warmup) -> dict:
             "hbm_frac": gbs / HBM_PEAK_GBS, "tokens/s": N / (ms * 1e-3)}
 
 
+# The pages' whole-layer shapes (flash-linear-attention GatedDeltaNet with
+# num_heads=6, expand_v=2; page "fused q/k/v short conv", Benchmark /
+# Performance) and their B200 forward times with the fused conv, as context.
+WHOLE_LAYER_SHAPES = [  # (B, T, hidden, head_dim, act, B200 fwd ms)
+    (2, 2048, 2048, 256, "bf16", 1.540),
+    (1, 128, 512, 64, "bf16", 1.493),
+    (2, 100, 512, 64, "bf16", 1.486),
+    (2, 256, 512, 64, "f16", 1.488),
+]
+
+
+def whole_layer_leg(gdn, synth, torch) -> list:
+    """The whole layer forward: one input-projection GEMM to the fused
+    q|k|v|gate|b|a buffer, the layer core on views of it, the output-projection
+    GEMM. The GEMMs are plain library GEMMs (torch.matmul, which runs
+    hipBLASLt/rocBLAS); the core is this library. Timed like the pages'
+    script: untimed calls, then per-call HIP events with the caches flushed by
+    a 512 MB write before each call, median of 200 calls."""
+    res = []
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for i, (B, T, Hd, hd, act, b200) in enumerate(WHOLE_LAYER_SHAPES):
+        Hqk, dk, Hv, dv = 6, hd, 6, 2 * hd
+        nq, nv = Hqk * dk, Hv * dv
+        C = 2 * nq + nv
+        width = 2 * nq + 2 * nv + 2 * Hv
+        dt = synth.TORCH_DTYPE[act]
+        seed = 900 + 10 * i
+        x = synth.randn((B, T, Hd), act, seed).cuda()
+        w_in = (synth.randn((Hd, width), "f32", seed + 1) * Hd ** -0.5).to(dt).cuda()
+        w_out = (synth.randn((nv, Hd), "f32", seed + 2) * nv ** -0.5).to(dt).cuda()
+        conv_w = torch.from_numpy(synth.uniform((C, 4), -0.5, 0.5, seed + 3)).to(dt).cuda()
+        A_log = torch.from_numpy(synth.uniform((Hv,), 1.0, 16.0, seed + 4)).log().float().cuda()
+        dt_bias = (0.1 * synth.randn((Hv,), "f32", seed + 5)).cuda()
+        norm_w = torch.ones(dv, dtype=dt, device="cuda")
+        dims = (Hqk, dk, Hv, dv)
+        ws = torch.empty(gdn.gdn_layer_workspace_bytes(B, T, dims, dt), dtype=torch.uint8, device="cuda")
+        core = torch.empty((B, T, Hv, dv), dtype=dt, device="cuda")
+
+        def fwd():
+            proj = torch.matmul(x, w_in)
+            o = 0
+            xq = proj[..., o:o + nq]; o += nq
+            xk = proj[..., o:o + nq]; o += nq
+            xv = proj[..., o:o + nv]; o += nv
+            gate = proj[..., o:o + nv].unflatten(-1, (Hv, dv)); o += nv
+            b = proj[..., o:o + Hv]; o += Hv
+            a = proj[..., o:o + Hv]
+            gdn.gdn_layer_fwd(xq, xk, xv, conv_w, None, a, b, A_log, dt_bias, gate, norm_w, None, dims,
+                              dk ** -0.5, workspace=ws, out=core)
+            return torch.matmul(core.flatten(-2), w_out)
+
+        for _ in range(8):
+            fwd()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(200):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fwd()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        ms = ts[len(ts) // 2]
+        res.append({"shape": f"B{B}-T{T}-H{Hd}-hd{hd}", "dtype": act, "ms": ms, "tokens/s": B * T / (ms * 1e-3),
+                    "pages_b200_fwd_ms": b200})
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +245,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-seqs", type=int, default=256,
                     help="sequences of the decode-step leg (0 skips it)")
+    ap.add_argument("--no-whole-layer", action="store_true",
+                    help="skip the whole-layer leg (projection GEMMs + layer core)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -283,7 +355,9 @@ def main() -> int:
 
     # the chunk stage: chunk prep + chunk state (two launches) where a workspace
     # applies, else the single recurrence kernel
-    chunk_kernel = ("chunk_prep_kernel+chunk_state_kernel" if cws is not None else "chunk_rule_kernel")
+    chunk_kernel = ("chunk_rule_kernel" if cws is None else
+                    "chunk_prep_kernel+chunk_state_wide_kernel" if s.dk == 256 else
+                    "chunk_prep_kernel+chunk_state_kernel")
     stages = {
         "prologue": {"kernel": "prologue_kernel", "ms": t_pro, "bytes": pb, "GB/s": gbs(pb, t_pro),
                      "hbm_frac": gbs(pb, t_pro) / HBM_PEAK_GBS},
@@ -313,6 +387,11 @@ def main() -> int:
         decode = decode_leg(gdn, synth, torch, s, d, dims, scale, args.decode_seqs, args.steps,
                             args.warmup)
 
+    whole = None
+    if not args.no_whole_layer:
+        print("[bench] whole-layer leg", file=sys.stderr, flush=True)
+        whole = whole_layer_leg(gdn, synth, torch)
+
     result = {
         "metric": METRIC,
         "value": ntok / (ms * 1e-3),
@@ -331,6 +410,7 @@ def main() -> int:
         "roofline": roof,
         "stages": stages,
         "decode": decode,
+        "whole_layer": whole,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

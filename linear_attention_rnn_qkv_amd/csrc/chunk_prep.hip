@@ -92,7 +92,7 @@ struct PrepLds {
 __device__ __forceinline__ int blk(int mi, int ni) { return mi * (mi + 1) / 2 + ni; }
 
 template <typename T, int DK, int NV>
-__global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_eu(NV == 2 ? 8 : 6))) void chunk_prep_kernel(
+__global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_eu(DK == 256 ? 4 : NV == 2 ? 8 : 6))) void chunk_prep_kernel(
     ChunkArgs p) {
   using MF = M2<T>;
   using f8 = typename MF::f8;
@@ -493,8 +493,10 @@ hipError_t launch_prep(const ChunkArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_chunk_prep(const ChunkArgs &a, hipStream_t s) {
-  if (a.act == kBF16) return a.dk == 64 ? launch_prep<bf16, 64>(a, s) : launch_prep<bf16, 128>(a, s);
-  if (a.act == kF16) return a.dk == 64 ? launch_prep<f16, 64>(a, s) : launch_prep<f16, 128>(a, s);
+  if (a.act == kBF16)
+    return a.dk == 64 ? launch_prep<bf16, 64>(a, s) : a.dk == 128 ? launch_prep<bf16, 128>(a, s) : launch_prep<bf16, 256>(a, s);
+  if (a.act == kF16)
+    return a.dk == 64 ? launch_prep<f16, 64>(a, s) : a.dk == 128 ? launch_prep<f16, 128>(a, s) : launch_prep<f16, 256>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -391,9 +391,10 @@ hipError_t launch_dk(const ChunkArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_chunk_prep(const ChunkArgs &a, hipStream_t s);
+hipError_t launch_chunk_state_wide(const ChunkArgs &a, hipStream_t s);
 
 bool chunk_split_supported(int64_t dk, int32_t act) {
-  return (act == kBF16 || act == kF16) && (dk == 64 || dk == 128);
+  return (act == kBF16 || act == kF16) && (dk == 64 || dk == 128 || dk == 256);
 }
 
 hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s) {
@@ -401,6 +402,7 @@ hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s) {
   if (!a.ws_rec || (a.cu_seqlens && !a.cu_chunks)) return hipErrorInvalidValue;
   hipError_t e = launch_chunk_prep(a, s);
   if (e != hipSuccess) return e;
+  if (a.dk == 256) return launch_chunk_state_wide(a, s);
   if (a.act == kBF16) return a.dk == 64 ? launch_dk<bf16, 64>(a, s) : launch_dk<bf16, 128>(a, s);
   if (a.act == kF16) return a.dk == 64 ? launch_dk<f16, 64>(a, s) : launch_dk<f16, 128>(a, s);
   return hipErrorInvalidValue;

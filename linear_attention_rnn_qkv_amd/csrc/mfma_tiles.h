@@ -70,15 +70,16 @@ __device__ __forceinline__ void g2l16(const void *gptr, unsigned char *lds) {
   __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)(lds_u8 *)lds, 16, 0, 0);
 }
 // XOR swizzle of the 16-byte units of a q/k tile row (DK 16-bit values per
-// row): row r's unit u is stored at unit u ^ kswz(r). For 256-byte rows the
-// mask is a GF(2)-linear map of r mod 16 (images of rows 1, 2, 4, 8: 6, 13,
+// row): row r's unit u is stored at unit u ^ kswz(r). For 256-byte rows (and
+// 512-byte rows, which span the 64 banks twice, so that the map acts on each
+// 256-byte half alike) the mask is a GF(2)-linear map of r mod 16 (images of rows 1, 2, 4, 8: 6, 13,
 // 8, 9), chosen by timing every invertible map on gfx950: 16-byte fragment
 // reads of 16 consecutive rows run without bank conflicts, and transposing
 // reads of 4 rows x 4 units per 16 lanes at the two-way minimum that 8-byte
 // reads of 32 lanes into one 16-byte column half allow.
 template <int DK>
 __device__ __forceinline__ constexpr int kswz(int r) {
-  if constexpr (DK == 128) return (int)((0xac7124f935e8bd60ull >> (4 * (r & 15))) & 15);
+  if constexpr (DK >= 128) return (int)((0xac7124f935e8bd60ull >> (4 * (r & 15))) & 15);
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 

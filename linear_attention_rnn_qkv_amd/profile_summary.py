@@ -33,6 +33,8 @@ KERNELS = {
                                                 "gdn_internal.h"]),
     "chunk_state_kernel": ("chunk_state_kernel", ["chunk_state.hip", "mfma_tiles.h", "device_common.h",
                                                   "gdn_internal.h"]),
+    "chunk_state_wide_kernel": ("chunk_state_wide_kernel", ["chunk_state_wide.hip", "mfma_tiles.h",
+                                                            "device_common.h", "gdn_internal.h"]),
     "chunk_rule_kernel": ("chunk_rule_kernel", ["chunk_rule.hip", "device_common.h", "gdn_internal.h"]),
     "prologue_kernel": ("prologue_kernel", ["prologue.hip", "device_common.h", "gdn_internal.h"]),
     "decode_kernel": ("decode_kernel", ["decode.hip", "device_common.h", "gdn_internal.h"]),

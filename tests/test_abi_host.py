@@ -35,9 +35,12 @@ def test_workspace_bytes():
     B, T, dims = 2, 1000, (6, 256, 6, 512)
     C = 2 * 6 * 256 + 6 * 512
     expect = a256(B * T * C * 2) + 2 * a256(B * T * 6 * 4) + a256(B * T * 6 * 512 * 2)
-    # dk = 256: the single-kernel recurrence, no chunk workspace
-    assert gdn.gdn_chunk_rule_workspace_bytes(B, T, dims, torch.bfloat16) == 0
-    assert gdn.gdn_layer_workspace_bytes(B, T, dims, torch.bfloat16) == expect
+    # dk = 256 BF16: chunk offsets, then one 14336-byte record per (chunk, value head)
+    cws = a256((B + 1) * 4) + B * 16 * 6 * 14336
+    assert gdn.gdn_chunk_rule_workspace_bytes(B, T, dims, torch.bfloat16) == cws
+    assert gdn.gdn_layer_workspace_bytes(B, T, dims, torch.bfloat16) == expect + cws
+    # FP32: the single-kernel recurrence, no chunk workspace
+    assert gdn.gdn_chunk_rule_workspace_bytes(B, T, dims, torch.float32) == 0
     assert gdn.gdn_layer_workspace_bytes(B, T, (0, 64, 1, 64), torch.bfloat16) == 0
     # dk = 128 BF16: chunk offsets, then one 14336-byte record per (chunk, value head)
     d2 = (16, 128, 32, 128)

@@ -170,11 +170,12 @@ def test_chunk_rule_no_decay(cfg, path):
 
 
 @pytest.mark.parametrize("path", list(PATHS))
-@pytest.mark.parametrize("dk,hqk,hv", [(64, 2, 8), (128, 4, 4), (64, 3, 3)], ids=["dk64-G4", "dk128-G1", "dk64-G1"])
+@pytest.mark.parametrize("dk,hqk,hv", [(64, 2, 8), (128, 4, 4), (64, 3, 3), (256, 2, 4), (256, 3, 3)],
+                         ids=["dk64-G4", "dk128-G1", "dk64-G1", "dk256-G2", "dk256-G1"])
 def test_chunk_rule_head_dims_and_group_sizes(dk, hqk, hv, path):
-    # The two-kernel path has separate code for dk 64 and 128 and for odd and
-    # even GQA group sizes; each is checked against the oracle with a state in
-    # and out.
+    # The two-kernel path has separate code for dk 64, 128 and 256 (its own
+    # state kernel) and for odd and even GQA group sizes; each is checked
+    # against the oracle with a state in and out.
     over = {"T": 300, "Hqk": hqk, "Hv": hv, "dk": dk}
     s, x, qkv, g, beta = _stress_inputs(3, over, 0)
     q, k, v = H.split_qkv(qkv, s)
@@ -206,6 +207,26 @@ def test_chunk_rule_empty_and_one_token_sequences(path):
     H.assert_close(f64(o), O.round_to(ro, s.act), TAU[s.act], "o")
     H.assert_close(f64(fin), rfin, TAU[s.act], "final state")
     assert torch.equal(fin[0], S0[0]) and torch.equal(fin[2], S0[2])
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_chunk_rule_dk256_packed_fp16_with_empty_sequences(path):
+    # dk = 256 on packed FP16 sequences of length 0, 1, partial and several
+    # chunks, with an initial state.
+    s, x, qkv, g, beta = _stress_inputs(4, {"lengths": (0, 130, 1, 64, 0, 7), "Hqk": 2, "Hv": 4, "dk": 256,
+                                            "dv": 64}, 0)
+    q, k, v = H.split_qkv(qkv, s)
+    cu = H.cu_of(x)
+    qd, kd, vd, gd, bd, cud = _gpu_stage_inputs(s, qkv, g, beta, cu)
+    S0 = synth.randn((len(cu) - 1, s.Hv, s.dv, s.dk), "f32", 81).cuda() * 0.5
+    o, fin = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.0625, True, 1e-6, cud, S0, output_final_state=True,
+                                    workspace=PATHS[path])
+    torch.cuda.synchronize()
+    ro, rfin = O.gated_delta_rule(q, k, v, g, beta, scale=0.0625, cu_seqlens=cu, initial_state=f64(S0),
+                                  output_final_state=True)
+    H.assert_close(f64(o), O.round_to(ro, s.act), TAU[s.act], "o")
+    H.assert_close(f64(fin), rfin, TAU[s.act], "final state")
+    assert torch.equal(fin[0], S0[0]) and torch.equal(fin[4], S0[4])
 
 
 @pytest.mark.parametrize("path", list(PATHS))
