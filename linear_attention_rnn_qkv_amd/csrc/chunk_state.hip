@@ -393,8 +393,11 @@ hipError_t launch_dk(const ChunkArgs &a, hipStream_t s) {
 hipError_t launch_chunk_prep(const ChunkArgs &a, hipStream_t s);
 hipError_t launch_chunk_state_wide(const ChunkArgs &a, hipStream_t s);
 
-bool chunk_split_supported(int64_t dk, int32_t act) {
-  return (act == kBF16 || act == kF16) && (dk == 64 || dk == 128 || dk == 256);
+// dv is covered in slices of 16 rows (dk <= 128) or 32 rows (dk 256).
+bool chunk_split_supported(int64_t dk, int64_t dv, int32_t act) {
+  if (act != kBF16 && act != kF16) return false;
+  if (dk == 64 || dk == 128) return dv % 16 == 0;
+  return dk == 256 && dv % 32 == 0;
 }
 
 hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s) {

@@ -13,14 +13,19 @@
 //
 // At dk = 256 a q or k tile of a chunk is 32 KB, so the three-slot LDS rings
 // of the dk <= 128 kernel do not fit. Here one workgroup = (sequence, value
-// head, 16 rows of dv) with four wavefronts and one barrier per chunk:
-//   wave 0     the whole step of chunk s: X and (Q S0^T)^T share the state
-//              fragments, then T' V, Vn, O^T (stored) and the state update;
-//              S lives in MFMA accumulators.
-//   waves 1-3  copy the k tile, the q tile, and the record with the v slice
-//              of chunk s + 1 into the other slot of two-slot LDS rings
-//              (global_load_lds); the copies are complete before the
-//              barrier that starts step s + 1.
+// head, 32 rows of dv) with four wavefronts and one barrier per chunk:
+//   waves 0, 1  the whole step of chunk s for 16 rows of dv each: X and
+//               (Q S0^T)^T share the state fragments, then T' V, Vn, O^T
+//               (stored) and the state update; S lives in MFMA
+//               accumulators. Each wave loads its own V fragments for the
+//               next chunk straight into registers.
+//   waves 2, 3  copy the k tile, the q tile and the record of chunk s + 1
+//               into the other slot of two-slot LDS rings (global_load_lds);
+//               the copies are complete before the barrier that starts
+//               step s + 1.
+// Two compute waves per workgroup halve the workgroup count for the same
+// LDS, so that a whole launch of the common shapes is resident at once (the
+// rings take almost all of a CU's 160 KB).
 // The operand layouts, the dk permutation of the state tiles and the XOR
 // swizzle of the q/k tiles are those of the dk <= 128 kernel.
 #include "gdn_internal.h"
@@ -31,7 +36,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int BT = 64;
-constexpr int DVT = 16;
+constexpr int DVT = 32;  // dv rows per workgroup, 16 per compute wave
 // bytes of the record the step reads: T', P and the factor rows aa, cw, zc,
 // beta, then e^{gamma_C} (one 16-byte unit)
 constexpr int kRecUse = (int)kRecF + 4 * BT * 4 + 16;
@@ -43,7 +48,6 @@ struct WideLds {
   alignas(16) unsigned char k[2][TILE];   // k rows of chunk c in slot c % 2 (swizzled)
   alignas(16) unsigned char q[2][TILE];   // q rows
   alignas(16) unsigned char rec[2][kRecUse];
-  alignas(16) T v[2][BT * DVT];           // v slice, row-major [64][16]
 };
 
 // dk permutation of the state accumulator tiles: tile mt = 2 pp + h, row
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_wide_kernel(ChunkArgs p)
   constexpr int RB = SM::RB;
   constexpr int NI = SM::TILE / 1024;  // 1 KB copies per q/k tile
   constexpr int NRC = kRecUse / 1024;  // whole 1 KB copies of the record
-  static_assert(NI <= 32 && NRC + 3 <= 32, "copies per lane and step");
+  static_assert(NI + NRC + 1 <= 48, "copies per lane and step");
   __shared__ SM sm;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -106,8 +110,9 @@ __global__ __launch_bounds__(kThreads) void chunk_state_wide_kernel(ChunkArgs p)
     return (int)(r < BT ? r : BT);
   };
 
-  if (wave == 0) {
+  if (wave < 2) {
     // ------------------------------------------------------------ the step
+    const int64_t jw = 16 * wave;  // this wave's dv rows j0 + jw .. + 15
     int fo[KT];  // row c of a 16-row tile, dk 32 pp + 8 g .. + 7
 #pragma unroll
     for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
@@ -116,25 +121,39 @@ __global__ __launch_bounds__(kThreads) void chunk_state_wide_kernel(ChunkArgs p)
     for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S[mt][i] = p.init_state ? p.init_state[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] : 0.f;
+        S[mt][i] = p.init_state ? p.init_state[st_base + (jw + c) * DK + dk_of(mt, 4 * g + i)] : 0.f;
     f8 Sf[KT];
 #pragma unroll
     for (int pp = 0; pp < KT; ++pp) Sf[pp] = cat8<T>(cvt4<T>(S[2 * pp]), cvt4<T>(S[2 * pp + 1]));
     // transposing reads of K^T fragments for the state update: lane 16 g + c
     // addresses row 4 g + c / 4 at dk dk_of(mt, 4 (c % 4)) .. + 3
     const int yrow = 4 * g + (c >> 2);
-    // V fragments (B operand of T' V) by transposing reads of the [64][16]
-    // v tile: lane 16 g + L reads the 4 values of row 4 g + L / 4 starting at
-    // column 4 (L % 4)
-    const int vtr = (4 * g + (c >> 2)) * (DVT * 2) + 8 * (c & 3);
+    // V fragments (B operand of T' V): lane (g, c) holds V[32 q + 16 hh + 4 g + i]
+    // [dv jw + c] in element 4 hh + i of fragment q; loaded from global one
+    // chunk ahead (rows past the end repeat the last row)
+    const T *vw = vb + jw + c;
+    auto load_v = [&](int cl, f8(&bv)[2]) {
+      const int nr = rows_of(cl);
+      const T *vc = vw + (int64_t)cl * BT * p.sv_t;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 32 * q + 16 * (e >> 2) + 4 * g + (e & 3);
+          bv[q][e] = vc[(int64_t)(r < nr ? r : nr - 1) * p.sv_t];
+        }
+    };
+    f8 Bn[2];
+    if (Nc > 0) load_v(0, Bn);
     for (int s = 0; s < Nc; ++s) {
       lds_barrier();
+      const f8 Bv[2] = {Bn[0], Bn[1]};
+      if (s + 1 < Nc) load_v(s + 1, Bn);
       const int sl = s & 1;
       const unsigned char *kt = sm.k[sl];
       const unsigned char *qt = sm.q[sl];
       const unsigned char *rec = sm.rec[sl];
       const float *fa = reinterpret_cast<const float *>(rec + kRecF);
-      const T *vt = sm.v[sl];
       const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
       // X = K S0^T and Z^T = S0 Q^T (lane (g, c) of z[mt]: Z[16 mt + c][dv 4 g + i])
       f32x4 X[4], z[4];
@@ -165,16 +184,6 @@ __global__ __launch_bounds__(kThreads) void chunk_state_wide_kernel(ChunkArgs p)
         Zc[mt] = z[mt] * fa[2 * BT + 16 * mt + c];
       }
       const float eC = fa[4 * BT];
-      // B operands of T' V: rows 32 q + 16 hh + 4 g + i, column c
-      f8 Bv[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const unsigned char *vb8 = reinterpret_cast<const unsigned char *>(vt) + vtr + 32 * q * (DVT * 2);
-        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb8));
-        const s16x4 r1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb8 + 16 * DVT * 2));
-        Bv[q] = cat8<T>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
-      }
       // Vn = T' V - T' (aa (.) X)
       f8 Rf[2];
 #pragma unroll
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_wide_kernel(ChunkArgs p)
       // O^T = Zc^T + Vn^T P^T: lane (g, c) holds o[16 mt + c][4 g .. 4 g + 3]
       {
         const int nr = rows_of(s);
-        T *orow = ob + (int64_t)s * BT * p.so_t;
+        T *orow = ob + jw + (int64_t)s * BT * p.so_t;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           f32x4 o = MF::k32(Wf[0], Pf[frag_id(mt, 0)], Zc[mt]);
@@ -230,43 +239,35 @@ __global__ __launch_bounds__(kThreads) void chunk_state_wide_kernel(ChunkArgs p)
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p.final_state[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] = S[mt][i];
+        for (int i = 0; i < 4; ++i) p.final_state[st_base + (jw + c) * DK + dk_of(mt, 4 * g + i)] = S[mt][i];
     }
   } else {
     // ------------------------------------------------------------ copies
-    // wave 1: the k tile, wave 2: the q tile, wave 3: the record and the v
-    // slice, of chunk cl into slot cl % 2.
-    const int role = wave - 1;
+    // wave 2: the k tile and the first half of the record; wave 3: the q
+    // tile, the rest of the record and its last 16 bytes; of chunk cl into
+    // slot cl % 2.
+    const int role = wave - 2;
+    constexpr int NR0 = (NRC + 1) / 2;
     auto issue = [&](int cl) {
       const int sl = cl & 1;
       const int nr = rows_of(cl);
       const int64_t t0 = (int64_t)cl * BT;
-      if (role < 2) {
-        const bool isk = role == 0;
-        const int64_t st = isk ? p.sk_t : p.sq_t;
-        const T *xb = (isk ? kb : qb) + t0 * st;
-        unsigned char *xt = isk ? sm.k[sl] : sm.q[sl];
+      const bool isk = role == 0;
+      const int64_t st = isk ? p.sk_t : p.sq_t;
+      const T *xb = (isk ? kb : qb) + t0 * st;
+      unsigned char *xt = isk ? sm.k[sl] : sm.q[sl];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int b = 1024 * i + 16 * lane;
-          const int r = b / RB, jp = (b % RB) >> 4;
-          const int j = jp ^ kswz<DK>(r);
-          const int rr = r < nr ? r : nr - 1;  // rows past the end repeat the last row
-          g2l16(xb + (int64_t)rr * st + 8 * j, xt + 1024 * i);
-        }
-      } else {
-        const unsigned char *rg = recb + (int64_t)cl * rec_stride;
-#pragma unroll
-        for (int i = 0; i < NRC; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * i);
-        if (lane == 0) g2l16(rg + 1024 * NRC, sm.rec[sl] + 1024 * NRC);
-        unsigned char *vt = reinterpret_cast<unsigned char *>(sm.v[sl]);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int r = 32 * half + (lane >> 1);
-          const int rr = r < nr ? r : nr - 1;
-          g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane & 1), vt + 1024 * half);
-        }
+      for (int i = 0; i < NI; ++i) {
+        const int b = 1024 * i + 16 * lane;
+        const int r = b / RB, jp = (b % RB) >> 4;
+        const int j = jp ^ kswz<DK>(r);
+        const int rr = r < nr ? r : nr - 1;  // rows past the end repeat the last row
+        g2l16(xb + (int64_t)rr * st + 8 * j, xt + 1024 * i);
       }
+      const unsigned char *rg = recb + (int64_t)cl * rec_stride;
+      const int i0 = isk ? 0 : NR0, i1 = isk ? NR0 : NRC;
+      for (int i = i0; i < i1; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * i);
+      if (!isk && lane == 0) g2l16(rg + 1024 * NRC, sm.rec[sl] + 1024 * NRC);
     };
     if (Nc > 0) issue(0);
     wait_vm<0>();

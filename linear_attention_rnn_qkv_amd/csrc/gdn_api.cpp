@@ -518,7 +518,7 @@ int64_t chunk_bound_of(int64_t B, int64_t T, int64_t n_seqs) {
   return n_seqs > 0 ? nc + n_seqs : B * nc;
 }
 size_t chunk_ws_bytes(int64_t B, int64_t T, int64_t n_seqs, int64_t dk, int64_t Hv, int64_t dv, int32_t act) {
-  if (!gdn::chunk_split_supported(dk, act) || dv % 16) return 0;
+  if (!gdn::chunk_split_supported(dk, dv, act)) return 0;
   const int64_t N = n_seqs > 0 ? n_seqs : B;
   return align256((size_t)(N + 1) * 4) + (size_t)chunk_bound_of(B, T, n_seqs) * (size_t)Hv * (size_t)gdn::kRecBytes;
 }
@@ -529,7 +529,7 @@ gdn_status attach_chunk_ws(gdn::ChunkArgs *p, void *ws, size_t ws_bytes) {
   p->cu_chunks = nullptr;
   p->chunk_bound = 0;
   if (!ws) return GDN_OK;
-  if (!gdn::chunk_split_supported(p->dk, p->act) || !p->rows16 || !p->o8 || p->dv % 16) return GDN_OK;  // not used
+  if (!gdn::chunk_split_supported(p->dk, p->dv, p->act) || !p->rows16 || !p->o8) return GDN_OK;  // not used
   const int64_t ns = p->cu_seqlens ? p->n_seqs : 0;
   const size_t need = chunk_ws_bytes(p->B, p->T, ns, p->dk, p->Hv, p->dv, p->act);
   if (ws_bytes < need)

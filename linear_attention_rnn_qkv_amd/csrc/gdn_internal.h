@@ -121,7 +121,7 @@ hipError_t launch_chunk_rule_v2(const ChunkArgs &a, hipStream_t s);
 
 // Two-kernel path: chunk prep (parallel over chunks and heads) then chunk
 // state (serial over chunks). Needs a.ws_rec / a.cu_chunks.
-bool chunk_split_supported(int64_t dk, int32_t act);
+bool chunk_split_supported(int64_t dk, int64_t dv, int32_t act);
 hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s);
 
 // Largest power-of-two alignment (bytes, <= 16) of an address or stride set.

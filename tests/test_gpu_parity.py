@@ -229,6 +229,20 @@ def test_chunk_rule_dk256_packed_fp16_with_empty_sequences(path):
     assert torch.equal(fin[0], S0[0]) and torch.equal(fin[4], S0[4])
 
 
+def test_chunk_rule_dk256_narrow_dv_falls_back():
+    # dk 256 with dv = 16 (not a multiple of the 32-row slices of the two-kernel
+    # path) runs the single-kernel recurrence even with a workspace.
+    s, x, qkv, g, beta = _stress_inputs(3, {"T": 100, "Hqk": 2, "Hv": 2, "dk": 256, "dv": 16}, 0)
+    assert gdn.gdn_chunk_rule_workspace_bytes(s.B, s.T, (s.Hqk, s.dk, s.Hv, s.dv), torch.bfloat16) == 0
+    q, k, v = H.split_qkv(qkv, s)
+    qd, kd, vd, gd, bd, _ = _gpu_stage_inputs(s, qkv, g, beta, None)
+    o, fin = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, 0.0625, True, 1e-6, output_final_state=True)
+    torch.cuda.synchronize()
+    ro, rfin = O.gated_delta_rule(q, k, v, g, beta, scale=0.0625, output_final_state=True)
+    H.assert_close(f64(o), O.round_to(ro, s.act), TAU[s.act], "o")
+    H.assert_close(f64(fin), rfin, TAU[s.act], "final state")
+
+
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("T", [1, 63, 65])
 def test_chunk_rule_short_sequences(T, path):
