@@ -1,0 +1,113 @@
+"""FP64 CPU oracle of the layer core's backward (first-order gradients).
+
+TEST INFRASTRUCTURE, like the rest of ``oracle/``: only ``tests/`` may use it;
+the HIP library never does, and the two share no code.
+
+The Megatron Core page "GDN Elementwise Fusion" (Execution and numerical
+behavior) states that the fused stages support first-order autograd; the
+Megatron-LM L2-fold pull request (Validation) and the flash-linear-attention
+fused-conv pull request (Test plan) check input and parameter gradients.
+Neither prints the backward formulas, so each function here is the plain
+forward definition of a stage, written in float64 with PyTorch CPU tensors,
+differentiated by autograd (a library primitive). Reading: the backward is the
+derivative of the stage's exact function (the activation-dtype roundings of
+the forward are treated as the identity), evaluated at the given stored
+values.
+
+Parity status: pinned by finite differences (``torch.autograd.gradcheck``,
+independent of autograd's own derivative rules) on small inputs and by closed
+forms at special points; see ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def _t(x, grad=False):
+    if x is None:
+        return None
+    t = torch.as_tensor(np.asarray(x, dtype=np.float64)).clone()
+    return t.requires_grad_(grad)
+
+
+def _np(t):
+    return None if t is None else t.detach().numpy()
+
+
+# --------------------------------------------------------------------------
+# Gated RMSNorm: out = (o * r * w) * silu(gate), r = (mean(o^2) + eps)^-1/2
+# --------------------------------------------------------------------------
+def gated_rmsnorm_fn(o, gate, w, eps):
+    """The forward of the gated norm (P2 option table, Execution and numerical
+    behavior) on float64 tensors, without the activation-dtype roundings."""
+    r = torch.rsqrt(torch.mean(o * o, dim=-1, keepdim=True) + eps)
+    return (o * r * w) * (gate * torch.sigmoid(gate))
+
+
+def gated_rmsnorm_bwd(o, gate, weight, dout, eps: float = 1e-5):
+    """Gradients (d_o, d_gate, d_weight) of sum(dout * out). o, gate, dout:
+    [..., dv]; weight: [dv]. d_weight sums over every row."""
+    o_, g_, w_ = _t(o, True), _t(gate, True), _t(weight, True)
+    out = gated_rmsnorm_fn(o_, g_, w_, eps)
+    d = torch.autograd.grad(out, (o_, g_, w_), _t(dout))
+    return tuple(_np(x) for x in d)
+
+
+# --------------------------------------------------------------------------
+# Prologue: conv + SiLU over q|k|v channels, beta and g
+# --------------------------------------------------------------------------
+def conv_silu_fn(x, w, bias, cu_seqlens=None):
+    """Depthwise causal conv (tap j multiplies token t - 3 + j, zero history
+    before each sequence start), bias, then SiLU (P3 Summary). x: [B, T, C];
+    w: [C, K]; bias: [C] or None. With cu_seqlens, B is 1 and every packed
+    sequence starts with zero history."""
+    B, T, C = x.shape
+    K = w.shape[1]
+
+    def conv_one(xs):  # one sequence [L, C]
+        L = xs.shape[0]
+        acc = torch.zeros((L, C), dtype=x.dtype)
+        if bias is not None:
+            acc = acc + bias[None, :]
+        for j in range(K):
+            lag = K - 1 - j  # tap j reads token t - lag
+            if lag >= L:
+                continue
+            shifted = torch.cat([torch.zeros((lag, C), dtype=x.dtype), xs[:L - lag]], 0)
+            acc = acc + w[None, :, j] * shifted
+        return acc
+
+    if cu_seqlens is None:
+        y = torch.stack([conv_one(x[i]) for i in range(B)], 0)
+    else:
+        cu = [int(c) for c in cu_seqlens]
+        y = torch.cat([conv_one(x[0, cu[n]:cu[n + 1]]) for n in range(len(cu) - 1)], 0)[None]
+    return y * torch.sigmoid(y)
+
+
+def beta_g_fn(b, a, A_log, dt_bias):
+    """beta = sigmoid(b); g = -exp(A_log) * softplus(a + dt_bias), softplus
+    returning its argument above 20 (the forward's reading)."""
+    beta = torch.sigmoid(b)
+    sp = torch.nn.functional.softplus(a + dt_bias, beta=1.0, threshold=20.0)
+    return beta, -torch.exp(A_log) * sp
+
+
+def prologue_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, d_qkv, d_g, d_beta,
+                 cu_seqlens=None):
+    """Gradients of sum(d_qkv * qkv) + sum(d_g * g) + sum(d_beta * beta) with
+    respect to x_q, x_k, x_v, conv_w, conv_b (None if absent), a, b, A_log and
+    dt_bias. qkv is the concatenated conv output [B, T, C]."""
+    xq, xk, xv = _t(x_q, True), _t(x_k, True), _t(x_v, True)
+    w, bias = _t(conv_w, True), _t(conv_b, True)
+    a_, b_, al, db_ = _t(a, True), _t(b, True), _t(A_log, True), _t(dt_bias, True)
+    x = torch.cat([xq, xk, xv], -1)
+    z = conv_silu_fn(x, w, bias, cu_seqlens)
+    beta, g = beta_g_fn(b_, a_, al, db_)
+    ins = [xq, xk, xv, w] + ([bias] if bias is not None else []) + [a_, b_, al, db_]
+    d = torch.autograd.grad((z, g, beta), ins, (_t(d_qkv), _t(d_g), _t(d_beta)))
+    d = [_np(t) for t in d]
+    if bias is None:
+        d.insert(4, None)
+    return tuple(d)
