@@ -14,6 +14,8 @@
  *   gdn_layer_fwd       the three stages in order, in a caller workspace
  *   gdn_decode_fwd      one recurrent step per sequence (conv cache and FP32
  *                       state updated in place), all stages in one kernel
+ *   gdn_gated_norm_bwd, gdn_prologue_bwd   first-order gradients of the
+ *                       gated norm and of the prologue
  *
  * Sources (web pages):
  *   [P1] Megatron-LM pull request "perf(gated_delta_net): fold q/k L2-norm
@@ -290,6 +292,74 @@ gdn_status gdn_decode_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
                           int32_t use_qk_l2norm_in_kernel, float l2_eps,
                           const gdn_tensor *gate, const gdn_tensor *norm_w,
                           float rms_eps, const gdn_tensor *out, void *stream);
+
+/*
+ * Backward (first-order gradients). The Megatron Core page "GDN Elementwise
+ * Fusion" (Execution and numerical behavior) gives the fused stages
+ * first-order autograd; the Megatron-LM L2-fold pull request (Validation) and
+ * the flash-linear-attention fused-conv pull request (Test plan) check input
+ * and parameter gradients. The gradients are those of the stage's exact
+ * function (the forward's activation-dtype roundings taken as the identity),
+ * computed in FP32. Parameter gradients are sums over tokens; each call adds
+ * them up in a fixed order (deterministic), using a caller workspace for the
+ * partial sums (256-byte aligned, at least the size the matching
+ * *_workspace_bytes call returns, not used by another call until this one's
+ * work on `stream` is done).
+ *
+ * gdn_gated_norm_bwd - with r, n = o r, y = n weight, out = y silu(gate) as
+ * in gdn_gated_norm_fwd, for the gradient dout of out:
+ *     d_gate = dout y silu'(gate),  dn = dout silu(gate) weight,
+ *     d_o = r (dn - n mean(dn n)),  d_weight = sum over rows of
+ *     dout silu(gate) n
+ *   o, gate, weight, eps  as in gdn_gated_norm_fwd
+ *   dout      [B, T, H, dv] o's dtype, any strides, inner 1
+ *   d_o       [B, T, H, dv] o's dtype, contiguous, 16-byte aligned
+ *   d_gate    [B, T, H, dv] gate's dtype, contiguous, 16-byte aligned
+ *   d_weight  [dv] F32 (written, not accumulated)
+ */
+size_t gdn_gated_norm_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H,
+                                          int64_t dv);
+gdn_status gdn_gated_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate,
+                              const gdn_tensor *weight, float eps,
+                              const gdn_tensor *dout, const gdn_tensor *d_o,
+                              const gdn_tensor *d_gate,
+                              const gdn_tensor *d_weight, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_prologue_bwd - gradients of the prologue (gdn_prologue_fwd with
+ * caller_l2norm = 0) for the gradients d_qkv of its conv output, d_g of g and
+ * d_beta of beta. Per channel c of each sequence, y_t = bias + sum_j
+ * w_j x_{t-3+j}, z_t = silu(y_t), e_t = d_qkv_t silu'(y_t):
+ *     dx_t = sum_j w_j e_{t+3-j} (tokens of the same sequence),
+ *     d_conv_w[c, j] = sum_t e_t x_{t-3+j},  d_conv_b[c] = sum_t e_t
+ *     d_b = d_beta beta (1 - beta),
+ *     d_a = -d_g exp(A_log) sigmoid(a + dt_bias)  (1 above softplus's 20),
+ *     d_dt_bias = sum of d_a,  d_A_log = sum of d_g g
+ *   x_q .. cu_seqlens, dims  as in gdn_prologue_fwd
+ *   d_qkv     [B, T, C] act dtype or F32, contiguous
+ *   d_g, d_beta  [B, T, Hv] F32, contiguous
+ *   dx_q, dx_k [B, T, Hqk*dk], dx_v [B, T, Hv*dv]  act dtype, contiguous
+ *   d_conv_w  [C, 4] F32;  d_conv_b [C] F32, given exactly when conv_b is
+ *   d_a, d_b  [B, T, Hv] act dtype, contiguous
+ *   d_A_log, d_dt_bias [Hv] F32
+ */
+size_t gdn_prologue_bwd_workspace_bytes(int64_t B, int64_t T,
+                                        const gdn_dims *dims);
+gdn_status gdn_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
+                            const gdn_tensor *x_v, const gdn_tensor *conv_w,
+                            const gdn_tensor *conv_b, const gdn_tensor *a,
+                            const gdn_tensor *b, const gdn_tensor *A_log,
+                            const gdn_tensor *dt_bias,
+                            const gdn_tensor *cu_seqlens, const gdn_dims *dims,
+                            const gdn_tensor *d_qkv, const gdn_tensor *d_g,
+                            const gdn_tensor *d_beta, const gdn_tensor *dx_q,
+                            const gdn_tensor *dx_k, const gdn_tensor *dx_v,
+                            const gdn_tensor *d_conv_w,
+                            const gdn_tensor *d_conv_b, const gdn_tensor *d_a,
+                            const gdn_tensor *d_b, const gdn_tensor *d_A_log,
+                            const gdn_tensor *d_dt_bias, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

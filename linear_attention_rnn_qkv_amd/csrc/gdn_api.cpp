@@ -511,6 +511,197 @@ gdn_status plan_decode(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_t
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// ------------------------------------------------------------- backward
+int64_t norm_bwd_blocks(int64_t rows, int64_t dv) {
+  const int64_t rpb = 2048 / dv;  // rows per block and pass (4 waves, dv / 8 lanes per row)
+  const int64_t nb = (rows + rpb - 1) / rpb;
+  return nb < 1024 ? nb : 1024;
+}
+
+gdn_status plan_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_tensor *weight, float eps,
+                         const gdn_tensor *dout, const gdn_tensor *d_o, const gdn_tensor *d_gate,
+                         const gdn_tensor *d_weight, void *ws, size_t ws_bytes, gdn::NormBwdArgs *P) {
+  gdn::NormArgs f;
+  // o, gate, weight and eps as in the forward; d_o stands in for its output
+  TRY(plan_norm(o, gate, weight, eps, d_o, &f));
+  const int64_t so[4] = {f.B, f.T, f.H, f.dv}, sw[1] = {f.dv};
+  TRY(check(dout, "dout", 4, so));
+  TRY(check_dtype(dout, "dout", f.act));
+  TRY(check_inner(dout, "dout"));
+  TRY(check(d_gate, "d_gate", 4, so));
+  TRY(check_dtype(d_gate, "d_gate", gate->dtype));
+  TRY(check_contig(d_gate, "d_gate"));
+  TRY(check(d_weight, "d_weight", 1, sw));
+  TRY(check_dtype(d_weight, "d_weight", GDN_F32));
+  TRY(check_contig(d_weight, "d_weight"));
+  const gdn_tensor *ins[] = {o, gate, weight, dout};
+  const gdn_tensor *outs[] = {d_o, d_gate, d_weight};
+  for (auto *x : outs)
+    for (auto *i : ins)
+      if (overlaps(x, i)) return fail(GDN_ERR_INVALID_VALUE, "an output overlaps an input");
+  if (overlaps(d_o, d_gate) || overlaps(d_o, d_weight) || overlaps(d_gate, d_weight))
+    return fail(GDN_ERR_INVALID_VALUE, "outputs overlap each other");
+  if ((uintptr_t)d_gate->data % 16) return fail(GDN_ERR_NOT_SUPPORTED, "d_gate must be 16-byte aligned");
+  const int64_t nb = norm_bwd_blocks(f.B * f.T * f.H, f.dv);
+  const size_t need = (size_t)nb * (size_t)f.dv * 4;
+  if (!ws || ws_bytes < need)
+    return fail(GDN_ERR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  if ((uintptr_t)ws % 256) return fail(GDN_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  gdn::NormBwdArgs &p = *P;
+  memset(&p, 0, sizeof p);
+  p.o = f.o; p.so_b = f.so_b; p.so_t = f.so_t; p.so_h = f.so_h;
+  p.gate = f.gate; p.sg_b = f.sg_b; p.sg_t = f.sg_t; p.sg_h = f.sg_h;
+  p.dout = dout->data; p.sd_b = dout->stride[0]; p.sd_t = dout->stride[1]; p.sd_h = dout->stride[2];
+  p.w = f.w; p.d_o = d_o->data; p.d_gate = d_gate->data;
+  p.d_w = static_cast<float *>(d_weight->data);
+  p.part = static_cast<float *>(ws);
+  p.nblocks = nb;
+  p.B = f.B; p.T = f.T; p.H = f.H; p.dv = f.dv;
+  p.act = f.act; p.gate_dtype = f.gate_dtype; p.w_dtype = f.w_dtype;
+  p.o_align = f.o_align; p.gate_align = f.gate_align; p.dout_align = row_align(dout, 3);
+  p.eps = eps;
+  return GDN_OK;
+}
+
+constexpr int64_t kBwdTile = 256;  // tokens per tile of the prologue backward
+
+size_t prologue_bwd_ws(int64_t B, int64_t T, const gdn_dims *d) {
+  const int64_t ntiles = (B * T + kBwdTile - 1) / kBwdTile;
+  const int64_t C = 2 * d->Hqk * d->dk + d->Hv * d->dv;
+  return align256((size_t)(ntiles * C * 5 * 4)) + align256((size_t)(ntiles * d->Hv * 2 * 4));
+}
+
+gdn_status plan_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
+                             const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *a,
+                             const gdn_tensor *b, const gdn_tensor *A_log, const gdn_tensor *dt_bias,
+                             const gdn_tensor *cu_seqlens, const gdn_dims *dims, const gdn_tensor *d_qkv,
+                             const gdn_tensor *d_g, const gdn_tensor *d_beta, const gdn_tensor *dx_q,
+                             const gdn_tensor *dx_k, const gdn_tensor *dx_v, const gdn_tensor *d_conv_w,
+                             const gdn_tensor *d_conv_b, const gdn_tensor *d_a, const gdn_tensor *d_b,
+                             const gdn_tensor *d_A_log, const gdn_tensor *d_dt_bias, void *ws, size_t ws_bytes,
+                             gdn::PrologueBwdArgs *P) {
+  TRY(check_dims(dims));
+  if (!x_q) return fail(GDN_ERR_INVALID_VALUE, "x_q: descriptor is NULL");
+  if (x_q->ndim != 3) return fail(GDN_ERR_INVALID_VALUE, "x_q: expected [B, T, Hqk*dk]");
+  const int64_t B = x_q->shape[0], T = x_q->shape[1], Hv = dims->Hv;
+  const int64_t nq = dims->Hqk * dims->dk, nv = Hv * dims->dv, C = 2 * nq + nv;
+  const int64_t sq[3] = {B, T, nq}, sv[3] = {B, T, nv}, sw[2] = {C, 4}, sc[1] = {C};
+  const int64_t sab[3] = {B, T, Hv}, sh[1] = {Hv}, so[3] = {B, T, C};
+  if (B * T == 0) return fail(GDN_ERR_INVALID_VALUE, "empty input (B*T == 0)");
+  TRY(check(x_q, "x_q", 3, sq));
+  const int32_t act = x_q->dtype;
+  if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "x_q: dtype must be F32, BF16 or F16");
+  TRY(check(x_k, "x_k", 3, sq));
+  TRY(check(x_v, "x_v", 3, sv));
+  TRY(check_dtype(x_k, "x_k", act));
+  TRY(check_dtype(x_v, "x_v", act));
+  TRY(check_inner(x_q, "x_q"));
+  TRY(check_inner(x_k, "x_k"));
+  TRY(check_inner(x_v, "x_v"));
+  TRY(check(conv_w, "conv_w", 2, sw));
+  if (conv_w->dtype != act && conv_w->dtype != GDN_F32)
+    return fail(GDN_ERR_INVALID_VALUE, "conv_w: dtype must be the activation dtype or F32");
+  TRY(check_contig(conv_w, "conv_w"));
+  if (conv_b) {
+    TRY(check(conv_b, "conv_b", 1, sc));
+    if (conv_b->dtype != act && conv_b->dtype != GDN_F32)
+      return fail(GDN_ERR_INVALID_VALUE, "conv_b: dtype must be the activation dtype or F32");
+    TRY(check_contig(conv_b, "conv_b"));
+  }
+  TRY(check(a, "a", 3, sab));
+  TRY(check(b, "b", 3, sab));
+  TRY(check_dtype(a, "a", act));
+  TRY(check_dtype(b, "b", act));
+  TRY(check_inner(a, "a"));
+  TRY(check_inner(b, "b"));
+  TRY(check(A_log, "A_log", 1, sh));
+  TRY(check(dt_bias, "dt_bias", 1, sh));
+  TRY(check_dtype(A_log, "A_log", GDN_F32));
+  TRY(check_dtype(dt_bias, "dt_bias", GDN_F32));
+  TRY(check_contig(A_log, "A_log"));
+  TRY(check_contig(dt_bias, "dt_bias"));
+  int64_t n_seqs = 0;
+  TRY(check_cu(cu_seqlens, B, &n_seqs));
+  TRY(check(d_qkv, "d_qkv", 3, so));
+  if (d_qkv->dtype != act && d_qkv->dtype != GDN_F32)
+    return fail(GDN_ERR_INVALID_VALUE, "d_qkv: dtype must be the activation dtype or F32");
+  TRY(check_contig(d_qkv, "d_qkv"));
+  TRY(check(d_g, "d_g", 3, sab));
+  TRY(check(d_beta, "d_beta", 3, sab));
+  TRY(check_dtype(d_g, "d_g", GDN_F32));
+  TRY(check_dtype(d_beta, "d_beta", GDN_F32));
+  TRY(check_contig(d_g, "d_g"));
+  TRY(check_contig(d_beta, "d_beta"));
+  TRY(check(dx_q, "dx_q", 3, sq));
+  TRY(check(dx_k, "dx_k", 3, sq));
+  TRY(check(dx_v, "dx_v", 3, sv));
+  TRY(check(d_a, "d_a", 3, sab));
+  TRY(check(d_b, "d_b", 3, sab));
+  for (const gdn_tensor *t : {dx_q, dx_k, dx_v, d_a, d_b}) {
+    TRY(check_dtype(t, "gradient", act));
+    TRY(check_contig(t, "gradient"));
+  }
+  TRY(check(d_conv_w, "d_conv_w", 2, sw));
+  TRY(check_dtype(d_conv_w, "d_conv_w", GDN_F32));
+  TRY(check_contig(d_conv_w, "d_conv_w"));
+  if (!conv_b != !d_conv_b) return fail(GDN_ERR_INVALID_VALUE, "d_conv_b must be given exactly when conv_b is");
+  if (d_conv_b) {
+    TRY(check(d_conv_b, "d_conv_b", 1, sc));
+    TRY(check_dtype(d_conv_b, "d_conv_b", GDN_F32));
+    TRY(check_contig(d_conv_b, "d_conv_b"));
+  }
+  TRY(check(d_A_log, "d_A_log", 1, sh));
+  TRY(check(d_dt_bias, "d_dt_bias", 1, sh));
+  TRY(check_dtype(d_A_log, "d_A_log", GDN_F32));
+  TRY(check_dtype(d_dt_bias, "d_dt_bias", GDN_F32));
+  const gdn_tensor *ins[] = {x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, d_qkv, d_g, d_beta};
+  const gdn_tensor *outs[] = {dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b, d_A_log, d_dt_bias};
+  for (auto *x : outs)
+    for (auto *i : ins)
+      if (overlaps(x, i)) return fail(GDN_ERR_INVALID_VALUE, "an output overlaps an input");
+  for (size_t i = 0; i < 9; ++i)
+    for (size_t j = i + 1; j < 9; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(GDN_ERR_INVALID_VALUE, "outputs overlap each other");
+  const size_t need = prologue_bwd_ws(B, T, dims);
+  if (!ws || ws_bytes < need)
+    return fail(GDN_ERR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  if ((uintptr_t)ws % 256) return fail(GDN_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  if (C > 0x7fffffff / 5) return fail(GDN_ERR_NOT_SUPPORTED, "too many channels");
+
+  gdn::PrologueBwdArgs &p = *P;
+  memset(&p, 0, sizeof p);
+  p.xq = x_q->data; p.xk = x_k->data; p.xv = x_v->data;
+  p.sxq_b = x_q->stride[0]; p.sxq_t = x_q->stride[1];
+  p.sxk_b = x_k->stride[0]; p.sxk_t = x_k->stride[1];
+  p.sxv_b = x_v->stride[0]; p.sxv_t = x_v->stride[1];
+  p.conv_w = conv_w->data; p.w_dtype = conv_w->dtype;
+  p.conv_b = conv_b ? conv_b->data : nullptr; p.b_dtype = conv_b ? conv_b->dtype : act;
+  p.a = a->data; p.b = b->data;
+  p.sa_b = a->stride[0]; p.sa_t = a->stride[1]; p.sb_b = b->stride[0]; p.sb_t = b->stride[1];
+  p.A_log = static_cast<const float *>(A_log->data);
+  p.dt_bias = static_cast<const float *>(dt_bias->data);
+  p.cu_seqlens = cu_seqlens ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
+  p.n_seqs = n_seqs;
+  p.dqkv = d_qkv->data; p.dqkv_dtype = d_qkv->dtype;
+  p.d_g = static_cast<const float *>(d_g->data);
+  p.d_beta = static_cast<const float *>(d_beta->data);
+  p.dxq = dx_q->data; p.dxk = dx_k->data; p.dxv = dx_v->data;
+  p.d_conv_w = static_cast<float *>(d_conv_w->data);
+  p.d_conv_b = d_conv_b ? static_cast<float *>(d_conv_b->data) : nullptr;
+  p.d_a = d_a->data; p.d_b = d_b->data;
+  p.d_A_log = static_cast<float *>(d_A_log->data);
+  p.d_dt_bias = static_cast<float *>(d_dt_bias->data);
+  p.tile_tokens = kBwdTile;
+  p.ntiles = (B * T + kBwdTile - 1) / kBwdTile;
+  p.part_conv = static_cast<float *>(ws);
+  p.part_head = reinterpret_cast<float *>(static_cast<char *>(ws) + align256((size_t)(p.ntiles * C * 5 * 4)));
+  p.B = B; p.T = T; p.Hqk = dims->Hqk; p.dk = dims->dk; p.Hv = Hv; p.dv = dims->dv; p.C = C;
+  p.act = act;
+  return GDN_OK;
+}
+
+
+
 // Workspace of the two-kernel chunk path: chunk offsets of packed sequences,
 // then one record per (chunk, value head). 0 when that path does not apply.
 int64_t chunk_bound_of(int64_t B, int64_t T, int64_t n_seqs) {
@@ -609,6 +800,42 @@ gdn_status gdn_decode_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gd
   TRY(plan_decode(x_q, x_k, x_v, conv_w, conv_b, conv_state, a, b, A_log, dt_bias, state, gate, norm_w, dims,
                   scale, use_qk_l2norm_in_kernel, l2_eps, rms_eps, out, &p));
   return launched(gdn::launch_decode(p, static_cast<hipStream_t>(stream)), "decode");
+}
+
+size_t gdn_gated_norm_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dv) {
+  if (B < 0 || T < 0 || H < 0 || dv < 64 || dv > 512 || !pow2(dv)) return 0;
+  return align256((size_t)norm_bwd_blocks(B * T * H, dv) * (size_t)dv * 4);
+}
+
+gdn_status gdn_gated_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_tensor *weight, float eps,
+                              const gdn_tensor *dout, const gdn_tensor *d_o, const gdn_tensor *d_gate,
+                              const gdn_tensor *d_weight, void *workspace, size_t workspace_bytes, void *stream) {
+  g_error.clear();
+  gdn::NormBwdArgs p;
+  TRY(plan_norm_bwd(o, gate, weight, eps, dout, d_o, d_gate, d_weight, workspace, workspace_bytes, &p));
+  return launched(gdn::launch_gated_norm_bwd(p, static_cast<hipStream_t>(stream)), "gated norm backward");
+}
+
+size_t gdn_prologue_bwd_workspace_bytes(int64_t B, int64_t T, const gdn_dims *dims) {
+  if (!dims || B < 0 || T < 0 || dims->Hqk <= 0 || dims->dk <= 0 || dims->Hv <= 0 || dims->dv <= 0) return 0;
+  return prologue_bwd_ws(B, T, dims);
+}
+
+gdn_status gdn_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
+                            const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *a,
+                            const gdn_tensor *b, const gdn_tensor *A_log, const gdn_tensor *dt_bias,
+                            const gdn_tensor *cu_seqlens, const gdn_dims *dims, const gdn_tensor *d_qkv,
+                            const gdn_tensor *d_g, const gdn_tensor *d_beta, const gdn_tensor *dx_q,
+                            const gdn_tensor *dx_k, const gdn_tensor *dx_v, const gdn_tensor *d_conv_w,
+                            const gdn_tensor *d_conv_b, const gdn_tensor *d_a, const gdn_tensor *d_b,
+                            const gdn_tensor *d_A_log, const gdn_tensor *d_dt_bias, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  g_error.clear();
+  gdn::PrologueBwdArgs p;
+  TRY(plan_prologue_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, dims, d_qkv, d_g, d_beta,
+                        dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b, d_A_log, d_dt_bias, workspace,
+                        workspace_bytes, &p));
+  return launched(gdn::launch_prologue_bwd(p, static_cast<hipStream_t>(stream)), "prologue backward");
 }
 
 size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *dims,

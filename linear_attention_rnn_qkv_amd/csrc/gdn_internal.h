@@ -105,12 +105,53 @@ struct DecodeArgs {
   float scale, l2_eps, rms_eps;
 };
 
+// Backward of the gated norm.
+struct NormBwdArgs {
+  const void *o, *gate, *dout, *w;
+  int64_t so_b, so_t, so_h, sg_b, sg_t, sg_h, sd_b, sd_t, sd_h;
+  void *d_o, *d_gate;    // contiguous [B, T, H, dv]: o's dtype, gate's dtype
+  float *d_w;            // [dv]
+  float *part;           // workspace [nblocks][dv]
+  int64_t nblocks;
+  int64_t B, T, H, dv;
+  int32_t act, gate_dtype, w_dtype;
+  int32_t o_align, gate_align, dout_align;
+  float eps;
+};
+
+// Backward of the prologue (conv + SiLU, beta and g).
+struct PrologueBwdArgs {
+  const void *xq, *xk, *xv;
+  int64_t sxq_b, sxq_t, sxk_b, sxk_t, sxv_b, sxv_t;
+  const void *conv_w, *conv_b;
+  int32_t w_dtype, b_dtype;
+  const void *a, *b;
+  int64_t sa_b, sa_t, sb_b, sb_t;
+  const float *A_log, *dt_bias;
+  const int32_t *cu_seqlens;
+  int64_t n_seqs;
+  const void *dqkv;      // [B, T, C] contiguous, act dtype or F32
+  int32_t dqkv_dtype;
+  const float *d_g, *d_beta;  // [B, T, Hv] contiguous
+  void *dxq, *dxk, *dxv;      // contiguous, act dtype
+  float *d_conv_w, *d_conv_b; // [C, 4], [C] or null
+  void *d_a, *d_b;            // [B, T, Hv] contiguous, act dtype
+  float *d_A_log, *d_dt_bias; // [Hv]
+  float *part_conv;           // workspace [ntiles][C][5]
+  float *part_head;           // workspace [ntiles][Hv][2]
+  int64_t ntiles, tile_tokens;
+  int64_t B, T, Hqk, dk, Hv, dv, C;
+  int32_t act;
+};
+
 // Each returns the HIP error of the launch (hipSuccess if queued).
 hipError_t launch_prologue(const PrologueArgs &a, hipStream_t s);
 hipError_t launch_chunk_rule(const ChunkArgs &a, hipStream_t s);
 hipError_t launch_gated_norm(const NormArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 bool decode_supported(int64_t dk, int64_t G, int64_t dv);
+hipError_t launch_gated_norm_bwd(const NormBwdArgs &a, hipStream_t s);
+hipError_t launch_prologue_bwd(const PrologueBwdArgs &a, hipStream_t s);
 
 // Host-side capability query used by validation (no device calls).
 bool chunk_rule_supported(int64_t dk, int32_t act);

@@ -66,8 +66,14 @@ def lib() -> ctypes.CDLL:
         L.gdn_layer_fwd.argtypes = ([P] * 12 + [ctypes.POINTER(GdnDims), f32, i32, f32, f32, vp,
                                                 ctypes.c_size_t, P, vp])
         L.gdn_decode_fwd.argtypes = ([P] * 11 + [ctypes.POINTER(GdnDims), f32, i32, f32, P, P, f32, P, vp])
+        L.gdn_gated_norm_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 4
+        L.gdn_gated_norm_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_gated_norm_bwd.argtypes = [P, P, P, f32, P, P, P, P, vp, ctypes.c_size_t, vp]
+        L.gdn_prologue_bwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(GdnDims)]
+        L.gdn_prologue_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_prologue_bwd.argtypes = [P] * 10 + [ctypes.POINTER(GdnDims)] + [P] * 12 + [vp, ctypes.c_size_t, vp]
         for name in ("gdn_prologue_fwd", "gdn_chunk_rule_fwd", "gdn_gated_norm_fwd", "gdn_layer_fwd",
-                     "gdn_decode_fwd"):
+                     "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_prologue_bwd"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -227,6 +233,53 @@ def gdn_decode_fwd(x_q, x_k, x_v, conv_w, conv_b, conv_state, a, b, A_log, dt_bi
                                 int(bool(use_qk_l2norm_in_kernel)), float(l2_eps), _p(desc(gate)),
                                 _p(desc(norm_w)), float(rms_eps), _p(desc(out)), _stream(x_q)))
     return out
+
+
+def _ws(nbytes: int, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def gdn_gated_norm_bwd(o, gate, weight, dout, eps: float = 1e-5, workspace=None):
+    """Gradients of the gated norm. Returns (d_o, d_gate, d_weight F32)."""
+    B, T, H, dv = o.shape
+    d_o = torch.empty(o.shape, dtype=o.dtype, device=o.device)
+    d_gate = torch.empty(gate.shape, dtype=gate.dtype, device=o.device)
+    d_w = torch.empty(dv, dtype=torch.float32, device=o.device)
+    nb = int(lib().gdn_gated_norm_bwd_workspace_bytes(B, T, H, dv))
+    if workspace is None:
+        workspace = _ws(nb, o.device)
+    D = [desc(t) for t in (o, gate, weight)]
+    E = [desc(t) for t in (dout, d_o, d_gate, d_w)]
+    _check(lib().gdn_gated_norm_bwd(*[_p(d) for d in D], float(eps), *[_p(d) for d in E],
+                                    ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+                                    _stream(o)))
+    return d_o, d_gate, d_w
+
+
+def gdn_prologue_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, dims: Sequence[int],
+                     d_qkv, d_g, d_beta, workspace=None):
+    """Gradients of the prologue. Returns (dx_q, dx_k, dx_v, d_conv_w, d_conv_b or None,
+    d_a, d_b, d_A_log, d_dt_bias)."""
+    Hqk, dk, Hv, dv = dims
+    B, T = x_q.shape[0], x_q.shape[1]
+    C = 2 * Hqk * dk + Hv * dv
+    dev, dt = x_q.device, x_q.dtype
+    e = lambda *shape, d=dt: torch.empty(shape, dtype=d, device=dev)  # noqa: E731
+    dxq, dxk, dxv = e(B, T, Hqk * dk), e(B, T, Hqk * dk), e(B, T, Hv * dv)
+    dw = e(C, 4, d=torch.float32)
+    dbias = e(C, d=torch.float32) if conv_b is not None else None
+    da, db = e(B, T, Hv), e(B, T, Hv)
+    dal, ddt = e(Hv, d=torch.float32), e(Hv, d=torch.float32)
+    gd = dims_of(Hqk, dk, Hv, dv)
+    nb = int(lib().gdn_prologue_bwd_workspace_bytes(B, T, ctypes.byref(gd)))
+    if workspace is None:
+        workspace = _ws(nb, dev)
+    D = [desc(t) for t in (x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens)]
+    E = [desc(t) for t in (d_qkv, d_g, d_beta, dxq, dxk, dxv, dw, dbias, da, db, dal, ddt)]
+    _check(lib().gdn_prologue_bwd(*[_p(d) for d in D], ctypes.byref(gd), *[_p(d) for d in E],
+                                  ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
+                                  _stream(x_q)))
+    return dxq, dxk, dxv, dw, dbias, da, db, dal, ddt
 
 
 def dtype_name(t: torch.dtype) -> str:

@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol():
     names = set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", hdr))
     assert names == {"gdn_last_error", "gdn_version", "gdn_prologue_fwd", "gdn_chunk_rule_fwd",
                      "gdn_chunk_rule_workspace_bytes", "gdn_gated_norm_fwd", "gdn_layer_workspace_bytes",
-                     "gdn_layer_fwd", "gdn_decode_fwd"}
+                     "gdn_layer_fwd", "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_gated_norm_bwd_workspace_bytes",
+                     "gdn_prologue_bwd", "gdn_prologue_bwd_workspace_bytes"}
     L = gdn.lib()
     for n in names:
         assert hasattr(L, n), n
