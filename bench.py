@@ -176,6 +176,52 @@ WHOLE_LAYER_SHAPES = [  # (B, T, hidden, head_dim, act, B200 fwd ms)
 ]
 
 
+def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup) -> dict:
+    """The backward calls that exist so far (gated norm, prologue) at the
+    workload's shape, each against the HBM roof: per-call HIP events on the
+    current stream, mean over `steps` calls. Algorithmic bytes per token:
+    norm Hv dv (3 e + 2 e_g) (o, dout, d_o; gate, d_gate); prologue
+    3 C e + 4 Hv e + 8 Hv (x, d_qkv, dx; a, b, d_a, d_b; d_g, d_beta)."""
+    e = {"f32": 4, "bf16": 2, "f16": 2}[s.act]
+    eg = {"f32": 4, "bf16": 2, "f16": 2}[s.gate_dtype]
+    ntok = s.tokens
+    dims_t = (s.Hqk, s.dk, s.Hv, s.dv)
+    dout = synth.randn((s.B, s.T, s.Hv, s.dv), s.act, 61).cuda()
+    dqkv = synth.randn((s.B, s.T, s.C), s.act, 62).cuda()
+    dg = synth.randn((s.B, s.T, s.Hv), "f32", 63).cuda()
+    dbeta = synth.randn((s.B, s.T, s.Hv), "f32", 64).cuda()
+    nws = torch.empty(gdn.lib().gdn_gated_norm_bwd_workspace_bytes(s.B, s.T, s.Hv, s.dv), dtype=torch.uint8,
+                      device="cuda")
+    pws = torch.empty(gdn.lib().gdn_prologue_bwd_workspace_bytes(s.B, s.T, gdn.dims_of(*dims_t)),
+                      dtype=torch.uint8, device="cuda")
+
+    def norm_b():
+        gdn.gdn_gated_norm_bwd(o, d["gate"], d["norm_w"], dout, 1e-5, workspace=nws)
+
+    def pro_b():
+        gdn.gdn_prologue_bwd(d["x_q"], d["x_k"], d["x_v"], d["conv_w"], None, d["a"], d["b"], d["A_log"],
+                             d["dt_bias"], d["cu_seqlens"], dims, dqkv, dg, dbeta, workspace=pws)
+
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, fn, per_tok in (("gated_norm_bwd", norm_b, s.Hv * s.dv * (3 * e + 2 * eg)),
+                              ("prologue_bwd", pro_b, 3 * s.C * e + 4 * s.Hv * e + 8 * s.Hv)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nbytes = per_tok * ntok
+        out[name] = {"ms": ms, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                     "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
 def whole_layer_leg(gdn, synth, torch) -> list:
     """The whole layer forward: one input-projection GEMM to the fused
     q|k|v|gate|b|a buffer, the layer core on views of it, the output-projection
@@ -245,6 +291,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-seqs", type=int, default=256,
                     help="sequences of the decode-step leg (0 skips it)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-whole-layer", action="store_true",
                     help="skip the whole-layer leg (projection GEMMs + layer core)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -387,6 +434,11 @@ def main() -> int:
         decode = decode_leg(gdn, synth, torch, s, d, dims, scale, args.decode_seqs, args.steps,
                             args.warmup)
 
+    backward = None
+    if not args.no_backward:
+        print("[bench] backward leg", file=sys.stderr, flush=True)
+        backward = backward_leg(gdn, synth, torch, s, d, o, dims, args.steps, args.warmup)
+
     whole = None
     if not args.no_whole_layer:
         print("[bench] whole-layer leg", file=sys.stderr, flush=True)
@@ -411,6 +463,7 @@ def main() -> int:
         "stages": stages,
         "decode": decode,
         "whole_layer": whole,
+        "backward": backward,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -34,19 +34,44 @@ __device__ __forceinline__ float dsilu(float x) {
   return s * (1.0f + x * (1.0f - s));
 }
 
-// out[i] = sum_p part[p * n + i], p in order.
-__global__ __launch_bounds__(256) void sum_partials_kernel(const float *__restrict__ part, int64_t nparts, int64_t n,
-                                                           float *__restrict__ out) {
+// out[i] = sum_p part[p * n + i] in a fixed order, in two levels: block
+// (x, g) sums the parts of group g for 64 outputs (four interleaved
+// subgroups, then their sum in order) into mid[g][i]; then the groups are
+// added in order.
+constexpr int kRedGroups = 32;
+
+__global__ __launch_bounds__(256) void sum_partials_a(const float *__restrict__ part, int64_t nparts, int64_t n,
+                                                      float *__restrict__ mid) {
+  __shared__ float red[4][64];
+  const int sub = threadIdx.x >> 6, o = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 64 + o, g = blockIdx.y;
+  const int64_t lo = nparts * g / gridDim.y, hi = nparts * (g + 1) / gridDim.y;
+  float acc = 0.f;
+  if (i < n)
+    for (int64_t q = lo + sub; q < hi; q += 4) acc += part[q * n + i];
+  red[sub][o] = acc;
+  __syncthreads();
+  if (sub == 0 && i < n) mid[g * n + i] = ((red[0][o] + red[1][o]) + red[2][o]) + red[3][o];
+}
+
+__global__ __launch_bounds__(256) void sum_partials_b(const float *__restrict__ mid, int64_t ng, int64_t n,
+                                                      float *__restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float acc = 0.f;
-  for (int64_t p = 0; p < nparts; ++p) acc += part[p * n + i];
+  for (int64_t g = 0; g < ng; ++g) acc += mid[g * n + i];
   out[i] = acc;
 }
 
-hipError_t sum_partials(const float *part, int64_t nparts, int64_t n, float *out, hipStream_t s) {
+// mid: scratch of kRedGroups * n floats
+hipError_t sum_partials(const float *part, int64_t nparts, int64_t n, float *mid, float *out, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, nparts, n, out);
+  const int64_t ng = nparts < kRedGroups ? (nparts > 0 ? nparts : 1) : kRedGroups;
+  hipLaunchKernelGGL(sum_partials_a, dim3((unsigned)((n + 63) / 64), (unsigned)ng), dim3(256), 0, s, part, nparts, n,
+                     mid);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sum_partials_b, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, mid, ng, n, out);
   return hipGetLastError();
 }
 
@@ -69,20 +94,31 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_bwd_kernel(NormBwdArg
 #pragma unroll
   for (int i = 0; i < E; ++i) dw[i] = 0.f;
 
-  for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < nrows; row0 += (int64_t)gridDim.x * RPB) {
-    const int64_t row = row0 + rg;
-    const bool live = row < nrows;
-    float o[E], gt[E], du[E];
-    if (live) {
-      const int64_t h = row % p.H, bt = row / p.H, t = bt % p.T, b = bt / p.T;
-      load_vec<T, E>(static_cast<const T *>(p.o) + b * p.so_b + t * p.so_t + h * p.so_h + c0, p.o_align, o);
-      load_vec<TG, E>(static_cast<const TG *>(p.gate) + b * p.sg_b + t * p.sg_t + h * p.sg_h + c0, p.gate_align,
-                      gt);
-      load_vec<T, E>(static_cast<const T *>(p.dout) + b * p.sd_b + t * p.sd_t + h * p.sd_h + c0, p.dout_align, du);
-    } else {
+  // two rows per lane and pass, all six loads issued before any arithmetic
+  for (int64_t row0 = (int64_t)blockIdx.x * 2 * RPB; row0 < nrows; row0 += (int64_t)gridDim.x * 2 * RPB) {
+    float O[2][E], G[2][E], D[2][E];
 #pragma unroll
-      for (int i = 0; i < E; ++i) o[i] = gt[i] = du[i] = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      const int64_t row = row0 + u * RPB + rg;
+      if (row < nrows) {
+        const int64_t h = row % p.H, bt = row / p.H, t = bt % p.T, b = bt / p.T;
+        load_vec_nt<T, E>(static_cast<const T *>(p.o) + b * p.so_b + t * p.so_t + h * p.so_h + c0, p.o_align, O[u]);
+        load_vec_nt<TG, E>(static_cast<const TG *>(p.gate) + b * p.sg_b + t * p.sg_t + h * p.sg_h + c0, p.gate_align,
+                           G[u]);
+        load_vec_nt<T, E>(static_cast<const T *>(p.dout) + b * p.sd_b + t * p.sd_t + h * p.sd_h + c0, p.dout_align,
+                          D[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) O[u][i] = G[u][i] = D[u][i] = 0.f;
+      }
     }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t row = row0 + u * RPB + rg;
+    const bool live = row < nrows;
+    const float(&o)[E] = O[u];
+    const float(&gt)[E] = G[u];
+    const float(&du)[E] = D[u];
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < E; ++i) ss += o[i] * o[i];
@@ -104,9 +140,10 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_bwd_kernel(NormBwdArg
 #pragma unroll
     for (int i = 0; i < E; ++i) d_o[i] = r * (dn[i] - n[i] * dot);
     if (live) {
-      store_vec<T, E>(static_cast<T *>(p.d_o) + row * DV + c0, d_o);
-      store_vec<TG, E>(static_cast<TG *>(p.d_gate) + row * DV + c0, dgate);
+      store_vec_nt<T, E>(static_cast<T *>(p.d_o) + row * DV + c0, d_o);
+      store_vec_nt<TG, E>(static_cast<TG *>(p.d_gate) + row * DV + c0, dgate);
     }
+  }
   }
   // block partial of d_w: rows groups of the block summed in a fixed order
 #pragma unroll
@@ -124,7 +161,7 @@ hipError_t norm_bwd_dv(const NormBwdArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((gated_norm_bwd_kernel<T, TG, TW, DV>), dim3((unsigned)a.nblocks), dim3(kNormThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return sum_partials(a.part, a.nblocks, DV, a.d_w, s);
+  return sum_partials(a.part, a.nblocks, DV, a.mid, a.d_w, s);
 }
 
 template <typename T, typename TG, typename TW>
@@ -195,13 +232,15 @@ struct SeqTrack {
   }
 };
 
-// One thread per channel walks the tokens of one tile in order with rolling
-// windows: xw[k] = x_{t-3+k} (k < 8) and ew[k] = e_{t+k} (k < 4), where
-// e_u = dz_u silu'(y_u). The tile reads 3 tokens of x before it and 4 ahead;
-// x and dz are fetched 8 tokens at a time.
-template <typename T>
+// One thread per VEC adjacent channels walks the tokens of one tile in order
+// with rolling windows: xw[k] = x_{t-3+k} (k < 8) and ew[k] = e_{t+k} (k < 4),
+// where e_u = dz_u silu'(y_u). The tile reads 3 tokens of x before it and 4
+// ahead; x and dz are fetched NB tokens at a time (vector accesses of VEC
+// elements).
+template <typename T, int VEC>
 __global__ __launch_bounds__(kConvThreads) void conv_bwd_kernel(PrologueBwdArgs p) {
-  const int64_t c = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;
+  constexpr int NB = 4;
+  const int64_t c = ((int64_t)blockIdx.x * kConvThreads + threadIdx.x) * VEC;
   const int64_t tile = blockIdx.y;
   if (c >= p.C) return;
   const int64_t nq = p.Hqk * p.dk;
@@ -216,149 +255,190 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_kernel(PrologueBwdArgs 
     xs = static_cast<const T *>(p.xv); sb = p.sxv_b; st = p.sxv_t; cc = c - 2 * nq; dxs = static_cast<T *>(p.dxv);
     ldx = p.Hv * p.dv;
   }
-  float w[4];
+  float w[4][VEC], bias[VEC];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = ldf<T>(p.conv_w, p.w_dtype, 4 * c + j);
-  const float bias = p.conv_b ? ldf<T>(p.conv_b, p.b_dtype, c) : 0.f;
+  for (int v = 0; v < VEC; ++v) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j][v] = ldf<T>(p.conv_w, p.w_dtype, 4 * (c + v) + j);
+    bias[v] = p.conv_b ? ldf<T>(p.conv_b, p.b_dtype, c + v) : 0.f;
+  }
 
   const int64_t ntok = p.B * p.T;
   const int64_t t0 = tile * p.tile_tokens;
   const int64_t t1 = t0 + p.tile_tokens < ntok ? t0 + p.tile_tokens : ntok;
-  auto xat = [&](int64_t u) -> float {  // raw x at flattened token u, 0 outside [0, ntok)
-    if (u < 0 || u >= ntok) return 0.f;
-    return f(xs[(u / p.T) * sb + (u % p.T) * st + cc]);
+  const bool flat = sb == p.T * st;  // rows of consecutive batch entries follow each other
+  auto xat = [&](int64_t u, float(&out)[VEC]) {  // raw x at flattened token u, 0 outside [0, ntok)
+    if (u < 0 || u >= ntok) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) out[v] = 0.f;
+      return;
+    }
+    const int64_t row = flat ? u * st : (u / p.T) * sb + (u % p.T) * st;
+    load_vec<T, VEC>(xs + row + cc, p.x_align, out);
   };
-  auto dzat = [&](int64_t u) -> float { return u < ntok ? ldf<T>(p.dqkv, p.dqkv_dtype, u * p.C + c) : 0.f; };
+  auto dzat = [&](int64_t u, float(&out)[VEC]) {
+    if (u >= ntok) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) out[v] = 0.f;
+      return;
+    }
+    if (p.dqkv_dtype == kF32) load_vec<float, VEC>(static_cast<const float *>(p.dqkv) + u * p.C + c, p.dq_align, out);
+    else load_vec<T, VEC>(static_cast<const T *>(p.dqkv) + u * p.C + c, p.dq_align, out);
+  };
   SeqTrack tt{p.cu_seqlens, p.n_seqs, p.T, 0, 0, 0};  // sequence of t
   SeqTrack tu{p.cu_seqlens, p.n_seqs, p.T, 0, 0, 0};  // sequence of the lookahead token
   tt.init(t0);
   tu.init(t0);
-  // e_u from x_{u-3} .. x_u (window values xa..xd), inside u's sequence
-  auto e_of = [&](int64_t u, float xa, float xb, float xc, float xd, float dz) -> float {
-    if (u >= ntok) return 0.f;
+  // e_u from x_{u-3} .. x_u (xw rows k0 .. k0 + 3), inside u's sequence
+  float xw[8][VEC], ew[4][VEC];
+  auto e_of = [&](int64_t u, int k0, const float(&dz)[VEC], float(&e)[VEC]) {
+    if (u >= ntok) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) e[v] = 0.f;
+      return;
+    }
     tu.advance(u);
     const int64_t s0 = tu.s0;
-    const float y = bias + (u - 3 >= s0 ? w[0] * xa : 0.f) + (u - 2 >= s0 ? w[1] * xb : 0.f) +
-                    (u - 1 >= s0 ? w[2] * xc : 0.f) + w[3] * xd;
-    return dz * dsilu(y);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      float y = bias[v] + w[3][v] * xw[k0 + 3][v];
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (u - 3 + j >= s0) y += w[j][v] * xw[k0 + j][v];
+      e[v] = dz[v] * dsilu(y);
+    }
   };
-  float xw[8], ew[4];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) xw[k] = xat(t0 - 3 + k);
+  for (int k = 0; k < 8; ++k) xat(t0 - 3 + k, xw[k]);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) ew[k] = e_of(t0 + k, xw[k], xw[k + 1], xw[k + 2], xw[k + 3], dzat(t0 + k));
-  float dw[4] = {0.f, 0.f, 0.f, 0.f}, db = 0.f;
-  for (int64_t tb = t0; tb < t1; tb += 8) {
-    // x_{t+5} and dz_{t+4} for the 8 tokens t of this group, fetched together
-    float xn[8], dzn[8];
+  for (int k = 0; k < 4; ++k) {
+    float dz[VEC];
+    dzat(t0 + k, dz);
+    e_of(t0 + k, k, dz, ew[k]);
+  }
+  float dw[4][VEC], db[VEC];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      xn[k] = xat(tb + 5 + k);
-      dzn[k] = dzat(tb + 4 + k);
+  for (int v = 0; v < VEC; ++v) {
+    db[v] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dw[j][v] = 0.f;
+  }
+  for (int64_t tb = t0; tb < t1; tb += NB) {
+    // x_{t+5} and dz_{t+4} for the NB tokens t of this group, fetched together
+    float xn[NB][VEC], dzn[NB][VEC];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      xat(tb + 5 + k, xn[k]);
+      dzat(tb + 4 + k, dzn[k]);
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NB; ++k) {
       const int64_t t = tb + k;
       if (t >= t1) break;
       tt.advance(t);
       // dx_t = sum_j w_j e_{t+3-j} over tokens of t's sequence
-      float dx = 0.f;
+      float dx[VEC];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (t + 3 - j < tt.s1) dx += w[j] * ew[3 - j];
-      dxs[t * ldx + cc] = to<T>(dx);
-      db += ew[0];
+      for (int v = 0; v < VEC; ++v) {
+        float acc = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (t - 3 + j >= tt.s0) dw[j] += ew[0] * xw[j];
+        for (int j = 0; j < 4; ++j)
+          if (t + 3 - j < tt.s1) acc += w[j][v] * ew[3 - j][v];
+        dx[v] = acc;
+        db[v] += ew[0][v];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (t - 3 + j >= tt.s0) dw[j][v] += ew[0][v] * xw[j][v];
+      }
+      store_vec<T, VEC>(dxs + t * ldx + cc, dx);
       // advance the windows to t + 1: e_{t+4} uses x_{t+1} .. x_{t+4}
-      const float e4 = e_of(t + 4, xw[4], xw[5], xw[6], xw[7], dzn[k]);
+      float e4[VEC];
+      e_of(t + 4, 4, dzn[k], e4);
 #pragma unroll
-      for (int q = 0; q < 7; ++q) xw[q] = xw[q + 1];
-      xw[7] = xn[k];
+      for (int q = 0; q < 7; ++q)
 #pragma unroll
-      for (int q = 0; q < 3; ++q) ew[q] = ew[q + 1];
-      ew[3] = e4;
+        for (int v = 0; v < VEC; ++v) xw[q][v] = xw[q + 1][v];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) xw[7][v] = xn[k][v];
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) ew[q][v] = ew[q + 1][v];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) ew[3][v] = e4[v];
     }
   }
-  float *part = p.part_conv + (tile * p.C + c) * 5;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) part[j] = dw[j];
-  part[4] = db;
+  for (int v = 0; v < VEC; ++v) {
+    float *pw = p.part_w + (tile * p.C + c + v) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pw[j] = dw[j][v];
+    p.part_b[tile * p.C + c + v] = db[v];
+  }
 }
 
-// One block per (tile, value head): d_a, d_b per token and the tile's sums of
-// d_a and d_g g.
+// One block per tile of head_tile tokens (head_tile * Hv <= 4096): d_a and
+// d_b of every (token, head) element in order of memory, and per head the
+// tile's sums of d_a and d_g g (contributions staged in LDS, then added in
+// token order).
 template <typename T>
 __global__ __launch_bounds__(256) void beta_g_bwd_kernel(PrologueBwdArgs p) {
-  __shared__ float red[2][4];
-  const int64_t tile = blockIdx.x, h = blockIdx.y;
+  __shared__ float ca[4096], cg[4096];
+  const int64_t Hv = p.Hv;
   const int64_t ntok = p.B * p.T;
-  const int64_t t0 = tile * p.tile_tokens;
-  const int64_t t1 = t0 + p.tile_tokens < ntok ? t0 + p.tile_tokens : ntok;
-  const float ea = __expf(p.A_log[h]), dtb = p.dt_bias[h];
-  float sa = 0.f, sg = 0.f;
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += 256) {
-    const int64_t b = t / p.T, tt = t % p.T;
-    const float bv = f(static_cast<const T *>(p.b)[b * p.sb_b + tt * p.sb_t + h]);
-    const float av = f(static_cast<const T *>(p.a)[b * p.sa_b + tt * p.sa_t + h]);
-    const float dg = p.d_g[t * p.Hv + h], dbeta = p.d_beta[t * p.Hv + h];
-    const float beta = sigm(bv);
-    const float xa = av + dtb;
+  const int64_t t0 = (int64_t)blockIdx.x * p.head_tile;
+  const int64_t t1 = t0 + p.head_tile < ntok ? t0 + p.head_tile : ntok;
+  const int64_t ne = (t1 - t0) * Hv;
+  const bool fa = p.sa_b == p.T * p.sa_t, fb = p.sb_b == p.T * p.sb_t;
+  for (int64_t k = threadIdx.x; k < ne; k += 256) {
+    const int64_t t = t0 + k / Hv, h = k % Hv;
+    const int64_t ra = fa ? t * p.sa_t : (t / p.T) * p.sa_b + (t % p.T) * p.sa_t;
+    const int64_t rb = fb ? t * p.sb_t : (t / p.T) * p.sb_b + (t % p.T) * p.sb_t;
+    const float av = f(static_cast<const T *>(p.a)[ra + h]);
+    const float bv = f(static_cast<const T *>(p.b)[rb + h]);
+    const int64_t e = t * Hv + h;
+    const float dg = p.d_g[e], dbeta = p.d_beta[e];
+    const float ea = __expf(p.A_log[h]);
+    const float xa = av + p.dt_bias[h];
     const float sp = xa > 20.f ? xa : log1pf(__expf(xa));
     const float spd = xa > 20.f ? 1.f : sigm(xa);
+    const float beta = sigm(bv);
     const float da = -dg * ea * spd;
-    static_cast<T *>(p.d_b)[t * p.Hv + h] = to<T>(dbeta * beta * (1.f - beta));
-    static_cast<T *>(p.d_a)[t * p.Hv + h] = to<T>(da);
-    sa += da;
-    sg += dg * (-ea * sp);
-  }
-  sa = group_sum<64>(sa);
-  sg = group_sum<64>(sg);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    red[0][wave] = sa;
-    red[1][wave] = sg;
+    static_cast<T *>(p.d_b)[e] = to<T>(dbeta * beta * (1.f - beta));
+    static_cast<T *>(p.d_a)[e] = to<T>(da);
+    ca[k] = da;
+    cg[k] = dg * (-ea * sp);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float* part = p.part_head + (tile * p.Hv + h) * 2;
-    part[0] = red[0][0] + red[0][1] + red[0][2] + red[0][3];  // d_dt_bias
-    part[1] = red[1][0] + red[1][1] + red[1][2] + red[1][3];  // d_A_log
-  }
-}
-
-// [ntiles][Hv][2] -> d_dt_bias, d_A_log; [ntiles][C][5] -> d_w [C][4], d_b [C]
-__global__ __launch_bounds__(256) void prologue_sums_kernel(PrologueBwdArgs p) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t nconv = p.C * 5;
-  if (i < nconv) {
-    float acc = 0.f;
-    for (int64_t q = 0; q < p.ntiles; ++q) acc += p.part_conv[q * nconv + i];
-    const int64_t c = i / 5, j = i % 5;
-    if (j < 4) p.d_conv_w[c * 4 + j] = acc;
-    else if (p.d_conv_b) p.d_conv_b[c] = acc;
-  } else if (i < nconv + 2 * p.Hv) {
-    const int64_t k = i - nconv, h = k / 2, j = k % 2;
-    float acc = 0.f;
-    for (int64_t q = 0; q < p.ntiles; ++q) acc += p.part_head[(q * p.Hv + h) * 2 + j];
-    if (j == 0) p.d_dt_bias[h] = acc;
-    else p.d_A_log[h] = acc;
+  for (int64_t h = threadIdx.x; h < Hv; h += 256) {
+    float sa = 0.f, sg = 0.f;
+    for (int64_t t = 0; t < t1 - t0; ++t) {
+      sa += ca[t * Hv + h];
+      sg += cg[t * Hv + h];
+    }
+    p.part_dt[blockIdx.x * Hv + h] = sa;
+    p.part_al[blockIdx.x * Hv + h] = sg;
   }
 }
 
 template <typename T>
 hipError_t prologue_bwd_t(const PrologueBwdArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((conv_bwd_kernel<T>), dim3((unsigned)((a.C + kConvThreads - 1) / kConvThreads), (unsigned)a.ntiles),
-                     dim3(kConvThreads), 0, s, a);
+  if (a.vec4)
+    hipLaunchKernelGGL((conv_bwd_kernel<T, 4>), dim3((unsigned)((a.C / 4 + kConvThreads - 1) / kConvThreads),
+                       (unsigned)a.ntiles), dim3(kConvThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv_bwd_kernel<T, 1>), dim3((unsigned)((a.C + kConvThreads - 1) / kConvThreads),
+                       (unsigned)a.ntiles), dim3(kConvThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((beta_g_bwd_kernel<T>), dim3((unsigned)a.ntiles, (unsigned)a.Hv), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((beta_g_bwd_kernel<T>), dim3((unsigned)a.nhtiles), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = a.C * 5 + 2 * a.Hv;
-  hipLaunchKernelGGL(prologue_sums_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
-  return hipGetLastError();
+  e = sum_partials(a.part_w, a.ntiles, a.C * 4, a.mid, a.d_conv_w, s);
+  if (e == hipSuccess && a.d_conv_b) e = sum_partials(a.part_b, a.ntiles, a.C, a.mid, a.d_conv_b, s);
+  if (e == hipSuccess) e = sum_partials(a.part_dt, a.nhtiles, a.Hv, a.mid, a.d_dt_bias, s);
+  if (e == hipSuccess) e = sum_partials(a.part_al, a.nhtiles, a.Hv, a.mid, a.d_A_log, s);
+  return e;
 }
 
 }  // namespace

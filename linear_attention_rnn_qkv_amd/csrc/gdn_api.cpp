@@ -513,9 +513,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ------------------------------------------------------------- backward
 int64_t norm_bwd_blocks(int64_t rows, int64_t dv) {
-  const int64_t rpb = 2048 / dv;  // rows per block and pass (4 waves, dv / 8 lanes per row)
+  const int64_t rpb = 2 * 2048 / dv;  // rows per block and pass (4 waves, dv / 8 lanes per row, 2 rows)
   const int64_t nb = (rows + rpb - 1) / rpb;
-  return nb < 1024 ? nb : 1024;
+  return nb < 8192 ? nb : 8192;
 }
 
 gdn_status plan_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_tensor *weight, float eps,
@@ -543,7 +543,7 @@ gdn_status plan_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_
     return fail(GDN_ERR_INVALID_VALUE, "outputs overlap each other");
   if ((uintptr_t)d_gate->data % 16) return fail(GDN_ERR_NOT_SUPPORTED, "d_gate must be 16-byte aligned");
   const int64_t nb = norm_bwd_blocks(f.B * f.T * f.H, f.dv);
-  const size_t need = (size_t)nb * (size_t)f.dv * 4;
+  const size_t need = align256((size_t)nb * (size_t)f.dv * 4) + align256((size_t)32 * f.dv * 4);
   if (!ws || ws_bytes < need)
     return fail(GDN_ERR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
   if ((uintptr_t)ws % 256) return fail(GDN_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
@@ -555,6 +555,7 @@ gdn_status plan_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_
   p.w = f.w; p.d_o = d_o->data; p.d_gate = d_gate->data;
   p.d_w = static_cast<float *>(d_weight->data);
   p.part = static_cast<float *>(ws);
+  p.mid = reinterpret_cast<float *>(static_cast<char *>(ws) + align256((size_t)nb * (size_t)f.dv * 4));
   p.nblocks = nb;
   p.B = f.B; p.T = f.T; p.H = f.H; p.dv = f.dv;
   p.act = f.act; p.gate_dtype = f.gate_dtype; p.w_dtype = f.w_dtype;
@@ -565,11 +566,27 @@ gdn_status plan_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_
 
 constexpr int64_t kBwdTile = 256;  // tokens per tile of the prologue backward
 
-size_t prologue_bwd_ws(int64_t B, int64_t T, const gdn_dims *d) {
-  const int64_t ntiles = (B * T + kBwdTile - 1) / kBwdTile;
-  const int64_t C = 2 * d->Hqk * d->dk + d->Hv * d->dv;
-  return align256((size_t)(ntiles * C * 5 * 4)) + align256((size_t)(ntiles * d->Hv * 2 * 4));
+// Workspace of the prologue backward: per token tile, partial sums of d_conv_w
+// [C][4] and d_conv_b [C]; per head tile (4096 / Hv tokens), of d_dt_bias and
+// d_A_log [Hv]; then the reduction scratch [32][C * 4].
+struct ProBwdWs {
+  int64_t ntiles, head_tile, nhtiles;
+  size_t w, b, h, mid;  // byte sizes of the regions, each 256-byte aligned
+  size_t total() const { return w + b + 2 * h + mid; }
+};
+ProBwdWs prologue_bwd_layout(int64_t B, int64_t T, const gdn_dims *d) {
+  ProBwdWs L;
+  const int64_t ntok = B * T, C = 2 * d->Hqk * d->dk + d->Hv * d->dv;
+  L.ntiles = (ntok + kBwdTile - 1) / kBwdTile;
+  L.head_tile = d->Hv <= 4096 ? 4096 / d->Hv : 1;
+  L.nhtiles = (ntok + L.head_tile - 1) / L.head_tile;
+  L.w = align256((size_t)(L.ntiles * C * 4 * 4));
+  L.b = align256((size_t)(L.ntiles * C * 4));
+  L.h = align256((size_t)(L.nhtiles * d->Hv * 4));
+  L.mid = align256((size_t)(32 * C * 4 * 4));
+  return L;
 }
+size_t prologue_bwd_ws(int64_t B, int64_t T, const gdn_dims *d) { return prologue_bwd_layout(B, T, d).total(); }
 
 gdn_status plan_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
                              const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *a,
@@ -667,6 +684,7 @@ gdn_status plan_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const
     return fail(GDN_ERR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
   if ((uintptr_t)ws % 256) return fail(GDN_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
   if (C > 0x7fffffff / 5) return fail(GDN_ERR_NOT_SUPPORTED, "too many channels");
+  if (Hv > 4096) return fail(GDN_ERR_NOT_SUPPORTED, "prologue backward: more than 4096 value heads");
 
   gdn::PrologueBwdArgs &p = *P;
   memset(&p, 0, sizeof p);
@@ -691,12 +709,35 @@ gdn_status plan_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const
   p.d_a = d_a->data; p.d_b = d_b->data;
   p.d_A_log = static_cast<float *>(d_A_log->data);
   p.d_dt_bias = static_cast<float *>(d_dt_bias->data);
+  const ProBwdWs L = prologue_bwd_layout(B, T, dims);
   p.tile_tokens = kBwdTile;
-  p.ntiles = (B * T + kBwdTile - 1) / kBwdTile;
-  p.part_conv = static_cast<float *>(ws);
-  p.part_head = reinterpret_cast<float *>(static_cast<char *>(ws) + align256((size_t)(p.ntiles * C * 5 * 4)));
+  p.ntiles = L.ntiles;
+  p.head_tile = L.head_tile;
+  p.nhtiles = L.nhtiles;
+  char *w = static_cast<char *>(ws);
+  p.part_w = reinterpret_cast<float *>(w);
+  p.part_b = reinterpret_cast<float *>(w + L.w);
+  p.part_dt = reinterpret_cast<float *>(w + L.w + L.b);
+  p.part_al = reinterpret_cast<float *>(w + L.w + L.b + L.h);
+  p.mid = reinterpret_cast<float *>(w + L.w + L.b + 2 * L.h);
   p.B = B; p.T = T; p.Hqk = dims->Hqk; p.dk = dims->dk; p.Hv = Hv; p.dv = dims->dv; p.C = C;
   p.act = act;
+  int xa = 16;
+  for (const gdn_tensor *x : {x_q, x_k, x_v}) {
+    const int r = row_align(x, 2);
+    xa = r < xa ? r : xa;
+  }
+  p.x_align = xa;
+  p.dq_align = row_align(d_qkv, 2);
+  const int64_t es = elem_size(act), eq = elem_size(d_qkv->dtype);
+  int oa = 16;
+  for (const gdn_tensor *x : {dx_q, dx_k, dx_v}) {
+    const int r = row_align(x, 2);
+    oa = r < oa ? r : oa;
+  }
+  // four channels per thread: the q/k/v segments split at multiples of 4 and
+  // every row start is aligned to a 4-element access
+  p.vec4 = nq % 4 == 0 && nv % 4 == 0 && xa >= 4 * es && p.dq_align >= 4 * eq && oa >= (4 * es < 16 ? 4 * es : 16);
   return GDN_OK;
 }
 
@@ -804,7 +845,7 @@ gdn_status gdn_decode_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gd
 
 size_t gdn_gated_norm_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dv) {
   if (B < 0 || T < 0 || H < 0 || dv < 64 || dv > 512 || !pow2(dv)) return 0;
-  return align256((size_t)norm_bwd_blocks(B * T * H, dv) * (size_t)dv * 4);
+  return align256((size_t)norm_bwd_blocks(B * T * H, dv) * (size_t)dv * 4) + align256((size_t)32 * dv * 4);
 }
 
 gdn_status gdn_gated_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_tensor *weight, float eps,

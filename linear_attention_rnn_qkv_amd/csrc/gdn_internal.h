@@ -112,6 +112,7 @@ struct NormBwdArgs {
   void *d_o, *d_gate;    // contiguous [B, T, H, dv]: o's dtype, gate's dtype
   float *d_w;            // [dv]
   float *part;           // workspace [nblocks][dv]
+  float *mid;            // workspace [32][dv]
   int64_t nblocks;
   int64_t B, T, H, dv;
   int32_t act, gate_dtype, w_dtype;
@@ -137,11 +138,16 @@ struct PrologueBwdArgs {
   float *d_conv_w, *d_conv_b; // [C, 4], [C] or null
   void *d_a, *d_b;            // [B, T, Hv] contiguous, act dtype
   float *d_A_log, *d_dt_bias; // [Hv]
-  float *part_conv;           // workspace [ntiles][C][5]
-  float *part_head;           // workspace [ntiles][Hv][2]
-  int64_t ntiles, tile_tokens;
+  // workspace: partial sums per token tile, and the reduction scratch
+  float *part_w;              // [ntiles][C][4]
+  float *part_b;              // [ntiles][C]
+  float *part_dt, *part_al;   // [nhtiles][Hv]
+  float *mid;                 // [32][C * 4]
+  int64_t ntiles, tile_tokens, nhtiles, head_tile;
   int64_t B, T, Hqk, dk, Hv, dv, C;
   int32_t act;
+  int32_t vec4;              // 4 channels per thread (segments and rows allow it)
+  int32_t x_align, dq_align; // bytes guaranteed for x rows and d_qkv rows
 };
 
 // Each returns the HIP error of the launch (hipSuccess if queued).

@@ -227,3 +227,31 @@ def test_error_message_is_per_call():
     with pytest.raises(gdn.GdnError):
         _nrm(o=torch.zeros(1, 0, 2, 64, dtype=torch.bfloat16))
     assert "empty" in gdn.gdn_last_error()
+
+
+def test_backward_workspace_bytes_and_rejections():
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # gated norm: one [dv] FP32 partial per block, at most 8192 blocks of 4096 / dv rows
+    assert gdn.lib().gdn_gated_norm_bwd_workspace_bytes(1, 100, 2, 128) == a256(7 * 128 * 4) + 32 * 128 * 4
+    assert gdn.lib().gdn_gated_norm_bwd_workspace_bytes(1, 1 << 20, 32, 128) == 8192 * 128 * 4 + 32 * 128 * 4
+    assert gdn.lib().gdn_gated_norm_bwd_workspace_bytes(1, 10, 2, 96) == 0
+    # prologue: [tiles of 256 tokens][C][4] and [tiles][C], [head tiles of 4096 / Hv tokens][Hv] twice,
+    # then the reduction scratch [32][C * 4], all FP32
+    gd = gdn.dims_of(2, 64, 4, 64)
+    C = 2 * 128 + 256
+    assert gdn.lib().gdn_prologue_bwd_workspace_bytes(1, 600, gd) == (a256(3 * C * 16) + a256(3 * C * 4) +
+                                                                      2 * a256(1 * 4 * 4) + a256(32 * C * 16))
+    o = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    w = torch.ones(64, dtype=torch.bfloat16)
+    _expect(INVALID, "dout: dtype", gdn.gdn_gated_norm_bwd, o, o.clone(), w, o.half())
+    _expect(INVALID, "workspace too small", gdn.gdn_gated_norm_bwd, o, o.clone(), w, o.clone(),
+            workspace=torch.zeros(16, dtype=torch.uint8))
+    x = _prologue_inputs()
+    B, T, Hv = 1, 8, 4
+    dq = torch.zeros(B, T, C, dtype=torch.bfloat16)
+    dg, dbt = torch.zeros(B, T, Hv), torch.zeros(B, T, Hv)
+    args = [x[k] for k in ("x_q", "x_k", "x_v", "conv_w", "conv_b", "a", "b", "A_log", "dt_bias", "cu_seqlens")]
+    _expect(INVALID, "d_qkv: dim", gdn.gdn_prologue_bwd, *args, x["dims"], dq[..., :C - 8], dg, dbt)
+    _expect(INVALID, "d_g: dtype", gdn.gdn_prologue_bwd, *args, x["dims"], dq, dg.bfloat16(), dbt)
+    _expect(INVALID, "workspace too small", gdn.gdn_prologue_bwd, *args, x["dims"], dq, dg, dbt,
+            workspace=torch.zeros(16, dtype=torch.uint8))
