@@ -39,12 +39,17 @@ KERNELS = {
     "prologue_kernel": ("prologue_kernel", ["prologue.hip", "device_common.h", "gdn_internal.h"]),
     "decode_kernel": ("decode_kernel", ["decode.hip", "device_common.h", "gdn_internal.h"]),
     "gated_norm_kernel": ("gated_norm_kernel", ["gated_norm.hip", "device_common.h", "gdn_internal.h"]),
+    "gated_norm_bwd_kernel": ("gated_norm_bwd_kernel", ["backward.hip", "device_common.h", "gdn_internal.h"]),
+    "conv_bwd_kernel": ("conv_bwd_kernel", ["backward.hip", "device_common.h", "gdn_internal.h"]),
+    "beta_g_bwd_kernel": ("beta_g_bwd_kernel", ["backward.hip", "device_common.h", "gdn_internal.h"]),
+    "sum_partials_a": ("sum_partials_a", ["backward.hip", "device_common.h", "gdn_internal.h"]),
+    "sum_partials_b": ("sum_partials_b", ["backward.hip", "device_common.h", "gdn_internal.h"]),
 }
 
 
 def short_name(symbol: str) -> str | None:
     for frag, (name, _) in KERNELS.items():
-        if frag + "I" in symbol or symbol.endswith(frag):
+        if frag + "I" in symbol or symbol.endswith(frag) or "::" + frag + "(" in symbol:
             return name
     return None
 
