@@ -28,7 +28,7 @@
 namespace gdn {
 namespace {
 
-__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float dsilu(float x) {
   const float s = sigm(x);
   return s * (1.0f + x * (1.0f - s));
@@ -237,7 +237,7 @@ struct SeqTrack {
 // where e_u = dz_u silu'(y_u). The tile reads 3 tokens of x before it and 4
 // ahead; x and dz are fetched NB tokens at a time (vector accesses of VEC
 // elements).
-template <typename T, int VEC>
+template <typename T, int VEC, bool FLAT>
 __global__ __launch_bounds__(kConvThreads) void conv_bwd_kernel(PrologueBwdArgs p) {
   constexpr int NB = 4;
   const int64_t c = ((int64_t)blockIdx.x * kConvThreads + threadIdx.x) * VEC;
@@ -266,14 +266,17 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_kernel(PrologueBwdArgs 
   const int64_t ntok = p.B * p.T;
   const int64_t t0 = tile * p.tile_tokens;
   const int64_t t1 = t0 + p.tile_tokens < ntok ? t0 + p.tile_tokens : ntok;
-  const bool flat = sb == p.T * st;  // rows of consecutive batch entries follow each other
+  // FLAT: the x rows of consecutive batch entries follow each other
+  // (batch stride T times the token stride), so no division is needed
   auto xat = [&](int64_t u, float(&out)[VEC]) {  // raw x at flattened token u, 0 outside [0, ntok)
     if (u < 0 || u >= ntok) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) out[v] = 0.f;
       return;
     }
-    const int64_t row = flat ? u * st : (u / p.T) * sb + (u % p.T) * st;
+    int64_t row;
+    if constexpr (FLAT) row = u * st;
+    else row = (u / p.T) * sb + (u % p.T) * st;
     load_vec<T, VEC>(xs + row + cc, p.x_align, out);
   };
   auto dzat = [&](int64_t u, float(&out)[VEC]) {
@@ -423,12 +426,12 @@ __global__ __launch_bounds__(256) void beta_g_bwd_kernel(PrologueBwdArgs p) {
 
 template <typename T>
 hipError_t prologue_bwd_t(const PrologueBwdArgs &a, hipStream_t s) {
-  if (a.vec4)
-    hipLaunchKernelGGL((conv_bwd_kernel<T, 4>), dim3((unsigned)((a.C / 4 + kConvThreads - 1) / kConvThreads),
-                       (unsigned)a.ntiles), dim3(kConvThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((conv_bwd_kernel<T, 1>), dim3((unsigned)((a.C + kConvThreads - 1) / kConvThreads),
-                       (unsigned)a.ntiles), dim3(kConvThreads), 0, s, a);
+  const dim3 g4((unsigned)((a.C / 4 + kConvThreads - 1) / kConvThreads), (unsigned)a.ntiles);
+  const dim3 g1((unsigned)((a.C + kConvThreads - 1) / kConvThreads), (unsigned)a.ntiles);
+  if (a.vec4 && a.x_flat) hipLaunchKernelGGL((conv_bwd_kernel<T, 4, true>), g4, dim3(kConvThreads), 0, s, a);
+  else if (a.vec4) hipLaunchKernelGGL((conv_bwd_kernel<T, 4, false>), g4, dim3(kConvThreads), 0, s, a);
+  else if (a.x_flat) hipLaunchKernelGGL((conv_bwd_kernel<T, 1, true>), g1, dim3(kConvThreads), 0, s, a);
+  else hipLaunchKernelGGL((conv_bwd_kernel<T, 1, false>), g1, dim3(kConvThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((beta_g_bwd_kernel<T>), dim3((unsigned)a.nhtiles), dim3(256), 0, s, a);

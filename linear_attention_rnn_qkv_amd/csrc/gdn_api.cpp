@@ -738,6 +738,9 @@ gdn_status plan_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const
   // four channels per thread: the q/k/v segments split at multiples of 4 and
   // every row start is aligned to a 4-element access
   p.vec4 = nq % 4 == 0 && nv % 4 == 0 && xa >= 4 * es && p.dq_align >= 4 * eq && oa >= (4 * es < 16 ? 4 * es : 16);
+  p.x_flat = 1;
+  for (const gdn_tensor *x : {x_q, x_k, x_v})
+    if (B > 1 && x->stride[0] != T * x->stride[1]) p.x_flat = 0;
   return GDN_OK;
 }
 

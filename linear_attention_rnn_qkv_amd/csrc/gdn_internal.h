@@ -147,6 +147,7 @@ struct PrologueBwdArgs {
   int64_t B, T, Hqk, dk, Hv, dv, C;
   int32_t act;
   int32_t vec4;              // 4 channels per thread (segments and rows allow it)
+  int32_t x_flat;            // every x view has batch stride T times its token stride
   int32_t x_align, dq_align; // bytes guaranteed for x rows and d_qkv rows
 };
 
