@@ -14,7 +14,8 @@
 // (Gated DeltaNet's parameterisation; the pages do not print them).
 //
 // Layout and schedule (HBM-bound): a thread owns VEC consecutive channels and
-// walks a tile of 128 tokens in batches of 8, double-buffered so that the
+// walks a tile of 128 tokens (16 when the launch would have few blocks) in
+// batches of 8, double-buffered so that the
 // next batch's loads (raw packed vectors) are in flight during the arithmetic
 // of the current one. It convolves over a window that keeps the three previous
 // inputs in registers, so each input element is read once (plus a 3-token halo
@@ -32,7 +33,8 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 128;  // tokens per block
+constexpr int kTile = 128;      // tokens per block
+constexpr int kSmallTile = 16;  // tokens per block when the launch would have few blocks
 constexpr int kUnroll = 8;   // tokens per load batch
 
 template <typename TW>
@@ -72,13 +74,13 @@ __device__ void beta_g_tile(const PrologueArgs &p, int64_t b, int64_t t0, int64_
   }
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, int TILE>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs p) {
   // Consecutive blocks cover consecutive token tiles of one channel block.
   const int cb = (int)blockIdx.y;
   const int64_t b = blockIdx.z;
-  const int64_t t0 = (int64_t)blockIdx.x * kTile;
-  const int64_t t1 = t0 + kTile < p.T ? t0 + kTile : p.T;
+  const int64_t t0 = (int64_t)blockIdx.x * TILE;
+  const int64_t t1 = t0 + TILE < p.T ? t0 + TILE : p.T;
   const int64_t c0 = ((int64_t)cb * kThreads + threadIdx.x) * VEC;
   const bool active = c0 < p.C;
   const int64_t nq = p.Hqk * p.dk;
@@ -228,10 +230,10 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs p) {
     }
   };
   T ra[kUnroll][VEC], rb[kUnroll][VEC];
-  if (t1 - t0 == kTile) {
+  if (t1 - t0 == TILE) {
     // Full tile: double-buffered with a fixed trip count, the loads of batch
     // i + 1 in flight during the arithmetic of batch i.
-    constexpr int kPairs = kTile / (2 * kUnroll);
+    constexpr int kPairs = TILE / (2 * kUnroll);
     load_batch(t0, ra);
     int64_t tb = t0;
     for (int i = 0; i < kPairs - 1; ++i, tb += 2 * kUnroll) {
@@ -260,9 +262,14 @@ template <typename T, int VEC>
 hipError_t launch_vec(const PrologueArgs &a, hipStream_t s) {
   const int64_t per_block = (int64_t)kThreads * VEC;
   const int64_t cblocks = (a.C + per_block - 1) / per_block;
-  const int64_t tblocks = (a.T + kTile - 1) / kTile;
+  // short inputs: smaller token tiles, so that the launch has enough blocks
+  // (each block walks its tile's tokens in order)
+  const bool small = ((a.T + kTile - 1) / kTile) * cblocks * a.B < 256;
+  const int tile = small ? kSmallTile : kTile;
+  const int64_t tblocks = (a.T + tile - 1) / tile;
   dim3 grid((unsigned)tblocks, (unsigned)cblocks, (unsigned)a.B);
-  hipLaunchKernelGGL((prologue_kernel<T, VEC>), grid, dim3(kThreads), 0, s, a);
+  if (small) hipLaunchKernelGGL((prologue_kernel<T, VEC, kSmallTile>), grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((prologue_kernel<T, VEC, kTile>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
