@@ -255,3 +255,18 @@ def test_backward_workspace_bytes_and_rejections():
     _expect(INVALID, "d_g: dtype", gdn.gdn_prologue_bwd, *args, x["dims"], dq, dg.bfloat16(), dbt)
     _expect(INVALID, "workspace too small", gdn.gdn_prologue_bwd, *args, x["dims"], dq, dg, dbt,
             workspace=torch.zeros(16, dtype=torch.uint8))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_binding_has_no_cpu_path():
+    # every compute call goes through the library; the binding module imports
+    # neither the oracle nor any fallback
+    src = open(os.path.join(ROOT, "linear_attention_rnn_qkv_amd", "gdn.py")).read()
+    assert "oracle" not in src and "numpy" not in src
