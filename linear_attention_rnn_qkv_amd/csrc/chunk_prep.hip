@@ -104,8 +104,15 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
 
   const int lane = threadIdx.x & 63, hv = threadIdx.x >> 8, wave = (threadIdx.x >> 6) & 3;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t gc = blockIdx.x;
-  const int64_t h = blockIdx.y * NV + hv;
+  // The head groups of one chunk read the same g and beta cache lines (token
+  // rows of all heads): consecutive linear block ids go to different XCDs,
+  // so the ids are permuted to place the blocks of a chunk on one XCD and
+  // its L2.
+  int64_t lid = blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
+  const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
+  if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
+  const int64_t gc = lid / gridDim.y, hy = lid % gridDim.y;
+  const int64_t h = hy * NV + hv;
   const int64_t hk = h / (p.Hv / p.Hqk);
   float(&fac)[P_N][BT] = sm.fac[hv];
   typename SM::Mats &mm = sm.u.m[hv];
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
   const int wid = threadIdx.x >> 6;
   float graw = 0.f, braw = 0.f;
   if (wid < NV) {
-    const int64_t hs = blockIdx.y * NV + wid;
+    const int64_t hs = hy * NV + wid;
     const float *gp = p.g + brow * p.sg_b + hs * p.sg_h + t0 * p.sg_t;
     const float *bp = p.beta + brow * p.sbt_b + hs * p.sbt_h + t0 * p.sbt_t;
     const int64_t li = lane < nr ? lane : nr - 1;
@@ -322,7 +329,7 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
     } else {
       // P fragment f = (mt, q) = cat(tile (mt, 2 q), tile (mt, 2 q + 1)); lane
       // (g, c) of tile (mi, ni): query row r = 16 mi + c, key i = 16 ni + 4 g + j.
-      unsigned char *rv = p.ws_rec + (gc * p.Hv + blockIdx.y * NV + v) * kRecBytes;
+      unsigned char *rv = p.ws_rec + (gc * p.Hv + hy * NV + v) * kRecBytes;
       f32x4 pv[3];
 #pragma unroll
       for (int t = 0; t < NTL; ++t) {
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(kPrepThreads * NV) __attribute__((amdgpu_waves_per_
     });
   if (wid < NV) {
     const float(&fv)[P_N][BT] = sm.fac[wid];
-    float *rf = reinterpret_cast<float *>(p.ws_rec + (gc * p.Hv + blockIdx.y * NV + wid) * kRecBytes + kRecF);
+    float *rf = reinterpret_cast<float *>(p.ws_rec + (gc * p.Hv + hy * NV + wid) * kRecBytes + kRecF);
     const float eg = fv[P_EG][lane], rk = fv[P_RK][lane];
     rf[0 * BT + lane] = eg * rk;                          // aa (beta is in T')
     rf[1 * BT + lane] = fv[P_ECG][lane] * rk;             // cw
