@@ -61,7 +61,10 @@ __device__ __forceinline__ constexpr int dk_of(int mt, int r) {
 __device__ __forceinline__ constexpr int frag_id(int mt, int q) { return q == 0 ? mt : 2 + mt; }
 
 template <typename T, int DK>
-__global__ __launch_bounds__(kThreads) void chunk_state_wide_kernel(ChunkArgs p) {
+// One workgroup per CU (the LDS rings), one wave per SIMD: the compute waves
+// may use the whole register file.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_state_wide_kernel(
+    ChunkArgs p) {
   using MF = M2<T>;
   using f8 = typename MF::f8;
   using v4 = typename MF::v4;
@@ -159,14 +162,22 @@ __global__ __launch_bounds__(kThreads) void chunk_state_wide_kernel(ChunkArgs p)
       f32x4 X[4], z[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) X[mt] = z[mt] = zero4;
+      // every fragment read of the step is issued before its products (LDS
+      // latency, not the MFMA issue rate, bounds this wave's step)
+      f8 kfa[KT][4], qfa[KT][4];
+#pragma unroll
+      for (int pp = 0; pp < KT; ++pp)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          kfa[pp][mt] = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
+          qfa[pp][mt] = *reinterpret_cast<const f8 *>(qt + mt * 16 * RB + fo[pp]);
+        }
 #pragma unroll
       for (int pp = 0; pp < KT; ++pp) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const f8 kf = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
-          const f8 qf = *reinterpret_cast<const f8 *>(qt + mt * 16 * RB + fo[pp]);
-          X[mt] = MF::k32(kf, Sf[pp], X[mt]);
-          z[mt] = MF::k32(Sf[pp], qf, z[mt]);
+          X[mt] = MF::k32(kfa[pp][mt], Sf[pp], X[mt]);
+          z[mt] = MF::k32(Sf[pp], qfa[pp][mt], z[mt]);
         }
       }
       f8 Tf[6], Pf[6];
@@ -218,18 +229,24 @@ __global__ __launch_bounds__(kThreads) void chunk_state_wide_kernel(ChunkArgs p)
         }
       }
       // S = e^{gamma_C} S0 + K^T (cw (.) Vn)
+      f8 kt8[NT][2];
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
         const int tro = yrow * RB + (((4 * (mt >> 1) + (c & 3)) ^ kswz<DK>(yrow)) << 4) + 8 * (mt & 1);
-        f32x4 acc = S[mt] * eC;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const unsigned char *a1 = kt + tro + (32 * q) * RB;
           const unsigned char *a2 = kt + tro + (32 * q + 16) * RB;
           const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(a1));
           const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(a2));
-          acc = MF::k32(cat8<T>(__builtin_bit_cast(v4, r1), __builtin_bit_cast(v4, r2)), Bw[q], acc);
+          kt8[mt][q] = cat8<T>(__builtin_bit_cast(v4, r1), __builtin_bit_cast(v4, r2));
         }
+      }
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        f32x4 acc = S[mt] * eC;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) acc = MF::k32(kt8[mt][q], Bw[q], acc);
         S[mt] = acc;
       }
 #pragma unroll
