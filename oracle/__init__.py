@@ -23,8 +23,8 @@ Parity status of each function (what pins it; the pins live in
                           of ``gated_delta_rule``); the cache shift is exact;
                           a closed form for one step from a nonzero state.
 
-``backward.py`` (first-order gradients of the gated norm and of the prologue,
-by float64 autograd of the plain forward) is pinned by finite differences and
+``backward.py`` (first-order gradients of the gated norm, of the prologue and
+of the gated delta rule, by float64 autograd of the plain forward) is pinned by finite differences and
 closed forms in ``tests/test_oracle_backward_pins.py``.
 
 No function is "parity unpinned", but the absolute values of the layer have no

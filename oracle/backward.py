@@ -14,9 +14,14 @@ derivative of the stage's exact function (the activation-dtype roundings of
 the forward are treated as the identity), evaluated at the given stored
 values.
 
+The recurrence (``gated_delta_rule_fn``) is the gated delta rule written
+token by token; its backward (``chunk_rule_bwd``) is autograd of it.
+
 Parity status: pinned by finite differences (``torch.autograd.gradcheck``,
 independent of autograd's own derivative rules) on small inputs and by closed
-forms at special points; see ``tests/test_oracle_pins.py``.
+forms at special points (one token from a zero state, zero write strength,
+the last write's value gradient); the recurrence's forward equals the pinned
+C recurrence of ``gdn.py``. See ``tests/test_oracle_backward_pins.py``.
 """
 from __future__ import annotations
 
@@ -110,4 +115,71 @@ def prologue_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, d_qkv, d_g
     d = [_np(t) for t in d]
     if bias is None:
         d.insert(4, None)
+    return tuple(d)
+
+
+# --------------------------------------------------------------------------
+# The gated delta rule (the recurrence of gdn_chunk_rule_fwd)
+# --------------------------------------------------------------------------
+def _l2n(x, eps):
+    return x / torch.sqrt(torch.sum(x * x, dim=-1, keepdim=True) + eps)
+
+
+def gated_delta_rule_fn(q, k, v, g, beta, scale=1.0, use_qk_l2norm=True, l2_eps=1e-6,
+                        cu_seqlens=None, initial_state=None):
+    """The token-by-token recurrence on float64 tensors (Gated DeltaNet's
+    gated delta rule, which the pages run in chunked form; P1 What/Why for the
+    q/k normalisation folded into it):
+        S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+        o_t = scale S_t q_t.
+    q, k: [B, T, Hqk, dk]; v: [B, T, Hv, dv]; g, beta: [B, T, Hv]; value head
+    h reads q/k head h // (Hv // Hqk). Returns (o [B, T, Hv, dv], final state
+    [N, Hv, dv, dk])."""
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    G = Hv // Hqk
+    if use_qk_l2norm:
+        q, k = _l2n(q, l2_eps), _l2n(k, l2_eps)
+    q = q.repeat_interleave(G, dim=2)
+    k = k.repeat_interleave(G, dim=2)
+    if cu_seqlens is None:
+        spans = [(b, 0, T) for b in range(B)]
+    else:
+        cu = [int(c) for c in cu_seqlens]
+        spans = [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+    outs, finals = [], []
+    for n, (b, t0, t1) in enumerate(spans):
+        S = torch.zeros((Hv, dv, dk), dtype=q.dtype) if initial_state is None else initial_state[n]
+        for t in range(t0, t1):
+            kt, vt, qt = k[b, t], v[b, t], q[b, t]          # [Hv, dk], [Hv, dv], [Hv, dk]
+            Sk = torch.einsum("hij,hj->hi", S, kt)
+            S = torch.exp(g[b, t])[:, None, None] * (S - beta[b, t][:, None, None] * Sk[:, :, None] * kt[:, None, :]) \
+                + beta[b, t][:, None, None] * vt[:, :, None] * kt[:, None, :]
+            outs.append((b, t, scale * torch.einsum("hij,hj->hi", S, qt)))
+        finals.append(S)
+    rows = [[None] * T for _ in range(B)]
+    for b, t, o in outs:
+        rows[b][t] = o
+    o = torch.stack([torch.stack(r, 0) if T else torch.zeros((0, Hv, dv), dtype=q.dtype) for r in rows], 0)
+    return o, torch.stack(finals, 0)
+
+
+def chunk_rule_bwd(q, k, v, g, beta, d_o, scale=1.0, use_qk_l2norm=True, l2_eps=1e-6,
+                   cu_seqlens=None, initial_state=None, d_final_state=None):
+    """Gradients (dq, dk, dv, dg, dbeta, d_initial_state) of
+    sum(d_o * o) + sum(d_final_state * S_final) for gated_delta_rule_fn.
+    d_initial_state is None when initial_state is None."""
+    q_, k_, v_ = _t(q, True), _t(k, True), _t(v, True)
+    g_, b_ = _t(g, True), _t(beta, True)
+    h0 = _t(initial_state, True)
+    o, fin = gated_delta_rule_fn(q_, k_, v_, g_, b_, scale, use_qk_l2norm, l2_eps, cu_seqlens, h0)
+    outs, grads = [o], [_t(d_o)]
+    if d_final_state is not None:
+        outs.append(fin)
+        grads.append(_t(d_final_state))
+    ins = [q_, k_, v_, g_, b_] + ([h0] if h0 is not None else [])
+    d = torch.autograd.grad(outs, ins, grads, allow_unused=True)
+    d = [np.zeros(x.shape) if gr is None else _np(gr) for x, gr in zip(ins, d)]
+    if h0 is None:
+        d.append(None)
     return tuple(d)

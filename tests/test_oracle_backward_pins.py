@@ -93,3 +93,89 @@ def test_prologue_gradient_closed_forms():
     np.testing.assert_allclose(da, -d_g * np.exp(A_log) / 2, rtol=1e-14)
     np.testing.assert_allclose(ddt, np.sum(-d_g * np.exp(A_log) / 2, (0, 1)), rtol=1e-13)
     np.testing.assert_allclose(dal, np.sum(-d_g * np.exp(A_log) * np.log(2.0), (0, 1)), rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# The gated delta rule's backward
+# --------------------------------------------------------------------------
+def _rule_inputs(rng, B, T, Hqk, dk, Hv, dv):
+    return (rng.normal(size=(B, T, Hqk, dk)), rng.normal(size=(B, T, Hqk, dk)), rng.normal(size=(B, T, Hv, dv)),
+            -rng.uniform(0.01, 1.0, (B, T, Hv)), rng.uniform(0.05, 1.0, (B, T, Hv)))
+
+
+@pytest.mark.parametrize("use_l2,cu", [(True, None), (False, None), (True, [0, 3, 3, 10])])
+def test_rule_forward_is_the_oracle_forward(use_l2, cu):
+    rng = np.random.default_rng(10)
+    B = 1 if cu else 2
+    q, k, v, g, b = _rule_inputs(rng, B, 10, 2, 8, 4, 6)
+    N = len(cu) - 1 if cu else B
+    h0 = rng.normal(size=(N, 4, 6, 8))
+    o, fin = OB.gated_delta_rule_fn(*(torch.tensor(x) for x in (q, k, v, g, b)), 0.7, use_l2, 1e-6, cu,
+                                    torch.tensor(h0))
+    ro, rfin = O.gated_delta_rule(q, k, v, g, b, 0.7, use_l2, 1e-6, cu, h0, True)
+    np.testing.assert_allclose(o.numpy(), ro, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(fin.numpy(), rfin, rtol=1e-12, atol=1e-13)
+
+
+def test_rule_gradients_match_finite_differences():
+    rng = np.random.default_rng(11)
+    q, k, v, g, b = (torch.tensor(x, requires_grad=True) for x in _rule_inputs(rng, 1, 6, 1, 3, 2, 2))
+    h0 = torch.tensor(rng.normal(size=(2, 2, 2, 3)), requires_grad=True)
+    cu = [0, 4, 6]
+
+    def f(q, k, v, g, b, h0):
+        o, fin = OB.gated_delta_rule_fn(q, k, v, g, b, 0.6, True, 1e-6, cu, h0)
+        return o, fin
+
+    assert torch.autograd.gradcheck(f, (q, k, v, g, b, h0))
+
+
+def test_rule_gradient_closed_form_one_token_from_zero():
+    # S = beta v k^T and o = scale beta (k.q) v with unit q, k: dv = scale beta
+    # (k.q) dO, dbeta = scale (k.q) (v.dO), dg = 0 (the decay multiplies S0 = 0)
+    rng = np.random.default_rng(12)
+    q, k, v, g, b = _rule_inputs(rng, 1, 1, 1, 5, 1, 4)
+    dO = rng.normal(size=(1, 1, 1, 4))
+    dq, dk, dv, dg, db, dh0 = OB.chunk_rule_bwd(q, k, v, g, b, dO, 0.8)
+    qh, kh = O.l2norm(q), O.l2norm(k)
+    kq = float(np.sum(qh * kh))
+    np.testing.assert_allclose(dv, 0.8 * b[..., None] * kq * dO, rtol=1e-12)
+    np.testing.assert_allclose(db, 0.8 * kq * np.sum(v * dO, -1), rtol=1e-12)
+    np.testing.assert_array_equal(dg, 0.0)
+    assert dh0 is None
+    # d/dq of (qh . c) with qh = q / |q| (eps 1e-6) is (c - qh (qh . c)) / |q|
+    c = 0.8 * b[0, 0, 0] * kh[0, 0, 0] * float(np.sum(v * dO))
+    n = np.sqrt(np.sum(q * q) + 1e-6)
+    np.testing.assert_allclose(dq[0, 0, 0], (c - qh[0, 0, 0] * np.dot(qh[0, 0, 0], c)) / n, rtol=1e-10)
+
+
+def test_rule_gradient_closed_form_zero_write_strength():
+    # beta = 0: S_t = exp(G_t) S0 with G_t the running sum of g, so
+    # o_t = scale exp(G_t) S0 q_t, dv = 0, dS0 = scale sum_t exp(G_t) dO_t q_t^T
+    # and dg_t = sum_{u >= t} scale exp(G_u) dO_u . (S0 q_u)
+    rng = np.random.default_rng(13)
+    q, k, v, g, _ = _rule_inputs(rng, 1, 5, 1, 4, 1, 3)
+    b = np.zeros((1, 5, 1))
+    h0 = rng.normal(size=(1, 1, 3, 4))
+    dO = rng.normal(size=(1, 5, 1, 3))
+    dq, dk, dv, dg, db, dh0 = OB.chunk_rule_bwd(q, k, v, g, b, dO, 0.5, False, 0.0, None, h0)
+    G = np.cumsum(g[0, :, 0])
+    qs = q[0, :, 0]
+    np.testing.assert_array_equal(dv, 0.0)
+    np.testing.assert_array_equal(dk, 0.0)
+    np.testing.assert_allclose(dh0[0, 0], 0.5 * np.einsum("t,ti,tj->ij", np.exp(G), dO[0, :, 0], qs), rtol=1e-12)
+    per = 0.5 * np.exp(G) * np.einsum("ti,ij,tj->t", dO[0, :, 0], h0[0, 0], qs)
+    np.testing.assert_allclose(dg[0, :, 0], np.cumsum(per[::-1])[::-1], rtol=1e-12)
+    np.testing.assert_allclose(dq[0, :, 0], 0.5 * np.exp(G)[:, None] * (dO[0, :, 0] @ h0[0, 0]), rtol=1e-12)
+
+
+def test_rule_gradient_of_the_final_state_alone():
+    # With dO = 0 and dS_T = I-like probe E_ij, the gradient of v_T (last token)
+    # is beta_T E k_T (the last write is beta_T v_T k_T^T, nothing decays it)
+    rng = np.random.default_rng(14)
+    q, k, v, g, b = _rule_inputs(rng, 1, 4, 1, 3, 1, 2)
+    dO = np.zeros((1, 4, 1, 2))
+    E = rng.normal(size=(1, 1, 2, 3))
+    _, _, dv, _, _, _ = OB.chunk_rule_bwd(q, k, v, g, b, dO, 1.0, True, 1e-6, None, None, E)
+    kh = O.l2norm(k)
+    np.testing.assert_allclose(dv[0, 3, 0], b[0, 3, 0] * E[0, 0] @ kh[0, 3, 0], rtol=1e-12)
