@@ -14,8 +14,9 @@
  *   gdn_layer_fwd       the three stages in order, in a caller workspace
  *   gdn_decode_fwd      one recurrent step per sequence (conv cache and FP32
  *                       state updated in place), all stages in one kernel
- *   gdn_gated_norm_bwd, gdn_prologue_bwd   first-order gradients of the
- *                       gated norm and of the prologue
+ *   gdn_gated_norm_bwd, gdn_prologue_bwd, gdn_chunk_rule_bwd
+ *                       first-order gradients of the gated norm, of the
+ *                       prologue and of the chunked gated delta rule
  *
  * Sources (web pages):
  *   [P1] Megatron-LM pull request "perf(gated_delta_net): fold q/k L2-norm
@@ -360,6 +361,58 @@ gdn_status gdn_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
                             const gdn_tensor *d_b, const gdn_tensor *d_A_log,
                             const gdn_tensor *d_dt_bias, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_chunk_rule_bwd - first-order gradients of gdn_chunk_rule_fwd ([P2]
+ * Execution and numerical behavior: the fused stages support first-order
+ * autograd; [P1] Validation checks q/k gradients through the L2 fold).
+ * Gradients of L = sum(d_o * o) + sum(d_final_state * final_state) with
+ * respect to q, k, v, g, beta and the initial state, where o and the final
+ * state are the exact function the forward computes (its activation-dtype
+ * roundings treated as the identity). Arithmetic is FP32; the chunk's state
+ * entering every chunk is recomputed into the workspace, so the forward's
+ * output is not needed.
+ *
+ *   q, k, v, g, beta, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens,
+ *   initial_state   as in gdn_chunk_rule_fwd (initial_state NULL: zero)
+ *   d_o             [B, T, Hv, dv] act dtype, any strides, inner 1
+ *   d_final_state   [N, Hv, dv, dk] F32 contiguous, or NULL (zero)
+ *   dq, dk          [B, T, Hqk, dk] contiguous, act dtype or F32 (dq, dk and
+ *                   dv share one dtype); dq and dk sum over the value heads
+ *                   of each GQA group
+ *   dv              [B, T, Hv, dv] contiguous
+ *   dg, dbeta       [B, T, Hv] F32 contiguous
+ *   d_initial_state [N, Hv, dv, dk] F32 contiguous, or NULL (not written);
+ *                   for an empty packed sequence it equals d_final_state
+ *   workspace       device memory of gdn_chunk_rule_bwd_workspace_bytes(...)
+ *                   bytes, 256-byte aligned, required; it must not overlap
+ *                   any tensor argument or be used by another call until
+ *                   this call's work on `stream` is done
+ * Outputs must not overlap inputs or each other. Supported: dk 64 or 128,
+ * dv a multiple of 16 (GDN_ERR_NOT_SUPPORTED otherwise).
+ */
+gdn_status gdn_chunk_rule_bwd(const gdn_tensor *q, const gdn_tensor *k,
+                              const gdn_tensor *v, const gdn_tensor *g,
+                              const gdn_tensor *beta, float scale,
+                              int32_t use_qk_l2norm_in_kernel, float l2_eps,
+                              const gdn_tensor *cu_seqlens,
+                              const gdn_tensor *initial_state,
+                              const gdn_tensor *d_o,
+                              const gdn_tensor *d_final_state,
+                              const gdn_tensor *dq, const gdn_tensor *dk,
+                              const gdn_tensor *dv, const gdn_tensor *dg,
+                              const gdn_tensor *dbeta,
+                              const gdn_tensor *d_initial_state,
+                              void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Bytes of workspace gdn_chunk_rule_bwd needs (n_seqs as in
+ * gdn_chunk_rule_workspace_bytes). With C = number of chunk rows
+ * (ceil(T/64) + n_seqs packed, B*ceil(T/64) dense), about
+ * 4 C (2 Hqk 64 dk + 2 Hv 64 64 + 2 Hv dv dk + 3 Hv 64 dv) bytes. 0 for
+ * invalid or unsupported geometry. */
+size_t gdn_chunk_rule_bwd_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs,
+                                          const gdn_dims *dims);
 
 #ifdef __cplusplus
 }

@@ -499,6 +499,11 @@ hipError_t launch_prep(const ChunkArgs &a, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_chunk_index(const int32_t *cu, int64_t n_seqs, int32_t *cuc, hipStream_t s) {
+  hipLaunchKernelGGL(chunk_index_kernel, dim3(1), dim3(256), 0, s, cu, n_seqs, cuc);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_prep(const ChunkArgs &a, hipStream_t s) {
   if (a.act == kBF16)
     return a.dk == 64 ? launch_prep<bf16, 64>(a, s) : a.dk == 128 ? launch_prep<bf16, 128>(a, s) : launch_prep<bf16, 256>(a, s);

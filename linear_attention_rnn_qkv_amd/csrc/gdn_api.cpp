@@ -777,6 +777,152 @@ gdn_status attach_chunk_ws(gdn::ChunkArgs *p, void *ws, size_t ws_bytes) {
   return GDN_OK;
 }
 
+// Workspace of the chunk-rule backward (offsets in bytes, each 256-aligned).
+struct ChunkBwdWs {
+  size_t cu, qn, kn, rq, rk, gam, mm, pp, s0, ds, rr, del, drp, total;
+};
+ChunkBwdWs chunk_bwd_layout(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *d) {
+  ChunkBwdWs w;
+  const size_t N = (size_t)(n_seqs > 0 ? n_seqs : B), cb = (size_t)chunk_bound_of(B, T, n_seqs);
+  const size_t Hqk = (size_t)d->Hqk, Hv = (size_t)d->Hv, dk = (size_t)d->dk, dv = (size_t)d->dv;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  w.cu = take((N + 1) * 4);
+  w.qn = take(cb * Hqk * 64 * dk * 4);
+  w.kn = take(cb * Hqk * 64 * dk * 4);
+  w.rq = take(cb * Hqk * 64 * 4);
+  w.rk = take(cb * Hqk * 64 * 4);
+  w.gam = take(cb * Hv * 64 * 4);
+  w.mm = take(cb * Hv * 64 * 64 * 4);
+  w.pp = take(cb * Hv * 64 * 64 * 4);
+  w.s0 = take(cb * Hv * dv * dk * 4);
+  w.ds = take(cb * Hv * dv * dk * 4);
+  w.rr = take(cb * Hv * 64 * dv * 4);
+  w.del = take(cb * Hv * 64 * dv * 4);
+  w.drp = take(cb * Hv * 64 * dv * 4);
+  w.total = o;
+  return w;
+}
+
+gdn_status plan_chunk_bwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, const gdn_tensor *g,
+                          const gdn_tensor *beta, float scale, int32_t use_l2, float l2_eps,
+                          const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state, const gdn_tensor *d_o,
+                          const gdn_tensor *d_final, const gdn_tensor *dq, const gdn_tensor *dk,
+                          const gdn_tensor *dv, const gdn_tensor *dg, const gdn_tensor *dbeta,
+                          const gdn_tensor *d_init, void *ws, size_t ws_bytes, gdn::ChunkBwdArgs *P) {
+  if (!q || q->ndim != 4) return fail(GDN_ERR_INVALID_VALUE, "q: expected [B, T, Hqk, dk]");
+  if (!v || v->ndim != 4) return fail(GDN_ERR_INVALID_VALUE, "v: expected [B, T, Hv, dv]");
+  const int64_t B = q->shape[0], T = q->shape[1], Hqk = q->shape[2], dkn = q->shape[3];
+  const int64_t Hv = v->shape[2], dvn = v->shape[3];
+  if (B * T == 0) return fail(GDN_ERR_INVALID_VALUE, "empty input (B*T == 0)");
+  const gdn_dims d = {Hqk, dkn, Hv, dvn};
+  TRY(check_dims(&d));
+  const int64_t sq[4] = {B, T, Hqk, dkn}, svv[4] = {B, T, Hv, dvn}, sg[3] = {B, T, Hv};
+  TRY(check(q, "q", 4, sq));
+  const int32_t act = q->dtype;
+  if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "q: dtype must be F32, BF16 or F16");
+  TRY(check(k, "k", 4, sq));
+  TRY(check(v, "v", 4, svv));
+  TRY(check(d_o, "d_o", 4, svv));
+  TRY(check_dtype(k, "k", act));
+  TRY(check_dtype(v, "v", act));
+  TRY(check_dtype(d_o, "d_o", act));
+  TRY(check_inner(q, "q"));
+  TRY(check_inner(k, "k"));
+  TRY(check_inner(v, "v"));
+  TRY(check_inner(d_o, "d_o"));
+  TRY(check(g, "g", 3, sg));
+  TRY(check(beta, "beta", 3, sg));
+  TRY(check_dtype(g, "g", GDN_F32));
+  TRY(check_dtype(beta, "beta", GDN_F32));
+  int64_t n_seqs = 0;
+  TRY(check_cu(cu_seqlens, B, &n_seqs));
+  const int64_t ss[4] = {n_seqs, Hv, dvn, dkn};
+  const gdn_tensor *states[] = {initial_state, d_final, d_init};
+  const char *snames[] = {"initial_state", "d_final_state", "d_initial_state"};
+  for (int i = 0; i < 3; ++i)
+    if (states[i]) {
+      TRY(check(states[i], snames[i], 4, ss));
+      TRY(check_dtype(states[i], snames[i], GDN_F32));
+      TRY(check_contig(states[i], snames[i]));
+    }
+  TRY(check(dq, "dq", 4, sq));
+  const int32_t gdt = dq->dtype;
+  if (gdt != act && gdt != GDN_F32) return fail(GDN_ERR_INVALID_VALUE, "dq: dtype must be q's or F32");
+  TRY(check(dk, "dk", 4, sq));
+  TRY(check(dv, "dv", 4, svv));
+  TRY(check_dtype(dk, "dk", gdt));
+  TRY(check_dtype(dv, "dv", gdt));
+  TRY(check(dg, "dg", 3, sg));
+  TRY(check(dbeta, "dbeta", 3, sg));
+  TRY(check_dtype(dg, "dg", GDN_F32));
+  TRY(check_dtype(dbeta, "dbeta", GDN_F32));
+  const gdn_tensor *outs[] = {dq, dk, dv, dg, dbeta, d_init};
+  const char *onames[] = {"dq", "dk", "dv", "dg", "dbeta", "d_initial_state"};
+  for (int i = 0; i < 5; ++i) TRY(check_contig(outs[i], onames[i]));
+  if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_VALUE, "scale must be finite");
+  if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps)) return fail(GDN_ERR_INVALID_VALUE, "l2_eps must be finite and >= 0");
+  if (!gdn::chunk_bwd_supported(dkn, dvn))
+    return fail(GDN_ERR_NOT_SUPPORTED, "chunk rule backward: dk=%lld dv=%lld is not instantiated (dk 64 or 128)",
+                (long long)dkn, (long long)dvn);
+  if (n_seqs > 65535 || Hv > 65535 || Hqk > 65535)
+    return fail(GDN_ERR_NOT_SUPPORTED, "chunk rule backward: at most 65535 sequences and heads");
+  const int64_t ns = cu_seqlens ? n_seqs : 0;
+  const ChunkBwdWs L = chunk_bwd_layout(B, T, ns, &d);
+  if (!ws) return fail(GDN_ERR_INVALID_VALUE, "chunk rule backward: a workspace is required");
+  if (ws_bytes < L.total)
+    return fail(GDN_ERR_INVALID_VALUE, "chunk backward workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  if ((uintptr_t)ws % 256) return fail(GDN_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  const gdn_tensor wsd = {ws, GDN_BF16, 1, {(int64_t)(ws_bytes / 2)}, {1}};
+  const gdn_tensor *ins[] = {q, k, v, g, beta, cu_seqlens, initial_state, d_o, d_final};
+  for (int i = 0; i < 6; ++i) {
+    if (!outs[i]) continue;
+    for (auto *t : ins)
+      if (overlaps(outs[i], t)) return fail(GDN_ERR_INVALID_VALUE, "%s overlaps an input", onames[i]);
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], outs[j]))
+        return fail(GDN_ERR_INVALID_VALUE, "%s overlaps %s", onames[i], onames[j]);
+    if (overlaps(&wsd, outs[i])) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps %s", onames[i]);
+  }
+  for (auto *t : ins)
+    if (overlaps(&wsd, t)) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps an input");
+
+  gdn::ChunkBwdArgs &p = *P;
+  memset(&p, 0, sizeof p);
+  p.q = q->data; p.k = k->data; p.v = v->data;
+  p.sq_b = q->stride[0]; p.sq_t = q->stride[1]; p.sq_h = q->stride[2];
+  p.sk_b = k->stride[0]; p.sk_t = k->stride[1]; p.sk_h = k->stride[2];
+  p.sv_b = v->stride[0]; p.sv_t = v->stride[1]; p.sv_h = v->stride[2];
+  p.g = static_cast<const float *>(g->data);
+  p.beta = static_cast<const float *>(beta->data);
+  p.sg_b = g->stride[0]; p.sg_t = g->stride[1]; p.sg_h = g->stride[2];
+  p.sbt_b = beta->stride[0]; p.sbt_t = beta->stride[1]; p.sbt_h = beta->stride[2];
+  p.d_o = d_o->data;
+  p.sdo_b = d_o->stride[0]; p.sdo_t = d_o->stride[1]; p.sdo_h = d_o->stride[2];
+  p.cu_seqlens = cu_seqlens ? static_cast<const int32_t *>(cu_seqlens->data) : nullptr;
+  p.n_seqs = n_seqs;
+  p.init_state = initial_state ? static_cast<const float *>(initial_state->data) : nullptr;
+  p.d_final = d_final ? static_cast<const float *>(d_final->data) : nullptr;
+  p.dqq = dq->data; p.dkk = dk->data; p.dvv = dv->data;
+  p.dg = static_cast<float *>(dg->data);
+  p.dbeta = static_cast<float *>(dbeta->data);
+  p.d_init = d_init ? static_cast<float *>(d_init->data) : nullptr;
+  p.B = B; p.T = T; p.Hqk = Hqk; p.dk = dkn; p.Hv = Hv; p.dv = dvn;
+  p.act = act; p.grad_dtype = gdt; p.use_l2 = use_l2 ? 1 : 0; p.l2_eps = l2_eps; p.scale = scale;
+  char *w = static_cast<char *>(ws);
+  auto fp = [&](size_t off) { return reinterpret_cast<float *>(w + off); };
+  p.cu_chunks = reinterpret_cast<int32_t *>(w + L.cu);
+  p.chunk_bound = chunk_bound_of(B, T, ns);
+  p.qn = fp(L.qn); p.kn = fp(L.kn); p.rq = fp(L.rq); p.rk = fp(L.rk); p.gam = fp(L.gam);
+  p.mm = fp(L.mm); p.pp = fp(L.pp); p.s0 = fp(L.s0); p.ds = fp(L.ds);
+  p.rr = fp(L.rr); p.del = fp(L.del); p.drp = fp(L.drp);
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -880,6 +1026,27 @@ gdn_status gdn_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const 
                         dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b, d_A_log, d_dt_bias, workspace,
                         workspace_bytes, &p));
   return launched(gdn::launch_prologue_bwd(p, static_cast<hipStream_t>(stream)), "prologue backward");
+}
+
+size_t gdn_chunk_rule_bwd_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *dims) {
+  if (!dims || B <= 0 || T <= 0 || n_seqs < 0) return 0;
+  if (dims->Hqk <= 0 || dims->dk <= 0 || dims->Hv <= 0 || dims->dv <= 0) return 0;
+  if (!gdn::chunk_bwd_supported(dims->dk, dims->dv)) return 0;
+  return chunk_bwd_layout(B, T, n_seqs, dims).total;
+}
+
+gdn_status gdn_chunk_rule_bwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v, const gdn_tensor *g,
+                              const gdn_tensor *beta, float scale, int32_t use_qk_l2norm_in_kernel, float l2_eps,
+                              const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
+                              const gdn_tensor *d_o, const gdn_tensor *d_final_state, const gdn_tensor *dq,
+                              const gdn_tensor *dk, const gdn_tensor *dv, const gdn_tensor *dg,
+                              const gdn_tensor *dbeta, const gdn_tensor *d_initial_state, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  g_error.clear();
+  gdn::ChunkBwdArgs P;
+  TRY(plan_chunk_bwd(q, k, v, g, beta, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, initial_state, d_o,
+                     d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, &P));
+  return launched(gdn::launch_chunk_bwd(P, (hipStream_t)stream), "chunk rule backward");
 }
 
 size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *dims,

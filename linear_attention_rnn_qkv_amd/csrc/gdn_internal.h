@@ -151,6 +151,35 @@ struct PrologueBwdArgs {
   int32_t x_align, dq_align; // bytes guaranteed for x rows and d_qkv rows
 };
 
+// Backward of the chunked gated delta rule. Workspace arrays are FP32, per
+// chunk row gc (chunk_bound of them) and head:
+//   qn, kn [gc][Hqk][64][dk] unit q, k rows; rq, rk [gc][Hqk][64] inverse norms
+//   gam [gc][Hv][64] running sum of g in the chunk; mm, pp [gc][Hv][64][64]
+//   (I + A)^-1 and scale * masked decayed q.k; s0, ds [gc][Hv][dv][dk] state
+//   entering the chunk and gradient of the state leaving it; rr, del, drp
+//   [gc][Hv][64][dv] R, Delta and M^T dDelta.
+struct ChunkBwdArgs {
+  const void *q, *k, *v;
+  int64_t sq_b, sq_t, sq_h, sk_b, sk_t, sk_h, sv_b, sv_t, sv_h;
+  const float *g, *beta;
+  int64_t sg_b, sg_t, sg_h, sbt_b, sbt_t, sbt_h;
+  const void *d_o;
+  int64_t sdo_b, sdo_t, sdo_h;
+  const int32_t *cu_seqlens;  // null => dense
+  int64_t n_seqs;             // B when dense
+  const float *init_state;    // [N, Hv, dv, dk] or null
+  const float *d_final;       // [N, Hv, dv, dk] or null
+  void *dqq, *dkk, *dvv;       // contiguous [B, T, H, d], grad_dtype
+  float *dg, *dbeta;          // [B, T, Hv] contiguous
+  float *d_init;              // [N, Hv, dv, dk] or null
+  int64_t B, T, Hqk, dk, Hv, dv;
+  int32_t act, grad_dtype, use_l2;
+  float l2_eps, scale;
+  int32_t *cu_chunks;         // [n_seqs + 1] (packed sequences)
+  int64_t chunk_bound;
+  float *qn, *kn, *rq, *rk, *gam, *mm, *pp, *s0, *ds, *rr, *del, *drp;
+};
+
 // Each returns the HIP error of the launch (hipSuccess if queued).
 hipError_t launch_prologue(const PrologueArgs &a, hipStream_t s);
 hipError_t launch_chunk_rule(const ChunkArgs &a, hipStream_t s);
@@ -171,6 +200,13 @@ hipError_t launch_chunk_rule_v2(const ChunkArgs &a, hipStream_t s);
 // state (serial over chunks). Needs a.ws_rec / a.cu_chunks.
 bool chunk_split_supported(int64_t dk, int64_t dv, int32_t act);
 hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s);
+
+// Backward of the chunk rule (dk 64 or 128, dv a multiple of 16).
+bool chunk_bwd_supported(int64_t dk, int64_t dv);
+hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t s);
+
+// cuc[n] = sum over sequences m < n of ceil(len_m / 64), for n in [0, n_seqs].
+hipError_t launch_chunk_index(const int32_t *cu, int64_t n_seqs, int32_t *cuc, hipStream_t s);
 
 // Largest power-of-two alignment (bytes, <= 16) of an address or stride set.
 inline int align_of_host(uint64_t addr) {

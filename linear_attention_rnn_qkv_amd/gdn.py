@@ -72,8 +72,12 @@ def lib() -> ctypes.CDLL:
         L.gdn_prologue_bwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(GdnDims)]
         L.gdn_prologue_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_prologue_bwd.argtypes = [P] * 10 + [ctypes.POINTER(GdnDims)] + [P] * 12 + [vp, ctypes.c_size_t, vp]
+        L.gdn_chunk_rule_bwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                         ctypes.POINTER(GdnDims)]
+        L.gdn_chunk_rule_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_chunk_rule_bwd.argtypes = [P] * 5 + [f32, i32, f32] + [P] * 10 + [vp, ctypes.c_size_t, vp]
         for name in ("gdn_prologue_fwd", "gdn_chunk_rule_fwd", "gdn_gated_norm_fwd", "gdn_layer_fwd",
-                     "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_prologue_bwd"):
+                     "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_prologue_bwd", "gdn_chunk_rule_bwd"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -280,6 +284,37 @@ def gdn_prologue_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seq
                                   ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()),
                                   _stream(x_q)))
     return dxq, dxk, dxv, dw, dbias, da, db, dal, ddt
+
+
+def gdn_chunk_rule_bwd_workspace_bytes(B: int, T: int, dims: Sequence[int], n_seqs: int = 0) -> int:
+    gd = dims_of(*dims)
+    return int(lib().gdn_chunk_rule_bwd_workspace_bytes(int(B), int(T), int(n_seqs), ctypes.byref(gd)))
+
+
+def gdn_chunk_rule_bwd(q, k, v, g, beta, d_o, scale: float, use_qk_l2norm_in_kernel: bool = True,
+                       l2_eps: float = 1e-6, cu_seqlens=None, initial_state=None, d_final_state=None,
+                       want_d_initial_state: bool = False, grad_dtype=None, workspace=None):
+    """Gradients of the chunked gated delta rule. Returns
+    (dq, dk, dv, dg, dbeta, d_initial_state or None); dq, dk, dv in
+    grad_dtype (default q's dtype), dg and dbeta FP32."""
+    B, T, Hv, dv = v.shape
+    Hqk, dk = q.shape[2], q.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    dev = q.device
+    gdt = q.dtype if grad_dtype is None else grad_dtype
+    e = lambda *shape, d=gdt: torch.empty(shape, dtype=d, device=dev)  # noqa: E731
+    dq, dkk, dvv = e(B, T, Hqk, dk), e(B, T, Hqk, dk), e(B, T, Hv, dv)
+    dg, db = e(B, T, Hv, d=torch.float32), e(B, T, Hv, d=torch.float32)
+    dh0 = e(N, Hv, dv, dk, d=torch.float32) if want_d_initial_state else None
+    if workspace is None:
+        nb = gdn_chunk_rule_bwd_workspace_bytes(B, T, (Hqk, dk, Hv, dv), 0 if cu_seqlens is None else N)
+        workspace = _ws(nb, dev)
+    D = [desc(t) for t in (q, k, v, g, beta)]
+    E = [desc(t) for t in (cu_seqlens, initial_state, d_o, d_final_state, dq, dkk, dvv, dg, db, dh0)]
+    _check(lib().gdn_chunk_rule_bwd(*[_p(d) for d in D], float(scale), int(bool(use_qk_l2norm_in_kernel)),
+                                    float(l2_eps), *[_p(d) for d in E], ctypes.c_void_p(workspace.data_ptr()),
+                                    ctypes.c_size_t(workspace.numel()), _stream(q)))
+    return dq, dkk, dvv, dg, db, dh0
 
 
 def dtype_name(t: torch.dtype) -> str:

@@ -23,7 +23,8 @@ def test_exports_every_declared_symbol():
     assert names == {"gdn_last_error", "gdn_version", "gdn_prologue_fwd", "gdn_chunk_rule_fwd",
                      "gdn_chunk_rule_workspace_bytes", "gdn_gated_norm_fwd", "gdn_layer_workspace_bytes",
                      "gdn_layer_fwd", "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_gated_norm_bwd_workspace_bytes",
-                     "gdn_prologue_bwd", "gdn_prologue_bwd_workspace_bytes"}
+                     "gdn_prologue_bwd", "gdn_prologue_bwd_workspace_bytes", "gdn_chunk_rule_bwd",
+                     "gdn_chunk_rule_bwd_workspace_bytes"}
     L = gdn.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -255,6 +256,36 @@ def test_backward_workspace_bytes_and_rejections():
     _expect(INVALID, "d_g: dtype", gdn.gdn_prologue_bwd, *args, x["dims"], dq, dg.bfloat16(), dbt)
     _expect(INVALID, "workspace too small", gdn.gdn_prologue_bwd, *args, x["dims"], dq, dg, dbt,
             workspace=torch.zeros(16, dtype=torch.uint8))
+
+
+def _rule_bwd_inputs(B=1, T=8, Hqk=2, dk=64, Hv=4, dv=32, dt=torch.bfloat16):
+    q, k = torch.zeros(B, T, Hqk, dk, dtype=dt), torch.zeros(B, T, Hqk, dk, dtype=dt)
+    v, do = torch.zeros(B, T, Hv, dv, dtype=dt), torch.zeros(B, T, Hv, dv, dtype=dt)
+    g, beta = torch.zeros(B, T, Hv), torch.zeros(B, T, Hv)
+    return q, k, v, g, beta, do
+
+
+def test_chunk_rule_bwd_workspace_bytes_and_rejections():
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # dense B=2, T=100: 4 chunk rows. Chunk offsets, unit q and k rows, their
+    # inverse norms, gamma, (I + A)^-1 and P, S0 and dS, then R, Delta, dR'
+    cb, Hqk, dk, Hv, dv = 4, 2, 64, 4, 32
+    expect = (a256(3 * 4) + 2 * a256(cb * Hqk * 64 * dk * 4) + 2 * a256(cb * Hqk * 64 * 4) +
+              a256(cb * Hv * 64 * 4) + 2 * a256(cb * Hv * 64 * 64 * 4) + 2 * a256(cb * Hv * dv * dk * 4) +
+              3 * a256(cb * Hv * 64 * dv * 4))
+    assert gdn.gdn_chunk_rule_bwd_workspace_bytes(2, 100, (Hqk, dk, Hv, dv)) == expect
+    # packed: ceil(T / 64) + n_seqs rows
+    assert gdn.gdn_chunk_rule_bwd_workspace_bytes(1, 100, (1, 128, 1, 64), n_seqs=3) > 0
+    assert gdn.gdn_chunk_rule_bwd_workspace_bytes(1, 100, (1, 256, 1, 64)) == 0  # dk 256 not built
+    q, k, v, g, beta, do = _rule_bwd_inputs()
+    _expect(INVALID, "d_o: dtype", gdn.gdn_chunk_rule_bwd, q, k, v, g, beta, do.half(), 0.125)
+    _expect(INVALID, "dq: dtype", gdn.gdn_chunk_rule_bwd, q, k, v, g, beta, do, 0.125, grad_dtype=torch.float16)
+    _expect(INVALID, "workspace too small", gdn.gdn_chunk_rule_bwd, q, k, v, g, beta, do, 0.125,
+            workspace=torch.zeros(16, dtype=torch.uint8))
+    _expect(INVALID, "d_final_state: dim", gdn.gdn_chunk_rule_bwd, q, k, v, g, beta, do, 0.125,
+            d_final_state=torch.zeros(1, 4, 32, 32))
+    q2, k2, v2, g2, b2, do2 = _rule_bwd_inputs(dk=256)
+    _expect(UNSUPPORTED, "dk=256", gdn.gdn_chunk_rule_bwd, q2, k2, v2, g2, b2, do2, 0.0625)
 
 
 def test_bench_refuses_more_than_one_gpu():
