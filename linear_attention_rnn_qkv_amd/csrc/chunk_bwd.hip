@@ -36,26 +36,7 @@ namespace {
 
 constexpr int BT = 64;
 constexpr int kThreads = 256;
-constexpr int XP = 17;  // row stride of [64][16] tiles
 constexpr int MP = 65;  // row stride of [64][64] tiles
-
-// acc[r][c] += sum_k A(ty + 16 r, k) * B(k, tx + 16 c), with
-// A(i, k) = A[i * ars + k * acs] and B(k, j) = B[k * brs + j * bcs].
-template <int RM, int CN>
-__device__ __forceinline__ void mm(float (&acc)[RM][CN], const float *A, int ars, int acs, const float *B, int brs,
-                                   int bcs, int kn, int ty, int tx) {
-  for (int kk = 0; kk < kn; ++kk) {
-    float a[RM], b[CN];
-#pragma unroll
-    for (int r = 0; r < RM; ++r) a[r] = A[(ty + 16 * r) * ars + kk * acs];
-#pragma unroll
-    for (int c = 0; c < CN; ++c) b[c] = B[kk * brs + (tx + 16 * c) * bcs];
-#pragma unroll
-    for (int r = 0; r < RM; ++r)
-#pragma unroll
-      for (int c = 0; c < CN; ++c) acc[r][c] = fmaf(a[r], b[c], acc[r][c]);
-  }
-}
 
 template <int RM, int CN>
 __device__ __forceinline__ void zero(float (&acc)[RM][CN]) {
@@ -122,51 +103,201 @@ __device__ __forceinline__ void seq_pos(const ChunkBwdArgs &p, int64_t n, int64_
 }
 
 // ---------------------------------------------------------------------------
+// Vector-read products for the serial kernels. Operands in LDS, FP32.
+//   mm_kk: A(i, k) = A[k * lda + i] (k-major), B(k, j) = B[k * ldb + j]
+//   mm_rk: A(i, k) = A[i * lda + k] (row-major; k0, k1 multiples of 4)
+//   mm_rr: as mm_rk, and B(k, j) = B[j * ldb + k] (so the product is A B^T)
+// acc[r][c] += sum_{k0 <= k < k1} A(r0 + r, k) B(k, c0 + c). Strides and
+// r0, c0 keep every vector read aligned to its size.
+// ---------------------------------------------------------------------------
+typedef float fv4 __attribute__((ext_vector_type(4)));
+typedef float fv2 __attribute__((ext_vector_type(2)));
+
+template <int N>
+__device__ __forceinline__ void ldv(const float *p, float (&o)[N]) {
+  if constexpr (N == 4) {
+    const fv4 v = *reinterpret_cast<const fv4 *>(p);
+    o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+  } else if constexpr (N == 2) {
+    const fv2 v = *reinterpret_cast<const fv2 *>(p);
+    o[0] = v[0]; o[1] = v[1];
+  } else if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const fv4 v = *reinterpret_cast<const fv4 *>(p + i);
+      o[i] = v[0]; o[i + 1] = v[1]; o[i + 2] = v[2]; o[i + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) o[i] = p[i];
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void stv(float *p, const float (&o)[N]) {
+  if constexpr (N == 4) {
+    *reinterpret_cast<fv4 *>(p) = fv4{o[0], o[1], o[2], o[3]};
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<fv2 *>(p) = fv2{o[0], o[1]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) p[i] = o[i];
+  }
+}
+
+template <int RM, int CN>
+__device__ __forceinline__ void mm_kk(float (&acc)[RM][CN], const float *A, int lda, int r0, const float *B, int ldb,
+                                      int c0, int k0, int k1) {
+  for (int k = k0; k < k1; ++k) {
+    float a[RM], b[CN];
+    ldv<RM>(A + k * lda + r0, a);
+    ldv<CN>(B + k * ldb + c0, b);
+#pragma unroll
+    for (int r = 0; r < RM; ++r)
+#pragma unroll
+      for (int c = 0; c < CN; ++c) acc[r][c] = fmaf(a[r], b[c], acc[r][c]);
+  }
+}
+
+template <int RM, int CN>
+__device__ __forceinline__ void mm_rk(float (&acc)[RM][CN], const float *A, int lda, int r0, const float *B, int ldb,
+                                      int c0, int k0, int k1) {
+  for (int k = k0; k < k1; k += 4) {
+    float a[RM][4];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) ldv<4>(A + (r0 + r) * lda + k, a[r]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      float b[CN];
+      ldv<CN>(B + (k + kk) * ldb + c0, b);
+#pragma unroll
+      for (int r = 0; r < RM; ++r)
+#pragma unroll
+        for (int c = 0; c < CN; ++c) acc[r][c] = fmaf(a[r][kk], b[c], acc[r][c]);
+    }
+  }
+}
+
+template <int RM, int CN>
+__device__ __forceinline__ void mm_rr(float (&acc)[RM][CN], const float *A, int lda, int r0, const float *B, int ldb,
+                                      int c0, int k0, int k1) {
+  for (int k = k0; k < k1; k += 4) {
+    float a[RM][4], b[CN][4];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) ldv<4>(A + (r0 + r) * lda + k, a[r]);
+#pragma unroll
+    for (int c = 0; c < CN; ++c) ldv<4>(B + (c0 + c) * ldb + k, b[c]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int r = 0; r < RM; ++r)
+#pragma unroll
+        for (int c = 0; c < CN; ++c) acc[r][c] = fmaf(a[r][kk], b[c][kk], acc[r][c]);
+  }
+}
+
+// A 64 x 16 product split over the contraction: wave w's lanes hold 4 x 4
+// tiles (rows 4 (lane >> 2), columns 4 (lane & 3)) of its partial sum; the
+// four partials meet in `red` and thread tid gets row tid >> 2, columns
+// 4 (tid & 3) .. + 3 of the total.
+__device__ __forceinline__ void ksplit_sum(float *red, const float (&acc)[4][4], float (&out)[4]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tg = lane >> 2, ig = lane & 3;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) stv<4>(red + w * 1024 + (4 * tg + r) * 16 + 4 * ig, acc[r]);
+  __syncthreads();
+  const int t = threadIdx.x >> 2, i4 = 4 * (threadIdx.x & 3);
+  ldv<4>(red + t * 16 + i4, out);
+#pragma unroll
+  for (int ww = 1; ww < 4; ++ww) {
+    float x[4];
+    ldv<4>(red + ww * 1024 + t * 16 + i4, x);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[c] += x[c];
+  }
+}
+
+// Chunk factors shared by the serial kernels: exp(gamma), exp(gamma_C - gamma)
+// (0 past the last row), beta (0 past the last row), exp(gamma_C).
+struct Fac {
+  float eg[BT], cw[BT], beta[BT], eC;
+};
+
+__device__ __forceinline__ void load_fac(const ChunkBwdArgs &p, Fac &F, int64_t gc, int64_t h, int64_t brow, int64_t t0,
+                                         int nr) {
+  if (threadIdx.x < BT) {
+    const int t = threadIdx.x;
+    const float *gm = p.gam + (gc * p.Hv + h) * BT;
+    const float gl = gm[nr - 1], gt = gm[t];
+    F.eg[t] = __expf(gt);
+    F.cw[t] = t < nr ? __expf(gl - gt) : 0.f;
+    F.beta[t] = t < nr ? p.beta[brow * p.sbt_b + (t0 + t) * p.sbt_t + h * p.sbt_h] : 0.f;
+    if (t == 0) F.eC = __expf(gl);
+  }
+}
+
+// Rows [0, 64) x cols [0, D) of a contiguous FP32 [64][D] array into LDS rows
+// of stride ld (float4 copies).
+template <int D>
+__device__ __forceinline__ void copy_rows(float *dst, int ld, const float *src) {
+  constexpr int Q = D / 4;
+  for (int e = threadIdx.x; e < BT * Q; e += kThreads) {
+    const int t = e / Q, j = 4 * (e % Q);
+    *reinterpret_cast<fv4 *>(dst + t * ld + j) = *reinterpret_cast<const fv4 *>(src + t * D + j);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Prep: unit q, k rows per (chunk, q/k head); gamma, M and scale * Pt per
 // value head of the group.
 // ---------------------------------------------------------------------------
 template <typename T, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
-  constexpr int KP = DK + 1;
-  __shared__ float sQ[BT * KP], sK[BT * KP];
-  __shared__ float sA[BT * MP], sM[BT * MP];
+  constexpr int KP = DK + 4;
+  __shared__ alignas(16) float sQ[BT * KP], sK[BT * KP];
+  __shared__ alignas(16) float sA[BT * MP], sM[BT * MP];
   __shared__ float sgam[BT], sbeta[BT];
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
   const int64_t gc = blockIdx.x, hk = blockIdx.y;
   const ChunkPos cp = chunk_pos(p, gc);
   if (!cp.valid) return;
   const int nr = cp.nr;
   const int64_t G = p.Hv / p.Hqk;
 
-  // q, k rows of the chunk (zero past the last token)
-  for (int e = tid; e < BT * DK; e += kThreads) {
-    const int t = e / DK, j = e % DK;
-    float qv = 0.f, kv = 0.f;
-    if (t < nr) {
-      const int64_t tt = cp.t0 + t;
-      qv = f(static_cast<const T *>(p.q)[cp.brow * p.sq_b + tt * p.sq_t + hk * p.sq_h + j]);
-      kv = f(static_cast<const T *>(p.k)[cp.brow * p.sk_b + tt * p.sk_t + hk * p.sk_h + j]);
-    }
-    sQ[t * KP + j] = qv;
-    sK[t * KP + j] = kv;
-  }
-  __syncthreads();
-  // inverse norms: four lanes per row
+  // q, k rows of the chunk (zero past the last token), four lanes per row
   {
     const int t = tid >> 2, part = tid & 3;
+    constexpr int SEG = DK / 4;  // columns part * SEG .. + SEG - 1
+    float qv[SEG], kv[SEG];
+#pragma unroll
+    for (int q = 0; q < SEG; ++q) qv[q] = kv[q] = 0.f;
+    if (t < nr) {
+      const int64_t tt = cp.t0 + t;
+      load_vec<T, SEG>(static_cast<const T *>(p.q) + cp.brow * p.sq_b + tt * p.sq_t + hk * p.sq_h + part * SEG,
+                       (int)sizeof(T), qv);
+      load_vec<T, SEG>(static_cast<const T *>(p.k) + cp.brow * p.sk_b + tt * p.sk_t + hk * p.sk_h + part * SEG,
+                       (int)sizeof(T), kv);
+    }
     float sq = 0.f, sk = 0.f;
-    for (int j = part; j < DK; j += 4) {
-      sq = fmaf(sQ[t * KP + j], sQ[t * KP + j], sq);
-      sk = fmaf(sK[t * KP + j], sK[t * KP + j], sk);
+#pragma unroll
+    for (int q = 0; q < SEG; ++q) {
+      sq = fmaf(qv[q], qv[q], sq);
+      sk = fmaf(kv[q], kv[q], sk);
     }
     sq = group_sum<4>(sq);
     sk = group_sum<4>(sk);
     const float rq = p.use_l2 ? 1.f / sqrtf(sq + p.l2_eps) : 1.f;
     const float rk = p.use_l2 ? 1.f / sqrtf(sk + p.l2_eps) : 1.f;
-    __syncthreads();
-    for (int j = part; j < DK; j += 4) {
-      sQ[t * KP + j] *= rq;
-      sK[t * KP + j] *= rk;
+    float *qn = p.qn + ((gc * p.Hqk + hk) * BT + t) * DK + part * SEG;
+    float *kn = p.kn + ((gc * p.Hqk + hk) * BT + t) * DK + part * SEG;
+#pragma unroll
+    for (int q = 0; q < SEG; q += 4) {
+      float a[4] = {qv[q] * rq, qv[q + 1] * rq, qv[q + 2] * rq, qv[q + 3] * rq};
+      float b[4] = {kv[q] * rk, kv[q + 1] * rk, kv[q + 2] * rk, kv[q + 3] * rk};
+      stv<4>(sQ + t * KP + part * SEG + q, a);
+      stv<4>(sK + t * KP + part * SEG + q, b);
+      stv<4>(qn + q, a);
+      stv<4>(kn + q, b);
     }
     if (part == 0) {
       p.rq[(gc * p.Hqk + hk) * BT + t] = rq;
@@ -174,20 +305,12 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
     }
   }
   __syncthreads();
-  {
-    float *qn = p.qn + (gc * p.Hqk + hk) * BT * DK, *kn = p.kn + (gc * p.Hqk + hk) * BT * DK;
-    for (int e = tid; e < BT * DK; e += kThreads) {
-      const int t = e / DK, j = e % DK;
-      qn[e] = sQ[t * KP + j];
-      kn[e] = sK[t * KP + j];
-    }
-  }
-  // G = K K^T and QK = Q K^T; thread owns rows ty + 16 r, columns tx + 16 c
+  // G = K K^T and QK = Q K^T; thread owns rows 4 rg .., columns 4 cg ..
   float gg[4][4], qk[4][4];
   zero(gg);
   zero(qk);
-  mm(gg, sK, KP, 1, sK, 1, KP, DK, ty, tx);
-  mm(qk, sQ, KP, 1, sK, 1, KP, DK, ty, tx);
+  mm_rr(gg, sK, KP, 4 * rg, sK, KP, 4 * cg, 0, DK);
+  mm_rr(qk, sQ, KP, 4 * rg, sK, KP, 4 * cg, 0, DK);
 
   for (int64_t vh = 0; vh < G; ++vh) {
     const int64_t h = hk * G + vh;
@@ -213,14 +336,18 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
     {
       float *pp = p.pp + (gc * p.Hv + h) * BT * BT;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * rg + r;
+        float pv[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int t = ty + 16 * r, s = tx + 16 * c;
+          const int s = 4 * cg + c;
           const float e = s <= t ? __expf(sgam[t] - sgam[s]) : 0.f;
           sA[t * MP + s] = s < t ? sbeta[t] * e * gg[r][c] : 0.f;
-          pp[t * BT + s] = p.scale * e * qk[r][c];
+          pv[c] = p.scale * e * qk[r][c];
         }
+        stv<4>(pp + t * BT + 4 * cg, pv);
+      }
     }
     __syncthreads();
     // M = (I + A)^-1 by forward substitution, column c by four lanes; lane
@@ -253,241 +380,251 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Forward states: S0 of every chunk, R and Delta, for 16 value rows.
+// Forward states: S0 of every chunk, R and Delta, for 16 value rows. The
+// state slice is kept transposed in LDS (sST[j][i]).
 // ---------------------------------------------------------------------------
 template <typename T, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_states_kernel(ChunkBwdArgs p) {
-  constexpr int KP = DK + 1, CN = DK / 16;
-  __shared__ float sK[BT * KP], sM[BT * MP], sS[16 * KP];
-  __shared__ float sX[BT * XP], sV[BT * XP];
-  __shared__ float seg[BT], scw[BT], sbeta[BT];
-  __shared__ float seC;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  constexpr int KP = DK + 4, CJ = DK / 64;
+  __shared__ alignas(16) float sK[BT * KP];    // unit k rows [t][j]
+  __shared__ alignas(16) float sM[BT * 68];    // M [t][s]
+  __shared__ alignas(16) float sST[DK * 16];   // S^T [j][i]
+  __shared__ alignas(16) float sX[BT * 16];    // beta R [s][i]
+  __shared__ alignas(16) float sV[BT * 16];    // v, then cw Delta [s][i]
+  __shared__ alignas(16) float red[4 * 1024];
+  __shared__ Fac F;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t j0 = (int64_t)blockIdx.x * 16, h = blockIdx.y, n = blockIdx.z;
   const int64_t hk = h / (p.Hv / p.Hqk);
   int64_t brow, bos, L, gc0;
   seq_pos(p, n, brow, bos, L, gc0);
   const int64_t nch = (L + BT - 1) / BT;
+  const int et = tid >> 2, ei = 4 * (tid & 3);  // epilogue: row et, columns ei .. ei + 3
+  const int ig = tid & 3, jg = tid >> 2;        // state update: rows 4 ig .., columns CJ jg ..
 
   for (int e = tid; e < 16 * DK; e += kThreads) {
     const int i = e / DK, j = e % DK;
-    sS[i * KP + j] = p.init_state ? p.init_state[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] : 0.f;
+    sST[j * 16 + i] = p.init_state ? p.init_state[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] : 0.f;
   }
   __syncthreads();
   for (int64_t c = 0; c < nch; ++c) {
     const int64_t gc = gc0 + c, t0 = bos + c * BT;
     const int nr = (int)(L - c * BT < BT ? L - c * BT : BT);
     float *s0 = p.s0 + ((gc * p.Hv + h) * p.dv + j0) * DK;
-    for (int e = tid; e < 16 * DK; e += kThreads) s0[e] = sS[(e / DK) * KP + e % DK];
-    const float *kn = p.kn + (gc * p.Hqk + hk) * BT * DK;
-    for (int e = tid; e < BT * DK; e += kThreads) sK[(e / DK) * KP + e % DK] = kn[e];
-    const float *mm_ = p.mm + (gc * p.Hv + h) * BT * BT;
-    for (int e = tid; e < BT * BT; e += kThreads) sM[(e >> 6) * MP + (e & 63)] = mm_[e];
-    if (tid < BT) {
-      const float *gm = p.gam + (gc * p.Hv + h) * BT;
-      const float gl = gm[nr - 1], gt = gm[tid];
-      seg[tid] = __expf(gt);
-      scw[tid] = tid < nr ? __expf(gl - gt) : 0.f;
-      sbeta[tid] = tid < nr ? p.beta[brow * p.sbt_b + (t0 + tid) * p.sbt_t + h * p.sbt_h] : 0.f;
-      if (tid == 0) seC = __expf(gl);
-    }
-    for (int e = tid; e < BT * 16; e += kThreads) {
-      const int t = e >> 4, i = e & 15;
-      sV[t * XP + i] = t < nr ? f(static_cast<const T *>(p.v)[brow * p.sv_b + (t0 + t) * p.sv_t + h * p.sv_h + j0 + i])
-                              : 0.f;
+    for (int e = tid; e < 16 * DK; e += kThreads) s0[e] = sST[(e % DK) * 16 + e / DK];
+    copy_rows<DK>(sK, KP, p.kn + (gc * p.Hqk + hk) * BT * DK);
+    copy_rows<BT>(sM, 68, p.mm + (gc * p.Hv + h) * BT * BT);
+    load_fac(p, F, gc, h, brow, t0, nr);
+    {
+      float vv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (et < nr) load_vec<T, 4>(static_cast<const T *>(p.v) + brow * p.sv_b + (t0 + et) * p.sv_t + h * p.sv_h + j0 + ei,
+                                  (int)sizeof(T), vv);
+      stv<4>(sV + et * 16 + ei, vv);
     }
     __syncthreads();
-    // KS = K S0^T; R = V - exp(gamma) KS; X = beta R
+    // KS = K S0^T (contraction over dk, a quarter per wave); R = V - exp(gamma) KS
     {
-      float ks[4][1];
-      zero(ks);
-      mm(ks, sK, KP, 1, sS, 1, KP, DK, ty, tx);
-      float *rr = p.rr + (gc * p.Hv + h) * BT * p.dv + j0;
+      float acc[4][4];
+      zero(acc);
+      mm_rk(acc, sK, KP, 4 * (lane >> 2), sST, 16, 4 * (lane & 3), w * (DK / 4), (w + 1) * (DK / 4));
+      float ks[4];
+      ksplit_sum(red, acc, ks);
+      float vv[4], R[4], X[4];
+      ldv<4>(sV + et * 16 + ei, vv);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = ty + 16 * r;
-        const float R = sV[t * XP + tx] - seg[t] * ks[r][0];
-        rr[t * p.dv + tx] = R;
-        sX[t * XP + tx] = sbeta[t] * R;
+      for (int q = 0; q < 4; ++q) {
+        R[q] = vv[q] - F.eg[et] * ks[q];
+        X[q] = F.beta[et] * R[q];
       }
+      stv<4>(p.rr + ((gc * p.Hv + h) * BT + et) * p.dv + j0 + ei, R);
+      stv<4>(sX + et * 16 + ei, X);
     }
     __syncthreads();
-    // Delta = M X; cw Delta to sV for the state update
+    // Delta = M X (contraction over s, 16 per wave)
     {
-      float dl[4][1];
-      zero(dl);
-      mm(dl, sM, MP, 1, sX, XP, 1, BT, ty, tx);
-      float *del = p.del + (gc * p.Hv + h) * BT * p.dv + j0;
+      float acc[4][4];
+      zero(acc);
+      mm_rk(acc, sM, 68, 4 * (lane >> 2), sX, 16, 4 * (lane & 3), 16 * w, 16 * w + 16);
+      float dl[4], cd[4];
+      ksplit_sum(red, acc, dl);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = ty + 16 * r;
-        del[t * p.dv + tx] = dl[r][0];
-        sV[t * XP + tx] = scw[t] * dl[r][0];
-      }
+      for (int q = 0; q < 4; ++q) cd[q] = F.cw[et] * dl[q];
+      stv<4>(p.del + ((gc * p.Hv + h) * BT + et) * p.dv + j0 + ei, dl);
+      stv<4>(sV + et * 16 + ei, cd);
     }
     __syncthreads();
-    // S = exp(gamma_C) S + (cw Delta)^T K; row i = ty, columns tx + 16 c
+    // S = exp(gamma_C) S + (cw Delta)^T K
     {
-      float sn[1][CN];
+      float acc[4][CJ];
 #pragma unroll
-      for (int cc = 0; cc < CN; ++cc) sn[0][cc] = seC * sS[ty * KP + tx + 16 * cc];
-      mm(sn, sV, 1, XP, sK, KP, 1, nr, ty, tx);
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int cc = 0; cc < CN; ++cc) sS[ty * KP + tx + 16 * cc] = sn[0][cc];
+        for (int q = 0; q < CJ; ++q) acc[r][q] = F.eC * sST[(CJ * jg + q) * 16 + 4 * ig + r];
+      mm_kk(acc, sV, 16, 4 * ig, sK, KP, CJ * jg, 0, nr);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < CJ; ++q) sST[(CJ * jg + q) * 16 + 4 * ig + r] = acc[r][q];
     }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// Reverse pass: dS carried from the last chunk to the first.
+// Reverse pass: dS carried from the last chunk to the first (kept transposed,
+// sDT[j][i]).
 // ---------------------------------------------------------------------------
 template <typename T, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
-  constexpr int KP = DK + 1, CN = DK / 16;
-  __shared__ float sK[BT * KP], sQ[BT * KP], sP[BT * MP], sM[BT * MP], sS[16 * KP];
-  __shared__ float sO[BT * XP], sD[BT * XP], sR[BT * XP];
-  __shared__ float seg[BT], scw[BT], sbeta[BT];
-  __shared__ float seC;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  constexpr int KP = DK + 4, CJ = DK / 64;
+  __shared__ alignas(16) float sK[BT * KP], sQ[BT * KP];  // unit rows [s][j]
+  __shared__ alignas(16) float sP[BT * BT], sM[BT * BT];  // as stored: [s][t]
+  __shared__ alignas(16) float sDT[DK * 16];              // dS^T [j][i]
+  __shared__ alignas(16) float sO[BT * 16], sR[BT * 16];  // dO, then scale exp(gamma) dO; exp(gamma) dv
+  __shared__ alignas(16) float red[4 * 1024];             // partials; red[0 .. 1024) then holds dDelta
+  __shared__ Fac F;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t j0 = (int64_t)blockIdx.x * 16, h = blockIdx.y, n = blockIdx.z;
   const int64_t hk = h / (p.Hv / p.Hqk);
   int64_t brow, bos, L, gc0;
   seq_pos(p, n, brow, bos, L, gc0);
   const int64_t nch = (L + BT - 1) / BT;
+  const int et = tid >> 2, ei = 4 * (tid & 3);
+  const int ig = tid & 3, jg = tid >> 2;
 
   for (int e = tid; e < 16 * DK; e += kThreads) {
     const int i = e / DK, j = e % DK;
-    sS[i * KP + j] = p.d_final ? p.d_final[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] : 0.f;
+    sDT[j * 16 + i] = p.d_final ? p.d_final[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] : 0.f;
   }
   __syncthreads();
   for (int64_t c = nch - 1; c >= 0; --c) {
     const int64_t gc = gc0 + c, t0 = bos + c * BT;
     const int nr = (int)(L - c * BT < BT ? L - c * BT : BT);
     float *ds = p.ds + ((gc * p.Hv + h) * p.dv + j0) * DK;
-    for (int e = tid; e < 16 * DK; e += kThreads) ds[e] = sS[(e / DK) * KP + e % DK];
-    const float *kn = p.kn + (gc * p.Hqk + hk) * BT * DK, *qn = p.qn + (gc * p.Hqk + hk) * BT * DK;
-    for (int e = tid; e < BT * DK; e += kThreads) {
-      sK[(e / DK) * KP + e % DK] = kn[e];
-      sQ[(e / DK) * KP + e % DK] = qn[e];
-    }
-    const float *mm_ = p.mm + (gc * p.Hv + h) * BT * BT, *pp = p.pp + (gc * p.Hv + h) * BT * BT;
-    for (int e = tid; e < BT * BT; e += kThreads) {
-      sM[(e >> 6) * MP + (e & 63)] = mm_[e];
-      sP[(e >> 6) * MP + (e & 63)] = pp[e];
-    }
-    if (tid < BT) {
-      const float *gm = p.gam + (gc * p.Hv + h) * BT;
-      const float gl = gm[nr - 1], gt = gm[tid];
-      seg[tid] = __expf(gt);
-      scw[tid] = tid < nr ? __expf(gl - gt) : 0.f;
-      sbeta[tid] = tid < nr ? p.beta[brow * p.sbt_b + (t0 + tid) * p.sbt_t + h * p.sbt_h] : 0.f;
-      if (tid == 0) seC = __expf(gl);
-    }
-    for (int e = tid; e < BT * 16; e += kThreads) {
-      const int t = e >> 4, i = e & 15;
-      sO[t * XP + i] =
-          t < nr ? f(static_cast<const T *>(p.d_o)[brow * p.sdo_b + (t0 + t) * p.sdo_t + h * p.sdo_h + j0 + i]) : 0.f;
+    for (int e = tid; e < 16 * DK; e += kThreads) ds[e] = sDT[(e % DK) * 16 + e / DK];
+    copy_rows<DK>(sK, KP, p.kn + (gc * p.Hqk + hk) * BT * DK);
+    copy_rows<DK>(sQ, KP, p.qn + (gc * p.Hqk + hk) * BT * DK);
+    copy_rows<BT>(sM, BT, p.mm + (gc * p.Hv + h) * BT * BT);
+    copy_rows<BT>(sP, BT, p.pp + (gc * p.Hv + h) * BT * BT);
+    load_fac(p, F, gc, h, brow, t0, nr);
+    {
+      float oo[4] = {0.f, 0.f, 0.f, 0.f};
+      if (et < nr)
+        load_vec<T, 4>(static_cast<const T *>(p.d_o) + brow * p.sdo_b + (t0 + et) * p.sdo_t + h * p.sdo_h + j0 + ei,
+                       (int)sizeof(T), oo);
+      stv<4>(sO + et * 16 + ei, oo);
     }
     __syncthreads();
-    // dDelta = Pt'^T dO + cw (K dS^T)   (scale is inside the stored Pt)
+    // dDelta = Pt'^T dO + cw (K dS^T): both contractions split over the waves
     {
-      float a1[4][1], a2[4][1];
+      float a1[4][4], a2[4][4];
       zero(a1);
       zero(a2);
-      mm(a1, sP, 1, MP, sO, XP, 1, nr, ty, tx);
-      mm(a2, sK, KP, 1, sS, 1, KP, DK, ty, tx);
+      const int r0 = 4 * (lane >> 2), c0 = 4 * (lane & 3);
+      mm_kk(a1, sP, BT, r0, sO, 16, c0, 16 * w, 16 * w + 16);
+      mm_rk(a2, sK, KP, r0, sDT, 16, c0, w * (DK / 4), (w + 1) * (DK / 4));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = ty + 16 * r;
-        sD[t * XP + tx] = a1[r][0] + scw[t] * a2[r][0];
-      }
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a1[r][q] = fmaf(F.cw[r0 + r], a2[r][q], a1[r][q]);
+      float dd[4];
+      ksplit_sum(red, a1, dd);
+      __syncthreads();  // every partial is read before red[0 ..) is overwritten
+      stv<4>(red + et * 16 + ei, dd);
     }
     __syncthreads();
-    // dR' = M^T dDelta; dv = beta dR'; exp(gamma) dv and scale exp(gamma) dO
-    // for the state update
+    // dR' = M^T dDelta; dv = beta dR'
     {
-      float a1[4][1];
+      float a1[4][4];
       zero(a1);
-      mm(a1, sM, 1, MP, sD, XP, 1, BT, ty, tx);
-      float *drp = p.drp + (gc * p.Hv + h) * BT * p.dv + j0;
+      mm_kk(a1, sM, BT, 4 * (lane >> 2), red, 16, 4 * (lane & 3), 16 * w, 16 * w + 16);
+      __syncthreads();  // dDelta in red[0 ..) is read by every wave before the partials land
+      float dr[4], dvv[4], er[4], oo[4];
+      ksplit_sum(red, a1, dr);
+      stv<4>(p.drp + ((gc * p.Hv + h) * BT + et) * p.dv + j0 + ei, dr);
+      ldv<4>(sO + et * 16 + ei, oo);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = ty + 16 * r;
-        drp[t * p.dv + tx] = a1[r][0];
-        const float dvv = sbeta[t] * a1[r][0];
-        if (t < nr)
-          store_grad<T>(p.dvv, p.grad_dtype, ((brow * p.T + t0 + t) * p.Hv + h) * p.dv + j0 + tx, dvv);
-        sR[t * XP + tx] = seg[t] * dvv;
-        sO[t * XP + tx] *= p.scale * seg[t];
+      for (int q = 0; q < 4; ++q) {
+        dvv[q] = F.beta[et] * dr[q];
+        er[q] = F.eg[et] * dvv[q];
+        oo[q] *= p.scale * F.eg[et];
       }
+      if (et < nr) {
+        const int64_t o = ((brow * p.T + t0 + et) * p.Hv + h) * p.dv + j0 + ei;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) store_grad<T>(p.dvv, p.grad_dtype, o + q, dvv[q]);
+      }
+      stv<4>(sR + et * 16 + ei, er);
+      stv<4>(sO + et * 16 + ei, oo);
     }
     __syncthreads();
     // dS0 = exp(gamma_C) dS + (scale exp(gamma) dO)^T Q - (exp(gamma) dv)^T K
     {
-      float a1[1][CN], a2[1][CN];
+      float a1[4][CJ], a2[4][CJ];
 #pragma unroll
-      for (int cc = 0; cc < CN; ++cc) {
-        a1[0][cc] = seC * sS[ty * KP + tx + 16 * cc];
-        a2[0][cc] = 0.f;
-      }
-      mm(a1, sO, 1, XP, sQ, KP, 1, nr, ty, tx);
-      mm(a2, sR, 1, XP, sK, KP, 1, nr, ty, tx);
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int cc = 0; cc < CN; ++cc) sS[ty * KP + tx + 16 * cc] = a1[0][cc] - a2[0][cc];
+        for (int q = 0; q < CJ; ++q) {
+          a1[r][q] = F.eC * sDT[(CJ * jg + q) * 16 + 4 * ig + r];
+          a2[r][q] = 0.f;
+        }
+      mm_kk(a1, sO, 16, 4 * ig, sQ, KP, CJ * jg, 0, nr);
+      mm_kk(a2, sR, 16, 4 * ig, sK, KP, CJ * jg, 0, nr);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < CJ; ++q) sDT[(CJ * jg + q) * 16 + 4 * ig + r] = a1[r][q] - a2[r][q];
     }
     __syncthreads();
   }
   if (p.d_init) {
     for (int e = tid; e < 16 * DK; e += kThreads) {
       const int i = e / DK, j = e % DK;
-      p.d_init[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] = sS[i * KP + j];
+      p.d_init[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] = sDT[j * 16 + i];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Gradients of q, k, g and beta per (chunk, q/k head).
+// Gradients of q, k, g and beta per (chunk, q/k head). The value-column
+// tiles are stored transposed ([i][t]) so that every product reads vectors.
+// Thread tid owns rows 4 (tid >> 4) .. + 3 and, of the 64 chunk columns,
+// 4 (tid & 15) .. + 3; of the dk columns, NJ (tid & 15) .. + NJ - 1.
 // ---------------------------------------------------------------------------
 template <int DK>
 struct GradTiles {
-  static constexpr int KP = DK + 1;
-  float o[BT * XP], d[BT * XP], rp[BT * XP], r[BT * XP];  // dO, Delta, dR', R
-  float s0[16 * KP], ds[16 * KP];                          // S0, dS_C rows
+  float o[16 * BT], d[16 * BT], rp[16 * BT], r[16 * BT];  // dO, Delta, dR', R as [i][t]
+  float s0[16 * DK], ds[16 * DK];                          // S0, dS_C rows [i][j]
 };
 
 template <typename T, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
-  constexpr int KP = DK + 1, CN = DK / 16;
-  __shared__ float sQ[BT * KP], sK[BT * KP];
-  __shared__ float sZ1[BT * MP], sZ2[BT * MP];  // dQK, dG
-  __shared__ union {
+  constexpr int KP = DK + 4, ZP = 68, NJ = DK / 16;
+  __shared__ alignas(16) float sQ[BT * KP], sK[BT * KP];
+  __shared__ alignas(16) float sZ1[BT * ZP], sZ2[BT * ZP];  // dQK, dG
+  __shared__ alignas(16) union {
     GradTiles<DK> t;
-    float z[BT * MP];  // a + p, for its column sums
+    float z[BT * ZP];  // a + p, for its column sums
   } u;
   __shared__ float sgam[BT], seg[BT], scw[BT], sbeta[BT];
   __shared__ float vrow[BT], vm[BT], vb[BT], red[kThreads];
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
+  const int r0 = 4 * rg, c0 = 4 * cg, j0c = NJ * cg;
   const int64_t gc = blockIdx.x, hk = blockIdx.y;
   const ChunkPos cp = chunk_pos(p, gc);
   if (!cp.valid) return;
   const int nr = cp.nr;
   const int64_t G = p.Hv / p.Hqk, dvn = p.dv;
 
-  {
-    const float *kn = p.kn + (gc * p.Hqk + hk) * BT * DK, *qn = p.qn + (gc * p.Hqk + hk) * BT * DK;
-    for (int e = tid; e < BT * DK; e += kThreads) {
-      sK[(e / DK) * KP + e % DK] = kn[e];
-      sQ[(e / DK) * KP + e % DK] = qn[e];
-    }
-  }
+  copy_rows<DK>(sK, KP, p.kn + (gc * p.Hqk + hk) * BT * DK);
+  copy_rows<DK>(sQ, KP, p.qn + (gc * p.Hqk + hk) * BT * DK);
   __syncthreads();
   float gg[4][4], qk[4][4];
   zero(gg);
   zero(qk);
-  mm(gg, sK, KP, 1, sK, 1, KP, DK, ty, tx);
-  mm(qk, sQ, KP, 1, sK, 1, KP, DK, ty, tx);
-  float dq[4][CN], dk[4][CN];
+  mm_rr(gg, sK, KP, r0, sK, KP, c0, 0, DK);
+  mm_rr(qk, sQ, KP, r0, sK, KP, c0, 0, DK);
+  float dq[4][NJ], dk[4][NJ];
   zero(dq);
   zero(dk);
 
@@ -502,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
       scw[tid] = tid < nr ? __expf(gl - gt) : 0.f;
       sbeta[tid] = tid < nr ? p.beta[cp.brow * p.sbt_b + (cp.t0 + tid) * p.sbt_t + h * p.sbt_h] : 0.f;
     }
-    float c1[4][4], c2[4][4], k1[4][CN], k2[4][CN], k3[4][CN];
+    float c1[4][4], c2[4][4], k1[4][NJ], k2[4][NJ], k3[4][NJ];
     zero(c1);
     zero(c2);
     zero(k1);
@@ -511,108 +648,112 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
     float db1 = 0.f, sdot = 0.f;
     const int64_t rowbase = (gc * p.Hv + h) * BT * dvn;
     const int64_t stbase = (gc * p.Hv + h) * dvn * DK;
-    for (int64_t j0 = 0; j0 < dvn; j0 += 16) {
+    for (int64_t jv = 0; jv < dvn; jv += 16) {
       __syncthreads();
-      for (int e = tid; e < BT * 16; e += kThreads) {
-        const int t = e >> 4, i = e & 15;
-        u.t.o[t * XP + i] = t < nr ? f(static_cast<const T *>(p.d_o)[cp.brow * p.sdo_b + (cp.t0 + t) * p.sdo_t +
-                                                                      h * p.sdo_h + j0 + i])
-                                   : 0.f;
-        const int64_t w = rowbase + t * dvn + j0 + i;
-        u.t.d[t * XP + i] = p.del[w];
-        u.t.rp[t * XP + i] = p.drp[w];
-        u.t.r[t * XP + i] = p.rr[w];
+      {  // row t = tid >> 2 of the tiles, value columns 4 (tid & 3) .. + 3
+        const int t = tid >> 2, i4 = 4 * (tid & 3);
+        float o4[4] = {0.f, 0.f, 0.f, 0.f}, d4[4], rp4[4], r4[4];
+        if (t < nr)
+          load_vec<T, 4>(static_cast<const T *>(p.d_o) + cp.brow * p.sdo_b + (cp.t0 + t) * p.sdo_t + h * p.sdo_h +
+                             jv + i4,
+                         (int)sizeof(T), o4);
+        const int64_t wo = rowbase + t * dvn + jv + i4;
+        ldv<4>(p.del + wo, d4);
+        ldv<4>(p.drp + wo, rp4);
+        ldv<4>(p.rr + wo, r4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          u.t.o[(i4 + q) * BT + t] = o4[q];
+          u.t.d[(i4 + q) * BT + t] = d4[q];
+          u.t.rp[(i4 + q) * BT + t] = rp4[q];
+          u.t.r[(i4 + q) * BT + t] = r4[q];
+        }
       }
-      for (int e = tid; e < 16 * DK; e += kThreads) {
-        const int i = e / DK, j = e % DK;
-        const int64_t w = stbase + (j0 + i) * DK + j;
-        const float a = p.s0[w], b = p.ds[w];
-        u.t.s0[i * KP + j] = a;
-        u.t.ds[i * KP + j] = b;
-        sdot = fmaf(a, b, sdot);
+      for (int e = 4 * tid; e < 16 * DK; e += 4 * kThreads) {
+        float a[4], b[4];
+        ldv<4>(p.s0 + stbase + jv * DK + e, a);
+        ldv<4>(p.ds + stbase + jv * DK + e, b);
+        stv<4>(u.t.s0 + e, a);
+        stv<4>(u.t.ds + e, b);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sdot = fmaf(a[q], b[q], sdot);
       }
       __syncthreads();
-      mm(c1, u.t.o, XP, 1, u.t.d, 1, XP, 16, ty, tx);
-      mm(c2, u.t.rp, XP, 1, u.t.d, 1, XP, 16, ty, tx);
-      mm(k1, u.t.o, XP, 1, u.t.s0, KP, 1, 16, ty, tx);
-      mm(k2, u.t.d, XP, 1, u.t.ds, KP, 1, 16, ty, tx);
-      mm(k3, u.t.rp, XP, 1, u.t.s0, KP, 1, 16, ty, tx);
+      mm_kk(c1, u.t.o, BT, r0, u.t.d, BT, c0, 0, 16);
+      mm_kk(c2, u.t.rp, BT, r0, u.t.d, BT, c0, 0, 16);
+      mm_kk(k1, u.t.o, BT, r0, u.t.s0, DK, j0c, 0, 16);
+      mm_kk(k2, u.t.d, BT, r0, u.t.ds, DK, j0c, 0, 16);
+      mm_kk(k3, u.t.rp, BT, r0, u.t.s0, DK, j0c, 0, 16);
       if (tid < BT)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) db1 = fmaf(u.t.rp[tid * XP + i], u.t.r[tid * XP + i], db1);
+        for (int i = 0; i < 16; ++i) db1 = fmaf(u.t.rp[i * BT + tid], u.t.r[i * BT + tid], db1);
     }
     __syncthreads();  // tiles dead: the union now holds a + p
-    // Elementwise C x C terms. Thread owns rows t = ty + 16 r, columns
-    // s = tx + 16 c.
     float rowz[4], roww[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = ty + 16 * r;
+      const int t = r0 + r;
       rowz[r] = 0.f;
       roww[r] = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int s = tx + 16 * c;
+        const int s = c0 + c;
         const float e = s <= t ? __expf(sgam[t] - sgam[s]) : 0.f;
-        const float dpt = p.scale * c1[r][c] * (s <= t ? 1.f : 0.f);  // dPt
-        const float dqk = dpt * e;
-        const float pz = dqk * qk[r][c];                               // dPt * Pt
-        const float da = s < t ? -c2[r][c] : 0.f;                      // dA
+        const float dqk = s <= t ? p.scale * c1[r][c] * e : 0.f;  // dPt o E
+        const float pz = dqk * qk[r][c];                           // dPt * Pt
+        const float da = s < t ? -c2[r][c] : 0.f;                  // dA
         const float eg = e * gg[r][c];
-        const float dg = da * sbeta[t] * e;                            // dG
-        const float az = da * sbeta[t] * eg;                           // dA * A
-        sZ1[t * MP + s] = dqk;
-        sZ2[t * MP + s] = dg;
-        u.z[t * MP + s] = az + pz;
+        const float az = da * sbeta[t] * eg;                       // dA * A
+        sZ1[t * ZP + s] = dqk;
+        sZ2[t * ZP + s] = da * sbeta[t] * e;                       // dG
+        u.z[t * ZP + s] = az + pz;
         rowz[r] += az + pz;
         roww[r] = fmaf(da, eg, roww[r]);
       }
     }
-    // row dots of the C x dk terms with the unit q, k rows
     float rdot[4], rm[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = ty + 16 * r;
+      const int t = r0 + r;
       float a = 0.f, b = 0.f, m = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < CN; ++cc) {
-        const int j = tx + 16 * cc;
-        a = fmaf(sQ[t * KP + j], k1[r][cc], a);
-        b = fmaf(sK[t * KP + j], k3[r][cc], b);
-        m = fmaf(sK[t * KP + j], k2[r][cc], m);
+      for (int q = 0; q < NJ; ++q) {
+        const int j = j0c + q;
+        a = fmaf(sQ[t * KP + j], k1[r][q], a);
+        b = fmaf(sK[t * KP + j], k3[r][q], b);
+        m = fmaf(sK[t * KP + j], k2[r][q], m);
       }
       const float rd = p.scale * seg[t] * a - seg[t] * sbeta[t] * b - scw[t] * m;
       rdot[r] = group_sum<16>(rd + rowz[r]);
       rm[r] = group_sum<16>(scw[t] * m);
       roww[r] = group_sum<16>(roww[r]);
     }
-    if (tx == 0)
+    if (cg == 0)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        vrow[ty + 16 * r] = rdot[r];
-        vm[ty + 16 * r] = rm[r];
-        vb[ty + 16 * r] = roww[r];
+        vrow[r0 + r] = rdot[r];
+        vm[r0 + r] = rm[r];
+        vb[r0 + r] = roww[r];
       }
     red[tid] = sdot;
-    // the q/k gradients of this value head
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = ty + 16 * r;
+      const int t = r0 + r;
 #pragma unroll
-      for (int cc = 0; cc < CN; ++cc) {
-        dq[r][cc] = fmaf(p.scale * seg[t], k1[r][cc], dq[r][cc]);
-        dk[r][cc] += scw[t] * k2[r][cc] - seg[t] * sbeta[t] * k3[r][cc];
+      for (int q = 0; q < NJ; ++q) {
+        dq[r][q] = fmaf(p.scale * seg[t], k1[r][q], dq[r][q]);
+        dk[r][q] += scw[t] * k2[r][q] - seg[t] * sbeta[t] * k3[r][q];
       }
     }
     __syncthreads();
-    mm(dq, sZ1, MP, 1, sK, KP, 1, BT, ty, tx);
-    mm(dk, sZ2, MP, 1, sK, KP, 1, BT, ty, tx);
-    mm(dk, sZ2, 1, MP, sK, KP, 1, BT, ty, tx);
-    mm(dk, sZ1, 1, MP, sQ, KP, 1, BT, ty, tx);
+    mm_rk(dq, sZ1, ZP, r0, sK, KP, j0c, 0, BT);
+    mm_rk(dk, sZ2, ZP, r0, sK, KP, j0c, 0, BT);
+    mm_kk(dk, sZ2, ZP, r0, sK, KP, j0c, 0, BT);
+    mm_kk(dk, sZ1, ZP, r0, sQ, KP, j0c, 0, BT);
     if (tid < BT) {  // wave 0: dgamma, its reverse running sum (dg), dbeta
       const int t = tid;
       float colz = 0.f;
-      for (int s = 0; s < BT; ++s) colz += u.z[s * MP + t];
+      for (int s = 0; s < BT; ++s) colz += u.z[s * ZP + t];
       float tot = 0.f;
       for (int i = 0; i < kThreads; ++i) tot += red[i];
       float sm = 0.f;
@@ -632,31 +773,30 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
       }
     }
   }
-  __syncthreads();
   // through the L2 fold: d(x / n) = (dx_hat - x_hat (x_hat . dx_hat)) / n
   {
     const float *rq = p.rq + (gc * p.Hqk + hk) * BT, *rk = p.rk + (gc * p.Hqk + hk) * BT;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = ty + 16 * r;
+      const int t = r0 + r;
       float a = 0.f, b = 0.f;
       if (p.use_l2) {
 #pragma unroll
-        for (int cc = 0; cc < CN; ++cc) {
-          const int j = tx + 16 * cc;
-          a = fmaf(sQ[t * KP + j], dq[r][cc], a);
-          b = fmaf(sK[t * KP + j], dk[r][cc], b);
+        for (int q = 0; q < NJ; ++q) {
+          const int j = j0c + q;
+          a = fmaf(sQ[t * KP + j], dq[r][q], a);
+          b = fmaf(sK[t * KP + j], dk[r][q], b);
         }
         a = group_sum<16>(a);
         b = group_sum<16>(b);
       }
       if (t < nr) {
-        const int64_t base = ((cp.brow * p.T + cp.t0 + t) * p.Hqk + hk) * DK;
+        const int64_t base = ((cp.brow * p.T + cp.t0 + t) * p.Hqk + hk) * DK + j0c;
 #pragma unroll
-        for (int cc = 0; cc < CN; ++cc) {
-          const int j = tx + 16 * cc;
-          store_grad<T>(p.dqq, p.grad_dtype, base + j, (dq[r][cc] - sQ[t * KP + j] * a) * rq[t]);
-          store_grad<T>(p.dkk, p.grad_dtype, base + j, (dk[r][cc] - sK[t * KP + j] * b) * rk[t]);
+        for (int q = 0; q < NJ; ++q) {
+          const int j = j0c + q;
+          store_grad<T>(p.dqq, p.grad_dtype, base + q, (dq[r][q] - sQ[t * KP + j] * a) * rq[t]);
+          store_grad<T>(p.dkk, p.grad_dtype, base + q, (dk[r][q] - sK[t * KP + j] * b) * rk[t]);
         }
       }
     }
