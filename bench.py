@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 METRIC = "GDN layer-core fwd tokens/s at 1 GPU; % of HBM BW / MFMA peak per stage"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 CHUNK = 64
 
 
@@ -176,12 +177,30 @@ WHOLE_LAYER_SHAPES = [  # (B, T, hidden, head_dim, act, B200 fwd ms)
 ]
 
 
-def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup) -> dict:
-    """The backward calls that exist so far (gated norm, prologue) at the
-    workload's shape, each against the HBM roof: per-call HIP events on the
-    current stream, mean over `steps` calls. Algorithmic bytes per token:
-    norm Hv dv (3 e + 2 e_g) (o, dout, d_o; gate, d_gate); prologue
-    3 C e + 4 Hv e + 8 Hv (x, d_qkv, dx; a, b, d_a, d_b; d_g, d_beta)."""
+def chunk_bwd_flops(s) -> float:
+    """Algorithmic FLOPs of the chunk-rule backward: per (chunk of C = 64
+    tokens, value head), 2 (8 C dk dv + 5 C^2 dv + 4 C^2 dk + 2 C^2 dk / G
+    + C^3 / 3): the state checkpoints (K S0^T, M X, the state update), the
+    reverse pass (P^T dO, K dS^T, M^T dDelta, two state-gradient products),
+    the per-chunk gradients (two C x C and three C x dk contractions over dv,
+    four C x dk contractions over the chunk, q.k and k.k per q/k head) and
+    the triangular inverse. Ragged chunks count as full ones."""
+    C, G = 64, s.Hv // s.Hqk
+    lens = s.lengths if s.lengths is not None else (s.T,) * s.B
+    chunks = sum((L + C - 1) // C for L in lens)
+    per = 2 * (8 * C * s.dk * s.dv + 5 * C * C * s.dv + 4 * C * C * s.dk + 2 * C * C * s.dk / G + C ** 3 / 3)
+    return chunks * s.Hv * per
+
+
+def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None) -> dict:
+    """The backward calls at the workload's shape: per-call HIP events on the
+    current stream, mean over `steps` calls. The gated norm and the prologue
+    are priced against the HBM roof (algorithmic bytes per token: norm
+    Hv dv (3 e + 2 e_g) (o, dout, d_o; gate, d_gate); prologue
+    3 C e + 4 Hv e + 8 Hv (x, d_qkv, dx; a, b, d_a, d_b; d_g, d_beta)); the
+    chunk-rule backward (FP32 vector arithmetic) against the FP32 vector
+    peak with chunk_bwd_flops. `rule` = (q, k, v, g, beta, scale) views of
+    the forward's prologue output."""
     e = {"f32": 4, "bf16": 2, "f16": 2}[s.act]
     eg = {"f32": 4, "bf16": 2, "f16": 2}[s.gate_dtype]
     ntok = s.tokens
@@ -202,10 +221,23 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup) -> dict:
         gdn.gdn_prologue_bwd(d["x_q"], d["x_k"], d["x_v"], d["conv_w"], None, d["a"], d["b"], d["A_log"],
                              d["dt_bias"], d["cu_seqlens"], dims, dqkv, dg, dbeta, workspace=pws)
 
+    legs = [("gated_norm_bwd", norm_b, s.Hv * s.dv * (3 * e + 2 * eg)),
+            ("prologue_bwd", pro_b, 3 * s.C * e + 4 * s.Hv * e + 8 * s.Hv)]
     out = {}
+    if rule is not None and s.dk in (64, 128):
+        q, k, v, g, beta, scale = rule
+        n_seqs = 0 if d["cu_seqlens"] is None else d["cu_seqlens"].shape[0] - 1
+        rws = torch.empty(gdn.gdn_chunk_rule_bwd_workspace_bytes(s.B, s.T, dims_t, n_seqs), dtype=torch.uint8,
+                          device="cuda")
+
+        def rule_b():
+            gdn.gdn_chunk_rule_bwd(q, k, v, g, beta, dout, scale, True, 1e-6, d["cu_seqlens"], workspace=rws)
+
+        legs.append(("chunk_rule_bwd", rule_b, None))
+    elif rule is not None:
+        out["chunk_rule_bwd"] = {"ms": None, "note": f"dk {s.dk} backward not built (dk 64 or 128)"}
     stream = torch.cuda.current_stream()
-    for name, fn, per_tok in (("gated_norm_bwd", norm_b, s.Hv * s.dv * (3 * e + 2 * eg)),
-                              ("prologue_bwd", pro_b, 3 * s.C * e + 4 * s.Hv * e + 8 * s.Hv)):
+    for name, fn, per_tok in legs:
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -216,9 +248,16 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup) -> dict:
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
+        if per_tok is None:
+            fl = chunk_bwd_flops(s)
+            out[name] = {"ms": ms, "flops": fl, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
+                         "alu_frac": fl / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, "arith": "f32"}
+            continue
         nbytes = per_tok * ntok
         out[name] = {"ms": ms, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
                      "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if all(out.get(n, {}).get("ms") for n in ("gated_norm_bwd", "chunk_rule_bwd", "prologue_bwd")):
+        out["layer_core_bwd_ms"] = sum(out[n]["ms"] for n in ("gated_norm_bwd", "chunk_rule_bwd", "prologue_bwd"))
     return out
 
 
@@ -456,7 +495,8 @@ def main() -> int:
     backward = None
     if not args.no_backward:
         print("[bench] backward leg", file=sys.stderr, flush=True)
-        backward = backward_leg(gdn, synth, torch, s, d, o, dims, args.steps, args.warmup)
+        backward = backward_leg(gdn, synth, torch, s, d, o, dims, args.steps, args.warmup,
+                                rule=(qv, kv, vv, g, beta, scale))
 
     whole = None
     if not args.no_whole_layer:

@@ -32,4 +32,6 @@ def test_bench_emits_one_json_line_with_roofline_and_cpu_baseline():
     cpu = out["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
     assert out["decode"]["seqs"] == 8 and out["decode"]["GB/s"] > 0
-    assert set(out["backward"]) == {"gated_norm_bwd", "prologue_bwd"}
+    assert set(out["backward"]) == {"gated_norm_bwd", "prologue_bwd", "chunk_rule_bwd", "layer_core_bwd_ms"}
+    rb = out["backward"]["chunk_rule_bwd"]
+    assert rb["ms"] > 0 and 0 < rb["alu_frac"] <= 1

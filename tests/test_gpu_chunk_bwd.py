@@ -111,3 +111,47 @@ def test_chunk_rule_bwd_strided_views_equal_contiguous():
     for n, x, y in zip(NAMES, a, b):
         if x is not None:
             assert torch.equal(x, y), n
+
+
+def test_chunk_rule_bwd_full_size_sampled_window():
+    """The 131072-token workload's shape (16 q/k heads, 32 value heads, dk = dv
+    = 128, BF16) in one call, with d_o zero except on the last 150 tokens.
+    The oracle follows one q/k head and its two value heads: the state after
+    the first T - 250 tokens from the pinned C recurrence, then autograd over
+    the last 250 tokens from that state. The 100 tokens before the nonzero
+    window get their gradients only through the state carried back over
+    chunk boundaries. Inputs are seeded draws (q, k, v ~ N(0, 1); g ~ -U(0.01,
+    0.5); beta ~ U(0.05, 1))."""
+    s = synth.spec(3)
+    B, T, Hqk, dk, Hv, dv = s.B, s.T, s.Hqk, s.dk, s.Hv, s.dv
+    q = synth.randn((B, T, Hqk, dk), "bf16", 500)
+    k = synth.randn((B, T, Hqk, dk), "bf16", 501)
+    v = synth.randn((B, T, Hv, dv), "bf16", 502)
+    g = O.round_to(-synth.uniform((B, T, Hv), 0.01, 0.5, 503), "f32")
+    beta = O.round_to(synth.uniform((B, T, Hv), 0.05, 1.0, 504), "f32")
+    W, W1 = 150, 100
+    t1 = T - W - W1
+    do = torch.zeros((B, T, Hv, dv), dtype=torch.bfloat16)
+    do[:, T - W:] = synth.randn((B, W, Hv, dv), "bf16", 505)
+    scale = dk ** -0.5
+    got = gdn.gdn_chunk_rule_bwd(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(g).float().cuda(),
+                                 torch.from_numpy(beta).float().cuda(), do.cuda(), scale)
+    torch.cuda.synchronize()
+    hq = 5
+    vh = [2 * hq, 2 * hq + 1]
+    qs, ks = f64(q[:, :, hq:hq + 1]), f64(k[:, :, hq:hq + 1])
+    vs, gs, bs = f64(v[:, :, vh]), g[:, :, vh], beta[:, :, vh]
+    _, S1 = O.gated_delta_rule(qs[:, :t1], ks[:, :t1], vs[:, :t1], gs[:, :t1], bs[:, :t1], scale=scale,
+                               output_final_state=True)
+    ref = OB.chunk_rule_bwd(qs[:, t1:], ks[:, t1:], vs[:, t1:], gs[:, t1:], bs[:, t1:], f64(do[:, t1:, vh]), scale,
+                            True, 1e-6, None, S1)
+    dq, dkk, dvv, dg, db, _ = got
+    tau = TAU["bf16"]
+    H.assert_close(f64(dq[:, t1:, hq:hq + 1]), ref[0], tau, "dq")
+    H.assert_close(f64(dkk[:, t1:, hq:hq + 1]), ref[1], tau, "dk")
+    H.assert_close(f64(dvv[:, t1:, vh]), ref[2], tau, "dv")
+    H.assert_close(f64(dg[:, t1:, vh]), ref[3], tau, "dg")
+    H.assert_close(f64(db[:, t1:, vh]), ref[4], tau, "dbeta")
+    # the carried part alone: tokens before the nonzero window
+    H.assert_close(f64(dvv[:, t1:T - W, vh]), ref[2][:, :W1], tau, "dv before the window")
+    assert float(np.abs(ref[2][:, :W1]).max()) > 0
