@@ -148,7 +148,23 @@ __device__ __forceinline__ void stv(float *p, const float (&o)[N]) {
 template <int RM, int CN>
 __device__ __forceinline__ void mm_kk(float (&acc)[RM][CN], const float *A, int lda, int r0, const float *B, int ldb,
                                       int c0, int k0, int k1) {
-  for (int k = k0; k < k1; ++k) {
+  // four contraction steps per block, all their reads issued before the FMAs
+  int k = k0;
+  for (; k + 4 <= k1; k += 4) {
+    float a[4][RM], b[4][CN];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      ldv<RM>(A + (k + kk) * lda + r0, a[kk]);
+      ldv<CN>(B + (k + kk) * ldb + c0, b[kk]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int r = 0; r < RM; ++r)
+#pragma unroll
+        for (int c = 0; c < CN; ++c) acc[r][c] = fmaf(a[kk][r], b[kk][c], acc[r][c]);
+  }
+  for (; k < k1; ++k) {
     float a[RM], b[CN];
     ldv<RM>(A + k * lda + r0, a);
     ldv<CN>(B + k * ldb + c0, b);
@@ -163,18 +179,17 @@ template <int RM, int CN>
 __device__ __forceinline__ void mm_rk(float (&acc)[RM][CN], const float *A, int lda, int r0, const float *B, int ldb,
                                       int c0, int k0, int k1) {
   for (int k = k0; k < k1; k += 4) {
-    float a[RM][4];
+    float a[RM][4], b[4][CN];
 #pragma unroll
     for (int r = 0; r < RM; ++r) ldv<4>(A + (r0 + r) * lda + k, a[r]);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      float b[CN];
-      ldv<CN>(B + (k + kk) * ldb + c0, b);
+    for (int kk = 0; kk < 4; ++kk) ldv<CN>(B + (k + kk) * ldb + c0, b[kk]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int r = 0; r < RM; ++r)
 #pragma unroll
-        for (int c = 0; c < CN; ++c) acc[r][c] = fmaf(a[r][kk], b[c], acc[r][c]);
-    }
+        for (int c = 0; c < CN; ++c) acc[r][c] = fmaf(a[r][kk], b[kk][c], acc[r][c]);
   }
 }
 
@@ -222,19 +237,6 @@ __device__ __forceinline__ void ksplit_sum(float *red, const float (&acc)[4][4],
 struct Fac {
   float eg[BT], cw[BT], beta[BT], eC;
 };
-
-__device__ __forceinline__ void load_fac(const ChunkBwdArgs &p, Fac &F, int64_t gc, int64_t h, int64_t brow, int64_t t0,
-                                         int nr) {
-  if (threadIdx.x < BT) {
-    const int t = threadIdx.x;
-    const float *gm = p.gam + (gc * p.Hv + h) * BT;
-    const float gl = gm[nr - 1], gt = gm[t];
-    F.eg[t] = __expf(gt);
-    F.cw[t] = t < nr ? __expf(gl - gt) : 0.f;
-    F.beta[t] = t < nr ? p.beta[brow * p.sbt_b + (t0 + t) * p.sbt_t + h * p.sbt_h] : 0.f;
-    if (t == 0) F.eC = __expf(gl);
-  }
-}
 
 // Rows [0, 64) x cols [0, D) of a contiguous FP32 [64][D] array into LDS rows
 // of stride ld (float4 copies).
@@ -406,22 +408,56 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(ChunkBwdArgs p) {
     const int i = e / DK, j = e % DK;
     sST[j * 16 + i] = p.init_state ? p.init_state[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] : 0.f;
   }
+  // The next chunk's operands are staged in registers while this one is
+  // computed: unit k rows, M, the v slice and the factors.
+  constexpr int NK = DK / 16;
+  fv4 rk[NK], rm[4];
+  float rv[4], rg = 0.f, rgl = 0.f, rb = 0.f;
+  auto fetch = [&](int64_t c) {
+    const int64_t gc = gc0 + c, t0 = bos + c * BT;
+    const int nr = (int)(L - c * BT < BT ? L - c * BT : BT);
+    const float *kn = p.kn + (gc * p.Hqk + hk) * BT * DK, *mm_ = p.mm + (gc * p.Hv + h) * BT * BT;
+#pragma unroll
+    for (int m = 0; m < NK; ++m) rk[m] = *reinterpret_cast<const fv4 *>(kn + 4 * (tid + kThreads * m));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) rm[m] = *reinterpret_cast<const fv4 *>(mm_ + 4 * (tid + kThreads * m));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rv[q] = 0.f;
+    if (et < nr) load_vec<T, 4>(static_cast<const T *>(p.v) + brow * p.sv_b + (t0 + et) * p.sv_t + h * p.sv_h + j0 + ei,
+                                (int)sizeof(T), rv);
+    if (tid < BT) {
+      const float *gm = p.gam + (gc * p.Hv + h) * BT;
+      rg = gm[tid];
+      rgl = gm[nr - 1];
+      rb = tid < nr ? p.beta[brow * p.sbt_b + (t0 + tid) * p.sbt_t + h * p.sbt_h] : 0.f;
+    }
+  };
+  if (nch > 0) fetch(0);
   __syncthreads();
   for (int64_t c = 0; c < nch; ++c) {
-    const int64_t gc = gc0 + c, t0 = bos + c * BT;
+    const int64_t gc = gc0 + c;
     const int nr = (int)(L - c * BT < BT ? L - c * BT : BT);
     float *s0 = p.s0 + ((gc * p.Hv + h) * p.dv + j0) * DK;
     for (int e = tid; e < 16 * DK; e += kThreads) s0[e] = sST[(e % DK) * 16 + e / DK];
-    copy_rows<DK>(sK, KP, p.kn + (gc * p.Hqk + hk) * BT * DK);
-    copy_rows<BT>(sM, 68, p.mm + (gc * p.Hv + h) * BT * BT);
-    load_fac(p, F, gc, h, brow, t0, nr);
-    {
-      float vv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (et < nr) load_vec<T, 4>(static_cast<const T *>(p.v) + brow * p.sv_b + (t0 + et) * p.sv_t + h * p.sv_h + j0 + ei,
-                                  (int)sizeof(T), vv);
-      stv<4>(sV + et * 16 + ei, vv);
+#pragma unroll
+    for (int m = 0; m < NK; ++m) {
+      const int e = 4 * (tid + kThreads * m);
+      *reinterpret_cast<fv4 *>(sK + (e / DK) * KP + e % DK) = rk[m];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = 4 * (tid + kThreads * m);
+      *reinterpret_cast<fv4 *>(sM + (e >> 6) * 68 + (e & 63)) = rm[m];
+    }
+    stv<4>(sV + et * 16 + ei, rv);
+    if (tid < BT) {
+      F.eg[tid] = __expf(rg);
+      F.cw[tid] = tid < nr ? __expf(rgl - rg) : 0.f;
+      F.beta[tid] = rb;
+      if (tid == 0) F.eC = __expf(rgl);
     }
     __syncthreads();
+    if (c + 1 < nch) fetch(c + 1);
     // KS = K S0^T (contraction over dk, a quarter per wave); R = V - exp(gamma) KS
     {
       float acc[4][4];
@@ -460,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(ChunkBwdArgs p) {
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int q = 0; q < CJ; ++q) acc[r][q] = F.eC * sST[(CJ * jg + q) * 16 + 4 * ig + r];
-      mm_kk(acc, sV, 16, 4 * ig, sK, KP, CJ * jg, 0, nr);
+      mm_kk(acc, sV, 16, 4 * ig, sK, KP, CJ * jg, 0, BT);  // rows past nr are zero
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -480,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
   __shared__ alignas(16) float sK[BT * KP], sQ[BT * KP];  // unit rows [s][j]
   __shared__ alignas(16) float sP[BT * BT], sM[BT * BT];  // as stored: [s][t]
   __shared__ alignas(16) float sDT[DK * 16];              // dS^T [j][i]
-  __shared__ alignas(16) float sO[BT * 16], sR[BT * 16];  // dO, then scale exp(gamma) dO; exp(gamma) dv
+  __shared__ alignas(16) float sO[BT * 16], sR[BT * 16];  // dO, then scale exp(gamma) dO; -exp(gamma) dv
   __shared__ alignas(16) float red[4 * 1024];             // partials; red[0 .. 1024) then holds dDelta
   __shared__ Fac F;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -496,37 +532,77 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
     const int i = e / DK, j = e % DK;
     sDT[j * 16 + i] = p.d_final ? p.d_final[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] : 0.f;
   }
+  // The next chunk's operands are staged in registers while this one is
+  // computed: unit k and q rows, M, scale * Pt, the dO slice and the factors.
+  constexpr int NK = DK / 16;
+  fv4 rk[NK], rq[NK], rm[4], rp[4];
+  float ro[4], rg = 0.f, rgl = 0.f, rb = 0.f;
+  auto fetch = [&](int64_t c) {
+    const int64_t gc = gc0 + c, t0 = bos + c * BT;
+    const int nr = (int)(L - c * BT < BT ? L - c * BT : BT);
+    const float *kn = p.kn + (gc * p.Hqk + hk) * BT * DK, *qn = p.qn + (gc * p.Hqk + hk) * BT * DK;
+    const float *mm_ = p.mm + (gc * p.Hv + h) * BT * BT, *pp = p.pp + (gc * p.Hv + h) * BT * BT;
+#pragma unroll
+    for (int m = 0; m < NK; ++m) {
+      rk[m] = *reinterpret_cast<const fv4 *>(kn + 4 * (tid + kThreads * m));
+      rq[m] = *reinterpret_cast<const fv4 *>(qn + 4 * (tid + kThreads * m));
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      rm[m] = *reinterpret_cast<const fv4 *>(mm_ + 4 * (tid + kThreads * m));
+      rp[m] = *reinterpret_cast<const fv4 *>(pp + 4 * (tid + kThreads * m));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ro[q] = 0.f;
+    if (et < nr)
+      load_vec<T, 4>(static_cast<const T *>(p.d_o) + brow * p.sdo_b + (t0 + et) * p.sdo_t + h * p.sdo_h + j0 + ei,
+                     (int)sizeof(T), ro);
+    if (tid < BT) {
+      const float *gm = p.gam + (gc * p.Hv + h) * BT;
+      rg = gm[tid];
+      rgl = gm[nr - 1];
+      rb = tid < nr ? p.beta[brow * p.sbt_b + (t0 + tid) * p.sbt_t + h * p.sbt_h] : 0.f;
+    }
+  };
+  if (nch > 0) fetch(nch - 1);
   __syncthreads();
   for (int64_t c = nch - 1; c >= 0; --c) {
     const int64_t gc = gc0 + c, t0 = bos + c * BT;
     const int nr = (int)(L - c * BT < BT ? L - c * BT : BT);
     float *ds = p.ds + ((gc * p.Hv + h) * p.dv + j0) * DK;
     for (int e = tid; e < 16 * DK; e += kThreads) ds[e] = sDT[(e % DK) * 16 + e / DK];
-    copy_rows<DK>(sK, KP, p.kn + (gc * p.Hqk + hk) * BT * DK);
-    copy_rows<DK>(sQ, KP, p.qn + (gc * p.Hqk + hk) * BT * DK);
-    copy_rows<BT>(sM, BT, p.mm + (gc * p.Hv + h) * BT * BT);
-    copy_rows<BT>(sP, BT, p.pp + (gc * p.Hv + h) * BT * BT);
-    load_fac(p, F, gc, h, brow, t0, nr);
-    {
-      float oo[4] = {0.f, 0.f, 0.f, 0.f};
-      if (et < nr)
-        load_vec<T, 4>(static_cast<const T *>(p.d_o) + brow * p.sdo_b + (t0 + et) * p.sdo_t + h * p.sdo_h + j0 + ei,
-                       (int)sizeof(T), oo);
-      stv<4>(sO + et * 16 + ei, oo);
+#pragma unroll
+    for (int m = 0; m < NK; ++m) {
+      const int e = 4 * (tid + kThreads * m);
+      *reinterpret_cast<fv4 *>(sK + (e / DK) * KP + e % DK) = rk[m];
+      *reinterpret_cast<fv4 *>(sQ + (e / DK) * KP + e % DK) = rq[m];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = 4 * (tid + kThreads * m);
+      *reinterpret_cast<fv4 *>(sM + e) = rm[m];
+      *reinterpret_cast<fv4 *>(sP + e) = rp[m];
+    }
+    stv<4>(sO + et * 16 + ei, ro);
+    if (tid < BT) {
+      F.eg[tid] = __expf(rg);
+      F.cw[tid] = tid < nr ? __expf(rgl - rg) : 0.f;
+      F.beta[tid] = rb;
+      if (tid == 0) F.eC = __expf(rgl);
     }
     __syncthreads();
-    // dDelta = Pt'^T dO + cw (K dS^T): both contractions split over the waves
+    if (c > 0) fetch(c - 1);
+    // dDelta = cw (K dS^T) + Pt'^T dO: both contractions split over the waves
     {
-      float a1[4][4], a2[4][4];
+      float a1[4][4];
       zero(a1);
-      zero(a2);
       const int r0 = 4 * (lane >> 2), c0 = 4 * (lane & 3);
-      mm_kk(a1, sP, BT, r0, sO, 16, c0, 16 * w, 16 * w + 16);
-      mm_rk(a2, sK, KP, r0, sDT, 16, c0, w * (DK / 4), (w + 1) * (DK / 4));
+      mm_rk(a1, sK, KP, r0, sDT, 16, c0, w * (DK / 4), (w + 1) * (DK / 4));
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a1[r][q] = fmaf(F.cw[r0 + r], a2[r][q], a1[r][q]);
+        for (int q = 0; q < 4; ++q) a1[r][q] *= F.cw[r0 + r];
+      mm_kk(a1, sP, BT, r0, sO, 16, c0, 16 * w, 16 * w + 16);
       float dd[4];
       ksplit_sum(red, a1, dd);
       __syncthreads();  // every partial is read before red[0 ..) is overwritten
@@ -546,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         dvv[q] = F.beta[et] * dr[q];
-        er[q] = F.eg[et] * dvv[q];
+        er[q] = -F.eg[et] * dvv[q];
         oo[q] *= p.scale * F.eg[et];
       }
       if (et < nr) {
@@ -560,20 +636,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
     __syncthreads();
     // dS0 = exp(gamma_C) dS + (scale exp(gamma) dO)^T Q - (exp(gamma) dv)^T K
     {
-      float a1[4][CJ], a2[4][CJ];
+      float a1[4][CJ];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int q = 0; q < CJ; ++q) {
-          a1[r][q] = F.eC * sDT[(CJ * jg + q) * 16 + 4 * ig + r];
-          a2[r][q] = 0.f;
-        }
-      mm_kk(a1, sO, 16, 4 * ig, sQ, KP, CJ * jg, 0, nr);
-      mm_kk(a2, sR, 16, 4 * ig, sK, KP, CJ * jg, 0, nr);
+        for (int q = 0; q < CJ; ++q) a1[r][q] = F.eC * sDT[(CJ * jg + q) * 16 + 4 * ig + r];
+      mm_kk(a1, sO, 16, 4 * ig, sQ, KP, CJ * jg, 0, BT);  // rows past nr are zero
+      mm_kk(a1, sR, 16, 4 * ig, sK, KP, CJ * jg, 0, BT);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int q = 0; q < CJ; ++q) sDT[(CJ * jg + q) * 16 + 4 * ig + r] = a1[r][q] - a2[r][q];
+        for (int q = 0; q < CJ; ++q) sDT[(CJ * jg + q) * 16 + 4 * ig + r] = a1[r][q];
     }
     __syncthreads();
   }
