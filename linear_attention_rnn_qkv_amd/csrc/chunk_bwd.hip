@@ -238,6 +238,19 @@ struct Fac {
   float eg[BT], cw[BT], beta[BT], eC;
 };
 
+// (value-row slice start, value head, sequence) of a serial-kernel workgroup.
+// Consecutive workgroup ids go to different XCDs; the ids are permuted so that
+// the slices of a head, and the value heads of a GQA group, share one XCD
+// and its L2, which then serves their common chunk operands (k, q, M, P).
+__device__ __forceinline__ void serial_ids(const ChunkBwdArgs &p, int64_t &j0, int64_t &h, int64_t &n) {
+  const int64_t ns = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  int64_t lid = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
+  j0 = (lid % ns) * 16;
+  h = (lid / ns) % p.Hv;
+  n = lid / (ns * p.Hv);
+}
+
 // Rows [0, 64) x cols [0, D) of a contiguous FP32 [64][D] array into LDS rows
 // of stride ld (float4 copies).
 template <int D>
@@ -396,7 +409,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(ChunkBwdArgs p) {
   __shared__ alignas(16) float red[4 * 1024];
   __shared__ Fac F;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t j0 = (int64_t)blockIdx.x * 16, h = blockIdx.y, n = blockIdx.z;
+  int64_t j0, h, n;
+  serial_ids(p, j0, h, n);
   const int64_t hk = h / (p.Hv / p.Hqk);
   int64_t brow, bos, L, gc0;
   seq_pos(p, n, brow, bos, L, gc0);
@@ -520,7 +534,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
   __shared__ alignas(16) float red[4 * 1024];             // partials; red[0 .. 1024) then holds dDelta
   __shared__ Fac F;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t j0 = (int64_t)blockIdx.x * 16, h = blockIdx.y, n = blockIdx.z;
+  int64_t j0, h, n;
+  serial_ids(p, j0, h, n);
   const int64_t hk = h / (p.Hv / p.Hqk);
   int64_t brow, bos, L, gc0;
   seq_pos(p, n, brow, bos, L, gc0);

@@ -44,6 +44,10 @@ KERNELS = {
     "beta_g_bwd_kernel": ("beta_g_bwd_kernel", ["backward.hip", "device_common.h", "gdn_internal.h"]),
     "sum_partials_a": ("sum_partials_a", ["backward.hip", "device_common.h", "gdn_internal.h"]),
     "sum_partials_b": ("sum_partials_b", ["backward.hip", "device_common.h", "gdn_internal.h"]),
+    "bwd_prep_kernel": ("bwd_prep_kernel", ["chunk_bwd.hip", "device_common.h", "gdn_internal.h"]),
+    "bwd_states_kernel": ("bwd_states_kernel", ["chunk_bwd.hip", "device_common.h", "gdn_internal.h"]),
+    "bwd_dstate_kernel": ("bwd_dstate_kernel", ["chunk_bwd.hip", "device_common.h", "gdn_internal.h"]),
+    "bwd_grad_kernel": ("bwd_grad_kernel", ["chunk_bwd.hip", "device_common.h", "gdn_internal.h"]),
 }
 
 
