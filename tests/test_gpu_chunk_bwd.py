@@ -1,7 +1,7 @@
 """GPU parity of gdn_chunk_rule_bwd (through the C ABI) against the FP64
 oracle (float64 autograd of the token-by-token gated delta rule) on the same
 seeded inputs. Tolerance per output tensor: max|gpu - oracle| <= tau *
-max|oracle|, tau = 1e-4 (FP32 workloads), 2e-2 (BF16/FP16). Gradients are
+max|oracle|, tau = 1e-4 (FP32 workloads), 5e-3 (BF16/FP16). Gradients are
 also checked to be identical across two calls (no atomics)."""
 import numpy as np
 import pytest
@@ -14,7 +14,10 @@ from . import _gdn_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-TAU = H.TAU
+# Gradient bar for 16-bit workloads: 5e-3 of the largest reference gradient,
+# the bar the fused-conv pull request's test plan holds parameter gradients
+# to; FP32 workloads keep 1e-4.
+TAU = {"f32": 1e-4, "bf16": 5e-3, "f16": 5e-3}
 f64 = H.f64
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")
 
