@@ -54,6 +54,7 @@ CASES = [
     ("fp16-packed-with-empty", 4, {"lengths": (1, 63, 0, 64, 65, 2, 0, 130), "Hqk": 1, "Hv": 2}, True, True),
     ("bf16-dk64-dv256-T200", 0, {"act": "bf16", "T": 200, "Hqk": 1, "Hv": 1, "dv": 256}, True, True),
     ("fp32-no-l2-T90", 0, {"T": 90, "Hqk": 1, "Hv": 2, "dv": 64}, False, False),
+    ("bf16-group4-T129", 2, {"T": 129, "Hqk": 2, "Hv": 8, "dv": 64}, True, True),
 ]
 
 
