@@ -224,7 +224,7 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None) -> 
     legs = [("gated_norm_bwd", norm_b, s.Hv * s.dv * (3 * e + 2 * eg)),
             ("prologue_bwd", pro_b, 3 * s.C * e + 4 * s.Hv * e + 8 * s.Hv)]
     out = {}
-    if rule is not None and s.dk in (64, 128):
+    if rule is not None and s.dk in (64, 128, 256):
         q, k, v, g, beta, scale = rule
         n_seqs = 0 if d["cu_seqlens"] is None else d["cu_seqlens"].shape[0] - 1
         rws = torch.empty(gdn.gdn_chunk_rule_bwd_workspace_bytes(s.B, s.T, dims_t, n_seqs), dtype=torch.uint8,
@@ -234,8 +234,6 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None) -> 
             gdn.gdn_chunk_rule_bwd(q, k, v, g, beta, dout, scale, True, 1e-6, d["cu_seqlens"], workspace=rws)
 
         legs.append(("chunk_rule_bwd", rule_b, None))
-    elif rule is not None:
-        out["chunk_rule_bwd"] = {"ms": None, "note": f"dk {s.dk} backward not built (dk 64 or 128)"}
     stream = torch.cuda.current_stream()
     for name, fn, per_tok in legs:
         for _ in range(warmup):

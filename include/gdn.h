@@ -388,8 +388,8 @@ gdn_status gdn_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
  *                   bytes, 256-byte aligned, required; it must not overlap
  *                   any tensor argument or be used by another call until
  *                   this call's work on `stream` is done
- * Outputs must not overlap inputs or each other. Supported: dk 64 or 128,
- * dv a multiple of 16 (GDN_ERR_NOT_SUPPORTED otherwise).
+ * Outputs must not overlap inputs or each other. Supported: dk 64, 128 or
+ * 256, dv a multiple of 16 (GDN_ERR_NOT_SUPPORTED otherwise).
  */
 gdn_status gdn_chunk_rule_bwd(const gdn_tensor *q, const gdn_tensor *k,
                               const gdn_tensor *v, const gdn_tensor *g,

@@ -150,6 +150,7 @@ __device__ __forceinline__ void mm_kk(float (&acc)[RM][CN], const float *A, int 
                                       int c0, int k0, int k1) {
   // four contraction steps per block, all their reads issued before the FMAs
   int k = k0;
+#pragma unroll 2
   for (; k + 4 <= k1; k += 4) {
     float a[4][RM], b[4][CN];
 #pragma unroll
@@ -178,6 +179,7 @@ __device__ __forceinline__ void mm_kk(float (&acc)[RM][CN], const float *A, int 
 template <int RM, int CN>
 __device__ __forceinline__ void mm_rk(float (&acc)[RM][CN], const float *A, int lda, int r0, const float *B, int ldb,
                                       int c0, int k0, int k1) {
+#pragma unroll 2
   for (int k = k0; k < k1; k += 4) {
     float a[RM][4], b[4][CN];
 #pragma unroll
@@ -196,6 +198,7 @@ __device__ __forceinline__ void mm_rk(float (&acc)[RM][CN], const float *A, int 
 template <int RM, int CN>
 __device__ __forceinline__ void mm_rr(float (&acc)[RM][CN], const float *A, int lda, int r0, const float *B, int ldb,
                                       int c0, int k0, int k1) {
+#pragma unroll 2
   for (int k = k0; k < k1; k += 4) {
     float a[RM][4], b[CN][4];
 #pragma unroll
@@ -269,8 +272,17 @@ __device__ __forceinline__ void copy_rows(float *dst, int ld, const float *src) 
 template <typename T, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
   constexpr int KP = DK + 4;
-  __shared__ alignas(16) float sQ[BT * KP], sK[BT * KP];
-  __shared__ alignas(16) float sA[BT * MP], sM[BT * MP];
+  // the q/k tiles are dead once K K^T and Q K^T are in registers; A and M
+  // then reuse their LDS
+  __shared__ alignas(16) union {
+    struct {
+      float q[BT * KP], k[BT * KP];
+    } x;
+    struct {
+      float a[BT * MP], m[BT * MP];
+    } y;
+  } lds;
+  float *sQ = lds.x.q, *sK = lds.x.k, *sA = lds.y.a, *sM = lds.y.m;
   __shared__ float sgam[BT], sbeta[BT];
   const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
   const int64_t gc = blockIdx.x, hk = blockIdx.y;
@@ -527,7 +539,10 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(ChunkBwdArgs p) {
 template <typename T, int DK>
 __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
   constexpr int KP = DK + 4, CJ = DK / 64;
-  __shared__ alignas(16) float sK[BT * KP], sQ[BT * KP];  // unit rows [s][j]
+  // dk 256: the unit q rows are read from the workspace (L2) in the state
+  // update instead of being staged in LDS, which would not hold them
+  constexpr bool QG = DK > 128;
+  __shared__ alignas(16) float sK[BT * KP], sQs[QG ? 4 : BT * KP];  // unit rows [s][j]
   __shared__ alignas(16) float sP[BT * BT], sM[BT * BT];  // as stored: [s][t]
   __shared__ alignas(16) float sDT[DK * 16];              // dS^T [j][i]
   __shared__ alignas(16) float sO[BT * 16], sR[BT * 16];  // dO, then scale exp(gamma) dO; -exp(gamma) dv
@@ -549,8 +564,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
   }
   // The next chunk's operands are staged in registers while this one is
   // computed: unit k and q rows, M, scale * Pt, the dO slice and the factors.
-  constexpr int NK = DK / 16;
-  fv4 rk[NK], rq[NK], rm[4], rp[4];
+  constexpr int NK = DK / 16, NQ = QG ? 1 : NK;
+  fv4 rk[NK], rq[NQ], rm[4], rp[4];
   float ro[4], rg = 0.f, rgl = 0.f, rb = 0.f;
   auto fetch = [&](int64_t c) {
     const int64_t gc = gc0 + c, t0 = bos + c * BT;
@@ -558,9 +573,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
     const float *kn = p.kn + (gc * p.Hqk + hk) * BT * DK, *qn = p.qn + (gc * p.Hqk + hk) * BT * DK;
     const float *mm_ = p.mm + (gc * p.Hv + h) * BT * BT, *pp = p.pp + (gc * p.Hv + h) * BT * BT;
 #pragma unroll
-    for (int m = 0; m < NK; ++m) {
-      rk[m] = *reinterpret_cast<const fv4 *>(kn + 4 * (tid + kThreads * m));
-      rq[m] = *reinterpret_cast<const fv4 *>(qn + 4 * (tid + kThreads * m));
+    for (int m = 0; m < NK; ++m) rk[m] = *reinterpret_cast<const fv4 *>(kn + 4 * (tid + kThreads * m));
+    if constexpr (!QG) {
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) rq[m] = *reinterpret_cast<const fv4 *>(qn + 4 * (tid + kThreads * m));
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -590,7 +606,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
     for (int m = 0; m < NK; ++m) {
       const int e = 4 * (tid + kThreads * m);
       *reinterpret_cast<fv4 *>(sK + (e / DK) * KP + e % DK) = rk[m];
-      *reinterpret_cast<fv4 *>(sQ + (e / DK) * KP + e % DK) = rq[m];
+    }
+    if constexpr (!QG) {
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) {
+        const int e = 4 * (tid + kThreads * m);
+        *reinterpret_cast<fv4 *>(sQs + (e / DK) * KP + e % DK) = rq[m];
+      }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -656,7 +678,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int q = 0; q < CJ; ++q) a1[r][q] = F.eC * sDT[(CJ * jg + q) * 16 + 4 * ig + r];
-      mm_kk(a1, sO, 16, 4 * ig, sQ, KP, CJ * jg, 0, BT);  // rows past nr are zero
+      if constexpr (QG)
+        mm_kk(a1, sO, 16, 4 * ig, p.qn + (gc * p.Hqk + hk) * BT * DK, DK, CJ * jg, 0, BT);  // rows past nr are zero
+      else
+        mm_kk(a1, sO, 16, 4 * ig, sQs, KP, CJ * jg, 0, BT);
       mm_kk(a1, sR, 16, 4 * ig, sK, KP, CJ * jg, 0, BT);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -685,33 +710,56 @@ struct GradTiles {
   float s0[16 * DK], ds[16 * DK];                          // S0, dS_C rows [i][j]
 };
 
+// Threads of the gradient kernel: 512 (two waves per SIMD; each thread holds
+// 4 chunk rows by 2 chunk columns and by dk / 32 dk columns). For dk 256 the
+// unit q, k rows are read from the workspace (L2) instead of LDS.
+template <int DK>
+constexpr int grad_threads() { return 512; }
+
 template <typename T, int DK>
-__global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
-  constexpr int KP = DK + 4, ZP = 68, NJ = DK / 16;
-  __shared__ alignas(16) float sQ[BT * KP], sK[BT * KP];
+__global__ __launch_bounds__(grad_threads<DK>()) void bwd_grad_kernel(ChunkBwdArgs p) {
+  constexpr int NT = grad_threads<DK>();
+  constexpr bool QKG = DK > 128;
+  constexpr int CG = NT / 16;        // column groups: threads per row group
+  constexpr int CCN = BT / CG;       // chunk columns per thread (4 or 2)
+  constexpr int NJ = DK / CG;        // dk columns per thread
+  constexpr int TPR = 1024 / NT;     // tile elements per thread per [64][16] array
+  constexpr int KP = DK + 4, ZP = 68;
+  __shared__ alignas(16) float sQK[QKG ? 4 : 2 * BT * KP];
   __shared__ alignas(16) float sZ1[BT * ZP], sZ2[BT * ZP];  // dQK, dG
   __shared__ alignas(16) union {
     GradTiles<DK> t;
     float z[BT * ZP];  // a + p, for its column sums
   } u;
   __shared__ float sgam[BT], seg[BT], scw[BT], sbeta[BT];
-  __shared__ float vrow[BT], vm[BT], vb[BT], red[kThreads];
-  const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
-  const int r0 = 4 * rg, c0 = 4 * cg, j0c = NJ * cg;
+  __shared__ float vrow[BT], vm[BT], vb[BT], red[NT];
+  const int tid = threadIdx.x, rg = tid / CG, cg = tid % CG;
+  const int r0 = 4 * rg, c0 = CCN * cg, j0c = NJ * cg;
   const int64_t gc = blockIdx.x, hk = blockIdx.y;
   const ChunkPos cp = chunk_pos(p, gc);
   if (!cp.valid) return;
   const int nr = cp.nr;
   const int64_t G = p.Hv / p.Hqk, dvn = p.dv;
 
-  copy_rows<DK>(sK, KP, p.kn + (gc * p.Hqk + hk) * BT * DK);
-  copy_rows<DK>(sQ, KP, p.qn + (gc * p.Hqk + hk) * BT * DK);
+  const float *sQ, *sK;  // unit q, k rows, row stride QS
+  int QS;
+  if constexpr (QKG) {
+    sQ = p.qn + (gc * p.Hqk + hk) * BT * DK;
+    sK = p.kn + (gc * p.Hqk + hk) * BT * DK;
+    QS = DK;
+  } else {
+    copy_rows<DK>(sQK + BT * KP, KP, p.kn + (gc * p.Hqk + hk) * BT * DK);
+    copy_rows<DK>(sQK, KP, p.qn + (gc * p.Hqk + hk) * BT * DK);
+    sQ = sQK;
+    sK = sQK + BT * KP;
+    QS = KP;
+  }
   __syncthreads();
-  float gg[4][4], qk[4][4];
+  float gg[4][CCN], qk[4][CCN];
   zero(gg);
   zero(qk);
-  mm_rr(gg, sK, KP, r0, sK, KP, c0, 0, DK);
-  mm_rr(qk, sQ, KP, r0, sK, KP, c0, 0, DK);
+  mm_rr(gg, sK, QS, r0, sK, QS, c0, 0, DK);
+  mm_rr(qk, sQ, QS, r0, sK, QS, c0, 0, DK);
   float dq[4][NJ], dk[4][NJ];
   zero(dq);
   zero(dk);
@@ -727,7 +775,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
       scw[tid] = tid < nr ? __expf(gl - gt) : 0.f;
       sbeta[tid] = tid < nr ? p.beta[cp.brow * p.sbt_b + (cp.t0 + tid) * p.sbt_t + h * p.sbt_h] : 0.f;
     }
-    float c1[4][4], c2[4][4], k1[4][NJ], k2[4][NJ], k3[4][NJ];
+    float c1[4][CCN], c2[4][CCN], k1[4][NJ], k2[4][NJ], k3[4][NJ];
     zero(c1);
     zero(c2);
     zero(k1);
@@ -738,26 +786,28 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
     const int64_t stbase = (gc * p.Hv + h) * dvn * DK;
     for (int64_t jv = 0; jv < dvn; jv += 16) {
       __syncthreads();
-      {  // row t = tid >> 2 of the tiles, value columns 4 (tid & 3) .. + 3
-        const int t = tid >> 2, i4 = 4 * (tid & 3);
-        float o4[4] = {0.f, 0.f, 0.f, 0.f}, d4[4], rp4[4], r4[4];
-        if (t < nr)
-          load_vec<T, 4>(static_cast<const T *>(p.d_o) + cp.brow * p.sdo_b + (cp.t0 + t) * p.sdo_t + h * p.sdo_h +
-                             jv + i4,
-                         (int)sizeof(T), o4);
-        const int64_t wo = rowbase + t * dvn + jv + i4;
-        ldv<4>(p.del + wo, d4);
-        ldv<4>(p.drp + wo, rp4);
-        ldv<4>(p.rr + wo, r4);
+      {  // row t of the tiles, value columns i4 .. i4 + TPR - 1
+        const int t = tid / (16 / TPR), i4 = TPR * (tid % (16 / TPR));
+        float o4[TPR], d4[TPR], rp4[TPR], r4[TPR];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < TPR; ++q) o4[q] = 0.f;
+        if (t < nr)
+          load_vec<T, TPR>(static_cast<const T *>(p.d_o) + cp.brow * p.sdo_b + (cp.t0 + t) * p.sdo_t + h * p.sdo_h +
+                               jv + i4,
+                           (int)sizeof(T), o4);
+        const int64_t wo = rowbase + t * dvn + jv + i4;
+        ldv<TPR>(p.del + wo, d4);
+        ldv<TPR>(p.drp + wo, rp4);
+        ldv<TPR>(p.rr + wo, r4);
+#pragma unroll
+        for (int q = 0; q < TPR; ++q) {
           u.t.o[(i4 + q) * BT + t] = o4[q];
           u.t.d[(i4 + q) * BT + t] = d4[q];
           u.t.rp[(i4 + q) * BT + t] = rp4[q];
           u.t.r[(i4 + q) * BT + t] = r4[q];
         }
       }
-      for (int e = 4 * tid; e < 16 * DK; e += 4 * kThreads) {
+      for (int e = 4 * tid; e < 16 * DK; e += 4 * NT) {
         float a[4], b[4];
         ldv<4>(p.s0 + stbase + jv * DK + e, a);
         ldv<4>(p.ds + stbase + jv * DK + e, b);
@@ -784,7 +834,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
       rowz[r] = 0.f;
       roww[r] = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < CCN; ++c) {
         const int s = c0 + c;
         const float e = s <= t ? __expf(sgam[t] - sgam[s]) : 0.f;
         const float dqk = s <= t ? p.scale * c1[r][c] * e : 0.f;  // dPt o E
@@ -807,14 +857,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
 #pragma unroll
       for (int q = 0; q < NJ; ++q) {
         const int j = j0c + q;
-        a = fmaf(sQ[t * KP + j], k1[r][q], a);
-        b = fmaf(sK[t * KP + j], k3[r][q], b);
-        m = fmaf(sK[t * KP + j], k2[r][q], m);
+        a = fmaf(sQ[t * QS + j], k1[r][q], a);
+        b = fmaf(sK[t * QS + j], k3[r][q], b);
+        m = fmaf(sK[t * QS + j], k2[r][q], m);
       }
       const float rd = p.scale * seg[t] * a - seg[t] * sbeta[t] * b - scw[t] * m;
-      rdot[r] = group_sum<16>(rd + rowz[r]);
-      rm[r] = group_sum<16>(scw[t] * m);
-      roww[r] = group_sum<16>(roww[r]);
+      rdot[r] = group_sum<CG>(rd + rowz[r]);
+      rm[r] = group_sum<CG>(scw[t] * m);
+      roww[r] = group_sum<CG>(roww[r]);
     }
     if (cg == 0)
 #pragma unroll
@@ -834,16 +884,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
       }
     }
     __syncthreads();
-    mm_rk(dq, sZ1, ZP, r0, sK, KP, j0c, 0, BT);
-    mm_rk(dk, sZ2, ZP, r0, sK, KP, j0c, 0, BT);
-    mm_kk(dk, sZ2, ZP, r0, sK, KP, j0c, 0, BT);
-    mm_kk(dk, sZ1, ZP, r0, sQ, KP, j0c, 0, BT);
+    mm_rk(dq, sZ1, ZP, r0, sK, QS, j0c, 0, BT);
+    mm_rk(dk, sZ2, ZP, r0, sK, QS, j0c, 0, BT);
+    mm_kk(dk, sZ2, ZP, r0, sK, QS, j0c, 0, BT);
+    mm_kk(dk, sZ1, ZP, r0, sQ, QS, j0c, 0, BT);
     if (tid < BT) {  // wave 0: dgamma, its reverse running sum (dg), dbeta
       const int t = tid;
       float colz = 0.f;
       for (int s = 0; s < BT; ++s) colz += u.z[s * ZP + t];
       float tot = 0.f;
-      for (int i = 0; i < kThreads; ++i) tot += red[i];
+      for (int i = 0; i < NT; ++i) tot += red[i];
       float sm = 0.f;
       for (int s = 0; s < BT; ++s) sm += vm[s];
       float dgam = vrow[t] - colz;
@@ -872,19 +922,19 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(ChunkBwdArgs p) {
 #pragma unroll
         for (int q = 0; q < NJ; ++q) {
           const int j = j0c + q;
-          a = fmaf(sQ[t * KP + j], dq[r][q], a);
-          b = fmaf(sK[t * KP + j], dk[r][q], b);
+          a = fmaf(sQ[t * QS + j], dq[r][q], a);
+          b = fmaf(sK[t * QS + j], dk[r][q], b);
         }
-        a = group_sum<16>(a);
-        b = group_sum<16>(b);
+        a = group_sum<CG>(a);
+        b = group_sum<CG>(b);
       }
       if (t < nr) {
         const int64_t base = ((cp.brow * p.T + cp.t0 + t) * p.Hqk + hk) * DK + j0c;
 #pragma unroll
         for (int q = 0; q < NJ; ++q) {
           const int j = j0c + q;
-          store_grad<T>(p.dqq, p.grad_dtype, base + q, (dq[r][q] - sQ[t * KP + j] * a) * rq[t]);
-          store_grad<T>(p.dkk, p.grad_dtype, base + q, (dk[r][q] - sK[t * KP + j] * b) * rk[t]);
+          store_grad<T>(p.dqq, p.grad_dtype, base + q, (dq[r][q] - sQ[t * QS + j] * a) * rq[t]);
+          store_grad<T>(p.dkk, p.grad_dtype, base + q, (dk[r][q] - sK[t * QS + j] * b) * rk[t]);
         }
       }
     }
@@ -903,8 +953,8 @@ hipError_t launch_t(const ChunkBwdArgs &a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), sg, dim3(kThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_grad_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk), dim3(kThreads), 0, s,
-                     a);
+  hipLaunchKernelGGL((bwd_grad_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk),
+                     dim3(grad_threads<DK>()), 0, s, a);
   return hipGetLastError();
 }
 
@@ -912,12 +962,13 @@ template <typename T>
 hipError_t launch_dk(const ChunkBwdArgs &a, hipStream_t s) {
   if (a.dk == 64) return launch_t<T, 64>(a, s);
   if (a.dk == 128) return launch_t<T, 128>(a, s);
+  if (a.dk == 256) return launch_t<T, 256>(a, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool chunk_bwd_supported(int64_t dk, int64_t dv) { return (dk == 64 || dk == 128) && dv % 16 == 0; }
+bool chunk_bwd_supported(int64_t dk, int64_t dv) { return (dk == 64 || dk == 128 || dk == 256) && dv % 16 == 0; }
 
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t s) {
   if (a.cu_seqlens) {

@@ -867,7 +867,8 @@ gdn_status plan_chunk_bwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_te
   if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_VALUE, "scale must be finite");
   if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps)) return fail(GDN_ERR_INVALID_VALUE, "l2_eps must be finite and >= 0");
   if (!gdn::chunk_bwd_supported(dkn, dvn))
-    return fail(GDN_ERR_NOT_SUPPORTED, "chunk rule backward: dk=%lld dv=%lld is not instantiated (dk 64 or 128)",
+    return fail(GDN_ERR_NOT_SUPPORTED,
+                "chunk rule backward: dk=%lld dv=%lld is not instantiated (dk 64, 128 or 256; dv a multiple of 16)",
                 (long long)dkn, (long long)dvn);
   if (n_seqs > 65535 || Hv > 65535 || Hqk > 65535)
     return fail(GDN_ERR_NOT_SUPPORTED, "chunk rule backward: at most 65535 sequences and heads");

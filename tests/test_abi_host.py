@@ -276,7 +276,8 @@ def test_chunk_rule_bwd_workspace_bytes_and_rejections():
     assert gdn.gdn_chunk_rule_bwd_workspace_bytes(2, 100, (Hqk, dk, Hv, dv)) == expect
     # packed: ceil(T / 64) + n_seqs rows
     assert gdn.gdn_chunk_rule_bwd_workspace_bytes(1, 100, (1, 128, 1, 64), n_seqs=3) > 0
-    assert gdn.gdn_chunk_rule_bwd_workspace_bytes(1, 100, (1, 256, 1, 64)) == 0  # dk 256 not built
+    assert gdn.gdn_chunk_rule_bwd_workspace_bytes(1, 100, (1, 256, 1, 64)) > 0
+    assert gdn.gdn_chunk_rule_bwd_workspace_bytes(1, 100, (1, 512, 1, 64)) == 0  # dk 512 not built
     q, k, v, g, beta, do = _rule_bwd_inputs()
     _expect(INVALID, "d_o: dtype", gdn.gdn_chunk_rule_bwd, q, k, v, g, beta, do.half(), 0.125)
     _expect(INVALID, "dq: dtype", gdn.gdn_chunk_rule_bwd, q, k, v, g, beta, do, 0.125, grad_dtype=torch.float16)
@@ -284,8 +285,10 @@ def test_chunk_rule_bwd_workspace_bytes_and_rejections():
             workspace=torch.zeros(16, dtype=torch.uint8))
     _expect(INVALID, "d_final_state: dim", gdn.gdn_chunk_rule_bwd, q, k, v, g, beta, do, 0.125,
             d_final_state=torch.zeros(1, 4, 32, 32))
-    q2, k2, v2, g2, b2, do2 = _rule_bwd_inputs(dk=256)
-    _expect(UNSUPPORTED, "dk=256", gdn.gdn_chunk_rule_bwd, q2, k2, v2, g2, b2, do2, 0.0625)
+    q2, k2, v2, g2, b2, do2 = _rule_bwd_inputs(dk=512)
+    _expect(UNSUPPORTED, "dk=512", gdn.gdn_chunk_rule_bwd, q2, k2, v2, g2, b2, do2, 0.0625)
+    q3, k3, v3, g3, b3, do3 = _rule_bwd_inputs(dv=8)
+    _expect(UNSUPPORTED, "dv=8", gdn.gdn_chunk_rule_bwd, q3, k3, v3, g3, b3, do3, 0.125)
 
 
 def test_bench_refuses_more_than_one_gpu():
