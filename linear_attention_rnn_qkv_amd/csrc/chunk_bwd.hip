@@ -214,24 +214,27 @@ __device__ __forceinline__ void mm_rr(float (&acc)[RM][CN], const float *A, int 
   }
 }
 
+// The serial kernels run kSer threads (kSerW waves, two per SIMD).
+constexpr int kSer = 512, kSerW = kSer / 64;
+
 // A 64 x 16 product split over the contraction: wave w's lanes hold 4 x 4
 // tiles (rows 4 (lane >> 2), columns 4 (lane & 3)) of its partial sum; the
-// four partials meet in `red` and thread tid gets row tid >> 2, columns
-// 4 (tid & 3) .. + 3 of the total.
-__device__ __forceinline__ void ksplit_sum(float *red, const float (&acc)[4][4], float (&out)[4]) {
+// kSerW partials meet in `red` and thread tid gets row tid >> 3, columns
+// 2 (tid & 7) and + 1 of the total.
+__device__ __forceinline__ void ksplit_sum(float *red, const float (&acc)[4][4], float (&out)[2]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tg = lane >> 2, ig = lane & 3;
 #pragma unroll
   for (int r = 0; r < 4; ++r) stv<4>(red + w * 1024 + (4 * tg + r) * 16 + 4 * ig, acc[r]);
   __syncthreads();
-  const int t = threadIdx.x >> 2, i4 = 4 * (threadIdx.x & 3);
-  ldv<4>(red + t * 16 + i4, out);
+  const int t = threadIdx.x >> 3, i2 = 2 * (threadIdx.x & 7);
+  ldv<2>(red + t * 16 + i2, out);
 #pragma unroll
-  for (int ww = 1; ww < 4; ++ww) {
-    float x[4];
-    ldv<4>(red + ww * 1024 + t * 16 + i4, x);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) out[c] += x[c];
+  for (int ww = 1; ww < kSerW; ++ww) {
+    float x[2];
+    ldv<2>(red + ww * 1024 + t * 16 + i2, x);
+    out[0] += x[0];
+    out[1] += x[1];
   }
 }
 
@@ -411,14 +414,15 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
 // state slice is kept transposed in LDS (sST[j][i]).
 // ---------------------------------------------------------------------------
 template <typename T, int DK>
-__global__ __launch_bounds__(kThreads) void bwd_states_kernel(ChunkBwdArgs p) {
-  constexpr int KP = DK + 4, CJ = DK / 64;
+__global__ __launch_bounds__(kSer) void bwd_states_kernel(ChunkBwdArgs p) {
+  // state update tiles: RI value rows by CJ dk columns per thread
+  constexpr int KP = DK + 4, RI = DK >= 128 ? 4 : 2, CJ = DK / 32 / RI, NIG = 16 / RI;
   __shared__ alignas(16) float sK[BT * KP];    // unit k rows [t][j]
   __shared__ alignas(16) float sM[BT * 68];    // M [t][s]
   __shared__ alignas(16) float sST[DK * 16];   // S^T [j][i]
   __shared__ alignas(16) float sX[BT * 16];    // beta R [s][i]
   __shared__ alignas(16) float sV[BT * 16];    // v, then cw Delta [s][i]
-  __shared__ alignas(16) float red[4 * 1024];
+  __shared__ alignas(16) float red[kSerW * 1024];
   __shared__ Fac F;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int64_t j0, h, n;
@@ -427,29 +431,29 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(ChunkBwdArgs p) {
   int64_t brow, bos, L, gc0;
   seq_pos(p, n, brow, bos, L, gc0);
   const int64_t nch = (L + BT - 1) / BT;
-  const int et = tid >> 2, ei = 4 * (tid & 3);  // epilogue: row et, columns ei .. ei + 3
-  const int ig = tid & 3, jg = tid >> 2;        // state update: rows 4 ig .., columns CJ jg ..
+  const int et = tid >> 3, ei = 2 * (tid & 7);  // epilogue: row et, columns ei .. ei + 3
+  const int ig = tid % NIG, jg = tid / NIG;     // state update: rows RI ig .., columns CJ jg ..
 
-  for (int e = tid; e < 16 * DK; e += kThreads) {
+  for (int e = tid; e < 16 * DK; e += kSer) {
     const int i = e / DK, j = e % DK;
     sST[j * 16 + i] = p.init_state ? p.init_state[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] : 0.f;
   }
   // The next chunk's operands are staged in registers while this one is
   // computed: unit k rows, M, the v slice and the factors.
-  constexpr int NK = DK / 16;
-  fv4 rk[NK], rm[4];
-  float rv[4], rg = 0.f, rgl = 0.f, rb = 0.f;
+  constexpr int NK = DK / 32;
+  fv4 rk[NK], rm[2];
+  float rv[2], rg = 0.f, rgl = 0.f, rb = 0.f;
   auto fetch = [&](int64_t c) {
     const int64_t gc = gc0 + c, t0 = bos + c * BT;
     const int nr = (int)(L - c * BT < BT ? L - c * BT : BT);
     const float *kn = p.kn + (gc * p.Hqk + hk) * BT * DK, *mm_ = p.mm + (gc * p.Hv + h) * BT * BT;
 #pragma unroll
-    for (int m = 0; m < NK; ++m) rk[m] = *reinterpret_cast<const fv4 *>(kn + 4 * (tid + kThreads * m));
+    for (int m = 0; m < NK; ++m) rk[m] = *reinterpret_cast<const fv4 *>(kn + 4 * (tid + kSer * m));
 #pragma unroll
-    for (int m = 0; m < 4; ++m) rm[m] = *reinterpret_cast<const fv4 *>(mm_ + 4 * (tid + kThreads * m));
+    for (int m = 0; m < 2; ++m) rm[m] = *reinterpret_cast<const fv4 *>(mm_ + 4 * (tid + kSer * m));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) rv[q] = 0.f;
-    if (et < nr) load_vec<T, 4>(static_cast<const T *>(p.v) + brow * p.sv_b + (t0 + et) * p.sv_t + h * p.sv_h + j0 + ei,
+    for (int q = 0; q < 2; ++q) rv[q] = 0.f;
+    if (et < nr) load_vec<T, 2>(static_cast<const T *>(p.v) + brow * p.sv_b + (t0 + et) * p.sv_t + h * p.sv_h + j0 + ei,
                                 (int)sizeof(T), rv);
     if (tid < BT) {
       const float *gm = p.gam + (gc * p.Hv + h) * BT;
@@ -464,18 +468,18 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(ChunkBwdArgs p) {
     const int64_t gc = gc0 + c;
     const int nr = (int)(L - c * BT < BT ? L - c * BT : BT);
     float *s0 = p.s0 + ((gc * p.Hv + h) * p.dv + j0) * DK;
-    for (int e = tid; e < 16 * DK; e += kThreads) s0[e] = sST[(e % DK) * 16 + e / DK];
+    for (int e = tid; e < 16 * DK; e += kSer) s0[e] = sST[(e % DK) * 16 + e / DK];
 #pragma unroll
     for (int m = 0; m < NK; ++m) {
-      const int e = 4 * (tid + kThreads * m);
+      const int e = 4 * (tid + kSer * m);
       *reinterpret_cast<fv4 *>(sK + (e / DK) * KP + e % DK) = rk[m];
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int e = 4 * (tid + kThreads * m);
+    for (int m = 0; m < 2; ++m) {
+      const int e = 4 * (tid + kSer * m);
       *reinterpret_cast<fv4 *>(sM + (e >> 6) * 68 + (e & 63)) = rm[m];
     }
-    stv<4>(sV + et * 16 + ei, rv);
+    stv<2>(sV + et * 16 + ei, rv);
     if (tid < BT) {
       F.eg[tid] = __expf(rg);
       F.cw[tid] = tid < nr ? __expf(rgl - rg) : 0.f;
@@ -488,45 +492,45 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(ChunkBwdArgs p) {
     {
       float acc[4][4];
       zero(acc);
-      mm_rk(acc, sK, KP, 4 * (lane >> 2), sST, 16, 4 * (lane & 3), w * (DK / 4), (w + 1) * (DK / 4));
-      float ks[4];
+      mm_rk(acc, sK, KP, 4 * (lane >> 2), sST, 16, 4 * (lane & 3), w * (DK / kSerW), (w + 1) * (DK / kSerW));
+      float ks[2];
       ksplit_sum(red, acc, ks);
-      float vv[4], R[4], X[4];
-      ldv<4>(sV + et * 16 + ei, vv);
+      float vv[2], R[2], X[2];
+      ldv<2>(sV + et * 16 + ei, vv);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 2; ++q) {
         R[q] = vv[q] - F.eg[et] * ks[q];
         X[q] = F.beta[et] * R[q];
       }
-      stv<4>(p.rr + ((gc * p.Hv + h) * BT + et) * p.dv + j0 + ei, R);
-      stv<4>(sX + et * 16 + ei, X);
+      stv<2>(p.rr + ((gc * p.Hv + h) * BT + et) * p.dv + j0 + ei, R);
+      stv<2>(sX + et * 16 + ei, X);
     }
     __syncthreads();
     // Delta = M X (contraction over s, 16 per wave)
     {
       float acc[4][4];
       zero(acc);
-      mm_rk(acc, sM, 68, 4 * (lane >> 2), sX, 16, 4 * (lane & 3), 16 * w, 16 * w + 16);
-      float dl[4], cd[4];
+      mm_rk(acc, sM, 68, 4 * (lane >> 2), sX, 16, 4 * (lane & 3), 8 * w, 8 * w + 8);
+      float dl[2], cd[2];
       ksplit_sum(red, acc, dl);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) cd[q] = F.cw[et] * dl[q];
-      stv<4>(p.del + ((gc * p.Hv + h) * BT + et) * p.dv + j0 + ei, dl);
-      stv<4>(sV + et * 16 + ei, cd);
+      for (int q = 0; q < 2; ++q) cd[q] = F.cw[et] * dl[q];
+      stv<2>(p.del + ((gc * p.Hv + h) * BT + et) * p.dv + j0 + ei, dl);
+      stv<2>(sV + et * 16 + ei, cd);
     }
     __syncthreads();
     // S = exp(gamma_C) S + (cw Delta)^T K
     {
-      float acc[4][CJ];
+      float acc[RI][CJ];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < RI; ++r)
 #pragma unroll
-        for (int q = 0; q < CJ; ++q) acc[r][q] = F.eC * sST[(CJ * jg + q) * 16 + 4 * ig + r];
-      mm_kk(acc, sV, 16, 4 * ig, sK, KP, CJ * jg, 0, BT);  // rows past nr are zero
+        for (int q = 0; q < CJ; ++q) acc[r][q] = F.eC * sST[(CJ * jg + q) * 16 + RI * ig + r];
+      mm_kk(acc, sV, 16, RI * ig, sK, KP, CJ * jg, 0, BT);  // rows past nr are zero
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < RI; ++r)
 #pragma unroll
-        for (int q = 0; q < CJ; ++q) sST[(CJ * jg + q) * 16 + 4 * ig + r] = acc[r][q];
+        for (int q = 0; q < CJ; ++q) sST[(CJ * jg + q) * 16 + RI * ig + r] = acc[r][q];
     }
     __syncthreads();
   }
@@ -537,8 +541,9 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(ChunkBwdArgs p) {
 // sDT[j][i]).
 // ---------------------------------------------------------------------------
 template <typename T, int DK>
-__global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
-  constexpr int KP = DK + 4, CJ = DK / 64;
+__global__ __launch_bounds__(kSer) void bwd_dstate_kernel(ChunkBwdArgs p) {
+  // state update tiles: RI value rows by CJ dk columns per thread
+  constexpr int KP = DK + 4, RI = DK >= 128 ? 4 : 2, CJ = DK / 32 / RI, NIG = 16 / RI;
   // dk 256: the unit q rows are read from the workspace (L2) in the state
   // update instead of being staged in LDS, which would not hold them
   constexpr bool QG = DK > 128;
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
   __shared__ alignas(16) float sP[BT * BT], sM[BT * BT];  // as stored: [s][t]
   __shared__ alignas(16) float sDT[DK * 16];              // dS^T [j][i]
   __shared__ alignas(16) float sO[BT * 16], sR[BT * 16];  // dO, then scale exp(gamma) dO; -exp(gamma) dv
-  __shared__ alignas(16) float red[4 * 1024];             // partials; red[0 .. 1024) then holds dDelta
+  __shared__ alignas(16) float red[kSerW * 1024];             // partials; red[0 .. 1024) then holds dDelta
   __shared__ Fac F;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int64_t j0, h, n;
@@ -555,38 +560,38 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
   int64_t brow, bos, L, gc0;
   seq_pos(p, n, brow, bos, L, gc0);
   const int64_t nch = (L + BT - 1) / BT;
-  const int et = tid >> 2, ei = 4 * (tid & 3);
-  const int ig = tid & 3, jg = tid >> 2;
+  const int et = tid >> 3, ei = 2 * (tid & 7);
+  const int ig = tid % NIG, jg = tid / NIG;
 
-  for (int e = tid; e < 16 * DK; e += kThreads) {
+  for (int e = tid; e < 16 * DK; e += kSer) {
     const int i = e / DK, j = e % DK;
     sDT[j * 16 + i] = p.d_final ? p.d_final[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] : 0.f;
   }
   // The next chunk's operands are staged in registers while this one is
   // computed: unit k and q rows, M, scale * Pt, the dO slice and the factors.
-  constexpr int NK = DK / 16, NQ = QG ? 1 : NK;
-  fv4 rk[NK], rq[NQ], rm[4], rp[4];
-  float ro[4], rg = 0.f, rgl = 0.f, rb = 0.f;
+  constexpr int NK = DK / 32, NQ = QG ? 1 : NK;
+  fv4 rk[NK], rq[NQ], rm[2], rp[2];
+  float ro[2], rg = 0.f, rgl = 0.f, rb = 0.f;
   auto fetch = [&](int64_t c) {
     const int64_t gc = gc0 + c, t0 = bos + c * BT;
     const int nr = (int)(L - c * BT < BT ? L - c * BT : BT);
     const float *kn = p.kn + (gc * p.Hqk + hk) * BT * DK, *qn = p.qn + (gc * p.Hqk + hk) * BT * DK;
     const float *mm_ = p.mm + (gc * p.Hv + h) * BT * BT, *pp = p.pp + (gc * p.Hv + h) * BT * BT;
 #pragma unroll
-    for (int m = 0; m < NK; ++m) rk[m] = *reinterpret_cast<const fv4 *>(kn + 4 * (tid + kThreads * m));
+    for (int m = 0; m < NK; ++m) rk[m] = *reinterpret_cast<const fv4 *>(kn + 4 * (tid + kSer * m));
     if constexpr (!QG) {
 #pragma unroll
-      for (int m = 0; m < NQ; ++m) rq[m] = *reinterpret_cast<const fv4 *>(qn + 4 * (tid + kThreads * m));
+      for (int m = 0; m < NQ; ++m) rq[m] = *reinterpret_cast<const fv4 *>(qn + 4 * (tid + kSer * m));
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      rm[m] = *reinterpret_cast<const fv4 *>(mm_ + 4 * (tid + kThreads * m));
-      rp[m] = *reinterpret_cast<const fv4 *>(pp + 4 * (tid + kThreads * m));
+    for (int m = 0; m < 2; ++m) {
+      rm[m] = *reinterpret_cast<const fv4 *>(mm_ + 4 * (tid + kSer * m));
+      rp[m] = *reinterpret_cast<const fv4 *>(pp + 4 * (tid + kSer * m));
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ro[q] = 0.f;
+    for (int q = 0; q < 2; ++q) ro[q] = 0.f;
     if (et < nr)
-      load_vec<T, 4>(static_cast<const T *>(p.d_o) + brow * p.sdo_b + (t0 + et) * p.sdo_t + h * p.sdo_h + j0 + ei,
+      load_vec<T, 2>(static_cast<const T *>(p.d_o) + brow * p.sdo_b + (t0 + et) * p.sdo_t + h * p.sdo_h + j0 + ei,
                      (int)sizeof(T), ro);
     if (tid < BT) {
       const float *gm = p.gam + (gc * p.Hv + h) * BT;
@@ -601,26 +606,26 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
     const int64_t gc = gc0 + c, t0 = bos + c * BT;
     const int nr = (int)(L - c * BT < BT ? L - c * BT : BT);
     float *ds = p.ds + ((gc * p.Hv + h) * p.dv + j0) * DK;
-    for (int e = tid; e < 16 * DK; e += kThreads) ds[e] = sDT[(e % DK) * 16 + e / DK];
+    for (int e = tid; e < 16 * DK; e += kSer) ds[e] = sDT[(e % DK) * 16 + e / DK];
 #pragma unroll
     for (int m = 0; m < NK; ++m) {
-      const int e = 4 * (tid + kThreads * m);
+      const int e = 4 * (tid + kSer * m);
       *reinterpret_cast<fv4 *>(sK + (e / DK) * KP + e % DK) = rk[m];
     }
     if constexpr (!QG) {
 #pragma unroll
       for (int m = 0; m < NQ; ++m) {
-        const int e = 4 * (tid + kThreads * m);
+        const int e = 4 * (tid + kSer * m);
         *reinterpret_cast<fv4 *>(sQs + (e / DK) * KP + e % DK) = rq[m];
       }
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int e = 4 * (tid + kThreads * m);
+    for (int m = 0; m < 2; ++m) {
+      const int e = 4 * (tid + kSer * m);
       *reinterpret_cast<fv4 *>(sM + e) = rm[m];
       *reinterpret_cast<fv4 *>(sP + e) = rp[m];
     }
-    stv<4>(sO + et * 16 + ei, ro);
+    stv<2>(sO + et * 16 + ei, ro);
     if (tid < BT) {
       F.eg[tid] = __expf(rg);
       F.cw[tid] = tid < nr ? __expf(rgl - rg) : 0.f;
@@ -634,30 +639,30 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
       float a1[4][4];
       zero(a1);
       const int r0 = 4 * (lane >> 2), c0 = 4 * (lane & 3);
-      mm_rk(a1, sK, KP, r0, sDT, 16, c0, w * (DK / 4), (w + 1) * (DK / 4));
+      mm_rk(a1, sK, KP, r0, sDT, 16, c0, w * (DK / kSerW), (w + 1) * (DK / kSerW));
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int q = 0; q < 4; ++q) a1[r][q] *= F.cw[r0 + r];
-      mm_kk(a1, sP, BT, r0, sO, 16, c0, 16 * w, 16 * w + 16);
-      float dd[4];
+      mm_kk(a1, sP, BT, r0, sO, 16, c0, 8 * w, 8 * w + 8);
+      float dd[2];
       ksplit_sum(red, a1, dd);
       __syncthreads();  // every partial is read before red[0 ..) is overwritten
-      stv<4>(red + et * 16 + ei, dd);
+      stv<2>(red + et * 16 + ei, dd);
     }
     __syncthreads();
     // dR' = M^T dDelta; dv = beta dR'
     {
       float a1[4][4];
       zero(a1);
-      mm_kk(a1, sM, BT, 4 * (lane >> 2), red, 16, 4 * (lane & 3), 16 * w, 16 * w + 16);
+      mm_kk(a1, sM, BT, 4 * (lane >> 2), red, 16, 4 * (lane & 3), 8 * w, 8 * w + 8);
       __syncthreads();  // dDelta in red[0 ..) is read by every wave before the partials land
-      float dr[4], dvv[4], er[4], oo[4];
+      float dr[2], dvv[2], er[2], oo[2];
       ksplit_sum(red, a1, dr);
-      stv<4>(p.drp + ((gc * p.Hv + h) * BT + et) * p.dv + j0 + ei, dr);
-      ldv<4>(sO + et * 16 + ei, oo);
+      stv<2>(p.drp + ((gc * p.Hv + h) * BT + et) * p.dv + j0 + ei, dr);
+      ldv<2>(sO + et * 16 + ei, oo);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 2; ++q) {
         dvv[q] = F.beta[et] * dr[q];
         er[q] = -F.eg[et] * dvv[q];
         oo[q] *= p.scale * F.eg[et];
@@ -665,33 +670,33 @@ __global__ __launch_bounds__(kThreads) void bwd_dstate_kernel(ChunkBwdArgs p) {
       if (et < nr) {
         const int64_t o = ((brow * p.T + t0 + et) * p.Hv + h) * p.dv + j0 + ei;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) store_grad<T>(p.dvv, p.grad_dtype, o + q, dvv[q]);
+        for (int q = 0; q < 2; ++q) store_grad<T>(p.dvv, p.grad_dtype, o + q, dvv[q]);
       }
-      stv<4>(sR + et * 16 + ei, er);
-      stv<4>(sO + et * 16 + ei, oo);
+      stv<2>(sR + et * 16 + ei, er);
+      stv<2>(sO + et * 16 + ei, oo);
     }
     __syncthreads();
     // dS0 = exp(gamma_C) dS + (scale exp(gamma) dO)^T Q - (exp(gamma) dv)^T K
     {
-      float a1[4][CJ];
+      float a1[RI][CJ];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < RI; ++r)
 #pragma unroll
-        for (int q = 0; q < CJ; ++q) a1[r][q] = F.eC * sDT[(CJ * jg + q) * 16 + 4 * ig + r];
+        for (int q = 0; q < CJ; ++q) a1[r][q] = F.eC * sDT[(CJ * jg + q) * 16 + RI * ig + r];
       if constexpr (QG)
-        mm_kk(a1, sO, 16, 4 * ig, p.qn + (gc * p.Hqk + hk) * BT * DK, DK, CJ * jg, 0, BT);  // rows past nr are zero
+        mm_kk(a1, sO, 16, RI * ig, p.qn + (gc * p.Hqk + hk) * BT * DK, DK, CJ * jg, 0, BT);  // rows past nr are zero
       else
-        mm_kk(a1, sO, 16, 4 * ig, sQs, KP, CJ * jg, 0, BT);
-      mm_kk(a1, sR, 16, 4 * ig, sK, KP, CJ * jg, 0, BT);
+        mm_kk(a1, sO, 16, RI * ig, sQs, KP, CJ * jg, 0, BT);
+      mm_kk(a1, sR, 16, RI * ig, sK, KP, CJ * jg, 0, BT);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < RI; ++r)
 #pragma unroll
-        for (int q = 0; q < CJ; ++q) sDT[(CJ * jg + q) * 16 + 4 * ig + r] = a1[r][q];
+        for (int q = 0; q < CJ; ++q) sDT[(CJ * jg + q) * 16 + RI * ig + r] = a1[r][q];
     }
     __syncthreads();
   }
   if (p.d_init) {
-    for (int e = tid; e < 16 * DK; e += kThreads) {
+    for (int e = tid; e < 16 * DK; e += kSer) {
       const int i = e / DK, j = e % DK;
       p.d_init[((n * p.Hv + h) * p.dv + j0 + i) * DK + j] = sDT[j * 16 + i];
     }
@@ -949,9 +954,9 @@ hipError_t launch_t(const ChunkBwdArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 sg((unsigned)(a.dv / 16), (unsigned)a.Hv, (unsigned)N);
-  hipLaunchKernelGGL((bwd_states_kernel<T, DK>), sg, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_states_kernel<T, DK>), sg, dim3(kSer), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), sg, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), sg, dim3(kSer), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_grad_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk),
                      dim3(grad_threads<DK>()), 0, s, a);
