@@ -354,7 +354,7 @@ def main() -> int:
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the layer core "
+        print(f"bench.py: runs on one GPU only (got --gpus {args.gpus}); the layer core "
               "shards by heads or sequences without a collective, which is not built here.",
               file=sys.stderr)
         return 2

@@ -12,9 +12,9 @@
 //   S_C   = exp(gamma_C) S0 + Delta^T diag(exp(gamma_C - gamma)) K
 // (the gated delta rule of Gated DeltaNet, Yang, Kautz and Hatamizadeh, in
 // the chunked form that the flash-linear-attention pull request's chunk mode
-// and the Megatron-LM L2-fold pull request run; the pages state that the
-// fused stages support first-order autograd, Megatron Core "GDN Elementwise
-// Fusion", Execution and numerical behavior).
+// and the Megatron-LM L2-fold pull request run; first-order autograd of the
+// fused stages: Megatron Core "GDN Elementwise Fusion", Execution and
+// numerical behavior).
 //
 // Kernels, in launch order:
 //   bwd_prep_kernel    per (chunk, q/k head): unit q, k rows, then per value
@@ -26,8 +26,8 @@
 //                      leaving each chunk), dR' = M^T dDelta, dv and dS0
 //   bwd_grad_kernel    per (chunk, q/k head), the value heads of the group
 //                      in turn: dq, dk (through the L2 fold), dg, dbeta
-// Products run on the vector ALU from LDS tiles (a first version; the
-// forward's MFMA layouts are not reused here).
+// Products run in FP32 on the vector ALU from LDS tiles; the forward's MFMA
+// records (BF16 fragments of M diag(beta), not M) are not reused.
 #include "device_common.h"
 #include "gdn_internal.h"
 
