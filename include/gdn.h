@@ -17,6 +17,8 @@
  *   gdn_gated_norm_bwd, gdn_prologue_bwd, gdn_chunk_rule_bwd
  *                       first-order gradients of the gated norm, of the
  *                       prologue and of the chunked gated delta rule
+ *   gdn_layer_bwd       the gradients of gdn_layer_fwd: the forward stages
+ *                       recomputed, then the three backward stages
  *
  * Sources (web pages):
  *   [P1] Megatron-LM pull request "perf(gated_delta_net): fold q/k L2-norm
@@ -413,6 +415,57 @@ gdn_status gdn_chunk_rule_bwd(const gdn_tensor *q, const gdn_tensor *k,
  * invalid or unsupported geometry. */
 size_t gdn_chunk_rule_bwd_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs,
                                           const gdn_dims *dims);
+
+/*
+ * gdn_layer_bwd - first-order gradients of gdn_layer_fwd ([P2] Execution and
+ * numerical behavior: the fused stages support first-order autograd; [P3]
+ * Test plan: input and parameter gradients of the fused layer checked).
+ * Gradients of L = sum(d_out * out) with respect to every input and
+ * parameter of gdn_layer_fwd. On `stream`, in a caller workspace: the
+ * prologue and the chunk rule are recomputed (qkv, g, beta and o as
+ * gdn_layer_fwd materialises them), then gdn_gated_norm_bwd (d_o in the act
+ * dtype), gdn_chunk_rule_bwd (dq, dk, dv into one FP32 [B, T, C] buffer,
+ * dg, dbeta) and gdn_prologue_bwd run. Each stage's gradient is evaluated at
+ * the stored values of its inputs, the roundings taken as the identity.
+ *
+ *   inputs          as in gdn_layer_fwd (initial state: none)
+ *   d_out           [B, T, Hv, dv] act dtype, any strides, inner 1
+ *   dx_q, dx_k, dx_v, d_conv_w, d_conv_b (NULL when conv_b is NULL), d_a,
+ *   d_b, d_A_log, d_dt_bias   as the outputs of gdn_prologue_bwd
+ *   d_gate          [B, T, Hv, dv] gate's dtype, contiguous
+ *   d_norm_w        [dv] F32
+ *   workspace       gdn_layer_bwd_workspace_bytes(...) bytes, 256-byte
+ *                   aligned, owned by the caller and not used by any other
+ *                   call until this call's work on `stream` is done
+ * Outputs must not overlap inputs, each other or the workspace. Supported:
+ * the geometries of gdn_chunk_rule_bwd.
+ */
+gdn_status gdn_layer_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
+                         const gdn_tensor *x_v, const gdn_tensor *conv_w,
+                         const gdn_tensor *conv_b, const gdn_tensor *a,
+                         const gdn_tensor *b, const gdn_tensor *A_log,
+                         const gdn_tensor *dt_bias, const gdn_tensor *gate,
+                         const gdn_tensor *norm_w,
+                         const gdn_tensor *cu_seqlens, const gdn_dims *dims,
+                         float scale, int32_t use_qk_l2norm_in_kernel,
+                         float l2_eps, float rms_eps,
+                         const gdn_tensor *d_out, const gdn_tensor *dx_q,
+                         const gdn_tensor *dx_k, const gdn_tensor *dx_v,
+                         const gdn_tensor *d_conv_w,
+                         const gdn_tensor *d_conv_b, const gdn_tensor *d_a,
+                         const gdn_tensor *d_b, const gdn_tensor *d_A_log,
+                         const gdn_tensor *d_dt_bias,
+                         const gdn_tensor *d_gate, const gdn_tensor *d_norm_w,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Bytes of workspace gdn_layer_bwd needs (n_seqs as in
+ * gdn_layer_workspace_bytes): the forward stage outputs and the chunk
+ * forward's workspace, d_o, d_qkv (FP32), dg and dbeta, and the three
+ * backward stages' workspaces, each 256-byte aligned. 0 for invalid or
+ * unsupported geometry. */
+size_t gdn_layer_bwd_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs,
+                                     const gdn_dims *dims, int32_t act_dtype);
 
 #ifdef __cplusplus
 }

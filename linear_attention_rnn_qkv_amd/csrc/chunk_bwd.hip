@@ -668,7 +668,7 @@ __global__ __launch_bounds__(kSer) void bwd_dstate_kernel(ChunkBwdArgs p) {
         oo[q] *= p.scale * F.eg[et];
       }
       if (et < nr) {
-        const int64_t o = ((brow * p.T + t0 + et) * p.Hv + h) * p.dv + j0 + ei;
+        const int64_t o = brow * p.sdv_b + (t0 + et) * p.sdv_t + h * p.dv + j0 + ei;
 #pragma unroll
         for (int q = 0; q < 2; ++q) store_grad<T>(p.dvv, p.grad_dtype, o + q, dvv[q]);
       }
@@ -934,12 +934,13 @@ __global__ __launch_bounds__(grad_threads<DK>()) void bwd_grad_kernel(ChunkBwdAr
         b = group_sum<CG>(b);
       }
       if (t < nr) {
-        const int64_t base = ((cp.brow * p.T + cp.t0 + t) * p.Hqk + hk) * DK + j0c;
+        const int64_t tt = cp.t0 + t, hq = hk * DK + j0c;
+        const int64_t bq = cp.brow * p.sdq_b + tt * p.sdq_t + hq, bk = cp.brow * p.sdk_b + tt * p.sdk_t + hq;
 #pragma unroll
         for (int q = 0; q < NJ; ++q) {
           const int j = j0c + q;
-          store_grad<T>(p.dqq, p.grad_dtype, base + q, (dq[r][q] - sQ[t * QS + j] * a) * rq[t]);
-          store_grad<T>(p.dkk, p.grad_dtype, base + q, (dk[r][q] - sK[t * QS + j] * b) * rk[t]);
+          store_grad<T>(p.dqq, p.grad_dtype, bq + q, (dq[r][q] - sQ[t * QS + j] * a) * rq[t]);
+          store_grad<T>(p.dkk, p.grad_dtype, bk + q, (dk[r][q] - sK[t * QS + j] * b) * rk[t]);
         }
       }
     }

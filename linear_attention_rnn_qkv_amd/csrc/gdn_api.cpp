@@ -813,7 +813,11 @@ gdn_status plan_chunk_bwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_te
                           const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state, const gdn_tensor *d_o,
                           const gdn_tensor *d_final, const gdn_tensor *dq, const gdn_tensor *dk,
                           const gdn_tensor *dv, const gdn_tensor *dg, const gdn_tensor *dbeta,
-                          const gdn_tensor *d_init, void *ws, size_t ws_bytes, gdn::ChunkBwdArgs *P) {
+                          const gdn_tensor *d_init, void *ws, size_t ws_bytes, gdn::ChunkBwdArgs *P,
+                          bool grad_views = false) {
+  // grad_views (the layer backward): dq, dk, dv may be channel views of one
+  // [B, T, C] buffer (head stride d, inner stride 1) instead of contiguous
+  // tensors; they then share a byte range without sharing an element.
   if (!q || q->ndim != 4) return fail(GDN_ERR_INVALID_VALUE, "q: expected [B, T, Hqk, dk]");
   if (!v || v->ndim != 4) return fail(GDN_ERR_INVALID_VALUE, "v: expected [B, T, Hv, dv]");
   const int64_t B = q->shape[0], T = q->shape[1], Hqk = q->shape[2], dkn = q->shape[3];
@@ -863,7 +867,14 @@ gdn_status plan_chunk_bwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_te
   TRY(check_dtype(dbeta, "dbeta", GDN_F32));
   const gdn_tensor *outs[] = {dq, dk, dv, dg, dbeta, d_init};
   const char *onames[] = {"dq", "dk", "dv", "dg", "dbeta", "d_initial_state"};
-  for (int i = 0; i < 5; ++i) TRY(check_contig(outs[i], onames[i]));
+  for (int i = 0; i < 5; ++i) {
+    if (grad_views && i < 3) {
+      if (outs[i]->stride[3] != 1 || outs[i]->stride[2] != outs[i]->shape[3])
+        return fail(GDN_ERR_INVALID_VALUE, "%s: head stride must be the head dim, inner stride 1", onames[i]);
+      continue;
+    }
+    TRY(check_contig(outs[i], onames[i]));
+  }
   if (!std::isfinite(scale)) return fail(GDN_ERR_INVALID_VALUE, "scale must be finite");
   if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps)) return fail(GDN_ERR_INVALID_VALUE, "l2_eps must be finite and >= 0");
   if (!gdn::chunk_bwd_supported(dkn, dvn))
@@ -885,7 +896,7 @@ gdn_status plan_chunk_bwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_te
     for (auto *t : ins)
       if (overlaps(outs[i], t)) return fail(GDN_ERR_INVALID_VALUE, "%s overlaps an input", onames[i]);
     for (int j = i + 1; j < 6; ++j)
-      if (overlaps(outs[i], outs[j]))
+      if (!(grad_views && j < 3) && overlaps(outs[i], outs[j]))
         return fail(GDN_ERR_INVALID_VALUE, "%s overlaps %s", onames[i], onames[j]);
     if (overlaps(&wsd, outs[i])) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps %s", onames[i]);
   }
@@ -909,6 +920,9 @@ gdn_status plan_chunk_bwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_te
   p.init_state = initial_state ? static_cast<const float *>(initial_state->data) : nullptr;
   p.d_final = d_final ? static_cast<const float *>(d_final->data) : nullptr;
   p.dqq = dq->data; p.dkk = dk->data; p.dvv = dv->data;
+  p.sdq_b = dq->stride[0]; p.sdq_t = dq->stride[1];
+  p.sdk_b = dk->stride[0]; p.sdk_t = dk->stride[1];
+  p.sdv_b = dv->stride[0]; p.sdv_t = dv->stride[1];
   p.dg = static_cast<float *>(dg->data);
   p.dbeta = static_cast<float *>(dbeta->data);
   p.d_init = d_init ? static_cast<float *>(d_init->data) : nullptr;
@@ -922,6 +936,45 @@ gdn_status plan_chunk_bwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_te
   p.mm = fp(L.mm); p.pp = fp(L.pp); p.s0 = fp(L.s0); p.ds = fp(L.ds);
   p.rr = fp(L.rr); p.del = fp(L.del); p.drp = fp(L.drp);
   return GDN_OK;
+}
+
+// Workspace of the layer backward (byte offsets, each 256-aligned): the
+// recomputed forward stage outputs, the chunk forward's workspace, d_o and the
+// gated-norm backward's partials, d_qkv (FP32) with dg and dbeta, then the
+// chunk-rule and prologue backward workspaces.
+struct LayerBwdWs {
+  size_t qkv, g, beta, o, cfw, d_o, nbw, dqkv, dg, dbeta, cbw, pbw, total;
+  size_t cfw_n, nbw_n, cbw_n, pbw_n;
+};
+LayerBwdWs layer_bwd_layout(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *d, int32_t act) {
+  LayerBwdWs w;
+  const size_t n = (size_t)(B * T), es = (size_t)elem_size(act);
+  const size_t C = (size_t)(2 * d->Hqk * d->dk + d->Hv * d->dv), Hv = (size_t)d->Hv, HD = (size_t)(d->Hv * d->dv);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  w.cfw_n = chunk_ws_bytes(B, T, n_seqs, d->dk, d->Hv, d->dv, act);
+  w.nbw_n = (size_t)align256((size_t)norm_bwd_blocks(B * T * d->Hv, d->dv) * (size_t)d->dv * 4) +
+            align256((size_t)32 * d->dv * 4);
+  w.cbw_n = chunk_bwd_layout(B, T, n_seqs, d).total;
+  w.pbw_n = prologue_bwd_ws(B, T, d);
+  w.qkv = take(n * C * es);
+  w.g = take(n * Hv * 4);
+  w.beta = take(n * Hv * 4);
+  w.o = take(n * HD * es);
+  w.cfw = take(w.cfw_n);
+  w.d_o = take(n * HD * es);
+  w.nbw = take(w.nbw_n);
+  w.dqkv = take(n * C * 4);
+  w.dg = take(n * Hv * 4);
+  w.dbeta = take(n * Hv * 4);
+  w.cbw = take(w.cbw_n);
+  w.pbw = take(w.pbw_n);
+  w.total = o;
+  return w;
 }
 
 }  // namespace
@@ -1048,6 +1101,104 @@ gdn_status gdn_chunk_rule_bwd(const gdn_tensor *q, const gdn_tensor *k, const gd
   TRY(plan_chunk_bwd(q, k, v, g, beta, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, initial_state, d_o,
                      d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, workspace, workspace_bytes, &P));
   return launched(gdn::launch_chunk_bwd(P, (hipStream_t)stream), "chunk rule backward");
+}
+
+size_t gdn_layer_bwd_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *dims,
+                                     int32_t act_dtype) {
+  if (!dims || B <= 0 || T <= 0 || n_seqs < 0 || !is_act(act_dtype)) return 0;
+  if (dims->Hqk <= 0 || dims->dk <= 0 || dims->Hv <= 0 || dims->dv < 64 || dims->dv > 512 || !pow2(dims->dv))
+    return 0;
+  if (!gdn::chunk_bwd_supported(dims->dk, dims->dv)) return 0;
+  return layer_bwd_layout(B, T, n_seqs, dims, act_dtype).total;
+}
+
+gdn_status gdn_layer_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
+                         const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *a,
+                         const gdn_tensor *b, const gdn_tensor *A_log, const gdn_tensor *dt_bias,
+                         const gdn_tensor *gate, const gdn_tensor *norm_w, const gdn_tensor *cu_seqlens,
+                         const gdn_dims *dims, float scale, int32_t use_qk_l2norm_in_kernel, float l2_eps,
+                         float rms_eps, const gdn_tensor *d_out, const gdn_tensor *dx_q, const gdn_tensor *dx_k,
+                         const gdn_tensor *dx_v, const gdn_tensor *d_conv_w, const gdn_tensor *d_conv_b,
+                         const gdn_tensor *d_a, const gdn_tensor *d_b, const gdn_tensor *d_A_log,
+                         const gdn_tensor *d_dt_bias, const gdn_tensor *d_gate, const gdn_tensor *d_norm_w,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  g_error.clear();
+  TRY(check_dims(dims));
+  if (!x_q || x_q->ndim != 3) return fail(GDN_ERR_INVALID_VALUE, "x_q: expected [B, T, Hqk*dk]");
+  const int64_t B = x_q->shape[0], T = x_q->shape[1];
+  const int32_t act = x_q->dtype;
+  if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "x_q: dtype must be F32, BF16 or F16");
+  if (B * T == 0) return fail(GDN_ERR_INVALID_VALUE, "empty input (B*T == 0)");
+  int64_t n_seqs = 0;
+  if (cu_seqlens) {
+    if (cu_seqlens->ndim != 1 || cu_seqlens->shape[0] < 1)
+      return fail(GDN_ERR_INVALID_VALUE, "cu_seqlens: expected [N+1]");
+    n_seqs = cu_seqlens->shape[0] - 1;
+  }
+  if (!gdn::chunk_bwd_supported(dims->dk, dims->dv))
+    return fail(GDN_ERR_NOT_SUPPORTED, "layer backward: dk=%lld dv=%lld is not instantiated", (long long)dims->dk,
+                (long long)dims->dv);
+  const LayerBwdWs L = layer_bwd_layout(B, T, n_seqs, dims, act);
+  if (!workspace) return fail(GDN_ERR_INVALID_VALUE, "workspace is NULL");
+  if (workspace_bytes < L.total)
+    return fail(GDN_ERR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+  if ((uintptr_t)workspace % 256) return fail(GDN_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+
+  const int64_t Hqk = dims->Hqk, dk = dims->dk, Hv = dims->Hv, dv = dims->dv;
+  const int64_t nq = Hqk * dk, C = 2 * nq + Hv * dv, es = elem_size(act);
+  char *w = static_cast<char *>(workspace);
+  gdn_tensor qkv = {w + L.qkv, act, 3, {B, T, C}, {T * C, C, 1}};
+  gdn_tensor gt = {w + L.g, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
+  gdn_tensor bt = {w + L.beta, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
+  gdn_tensor ot = {w + L.o, act, 4, {B, T, Hv, dv}, {T * Hv * dv, Hv * dv, dv, 1}};
+  gdn_tensor dot = {w + L.d_o, act, 4, {B, T, Hv, dv}, {T * Hv * dv, Hv * dv, dv, 1}};
+  gdn_tensor dqkv = {w + L.dqkv, GDN_F32, 3, {B, T, C}, {T * C, C, 1}};
+  gdn_tensor dgt = {w + L.dg, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
+  gdn_tensor dbt = {w + L.dbeta, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
+  char *qb = w + L.qkv, *db = w + L.dqkv;
+  gdn_tensor qv = {qb, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor kv = {qb + nq * es, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor vv = {qb + 2 * nq * es, act, 4, {B, T, Hv, dv}, {T * C, C, dv, 1}};
+  gdn_tensor dqv = {db, GDN_F32, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor dkv = {db + nq * 4, GDN_F32, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor dvv = {db + 2 * nq * 4, GDN_F32, 4, {B, T, Hv, dv}, {T * C, C, dv, 1}};
+  gdn_tensor wsd = {workspace, GDN_BF16, 1, {(int64_t)(L.total / 2)}, {1}};
+
+  // Plan every stage before launching anything.
+  gdn::PrologueArgs PP;
+  gdn::ChunkArgs PC;
+  gdn::NormBwdArgs PN;
+  gdn::ChunkBwdArgs PB;
+  gdn::PrologueBwdArgs PR;
+  TRY(plan_prologue(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, dims, 0, l2_eps, &qkv, &gt,
+                    &bt, &PP));
+  TRY(plan_chunk(&qv, &kv, &vv, &gt, &bt, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, nullptr, &ot,
+                 nullptr, &PC));
+  TRY(attach_chunk_ws(&PC, L.cfw_n ? w + L.cfw : nullptr, L.cfw_n));
+  TRY(plan_norm_bwd(&ot, gate, norm_w, rms_eps, d_out, &dot, d_gate, d_norm_w, w + L.nbw, L.nbw_n, &PN));
+  TRY(plan_chunk_bwd(&qv, &kv, &vv, &gt, &bt, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, nullptr, &dot,
+                     nullptr, &dqv, &dkv, &dvv, &dgt, &dbt, nullptr, w + L.cbw, L.cbw_n, &PB, true));
+  TRY(plan_prologue_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, dims, &dqkv, &dgt, &dbt,
+                        dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b, d_A_log, d_dt_bias, w + L.pbw, L.pbw_n,
+                        &PR));
+  const gdn_tensor *ins[] = {x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens, d_out};
+  const gdn_tensor *outs[] = {dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b, d_A_log, d_dt_bias, d_gate, d_norm_w};
+  for (auto *t : ins)
+    if (overlaps(&wsd, t)) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps an input");
+  for (size_t i = 0; i < sizeof outs / sizeof outs[0]; ++i) {
+    if (overlaps(&wsd, outs[i])) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps an output");
+    for (auto *t : ins)
+      if (overlaps(outs[i], t)) return fail(GDN_ERR_INVALID_VALUE, "an output overlaps an input");
+    for (size_t j = i + 1; j < sizeof outs / sizeof outs[0]; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(GDN_ERR_INVALID_VALUE, "two outputs overlap");
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  TRY(launched(gdn::launch_prologue(PP, s), "prologue"));
+  TRY(launched(gdn::launch_chunk_rule(PC, s), "chunk rule"));
+  TRY(launched(gdn::launch_gated_norm_bwd(PN, s), "gated norm backward"));
+  TRY(launched(gdn::launch_chunk_bwd(PB, s), "chunk rule backward"));
+  return launched(gdn::launch_prologue_bwd(PR, s), "prologue backward");
 }
 
 size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *dims,

@@ -169,7 +169,8 @@ struct ChunkBwdArgs {
   int64_t n_seqs;             // B when dense
   const float *init_state;    // [N, Hv, dv, dk] or null
   const float *d_final;       // [N, Hv, dv, dk] or null
-  void *dqq, *dkk, *dvv;       // contiguous [B, T, H, d], grad_dtype
+  void *dqq, *dkk, *dvv;       // [B, T, H, d], grad_dtype, head stride d, inner 1
+  int64_t sdq_b, sdq_t, sdk_b, sdk_t, sdv_b, sdv_t;
   float *dg, *dbeta;          // [B, T, Hv] contiguous
   float *d_init;              // [N, Hv, dv, dk] or null
   int64_t B, T, Hqk, dk, Hv, dv;

@@ -76,8 +76,14 @@ def lib() -> ctypes.CDLL:
                                                          ctypes.POINTER(GdnDims)]
         L.gdn_chunk_rule_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_chunk_rule_bwd.argtypes = [P] * 5 + [f32, i32, f32] + [P] * 10 + [vp, ctypes.c_size_t, vp]
+        L.gdn_layer_bwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                    ctypes.POINTER(GdnDims), i32]
+        L.gdn_layer_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_layer_bwd.argtypes = ([P] * 12 + [ctypes.POINTER(GdnDims), f32, i32, f32, f32] + [P] * 12 +
+                                    [vp, ctypes.c_size_t, vp])
         for name in ("gdn_prologue_fwd", "gdn_chunk_rule_fwd", "gdn_gated_norm_fwd", "gdn_layer_fwd",
-                     "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_prologue_bwd", "gdn_chunk_rule_bwd"):
+                     "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_prologue_bwd", "gdn_chunk_rule_bwd",
+                     "gdn_layer_bwd"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -315,6 +321,42 @@ def gdn_chunk_rule_bwd(q, k, v, g, beta, d_o, scale: float, use_qk_l2norm_in_ker
                                     float(l2_eps), *[_p(d) for d in E], ctypes.c_void_p(workspace.data_ptr()),
                                     ctypes.c_size_t(workspace.numel()), _stream(q)))
     return dq, dkk, dvv, dg, db, dh0
+
+
+def gdn_layer_bwd_workspace_bytes(B: int, T: int, dims: Sequence[int], dtype: torch.dtype,
+                                  n_seqs: int = 0) -> int:
+    gd = dims_of(*dims)
+    return int(lib().gdn_layer_bwd_workspace_bytes(int(B), int(T), int(n_seqs), ctypes.byref(gd), DTYPE[dtype]))
+
+
+def gdn_layer_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens,
+                  dims: Sequence[int], scale: float, d_out, use_qk_l2norm_in_kernel: bool = True,
+                  l2_eps: float = 1e-6, rms_eps: float = 1e-5, workspace=None):
+    """Gradients of gdn_layer_fwd. Returns (dx_q, dx_k, dx_v, d_conv_w, d_conv_b or None, d_a, d_b,
+    d_A_log, d_dt_bias, d_gate, d_norm_w)."""
+    Hqk, dk, Hv, dv = dims
+    B, T = x_q.shape[0], x_q.shape[1]
+    C = 2 * Hqk * dk + Hv * dv
+    dev, dt = x_q.device, x_q.dtype
+    e = lambda *shape, d=dt: torch.empty(shape, dtype=d, device=dev)  # noqa: E731
+    dxq, dxk, dxv = e(B, T, Hqk * dk), e(B, T, Hqk * dk), e(B, T, Hv * dv)
+    dw = e(C, 4, d=torch.float32)
+    dbias = e(C, d=torch.float32) if conv_b is not None else None
+    da, db = e(B, T, Hv), e(B, T, Hv)
+    dal, ddt = e(Hv, d=torch.float32), e(Hv, d=torch.float32)
+    dgate = e(B, T, Hv, dv, d=gate.dtype)
+    dnw = e(dv, d=torch.float32)
+    if workspace is None:
+        n_seqs = 0 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+        workspace = _ws(gdn_layer_bwd_workspace_bytes(B, T, dims, dt, n_seqs), dev)
+    gd = dims_of(Hqk, dk, Hv, dv)
+    D = [desc(t) for t in (x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens)]
+    E = [desc(t) for t in (d_out, dxq, dxk, dxv, dw, dbias, da, db, dal, ddt, dgate, dnw)]
+    _check(lib().gdn_layer_bwd(*[_p(d) for d in D], ctypes.byref(gd), float(scale),
+                               int(bool(use_qk_l2norm_in_kernel)), float(l2_eps), float(rms_eps),
+                               *[_p(d) for d in E], ctypes.c_void_p(workspace.data_ptr()),
+                               ctypes.c_size_t(workspace.numel()), _stream(x_q)))
+    return dxq, dxk, dxv, dw, dbias, da, db, dal, ddt, dgate, dnw
 
 
 def dtype_name(t: torch.dtype) -> str:

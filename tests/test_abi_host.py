@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
                      "gdn_chunk_rule_workspace_bytes", "gdn_gated_norm_fwd", "gdn_layer_workspace_bytes",
                      "gdn_layer_fwd", "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_gated_norm_bwd_workspace_bytes",
                      "gdn_prologue_bwd", "gdn_prologue_bwd_workspace_bytes", "gdn_chunk_rule_bwd",
-                     "gdn_chunk_rule_bwd_workspace_bytes"}
+                     "gdn_chunk_rule_bwd_workspace_bytes", "gdn_layer_bwd", "gdn_layer_bwd_workspace_bytes"}
     L = gdn.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -289,6 +289,28 @@ def test_chunk_rule_bwd_workspace_bytes_and_rejections():
     _expect(UNSUPPORTED, "dk=512", gdn.gdn_chunk_rule_bwd, q2, k2, v2, g2, b2, do2, 0.0625)
     q3, k3, v3, g3, b3, do3 = _rule_bwd_inputs(dv=8)
     _expect(UNSUPPORTED, "dv=8", gdn.gdn_chunk_rule_bwd, q3, k3, v3, g3, b3, do3, 0.125)
+
+
+def test_layer_bwd_workspace_bytes_and_rejections():
+    # the layer backward holds the forward's stage outputs, the chunk forward's
+    # workspace, d_o, d_qkv (FP32), dg, dbeta and the three backward workspaces
+    dims = (2, 64, 4, 64)
+    n = gdn.gdn_layer_bwd_workspace_bytes(1, 100, dims, torch.bfloat16)
+    assert n > gdn.gdn_chunk_rule_bwd_workspace_bytes(1, 100, dims) + 100 * (2 * 128 + 256) * 4
+    assert gdn.gdn_layer_bwd_workspace_bytes(1, 100, (1, 512, 1, 64), torch.bfloat16) == 0
+    x = _prologue_inputs()
+    B, T, Hv, dv = 1, 8, 4, 64
+    gate = torch.zeros(B, T, Hv, dv, dtype=torch.bfloat16)
+    nw = torch.ones(dv, dtype=torch.bfloat16)
+    d_out = torch.zeros(B, T, Hv, dv, dtype=torch.bfloat16)
+    args = [x[k] for k in ("x_q", "x_k", "x_v", "conv_w", "conv_b", "a", "b", "A_log", "dt_bias")]
+    _expect(INVALID, "workspace too small", gdn.gdn_layer_bwd, *args, gate, nw, x["cu_seqlens"], x["dims"], 0.125,
+            d_out, workspace=torch.zeros(16, dtype=torch.uint8))
+    nb = gdn.gdn_layer_bwd_workspace_bytes(B, T, x["dims"], torch.bfloat16)
+    raw = torch.zeros(nb + 256, dtype=torch.uint8)
+    off = (-raw.data_ptr()) % 256
+    _expect(INVALID, "dout: dtype", gdn.gdn_layer_bwd, *args, gate, nw, x["cu_seqlens"], x["dims"], 0.125,
+            d_out.half(), workspace=raw[off:off + nb])
 
 
 def test_bench_refuses_more_than_one_gpu():
