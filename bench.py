@@ -254,8 +254,28 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None) -> 
         nbytes = per_tok * ntok
         out[name] = {"ms": ms, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
                      "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    if all(out.get(n, {}).get("ms") for n in ("gated_norm_bwd", "chunk_rule_bwd", "prologue_bwd")):
-        out["layer_core_bwd_ms"] = sum(out[n]["ms"] for n in ("gated_norm_bwd", "chunk_rule_bwd", "prologue_bwd"))
+    if s.dk in (64, 128, 256):
+        # the whole layer-core backward in one call (its forward stages recomputed)
+        scale = rule[5] if rule is not None else s.dk ** -0.5
+        n_seqs = 0 if d["cu_seqlens"] is None else d["cu_seqlens"].shape[0] - 1
+        lws = torch.empty(gdn.gdn_layer_bwd_workspace_bytes(s.B, s.T, dims_t, dout.dtype, n_seqs),
+                          dtype=torch.uint8, device="cuda")
+
+        def layer_b():
+            gdn.gdn_layer_bwd(d["x_q"], d["x_k"], d["x_v"], d["conv_w"], None, d["a"], d["b"], d["A_log"],
+                              d["dt_bias"], d["gate"], d["norm_w"], d["cu_seqlens"], dims, scale, dout, workspace=lws)
+
+        for _ in range(warmup):
+            layer_b()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            layer_b()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["layer_core_bwd_ms"] = e0.elapsed_time(e1) / steps
+        del lws
     return out
 
 
