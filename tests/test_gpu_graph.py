@@ -95,3 +95,46 @@ def test_decode_graph_replays_advance_the_state():
         torch.cuda.synchronize()
         assert torch.equal(og, eager[i]), f"replay {i}"
     assert torch.equal(sg, se) and torch.equal(cg, ce)
+
+
+@pytest.mark.parametrize("cfg,over", [(2, {"T": 150, "Hqk": 1, "Hv": 2}), (4, {"lengths": (5, 70, 1, 64),
+                                                                             "Hqk": 1, "Hv": 2})],
+                         ids=["bf16-gqa", "fp16-packed"])
+def test_layer_bwd_graph_replays_equal_eager(cfg, over):
+    """The whole layer-core backward (its forward recomputed, then the three
+    backward stages, every partial sum in the caller's workspace) captured
+    once and replayed; every gradient of every replay equals the eager call."""
+    s = synth.spec(cfg).replace(**over)
+    x = H.to_dev(synth.make_inputs(s))
+    dims = (s.Hqk, s.dk, s.Hv, s.dv)
+    dt = synth.TORCH_DTYPE[s.act]
+    n_seqs = 0 if x["cu_seqlens"] is None else x["cu_seqlens"].shape[0] - 1
+    ws = torch.empty(gdn.gdn_layer_bwd_workspace_bytes(s.B, s.T, dims, dt, n_seqs), dtype=torch.uint8,
+                     device="cuda")
+    d_out = synth.randn((s.B, s.T, s.Hv, s.dv), s.act, 700 + cfg).cuda()
+
+    def run():
+        return gdn.gdn_layer_bwd(x["x_q"], x["x_k"], x["x_v"], x["conv_w"], None, x["a"], x["b"], x["A_log"],
+                                 x["dt_bias"], x["gate"], x["norm_w"], x["cu_seqlens"], dims, s.dk ** -0.5, d_out,
+                                 workspace=ws)
+
+    eager = [t.clone() for t in run() if t is not None]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = [t for t in run() if t is not None]
+    for i in range(3):
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), f"replay {i}: gradient {j} differs from the eager call"
+        run()  # eager work between replays
+        torch.cuda.synchronize()
