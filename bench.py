@@ -192,7 +192,7 @@ def chunk_bwd_flops(s) -> float:
     return chunks * s.Hv * per
 
 
-def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None) -> dict:
+def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None, layer=True) -> dict:
     """The backward calls at the workload's shape: per-call HIP events on the
     current stream, mean over `steps` calls. The gated norm and the prologue
     are priced against the HBM roof (algorithmic bytes per token: norm
@@ -254,7 +254,7 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None) -> 
         nbytes = per_tok * ntok
         out[name] = {"ms": ms, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
                      "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    if s.dk in (64, 128, 256):
+    if layer and s.dk in (64, 128, 256):
         # the whole layer-core backward in one call (its forward stages recomputed)
         scale = rule[5] if rule is not None else s.dk ** -0.5
         n_seqs = 0 if d["cu_seqlens"] is None else d["cu_seqlens"].shape[0] - 1
@@ -370,6 +370,9 @@ def main() -> int:
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-whole-layer", action="store_true",
                     help="skip the whole-layer leg (projection GEMMs + layer core)")
+    ap.add_argument("--no-layer-bwd", action="store_true",
+                    help="skip the one-call layer-core backward (its prologue backward reads an FP32 d_qkv, "
+                         "so per-kernel counter averages would mix two workloads)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -514,7 +517,7 @@ def main() -> int:
     if not args.no_backward:
         print("[bench] backward leg", file=sys.stderr, flush=True)
         backward = backward_leg(gdn, synth, torch, s, d, o, dims, args.steps, args.warmup,
-                                rule=(qv, kv, vv, g, beta, scale))
+                                rule=(qv, kv, vv, g, beta, scale), layer=not args.no_layer_bwd)
 
     whole = None
     if not args.no_whole_layer:
