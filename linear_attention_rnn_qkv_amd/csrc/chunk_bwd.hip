@@ -737,7 +737,7 @@ __global__ __launch_bounds__(grad_threads<DK>()) void bwd_grad_kernel(ChunkBwdAr
     float z[BT * ZP];  // a + p, for its column sums
   } u;
   __shared__ float sgam[BT], seg[BT], scw[BT], sbeta[BT];
-  __shared__ float vrow[BT], vm[BT], vb[BT], red[NT];
+  __shared__ float vrow[BT], vm[BT], vb[BT], red[NT / 64];
   const int tid = threadIdx.x, rg = tid / CG, cg = tid % CG;
   const int r0 = 4 * rg, c0 = CCN * cg, j0c = NJ * cg;
   const int64_t gc = blockIdx.x, hk = blockIdx.y;
@@ -878,7 +878,10 @@ __global__ __launch_bounds__(grad_threads<DK>()) void bwd_grad_kernel(ChunkBwdAr
         vm[r0 + r] = rm[r];
         vb[r0 + r] = roww[r];
       }
-    red[tid] = sdot;
+    {  // per-wave total of <dS, S0>
+      const float a = group_sum<64>(sdot);
+      if ((tid & 63) == 0) red[tid >> 6] = a;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = r0 + r;
@@ -898,7 +901,7 @@ __global__ __launch_bounds__(grad_threads<DK>()) void bwd_grad_kernel(ChunkBwdAr
       float colz = 0.f;
       for (int s = 0; s < BT; ++s) colz += u.z[s * ZP + t];
       float tot = 0.f;
-      for (int i = 0; i < NT; ++i) tot += red[i];
+      for (int i = 0; i < NT / 64; ++i) tot += red[i];
       float sm = 0.f;
       for (int s = 0; s < BT; ++s) sm += vm[s];
       float dgam = vrow[t] - colz;
