@@ -262,7 +262,7 @@ __device__ __forceinline__ void serial_ids(const ChunkBwdArgs &p, int64_t &j0, i
 template <int D>
 __device__ __forceinline__ void copy_rows(float *dst, int ld, const float *src) {
   constexpr int Q = D / 4;
-  for (int e = threadIdx.x; e < BT * Q; e += kThreads) {
+  for (int e = threadIdx.x; e < BT * Q; e += blockDim.x) {
     const int t = e / Q, j = 4 * (e % Q);
     *reinterpret_cast<fv4 *>(dst + t * ld + j) = *reinterpret_cast<const fv4 *>(src + t * D + j);
   }
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kSer) void bwd_states_kernel(ChunkBwdArgs p) {
     }
     __syncthreads();
     if (c + 1 < nch) fetch(c + 1);
-    // KS = K S0^T (contraction over dk, a quarter per wave); R = V - exp(gamma) KS
+    // KS = K S0^T (contraction over dk, an eighth per wave); R = V - exp(gamma) KS
     {
       float acc[4][4];
       zero(acc);
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(kSer) void bwd_states_kernel(ChunkBwdArgs p) {
       stv<2>(sX + et * 16 + ei, X);
     }
     __syncthreads();
-    // Delta = M X (contraction over s, 16 per wave)
+    // Delta = M X (contraction over s, 8 per wave)
     {
       float acc[4][4];
       zero(acc);
