@@ -564,20 +564,29 @@ gdn_status plan_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_
   return GDN_OK;
 }
 
-constexpr int64_t kBwdTile = 256;  // tokens per tile of the prologue backward
+// Tokens per tile of the prologue backward: 256, halved down to 32 while the
+// conv launch (one 256-thread block per 1024 channels and tile) would have
+// fewer than 2048 blocks, eight per CU.
+int64_t prologue_bwd_tile(int64_t ntok, int64_t C) {
+  const int64_t chb = (C / 4 + 255) / 256;
+  int64_t tile = 256;
+  while (tile > 32 && ((ntok + tile - 1) / tile) * chb < 2048) tile /= 2;
+  return tile;
+}
 
 // Workspace of the prologue backward: per token tile, partial sums of d_conv_w
 // [C][4] and d_conv_b [C]; per head tile (4096 / Hv tokens), of d_dt_bias and
 // d_A_log [Hv]; then the reduction scratch [32][C * 4].
 struct ProBwdWs {
-  int64_t ntiles, head_tile, nhtiles;
+  int64_t tile, ntiles, head_tile, nhtiles;
   size_t w, b, h, mid;  // byte sizes of the regions, each 256-byte aligned
   size_t total() const { return w + b + 2 * h + mid; }
 };
 ProBwdWs prologue_bwd_layout(int64_t B, int64_t T, const gdn_dims *d) {
   ProBwdWs L;
   const int64_t ntok = B * T, C = 2 * d->Hqk * d->dk + d->Hv * d->dv;
-  L.ntiles = (ntok + kBwdTile - 1) / kBwdTile;
+  L.tile = prologue_bwd_tile(ntok, C);
+  L.ntiles = (ntok + L.tile - 1) / L.tile;
   L.head_tile = d->Hv <= 4096 ? 4096 / d->Hv : 1;
   L.nhtiles = (ntok + L.head_tile - 1) / L.head_tile;
   L.w = align256((size_t)(L.ntiles * C * 4 * 4));
@@ -710,7 +719,7 @@ gdn_status plan_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const
   p.d_A_log = static_cast<float *>(d_A_log->data);
   p.d_dt_bias = static_cast<float *>(d_dt_bias->data);
   const ProBwdWs L = prologue_bwd_layout(B, T, dims);
-  p.tile_tokens = kBwdTile;
+  p.tile_tokens = L.tile;
   p.ntiles = L.ntiles;
   p.head_tile = L.head_tile;
   p.nhtiles = L.nhtiles;
