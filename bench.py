@@ -169,11 +169,11 @@ def decode_leg(gdn, synth, torch, s, d, dims, scale, N, steps, warmup) -> dict:
 # The pages' whole-layer shapes (flash-linear-attention GatedDeltaNet with
 # num_heads=6, expand_v=2; page "fused q/k/v short conv", Benchmark /
 # Performance) and their B200 forward times with the fused conv, as context.
-WHOLE_LAYER_SHAPES = [  # (B, T, hidden, head_dim, act, B200 fwd ms)
-    (2, 2048, 2048, 256, "bf16", 1.540),
-    (1, 128, 512, 64, "bf16", 1.493),
-    (2, 100, 512, 64, "bf16", 1.486),
-    (2, 256, 512, 64, "f16", 1.488),
+WHOLE_LAYER_SHAPES = [  # (B, T, hidden, head_dim, act, B200 fused fwd ms, B200 fused fwd+bwd ms)
+    (2, 2048, 2048, 256, "bf16", 1.540, 4.084),
+    (1, 128, 512, 64, "bf16", 1.493, 4.066),
+    (2, 100, 512, 64, "bf16", 1.486, 4.088),
+    (2, 256, 512, 64, "f16", 1.488, 4.095),
 ]
 
 
@@ -282,13 +282,15 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None, lay
 def whole_layer_leg(gdn, synth, torch) -> list:
     """The whole layer forward: one input-projection GEMM to the fused
     q|k|v|gate|b|a buffer, the layer core on views of it, the output-projection
-    GEMM. The GEMMs are plain library GEMMs (torch.matmul, which runs
+    GEMM; and forward + backward (fwdbwd_ms): the backward of a summed output
+    through the output GEMM, gdn_layer_bwd, and the input GEMM's input and
+    weight gradients. The GEMMs are plain library GEMMs (torch.matmul, which runs
     hipBLASLt/rocBLAS); the core is this library. Timed like the pages'
     script: untimed calls, then per-call HIP events with the caches flushed by
     a 512 MB write before each call, median of 200 calls."""
     res = []
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    for i, (B, T, Hd, hd, act, b200) in enumerate(WHOLE_LAYER_SHAPES):
+    for i, (B, T, Hd, hd, act, b200, b200_fb) in enumerate(WHOLE_LAYER_SHAPES):
         Hqk, dk, Hv, dv = 6, hd, 6, 2 * hd
         nq, nv = Hqk * dk, Hv * dv
         C = 2 * nq + nv
@@ -347,13 +349,44 @@ def whole_layer_leg(gdn, synth, torch) -> list:
             ts.sort()
             return ts[len(ts) // 2]
 
+        # forward and backward of the layer, as the pages' fwd+bwd timing runs
+        # layer(x).sum().backward(): d(sum) = 1 at the output; the backward
+        # recomputes the core's forward (gdn_layer_bwd), then the projection
+        # GEMMs' input and weight gradients
+        lws = torch.empty(gdn.gdn_layer_bwd_workspace_bytes(B, T, dims, dt), dtype=torch.uint8, device="cuda")
+        w_in_t, w_out_t = w_in.t().contiguous(), w_out.t().contiguous()
+        x_t = x.flatten(0, 1).t().contiguous()
+        d_y = torch.ones((B, T, Hd), dtype=dt, device="cuda")
+
+        def fwdbwd():
+            proj = torch.matmul(x, w_in)
+            o = 0
+            xq = proj[..., o:o + nq]; o += nq
+            xk = proj[..., o:o + nq]; o += nq
+            xv = proj[..., o:o + nv]; o += nv
+            gate = proj[..., o:o + nv].unflatten(-1, (Hv, dv)); o += nv
+            b = proj[..., o:o + Hv]; o += Hv
+            a = proj[..., o:o + Hv]
+            gdn.gdn_layer_fwd(xq, xk, xv, conv_w, None, a, b, A_log, dt_bias, gate, norm_w, None, dims,
+                              dk ** -0.5, workspace=ws, out=core)
+            torch.matmul(core.flatten(-2), w_out)
+            d_core = torch.matmul(d_y, w_out_t).unflatten(-1, (Hv, dv))
+            torch.matmul(core.flatten(0, 1).flatten(-2).t().contiguous(), d_y.flatten(0, 1))  # d w_out
+            g = gdn.gdn_layer_bwd(xq, xk, xv, conv_w, None, a, b, A_log, dt_bias, gate, norm_w, None, dims,
+                                  dk ** -0.5, d_core, workspace=lws)
+            d_proj = torch.cat([g[0], g[1], g[2], g[9].flatten(-2), g[6], g[5]], -1)
+            torch.matmul(d_proj, w_in_t)  # d x
+            torch.matmul(x_t, d_proj.flatten(0, 1))  # d w_in
+
         ms = median_ms(fwd)
+        fb_ms = median_ms(fwdbwd)
         # the layer core alone on the same projection buffer
         proj_buf = torch.matmul(x, w_in)
         core_out = torch.empty((B, T, Hv, dv), dtype=dt, device="cuda")
         core_ms = median_ms(core_call)
         res.append({"shape": f"B{B}-T{T}-H{Hd}-hd{hd}", "dtype": act, "ms": ms, "tokens/s": B * T / (ms * 1e-3),
-                    "pages_b200_fwd_ms": b200, "core_ms": core_ms})
+                    "pages_b200_fwd_ms": b200, "core_ms": core_ms, "fwdbwd_ms": fb_ms,
+                    "pages_b200_fwdbwd_ms": b200_fb})
     return res
 
 
