@@ -119,45 +119,70 @@ def test_chunk_rule_bwd_strided_views_equal_contiguous():
             assert torch.equal(x, y), n
 
 
-def test_chunk_rule_bwd_full_size_sampled_window():
+@pytest.mark.parametrize("where", ["tail", "mid"])
+def test_chunk_rule_bwd_full_size_window(where):
     """The 131072-token workload's shape (16 q/k heads, 32 value heads, dk = dv
-    = 128, BF16) in one call, with d_o zero except on the last 150 tokens.
-    The oracle follows one q/k head and its two value heads: the state after
-    the first T - 250 tokens from the pinned C recurrence, then autograd over
-    the last 250 tokens from that state. The 100 tokens before the nonzero
-    window get their gradients only through the state carried back over
-    chunk boundaries. Inputs are seeded draws (q, k, v ~ N(0, 1); g ~ -U(0.01,
-    0.5); beta ~ U(0.05, 1))."""
+    = 128, BF16) in one call, with d_o zero except on a window of 150 tokens:
+    the sequence's last 150 tokens, or 150 tokens from 70037 (not a multiple
+    of the 64-token chunk). Every token of every head is checked:
+      * tokens [start - 100, end): all five gradients against the oracle
+        (float64 autograd of the token recurrence over [start - 356, end),
+        all heads, from a zero state; the state dropped at start - 356 reaches
+        the compared tokens scaled by at most exp(sum of g over 256 tokens),
+        asserted below 1e-12);
+      * dq is exactly zero outside the window (o_t depends on q_t only);
+      * after the window every gradient is exactly zero (no later d_o);
+      * before start - 100 every gradient is below the carried-decay bound:
+        it reaches token t through the state, scaled by
+        exp(sum of g over [t + 1, start)) <= D_h = exp(sum over the 100 tokens
+        before start), so |grad| <= 1e4 * D_h * (largest gradient).
+    Inputs are seeded draws (q, k, v ~ N(0, 1); g ~ -U(0.01, 0.5);
+    beta ~ U(0.05, 1))."""
     s = synth.spec(3)
     B, T, Hqk, dk, Hv, dv = s.B, s.T, s.Hqk, s.dk, s.Hv, s.dv
+    print(f"[bwd full size] window {where}", flush=True)
     q = synth.randn((B, T, Hqk, dk), "bf16", 500)
     k = synth.randn((B, T, Hqk, dk), "bf16", 501)
     v = synth.randn((B, T, Hv, dv), "bf16", 502)
     g = O.round_to(-synth.uniform((B, T, Hv), 0.01, 0.5, 503), "f32")
     beta = O.round_to(synth.uniform((B, T, Hv), 0.05, 1.0, 504), "f32")
-    W, W1 = 150, 100
-    t1 = T - W - W1
+    W, W1, LEAD = 150, 100, 256
+    start = T - W if where == "tail" else 70037
+    end = start + W
+    assert where == "tail" or start % 64 != 0
+    t1, t0 = start - W1, start - W1 - LEAD
     do = torch.zeros((B, T, Hv, dv), dtype=torch.bfloat16)
-    do[:, T - W:] = synth.randn((B, W, Hv, dv), "bf16", 505)
+    do[:, start:end] = synth.randn((B, W, Hv, dv), "bf16", 505)
     scale = dk ** -0.5
     got = gdn.gdn_chunk_rule_bwd(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(g).float().cuda(),
                                  torch.from_numpy(beta).float().cuda(), do.cuda(), scale)
     torch.cuda.synchronize()
-    hq = 5
-    vh = [2 * hq, 2 * hq + 1]
-    qs, ks = f64(q[:, :, hq:hq + 1]), f64(k[:, :, hq:hq + 1])
-    vs, gs, bs = f64(v[:, :, vh]), g[:, :, vh], beta[:, :, vh]
-    _, S1 = O.gated_delta_rule(qs[:, :t1], ks[:, :t1], vs[:, :t1], gs[:, :t1], bs[:, :t1], scale=scale,
-                               output_final_state=True)
-    ref = OB.chunk_rule_bwd(qs[:, t1:], ks[:, t1:], vs[:, t1:], gs[:, t1:], bs[:, t1:], f64(do[:, t1:, vh]), scale,
-                            True, 1e-6, None, S1)
     dq, dkk, dvv, dg, db, _ = got
+    for n, x in zip(NAMES, got[:5]):
+        assert torch.isfinite(x).all(), n
+    # exact zeros
+    assert not dq[:, :start].any() and not dq[:, end:].any(), "dq outside the window"
+    for n, x in zip(NAMES[:5], (dq, dkk, dvv, dg, db)):
+        assert not x[:, end:].any(), f"{n} after the window"
+    # the oracle over [t0, end), every head
+    lead = np.exp(np.sum(g[0, t0:t1], axis=0))
+    assert float(lead.max()) < 1e-12, lead.max()
+    ref = OB.chunk_rule_bwd(f64(q[:, t0:end]), f64(k[:, t0:end]), f64(v[:, t0:end]), g[:, t0:end],
+                            beta[:, t0:end], f64(do[:, t0:end]), scale)
     tau = TAU["bf16"]
-    H.assert_close(f64(dq[:, t1:, hq:hq + 1]), ref[0], tau, "dq")
-    H.assert_close(f64(dkk[:, t1:, hq:hq + 1]), ref[1], tau, "dk")
-    H.assert_close(f64(dvv[:, t1:, vh]), ref[2], tau, "dv")
-    H.assert_close(f64(dg[:, t1:, vh]), ref[3], tau, "dg")
-    H.assert_close(f64(db[:, t1:, vh]), ref[4], tau, "dbeta")
-    # the carried part alone: tokens before the nonzero window
-    H.assert_close(f64(dvv[:, t1:T - W, vh]), ref[2][:, :W1], tau, "dv before the window")
-    assert float(np.abs(ref[2][:, :W1]).max()) > 0
+    w = slice(t1 - t0, end - t0)
+    for n, x, r in zip(NAMES, (dq, dkk, dvv, dg, db), ref[:5]):
+        H.assert_close(f64(x[:, t1:end]), r[:, w], tau, n)
+    # the carried part alone (tokens before the window), against its own scale
+    for n, x, r in ((NAMES[1], dkk, ref[1]), (NAMES[2], dvv, ref[2])):
+        H.assert_close(f64(x[:, t1:start]), r[:, w][:, :W1], tau, f"{n} before the window")
+    assert float(np.abs(ref[2][:, w][:, :W1]).max()) > 0
+    # carried-decay bound before t1
+    D = np.exp(np.sum(g[0, t1:start], axis=0))  # [Hv]
+    bound = 1e4 * float(D.max())
+    assert bound < 1e-3, bound
+    for n, x, r in zip(NAMES[1:5], (dkk, dvv, dg, db), ref[1:5]):
+        big = float(np.abs(r[:, w]).max())
+        before = x[:, :t1].float().abs()
+        worst = float(before.max()) if before.numel() else 0.0
+        assert worst <= bound * big, (n, worst, bound * big)

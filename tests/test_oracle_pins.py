@@ -343,6 +343,30 @@ def test_gated_norm_matches_library_rms_norm_and_silu():
         np.testing.assert_allclose(got, ref, rtol=2.0 ** -(8 if act == "bf16" else 11), atol=0)
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_gated_norm_materialises_the_norm_in_the_activation_dtype(act):
+    """Reading R6 (the norm result is rounded to the activation dtype before
+    the FP32 gate multiply), pinned exactly. The expected values come from
+    library routines: torch's float64 rms_norm, torch's conversion to the
+    16-bit dtype, torch's silu. Inputs are 16-bit values; the weight is
+    drawn as 16-bit values too. The gate is chosen so that silu(gate) is
+    not a power of two, so rounding the norm result first changes the final
+    rounded output for many elements: an oracle that skipped that rounding
+    (or rounded the gate product only) fails the exact comparison."""
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}[act]
+    rng = np.random.default_rng(606)
+    o = torch.from_numpy(rng.standard_normal((64, 128))).to(dt).double()
+    w = torch.from_numpy(1 + rng.normal(0, 0.02, 128)).to(dt).double()
+    gate = torch.from_numpy(rng.standard_normal((64, 128)) * 3).to(dt).double()
+    y = F.rms_norm(o, (128,), w, eps=1e-5).to(dt).double()       # materialised norm
+    ref = (y * F.silu(gate)).to(dt).double().numpy()
+    got = O.gated_rmsnorm(o.numpy(), gate.numpy(), w.numpy(), 1e-5, act)
+    np.testing.assert_array_equal(got, ref)
+    # the pin has power: without the intermediate rounding the outputs differ
+    skip = (F.rms_norm(o, (128,), w, eps=1e-5) * F.silu(gate)).to(dt).double().numpy()
+    assert np.mean(skip != ref) > 0.05
+
+
 def test_gated_norm_rms_identity_gate_zero_and_scale_invariance():
     o = RNG.standard_normal((4, 3, 32)) * 10.0 ** RNG.integers(-2, 2, (4, 3, 1))
     w = 1 + RNG.normal(0, 0.02, 32)
