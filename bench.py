@@ -108,6 +108,107 @@ def measured_traffic(workload: str, kernel: str):
     return total
 
 
+def quantiles(ts) -> dict:
+    """Median and 20th / 80th percentiles (ms) of per-call times."""
+    ts = sorted(ts)
+    q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]  # noqa: E731
+    return {"median": q(0.5), "p20": q(0.2), "p80": q(0.8)}
+
+
+def mfma_counters(workload: str, kernel: str):
+    """Counter-based MFMA utilisation of a ('+'-joined) stage from the
+    committed rocprofv3 summary of this workload, if it was taken on the
+    kernels' current sources; else None. Per kernel: SQ_VALU_MFMA_BUSY_CYCLES
+    / (GRBM_GUI_ACTIVE x CUs), the fraction of the launch during which the
+    matrix cores were busy; the stage value weights the kernels by their
+    average durations."""
+    from linear_attention_rnn_qkv_amd import profile_summary as ps
+
+    path = os.path.join(ROOT, "profiles", f"mfma_counters.{workload}.json")
+    try:
+        with open(path) as fh:
+            recs = json.load(fh)["kernels"]
+    except (OSError, KeyError, ValueError):
+        return None
+    num = den = 0.0
+    for k in kernel.split("+"):
+        rec = recs.get(k)
+        if rec is None or k not in ps.KERNELS or rec.get("source_hash") != ps.source_hash(k):
+            return None
+        num += rec["mfma_busy"] * rec["avg_us"]
+        den += rec["avg_us"]
+    return num / den if den else None
+
+
+def stage_times(gdn, synth, torch, cfg: int, reps: int, flush_bytes: int = 512 << 20) -> dict:
+    """Per-stage and whole-layer times of workload ``cfg`` (median and
+    quantiles over ``reps`` calls, a 512 MB write before each call so that
+    no stage reads its inputs from the 256 MB Infinity Cache), with bytes and
+    roofline fractions. Used for the workloads beside the headline one."""
+    s = synth.spec(cfg)
+    print(f"[bench] stage times, workload {cfg} {s.name}", file=sys.stderr, flush=True)
+    x = synth.make_inputs(s)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    del x
+    dims = (s.Hqk, s.dk, s.Hv, s.dv)
+    scale = s.dk ** -0.5
+    dt = synth.TORCH_DTYPE[s.act]
+    n_seqs = 0 if d["cu_seqlens"] is None else d["cu_seqlens"].shape[0] - 1
+    ws = torch.empty(gdn.gdn_layer_workspace_bytes(s.B, s.T, dims, dt, n_seqs), dtype=torch.uint8, device="cuda")
+    cws_bytes = gdn.gdn_chunk_rule_workspace_bytes(s.B, s.T, dims, dt, n_seqs)
+    cws = torch.empty(cws_bytes, dtype=torch.uint8, device="cuda") if cws_bytes else None
+    out = torch.empty((s.B, s.T, s.Hv, s.dv), dtype=dt, device="cuda")
+    qkv = torch.empty((s.B, s.T, s.C), dtype=dt, device="cuda")
+    g = torch.empty((s.B, s.T, s.Hv), dtype=torch.float32, device="cuda")
+    beta = torch.empty_like(g)
+    o = torch.empty((s.B, s.T, s.Hv, s.dv), dtype=dt, device="cuda")
+    nq = s.Hqk * s.dk
+    qv = qkv[..., :nq].unflatten(-1, (s.Hqk, s.dk))
+    kv = qkv[..., nq:2 * nq].unflatten(-1, (s.Hqk, s.dk))
+    vv = qkv[..., 2 * nq:].unflatten(-1, (s.Hv, s.dv))
+    calls = {
+        "layer": lambda: gdn.gdn_layer_fwd(d["x_q"], d["x_k"], d["x_v"], d["conv_w"], None, d["a"], d["b"],
+                                           d["A_log"], d["dt_bias"], d["gate"], d["norm_w"], d["cu_seqlens"],
+                                           dims, scale, workspace=ws, out=out),
+        "prologue": lambda: gdn.gdn_prologue_fwd(d["x_q"], d["x_k"], d["x_v"], d["conv_w"], None, d["a"], d["b"],
+                                                 d["A_log"], d["dt_bias"], d["cu_seqlens"], dims, out_qkv=qkv,
+                                                 out_g=g, out_beta=beta),
+        "chunk_rule": lambda: gdn.gdn_chunk_rule_fwd(qv, kv, vv, g, beta, scale, True, 1e-6, d["cu_seqlens"],
+                                                     out_o=o, workspace=cws),
+        "gated_norm": lambda: gdn.gdn_gated_norm_fwd(o, d["gate"], d["norm_w"], 1e-5, out=out),
+    }
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[name] = quantiles(ts)
+    w = stage_work(s)
+    n = s.tokens
+    out_d = {"workload": s.name, "tokens": n, "reps": reps,
+             "layer_ms": res["layer"], "tokens/s": n / (res["layer"]["median"] * 1e-3)}
+    for name, key in (("prologue", "prologue_bytes"), ("chunk_rule", "chunk_bytes"), ("gated_norm", "norm_bytes")):
+        t = res[name]["median"]
+        gb = w[key] * n / (t * 1e-3) / 1e9
+        out_d[name] = {"ms": res[name], "GB/s": gb, "hbm_frac": gb / HBM_PEAK_GBS}
+        if name == "chunk_rule":
+            out_d[name]["TFLOP/s"] = w["chunk_flops"] * n / (t * 1e-3) / 1e12
+            out_d[name]["mfma_frac"] = out_d[name]["TFLOP/s"] / MFMA_PEAK_TFLOPS[s.act]
+    del ws, cws, qkv, o, out, d
+    torch.cuda.empty_cache()
+    return out_d
+
+
 def calibrate_copy(reps: int) -> int:
     """A plain device copy of COPY_BYTES, `reps` times: its byte counters per
     dispatch (which must read COPY_BYTES fetched and written) calibrate the
@@ -406,6 +507,10 @@ def main() -> int:
     ap.add_argument("--no-layer-bwd", action="store_true",
                     help="skip the one-call layer-core backward (its prologue backward reads an FP32 d_qkv, "
                          "so per-kernel counter averages would mix two workloads)")
+    ap.add_argument("--other-workloads", default="2,4",
+                    help="comma-separated workloads whose per-stage fractions are reported beside the headline "
+                         "one (median of --other-reps calls with the caches flushed before each); '' skips")
+    ap.add_argument("--other-reps", type=int, default=30)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -478,13 +583,17 @@ def main() -> int:
     # Timed region: exactly K steps of the layer core.
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        step_ev[i].record(stream)
         layer()
+    step_ev[args.steps].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    step_q = quantiles([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)])
     print(f"[bench] {args.steps} steps: {ms:.4f} ms/step", file=sys.stderr, flush=True)
 
     # Per-stage durations: the same three kernels, one event between each.
@@ -499,6 +608,11 @@ def main() -> int:
         norm()
         e[3].record(stream)
     torch.cuda.synchronize()
+    q_pro = quantiles([e[0].elapsed_time(e[1]) for e in evs])
+    q_chk = quantiles([e[1].elapsed_time(e[2]) for e in evs])
+    q_nrm = quantiles([e[2].elapsed_time(e[3]) for e in evs])
+    # stage time = the average launch duration (as the profiler reports it);
+    # median and quantiles beside it
     t_pro = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     t_chk = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     t_nrm = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
@@ -518,13 +632,14 @@ def main() -> int:
                     "chunk_prep_kernel+chunk_state_wide_kernel" if s.dk == 256 else
                     "chunk_prep_kernel+chunk_state_kernel")
     stages = {
-        "prologue": {"kernel": "prologue_kernel", "ms": t_pro, "bytes": pb, "GB/s": gbs(pb, t_pro),
+        "prologue": {"kernel": "prologue_kernel", "ms": t_pro, "ms_q": q_pro, "bytes": pb, "GB/s": gbs(pb, t_pro),
                      "hbm_frac": gbs(pb, t_pro) / HBM_PEAK_GBS},
-        "chunk_rule": {"kernel": chunk_kernel, "ms": t_chk, "bytes": cb, "flops": cf,
+        "chunk_rule": {"kernel": chunk_kernel, "ms": t_chk, "ms_q": q_chk, "bytes": cb, "flops": cf,
                        "GB/s": gbs(cb, t_chk), "hbm_frac": gbs(cb, t_chk) / HBM_PEAK_GBS,
                        "TFLOP/s": cf / (t_chk * 1e-3) / 1e12,
                        "mfma_frac": cf / (t_chk * 1e-3) / 1e12 / mfma_peak},
-        "gated_norm": {"kernel": "gated_norm_kernel", "ms": t_nrm, "bytes": nb, "GB/s": gbs(nb, t_nrm),
+        "gated_norm": {"kernel": "gated_norm_kernel", "ms": t_nrm, "ms_q": q_nrm, "bytes": nb,
+                       "GB/s": gbs(nb, t_nrm),
                        "hbm_frac": gbs(nb, t_nrm) / HBM_PEAK_GBS},
     }
     # dominant kernel and the roof that bounds it in the ideal
@@ -538,6 +653,10 @@ def main() -> int:
                 "frac": st["hbm_frac"]}
     roof["kernel"] = st["kernel"]
     roof["traffic"] = measured_traffic(s.name, st["kernel"])
+    if dom == "chunk_rule":
+        # matrix-core busy fraction from rocprofv3 counters (None if the
+        # committed counters were taken on other sources)
+        roof["mfma_util"] = mfma_counters(s.name, st["kernel"])
     for v in stages.values():
         v["traffic"] = measured_traffic(s.name, v["kernel"])
 
@@ -552,6 +671,11 @@ def main() -> int:
         backward = backward_leg(gdn, synth, torch, s, d, o, dims, args.steps, args.warmup,
                                 rule=(qv, kv, vv, g, beta, scale), layer=not args.no_layer_bwd)
 
+    others = None
+    if args.other_workloads:
+        others = [stage_times(gdn, synth, torch, int(c), args.other_reps) for c in args.other_workloads.split(",")
+                  if c.strip() and int(c) != args.config]
+
     whole = None
     if not args.no_whole_layer:
         print("[bench] whole-layer leg", file=sys.stderr, flush=True)
@@ -565,6 +689,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_q": step_q,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -574,6 +699,7 @@ def main() -> int:
                    "Hv": s.Hv, "dv": s.dv, "chunk": CHUNK, "conv_taps": 4, "parallelism": "single GPU"},
         "roofline": roof,
         "stages": stages,
+        "other_workloads": others,
         "decode": decode,
         "whole_layer": whole,
         "backward": backward,

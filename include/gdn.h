@@ -172,11 +172,13 @@ gdn_status gdn_prologue_fwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
  *              initial_state (each state is read before it is written)
  *   workspace  device memory of gdn_chunk_rule_workspace_bytes(...) bytes,
  *              256-byte aligned, or NULL. With a workspace, BF16/FP16 inputs
- *              with dk 64 or 128 and 16-byte aligned rows run as two kernels:
- *              a chunk prep that is parallel over (chunk, value head) and
- *              writes T = (I + A)^-1, P and row factors of every chunk to the
- *              workspace, then the serial state pass. Without one (or where
- *              that path does not apply) a single kernel does both. The
+ *              with dk 64 or 128 (dv a multiple of 16) or dk 256 (dv a
+ *              multiple of 32), 16-byte aligned q/k/v rows and 8-byte
+ *              aligned o rows run as two kernels: a chunk prep that is
+ *              parallel over (chunk, value head) and writes T = (I + A)^-1,
+ *              P and row factors of every chunk to the workspace, then the
+ *              serial state pass. Without one (or where that path does not
+ *              apply) a single kernel does both. The
  *              results agree to rounding. A workspace smaller than required
  *              is an error; the memory must not overlap any tensor argument
  *              and must not be used by any other call until this call's work
@@ -196,8 +198,8 @@ gdn_status gdn_chunk_rule_fwd(const gdn_tensor *q, const gdn_tensor *k,
 /* Bytes of chunk workspace for B*T tokens (n_seqs = number of packed
  * sequences with cu_seqlens, 0 without): 4*(N+1) rounded to 256, plus
  * (ceil(T/64) + n_seqs, or B*ceil(T/64)) * Hv records of 14336 bytes.
- * Returns 0 where the two-kernel path does not apply (F32 inputs, dk 256)
- * and for invalid arguments. */
+ * Returns 0 where the two-kernel path does not apply (F32 inputs; dk 256
+ * with dv not a multiple of 32) and for invalid arguments. */
 size_t gdn_chunk_rule_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs,
                                       const gdn_dims *dims, int32_t act_dtype);
 

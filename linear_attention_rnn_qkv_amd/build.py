@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
-SOURCES = ["gdn_api.cpp", "prologue.hip", "chunk_rule.hip", "chunk_rule_v2.hip", "chunk_prep.hip",
+SOURCES = ["gdn_api.cpp", "prologue.hip", "chunk_rule.hip", "chunk_prep.hip",
            "chunk_state.hip", "gated_norm.hip", "decode.hip",
            "chunk_state_wide.hip", "backward.hip", "chunk_bwd.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

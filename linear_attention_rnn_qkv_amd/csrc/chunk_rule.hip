@@ -421,7 +421,6 @@ bool chunk_rule_supported(int64_t dk, int32_t act) {
 hipError_t launch_chunk_rule(const ChunkArgs &a, hipStream_t s) {
   if (a.n_seqs == 0 || a.dv == 0) return hipSuccess;
   if (a.ws_rec && chunk_split_supported(a.dk, a.dv, a.act) && a.rows16 && a.o8) return launch_chunk_split(a, s);
-  if (chunk_rule_v2_supported(a.dk, a.act) && a.rows16) return launch_chunk_rule_v2(a, s);
   switch (a.act) {
     case kF32: return launch_t<float>(a, s);
     case kBF16: return launch_t<bf16>(a, s);

@@ -193,16 +193,12 @@ hipError_t launch_prologue_bwd(const PrologueBwdArgs &a, hipStream_t s);
 // Host-side capability query used by validation (no device calls).
 bool chunk_rule_supported(int64_t dk, int32_t act);
 
-// The wavefront-pipelined chunk kernel (16-bit inputs, dk 64 or 128).
-bool chunk_rule_v2_supported(int64_t dk, int32_t act);
-hipError_t launch_chunk_rule_v2(const ChunkArgs &a, hipStream_t s);
-
 // Two-kernel path: chunk prep (parallel over chunks and heads) then chunk
 // state (serial over chunks). Needs a.ws_rec / a.cu_chunks.
 bool chunk_split_supported(int64_t dk, int64_t dv, int32_t act);
 hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s);
 
-// Backward of the chunk rule (dk 64 or 128, dv a multiple of 16).
+// Backward of the chunk rule (dk 64, 128 or 256, dv a multiple of 16).
 bool chunk_bwd_supported(int64_t dk, int64_t dv);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t s);
 

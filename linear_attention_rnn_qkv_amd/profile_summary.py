@@ -27,8 +27,6 @@ COPY_BYTES = 1 << 30
 
 # kernel symbol fragment -> (short name, sources its machine code is built from)
 KERNELS = {
-    "chunk_rule_v2_kernel": ("chunk_rule_v2_kernel", ["chunk_rule_v2.hip", "mfma_tiles.h", "device_common.h",
-                                                      "gdn_internal.h"]),
     "chunk_prep_kernel": ("chunk_prep_kernel", ["chunk_prep.hip", "mfma_tiles.h", "device_common.h",
                                                 "gdn_internal.h"]),
     "chunk_state_kernel": ("chunk_state_kernel", ["chunk_state.hip", "mfma_tiles.h", "device_common.h",

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_bench_emits_one_json_line_with_roofline_and_cpu_baseline():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "2", "--steps", "2",
-                        "--warmup", "1", "--decode-seqs", "8", "--no-whole-layer", "--cpu-budget", "1"],
+                        "--warmup", "1", "--decode-seqs", "8", "--no-whole-layer", "--cpu-budget", "1",
+                        "--other-workloads", "0", "--other-reps", "3"],
                        capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
@@ -33,5 +34,11 @@ def test_bench_emits_one_json_line_with_roofline_and_cpu_baseline():
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
     assert out["decode"]["seqs"] == 8 and out["decode"]["GB/s"] > 0
     assert set(out["backward"]) == {"gated_norm_bwd", "prologue_bwd", "chunk_rule_bwd", "layer_core_bwd_ms"}
+    q = out["ms_per_step_q"]
+    assert 0 < q["p20"] <= q["median"] <= q["p80"]
+    (other,) = out["other_workloads"]
+    assert other["workload"] == "tiny-fp32" and other["tokens/s"] > 0
+    for st in ("prologue", "chunk_rule", "gated_norm"):
+        assert other[st]["hbm_frac"] > 0 and other[st]["ms"]["median"] > 0
     rb = out["backward"]["chunk_rule_bwd"]
     assert rb["ms"] > 0 and 0 < rb["alu_frac"] <= 1

@@ -34,8 +34,9 @@ SMALL = [
 ]
 IDS = [c[0] for c in SMALL]
 # The recurrence runs as two kernels (chunk prep + chunk state) when given a
-# workspace, as one kernel without; every recurrence test runs both.
-PATHS = {"split": "auto", "fused": None}
+# workspace, as one kernel (chunk_rule_kernel) without; every recurrence test
+# runs both.
+PATHS = {"split": "auto", "one-kernel": None}
 
 
 def _spec(cfg, over):
