@@ -195,6 +195,44 @@ gdn_status gdn_chunk_rule_fwd(const gdn_tensor *q, const gdn_tensor *k,
                               const gdn_tensor *final_state, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/*
+ * gdn_chunk_rule_fwd_noalloc - gdn_chunk_rule_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, arguments and
+ * results as gdn_chunk_rule_fwd with a workspace, except that the chunk
+ * records live in a static device array of GDN_NOALLOC_SCRATCH_BYTES that the
+ * library owns on every device it runs on (from the first call on a device
+ * until the process ends), not in a caller workspace. The call allocates and
+ * frees nothing.
+ *
+ * Limit: gdn_chunk_rule_workspace_bytes(...) for the call's shape must be at
+ * most GDN_NOALLOC_SCRATCH_BYTES (64 MiB: for example 4096 (chunk, value
+ * head) records, 8192 tokens of 32 value heads); a larger call is rejected
+ * with GDN_ERR_INVALID_VALUE before anything is launched (split the sequence
+ * with initial_state / final_state, or pass a workspace to
+ * gdn_chunk_rule_fwd). Where the two-kernel path does not apply (see
+ * gdn_chunk_rule_fwd), the single recurrence kernel runs and no scratch is
+ * used.
+ *
+ * Every call on one device shares that device's scratch: calls whose work
+ * overlaps on one device (different streams, different host threads) race
+ * and must be serialised by the caller. The scratch holds no state between
+ * calls (every call writes what it reads). `stream` must belong to the
+ * current device. A failure to look up the scratch's device address is
+ * GDN_ERR_LAUNCH.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_chunk_rule_fwd_noalloc(const gdn_tensor *q, const gdn_tensor *k,
+                                      const gdn_tensor *v, const gdn_tensor *g,
+                                      const gdn_tensor *beta, float scale,
+                                      int32_t use_qk_l2norm_in_kernel,
+                                      float l2_eps,
+                                      const gdn_tensor *cu_seqlens,
+                                      const gdn_tensor *initial_state,
+                                      const gdn_tensor *out_o,
+                                      const gdn_tensor *final_state,
+                                      void *stream);
+
 /* Bytes of chunk workspace for B*T tokens (n_seqs = number of packed
  * sequences with cu_seqlens, 0 without): 4*(N+1) rounded to 256, plus
  * (ceil(T/64) + n_seqs, or B*ceil(T/64)) * Hv records of 14336 bytes.

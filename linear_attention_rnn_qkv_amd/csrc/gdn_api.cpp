@@ -1027,6 +1027,31 @@ gdn_status gdn_chunk_rule_fwd(const gdn_tensor *q, const gdn_tensor *k, const gd
   return launched(gdn::launch_chunk_rule(P, (hipStream_t)stream), "chunk rule");
 }
 
+gdn_status gdn_chunk_rule_fwd_noalloc(const gdn_tensor *q, const gdn_tensor *k, const gdn_tensor *v,
+                                      const gdn_tensor *g, const gdn_tensor *beta, float scale,
+                                      int32_t use_qk_l2norm_in_kernel, float l2_eps,
+                                      const gdn_tensor *cu_seqlens, const gdn_tensor *initial_state,
+                                      const gdn_tensor *out_o, const gdn_tensor *final_state, void *stream) {
+  g_error.clear();
+  gdn::ChunkArgs P;
+  TRY(plan_chunk(q, k, v, g, beta, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, initial_state, out_o,
+                 final_state, &P));
+  const int64_t ns = P.cu_seqlens ? P.n_seqs : 0;
+  const size_t need = chunk_ws_bytes(P.B, P.T, ns, P.dk, P.Hv, P.dv, P.act);
+  if (need > 0 && P.rows16 && P.o8) {  // the two-kernel path applies: records in the static scratch
+    if (need > GDN_NOALLOC_SCRATCH_BYTES)
+      return fail(GDN_ERR_INVALID_VALUE,
+                  "chunk records need %zu bytes, more than the %zu bytes of static scratch; split the "
+                  "sequence (initial_state / final_state) or call gdn_chunk_rule_fwd with a workspace",
+                  need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    void *scr = nullptr;
+    const hipError_t e = gdn::static_scratch(&scr);
+    if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "static scratch: %s", hipGetErrorString(e));
+    TRY(attach_chunk_ws(&P, scr, (size_t)GDN_NOALLOC_SCRATCH_BYTES));
+  }
+  return launched(gdn::launch_chunk_rule(P, (hipStream_t)stream), "chunk rule");
+}
+
 size_t gdn_chunk_rule_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *dims,
                                       int32_t act_dtype) {
   if (!dims || B < 0 || T < 0 || n_seqs < 0 || !is_act(act_dtype)) return 0;

@@ -202,6 +202,10 @@ hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s);
 bool chunk_bwd_supported(int64_t dk, int64_t dv);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t s);
 
+// Device address of the static chunk scratch (GDN_NOALLOC_SCRATCH_BYTES) on
+// the current device; looked up once per device.
+hipError_t static_scratch(void **out);
+
 // cuc[n] = sum over sequences m < n of ceil(len_m / 64), for n in [0, n_seqs].
 hipError_t launch_chunk_index(const int32_t *cu, int64_t n_seqs, int32_t *cuc, hipStream_t s);
 

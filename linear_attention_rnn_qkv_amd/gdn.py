@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_VALUE, GDN_ERR_NOT_SUPPORTED, GDN_ERR_LAUNCH = 0, 1, 2, 3
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20  # static chunk scratch of gdn_chunk_rule_fwd_noalloc (gdn.h)
 DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2, torch.int32: 3}
 _NAMES = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
 
@@ -56,6 +57,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_version.restype = ctypes.c_char_p
         L.gdn_prologue_fwd.argtypes = [P] * 10 + [ctypes.POINTER(GdnDims), i32, f32, P, P, P, vp]
         L.gdn_chunk_rule_fwd.argtypes = [P, P, P, P, P, f32, i32, f32, P, P, P, P, vp, ctypes.c_size_t, vp]
+        L.gdn_chunk_rule_fwd_noalloc.argtypes = [P, P, P, P, P, f32, i32, f32, P, P, P, P, vp]
         L.gdn_chunk_rule_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                      ctypes.POINTER(GdnDims), i32]
         L.gdn_chunk_rule_workspace_bytes.restype = ctypes.c_size_t
@@ -188,6 +190,22 @@ def gdn_chunk_rule_fwd(q, k, v, g, beta, scale: float, use_qk_l2norm_in_kernel: 
     _check(lib().gdn_chunk_rule_fwd(*[_p(d) for d in D], float(scale),
                                     int(bool(use_qk_l2norm_in_kernel)), float(l2_eps),
                                     *[_p(d) for d in E], wptr, wlen, _stream(q)))
+    return out_o, final_state
+
+
+def gdn_chunk_rule_fwd_noalloc(q, k, v, g, beta, scale: float, use_qk_l2norm_in_kernel: bool = True,
+                               l2_eps: float = 1e-6, cu_seqlens=None, initial_state=None, out_o=None,
+                               final_state=None):
+    """gdn_chunk_rule_fwd with the chunk records in the library's static
+    device scratch (the C call allocates nothing; outputs are the caller's).
+    Returns (o, final_state or None)."""
+    if out_o is None:
+        out_o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    D = [desc(t) for t in (q, k, v, g, beta)]
+    E = [desc(t) for t in (cu_seqlens, initial_state, out_o, final_state)]
+    _check(lib().gdn_chunk_rule_fwd_noalloc(*[_p(d) for d in D], float(scale),
+                                            int(bool(use_qk_l2norm_in_kernel)), float(l2_eps),
+                                            *[_p(d) for d in E], _stream(q)))
     return out_o, final_state
 
 

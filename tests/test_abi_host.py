@@ -24,7 +24,8 @@ def test_exports_every_declared_symbol():
                      "gdn_chunk_rule_workspace_bytes", "gdn_gated_norm_fwd", "gdn_layer_workspace_bytes",
                      "gdn_layer_fwd", "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_gated_norm_bwd_workspace_bytes",
                      "gdn_prologue_bwd", "gdn_prologue_bwd_workspace_bytes", "gdn_chunk_rule_bwd",
-                     "gdn_chunk_rule_bwd_workspace_bytes", "gdn_layer_bwd", "gdn_layer_bwd_workspace_bytes"}
+                     "gdn_chunk_rule_bwd_workspace_bytes", "gdn_layer_bwd", "gdn_layer_bwd_workspace_bytes",
+                     "gdn_chunk_rule_fwd_noalloc"}
     L = gdn.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -332,3 +333,19 @@ def test_binding_has_no_cpu_path():
     # neither the oracle nor any fallback
     src = open(os.path.join(ROOT, "linear_attention_rnn_qkv_amd", "gdn.py")).read()
     assert "oracle" not in src and "numpy" not in src
+
+
+def test_noalloc_rejects_inputs_beyond_the_static_scratch():
+    # 80 chunks x 64 value heads of 14336-byte records exceed the 64 MiB
+    # scratch: rejected from metadata before any device call
+    T, Hqk, dk, Hv, dv = 80 * 64, 1, 64, 64, 16
+    z = lambda *s, d=torch.bfloat16: torch.zeros(*s, dtype=d)  # noqa: E731
+    need = gdn.gdn_chunk_rule_workspace_bytes(1, T, (Hqk, dk, Hv, dv), torch.bfloat16)
+    assert need > gdn.GDN_NOALLOC_SCRATCH_BYTES
+    _expect(INVALID, "static scratch", gdn.gdn_chunk_rule_fwd_noalloc, z(1, T, Hqk, dk), z(1, T, Hqk, dk),
+            z(1, T, Hv, dv), z(1, T, Hv, d=torch.float32), z(1, T, Hv, d=torch.float32), 0.125,
+            out_o=z(1, T, Hv, dv))
+    # and the ordinary validation runs first
+    _expect(INVALID, "powers of two", gdn.gdn_chunk_rule_fwd_noalloc, z(1, T, Hqk, dk + 1), z(1, T, Hqk, dk),
+            z(1, T, Hv, dv), z(1, T, Hv, d=torch.float32), z(1, T, Hv, d=torch.float32), 0.125,
+            out_o=z(1, T, Hv, dv))
