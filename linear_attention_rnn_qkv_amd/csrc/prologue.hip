@@ -33,8 +33,6 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 128;      // tokens per block
-constexpr int kSmallTile = 16;  // tokens per block when the launch would have few blocks
 constexpr int kUnroll = 8;   // tokens per load batch
 
 template <typename TW>
@@ -62,7 +60,7 @@ template <typename T>
 __device__ void beta_g_tile(const PrologueArgs &p, int64_t b, int64_t t0, int64_t lo, int64_t hi) {
   const T *pa = static_cast<const T *>(p.a);
   const T *pb = static_cast<const T *>(p.b);
-  for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) {
+  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) {
     const int64_t t = t0 + i / p.Hv, h = i % p.Hv;
     const float bb = f(pb[b * p.sb_b + t * p.sb_t + h * p.sb_h]);
     const float aa = f(pa[b * p.sa_b + t * p.sa_t + h * p.sa_h]);
@@ -81,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs p) {
   const int64_t b = blockIdx.z;
   const int64_t t0 = (int64_t)blockIdx.x * TILE;
   const int64_t t1 = t0 + TILE < p.T ? t0 + TILE : p.T;
-  const int64_t c0 = ((int64_t)cb * kThreads + threadIdx.x) * VEC;
+  const int64_t c0 = ((int64_t)cb * blockDim.x + threadIdx.x) * VEC;
   const bool active = c0 < p.C;
   const int64_t nq = p.Hqk * p.dk;
 
@@ -129,10 +127,18 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs p) {
   int64_t bos = 0, next = LLONG_MAX, idx = 0;
   const int32_t *cu = p.cu_seqlens;
   if (cu) {
-    int64_t lo = 0, hi = p.n_seqs;  // invariant: cu[lo] <= t0
-    while (hi - lo > 1) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (cu[mid] <= t0) lo = mid; else hi = mid;
+    // the last lo with cu[lo] <= t0 (cu[0] = 0 <= t0): 64 strided samples
+    // per round, one memory round trip each, the interval narrowed by the
+    // count of samples <= t0 (cu is nondecreasing)
+    int64_t lo = 0, end = p.n_seqs + 1;  // candidates lo .. end - 1
+    const int lane = threadIdx.x & 63;
+    while (end - lo > 1) {
+      const int64_t step = (end - lo + 63) / 64;
+      const int64_t at = lo + lane * step;
+      const bool le = at < end && cu[at] <= t0;
+      const int cnt = __popcll(__ballot(le));  // >= 1: cu[lo] <= t0
+      lo += (int64_t)(cnt - 1) * step;
+      end = lo + step < end ? lo + step : end;
     }
     bos = cu[lo];
     idx = lo + 1;
@@ -258,19 +264,31 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs p) {
   }
 }
 
+// Token tile: the largest of 128, 64, 32, 16 tokens that still gives the
+// launch one block per CU, else 16 (each block walks its tile's tokens in
+// order; a short launch would leave most of the chip idle). Smaller tiles
+// re-read a 3-row halo per tile. Measured at 8192 tokens of 16 + 16 + 32
+// heads (256 blocks of 128 tokens): more, smaller blocks (64- or 32-token
+// tiles, or 128- and 64-thread blocks) were 2-27% slower.
+constexpr int64_t kMinBlocks = 256;
+
+template <typename T, int VEC, int TILE>
+hipError_t launch_tile(const PrologueArgs &a, int64_t cblocks, int threads, hipStream_t s) {
+  const int64_t tblocks = (a.T + TILE - 1) / TILE;
+  dim3 grid((unsigned)tblocks, (unsigned)cblocks, (unsigned)a.B);
+  hipLaunchKernelGGL((prologue_kernel<T, VEC, TILE>), grid, dim3(threads), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int VEC>
 hipError_t launch_vec(const PrologueArgs &a, hipStream_t s) {
-  const int64_t per_block = (int64_t)kThreads * VEC;
-  const int64_t cblocks = (a.C + per_block - 1) / per_block;
-  // short inputs: smaller token tiles, so that the launch has enough blocks
-  // (each block walks its tile's tokens in order)
-  const bool small = ((a.T + kTile - 1) / kTile) * cblocks * a.B < 256;
-  const int tile = small ? kSmallTile : kTile;
-  const int64_t tblocks = (a.T + tile - 1) / tile;
-  dim3 grid((unsigned)tblocks, (unsigned)cblocks, (unsigned)a.B);
-  if (small) hipLaunchKernelGGL((prologue_kernel<T, VEC, kSmallTile>), grid, dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL((prologue_kernel<T, VEC, kTile>), grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  const int threads = kThreads;
+  const int64_t cblocks = (a.C + (int64_t)threads * VEC - 1) / ((int64_t)threads * VEC);
+  auto blocks = [&](int64_t tile) { return ((a.T + tile - 1) / tile) * cblocks * a.B; };
+  if (blocks(128) >= kMinBlocks) return launch_tile<T, VEC, 128>(a, cblocks, threads, s);
+  if (blocks(64) >= kMinBlocks) return launch_tile<T, VEC, 64>(a, cblocks, threads, s);
+  if (blocks(32) >= kMinBlocks) return launch_tile<T, VEC, 32>(a, cblocks, threads, s);
+  return launch_tile<T, VEC, 16>(a, cblocks, threads, s);
 }
 
 template <typename T>
