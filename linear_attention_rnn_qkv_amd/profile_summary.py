@@ -11,6 +11,14 @@ DIR_* are rocprofv3 ``-d`` output directories (CSV format). The copy runs are
 ``bench.py --calibrate-copy``: a plain device copy of exactly 1 GiB read and
 1 GiB written per dispatch, whose FETCH_SIZE / WRITE_SIZE readings give the
 factor from counter KiB to bytes.
+
+``--mfma DIR`` adds a run with the matrix-core and LDS counters (MFMA_COUNTERS
+below): per kernel, the fraction of the chip's SIMD cycles during which the
+matrix cores were busy (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE, which
+counts each XCD's active cycles, times the SIMDs per XCD), the MFMA flops the
+counters saw (SQ_INSTS_VALU_MFMA_MOPS_* count units of 512 flops) and the share
+of LDS-active cycles lost to bank conflicts. They go to
+``mfma_counters.<workload>.json`` with the same source fingerprints.
 """
 from __future__ import annotations
 
@@ -24,6 +32,11 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 COPY_BYTES = 1 << 30
+# one rocprofv3 --pmc pass (8 SQ counters and one GRBM counter)
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                 "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_BUSY_CU_CYCLES",
+                 "GRBM_GUI_ACTIVE"]
+SIMDS_PER_XCD = 32 * 4  # 32 CUs of 4 SIMDs
 
 # kernel symbol fragment -> (short name, sources its machine code is built from)
 KERNELS = {
@@ -108,6 +121,7 @@ def main() -> int:
     ap.add_argument("--algorithmic", default="{}",
                     help='JSON {kernel: algorithmic bytes per launch} for the comparison column')
     ap.add_argument("--commands", default="", help="text block with the exact commands that were run")
+    ap.add_argument("--mfma", default="", help="rocprofv3 --pmc run with MFMA_COUNTERS")
     ap.add_argument("--out", default="profiles")
     a = ap.parse_args()
 
@@ -166,6 +180,36 @@ def main() -> int:
         alt = f"{al / 1e9:.3f}" if al else "-"
         lines.append(f"| {k} | {v['source_hash']} | {v['read_bytes'] / 1e9:.3f} | {v['write_bytes'] / 1e9:.3f} | "
                      f"{v['bytes'] / 1e9:.3f} | {alt} | {ratio} |")
+    if a.mfma:
+        mf = {n: counter_per_dispatch(a.mfma, n) for n in MFMA_COUNTERS}
+        recs = {}
+        for k in sorted(set(mf["SQ_VALU_MFMA_BUSY_CYCLES"]) & set(stats)):
+            if k not in KERNELS:
+                continue
+            busy = mf["SQ_VALU_MFMA_BUSY_CYCLES"][k]
+            gui = mf["GRBM_GUI_ACTIVE"][k]
+            mops = mf["SQ_INSTS_VALU_MFMA_MOPS_BF16"].get(k, 0.0) + mf["SQ_INSTS_VALU_MFMA_MOPS_F16"].get(k, 0.0)
+            lds = mf["SQ_LDS_IDX_ACTIVE"].get(k, 0.0)
+            recs[k] = {"source_hash": source_hash(k), "avg_us": stats[k]["avg_us"],
+                       "mfma_busy": busy / (gui * SIMDS_PER_XCD) if gui else 0.0,
+                       "mfma_instructions": mf["SQ_INSTS_MFMA"].get(k, 0.0),
+                       "mfma_16bit_flops": mops * 512.0,
+                       "mfma_16bit_TFLOP/s": mops * 512.0 / (stats[k]["avg_us"] * 1e-6) / 1e12,
+                       "lds_bank_conflict_share": mf["SQ_LDS_BANK_CONFLICT"].get(k, 0.0) / lds if lds else 0.0,
+                       "lds_instructions": mf["SQ_INSTS_LDS"].get(k, 0.0),
+                       "counters": {n: mf[n].get(k) for n in MFMA_COUNTERS}}
+        with open(os.path.join(a.out, f"mfma_counters.{a.workload}.json"), "w") as fh:
+            json.dump({"workload": a.workload, "simds_per_xcd": SIMDS_PER_XCD, "kernels": recs}, fh, indent=1)
+        lines += ["", "## Matrix cores and LDS (rocprofv3 --pmc, one pass of the counters below)", "",
+                  "Counters: " + ", ".join(MFMA_COUNTERS) + ". MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                  f"(GRBM_GUI_ACTIVE x {SIMDS_PER_XCD}): GRBM_GUI_ACTIVE sums each XCD's active cycles, so this "
+                  "is the share of all SIMD cycles of the launch with the matrix core busy (a 16x16x32 "
+                  "BF16/FP16 MFMA keeps it busy 16 cycles). MFMA flops = MOPS x 512.", "",
+                  "| kernel | source hash | MFMA busy | MFMA instructions | MFMA TFLOP/s (16-bit, counted) | "
+                  "LDS cycles lost to bank conflicts |", "|---|---|---|---|---|---|"]
+        for k, r in recs.items():
+            lines.append(f"| {k} | {r['source_hash']} | {r['mfma_busy']:.3f} | {r['mfma_instructions']:.3g} | "
+                         f"{r['mfma_16bit_TFLOP/s']:.1f} | {r['lds_bank_conflict_share']:.3f} |")
     with open(os.path.join(a.out, f"layer_core_kernels.{a.workload}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))

@@ -349,3 +349,22 @@ def test_noalloc_rejects_inputs_beyond_the_static_scratch():
     _expect(INVALID, "powers of two", gdn.gdn_chunk_rule_fwd_noalloc, z(1, T, Hqk, dk + 1), z(1, T, Hqk, dk),
             z(1, T, Hv, dv), z(1, T, Hv, d=torch.float32), z(1, T, Hv, d=torch.float32), 0.125,
             out_o=z(1, T, Hv, dv))
+
+
+def test_prologue_bwd_token_tile_per_size():
+    """The prologue backward's token tile (256 tokens, halved down to 32 while
+    its conv launch would have fewer than 2048 blocks) read back from the
+    workspace it asks for: per tile, [C][4] and [C] FP32 partial sums."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    dims = (16, 128, 32, 128)
+    C = 2 * 16 * 128 + 32 * 128
+
+    def expect(T, tile):
+        nt = (T + tile - 1) // tile
+        head_tile = 4096 // 32
+        nh = (T + head_tile - 1) // head_tile
+        return a256(nt * C * 16) + a256(nt * C * 4) + 2 * a256(nh * 32 * 4) + a256(32 * C * 16)
+    for T, tile in [(8192, 32), (16384, 64), (32768, 128), (65536, 256), (131072, 256), (100, 32)]:
+        got = gdn.lib().gdn_prologue_bwd_workspace_bytes(1, T, ctypes.byref(gdn.dims_of(*dims)))
+        assert got == expect(T, tile), (T, tile, got)

@@ -119,3 +119,44 @@ def test_prologue_bwd_full_size_sampled_channels():
     H.assert_close(f64(db.cpu()[..., vh]), ref[6], tau, "d_b")
     H.assert_close(f64(dal.cpu()[vh]), ref[7], tau, "d_A_log")
     H.assert_close(f64(ddt.cpu()[vh]), ref[8], tau, "d_dt_bias")
+
+
+@pytest.mark.parametrize("T,lengths", [(16384, None), (32768, (5000, 7, 12001, 64, 0, 15696))],
+                         ids=["T16384-dense", "T32768-packed"])
+def test_prologue_bwd_intermediate_sizes_sampled_channels(T, lengths):
+    """The 8192-token workload's head geometry (C = 8192) at the sizes where
+    the backward picks 64-token (16384 tokens) and 128-token (32768 tokens)
+    tiles; the packed case has boundaries inside tiles and an empty sequence.
+    One q/k head and its two value heads against the oracle."""
+    s = synth.spec(2).replace(T=T) if lengths is None else synth.spec(2).replace(lengths=lengths)
+    assert s.T == T
+    x = synth.make_inputs(s)
+    xd = H.to_dev(x)
+    dims = (s.Hqk, s.dk, s.Hv, s.dv)
+    d_qkv = synth.randn((s.B, s.T, s.C), s.act, 360).cuda()
+    d_g = synth.randn((s.B, s.T, s.Hv), "f32", 361).cuda()
+    d_beta = synth.randn((s.B, s.T, s.Hv), "f32", 362).cuda()
+    got = gdn.gdn_prologue_bwd(xd["x_q"], xd["x_k"], xd["x_v"], xd["conv_w"], None, xd["a"], xd["b"],
+                               xd["A_log"], xd["dt_bias"], xd["cu_seqlens"], dims, d_qkv, d_g, d_beta)
+    torch.cuda.synchronize()
+    hq = 5
+    vh = [2 * hq, 2 * hq + 1]
+    nq = s.Hqk * s.dk
+    qc = np.arange(hq * s.dk, (hq + 1) * s.dk)
+    vc = np.concatenate([np.arange(h * s.dv, (h + 1) * s.dv) for h in vh])
+    cols = np.concatenate([qc, nq + qc, 2 * nq + vc])
+    dq = d_qkv.cpu()
+    ref = OB.prologue_bwd(f64(x["x_q"][..., qc]), f64(x["x_k"][..., qc]), f64(x["x_v"][..., vc]),
+                          f64(x["conv_w"][cols]), None, f64(x["a"][..., vh]), f64(x["b"][..., vh]),
+                          f64(x["A_log"][vh]), f64(x["dt_bias"][vh]), f64(dq[..., cols]),
+                          f64(d_g.cpu()[..., vh]), f64(d_beta.cpu()[..., vh]), H.cu_of(x))
+    tau = TAU[s.act]
+    dxq, dxk, dxv, dw, _, da, db, dal, ddt = got
+    H.assert_close(f64(dxq.cpu()[..., qc]), ref[0], tau, "dx_q")
+    H.assert_close(f64(dxk.cpu()[..., qc]), ref[1], tau, "dx_k")
+    H.assert_close(f64(dxv.cpu()[..., vc]), ref[2], tau, "dx_v")
+    H.assert_close(f64(dw.cpu()[cols]), ref[3], tau, "d_conv_w")
+    H.assert_close(f64(da.cpu()[..., vh]), ref[5], tau, "d_a")
+    H.assert_close(f64(db.cpu()[..., vh]), ref[6], tau, "d_b")
+    H.assert_close(f64(dal.cpu()[vh]), ref[7], tau, "d_A_log")
+    H.assert_close(f64(ddt.cpu()[vh]), ref[8], tau, "d_dt_bias")
