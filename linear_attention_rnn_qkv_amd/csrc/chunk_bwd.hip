@@ -28,6 +28,7 @@
 //                      in turn: dq, dk (through the L2 fold), dg, dbeta
 // Products run in FP32 on the vector ALU from LDS tiles; the forward's MFMA
 // records (BF16 fragments of M diag(beta), not M) are not reused.
+#include "chunk_bwd_common.h"
 #include "device_common.h"
 #include "gdn_internal.h"
 
@@ -50,40 +51,6 @@ template <typename T>
 __device__ __forceinline__ void store_grad(void *base, int32_t dt, int64_t i, float x) {
   if (dt == kF32) static_cast<float *>(base)[i] = x;
   else static_cast<T *>(base)[i] = to<T>(x);
-}
-
-// Where chunk gc of the whole call lies: batch row, first token, rows.
-struct ChunkPos {
-  int64_t brow, t0;
-  int nr;
-  bool valid;
-};
-
-__device__ __forceinline__ ChunkPos chunk_pos(const ChunkBwdArgs &p, int64_t gc) {
-  ChunkPos c;
-  if (p.cu_seqlens) {
-    const int32_t *cuc = p.cu_chunks;
-    c.valid = gc < cuc[p.n_seqs];
-    if (!c.valid) return c;
-    int64_t lo = 0, hi = p.n_seqs;  // cuc[lo] <= gc < cuc[hi]
-    while (hi - lo > 1) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (cuc[mid] <= gc) lo = mid; else hi = mid;
-    }
-    const int64_t ch = gc - cuc[lo], bos = p.cu_seqlens[lo], L = p.cu_seqlens[lo + 1] - bos;
-    c.brow = 0;
-    c.t0 = bos + ch * BT;
-    c.nr = (int)(L - ch * BT < BT ? L - ch * BT : BT);
-  } else {
-    const int64_t nc = (p.T + BT - 1) / BT;
-    c.valid = gc < p.B * nc;
-    if (!c.valid) return c;
-    c.brow = gc / nc;
-    const int64_t ch = gc % nc;
-    c.t0 = ch * BT;
-    c.nr = (int)(p.T - c.t0 < BT ? p.T - c.t0 : BT);
-  }
-  return c;
 }
 
 // Sequence n: batch row, first token, length, first chunk of the call.
@@ -962,6 +929,7 @@ hipError_t launch_t(const ChunkBwdArgs &a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), sg, dim3(kSer), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (chunk_bwd_grad_mma_supported(a)) return launch_chunk_bwd_grad_mma(a, s);
   hipLaunchKernelGGL((bwd_grad_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk),
                      dim3(grad_threads<DK>()), 0, s, a);
   return hipGetLastError();
