@@ -18,7 +18,7 @@ OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 SOURCES = ["gdn_api.cpp", "prologue.hip", "chunk_rule.hip", "chunk_prep.hip",
            "chunk_state.hip", "gated_norm.hip", "decode.hip",
-           "chunk_state_wide.hip", "backward.hip", "chunk_bwd.hip", "chunk_bwd_mma.hip",
+           "chunk_state_wide.hip", "backward.hip", "chunk_bwd.hip", "chunk_bwd_mma.hip", "chunk_bwd_state_mma.hip",
            "noalloc.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          # no packed-FP32 instructions in generated device code

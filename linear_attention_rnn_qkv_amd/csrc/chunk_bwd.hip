@@ -249,11 +249,11 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
       float q[BT * KP], k[BT * KP];
     } x;
     struct {
-      float a[BT * MP], m[BT * MP];
+      float a[BT * MP], m[BT * MP], p[BT * MP];
     } y;
   } lds;
-  float *sQ = lds.x.q, *sK = lds.x.k, *sA = lds.y.a, *sM = lds.y.m;
-  __shared__ float sgam[BT], sbeta[BT];
+  float *sQ = lds.x.q, *sK = lds.x.k, *sA = lds.y.a, *sM = lds.y.m, *sP = lds.y.p;
+  __shared__ float sgam[BT], sbeta[BT], srq[BT], srk[BT];
   const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
   const int64_t gc = blockIdx.x, hk = blockIdx.y;
   const ChunkPos cp = chunk_pos(p, gc);
@@ -299,6 +299,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
     if (part == 0) {
       p.rq[(gc * p.Hqk + hk) * BT + t] = rq;
       p.rk[(gc * p.Hqk + hk) * BT + t] = rk;
+      srq[t] = rq;
+      srk[t] = rk;
     }
   }
   __syncthreads();
@@ -342,6 +344,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
           const float e = s <= t ? __expf(sgam[t] - sgam[s]) : 0.f;
           sA[t * MP + s] = s < t ? sbeta[t] * e * gg[r][c] : 0.f;
           pv[c] = p.scale * e * qk[r][c];
+          sP[t * MP + s] = t < nr ? pv[c] : 0.f;
         }
         stv<4>(pp + t * BT + 4 * cg, pv);
       }
@@ -371,6 +374,40 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
     {
       float *mm_ = p.mm + (gc * p.Hv + h) * BT * BT;
       for (int e = tid; e < BT * BT; e += kThreads) mm_[e] = sM[(e >> 6) * MP + (e & 63)];
+    }
+    if (p.brec) {  // the matrix-core reverse pass's record (16-bit activations)
+      unsigned char *br = p.brec + (gc * p.Hv + h) * kBrBytes;
+      // 6 fragments x 2 matrices x 64 lanes; hi and lo written together
+      for (int it = tid; it < 2 * 6 * 64; it += kThreads) {
+        const int lane = it & 63, fi = (it >> 6) % 6, mat = it / 384;
+        const int mt = fi < 2 ? fi : fi - 2, q = fi < 2 ? 0 : 1, g = lane >> 4, c = lane & 15;
+        const float *src = mat == 0 ? sM : sP;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = src[(32 * q + 16 * (e >> 2) + 4 * g + (e & 3)) * MP + 16 * mt + c];
+        bf16 hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hi[e] = to<bf16>(x[e]);
+          lo[e] = to<bf16>(x[e] - f(hi[e]));
+        }
+        const int64_t oh = (mat == 0 ? kBrMtH : kBrPH) + fi * 1024 + lane * 16;
+        const int64_t ol = (mat == 0 ? kBrMtL : kBrPL) + fi * 1024 + lane * 16;
+        __builtin_memcpy(br + oh, hi, 16);
+        __builtin_memcpy(br + ol, lo, 16);
+      }
+      if (tid < BT) {
+        const int t = tid;
+        float *fr = reinterpret_cast<float *>(br + kBrF);
+        const float gl = sgam[nr - 1], eg = __expf(sgam[t]);
+        const float cw = t < nr ? __expf(gl - sgam[t]) : 0.f;
+        fr[0 * BT + t] = eg;
+        fr[1 * BT + t] = cw * srk[t];
+        fr[2 * BT + t] = sbeta[t];
+        fr[3 * BT + t] = t < nr ? p.scale * eg * srq[t] : 0.f;
+        fr[4 * BT + t] = -eg * sbeta[t] * srk[t];
+        fr[5 * BT + t] = t == 0 ? __expf(gl) : 0.f;
+      }
     }
     __syncthreads();
   }
@@ -918,7 +955,11 @@ __global__ __launch_bounds__(grad_threads<DK>()) void bwd_grad_kernel(ChunkBwdAr
 }
 
 template <typename T, int DK>
-hipError_t launch_t(const ChunkBwdArgs &a, hipStream_t s) {
+hipError_t launch_t(const ChunkBwdArgs &a0, hipStream_t s) {
+  // the matrix-core reverse pass reads the records the prep writes
+  ChunkBwdArgs a = a0;
+  const bool ds_mma = chunk_bwd_state_mma_supported(a);
+  if (!ds_mma) a.brec = nullptr;
   const int64_t N = a.n_seqs;
   hipLaunchKernelGGL((bwd_prep_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk), dim3(kThreads), 0, s,
                      a);
@@ -927,8 +968,12 @@ hipError_t launch_t(const ChunkBwdArgs &a, hipStream_t s) {
   const dim3 sg((unsigned)(a.dv / 16), (unsigned)a.Hv, (unsigned)N);
   hipLaunchKernelGGL((bwd_states_kernel<T, DK>), sg, dim3(kSer), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), sg, dim3(kSer), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ds_mma) e = launch_chunk_bwd_dstate_mma(a, s);
+  else {
+    hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), sg, dim3(kSer), 0, s, a);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
   if (chunk_bwd_grad_mma_supported(a)) return launch_chunk_bwd_grad_mma(a, s);
   hipLaunchKernelGGL((bwd_grad_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk),
                      dim3(grad_threads<DK>()), 0, s, a);

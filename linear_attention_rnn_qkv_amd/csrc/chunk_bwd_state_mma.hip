@@ -1,0 +1,387 @@
+// Reverse state pass of the chunk-rule backward on the BF16 matrix cores, for
+// BF16 activations with dk 64 or 128: per (sequence, value head, 16 value
+// rows), serial over the chunks from the last to the first, the gradient dS
+// of the state leaving each chunk is carried in FP32 MFMA accumulators and
+// each chunk gives (unit q, k rows q^, k^; the algebra is written out at the
+// top of chunk_bwd.hip)
+//
+//   dDelta = cw (.) K^ dS^T + P'^T dO                 (P' = scale Pt)
+//   dR'    = M^T dDelta,   dv = beta (.) dR'
+//   dS0    = e^{gamma_C} dS + Q^T (fq (.) dO) + K^T (fk (.) dR')
+//
+// with fq = scale e^gamma rq and fk = -e^gamma beta rk on the raw BF16 q, k
+// rows. dS_C (for the gradient kernel) and dR' are written in FP32, dv in the
+// gradient dtype.
+//
+// Precision. K, Q and dO are exact BF16 operands; dS, dDelta, dR', the
+// scaled rows and the record's M^T, P'^T are split as x = hi + lo (BF16), and
+// products of two split operands take ah bh + ah bl + al bh, so that each
+// term carries a relative error near 2^-16.
+//
+// One workgroup = (sequence, value head, 16 rows of dv), eight wavefronts,
+// one barrier per step:
+//   wave 0     the chain: every product above, dS in accumulators;
+//   waves 2-7  copies (global_load_lds) of the k and q tiles, the dO slice
+//              and the record of the next chunk into a two-slot LDS ring.
+#include "chunk_bwd_common.h"
+#include "gdn_internal.h"
+#include "mfma_tiles.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThr = 512;
+constexpr int BT = 64;
+constexpr int DVT = 16;
+
+typedef bf16x8 f8;
+typedef bf16x4 v4;
+
+__device__ __forceinline__ f32x4 mma(f8 a, f8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// dk permutation of the state tiles (as in the forward state kernel):
+// accumulator tile mt = 2 pp + h, row 4 g + i holds dk 32 pp + 8 g + 4 h + i.
+__device__ __forceinline__ constexpr int dk_of(int mt, int r) {
+  return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3);
+}
+
+// fragment of (row tile mt, k pair q) of an upper-triangular record matrix
+__device__ __forceinline__ constexpr int up_frag(int mt, int q) { return q == 0 ? mt : 2 + mt; }
+
+__device__ __forceinline__ void split8(const float (&x)[8], f8 &hi, f8 &lo) {
+  const f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+  const v4 ah = __builtin_convertvector(a, v4), bh = __builtin_convertvector(b, v4);
+  const v4 al = __builtin_convertvector(a - __builtin_convertvector(ah, f32x4), v4);
+  const v4 bl = __builtin_convertvector(b - __builtin_convertvector(bh, f32x4), v4);
+  hi = cat8<bf16>(ah, bh);
+  lo = cat8<bf16>(al, bl);
+}
+__device__ __forceinline__ void split2x4(f32x4 a, f32x4 b, f8 &hi, f8 &lo) {
+  const v4 ah = __builtin_convertvector(a, v4), bh = __builtin_convertvector(b, v4);
+  const v4 al = __builtin_convertvector(a - __builtin_convertvector(ah, f32x4), v4);
+  const v4 bl = __builtin_convertvector(b - __builtin_convertvector(bh, f32x4), v4);
+  hi = cat8<bf16>(ah, bh);
+  lo = cat8<bf16>(al, bl);
+}
+
+template <int DK>
+struct DsLds {
+  static constexpr int RB = DK * 2;
+  static constexpr int TILE = BT * RB;
+  alignas(16) unsigned char k[2][TILE];   // raw k rows of the step's chunk (swizzled)
+  alignas(16) unsigned char q[2][TILE];   // raw q rows
+  alignas(16) bf16 o[2][BT * DVT];        // dO slice [64][16]
+  alignas(16) unsigned char rec[2][kBrBytes];
+};
+
+template <int N> struct Slot { static constexpr int v = N; };
+
+// Runs body(s, Slot<s mod 2>) for s = -1 .. last in order.
+template <typename F>
+__device__ __forceinline__ void for_steps2(int last, F &&body) {
+  for (int base = -2; base <= last; base += 2) {
+    if (base >= -1) body(base, Slot<0>{});
+    if (base + 1 <= last) body(base + 1, Slot<1>{});
+  }
+}
+
+template <int DK>
+__global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
+  using SM = DsLds<DK>;
+  constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB;
+  constexpr int NI = SM::TILE / 1024;           // 1 KB copies per q/k tile
+  constexpr int NR = (int)(kBrBytes / 1024);    // 1 KB copies per record
+  static_assert(NI % 2 == 0 && NR % 2 == 0 && NI / 2 <= 31 && NR / 2 + 1 <= 31, "copy split");
+  __shared__ SM sm;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  // slices of one head (which read the same tiles and records) on one XCD
+  const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
+  const int64_t j0 = (lid % ntile) * DVT;
+  const int64_t h = (lid / ntile) % gridDim.y;
+  const int64_t n = lid / (ntile * gridDim.y);
+  const int64_t hk = h / (p.Hv / p.Hqk);
+  int64_t brow, bos, L, gc0;
+  if (p.cu_seqlens) {
+    brow = 0;
+    bos = p.cu_seqlens[n];
+    L = p.cu_seqlens[n + 1] - bos;
+    gc0 = p.cu_chunks[n];
+  } else {
+    brow = n;
+    bos = 0;
+    L = p.T;
+    gc0 = n * ((p.T + BT - 1) / BT);
+  }
+  const int Nc = (int)((L + BT - 1) / BT);
+  // step s works on chunk Nc - 1 - s
+  auto rows_of = [&](int ch) -> int {
+    const int64_t r = L - (int64_t)ch * BT;
+    return (int)(r < BT ? r : BT);
+  };
+  const int64_t st_base = ((n * p.Hv + h) * p.dv + j0) * DK;
+
+  if (wave == 0) {
+    // ---------------------------------------------------------------- chain
+    int fo[KT];  // row c of a 16-row tile, dk 32 pp + 8 g .. + 7
+#pragma unroll
+    for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
+    // transposing-read offsets (K^T, Q^T fragments; see the forward state kernel)
+    const int yrow = 4 * g + (c >> 2);
+    int trc[NT];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+      trc[mt] = yrow * RB + (((4 * (mt >> 1) + (c & 3)) ^ kswz<DK>(yrow)) << 4) + 8 * (mt & 1);
+    const int otr = (4 * g + (c >> 2)) * (DVT * 2) + 8 * (c & 3);
+
+    f32x4 dS[NT];  // dS[mt][i] = dS[dv row c][dk dk_of(mt, 4 g + i)]
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dS[mt][i] = p.d_final ? p.d_final[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] : 0.f;
+
+    for_steps2(Nc - 1, [&](int s, auto SL) {
+      lds_barrier();
+      if (s < 0) return;
+      constexpr int sl = decltype(SL)::v;
+      const int ch = Nc - 1 - s;
+      const int64_t gc = gc0 + ch, t0 = bos + (int64_t)ch * BT;
+      const int nr = rows_of(ch);
+      const unsigned char *kt = sm.k[sl], *qt = sm.q[sl], *rec = sm.rec[sl];
+      const float *fa = reinterpret_cast<const float *>(rec + kBrF);
+      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+      // dS_C to the workspace (the gradient kernel reads it as [dv][dk])
+      {
+        float *dsw = p.ds + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(dsw + dk_of(mt, 4 * g)) = dS[mt];
+      }
+      // U = K dS^T (raw k rows), then dDelta = cw rk (.) U + P'^T dO
+      f32x4 dD[4];
+      {
+        f8 Sh[KT], Sl[KT];
+#pragma unroll
+        for (int pp = 0; pp < KT; ++pp) split2x4(dS[2 * pp], dS[2 * pp + 1], Sh[pp], Sl[pp]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 u = zero4;
+#pragma unroll
+          for (int pp = 0; pp < KT; ++pp) {
+            const f8 kf = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
+            u = mma(kf, Sh[pp], u);
+            u = mma(kf, Sl[pp], u);
+          }
+          const f32x4 cr = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 16 * mt + 4 * g]);
+          dD[mt] = u * cr;
+        }
+      }
+      // dO fragments (B operand, k slots in tile-pair order), exact
+      f8 Bo[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const unsigned char *ob = reinterpret_cast<const unsigned char *>(sm.o[sl]) + otr + 32 * q * (DVT * 2);
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ob));
+        const s16x4 r1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ob + 16 * DVT * 2));
+        Bo[q] = cat8<bf16>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if (q == 0 && mt >= 2) continue;
+          const int f = up_frag(mt, q);
+          const f8 ph = *reinterpret_cast<const f8 *>(rec + kBrPH + f * 1024 + lane * 16);
+          const f8 pl = *reinterpret_cast<const f8 *>(rec + kBrPL + f * 1024 + lane * 16);
+          dD[mt] = mma(ph, Bo[q], dD[mt]);
+          dD[mt] = mma(pl, Bo[q], dD[mt]);
+        }
+      // dR' = M^T dDelta
+      f32x4 dR[4];
+      {
+        f8 Dh[2], Dl[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) split2x4(dD[2 * q], dD[2 * q + 1], Dh[q], Dl[q]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 r = zero4;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            if (q == 0 && mt >= 2) continue;
+            const int f = up_frag(mt, q);
+            const f8 mh = *reinterpret_cast<const f8 *>(rec + kBrMtH + f * 1024 + lane * 16);
+            const f8 ml = *reinterpret_cast<const f8 *>(rec + kBrMtL + f * 1024 + lane * 16);
+            r = mma(mh, Dh[q], r);
+            r = mma(mh, Dl[q], r);
+            r = mma(ml, Dh[q], r);
+          }
+          dR[mt] = r;
+        }
+      }
+      // dR' (FP32) and dv = beta dR' (rows of the chunk only)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 bt = *reinterpret_cast<const f32x4 *>(&fa[2 * BT + 16 * mt + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * mt + 4 * g + i;
+          p.drp[((gc * p.Hv + h) * BT + t) * p.dv + j0 + c] = dR[mt][i];
+          if (t < nr) {
+            const int64_t o = brow * p.sdv_b + (t0 + t) * p.sdv_t + h * p.dv + j0 + c;
+            const float x = bt[i] * dR[mt][i];
+            if (p.grad_dtype == kF32) static_cast<float *>(p.dvv)[o] = x;
+            else static_cast<bf16 *>(p.dvv)[o] = to<bf16>(x);
+          }
+        }
+      }
+      // dS0 = e^{gamma_C} dS + Q^T (fq (.) dO) + K^T (fk (.) dR')
+      f8 Fqh[2], Fql[2], Fkh[2], Fkl[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f32x4 fq0 = *reinterpret_cast<const f32x4 *>(&fa[3 * BT + 32 * q + 4 * g]);
+        const f32x4 fq1 = *reinterpret_cast<const f32x4 *>(&fa[3 * BT + 32 * q + 16 + 4 * g]);
+        const f32x4 fk0 = *reinterpret_cast<const f32x4 *>(&fa[4 * BT + 32 * q + 4 * g]);
+        const f32x4 fk1 = *reinterpret_cast<const f32x4 *>(&fa[4 * BT + 32 * q + 16 + 4 * g]);
+        float xq[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xq[e] = fq0[e] * f(Bo[q][e]);
+          xq[4 + e] = fq1[e] * f(Bo[q][4 + e]);
+        }
+        split8(xq, Fqh[q], Fql[q]);
+        split2x4(fk0 * dR[2 * q], fk1 * dR[2 * q + 1], Fkh[q], Fkl[q]);
+      }
+      const float eC = fa[5 * BT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        f32x4 a = dS[mt] * eC;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const unsigned char *qa1 = qt + trc[mt] + (32 * q) * RB, *qa2 = qt + trc[mt] + (32 * q + 16) * RB;
+          const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
+          const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(qa1));
+          const s16x4 q2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(qa2));
+          const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
+          const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
+          const f8 qT = cat8<bf16>(__builtin_bit_cast(v4, q1), __builtin_bit_cast(v4, q2));
+          const f8 kT = cat8<bf16>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
+          a = mma(qT, Fqh[q], a);
+          a = mma(qT, Fql[q], a);
+          a = mma(kT, Fkh[q], a);
+          a = mma(kT, Fkl[q], a);
+        }
+        dS[mt] = a;
+      }
+    });
+    if (p.d_init) {
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+        *reinterpret_cast<f32x4 *>(p.d_init + st_base + (int64_t)c * DK + dk_of(mt, 4 * g)) = dS[mt];
+    }
+  } else if (wave == 1) {
+    for_steps2(Nc - 1, [&](int, auto) { lds_barrier(); });
+  } else {
+    // ------------------------------------------------------------- loads
+    // Waves 2, 3 copy the halves of the k tile, waves 4, 5 those of the q
+    // tile, waves 6, 7 the halves of the record and of the dO slice, for the
+    // chunk of step s + 1; they are complete before the barrier ending step s.
+    const int role = wave - 2;
+    if (role < 4) {
+      constexpr int NH = NI / 2;
+      const bool isk = role < 2;
+      const int i0 = (role & 1) * NH;
+      const int64_t st = isk ? p.sk_t : p.sq_t;
+      const bf16 *xb = static_cast<const bf16 *>(isk ? p.k : p.q) + brow * (isk ? p.sk_b : p.sq_b) +
+                       hk * (isk ? p.sk_h : p.sq_h) + bos * st;
+      uint32_t xoff[NH];
+#pragma unroll
+      for (int i = 0; i < NH; ++i) {
+        const int b = 1024 * (i0 + i) + 16 * lane;
+        const int r = b / RB, jp = (b % RB) >> 4;
+        const int j = jp ^ kswz<DK>(r);
+        xoff[i] = (uint32_t)(((int64_t)r * st + 8 * j) * 2);
+      }
+      for_steps2(Nc - 1, [&](int s, auto SL) {
+        lds_barrier();
+        constexpr int sl = (decltype(SL)::v + 1) % 2;  // slot of step s + 1
+        if (s + 1 < Nc) {
+          const int ch = Nc - 2 - s;
+          const int nr = rows_of(ch);
+          const int64_t t0 = (int64_t)ch * BT;
+          unsigned char *xt = (isk ? sm.k[sl] : sm.q[sl]) + 1024 * i0;
+          if (nr == BT) {
+            const unsigned char *xg = reinterpret_cast<const unsigned char *>(xb + t0 * st);
+#pragma unroll
+            for (int i = 0; i < NH; ++i) g2l16(xg + xoff[i], xt + 1024 * i);
+          } else {
+            // partial chunk: rows past its end repeat its last row
+#pragma unroll
+            for (int i = 0; i < NH; ++i) {
+              const int b = 1024 * (i0 + i) + 16 * lane;
+              const int r = b / RB, jp = (b % RB) >> 4;
+              const int j = jp ^ kswz<DK>(r);
+              const int rr = r < nr ? r : nr - 1;
+              g2l16(xb + (t0 + rr) * st + 8 * j, xt + 1024 * i);
+            }
+          }
+        }
+        wait_vm<0>();
+      });
+    } else {
+      constexpr int NRH = NR / 2;
+      const int half = role - 4;
+      const bf16 *ob = static_cast<const bf16 *>(p.d_o) + brow * p.sdo_b + h * p.sdo_h + j0 + bos * p.sdo_t;
+      for_steps2(Nc - 1, [&](int s, auto SL) {
+        lds_barrier();
+        constexpr int sl = (decltype(SL)::v + 1) % 2;
+        if (s + 1 < Nc) {
+          const int ch = Nc - 2 - s;
+          const int nr = rows_of(ch);
+          const int64_t t0 = (int64_t)ch * BT;
+          const unsigned char *rg = p.brec + ((gc0 + ch) * p.Hv + h) * kBrBytes + 1024 * NRH * half;
+#pragma unroll
+          for (int i = 0; i < NRH; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * (NRH * half + i));
+          // dO rows past the chunk's end repeat its last row (their factors are 0)
+          const int r = 32 * half + (lane >> 1);
+          const int rr = r < nr ? r : nr - 1;
+          g2l16(ob + (t0 + rr) * p.sdo_t + 8 * (lane & 1),
+                reinterpret_cast<unsigned char *>(sm.o[sl]) + 1024 * half);
+        }
+        wait_vm<0>();
+      });
+    }
+  }
+}
+
+template <int DK>
+hipError_t launch_ds(const ChunkBwdArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)(a.dv / DVT), (unsigned)a.Hv, (unsigned)a.n_seqs);
+  hipLaunchKernelGGL((bwd_dstate_mma_kernel<DK>), grid, dim3(kThr), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// BF16 activations, dk 64 or 128, dv a multiple of 16; q, k and d_o rows
+// 16-byte aligned (LDS DMA copies).
+bool chunk_bwd_state_mma_supported(const ChunkBwdArgs &a) {
+  if (a.act != kBF16 || !(a.dk == 64 || a.dk == 128) || a.dv % 16 != 0) return false;
+  const uint64_t qa = (uint64_t)(uintptr_t)a.q | (uint64_t)(a.sq_b * 2) | (uint64_t)(a.sq_t * 2) | (uint64_t)(a.sq_h * 2);
+  const uint64_t ka = (uint64_t)(uintptr_t)a.k | (uint64_t)(a.sk_b * 2) | (uint64_t)(a.sk_t * 2) | (uint64_t)(a.sk_h * 2);
+  const uint64_t oa =
+      (uint64_t)(uintptr_t)a.d_o | (uint64_t)(a.sdo_b * 2) | (uint64_t)(a.sdo_t * 2) | (uint64_t)(a.sdo_h * 2);
+  return align_of_host(qa) >= 16 && align_of_host(ka) >= 16 && align_of_host(oa) >= 16;
+}
+
+hipError_t launch_chunk_bwd_dstate_mma(const ChunkBwdArgs &a, hipStream_t s) {
+  return a.dk == 64 ? launch_ds<64>(a, s) : launch_ds<128>(a, s);
+}
+
+}  // namespace gdn

@@ -788,7 +788,7 @@ gdn_status attach_chunk_ws(gdn::ChunkArgs *p, void *ws, size_t ws_bytes) {
 
 // Workspace of the chunk-rule backward (offsets in bytes, each 256-aligned).
 struct ChunkBwdWs {
-  size_t cu, qn, kn, rq, rk, gam, mm, pp, s0, ds, rr, del, drp, total;
+  size_t cu, qn, kn, rq, rk, gam, mm, pp, s0, ds, rr, del, drp, brec, total;
 };
 ChunkBwdWs chunk_bwd_layout(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *d) {
   ChunkBwdWs w;
@@ -813,6 +813,7 @@ ChunkBwdWs chunk_bwd_layout(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims
   w.rr = take(cb * Hv * 64 * dv * 4);
   w.del = take(cb * Hv * 64 * dv * 4);
   w.drp = take(cb * Hv * 64 * dv * 4);
+  w.brec = take(cb * Hv * (size_t)gdn::kBrBytes);
   w.total = o;
   return w;
 }
@@ -944,6 +945,7 @@ gdn_status plan_chunk_bwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_te
   p.qn = fp(L.qn); p.kn = fp(L.kn); p.rq = fp(L.rq); p.rk = fp(L.rk); p.gam = fp(L.gam);
   p.mm = fp(L.mm); p.pp = fp(L.pp); p.s0 = fp(L.s0); p.ds = fp(L.ds);
   p.rr = fp(L.rr); p.del = fp(L.del); p.drp = fp(L.drp);
+  p.brec = reinterpret_cast<unsigned char *>(w + L.brec);
   return GDN_OK;
 }
 

@@ -179,7 +179,20 @@ struct ChunkBwdArgs {
   int32_t *cu_chunks;         // [n_seqs + 1] (packed sequences)
   int64_t chunk_bound;
   float *qn, *kn, *rq, *rk, *gam, *mm, *pp, *s0, *ds, *rr, *del, *drp;
+  unsigned char *brec;        // [gc][Hv] records of kBrBytes for the matrix-core reverse pass
 };
+
+// Backward record per (chunk, value head), written by the backward prep for
+// the matrix-core reverse pass: MFMA A-operand fragments of M^T and of P'^T
+// (M = (I + A)^-1, P' = scale * masked decayed q.k with its rows past the
+// chunk's end zeroed), each as BF16 hi and lo parts (x = hi + lo), then FP32
+// factor rows [6][64]: e^gamma, cw rk, beta, scale e^gamma rq (0 past the
+// end), -e^gamma beta rk, and e^{gamma_C} at [5][0]. Both matrices are upper
+// triangular; fragment f = (row tile mt, k pair q) in the order (0,0) (1,0)
+// (0,1) (1,1) (2,1) (3,1); element e of lane 16 g + c is
+// X[16 mt + c][32 q + 16 (e / 4) + 4 g + e % 4].
+constexpr int64_t kBrMtH = 0, kBrMtL = 6144, kBrPH = 12288, kBrPL = 18432, kBrF = 24576;
+constexpr int64_t kBrBytes = 26624;
 
 // Each returns the HIP error of the launch (hipSuccess if queued).
 hipError_t launch_prologue(const PrologueArgs &a, hipStream_t s);
@@ -205,6 +218,10 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t s);
 // 128, dv a multiple of 32, aligned rows); the FP32 kernel serves the rest.
 bool chunk_bwd_grad_mma_supported(const ChunkBwdArgs &a);
 hipError_t launch_chunk_bwd_grad_mma(const ChunkBwdArgs &a, hipStream_t s);
+// Its reverse state pass on the BF16 matrix cores (BF16 activations, dk 64 or
+// 128, 16-byte aligned q, k and d_o rows); needs a.brec written by the prep.
+bool chunk_bwd_state_mma_supported(const ChunkBwdArgs &a);
+hipError_t launch_chunk_bwd_dstate_mma(const ChunkBwdArgs &a, hipStream_t s);
 
 // Device address of the static chunk scratch (GDN_NOALLOC_SCRATCH_BYTES) on
 // the current device; looked up once per device.
