@@ -377,22 +377,29 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
     }
     if (p.brec) {  // the matrix-core reverse pass's record (16-bit activations)
       unsigned char *br = p.brec + (gc * p.Hv + h) * kBrBytes;
-      // 6 fragments x 2 matrices x 64 lanes; hi and lo written together
-      for (int it = tid; it < 2 * 6 * 64; it += kThreads) {
-        const int lane = it & 63, fi = (it >> 6) % 6, mat = it / 384;
-        const int mt = fi < 2 ? fi : fi - 2, q = fi < 2 ? 0 : 1, g = lane >> 4, c = lane & 15;
-        const float *src = mat == 0 ? sM : sP;
+      // 6 fragments x 3 matrices (M^T, P'^T, M) x 64 lanes; hi and lo
+      // written together
+      for (int it = tid; it < 3 * 6 * 64; it += kThreads) {
+        const int lane = it & 63, fi = (it >> 6) % 6, mat = it / 384, g = lane >> 4, c = lane & 15;
         float x[8];
+        if (mat < 2) {  // upper triangular: (0,0) (1,0) (0,1) (1,1) (2,1) (3,1), transposed reads
+          const int mt = fi < 2 ? fi : fi - 2, q = fi < 2 ? 0 : 1;
+          const float *src = mat == 0 ? sM : sP;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = src[(32 * q + 16 * (e >> 2) + 4 * g + (e & 3)) * MP + 16 * mt + c];
+          for (int e = 0; e < 8; ++e) x[e] = src[(32 * q + 16 * (e >> 2) + 4 * g + (e & 3)) * MP + 16 * mt + c];
+        } else {  // M, lower triangular: (0,0) (1,0) (2,0) (3,0) (2,1) (3,1)
+          const int mt = fi < 4 ? fi : fi - 2, q = fi < 4 ? 0 : 1;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = sM[(16 * mt + c) * MP + 32 * q + 16 * (e >> 2) + 4 * g + (e & 3)];
+        }
         bf16 hi[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           hi[e] = to<bf16>(x[e]);
           lo[e] = to<bf16>(x[e] - f(hi[e]));
         }
-        const int64_t oh = (mat == 0 ? kBrMtH : kBrPH) + fi * 1024 + lane * 16;
-        const int64_t ol = (mat == 0 ? kBrMtL : kBrPL) + fi * 1024 + lane * 16;
+        const int64_t oh = (mat == 0 ? kBrMtH : mat == 1 ? kBrPH : kBrMH) + fi * 1024 + lane * 16;
+        const int64_t ol = (mat == 0 ? kBrMtL : mat == 1 ? kBrPL : kBrML) + fi * 1024 + lane * 16;
         __builtin_memcpy(br + oh, hi, 16);
         __builtin_memcpy(br + ol, lo, 16);
       }
@@ -407,6 +414,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
         fr[3 * BT + t] = t < nr ? p.scale * eg * srq[t] : 0.f;
         fr[4 * BT + t] = -eg * sbeta[t] * srk[t];
         fr[5 * BT + t] = t == 0 ? __expf(gl) : 0.f;
+        fr[6 * BT + t] = eg * srk[t];
+        fr[7 * BT + t] = 0.f;
       }
     }
     __syncthreads();
@@ -966,8 +975,12 @@ hipError_t launch_t(const ChunkBwdArgs &a0, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 sg((unsigned)(a.dv / 16), (unsigned)a.Hv, (unsigned)N);
-  hipLaunchKernelGGL((bwd_states_kernel<T, DK>), sg, dim3(kSer), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ds_mma) e = launch_chunk_bwd_states_mma(a, s);
+  else {
+    hipLaunchKernelGGL((bwd_states_kernel<T, DK>), sg, dim3(kSer), 0, s, a);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
   if (ds_mma) e = launch_chunk_bwd_dstate_mma(a, s);
   else {
     hipLaunchKernelGGL((bwd_dstate_kernel<T, DK>), sg, dim3(kSer), 0, s, a);

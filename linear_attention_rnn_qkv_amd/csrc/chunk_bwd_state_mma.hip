@@ -19,8 +19,14 @@
 // term carries a relative error near 2^-16.
 //
 // One workgroup = (sequence, value head, 16 rows of dv), eight wavefronts,
-// one barrier per step:
-//   wave 0     the chain: every product above, dS in accumulators;
+// two barriers per step (B0 at its start, B1 in its middle):
+//   wave 0     the chain: before B1 U = K dS^T, after it dDelta, dR' and the
+//              K^T part of the update; dS in accumulators;
+//   wave 1     the products that do not depend on dS: before B1
+//              G = P'^T dO (read by the chain after B1), after it the q term
+//              Q^T (fq (.) dO) (added to dS by the chain at the next step);
+//              and the stores of the previous step's dR' and dv from a
+//              two-slot LDS stage, so that the chain issues only dS_C's;
 //   waves 2-7  copies (global_load_lds) of the k and q tiles, the dO slice
 //              and the record of the next chunk into a two-slot LDS ring.
 #include "chunk_bwd_common.h"
@@ -66,6 +72,12 @@ __device__ __forceinline__ void split2x4(f32x4 a, f32x4 b, f8 &hi, f8 &lo) {
   lo = cat8<bf16>(al, bl);
 }
 
+// the reverse pass copies bytes [kBrF, kBrBytes) of each record: offsets
+// within its copy
+constexpr int64_t kDsRec = kBrBytes - kBrF;
+constexpr int64_t kDsF = 0, kDsMtH = kBrMtH - kBrF, kDsMtL = kBrMtL - kBrF, kDsPH = kBrPH - kBrF,
+                  kDsPL = kBrPL - kBrF;
+
 template <int DK>
 struct DsLds {
   static constexpr int RB = DK * 2;
@@ -73,7 +85,10 @@ struct DsLds {
   alignas(16) unsigned char k[2][TILE];   // raw k rows of the step's chunk (swizzled)
   alignas(16) unsigned char q[2][TILE];   // raw q rows
   alignas(16) bf16 o[2][BT * DVT];        // dO slice [64][16]
-  alignas(16) unsigned char rec[2][kBrBytes];
+  alignas(16) unsigned char rec[2][kDsRec];
+  alignas(16) float gg[4 * 64 * 4];        // G = P'^T dO, accumulator layout [mt][lane][4]
+  alignas(16) float hq[DK / 16 * 64 * 4];  // q term of the state update, [mt][lane][4]
+  alignas(16) float stage[2][4 * 64 * 4 + 64];  // dR' [mt][lane][4], then beta
 };
 
 template <int N> struct Slot { static constexpr int v = N; };
@@ -92,7 +107,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
   using SM = DsLds<DK>;
   constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB;
   constexpr int NI = SM::TILE / 1024;           // 1 KB copies per q/k tile
-  constexpr int NR = (int)(kBrBytes / 1024);    // 1 KB copies per record
+  constexpr int NR = (int)(kDsRec / 1024);      // 1 KB copies per record
   static_assert(NI % 2 == 0 && NR % 2 == 0 && NI / 2 <= 31 && NR / 2 + 1 <= 31, "copy split");
   __shared__ SM sm;
 
@@ -126,19 +141,34 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
   };
   const int64_t st_base = ((n * p.Hv + h) * p.dv + j0) * DK;
 
+  // fragment offsets shared by the compute waves
+  int fo[KT];  // row c of a 16-row tile, dk 32 pp + 8 g .. + 7
+#pragma unroll
+  for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
+  // transposing-read offsets (K^T, Q^T fragments; see the forward state kernel)
+  const int yrow = 4 * g + (c >> 2);
+  int trc[NT];
+#pragma unroll
+  for (int mt = 0; mt < NT; ++mt)
+    trc[mt] = yrow * RB + (((4 * (mt >> 1) + (c & 3)) ^ kswz<DK>(yrow)) << 4) + 8 * (mt & 1);
+  const int otr = (4 * g + (c >> 2)) * (DVT * 2) + 8 * (c & 3);
+  // dO fragments of slot sl (B operand, k slots in tile-pair order), exact
+  auto dO_frags = [&](int sl, f8 (&Bo)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const unsigned char *ob = reinterpret_cast<const unsigned char *>(sm.o[sl]) + otr + 32 * q * (DVT * 2);
+      const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ob));
+      const s16x4 r1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ob + 16 * DVT * 2));
+      Bo[q] = cat8<bf16>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
+    }
+  };
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // Steps s = -1 .. Nc - 1, two barriers each (B0 at the start, B1 in the
+  // middle) in every wave, then one more after the last step.
   if (wave == 0) {
     // ---------------------------------------------------------------- chain
-    int fo[KT];  // row c of a 16-row tile, dk 32 pp + 8 g .. + 7
-#pragma unroll
-    for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
-    // transposing-read offsets (K^T, Q^T fragments; see the forward state kernel)
-    const int yrow = 4 * g + (c >> 2);
-    int trc[NT];
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
-      trc[mt] = yrow * RB + (((4 * (mt >> 1) + (c & 3)) ^ kswz<DK>(yrow)) << 4) + 8 * (mt & 1);
-    const int otr = (4 * g + (c >> 2)) * (DVT * 2) + 8 * (c & 3);
-
     f32x4 dS[NT];  // dS[mt][i] = dS[dv row c][dk dk_of(mt, 4 g + i)]
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt)
@@ -147,25 +177,24 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
         dS[mt][i] = p.d_final ? p.d_final[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] : 0.f;
 
     for_steps2(Nc - 1, [&](int s, auto SL) {
-      lds_barrier();
-      if (s < 0) return;
+      lds_barrier();  // B0
       constexpr int sl = decltype(SL)::v;
       const int ch = Nc - 1 - s;
-      const int64_t gc = gc0 + ch, t0 = bos + (int64_t)ch * BT;
-      const int nr = rows_of(ch);
-      const unsigned char *kt = sm.k[sl], *qt = sm.q[sl], *rec = sm.rec[sl];
-      const float *fa = reinterpret_cast<const float *>(rec + kBrF);
-      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-
-      // dS_C to the workspace (the gradient kernel reads it as [dv][dk])
-      {
+      const int64_t gc = gc0 + ch;
+      const unsigned char *kt = sm.k[sl], *rec = sm.rec[sl];
+      const float *fa = reinterpret_cast<const float *>(rec + kDsF);
+      f32x4 U[4];
+      if (s >= 0) {
+        // the q term of the previous step, then dS_C of this chunk to the
+        // workspace (the gradient kernel reads it as [dv][dk])
+        if (s > 0) {
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt) dS[mt] += *reinterpret_cast<const f32x4 *>(&sm.hq[(mt * 64 + lane) * 4]);
+        }
         float *dsw = p.ds + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(dsw + dk_of(mt, 4 * g)) = dS[mt];
-      }
-      // U = K dS^T (raw k rows), then dDelta = cw rk (.) U + P'^T dO
-      f32x4 dD[4];
-      {
+        // U = K dS^T (raw k rows)
         f8 Sh[KT], Sl[KT];
 #pragma unroll
         for (int pp = 0; pp < KT; ++pp) split2x4(dS[2 * pp], dS[2 * pp + 1], Sh[pp], Sl[pp]);
@@ -178,31 +207,18 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
             u = mma(kf, Sh[pp], u);
             u = mma(kf, Sl[pp], u);
           }
-          const f32x4 cr = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 16 * mt + 4 * g]);
-          dD[mt] = u * cr;
+          U[mt] = u;
         }
       }
-      // dO fragments (B operand, k slots in tile-pair order), exact
-      f8 Bo[2];
+      lds_barrier();  // B1: G of this chunk is in LDS
+      if (s < 0) return;
+      // dDelta = cw rk (.) U + P'^T dO
+      f32x4 dD[4];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const unsigned char *ob = reinterpret_cast<const unsigned char *>(sm.o[sl]) + otr + 32 * q * (DVT * 2);
-        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ob));
-        const s16x4 r1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ob + 16 * DVT * 2));
-        Bo[q] = cat8<bf16>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 cr = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 16 * mt + 4 * g]);
+        dD[mt] = U[mt] * cr + *reinterpret_cast<const f32x4 *>(&sm.gg[(mt * 64 + lane) * 4]);
       }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          if (q == 0 && mt >= 2) continue;
-          const int f = up_frag(mt, q);
-          const f8 ph = *reinterpret_cast<const f8 *>(rec + kBrPH + f * 1024 + lane * 16);
-          const f8 pl = *reinterpret_cast<const f8 *>(rec + kBrPL + f * 1024 + lane * 16);
-          dD[mt] = mma(ph, Bo[q], dD[mt]);
-          dD[mt] = mma(pl, Bo[q], dD[mt]);
-        }
       // dR' = M^T dDelta
       f32x4 dR[4];
       {
@@ -216,8 +232,8 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           for (int q = 0; q < 2; ++q) {
             if (q == 0 && mt >= 2) continue;
             const int f = up_frag(mt, q);
-            const f8 mh = *reinterpret_cast<const f8 *>(rec + kBrMtH + f * 1024 + lane * 16);
-            const f8 ml = *reinterpret_cast<const f8 *>(rec + kBrMtL + f * 1024 + lane * 16);
+            const f8 mh = *reinterpret_cast<const f8 *>(rec + kDsMtH + f * 1024 + lane * 16);
+            const f8 ml = *reinterpret_cast<const f8 *>(rec + kDsMtL + f * 1024 + lane * 16);
             r = mma(mh, Dh[q], r);
             r = mma(mh, Dl[q], r);
             r = mma(ml, Dh[q], r);
@@ -225,37 +241,19 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           dR[mt] = r;
         }
       }
-      // dR' (FP32) and dv = beta dR' (rows of the chunk only)
+      // dR' and beta to the stage; wave 1 stores them (and dv) next step
+      {
+        float *stg = sm.stage[sl];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 bt = *reinterpret_cast<const f32x4 *>(&fa[2 * BT + 16 * mt + 4 * g]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * mt + 4 * g + i;
-          p.drp[((gc * p.Hv + h) * BT + t) * p.dv + j0 + c] = dR[mt][i];
-          if (t < nr) {
-            const int64_t o = brow * p.sdv_b + (t0 + t) * p.sdv_t + h * p.dv + j0 + c;
-            const float x = bt[i] * dR[mt][i];
-            if (p.grad_dtype == kF32) static_cast<float *>(p.dvv)[o] = x;
-            else static_cast<bf16 *>(p.dvv)[o] = to<bf16>(x);
-          }
-        }
+        for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4 *>(&stg[(mt * 64 + lane) * 4]) = dR[mt];
+        stg[4 * 64 * 4 + lane] = fa[2 * BT + lane];
       }
-      // dS0 = e^{gamma_C} dS + Q^T (fq (.) dO) + K^T (fk (.) dR')
-      f8 Fqh[2], Fql[2], Fkh[2], Fkl[2];
+      // dS0 = e^{gamma_C} dS + K^T (fk (.) dR') (+ the q term, next step)
+      f8 Fkh[2], Fkl[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const f32x4 fq0 = *reinterpret_cast<const f32x4 *>(&fa[3 * BT + 32 * q + 4 * g]);
-        const f32x4 fq1 = *reinterpret_cast<const f32x4 *>(&fa[3 * BT + 32 * q + 16 + 4 * g]);
         const f32x4 fk0 = *reinterpret_cast<const f32x4 *>(&fa[4 * BT + 32 * q + 4 * g]);
         const f32x4 fk1 = *reinterpret_cast<const f32x4 *>(&fa[4 * BT + 32 * q + 16 + 4 * g]);
-        float xq[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xq[e] = fq0[e] * f(Bo[q][e]);
-          xq[4 + e] = fq1[e] * f(Bo[q][4 + e]);
-        }
-        split8(xq, Fqh[q], Fql[q]);
         split2x4(fk0 * dR[2 * q], fk1 * dR[2 * q + 1], Fkh[q], Fkl[q]);
       }
       const float eC = fa[5 * BT];
@@ -264,29 +262,118 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
         f32x4 a = dS[mt] * eC;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const unsigned char *qa1 = qt + trc[mt] + (32 * q) * RB, *qa2 = qt + trc[mt] + (32 * q + 16) * RB;
           const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
-          const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(qa1));
-          const s16x4 q2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(qa2));
           const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
           const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
-          const f8 qT = cat8<bf16>(__builtin_bit_cast(v4, q1), __builtin_bit_cast(v4, q2));
           const f8 kT = cat8<bf16>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
-          a = mma(qT, Fqh[q], a);
-          a = mma(qT, Fql[q], a);
           a = mma(kT, Fkh[q], a);
           a = mma(kT, Fkl[q], a);
         }
         dS[mt] = a;
       }
     });
+    lds_barrier();  // the last q term is in LDS
+    if (Nc > 0) {
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) dS[mt] += *reinterpret_cast<const f32x4 *>(&sm.hq[(mt * 64 + lane) * 4]);
+    }
     if (p.d_init) {
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
         *reinterpret_cast<f32x4 *>(p.d_init + st_base + (int64_t)c * DK + dk_of(mt, 4 * g)) = dS[mt];
     }
   } else if (wave == 1) {
-    for_steps2(Nc - 1, [&](int, auto) { lds_barrier(); });
+    // --------------------------------------- G = P'^T dO, q term, stores
+    // stage of step s2 (chunk Nc - 1 - s2) to dR' (FP32) and dv = beta dR'
+    auto store_stage = [&](int s2, const float *stg) {
+      const int ch = Nc - 1 - s2;
+      const int64_t gc = gc0 + ch, t0 = bos + (int64_t)ch * BT;
+      const int nr = rows_of(ch);
+      const int t = lane, mt = t >> 4, gg = (t >> 2) & 3, i = t & 3;
+      float x[16];
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc) x[cc] = stg[(mt * 64 + 16 * gg + cc) * 4 + i];
+      float *dr = p.drp + ((gc * p.Hv + h) * BT + t) * p.dv + j0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        *reinterpret_cast<f32x4 *>(dr + 4 * v) = f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
+      if (t < nr) {
+        const float bt = stg[4 * 64 * 4 + t];
+        const int64_t o = brow * p.sdv_b + (t0 + t) * p.sdv_t + h * p.dv + j0;
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) x[cc] *= bt;
+        if (p.grad_dtype == kF32) {
+          float *dv = static_cast<float *>(p.dvv) + o;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            *reinterpret_cast<f32x4 *>(dv + 4 * v) = f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
+        } else {
+          bf16 *dv = static_cast<bf16 *>(p.dvv) + o;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            *reinterpret_cast<v4 *>(dv + 4 * v) =
+                __builtin_convertvector(f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]}, v4);
+        }
+      }
+    };
+    for_steps2(Nc - 1, [&](int s, auto SL) {
+      lds_barrier();  // B0
+      constexpr int sl = decltype(SL)::v;
+      const unsigned char *qt = sm.q[sl], *rec = sm.rec[sl];
+      const float *fa = reinterpret_cast<const float *>(rec + kDsF);
+      f8 Bo[2];
+      if (s >= 0) {
+        dO_frags(sl, Bo);
+        // G = P'^T dO in the accumulator layout of dDelta
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 a = zero4;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            if (q == 0 && mt >= 2) continue;
+            const int f = up_frag(mt, q);
+            const f8 ph = *reinterpret_cast<const f8 *>(rec + kDsPH + f * 1024 + lane * 16);
+            const f8 pl = *reinterpret_cast<const f8 *>(rec + kDsPL + f * 1024 + lane * 16);
+            a = mma(ph, Bo[q], a);
+            a = mma(pl, Bo[q], a);
+          }
+          *reinterpret_cast<f32x4 *>(&sm.gg[(mt * 64 + lane) * 4]) = a;
+        }
+      }
+      if (s >= 1) store_stage(s - 1, sm.stage[(sl + 1) % 2]);
+      lds_barrier();  // B1
+      if (s < 0) return;
+      // q term Q^T (fq (.) dO), added to dS by the chain at the next step
+      f8 Fqh[2], Fql[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f32x4 fq0 = *reinterpret_cast<const f32x4 *>(&fa[3 * BT + 32 * q + 4 * g]);
+        const f32x4 fq1 = *reinterpret_cast<const f32x4 *>(&fa[3 * BT + 32 * q + 16 + 4 * g]);
+        float xq[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xq[e] = fq0[e] * f(Bo[q][e]);
+          xq[4 + e] = fq1[e] * f(Bo[q][4 + e]);
+        }
+        split8(xq, Fqh[q], Fql[q]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        f32x4 a = zero4;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const unsigned char *qa1 = qt + trc[mt] + (32 * q) * RB, *qa2 = qt + trc[mt] + (32 * q + 16) * RB;
+          const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(qa1));
+          const s16x4 q2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(qa2));
+          const f8 qT = cat8<bf16>(__builtin_bit_cast(v4, q1), __builtin_bit_cast(v4, q2));
+          a = mma(qT, Fqh[q], a);
+          a = mma(qT, Fql[q], a);
+        }
+        *reinterpret_cast<f32x4 *>(&sm.hq[(mt * 64 + lane) * 4]) = a;
+      }
+    });
+    lds_barrier();
+    if (Nc > 0) store_stage(Nc - 1, sm.stage[(Nc - 1) % 2]);
   } else {
     // ------------------------------------------------------------- loads
     // Waves 2, 3 copy the halves of the k tile, waves 4, 5 those of the q
@@ -332,8 +419,10 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
             }
           }
         }
+        lds_barrier();  // B1
         wait_vm<0>();
       });
+      lds_barrier();
     } else {
       constexpr int NRH = NR / 2;
       const int half = role - 4;
@@ -345,7 +434,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           const int ch = Nc - 2 - s;
           const int nr = rows_of(ch);
           const int64_t t0 = (int64_t)ch * BT;
-          const unsigned char *rg = p.brec + ((gc0 + ch) * p.Hv + h) * kBrBytes + 1024 * NRH * half;
+          const unsigned char *rg = p.brec + ((gc0 + ch) * p.Hv + h) * kBrBytes + kBrF + 1024 * NRH * half;
 #pragma unroll
           for (int i = 0; i < NRH; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * (NRH * half + i));
           // dO rows past the chunk's end repeat its last row (their factors are 0)
@@ -354,10 +443,299 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           g2l16(ob + (t0 + rr) * p.sdo_t + 8 * (lane & 1),
                 reinterpret_cast<unsigned char *>(sm.o[sl]) + 1024 * half);
         }
+        lds_barrier();  // B1
         wait_vm<0>();
+      });
+      lds_barrier();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward-state pass: per (sequence, value head, 16 value rows), serial over
+// the chunks in order, the state S (16 x dk) is carried in FP32 MFMA
+// accumulators and each chunk gives (raw BF16 k rows, factors from the
+// record)
+//
+//   U = K S^T,   R = V - (e^gamma rk) (.) U,   Delta = M (beta (.) R)
+//   S <- e^{gamma_C} S + K^T ((cw rk) (.) Delta)
+//
+// writing S0 (the state entering the chunk), R and Delta in FP32 for the
+// gradient kernel. Split operands as in the reverse pass. Wavefronts: 0 the
+// chain; 1 stores the previous step's R and Delta from a two-slot LDS stage;
+// 2-7 copy the k tile, the v slice and the record's [0, kBrMtH) part of the
+// chunk two steps ahead into a three-slot ring (one barrier per step).
+// ---------------------------------------------------------------------------
+template <int DK>
+struct StLds {
+  static constexpr int RB = DK * 2;
+  static constexpr int TILE = BT * RB;
+  alignas(16) unsigned char k[3][TILE];
+  alignas(16) bf16 v[3][BT * DVT];
+  alignas(16) unsigned char rec[3][kBrMtH];
+  alignas(16) float stage[2][2 * 4 * 64 * 4];  // R, then Delta, [mt][lane][4]
+};
+
+// Runs body(s, Slot<s mod 3>) for s = -2 .. last in order.
+template <typename F>
+__device__ __forceinline__ void for_steps3(int last, F &&body) {
+  for (int base = -3; base <= last; base += 3) {
+    if (base >= -2) body(base, Slot<0>{});
+    if (base + 1 >= -2 && base + 1 <= last) body(base + 1, Slot<1>{});
+    if (base + 2 <= last) body(base + 2, Slot<2>{});
+  }
+}
+
+template <int DK>
+__global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
+  using SM = StLds<DK>;
+  constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB;
+  constexpr int NI = SM::TILE / 1024;        // 1 KB copies per k tile
+  constexpr int NR = (int)(kBrMtH / 1024);   // 1 KB copies per record part
+  static_assert(NI % 4 == 0 && NR % 2 == 0, "copy split");
+  __shared__ SM sm;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
+  const int64_t j0 = (lid % ntile) * DVT;
+  const int64_t h = (lid / ntile) % gridDim.y;
+  const int64_t n = lid / (ntile * gridDim.y);
+  const int64_t hk = h / (p.Hv / p.Hqk);
+  int64_t brow, bos, L, gc0;
+  if (p.cu_seqlens) {
+    brow = 0;
+    bos = p.cu_seqlens[n];
+    L = p.cu_seqlens[n + 1] - bos;
+    gc0 = p.cu_chunks[n];
+  } else {
+    brow = n;
+    bos = 0;
+    L = p.T;
+    gc0 = n * ((p.T + BT - 1) / BT);
+  }
+  const int Nc = (int)((L + BT - 1) / BT);
+  auto rows_of = [&](int ch) -> int {
+    const int64_t r = L - (int64_t)ch * BT;
+    return (int)(r < BT ? r : BT);
+  };
+  const int64_t st_base = ((n * p.Hv + h) * p.dv + j0) * DK;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  if (wave == 0) {
+    // ---------------------------------------------------------------- chain
+    int fo[KT];
+#pragma unroll
+    for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
+    const int yrow = 4 * g + (c >> 2);
+    int trc[NT];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+      trc[mt] = yrow * RB + (((4 * (mt >> 1) + (c & 3)) ^ kswz<DK>(yrow)) << 4) + 8 * (mt & 1);
+    const int vtr = (4 * g + (c >> 2)) * (DVT * 2) + 8 * (c & 3);
+    f32x4 S[NT];  // S[mt][i] = S[dv row c][dk dk_of(mt, 4 g + i)]
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[mt][i] = p.init_state ? p.init_state[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] : 0.f;
+    for_steps3(Nc, [&](int s, auto SL) {
+      lds_barrier();
+      if (s < 0 || s >= Nc) return;
+      constexpr int sl = decltype(SL)::v;
+      const int64_t gc = gc0 + s;
+      const unsigned char *kt = sm.k[sl], *rec = sm.rec[sl];
+      const float *fa = reinterpret_cast<const float *>(rec + kBrF);
+      {  // S0 to the workspace ([dv][dk])
+        float *sw = p.s0 + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(sw + dk_of(mt, 4 * g)) = S[mt];
+      }
+      // U = K S^T
+      f32x4 U[4];
+      {
+        f8 Sh[KT], Sl[KT];
+#pragma unroll
+        for (int pp = 0; pp < KT; ++pp) split2x4(S[2 * pp], S[2 * pp + 1], Sh[pp], Sl[pp]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 u = zero4;
+#pragma unroll
+          for (int pp = 0; pp < KT; ++pp) {
+            const f8 kf = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
+            u = mma(kf, Sh[pp], u);
+            u = mma(kf, Sl[pp], u);
+          }
+          U[mt] = u;
+        }
+      }
+      // R = V - e^gamma rk (.) U; X = beta (.) R
+      f8 Bv[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const unsigned char *vb = reinterpret_cast<const unsigned char *>(sm.v[sl]) + vtr + 32 * q * (DVT * 2);
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb));
+        const s16x4 r1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb + 16 * DVT * 2));
+        Bv[q] = cat8<bf16>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
+      }
+      float *stg = sm.stage[s & 1];
+      f32x4 X[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 er = *reinterpret_cast<const f32x4 *>(&fa[6 * BT + 16 * mt + 4 * g]);
+        const f32x4 bt = *reinterpret_cast<const f32x4 *>(&fa[2 * BT + 16 * mt + 4 * g]);
+        f32x4 vv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[i] = f(Bv[mt >> 1][4 * (mt & 1) + i]);
+        const f32x4 r = vv - er * U[mt];
+        *reinterpret_cast<f32x4 *>(&stg[(mt * 64 + lane) * 4]) = r;
+        X[mt] = bt * r;
+      }
+      // Delta = M X
+      f32x4 Dl4[4];
+      {
+        f8 Xh[2], Xl[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) split2x4(X[2 * q], X[2 * q + 1], Xh[q], Xl[q]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 d = zero4;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            if (q == 1 && mt < 2) continue;
+            const int fi = q == 0 ? mt : 2 + mt;
+            const f8 mh = *reinterpret_cast<const f8 *>(rec + kBrMH + fi * 1024 + lane * 16);
+            const f8 ml = *reinterpret_cast<const f8 *>(rec + kBrML + fi * 1024 + lane * 16);
+            d = mma(mh, Xh[q], d);
+            d = mma(mh, Xl[q], d);
+            d = mma(ml, Xh[q], d);
+          }
+          Dl4[mt] = d;
+          *reinterpret_cast<f32x4 *>(&stg[((4 + mt) * 64 + lane) * 4]) = d;
+        }
+      }
+      // S = e^{gamma_C} S + K^T (cw rk (.) Delta)
+      f8 Bwh[2], Bwl[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 32 * q + 4 * g]);
+        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 32 * q + 16 + 4 * g]);
+        split2x4(c0 * Dl4[2 * q], c1 * Dl4[2 * q + 1], Bwh[q], Bwl[q]);
+      }
+      const float eC = fa[5 * BT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        f32x4 a = S[mt] * eC;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
+          const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
+          const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
+          const f8 kT = cat8<bf16>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
+          a = mma(kT, Bwh[q], a);
+          a = mma(kT, Bwl[q], a);
+        }
+        S[mt] = a;
+      }
+    });
+  } else if (wave == 1) {
+    // ------------------------------------ R and Delta of the previous step
+    for_steps3(Nc, [&](int s, auto) {
+      lds_barrier();
+      const int ch = s - 1;
+      if (ch < 0 || ch >= Nc) return;
+      const float *stg = sm.stage[ch & 1];
+      const int64_t gc = gc0 + ch;
+      const int t = lane, mt = t >> 4, gg = (t >> 2) & 3, i = t & 3;
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        float x[16];
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) x[cc] = stg[((4 * a + mt) * 64 + 16 * gg + cc) * 4 + i];
+        float *dst = (a == 0 ? p.rr : p.del) + ((gc * p.Hv + h) * BT + t) * p.dv + j0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          *reinterpret_cast<f32x4 *>(dst + 4 * v) = f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
+      }
+    });
+  } else {
+    // ------------------------------------------------------------- loads
+    // waves 2-5: quarters of the k tile; waves 6, 7: halves of the record
+    // part and of the v slice; for the chunk of step s + 2
+    const int role = wave - 2;
+    if (role < 4) {
+      constexpr int NQ = NI / 4;
+      const int i0 = role * NQ;
+      const bf16 *xb = static_cast<const bf16 *>(p.k) + brow * p.sk_b + hk * p.sk_h + bos * p.sk_t;
+      uint32_t xoff[NQ];
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int b = 1024 * (i0 + i) + 16 * lane;
+        const int r = b / RB, jp = (b % RB) >> 4;
+        const int j = jp ^ kswz<DK>(r);
+        xoff[i] = (uint32_t)(((int64_t)r * p.sk_t + 8 * j) * 2);
+      }
+      for_steps3(Nc, [&](int s, auto SL) {
+        lds_barrier();
+        constexpr int sl = (decltype(SL)::v + 2) % 3;
+        const int cl = s + 2;
+        const bool issue = cl < Nc;
+        if (issue) {
+          const int nr = rows_of(cl);
+          const int64_t t0 = (int64_t)cl * BT;
+          unsigned char *xt = sm.k[sl] + 1024 * i0;
+          if (nr == BT) {
+            const unsigned char *xg = reinterpret_cast<const unsigned char *>(xb + t0 * p.sk_t);
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) g2l16(xg + xoff[i], xt + 1024 * i);
+          } else {
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+              const int b = 1024 * (i0 + i) + 16 * lane;
+              const int r = b / RB, jp = (b % RB) >> 4;
+              const int j = jp ^ kswz<DK>(r);
+              const int rr = r < nr ? r : nr - 1;
+              g2l16(xb + (t0 + rr) * p.sk_t + 8 * j, xt + 1024 * i);
+            }
+          }
+        }
+        // the previous step's copies are complete before the next barrier
+        if (issue) wait_vm<NQ>(); else wait_vm<0>();
+      });
+    } else {
+      constexpr int NRH = NR / 2;
+      const int half = role - 4;
+      const bf16 *vb = static_cast<const bf16 *>(p.v) + brow * p.sv_b + h * p.sv_h + j0 + bos * p.sv_t;
+      for_steps3(Nc, [&](int s, auto SL) {
+        lds_barrier();
+        constexpr int sl = (decltype(SL)::v + 2) % 3;
+        const int cl = s + 2;
+        const bool issue = cl < Nc;
+        if (issue) {
+          const int nr = rows_of(cl);
+          const int64_t t0 = (int64_t)cl * BT;
+          const unsigned char *rg = p.brec + ((gc0 + cl) * p.Hv + h) * kBrBytes + 1024 * NRH * half;
+#pragma unroll
+          for (int i = 0; i < NRH; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * (NRH * half + i));
+          // v rows past the chunk's end repeat its last row (beta is 0 there)
+          const int r = 32 * half + (lane >> 1);
+          const int rr = r < nr ? r : nr - 1;
+          g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane & 1), reinterpret_cast<unsigned char *>(sm.v[sl]) + 1024 * half);
+        }
+        if (issue) wait_vm<NRH + 1>(); else wait_vm<0>();
       });
     }
   }
+}
+
+template <int DK>
+hipError_t launch_st(const ChunkBwdArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)(a.dv / DVT), (unsigned)a.Hv, (unsigned)a.n_seqs);
+  hipLaunchKernelGGL((bwd_states_mma_kernel<DK>), grid, dim3(kThr), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int DK>
@@ -369,19 +747,28 @@ hipError_t launch_ds(const ChunkBwdArgs &a, hipStream_t s) {
 
 }  // namespace
 
-// BF16 activations, dk 64 or 128, dv a multiple of 16; q, k and d_o rows
-// 16-byte aligned (LDS DMA copies).
+// BF16 activations, dk 64 or 128, dv a multiple of 16; q, k, v and d_o rows
+// 16-byte aligned (LDS DMA copies), dv rows aligned to 4 elements.
 bool chunk_bwd_state_mma_supported(const ChunkBwdArgs &a) {
   if (a.act != kBF16 || !(a.dk == 64 || a.dk == 128) || a.dv % 16 != 0) return false;
+  const uint64_t vva = (uint64_t)(uintptr_t)a.v | (uint64_t)(a.sv_b * 2) | (uint64_t)(a.sv_t * 2) | (uint64_t)(a.sv_h * 2);
+  if (align_of_host(vva) < 16) return false;
   const uint64_t qa = (uint64_t)(uintptr_t)a.q | (uint64_t)(a.sq_b * 2) | (uint64_t)(a.sq_t * 2) | (uint64_t)(a.sq_h * 2);
   const uint64_t ka = (uint64_t)(uintptr_t)a.k | (uint64_t)(a.sk_b * 2) | (uint64_t)(a.sk_t * 2) | (uint64_t)(a.sk_h * 2);
   const uint64_t oa =
       (uint64_t)(uintptr_t)a.d_o | (uint64_t)(a.sdo_b * 2) | (uint64_t)(a.sdo_t * 2) | (uint64_t)(a.sdo_h * 2);
-  return align_of_host(qa) >= 16 && align_of_host(ka) >= 16 && align_of_host(oa) >= 16;
+  const int64_t es = a.grad_dtype == kF32 ? 4 : 2;
+  const uint64_t va = (uint64_t)(uintptr_t)a.dvv | (uint64_t)(a.sdv_b * es) | (uint64_t)(a.sdv_t * es);
+  return align_of_host(qa) >= 16 && align_of_host(ka) >= 16 && align_of_host(oa) >= 16 &&
+         align_of_host(va) >= (int)(4 * es > 16 ? 16 : 4 * es);
 }
 
 hipError_t launch_chunk_bwd_dstate_mma(const ChunkBwdArgs &a, hipStream_t s) {
   return a.dk == 64 ? launch_ds<64>(a, s) : launch_ds<128>(a, s);
+}
+
+hipError_t launch_chunk_bwd_states_mma(const ChunkBwdArgs &a, hipStream_t s) {
+  return a.dk == 64 ? launch_st<64>(a, s) : launch_st<128>(a, s);
 }
 
 }  // namespace gdn

@@ -183,16 +183,19 @@ struct ChunkBwdArgs {
 };
 
 // Backward record per (chunk, value head), written by the backward prep for
-// the matrix-core reverse pass: MFMA A-operand fragments of M^T and of P'^T
-// (M = (I + A)^-1, P' = scale * masked decayed q.k with its rows past the
-// chunk's end zeroed), each as BF16 hi and lo parts (x = hi + lo), then FP32
-// factor rows [6][64]: e^gamma, cw rk, beta, scale e^gamma rq (0 past the
-// end), -e^gamma beta rk, and e^{gamma_C} at [5][0]. Both matrices are upper
-// triangular; fragment f = (row tile mt, k pair q) in the order (0,0) (1,0)
-// (0,1) (1,1) (2,1) (3,1); element e of lane 16 g + c is
-// X[16 mt + c][32 q + 16 (e / 4) + 4 g + e % 4].
-constexpr int64_t kBrMtH = 0, kBrMtL = 6144, kBrPH = 12288, kBrPL = 18432, kBrF = 24576;
-constexpr int64_t kBrBytes = 26624;
+// the matrix-core state passes: MFMA A-operand fragments of M, of M^T and of
+// P'^T (M = (I + A)^-1, P' = scale * masked decayed q.k with its rows past the
+// chunk's end zeroed), each as BF16 hi and lo parts (x = hi + lo), and FP32
+// factor rows [8][64]: e^gamma, cw rk, beta, scale e^gamma rq (0 past the
+// end), -e^gamma beta rk, e^{gamma_C} at [5][0], e^gamma rk. Fragment
+// element e of lane 16 g + c of fragment (row tile mt, k pair q) is
+// X[16 mt + c][32 q + 16 (e / 4) + 4 g + e % 4]; M (lower triangular) has
+// fragments (0,0) (1,0) (2,0) (3,0) (2,1) (3,1), M^T and P'^T (upper) have
+// (0,0) (1,0) (0,1) (1,1) (2,1) (3,1). The forward-state pass reads
+// [0, kBrMtH), the reverse pass [kBrF, kBrBytes).
+constexpr int64_t kBrMH = 0, kBrML = 6144, kBrF = 12288, kBrMtH = 14336, kBrMtL = 20480, kBrPH = 26624,
+                  kBrPL = 32768;
+constexpr int64_t kBrBytes = 38912;
 
 // Each returns the HIP error of the launch (hipSuccess if queued).
 hipError_t launch_prologue(const PrologueArgs &a, hipStream_t s);
@@ -222,6 +225,7 @@ hipError_t launch_chunk_bwd_grad_mma(const ChunkBwdArgs &a, hipStream_t s);
 // 128, 16-byte aligned q, k and d_o rows); needs a.brec written by the prep.
 bool chunk_bwd_state_mma_supported(const ChunkBwdArgs &a);
 hipError_t launch_chunk_bwd_dstate_mma(const ChunkBwdArgs &a, hipStream_t s);
+hipError_t launch_chunk_bwd_states_mma(const ChunkBwdArgs &a, hipStream_t s);
 
 // Device address of the static chunk scratch (GDN_NOALLOC_SCRATCH_BYTES) on
 // the current device; looked up once per device.

@@ -276,11 +276,11 @@ def test_chunk_rule_bwd_workspace_bytes_and_rejections():
     a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
     # dense B=2, T=100: 4 chunk rows. Chunk offsets, unit q and k rows, their
     # inverse norms, gamma, (I + A)^-1 and P, S0 and dS, then R, Delta, dR',
-    # then the 26624-byte records of the matrix-core reverse pass
+    # then the 38912-byte records of the matrix-core state passes
     cb, Hqk, dk, Hv, dv = 4, 2, 64, 4, 32
     expect = (a256(3 * 4) + 2 * a256(cb * Hqk * 64 * dk * 4) + 2 * a256(cb * Hqk * 64 * 4) +
               a256(cb * Hv * 64 * 4) + 2 * a256(cb * Hv * 64 * 64 * 4) + 2 * a256(cb * Hv * dv * dk * 4) +
-              3 * a256(cb * Hv * 64 * dv * 4) + a256(cb * Hv * 26624))
+              3 * a256(cb * Hv * 64 * dv * 4) + a256(cb * Hv * 38912))
     assert gdn.gdn_chunk_rule_bwd_workspace_bytes(2, 100, (Hqk, dk, Hv, dv)) == expect
     # packed: ceil(T / 64) + n_seqs rows
     assert gdn.gdn_chunk_rule_bwd_workspace_bytes(1, 100, (1, 128, 1, 64), n_seqs=3) > 0
