@@ -285,16 +285,17 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
     sk = group_sum<4>(sk);
     const float rq = p.use_l2 ? 1.f / sqrtf(sq + p.l2_eps) : 1.f;
     const float rk = p.use_l2 ? 1.f / sqrtf(sk + p.l2_eps) : 1.f;
-    float *qn = p.qn + ((gc * p.Hqk + hk) * BT + t) * DK + part * SEG;
-    float *kn = p.kn + ((gc * p.Hqk + hk) * BT + t) * DK + part * SEG;
+    const int64_t un = ((gc * p.Hqk + hk) * BT + t) * DK + part * SEG;  // unit rows (when written)
 #pragma unroll
     for (int q = 0; q < SEG; q += 4) {
       float a[4] = {qv[q] * rq, qv[q + 1] * rq, qv[q + 2] * rq, qv[q + 3] * rq};
       float b[4] = {kv[q] * rk, kv[q + 1] * rk, kv[q + 2] * rk, kv[q + 3] * rk};
       stv<4>(sQ + t * KP + part * SEG + q, a);
       stv<4>(sK + t * KP + part * SEG + q, b);
-      stv<4>(qn + q, a);
-      stv<4>(kn + q, b);
+      if (p.qn) {
+        stv<4>(p.qn + un + q, a);
+        stv<4>(p.kn + un + q, b);
+      }
     }
     if (part == 0) {
       p.rq[(gc * p.Hqk + hk) * BT + t] = rq;
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
     __syncthreads();
     // A (strict lower, beta-weighted) to LDS; scale * Pt to the workspace
     {
-      float *pp = p.pp + (gc * p.Hv + h) * BT * BT;
+      const int64_t pb = (gc * p.Hv + h) * BT * BT;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * rg + r;
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
           pv[c] = p.scale * e * qk[r][c];
           sP[t * MP + s] = t < nr ? pv[c] : 0.f;
         }
-        stv<4>(pp + t * BT + 4 * cg, pv);
+        if (p.pp) stv<4>(p.pp + pb + t * BT + 4 * cg, pv);
       }
     }
     __syncthreads();
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
       for (int u = 0; u < 16; ++u) sM[(4 * u + part) * MP + c] = mr[u];
     }
     __syncthreads();
-    {
+    if (p.mm) {
       float *mm_ = p.mm + (gc * p.Hv + h) * BT * BT;
       for (int e = tid; e < BT * BT; e += kThreads) mm_[e] = sM[(e >> 6) * MP + (e & 63)];
     }
@@ -965,10 +966,14 @@ __global__ __launch_bounds__(grad_threads<DK>()) void bwd_grad_kernel(ChunkBwdAr
 
 template <typename T, int DK>
 hipError_t launch_t(const ChunkBwdArgs &a0, hipStream_t s) {
-  // the matrix-core reverse pass reads the records the prep writes
+  // The matrix-core state passes read the records the prep writes, and no
+  // (I + A)^-1 or P in FP32; with the matrix-core gradient kernel as well,
+  // nothing reads the unit q, k rows. The prep skips what is not read.
   ChunkBwdArgs a = a0;
-  const bool ds_mma = chunk_bwd_state_mma_supported(a);
+  const bool ds_mma = chunk_bwd_state_mma_supported(a), grad_mma = chunk_bwd_grad_mma_supported(a);
   if (!ds_mma) a.brec = nullptr;
+  if (ds_mma) a.mm = a.pp = nullptr;
+  if (ds_mma && grad_mma) a.qn = a.kn = nullptr;
   const int64_t N = a.n_seqs;
   hipLaunchKernelGGL((bwd_prep_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk), dim3(kThreads), 0, s,
                      a);
