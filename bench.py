@@ -299,8 +299,10 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None, lay
     are priced against the HBM roof (algorithmic bytes per token: norm
     Hv dv (3 e + 2 e_g) (o, dout, d_o; gate, d_gate); prologue
     3 C e + 4 Hv e + 8 Hv (x, d_qkv, dx; a, b, d_a, d_b; d_g, d_beta)); the
-    chunk-rule backward (FP32 vector arithmetic) against the FP32 vector
-    peak with chunk_bwd_flops. `rule` = (q, k, v, g, beta, scale) views of
+    chunk-rule backward with chunk_bwd_flops against the peak of the
+    arithmetic it runs on (BF16 matrix cores with split operands for BF16
+    at dk 64/128, else the FP32 vector peak), and against the FP32 vector
+    peak for comparison. `rule` = (q, k, v, g, beta, scale) views of
     the forward's prologue output."""
     e = {"f32": 4, "bf16": 2, "f16": 2}[s.act]
     eg = {"f32": 4, "bf16": 2, "f16": 2}[s.gate_dtype]
@@ -349,8 +351,16 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None, lay
         ms = e0.elapsed_time(e1) / steps
         if per_tok is None:
             fl = chunk_bwd_flops(s)
-            out[name] = {"ms": ms, "flops": fl, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
-                         "alu_frac": fl / (ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, "arith": "f32"}
+            tf = fl / (ms * 1e-3) / 1e12
+            # BF16 workloads at dk 64/128 run the matrix-core kernels (FP32
+            # operands split into BF16 hi + lo parts, about three MFMA products
+            # per FP32 product); the rest run FP32 vector arithmetic
+            mma = s.act == "bf16" and s.dk in (64, 128)
+            out[name] = {"ms": ms, "flops": fl, "TFLOP/s": tf,
+                         "arith": "bf16 mfma, split operands" if mma else "f32 vector",
+                         "peak_TFLOP/s": MFMA_PEAK_TFLOPS["bf16"] if mma else FP32_VECTOR_PEAK_TFLOPS,
+                         "frac": tf / (MFMA_PEAK_TFLOPS["bf16"] if mma else FP32_VECTOR_PEAK_TFLOPS),
+                         "fp32_vector_frac": tf / FP32_VECTOR_PEAK_TFLOPS}
             continue
         nbytes = per_tok * ntok
         out[name] = {"ms": ms, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,

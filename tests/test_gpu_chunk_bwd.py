@@ -119,6 +119,31 @@ def test_chunk_rule_bwd_strided_views_equal_contiguous():
             assert torch.equal(x, y), n
 
 
+# BF16 workloads run matrix-core kernels where their operand rows allow: the
+# two state passes need 16-byte q, k, v and d_o rows, the gradient kernel
+# dv a multiple of 32 and 8-byte d_o rows. These cases pick each mix.
+MIXES = [
+    # name, dv, d_o row pitch (elements past dv)
+    ("states-mma-grad-fp32-dv16", 16, 0),
+    ("states-fp32-grad-mma-do8", 64, 4),
+    ("all-fp32-do2", 64, 1),
+]
+
+
+@pytest.mark.parametrize("name,dv,pad", MIXES, ids=[m[0] for m in MIXES])
+def test_chunk_rule_bwd_kernel_mixes(name, dv, pad):
+    s, q, k, v, g, beta, cu = _inputs(2, {"T": 130, "Hqk": 1, "Hv": 2, "dk": 64, "dv": dv, "B": 1})
+    (qd, kd, vd, gd, bd), cud = _dev(s, (q, k, v, g, beta), cu)
+    buf = synth.randn((s.B, s.T, s.Hv, dv + pad), s.act, 450).cuda()
+    do = buf[..., :dv]
+    h0 = synth.randn((1, s.Hv, dv, s.dk), "f32", 451).cuda() * 0.5
+    dht = synth.randn((1, s.Hv, dv, s.dk), "f32", 452).cuda() * 0.1
+    got = gdn.gdn_chunk_rule_bwd(qd, kd, vd, gd, bd, do, 0.125, True, 1e-6, None, h0, dht, want_d_initial_state=True)
+    torch.cuda.synchronize()
+    ref = OB.chunk_rule_bwd(q, k, v, g, beta, f64(do), 0.125, True, 1e-6, None, f64(h0), f64(dht))
+    _check(got, ref, TAU["bf16"])
+
+
 @pytest.mark.parametrize("where", ["tail", "mid"])
 def test_chunk_rule_bwd_full_size_window(where):
     """The 131072-token workload's shape (16 q/k heads, 32 value heads, dk = dv
