@@ -28,9 +28,12 @@
 //                      in turn: dq, dk (through the L2 fold), dg, dbeta
 // Products run in FP32 on the vector ALU from LDS tiles; the forward's MFMA
 // records (BF16 fragments of M diag(beta), not M) are not reused.
+#include <type_traits>
+
 #include "chunk_bwd_common.h"
 #include "device_common.h"
 #include "gdn_internal.h"
+#include "mfma_tiles.h"
 
 namespace gdn {
 namespace {
@@ -237,22 +240,41 @@ __device__ __forceinline__ void copy_rows(float *dst, int ld, const float *src) 
 
 // ---------------------------------------------------------------------------
 // Prep: unit q, k rows per (chunk, q/k head); gamma, M and scale * Pt per
-// value head of the group.
+// value head of the group. MMA (BF16 activations, dk 64/128, 16-byte rows,
+// the matrix-core passes downstream): the raw q, k rows go to LDS as
+// swizzled BF16 tiles and K K^T, Q K^T run on the matrix cores (exact
+// products of BF16 inputs, FP32 accumulation), scaled by the inverse norms
+// afterwards; nothing reads unit rows then, so none are written.
 // ---------------------------------------------------------------------------
-template <typename T, int DK>
+template <int DK, bool MMA>
+struct PrepX {  // FP32 unit rows
+  static constexpr int KP = DK + 4;
+  float q[BT * KP], k[BT * KP];
+};
+template <int DK>
+struct PrepX<DK, true> {  // raw BF16 rows (swizzled), then K K^T and Q K^T in FP32
+  union {
+    struct {
+      unsigned char q[BT * DK * 2], k[BT * DK * 2];
+    } t;
+    struct {
+      float gg[BT * MP], qk[BT * MP];
+    } r;
+  };
+};
+
+template <typename T, int DK, bool MMA = false>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
   constexpr int KP = DK + 4;
   // the q/k tiles are dead once K K^T and Q K^T are in registers; A and M
   // then reuse their LDS
   __shared__ alignas(16) union {
-    struct {
-      float q[BT * KP], k[BT * KP];
-    } x;
+    PrepX<DK, MMA> x;
     struct {
       float a[BT * MP], m[BT * MP], p[BT * MP];
     } y;
   } lds;
-  float *sQ = lds.x.q, *sK = lds.x.k, *sA = lds.y.a, *sM = lds.y.m, *sP = lds.y.p;
+  float *sA = lds.y.a, *sM = lds.y.m, *sP = lds.y.p;
   __shared__ float sgam[BT], sbeta[BT], srq[BT], srk[BT];
   const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
   const int64_t gc = blockIdx.x, hk = blockIdx.y;
@@ -262,7 +284,84 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
   const int64_t G = p.Hv / p.Hqk;
 
   // q, k rows of the chunk (zero past the last token), four lanes per row
-  {
+  float gg[4][4], qk[4][4];  // thread owns rows 4 rg .., columns 4 cg ..
+  if constexpr (MMA) {
+    constexpr int RB = DK * 2, SEG = DK / 4, NU = SEG / 8;  // 16-byte units per lane
+    const int t = tid >> 2, part = tid & 3;
+    const int64_t tt = cp.t0 + (t < nr ? t : nr - 1);
+    uint4 qv[NU], kv[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      qv[u] = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(p.q) + cp.brow * p.sq_b + tt * p.sq_t +
+                                               hk * p.sq_h + part * SEG + 8 * u);
+      kv[u] = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(p.k) + cp.brow * p.sk_b + tt * p.sk_t +
+                                               hk * p.sk_h + part * SEG + 8 * u);
+    }
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (t >= nr) qv[u] = kv[u] = uint4{0u, 0u, 0u, 0u};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, qv[u]), b = __builtin_bit_cast(bf16x8, kv[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq = fmaf(f(a[e]), f(a[e]), sq);
+        sk = fmaf(f(b[e]), f(b[e]), sk);
+      }
+      const int un = part * NU + u, off = t * RB + ((un ^ kswz<DK>(t)) << 4);
+      *reinterpret_cast<uint4 *>(lds.x.t.q + off) = qv[u];
+      *reinterpret_cast<uint4 *>(lds.x.t.k + off) = kv[u];
+    }
+    sq = group_sum<4>(sq);
+    sk = group_sum<4>(sk);
+    const float rq = p.use_l2 ? 1.f / sqrtf(sq + p.l2_eps) : 1.f;
+    const float rk = p.use_l2 ? 1.f / sqrtf(sk + p.l2_eps) : 1.f;
+    if (part == 0) {
+      p.rq[(gc * p.Hqk + hk) * BT + t] = rq;
+      p.rk[(gc * p.Hqk + hk) * BT + t] = rk;
+      srq[t] = rq;
+      srk[t] = rk;
+    }
+    __syncthreads();
+    // lower 16 x 16 tiles (w, n <= w) of K K^T and Q K^T, row tile w = wave
+    const int lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
+    auto rowk = [&](const unsigned char *x, int tile, int pp) -> bf16x8 {
+      const int r = 16 * tile + c;
+      return *reinterpret_cast<const bf16x8 *>(x + r * RB + (((4 * pp + g) ^ kswz<DK>(r)) << 4));
+    };
+    f32x4 ag[4], aq[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) ag[n] = aq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pp = 0; pp < DK / 32; ++pp) {
+      const bf16x8 kt = rowk(lds.x.t.k, w, pp), qt = rowk(lds.x.t.q, w, pp);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        if (n > w) continue;
+        const bf16x8 ks = rowk(lds.x.t.k, n, pp);
+        ag[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, ks, ag[n], 0, 0, 0);
+        aq[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt, ks, aq[n], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the tiles are read: their LDS takes the FP32 products
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * g + i, col = 16 * n + c;
+        lds.x.r.gg[r * MP + col] = n <= w ? ag[n][i] * srk[r] * srk[col] : 0.f;
+        lds.x.r.qk[r * MP + col] = n <= w ? aq[n][i] * srq[r] * srk[col] : 0.f;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        gg[r][cc] = lds.x.r.gg[(4 * rg + r) * MP + 4 * cg + cc];
+        qk[r][cc] = lds.x.r.qk[(4 * rg + r) * MP + 4 * cg + cc];
+      }
+    __syncthreads();  // A, M and P reuse this LDS
+  } else {
+    float *sQ = lds.x.q, *sK = lds.x.k;
     const int t = tid >> 2, part = tid & 3;
     constexpr int SEG = DK / 4;  // columns part * SEG .. + SEG - 1
     float qv[SEG], kv[SEG];
@@ -303,14 +402,14 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
       srq[t] = rq;
       srk[t] = rk;
     }
+    __syncthreads();
+    // G = K K^T and QK = Q K^T
+    zero(gg);
+    zero(qk);
+    mm_rr(gg, sK, KP, 4 * rg, sK, KP, 4 * cg, 0, DK);
+    mm_rr(qk, sQ, KP, 4 * rg, sK, KP, 4 * cg, 0, DK);
+    __syncthreads();  // A, M and P reuse this LDS
   }
-  __syncthreads();
-  // G = K K^T and QK = Q K^T; thread owns rows 4 rg .., columns 4 cg ..
-  float gg[4][4], qk[4][4];
-  zero(gg);
-  zero(qk);
-  mm_rr(gg, sK, KP, 4 * rg, sK, KP, 4 * cg, 0, DK);
-  mm_rr(qk, sQ, KP, 4 * rg, sK, KP, 4 * cg, 0, DK);
 
   for (int64_t vh = 0; vh < G; ++vh) {
     const int64_t h = hk * G + vh;
@@ -975,8 +1074,18 @@ hipError_t launch_t(const ChunkBwdArgs &a0, hipStream_t s) {
   if (ds_mma) a.mm = a.pp = nullptr;
   if (ds_mma && grad_mma) a.qn = a.kn = nullptr;
   const int64_t N = a.n_seqs;
-  hipLaunchKernelGGL((bwd_prep_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk), dim3(kThreads), 0, s,
-                     a);
+  // the matrix-core prep serves the all-matrix-core path (BF16, dk 64/128)
+  if constexpr (std::is_same<T, bf16>::value && DK <= 128) {
+    if (ds_mma && grad_mma)
+      hipLaunchKernelGGL((bwd_prep_kernel<T, DK, true>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk),
+                         dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_prep_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk), dim3(kThreads),
+                         0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_prep_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk), dim3(kThreads), 0,
+                       s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 sg((unsigned)(a.dv / 16), (unsigned)a.Hv, (unsigned)N);
