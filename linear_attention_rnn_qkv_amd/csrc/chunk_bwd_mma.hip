@@ -86,6 +86,7 @@ struct GradLds {
   float rowz[2][BT], roww[2][BT], pa[2][BT], pb[2][BT], pm[2][BT];
   float colz[4][BT];  // column sums of z over the rows of each row tile
   float db[BT];
+  alignas(16) float dgam[BT];
   float sdot[kThr / 64];
 };
 
@@ -112,7 +113,8 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
   // staging of a slab: thread tid holds row tid / 8, value columns
   // 4 (tid % 8) .. + 3 of d_o, Delta, dR', R, and S4 float4 of S0, dS.
   // Slab `it` of the flattened (value head, slab) order is fetched into
-  // registers while slab it - 1 is multiplied. Loads are never under a
+  // registers while slab it - 1 is multiplied (the first slab of a value
+  // head while the previous head's dq, dk products run). Loads are never under a
   // branch (rows past the chunk's end read its last row and are zeroed when
   // stored), so that they stay in flight.
   const int st_t = tid >> 3, st_c = 4 * (tid & 7);
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
         }
       }
       __syncthreads();
-      if ((int)vh * nslab + sl + 1 < (int)G * nslab) fetch((int)vh * nslab + sl + 1);
+      if (sl + 1 < nslab) fetch((int)vh * nslab + sl + 1);
       const f8 fo = rows(sm.u.s.o, tt);
       const f8 fdh = rows(sm.u.s.dh, tt), fdl = rows(sm.u.s.dl, tt);
       const f8 frh = rows(sm.u.s.rh, tt), frl = rows(sm.u.s.rl, tt);
@@ -298,30 +300,41 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
     // sums of z
     {
       float rz[4] = {0.f, 0.f, 0.f, 0.f}, rw[4] = {0.f, 0.f, 0.f, 0.f}, cz[2] = {0.f, 0.f};
+      // the lane's row and column factors, read once (the stores below would
+      // otherwise order every factor read behind them)
+      const f32x4 gtv = *reinterpret_cast<const f32x4 *>(&sm.gam[16 * tt + 4 * g]);
+      const f32x4 btv = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * tt + 4 * g]);
+      const float gsv[2] = {sm.gam[32 * jh + c], sm.gam[32 * jh + 16 + c]};
+      float z1v[2][4], z2v[2][4];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * tt + 4 * g + i, s = 16 * (2 * jh + a) + c;
-          const float e = s <= t ? __expf(sm.gam[t] - sm.gam[s]) : 0.f;
+          const float e = s <= t ? __expf(gtv[i] - gsv[a]) : 0.f;
           const float z1 = s <= t ? p.scale * c1[a][i] * e : 0.f;  // dPt o E
           const float da = s < t ? -c2[a][i] : 0.f;                // dA
           const float ge = e * gg[a][i];
-          const float bt = sm.beta[t];
-          const float zz = da * bt * ge + z1 * qk[a][i];           // dA * A + dPt * Pt
-          sm.u.e.z1[t * ZP + s] = z1;
-          sm.u.e.z2[t * ZP + s] = da * bt * e;                     // dG
+          const float zz = da * btv[i] * ge + z1 * qk[a][i];       // dA * A + dPt * Pt
+          z1v[a][i] = z1;
+          z2v[a][i] = da * btv[i] * e;                             // dG
           rz[i] += zz;
           cz[a] += zz;
           rw[i] = fmaf(da, ge, rw[i]);
         }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          rz[i] += __shfl_xor(rz[i], off, 64);
-          rw[i] += __shfl_xor(rw[i], off, 64);
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * tt + 4 * g + i, s = 16 * (2 * jh + a) + c;
+          sm.u.e.z1[t * ZP + s] = z1v[a][i];
+          sm.u.e.z2[t * ZP + s] = z2v[a][i];
         }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rz[i] = lane_sum<16>(rz[i]);
+        rw[i] = lane_sum<16>(rw[i]);
+      }
       if (c == 0)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -339,6 +352,7 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
     // dk half; dq, dk gain their direct terms
     {
       const int t = 16 * tt + c;
+      const float fq = p.scale * sm.eg[t], fk = sm.cw[t], fb = sm.eg[t] * sm.beta[t];
       float a = 0.f, b = 0.f, mm = 0.f;
 #pragma unroll
       for (int m = 0; m < NJW; ++m) {
@@ -363,7 +377,6 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
         sm.pb[jh][t] = b;
         sm.pm[jh][t] = mm;
       }
-      const float fq = p.scale * sm.eg[t], fk = sm.cw[t], fb = sm.eg[t] * sm.beta[t];
 #pragma unroll
       for (int m = 0; m < NJW; ++m)
 #pragma unroll
@@ -373,11 +386,9 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
         }
     }
     {
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) dbp += __shfl_xor(dbp, off, 64);
+      dbp = lane_sum<8>(dbp);
       if ((tid & 7) == 0) sm.db[st_t] = dbp;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) sdp += __shfl_xor(sdp, off, 64);
+      sdp = lane_sum<64>(sdp);
       if (lane == 0) sm.sdot[wave] = sdp;
     }
     __syncthreads();
@@ -410,8 +421,7 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
       const int t = tid;
       const float colz = sm.colz[0][t] + sm.colz[1][t] + sm.colz[2][t] + sm.colz[3][t];
       float svm = sm.cw[t] * sm.rk[t] * (sm.pm[0][t] + sm.pm[1][t]);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) svm += __shfl_xor(svm, off, 64);
+      svm = lane_sum<64>(svm);
       float tot = 0.f;
 #pragma unroll
       for (int i = 0; i < kThr / 64; ++i) tot += sm.sdot[i];
@@ -422,10 +432,16 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
       float dgam = rd + sm.rowz[0][t] + sm.rowz[1][t] - colz;
       if (t == nr - 1) dgam += __expf(sm.gam[t]) * tot + svm;
       if (t >= nr) dgam = 0.f;
+      // reverse running sum through LDS (broadcast reads; no cross-lane
+      // permutes, whose index registers spill)
+      sm.dgam[t] = dgam;
+      lds_fence_wave();
+      dgam = 0.f;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_down(dgam, off, 64);
-        if (t + off < 64) dgam += o;
+      for (int u = 0; u < BT; u += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.dgam[u]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dgam += u + e >= t ? x[e] : 0.f;
       }
       if (t < nr) {
         const int64_t o = (cp.brow * p.T + cp.t0 + t) * p.Hv + h;
@@ -434,6 +450,10 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
       }
     }
     __syncthreads();
+    // the next value head's first slab: its loads overlap the products below
+    // (issued only now, so that no load is in flight during the tail above,
+    // whose register reloads would wait for it)
+    if (vh + 1 < G) fetch((int)(vh + 1) * nslab);
     // dq^T += K^T W1^T, dk^T += K^T W2^T + Q^T W3^T (contraction over s)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {

@@ -174,6 +174,24 @@ __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 __device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Sum over aligned groups of W lanes (W a power of two <= 64).
+// Sum over aligned groups of W lanes (W = 2 .. 64), the result in every lane
+// of the group. Groups up to 16 lanes use DPP lane permutations on the
+// vector ALU (quad_perm xor 1, xor 2, then row_half_mirror, row_mirror), with
+// no LDS round trip; the steps across 16-lane rows use ds_bpermute.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int W> __device__ __forceinline__ float lane_sum(float v) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  v += dpp_f<0xB1>(v);                      // quad_perm [1, 0, 3, 2]
+  if constexpr (W >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if constexpr (W >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (W >= 16) v += dpp_f<0x140>(v); // row_mirror
+  if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 template <int W> __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
   for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
