@@ -185,15 +185,11 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
       const float *fa = reinterpret_cast<const float *>(rec + kDsF);
       f32x4 U[4];
       if (s >= 0) {
-        // the q term of the previous step, then dS_C of this chunk to the
-        // workspace (the gradient kernel reads it as [dv][dk])
+        // the q term of the previous step
         if (s > 0) {
 #pragma unroll
           for (int mt = 0; mt < NT; ++mt) dS[mt] += *reinterpret_cast<const f32x4 *>(&sm.hq[(mt * 64 + lane) * 4]);
         }
-        float *dsw = p.ds + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
-#pragma unroll
-        for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(dsw + dk_of(mt, 4 * g)) = dS[mt];
         // U = K dS^T (raw k rows)
         f8 Sh[KT], Sl[KT];
 #pragma unroll
@@ -209,6 +205,11 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           }
           U[mt] = u;
         }
+        // dS_C to the workspace (as [dv][dk]), issued after the products so
+        // that the stores do not wait behind the step's copies
+        float *dsw = p.ds + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(dsw + dk_of(mt, 4 * g)) = dS[mt];
       }
       lds_barrier();  // B1: G of this chunk is in LDS
       if (s < 0) return;
@@ -340,7 +341,6 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           *reinterpret_cast<f32x4 *>(&sm.gg[(mt * 64 + lane) * 4]) = a;
         }
       }
-      if (s >= 1) store_stage(s - 1, sm.stage[(sl + 1) % 2]);
       lds_barrier();  // B1
       if (s < 0) return;
       // q term Q^T (fq (.) dO), added to dS by the chain at the next step
@@ -371,6 +371,9 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
         }
         *reinterpret_cast<f32x4 *>(&sm.hq[(mt * 64 + lane) * 4]) = a;
       }
+      // the previous step's dR' and dv (its stage slot is rewritten only
+      // after the next middle barrier)
+      if (s >= 1) store_stage(s - 1, sm.stage[(sl + 1) % 2]);
     });
     lds_barrier();
     if (Nc > 0) store_stage(Nc - 1, sm.stage[(Nc - 1) % 2]);
@@ -548,11 +551,6 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
       const int64_t gc = gc0 + s;
       const unsigned char *kt = sm.k[sl], *rec = sm.rec[sl];
       const float *fa = reinterpret_cast<const float *>(rec + kBrF);
-      {  // S0 to the workspace ([dv][dk])
-        float *sw = p.s0 + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
-#pragma unroll
-        for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(sw + dk_of(mt, 4 * g)) = S[mt];
-      }
       // U = K S^T
       f32x4 U[4];
       {
@@ -570,6 +568,12 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
           }
           U[mt] = u;
         }
+      }
+      {  // S0 to the workspace ([dv][dk]), after the products (the stores do
+         // not wait behind the step's copies)
+        float *sw = p.s0 + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(sw + dk_of(mt, 4 * g)) = S[mt];
       }
       // R = V - e^gamma rk (.) U; X = beta (.) R
       f8 Bv[2];
