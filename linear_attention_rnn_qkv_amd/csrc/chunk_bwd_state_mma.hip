@@ -184,13 +184,20 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
       const unsigned char *kt = sm.k[sl], *rec = sm.rec[sl];
       const float *fa = reinterpret_cast<const float *>(rec + kDsF);
       f32x4 U[4];
+      f8 mth[6], mtl[6], kTr[NT][2];
       if (s >= 0) {
-        // the q term of the previous step
+        // U = K dS^T (raw k rows), with the q term of the previous step
+        // added first; every LDS fragment is read before the VALU work that
+        // precedes its products
+        f8 kfr[4][KT];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int pp = 0; pp < KT; ++pp) kfr[mt][pp] = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
         if (s > 0) {
 #pragma unroll
           for (int mt = 0; mt < NT; ++mt) dS[mt] += *reinterpret_cast<const f32x4 *>(&sm.hq[(mt * 64 + lane) * 4]);
         }
-        // U = K dS^T (raw k rows)
         f8 Sh[KT], Sl[KT];
 #pragma unroll
         for (int pp = 0; pp < KT; ++pp) split2x4(dS[2 * pp], dS[2 * pp + 1], Sh[pp], Sl[pp]);
@@ -199,12 +206,26 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           f32x4 u = zero4;
 #pragma unroll
           for (int pp = 0; pp < KT; ++pp) {
-            const f8 kf = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
-            u = mma(kf, Sh[pp], u);
-            u = mma(kf, Sl[pp], u);
+            u = mma(kfr[mt][pp], Sh[pp], u);
+            u = mma(kfr[mt][pp], Sl[pp], u);
           }
           U[mt] = u;
         }
+        // the M^T and K^T fragments of the second half
+#pragma unroll
+        for (int f = 0; f < 6; ++f) {
+          mth[f] = *reinterpret_cast<const f8 *>(rec + kDsMtH + f * 1024 + lane * 16);
+          mtl[f] = *reinterpret_cast<const f8 *>(rec + kDsMtL + f * 1024 + lane * 16);
+        }
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
+            const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
+            const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
+            kTr[mt][q] = cat8<bf16>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
+          }
         // dS_C to the workspace (as [dv][dk]), issued after the products so
         // that the stores do not wait behind the step's copies
         float *dsw = p.ds + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
@@ -233,11 +254,9 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           for (int q = 0; q < 2; ++q) {
             if (q == 0 && mt >= 2) continue;
             const int f = up_frag(mt, q);
-            const f8 mh = *reinterpret_cast<const f8 *>(rec + kDsMtH + f * 1024 + lane * 16);
-            const f8 ml = *reinterpret_cast<const f8 *>(rec + kDsMtL + f * 1024 + lane * 16);
-            r = mma(mh, Dh[q], r);
-            r = mma(mh, Dl[q], r);
-            r = mma(ml, Dh[q], r);
+            r = mma(mth[f], Dh[q], r);
+            r = mma(mth[f], Dl[q], r);
+            r = mma(mtl[f], Dh[q], r);
           }
           dR[mt] = r;
         }
@@ -263,12 +282,8 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
         f32x4 a = dS[mt] * eC;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
-          const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
-          const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
-          const f8 kT = cat8<bf16>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
-          a = mma(kT, Fkh[q], a);
-          a = mma(kT, Fkl[q], a);
+          a = mma(kTr[mt][q], Fkh[q], a);
+          a = mma(kTr[mt][q], Fkl[q], a);
         }
         dS[mt] = a;
       }
@@ -551,9 +566,16 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
       const int64_t gc = gc0 + s;
       const unsigned char *kt = sm.k[sl], *rec = sm.rec[sl];
       const float *fa = reinterpret_cast<const float *>(rec + kBrF);
-      // U = K S^T
+      // U = K S^T. Every LDS fragment of a product is read before the
+      // VALU work that precedes it, so that the reads overlap that work
+      // instead of feeding the products one at a time.
       f32x4 U[4];
       {
+        f8 kfr[4][KT];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int pp = 0; pp < KT; ++pp) kfr[mt][pp] = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
         f8 Sh[KT], Sl[KT];
 #pragma unroll
         for (int pp = 0; pp < KT; ++pp) split2x4(S[2 * pp], S[2 * pp + 1], Sh[pp], Sl[pp]);
@@ -562,13 +584,28 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
           f32x4 u = zero4;
 #pragma unroll
           for (int pp = 0; pp < KT; ++pp) {
-            const f8 kf = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
-            u = mma(kf, Sh[pp], u);
-            u = mma(kf, Sl[pp], u);
+            u = mma(kfr[mt][pp], Sh[pp], u);
+            u = mma(kfr[mt][pp], Sl[pp], u);
           }
           U[mt] = u;
         }
       }
+      // the M fragments and the K^T fragments of the update
+      f8 mfh[6], mfl[6], kTr[NT][2];
+#pragma unroll
+      for (int fi = 0; fi < 6; ++fi) {
+        mfh[fi] = *reinterpret_cast<const f8 *>(rec + kBrMH + fi * 1024 + lane * 16);
+        mfl[fi] = *reinterpret_cast<const f8 *>(rec + kBrML + fi * 1024 + lane * 16);
+      }
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
+          const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
+          const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
+          kTr[mt][q] = cat8<bf16>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
+        }
       {  // S0 to the workspace ([dv][dk]), after the products (the stores do
          // not wait behind the step's copies)
         float *sw = p.s0 + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
@@ -611,11 +648,9 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
           for (int q = 0; q < 2; ++q) {
             if (q == 1 && mt < 2) continue;
             const int fi = q == 0 ? mt : 2 + mt;
-            const f8 mh = *reinterpret_cast<const f8 *>(rec + kBrMH + fi * 1024 + lane * 16);
-            const f8 ml = *reinterpret_cast<const f8 *>(rec + kBrML + fi * 1024 + lane * 16);
-            d = mma(mh, Xh[q], d);
-            d = mma(mh, Xl[q], d);
-            d = mma(ml, Xh[q], d);
+            d = mma(mfh[fi], Xh[q], d);
+            d = mma(mfh[fi], Xl[q], d);
+            d = mma(mfl[fi], Xh[q], d);
           }
           Dl4[mt] = d;
           *reinterpret_cast<f32x4 *>(&stg[((4 + mt) * 64 + lane) * 4]) = d;
@@ -635,12 +670,8 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
         f32x4 a = S[mt] * eC;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
-          const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
-          const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
-          const f8 kT = cat8<bf16>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
-          a = mma(kT, Bwh[q], a);
-          a = mma(kT, Bwl[q], a);
+          a = mma(kTr[mt][q], Bwh[q], a);
+          a = mma(kTr[mt][q], Bwl[q], a);
         }
         S[mt] = a;
       }
