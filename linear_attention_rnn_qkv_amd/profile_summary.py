@@ -55,16 +55,28 @@ KERNELS = {
     "beta_g_bwd_kernel": ("beta_g_bwd_kernel", ["backward.hip", "device_common.h", "gdn_internal.h"]),
     "sum_partials_a": ("sum_partials_a", ["backward.hip", "device_common.h", "gdn_internal.h"]),
     "sum_partials_b": ("sum_partials_b", ["backward.hip", "device_common.h", "gdn_internal.h"]),
-    "bwd_prep_kernel": ("bwd_prep_kernel", ["chunk_bwd.hip", "device_common.h", "gdn_internal.h"]),
-    "bwd_states_kernel": ("bwd_states_kernel", ["chunk_bwd.hip", "device_common.h", "gdn_internal.h"]),
-    "bwd_dstate_kernel": ("bwd_dstate_kernel", ["chunk_bwd.hip", "device_common.h", "gdn_internal.h"]),
-    "bwd_grad_kernel": ("bwd_grad_kernel", ["chunk_bwd.hip", "device_common.h", "gdn_internal.h"]),
+    "bwd_prep_kernel": ("bwd_prep_kernel", ["chunk_bwd.hip", "chunk_bwd_common.h", "mfma_tiles.h",
+                                            "device_common.h", "gdn_internal.h"]),
+    "bwd_states_kernel": ("bwd_states_kernel", ["chunk_bwd.hip", "chunk_bwd_common.h", "mfma_tiles.h",
+                                                "device_common.h", "gdn_internal.h"]),
+    "bwd_dstate_kernel": ("bwd_dstate_kernel", ["chunk_bwd.hip", "chunk_bwd_common.h", "mfma_tiles.h",
+                                                "device_common.h", "gdn_internal.h"]),
+    "bwd_grad_kernel": ("bwd_grad_kernel", ["chunk_bwd.hip", "chunk_bwd_common.h", "mfma_tiles.h",
+                                            "device_common.h", "gdn_internal.h"]),
+    "bwd_states_mma_kernel": ("bwd_states_mma_kernel", ["chunk_bwd_state_mma.hip", "chunk_bwd_common.h",
+                                                        "mfma_tiles.h", "device_common.h", "gdn_internal.h"]),
+    "bwd_dstate_mma_kernel": ("bwd_dstate_mma_kernel", ["chunk_bwd_state_mma.hip", "chunk_bwd_common.h",
+                                                        "mfma_tiles.h", "device_common.h", "gdn_internal.h"]),
+    "bwd_grad_mma_kernel": ("bwd_grad_mma_kernel", ["chunk_bwd_mma.hip", "chunk_bwd_common.h", "mfma_tiles.h",
+                                                    "device_common.h", "gdn_internal.h"]),
 }
 
 
 def short_name(symbol: str) -> str | None:
     for frag, (name, _) in KERNELS.items():
-        if frag + "I" in symbol or symbol.endswith(frag) or "::" + frag + "(" in symbol:
+        # mangled (name + template arguments "I..."), plain, or demangled
+        # ("::name(" or "::name<") symbols
+        if frag + "I" in symbol or symbol.endswith(frag) or "::" + frag + "(" in symbol or "::" + frag + "<" in symbol:
             return name
     return None
 
