@@ -41,4 +41,5 @@ def test_bench_emits_one_json_line_with_roofline_and_cpu_baseline():
     for st in ("prologue", "chunk_rule", "gated_norm"):
         assert other[st]["hbm_frac"] > 0 and other[st]["ms"]["median"] > 0
     rb = out["backward"]["chunk_rule_bwd"]
-    assert rb["ms"] > 0 and 0 < rb["alu_frac"] <= 1
+    assert rb["ms"] > 0 and 0 < rb["frac"] <= 1 and 0 < rb["fp32_vector_frac"]
+    assert rb["arith"] in ("bf16 mfma, split operands", "f32 vector")
