@@ -264,7 +264,7 @@ struct PrepX<DK, true> {  // raw BF16 rows (swizzled), then K K^T and Q K^T in F
 };
 
 template <typename T, int DK, bool MMA = false>
-__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_prep_kernel(ChunkBwdArgs p) {
   constexpr int KP = DK + 4;
   // the q/k tiles are dead once K K^T and Q K^T are in registers; A and M
   // then reuse their LDS
@@ -311,8 +311,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
       *reinterpret_cast<uint4 *>(lds.x.t.q + off) = qv[u];
       *reinterpret_cast<uint4 *>(lds.x.t.k + off) = kv[u];
     }
-    sq = group_sum<4>(sq);
-    sk = group_sum<4>(sk);
+    sq = lane_sum<4>(sq);
+    sk = lane_sum<4>(sk);
     const float rq = p.use_l2 ? 1.f / sqrtf(sq + p.l2_eps) : 1.f;
     const float rk = p.use_l2 ? 1.f / sqrtf(sk + p.l2_eps) : 1.f;
     if (part == 0) {
@@ -380,8 +380,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
       sq = fmaf(qv[q], qv[q], sq);
       sk = fmaf(kv[q], kv[q], sk);
     }
-    sq = group_sum<4>(sq);
-    sk = group_sum<4>(sk);
+    sq = lane_sum<4>(sq);
+    sk = lane_sum<4>(sk);
     const float rq = p.use_l2 ? 1.f / sqrtf(sq + p.l2_eps) : 1.f;
     const float rk = p.use_l2 ? 1.f / sqrtf(sk + p.l2_eps) : 1.f;
     const int64_t un = ((gc * p.Hqk + hk) * BT + t) * DK + part * SEG;  // unit rows (when written)
@@ -450,25 +450,70 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(ChunkBwdArgs p) {
       }
     }
     __syncthreads();
-    // M = (I + A)^-1 by forward substitution, column c by four lanes; lane
-    // `part` keeps rows 4 u + part of its column in registers.
+    // M = (I + A)^-1 in 16 x 16 blocks. Diagonal blocks: wave j, lane c < 16
+    // solves column c of (I + A_jj) x = e_c by forward substitution; the
+    // strict upper blocks are zero.
     {
-      const int c = tid >> 2, part = tid & 3;
-      float mr[16];
+      const int lane = tid & 63, j = tid >> 6;
+      if (lane < 16) {
+        float x[16];
 #pragma unroll
-      for (int t = 0; t < BT; ++t) {
-        float sum = 0.f;
+        for (int r = 0; r < 16; ++r) x[r] = r == lane ? 1.f : 0.f;
 #pragma unroll
-        for (int u = 0; u < (t + 3) / 4; ++u) {
-          const int s = 4 * u + part;
-          if (s < t) sum = fmaf(sA[t * MP + s], mr[u], sum);
-        }
-        sum = group_sum<4>(sum);
-        const float mt = t == c ? 1.f : (t > c ? -sum : 0.f);
-        if ((t & 3) == part) mr[t >> 2] = mt;
+        for (int i = 0; i < 15; ++i)
+#pragma unroll
+          for (int r = i + 1; r < 16; ++r) x[r] = fmaf(-sA[(16 * j + r) * MP + 16 * j + i], x[i], x[r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sM[(16 * j + r) * MP + 16 * j + lane] = x[r];
       }
+      for (int e = tid; e < 6 * 256; e += kThreads) {  // blocks (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+        const int b = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+        const int bi = b < 3 ? 0 : (b < 5 ? 1 : 2), bj = b < 3 ? b + 1 : (b < 5 ? b - 1 : 3);
+        sM[(16 * bi + r) * MP + 16 * bj + cc] = 0.f;
+      }
+    }
+    __syncthreads();
+    //   Off-diagonal blocks: wave J owns block column J and forms, for
+    //   i = J + 1 .. 3, M_iJ = -M_ii sum_{k=J}^{i-1} A_ik M_kJ on the FP32
+    //   matrix cores (16x16x4, k index 4 g + kk in lane group g), so that an
+    //   accumulator (rows 4 g .. 4 g + 3 of column c) is directly the B
+    //   operand of the next product.
+    {
+      const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+      auto column = [&](auto jt) {
+        constexpr int J = decltype(jt)::value;
+        f32x4 mk[4];  // M_kJ, k > J
 #pragma unroll
-      for (int u = 0; u < 16; ++u) sM[(4 * u + part) * MP + c] = mr[u];
+        for (int i = J + 1; i < 4; ++i) {
+          f32x4 xv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = J; k < i; ++k) {
+            f32x4 bk;
+            if (k == J) {
+#pragma unroll
+              for (int kk = 0; kk < 4; ++kk) bk[kk] = sM[(16 * J + 4 * g + kk) * MP + 16 * J + c];
+            } else {
+              bk = mk[k];
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+              xv = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * i + c) * MP + 16 * k + 4 * g + kk], bk[kk], xv, 0, 0, 0);
+          }
+          f32x4 tv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            tv = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[(16 * i + c) * MP + 16 * i + 4 * g + kk], xv[kk], tv, 0, 0, 0);
+          mk[i] = -tv;
+        }
+#pragma unroll
+        for (int i = J + 1; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sM[(16 * i + 4 * g + r) * MP + 16 * J + c] = mk[i][r];
+      };
+      const int wv = tid >> 6;
+      if (wv == 0) column(std::integral_constant<int, 0>{});
+      else if (wv == 1) column(std::integral_constant<int, 1>{});
+      else if (wv == 2) column(std::integral_constant<int, 2>{});
     }
     __syncthreads();
     if (p.mm) {
