@@ -22,6 +22,8 @@
 // Parameter gradients are sums over tokens: each block writes its partial
 // sums to a caller workspace and a second kernel adds them in a fixed order,
 // so results do not depend on scheduling.
+#include <type_traits>
+
 #include "device_common.h"
 #include "gdn_internal.h"
 
@@ -232,13 +234,126 @@ struct SeqTrack {
   }
 };
 
+// The tile's partial sums of d_conv_w and d_conv_b for channels c .. c + VEC - 1.
+template <int VEC>
+__device__ __forceinline__ void write_conv_parts(const PrologueBwdArgs &p, int64_t tile, int64_t c,
+                                                 const float (&dw)[4][VEC], const float (&db)[VEC]) {
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    float *pw = p.part_w + (tile * p.C + c + v) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pw[j] = dw[j][v];
+    p.part_b[tile * p.C + c + v] = db[v];
+  }
+}
+
+// Tiles whose window (3 tokens before, 3 after) lies inside one sequence and
+// inside the call: four 16-bit channels per thread, token rows at x(u) =
+// xrow + u st, dz(u) = dzrow + u C, dx(u) = dxrow + u ldx. No boundary
+// conditions; x and dz are fetched 4 tokens at a time, a batch ahead of use,
+// with fixed-width non-temporal loads (unconditional: indices past the last
+// needed token repeat it). Three waves per SIMD fit (a deeper batch needs
+// more registers than that allows and was not faster).
+template <typename T, typename TD>
+__device__ __forceinline__ void conv_bwd_interior(const T *xrow, int64_t st, const TD *dzrow, int64_t C, T *dxrow,
+                                                  int64_t ldx, const float (&w)[4][4], const float (&bias)[4],
+                                                  int64_t t0, int64_t t1, float (&dw)[4][4], float (&db)[4]) {
+  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  using DR = typename std::conditional<sizeof(TD) == 2, u2, u4>::type;
+  constexpr int NB = 4;  // tokens per batch
+  const int64_t last = t1 + 2;  // last token whose x and dz are needed
+  auto ldxr = [&](int64_t u) -> u2 {
+    u = u < last ? u : last;
+    return __builtin_nontemporal_load(reinterpret_cast<const u2 *>(xrow + u * st));
+  };
+  auto ldzr = [&](int64_t u) -> DR {
+    u = u < last ? u : last;
+    return __builtin_nontemporal_load(reinterpret_cast<const DR *>(dzrow + u * C));
+  };
+  auto cvx = [](u2 r, float(&o)[4]) {
+    T t[4];
+    __builtin_memcpy(t, &r, 8);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o[v] = f(t[v]);
+  };
+  auto cvz = [](DR r, float(&o)[4]) {
+    TD t[4];
+    __builtin_memcpy(t, &r, sizeof(DR));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) o[v] = f(t[v]);
+  };
+  // e = dz silu'(b + sum_j w_j x_{u-3+j}) from x rows xa .. xa + 3
+  auto e_at = [&](const float(&x0)[4], const float(&x1)[4], const float(&x2)[4], const float(&x3)[4],
+                  const float(&dz)[4], float(&e)[4]) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float y = fmaf(w[0][v], x0[v], fmaf(w[1][v], x1[v], fmaf(w[2][v], x2[v], fmaf(w[3][v], x3[v], bias[v]))));
+      e[v] = dz[v] * dsilu(y);
+    }
+  };
+  float xw[7][4], ew[3][4];  // x_{t-3} .. x_{t+3}; e_t .. e_{t+2}
+#pragma unroll
+  for (int k = 0; k < 7; ++k) cvx(ldxr(t0 - 3 + k), xw[k]);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    float dz[4];
+    cvz(ldzr(t0 + k), dz);
+    e_at(xw[k], xw[k + 1], xw[k + 2], xw[k + 3], dz, ew[k]);
+  }
+  // batch for tokens tb .. tb + NB - 1: x_{t+4} and dz_{t+3}
+  auto fetch = [&](int64_t tb, u2(&xb)[NB], DR(&zb)[NB]) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      xb[k] = ldxr(tb + 4 + k);
+      zb[k] = ldzr(tb + 3 + k);
+    }
+  };
+  auto run = [&](int64_t tb, const u2(&xb)[NB], const DR(&zb)[NB]) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      float dz[4], e3[4], dx[4];
+      cvz(zb[k], dz);
+      e_at(xw[3], xw[4], xw[5], xw[6], dz, e3);  // e_{t+3}
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        dx[v] = fmaf(w[0][v], e3[v], fmaf(w[1][v], ew[2][v], fmaf(w[2][v], ew[1][v], w[3][v] * ew[0][v])));
+        db[v] += ew[0][v];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dw[j][v] = fmaf(ew[0][v], xw[j][v], dw[j][v]);
+      }
+      store_vec<T, 4>(dxrow + (tb + k) * ldx, dx);
+#pragma unroll
+      for (int q = 0; q < 6; ++q)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) xw[q][v] = xw[q + 1][v];
+      cvx(xb[k], xw[6]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        ew[0][v] = ew[1][v];
+        ew[1][v] = ew[2][v];
+        ew[2][v] = e3[v];
+      }
+    }
+  };
+  u2 xa[NB], xb[NB];
+  DR za[NB], zb[NB];
+  fetch(t0, xa, za);
+  for (int64_t tb = t0; tb < t1; tb += 2 * NB) {  // t1 - t0 is a multiple of 2 NB
+    fetch(tb + NB, xb, zb);
+    run(tb, xa, za);
+    fetch(tb + 2 * NB, xa, za);
+    run(tb + NB, xb, zb);
+  }
+}
+
 // One thread per VEC adjacent channels walks the tokens of one tile in order
 // with rolling windows: xw[k] = x_{t-3+k} (k < 8) and ew[k] = e_{t+k} (k < 4),
 // where e_u = dz_u silu'(y_u). The tile reads 3 tokens of x before it and 4
 // ahead; x and dz are fetched NB tokens at a time (vector accesses of VEC
 // elements).
 template <typename T, int VEC, bool FLAT>
-__global__ __launch_bounds__(kConvThreads) void conv_bwd_kernel(PrologueBwdArgs p) {
+__global__ __launch_bounds__(kConvThreads) __attribute__((amdgpu_waves_per_eu(3))) void conv_bwd_kernel(PrologueBwdArgs p) {
   constexpr int NB = 4;
   const int64_t c = ((int64_t)blockIdx.x * kConvThreads + threadIdx.x) * VEC;
   const int64_t tile = blockIdx.y;
@@ -292,6 +407,29 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_kernel(PrologueBwdArgs 
   SeqTrack tu{p.cu_seqlens, p.n_seqs, p.T, 0, 0, 0};  // sequence of the lookahead token
   tt.init(t0);
   tu.init(t0);
+  float dw[4][VEC], db[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    db[v] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dw[j][v] = 0.f;
+  }
+  if constexpr (VEC == 4 && sizeof(T) == 2) {
+    // the tile's window [t0 - 3, t1 + 2] inside one sequence (one batch row)
+    if (t1 - t0 == p.tile_tokens && p.tile_tokens % 16 == 0 && t0 >= 3 && t1 + 2 < ntok && tt.s0 <= t0 - 3 &&
+        t1 + 2 < tt.s1) {
+      const int64_t brow = FLAT ? 0 : t0 / p.T;
+      const T *xrow = xs + cc + (FLAT ? 0 : brow * sb - brow * p.T * st);
+      if (p.dqkv_dtype == kF32)
+        conv_bwd_interior<T, float>(xrow, st, static_cast<const float *>(p.dqkv) + c, p.C, dxs + cc, ldx, w, bias, t0,
+                                    t1, dw, db);
+      else
+        conv_bwd_interior<T, T>(xrow, st, static_cast<const T *>(p.dqkv) + c, p.C, dxs + cc, ldx, w, bias, t0, t1, dw,
+                                db);
+      write_conv_parts<VEC>(p, tile, c, dw, db);
+      return;
+    }
+  }
   // e_u from x_{u-3} .. x_u (xw rows k0 .. k0 + 3), inside u's sequence
   float xw[8][VEC], ew[4][VEC];
   auto e_of = [&](int64_t u, int k0, const float(&dz)[VEC], float(&e)[VEC]) {
@@ -318,13 +456,6 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_kernel(PrologueBwdArgs 
     float dz[VEC];
     dzat(t0 + k, dz);
     e_of(t0 + k, k, dz, ew[k]);
-  }
-  float dw[4][VEC], db[VEC];
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) {
-    db[v] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dw[j][v] = 0.f;
   }
   for (int64_t tb = t0; tb < t1; tb += NB) {
     // x_{t+5} and dz_{t+4} for the NB tokens t of this group, fetched together
@@ -371,13 +502,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_bwd_kernel(PrologueBwdArgs 
       for (int v = 0; v < VEC; ++v) ew[3][v] = e4[v];
     }
   }
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) {
-    float *pw = p.part_w + (tile * p.C + c + v) * 4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pw[j] = dw[j][v];
-    p.part_b[tile * p.C + c + v] = db[v];
-  }
+  write_conv_parts<VEC>(p, tile, c, dw, db);
 }
 
 // One block per tile of head_tile tokens (head_tile * Hv <= 4096): d_a and
