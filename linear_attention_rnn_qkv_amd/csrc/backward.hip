@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kNormThreads) void gated_norm_bwd_kernel(NormBwdArg
     for (int u = 0; u < 2; ++u) {
       const int64_t row = row0 + u * RPB + rg;
       if (row < nrows) {
-        const int64_t h = row % p.H, bt = row / p.H, t = bt % p.T, b = bt / p.T;
+        int64_t b, t, h;
+        split_row(p.rd, p.T, p.H, row, b, t, h);
         load_vec_nt<T, E>(static_cast<const T *>(p.o) + b * p.so_b + t * p.so_t + h * p.so_h + c0, p.o_align, O[u]);
         load_vec_nt<TG, E>(static_cast<const TG *>(p.gate) + b * p.sg_b + t * p.sg_t + h * p.sg_h + c0, p.gate_align,
                            G[u]);

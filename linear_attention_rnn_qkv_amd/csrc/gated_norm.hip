@@ -48,7 +48,8 @@ __global__ __launch_bounds__(kThreads) void gated_norm_kernel(NormArgs p) {
     const int64_t row = ((int64_t)blockIdx.x * kRowsPerLane + u) * RPB + wave * RPW + lane / LPR;
     rows[u] = row;
     if (row < nrows) {
-      const int64_t h = row % p.H, bt = row / p.H, t = bt % p.T, b = bt / p.T;
+      int64_t b, t, h;
+      split_row(p.rd, p.T, p.H, row, b, t, h);
       load_vec_nt<T, E>(static_cast<const T *>(p.o) + b * p.so_b + t * p.so_t + h * p.so_h + c0,
                      p.o_align, ov[u]);
       load_vec_nt<TG, E>(static_cast<const TG *>(p.gate) + b * p.sg_b + t * p.sg_t + h * p.sg_h + c0,

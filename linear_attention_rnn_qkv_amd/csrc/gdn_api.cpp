@@ -404,6 +404,7 @@ gdn_status plan_norm(const gdn_tensor *o, const gdn_tensor *gate, const gdn_tens
   p.o_align = row_align(o, 3);
   p.gate_align = row_align(gate, 3);
   p.eps = eps;
+  p.rd = gdn::row_div(B, T, H);
   return GDN_OK;
 }
 
@@ -561,6 +562,7 @@ gdn_status plan_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_
   p.act = f.act; p.gate_dtype = f.gate_dtype; p.w_dtype = f.w_dtype;
   p.o_align = f.o_align; p.gate_align = f.gate_align; p.dout_align = row_align(dout, 3);
   p.eps = eps;
+  p.rd = f.rd;
   return GDN_OK;
 }
 

@@ -67,6 +67,47 @@ constexpr int64_t kRecP = 6144;     // P (scaled, decayed, masked q.k), act dtyp
 constexpr int64_t kRecF = 12288;    // FP32 row factors [4][64]: aa, cw, zc, beta; then e^{gamma_C}
 constexpr int64_t kRecBytes = 14336;
 
+// Row r of a [B, T, H] grid of rows as (b, t, h). While B T H < 2^32 the two
+// divisions (by H, then by T) are multiplications by 32-bit magic numbers:
+// n / d = (umulhi(n, m) + n) >> s with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1, exact for every 32-bit n (the sum is
+// formed in 64 bits); else 64-bit division.
+struct RowDiv {
+  uint32_t h_m, h_s, t_m, t_s;
+  int32_t small;
+};
+inline void udiv_magic(uint32_t d, uint32_t &m, uint32_t &s) {
+  s = 0;
+  while (((uint64_t)1 << s) < d) ++s;
+  m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << s) - d)) / d + 1);
+}
+inline RowDiv row_div(int64_t B, int64_t T, int64_t H) {
+  RowDiv r{};
+  r.small = B * T * H < ((int64_t)1 << 32) ? 1 : 0;
+  if (r.small) {
+    udiv_magic((uint32_t)H, r.h_m, r.h_s);
+    udiv_magic((uint32_t)T, r.t_m, r.t_s);
+  }
+  return r;
+}
+__device__ __forceinline__ uint32_t udiv32(uint32_t n, uint32_t m, uint32_t s) {
+  return (uint32_t)((((uint64_t)n * m >> 32) + n) >> s);
+}
+__device__ __forceinline__ void split_row(const RowDiv &d, int64_t T, int64_t H, int64_t row, int64_t &b, int64_t &t,
+                                          int64_t &h) {
+  if (d.small) {
+    const uint32_t r = (uint32_t)row, bt = udiv32(r, d.h_m, d.h_s), bb = udiv32(bt, d.t_m, d.t_s);
+    h = r - bt * (uint32_t)H;
+    t = bt - bb * (uint32_t)T;
+    b = bb;
+  } else {
+    h = row % H;
+    const int64_t bt = row / H;
+    t = bt % T;
+    b = bt / T;
+  }
+}
+
 struct NormArgs {
   const void *o;
   int64_t so_b, so_t, so_h;
@@ -78,6 +119,7 @@ struct NormArgs {
   int32_t act, gate_dtype, w_dtype;
   int32_t o_align, gate_align;  // bytes guaranteed for every row start
   float eps;
+  RowDiv rd;
 };
 
 // One decode step (a new token per sequence, conv cache and state updated in
@@ -118,6 +160,7 @@ struct NormBwdArgs {
   int32_t act, gate_dtype, w_dtype;
   int32_t o_align, gate_align, dout_align;
   float eps;
+  RowDiv rd;
 };
 
 // Backward of the prologue (conv + SiLU, beta and g).
