@@ -300,8 +300,8 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None, lay
     Hv dv (3 e + 2 e_g) (o, dout, d_o; gate, d_gate); prologue
     3 C e + 4 Hv e + 8 Hv (x, d_qkv, dx; a, b, d_a, d_b; d_g, d_beta)); the
     chunk-rule backward with chunk_bwd_flops against the peak of the
-    arithmetic it runs on (BF16 matrix cores with split operands for BF16
-    at dk 64/128, else the FP32 vector peak), and against the FP32 vector
+    arithmetic it runs on (the 16-bit matrix cores with split operands for
+    BF16 and FP16 at dk 64/128, else the FP32 vector peak), and against the FP32 vector
     peak for comparison. `rule` = (q, k, v, g, beta, scale) views of
     the forward's prologue output."""
     e = {"f32": 4, "bf16": 2, "f16": 2}[s.act]
@@ -352,14 +352,15 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None, lay
         if per_tok is None:
             fl = chunk_bwd_flops(s)
             tf = fl / (ms * 1e-3) / 1e12
-            # BF16 workloads at dk 64/128 run the matrix-core kernels (FP32
-            # operands split into BF16 hi + lo parts, about three MFMA products
-            # per FP32 product); the rest run FP32 vector arithmetic
-            mma = s.act == "bf16" and s.dk in (64, 128)
+            # BF16 and FP16 workloads at dk 64/128 run the matrix-core kernels
+            # (FP32 operands split into 16-bit hi + lo parts, about three MFMA
+            # products per FP32 product); the rest run FP32 vector arithmetic
+            mma = s.act in ("bf16", "f16") and s.dk in (64, 128)
+            peak = MFMA_PEAK_TFLOPS[s.act] if mma else FP32_VECTOR_PEAK_TFLOPS
             out[name] = {"ms": ms, "flops": fl, "TFLOP/s": tf,
-                         "arith": "bf16 mfma, split operands" if mma else "f32 vector",
-                         "peak_TFLOP/s": MFMA_PEAK_TFLOPS["bf16"] if mma else FP32_VECTOR_PEAK_TFLOPS,
-                         "frac": tf / (MFMA_PEAK_TFLOPS["bf16"] if mma else FP32_VECTOR_PEAK_TFLOPS),
+                         "arith": f"{s.act} mfma, split operands" if mma else "f32 vector",
+                         "peak_TFLOP/s": peak,
+                         "frac": tf / peak,
                          "fp32_vector_frac": tf / FP32_VECTOR_PEAK_TFLOPS}
             continue
         nbytes = per_tok * ntok

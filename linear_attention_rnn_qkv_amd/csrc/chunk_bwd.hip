@@ -240,11 +240,11 @@ __device__ __forceinline__ void copy_rows(float *dst, int ld, const float *src) 
 
 // ---------------------------------------------------------------------------
 // Prep: unit q, k rows per (chunk, q/k head); gamma, M and scale * Pt per
-// value head of the group. MMA (BF16 activations, dk 64/128, 16-byte rows,
-// the matrix-core passes downstream): the raw q, k rows go to LDS as
-// swizzled BF16 tiles and K K^T, Q K^T run on the matrix cores (exact
-// products of BF16 inputs, FP32 accumulation), scaled by the inverse norms
-// afterwards; nothing reads unit rows then, so none are written.
+// value head of the group. MMA (BF16 or FP16 activations, dk 64/128, 16-byte
+// rows, the matrix-core passes downstream): the raw q, k rows go to LDS as
+// swizzled 16-bit tiles and K K^T, Q K^T run on the matrix cores (exact
+// products of the 16-bit inputs, FP32 accumulation), scaled by the inverse
+// norms afterwards; nothing reads unit rows then, so none are written.
 // ---------------------------------------------------------------------------
 template <int DK, bool MMA>
 struct PrepX {  // FP32 unit rows
@@ -286,22 +286,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // q, k rows of the chunk (zero past the last token), four lanes per row
   float gg[4][4], qk[4][4];  // thread owns rows 4 rg .., columns 4 cg ..
   if constexpr (MMA) {
+    using F8 = typename M2<T>::f8;
     constexpr int RB = DK * 2, SEG = DK / 4, NU = SEG / 8;  // 16-byte units per lane
     const int t = tid >> 2, part = tid & 3;
     const int64_t tt = cp.t0 + (t < nr ? t : nr - 1);
     uint4 qv[NU], kv[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      qv[u] = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(p.q) + cp.brow * p.sq_b + tt * p.sq_t +
+      qv[u] = *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.q) + cp.brow * p.sq_b + tt * p.sq_t +
                                                hk * p.sq_h + part * SEG + 8 * u);
-      kv[u] = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(p.k) + cp.brow * p.sk_b + tt * p.sk_t +
+      kv[u] = *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.k) + cp.brow * p.sk_b + tt * p.sk_t +
                                                hk * p.sk_h + part * SEG + 8 * u);
     }
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       if (t >= nr) qv[u] = kv[u] = uint4{0u, 0u, 0u, 0u};
-      const bf16x8 a = __builtin_bit_cast(bf16x8, qv[u]), b = __builtin_bit_cast(bf16x8, kv[u]);
+      const F8 a = __builtin_bit_cast(F8, qv[u]), b = __builtin_bit_cast(F8, kv[u]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         sq = fmaf(f(a[e]), f(a[e]), sq);
@@ -324,22 +325,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     __syncthreads();
     // lower 16 x 16 tiles (w, n <= w) of K K^T and Q K^T, row tile w = wave
     const int lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
-    auto rowk = [&](const unsigned char *x, int tile, int pp) -> bf16x8 {
+    auto rowk = [&](const unsigned char *x, int tile, int pp) -> F8 {
       const int r = 16 * tile + c;
-      return *reinterpret_cast<const bf16x8 *>(x + r * RB + (((4 * pp + g) ^ kswz<DK>(r)) << 4));
+      return *reinterpret_cast<const F8 *>(x + r * RB + (((4 * pp + g) ^ kswz<DK>(r)) << 4));
     };
     f32x4 ag[4], aq[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) ag[n] = aq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int pp = 0; pp < DK / 32; ++pp) {
-      const bf16x8 kt = rowk(lds.x.t.k, w, pp), qt = rowk(lds.x.t.q, w, pp);
+      const F8 kt = rowk(lds.x.t.k, w, pp), qt = rowk(lds.x.t.q, w, pp);
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         if (n > w) continue;
-        const bf16x8 ks = rowk(lds.x.t.k, n, pp);
-        ag[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, ks, ag[n], 0, 0, 0);
-        aq[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt, ks, aq[n], 0, 0, 0);
+        const F8 ks = rowk(lds.x.t.k, n, pp);
+        ag[n] = M2<T>::k32(kt, ks, ag[n]);
+        aq[n] = M2<T>::k32(qt, ks, aq[n]);
       }
     }
     __syncthreads();  // the tiles are read: their LDS takes the FP32 products
@@ -537,11 +538,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = sM[(16 * mt + c) * MP + 32 * q + 16 * (e >> 2) + 4 * g + (e & 3)];
         }
-        bf16 hi[8], lo[8];
+        // 16-bit parts in the activations' type (FP32 activations write no record)
+        using R16 = typename std::conditional<std::is_same<T, f16>::value, f16, bf16>::type;
+        R16 hi[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          hi[e] = to<bf16>(x[e]);
-          lo[e] = to<bf16>(x[e] - f(hi[e]));
+          hi[e] = to<R16>(x[e]);
+          lo[e] = to<R16>(x[e] - f(hi[e]));
         }
         const int64_t oh = (mat == 0 ? kBrMtH : mat == 1 ? kBrPH : kBrMH) + fi * 1024 + lane * 16;
         const int64_t ol = (mat == 0 ? kBrMtL : mat == 1 ? kBrPL : kBrML) + fi * 1024 + lane * 16;
@@ -1119,8 +1122,9 @@ hipError_t launch_t(const ChunkBwdArgs &a0, hipStream_t s) {
   if (ds_mma) a.mm = a.pp = nullptr;
   if (ds_mma && grad_mma) a.qn = a.kn = nullptr;
   const int64_t N = a.n_seqs;
-  // the matrix-core prep serves the all-matrix-core path (BF16, dk 64/128)
-  if constexpr (std::is_same<T, bf16>::value && DK <= 128) {
+  // the matrix-core prep serves the all-matrix-core path (BF16 or FP16, dk
+  // 64/128)
+  if constexpr ((std::is_same<T, bf16>::value || std::is_same<T, f16>::value) && DK <= 128) {
     if (ds_mma && grad_mma)
       hipLaunchKernelGGL((bwd_prep_kernel<T, DK, true>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk),
                          dim3(kThreads), 0, s, a);

@@ -1,21 +1,22 @@
-// Gradient kernel of the chunk-rule backward on the BF16 matrix cores
-// (v_mfma_f32_16x16x32_bf16, FP32 accumulation): dq, dk (through the L2
-// fold), dg and dbeta per (chunk, q/k head), the value heads of the GQA group
-// in turn, for BF16 activations with dk 64 or 128 and dv a multiple of 32.
-// It computes what the FP32 gradient kernel of chunk_bwd.hip computes, from
-// the same workspace arrays (gamma, inverse norms, R, Delta, M^T dDelta and
-// the states S0, dS_C); the forward and backward algebra is written out at
-// the top of chunk_bwd.hip (gated delta rule of Gated DeltaNet in the chunked
-// form of the flash-linear-attention and Megatron-LM pull requests;
-// first-order autograd as in Megatron Core "GDN Elementwise Fusion",
-// Execution and numerical behavior).
+// Gradient kernel of the chunk-rule backward on the 16-bit matrix cores
+// (v_mfma_f32_16x16x32_bf16 or _f16, FP32 accumulation): dq, dk (through the
+// L2 fold), dg and dbeta per (chunk, q/k head), the value heads of the GQA
+// group in turn, for BF16 or FP16 activations with dk 64 or 128 and dv a
+// multiple of 32. It computes what the FP32 gradient kernel of chunk_bwd.hip
+// computes, from the same workspace arrays (gamma, inverse norms, R, Delta,
+// M^T dDelta and the states S0, dS_C); the forward and backward algebra is
+// written out at the top of chunk_bwd.hip (gated delta rule of Gated
+// DeltaNet in the chunked form of the flash-linear-attention and Megatron-LM
+// pull requests; first-order autograd as in Megatron Core "GDN Elementwise
+// Fusion", Execution and numerical behavior).
 //
-// Precision. q, k and d_o are BF16 inputs and enter the products exactly.
-// Every FP32 operand x (workspace arrays, and the 64 x 64 matrices built from
-// them) is split into x = hi + lo, hi = bf16(x), lo = bf16(x - hi), and a
-// product of two such operands is taken as ah bh + ah bl + al bh: each term
-// then carries a relative error of about 2^-16 instead of the 2^-8 of a
-// single BF16 rounding.
+// Precision. q, k and d_o are 16-bit inputs and enter the products exactly
+// (on the instruction of their own type). Every FP32 operand x (workspace
+// arrays, and the 64 x 64 matrices built from them) is split into
+// x = hi + lo, hi = T(x), lo = T(x - hi), and a product of two such operands
+// is taken as ah bh + ah bl + al bh: each term then carries a relative error
+// of about 2^-16 (BF16) or 2^-22 (FP16, for values inside its range) instead
+// of a single 16-bit rounding.
 //
 // Products per value head (i runs over dv in slabs of 32, the MFMA depth):
 //   c1 = dO Delta^T, c2 = dR' Delta^T                     (64 x 64, [t][s])
@@ -40,14 +41,14 @@ namespace {
 constexpr int BT = 64;
 constexpr int kThr = 512;
 constexpr int SP = 40;  // row stride (16-bit elements) of the [64][32] slab tiles: 80-byte rows
-constexpr int WP = 72;  // row stride of the [64][64] BF16 operand matrices: 144-byte rows
+constexpr int WP = 72;  // row stride of the [64][64] 16-bit operand matrices: 144-byte rows
 constexpr int ZP = 65;  // row stride of the FP32 [64][64] matrices
 
-typedef bf16x8 f8;
-typedef bf16x4 v4;
-
-__device__ __forceinline__ f32x4 mma(f8 a, f8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// T is the activations' 16-bit type (bf16 or f16); the products run on the
+// matrix-core instruction of that type and split operands use its hi / lo.
+template <typename T>
+__device__ __forceinline__ f32x4 mma(typename M2<T>::f8 a, typename M2<T>::f8 b, f32x4 c) {
+  return M2<T>::k32(a, b, c);
 }
 
 // dk permutation of the dk x 64 tiles: row 4 g + i of tile mt is dk
@@ -57,12 +58,13 @@ __device__ __forceinline__ constexpr int dk_of(int mt, int r) {
   return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3);
 }
 
-__device__ __forceinline__ void split4(f32x4 x, v4 &hi, v4 &lo) {
-  hi = __builtin_convertvector(x, v4);
-  lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4), v4);
+template <typename V>
+__device__ __forceinline__ void split4(f32x4 x, V &hi, V &lo) {
+  hi = __builtin_convertvector(x, V);
+  lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4), V);
 }
 
-template <int DK>
+template <typename T, int DK>
 struct GradLds {
   static constexpr int RB = DK * 2;  // bytes per row of a dk-wide BF16 tile
   // raw q, k rows of the chunk (zero past the last token), 16-byte units
@@ -71,9 +73,9 @@ struct GradLds {
   alignas(16) unsigned char tk[BT * RB];
   union {
     struct {  // one slab of 32 value columns
-      alignas(16) bf16 o[BT * SP];                  // d_o [t][i]
-      alignas(16) bf16 dh[BT * SP], dl[BT * SP];    // Delta hi, lo
-      alignas(16) bf16 rh[BT * SP], rl[BT * SP];    // M^T dDelta hi, lo
+      alignas(16) T o[BT * SP];                  // d_o [t][i]
+      alignas(16) T dh[BT * SP], dl[BT * SP];    // Delta hi, lo
+      alignas(16) T rh[BT * SP], rl[BT * SP];    // M^T dDelta hi, lo
       alignas(16) unsigned char s0h[32 * RB], s0l[32 * RB];  // S0 [i][j], swizzled like q, k
       alignas(16) unsigned char dsh[32 * RB], dsl[32 * RB];  // dS_C [i][j]
     } s;
@@ -81,7 +83,7 @@ struct GradLds {
       float z1[BT * ZP], z2[BT * ZP];
     } e;
   } u;
-  alignas(16) bf16 w[6][BT * WP];  // hi, lo of Z1 diag(rk), (Z2 + Z2^T) diag(rk), (diag(rq) Z1)^T
+  alignas(16) T w[6][BT * WP];  // hi, lo of Z1 diag(rk), (Z2 + Z2^T) diag(rk), (diag(rq) Z1)^T
   float gam[BT], eg[BT], cw[BT], beta[BT], rq[BT], rk[BT];
   float rowz[2][BT], roww[2][BT], pa[2][BT], pb[2][BT], pm[2][BT];
   float colz[4][BT];  // column sums of z over the rows of each row tile
@@ -90,9 +92,11 @@ struct GradLds {
   float sdot[kThr / 64];
 };
 
-template <int DK>
+template <typename T, int DK>
 __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
-  using SM = GradLds<DK>;
+  using SM = GradLds<T, DK>;
+  using f8 = typename M2<T>::f8;
+  using v4 = typename M2<T>::v4;
   constexpr int RB = SM::RB;
   constexpr int NJW = DK / 32;  // dk tiles per wave
   constexpr int KS = DK / 32;   // MFMA steps over dk
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
   f32x4 sd4, sr4, sq4, s04[S4], sds4[S4];
   auto fetch = [&](int it) {
     const int64_t h = hk * G + it / nslab, i0 = 32 * (int64_t)(it % nslab);
-    so = *reinterpret_cast<const uint2 *>(static_cast<const bf16 *>(p.d_o) + cp.brow * p.sdo_b +
+    so = *reinterpret_cast<const uint2 *>(static_cast<const T *>(p.d_o) + cp.brow * p.sdo_b +
                                           (cp.t0 + st_tc) * p.sdo_t + h * p.sdo_h + i0 + st_c);
     const int64_t wo = ((gc * p.Hv + h) * BT + st_t) * dvn + i0 + st_c;
     sd4 = *reinterpret_cast<const f32x4 *>(p.del + wo);
@@ -146,9 +150,9 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
     for (int m = 0; m < NQK; ++m) {
       const int e = tid + kThr * m, r = e / UPR, un = e % UPR;
       const int64_t t = cp.t0 + (r < nr ? r : nr - 1);
-      qv[m] = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(p.q) + cp.brow * p.sq_b + t * p.sq_t +
+      qv[m] = *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.q) + cp.brow * p.sq_b + t * p.sq_t +
                                                hk * p.sq_h + 8 * un);
-      kv[m] = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(p.k) + cp.brow * p.sk_b + t * p.sk_t +
+      kv[m] = *reinterpret_cast<const uint4 *>(static_cast<const T *>(p.k) + cp.brow * p.sk_b + t * p.sk_t +
                                                hk * p.sk_h + 8 * un);
     }
     fetch(0);
@@ -182,10 +186,10 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
     const unsigned char *pb = x + rb * RB + ((un ^ kswz<DK>(rb)) << 4) + 8 * (mt & 1);
     const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(pa));
     const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(pb));
-    return cat8<bf16>(__builtin_bit_cast(v4, a), __builtin_bit_cast(v4, b));
+    return cat8<T>(__builtin_bit_cast(v4, a), __builtin_bit_cast(v4, b));
   };
   // row fragment of a [64][SP] slab tile: row 16 tile + c, columns 8 g .. + 7
-  auto rows = [&](const bf16 *x, int tile) -> f8 {
+  auto rows = [&](const T *x, int tile) -> f8 {
     return *reinterpret_cast<const f8 *>(x + (16 * tile + c) * SP + 8 * g);
   };
 
@@ -246,25 +250,25 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
       for (int a = 0; a < 2; ++a) {
         const int st = 2 * jh + a;
         const f8 sdh = rows(sm.u.s.dh, st), sdl = rows(sm.u.s.dl, st);
-        c1[a] = mma(fo, sdh, c1[a]);
-        c1[a] = mma(fo, sdl, c1[a]);
-        c2[a] = mma(frh, sdh, c2[a]);
-        c2[a] = mma(frh, sdl, c2[a]);
-        c2[a] = mma(frl, sdh, c2[a]);
+        c1[a] = mma<T>(fo, sdh, c1[a]);
+        c1[a] = mma<T>(fo, sdl, c1[a]);
+        c2[a] = mma<T>(frh, sdh, c2[a]);
+        c2[a] = mma<T>(frh, sdl, c2[a]);
+        c2[a] = mma<T>(frl, sdh, c2[a]);
       }
 #pragma unroll
       for (int m = 0; m < NJW; ++m) {
         const int mt = jh * NJW + m;
         const f8 ash = trk(sm.u.s.s0h, mt, 0), asl = trk(sm.u.s.s0l, mt, 0);
         const f8 adh = trk(sm.u.s.dsh, mt, 0), adl = trk(sm.u.s.dsl, mt, 0);
-        k1[m] = mma(ash, fo, k1[m]);
-        k1[m] = mma(asl, fo, k1[m]);
-        k2[m] = mma(adh, fdh, k2[m]);
-        k2[m] = mma(adh, fdl, k2[m]);
-        k2[m] = mma(adl, fdh, k2[m]);
-        k3[m] = mma(ash, frh, k3[m]);
-        k3[m] = mma(ash, frl, k3[m]);
-        k3[m] = mma(asl, frh, k3[m]);
+        k1[m] = mma<T>(ash, fo, k1[m]);
+        k1[m] = mma<T>(asl, fo, k1[m]);
+        k2[m] = mma<T>(adh, fdh, k2[m]);
+        k2[m] = mma<T>(adh, fdl, k2[m]);
+        k2[m] = mma<T>(adl, fdh, k2[m]);
+        k3[m] = mma<T>(ash, frh, k3[m]);
+        k3[m] = mma<T>(ash, frl, k3[m]);
+        k3[m] = mma<T>(asl, frh, k3[m]);
         // keep the scheduler from hoisting the next tile's fragment reads
         // (register pressure)
         __builtin_amdgcn_sched_barrier(0);
@@ -283,8 +287,8 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const f8 ks = rowk(sm.tk, 2 * jh + a, pp);
-        gg[a] = mma(kt, ks, gg[a]);
-        qk[a] = mma(qt, ks, qk[a]);
+        gg[a] = mma<T>(kt, ks, gg[a]);
+        qk[a] = mma<T>(qt, ks, qk[a]);
       }
     }
 #pragma unroll
@@ -409,8 +413,8 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
         v4 h0, l0, h1, l1;
         split4(f32x4{x[0], x[1], x[2], x[3]}, h0, l0);
         split4(f32x4{x[4], x[5], x[6], x[7]}, h1, l1);
-        *reinterpret_cast<f8 *>(&sm.w[2 * k][t * WP + s0]) = cat8<bf16>(h0, h1);
-        *reinterpret_cast<f8 *>(&sm.w[2 * k + 1][t * WP + s0]) = cat8<bf16>(l0, l1);
+        *reinterpret_cast<f8 *>(&sm.w[2 * k][t * WP + s0]) = cat8<T>(h0, h1);
+        *reinterpret_cast<f8 *>(&sm.w[2 * k + 1][t * WP + s0]) = cat8<T>(l0, l1);
       };
       put(0, w1);
       put(1, w2);
@@ -464,12 +468,12 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
       for (int m = 0; m < NJW; ++m) {
         const int mt = jh * NJW + m;
         const f8 kT = trk(sm.tk, mt, 32 * q), qT = trk(sm.tq, mt, 32 * q);
-        dq[m] = mma(kT, bw[0], dq[m]);
-        dq[m] = mma(kT, bw[1], dq[m]);
-        dk[m] = mma(kT, bw[2], dk[m]);
-        dk[m] = mma(kT, bw[3], dk[m]);
-        dk[m] = mma(qT, bw[4], dk[m]);
-        dk[m] = mma(qT, bw[5], dk[m]);
+        dq[m] = mma<T>(kT, bw[0], dq[m]);
+        dq[m] = mma<T>(kT, bw[1], dq[m]);
+        dk[m] = mma<T>(kT, bw[2], dk[m]);
+        dk[m] = mma<T>(kT, bw[3], dk[m]);
+        dk[m] = mma<T>(qT, bw[4], dk[m]);
+        dk[m] = mma<T>(qT, bw[5], dk[m]);
       }
     }
   }
@@ -525,26 +529,27 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
           *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dqq) + bq) = oq;
           *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dkk) + bk) = ok;
         } else {
-          *reinterpret_cast<v4 *>(static_cast<bf16 *>(p.dqq) + bq) = __builtin_convertvector(oq, v4);
-          *reinterpret_cast<v4 *>(static_cast<bf16 *>(p.dkk) + bk) = __builtin_convertvector(ok, v4);
+          *reinterpret_cast<v4 *>(static_cast<T *>(p.dqq) + bq) = __builtin_convertvector(oq, v4);
+          *reinterpret_cast<v4 *>(static_cast<T *>(p.dkk) + bk) = __builtin_convertvector(ok, v4);
         }
       }
     }
   }
 }
 
-template <int DK>
+template <typename T, int DK>
 hipError_t launch_grad(const ChunkBwdArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_grad_mma_kernel<DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk), dim3(kThr), 0, s, a);
+  hipLaunchKernelGGL((bwd_grad_mma_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk), dim3(kThr), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// BF16 activations, dk 64 or 128, dv a multiple of 32; q, k rows 16-byte
-// aligned, d_o rows 8-byte aligned, dq and dk rows aligned to 4 elements.
+// BF16 or FP16 activations, dk 64 or 128, dv a multiple of 32; q, k rows
+// 16-byte aligned, d_o rows 8-byte aligned, dq and dk rows aligned to 4
+// elements.
 bool chunk_bwd_grad_mma_supported(const ChunkBwdArgs &a) {
-  if (a.act != kBF16 || !(a.dk == 64 || a.dk == 128) || a.dv % 32 != 0) return false;
+  if ((a.act != kBF16 && a.act != kF16) || !(a.dk == 64 || a.dk == 128) || a.dv % 32 != 0) return false;
   const uint64_t qa = (uint64_t)(uintptr_t)a.q | (uint64_t)(a.sq_b * 2) | (uint64_t)(a.sq_t * 2) | (uint64_t)(a.sq_h * 2);
   const uint64_t ka = (uint64_t)(uintptr_t)a.k | (uint64_t)(a.sk_b * 2) | (uint64_t)(a.sk_t * 2) | (uint64_t)(a.sk_h * 2);
   const uint64_t oa =
@@ -557,7 +562,8 @@ bool chunk_bwd_grad_mma_supported(const ChunkBwdArgs &a) {
 }
 
 hipError_t launch_chunk_bwd_grad_mma(const ChunkBwdArgs &a, hipStream_t s) {
-  return a.dk == 64 ? launch_grad<64>(a, s) : launch_grad<128>(a, s);
+  if (a.act == kF16) return a.dk == 64 ? launch_grad<f16, 64>(a, s) : launch_grad<f16, 128>(a, s);
+  return a.dk == 64 ? launch_grad<bf16, 64>(a, s) : launch_grad<bf16, 128>(a, s);
 }
 
 }  // namespace gdn

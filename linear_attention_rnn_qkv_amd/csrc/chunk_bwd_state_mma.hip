@@ -1,5 +1,5 @@
-// Reverse state pass of the chunk-rule backward on the BF16 matrix cores, for
-// BF16 activations with dk 64 or 128: per (sequence, value head, 16 value
+// Reverse state pass of the chunk-rule backward on the 16-bit matrix cores,
+// for BF16 or FP16 activations with dk 64 or 128: per (sequence, value head, 16 value
 // rows), serial over the chunks from the last to the first, the gradient dS
 // of the state leaving each chunk is carried in FP32 MFMA accumulators and
 // each chunk gives (unit q, k rows q^, k^; the algebra is written out at the
@@ -9,14 +9,15 @@
 //   dR'    = M^T dDelta,   dv = beta (.) dR'
 //   dS0    = e^{gamma_C} dS + Q^T (fq (.) dO) + K^T (fk (.) dR')
 //
-// with fq = scale e^gamma rq and fk = -e^gamma beta rk on the raw BF16 q, k
+// with fq = scale e^gamma rq and fk = -e^gamma beta rk on the raw 16-bit q, k
 // rows. dS_C (for the gradient kernel) and dR' are written in FP32, dv in the
 // gradient dtype.
 //
-// Precision. K, Q and dO are exact BF16 operands; dS, dDelta, dR', the
-// scaled rows and the record's M^T, P'^T are split as x = hi + lo (BF16), and
-// products of two split operands take ah bh + ah bl + al bh, so that each
-// term carries a relative error near 2^-16.
+// Precision. K, Q and dO are exact 16-bit operands (on the instruction of
+// their own type); dS, dDelta, dR', the scaled rows and the record's M^T,
+// P'^T are split as x = hi + lo in that type, and products of two split
+// operands take ah bh + ah bl + al bh, so that each term carries a relative
+// error near 2^-16 (BF16) or 2^-22 (FP16, for values inside its range).
 //
 // One workgroup = (sequence, value head, 16 rows of dv), eight wavefronts,
 // two barriers per step (B0 at its start, B1 in its middle):
@@ -40,11 +41,11 @@ constexpr int kThr = 512;
 constexpr int BT = 64;
 constexpr int DVT = 16;
 
-typedef bf16x8 f8;
-typedef bf16x4 v4;
-
-__device__ __forceinline__ f32x4 mma(f8 a, f8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// T is the activations' 16-bit type (bf16 or f16): the products run on the
+// matrix-core instruction of that type and split operands use its hi / lo.
+template <typename T>
+__device__ __forceinline__ f32x4 mma(typename M2<T>::f8 a, typename M2<T>::f8 b, f32x4 c) {
+  return M2<T>::k32(a, b, c);
 }
 
 // dk permutation of the state tiles (as in the forward state kernel):
@@ -56,20 +57,18 @@ __device__ __forceinline__ constexpr int dk_of(int mt, int r) {
 // fragment of (row tile mt, k pair q) of an upper-triangular record matrix
 __device__ __forceinline__ constexpr int up_frag(int mt, int q) { return q == 0 ? mt : 2 + mt; }
 
-__device__ __forceinline__ void split8(const float (&x)[8], f8 &hi, f8 &lo) {
-  const f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+template <typename T>
+__device__ __forceinline__ void split2x4(f32x4 a, f32x4 b, typename M2<T>::f8 &hi, typename M2<T>::f8 &lo) {
+  using v4 = typename M2<T>::v4;
   const v4 ah = __builtin_convertvector(a, v4), bh = __builtin_convertvector(b, v4);
   const v4 al = __builtin_convertvector(a - __builtin_convertvector(ah, f32x4), v4);
   const v4 bl = __builtin_convertvector(b - __builtin_convertvector(bh, f32x4), v4);
-  hi = cat8<bf16>(ah, bh);
-  lo = cat8<bf16>(al, bl);
+  hi = cat8<T>(ah, bh);
+  lo = cat8<T>(al, bl);
 }
-__device__ __forceinline__ void split2x4(f32x4 a, f32x4 b, f8 &hi, f8 &lo) {
-  const v4 ah = __builtin_convertvector(a, v4), bh = __builtin_convertvector(b, v4);
-  const v4 al = __builtin_convertvector(a - __builtin_convertvector(ah, f32x4), v4);
-  const v4 bl = __builtin_convertvector(b - __builtin_convertvector(bh, f32x4), v4);
-  hi = cat8<bf16>(ah, bh);
-  lo = cat8<bf16>(al, bl);
+template <typename T>
+__device__ __forceinline__ void split8(const float (&x)[8], typename M2<T>::f8 &hi, typename M2<T>::f8 &lo) {
+  split2x4<T>(f32x4{x[0], x[1], x[2], x[3]}, f32x4{x[4], x[5], x[6], x[7]}, hi, lo);
 }
 
 // the reverse pass copies bytes [kBrF, kBrBytes) of each record: offsets
@@ -78,13 +77,13 @@ constexpr int64_t kDsRec = kBrBytes - kBrF;
 constexpr int64_t kDsF = 0, kDsMtH = kBrMtH - kBrF, kDsMtL = kBrMtL - kBrF, kDsPH = kBrPH - kBrF,
                   kDsPL = kBrPL - kBrF;
 
-template <int DK>
+template <typename T, int DK>
 struct DsLds {
   static constexpr int RB = DK * 2;
   static constexpr int TILE = BT * RB;
   alignas(16) unsigned char k[2][TILE];   // raw k rows of the step's chunk (swizzled)
   alignas(16) unsigned char q[2][TILE];   // raw q rows
-  alignas(16) bf16 o[2][BT * DVT];        // dO slice [64][16]
+  alignas(16) T o[2][BT * DVT];           // dO slice [64][16]
   alignas(16) unsigned char rec[2][kDsRec];
   alignas(16) float gg[4 * 64 * 4];        // G = P'^T dO, accumulator layout [mt][lane][4]
   alignas(16) float hq[DK / 16 * 64 * 4];  // q term of the state update, [mt][lane][4]
@@ -102,9 +101,11 @@ __device__ __forceinline__ void for_steps2(int last, F &&body) {
   }
 }
 
-template <int DK>
+template <typename T, int DK>
 __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
-  using SM = DsLds<DK>;
+  using SM = DsLds<T, DK>;
+  using f8 = typename M2<T>::f8;
+  using v4 = typename M2<T>::v4;
   constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB;
   constexpr int NI = SM::TILE / 1024;           // 1 KB copies per q/k tile
   constexpr int NR = (int)(kDsRec / 1024);      // 1 KB copies per record
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
       const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ob));
       const s16x4 r1 =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ob + 16 * DVT * 2));
-      Bo[q] = cat8<bf16>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
+      Bo[q] = cat8<T>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
     }
   };
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -200,14 +201,14 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
         }
         f8 Sh[KT], Sl[KT];
 #pragma unroll
-        for (int pp = 0; pp < KT; ++pp) split2x4(dS[2 * pp], dS[2 * pp + 1], Sh[pp], Sl[pp]);
+        for (int pp = 0; pp < KT; ++pp) split2x4<T>(dS[2 * pp], dS[2 * pp + 1], Sh[pp], Sl[pp]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           f32x4 u = zero4;
 #pragma unroll
           for (int pp = 0; pp < KT; ++pp) {
-            u = mma(kfr[mt][pp], Sh[pp], u);
-            u = mma(kfr[mt][pp], Sl[pp], u);
+            u = mma<T>(kfr[mt][pp], Sh[pp], u);
+            u = mma<T>(kfr[mt][pp], Sl[pp], u);
           }
           U[mt] = u;
         }
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
             const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
             const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
             const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
-            kTr[mt][q] = cat8<bf16>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
+            kTr[mt][q] = cat8<T>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
           }
         // dS_C to the workspace (as [dv][dk]), issued after the products so
         // that the stores do not wait behind the step's copies
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
       {
         f8 Dh[2], Dl[2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) split2x4(dD[2 * q], dD[2 * q + 1], Dh[q], Dl[q]);
+        for (int q = 0; q < 2; ++q) split2x4<T>(dD[2 * q], dD[2 * q + 1], Dh[q], Dl[q]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           f32x4 r = zero4;
@@ -254,9 +255,9 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           for (int q = 0; q < 2; ++q) {
             if (q == 0 && mt >= 2) continue;
             const int f = up_frag(mt, q);
-            r = mma(mth[f], Dh[q], r);
-            r = mma(mth[f], Dl[q], r);
-            r = mma(mtl[f], Dh[q], r);
+            r = mma<T>(mth[f], Dh[q], r);
+            r = mma<T>(mth[f], Dl[q], r);
+            r = mma<T>(mtl[f], Dh[q], r);
           }
           dR[mt] = r;
         }
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
       for (int q = 0; q < 2; ++q) {
         const f32x4 fk0 = *reinterpret_cast<const f32x4 *>(&fa[4 * BT + 32 * q + 4 * g]);
         const f32x4 fk1 = *reinterpret_cast<const f32x4 *>(&fa[4 * BT + 32 * q + 16 + 4 * g]);
-        split2x4(fk0 * dR[2 * q], fk1 * dR[2 * q + 1], Fkh[q], Fkl[q]);
+        split2x4<T>(fk0 * dR[2 * q], fk1 * dR[2 * q + 1], Fkh[q], Fkl[q]);
       }
       const float eC = fa[5 * BT];
 #pragma unroll
@@ -282,8 +283,8 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
         f32x4 a = dS[mt] * eC;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          a = mma(kTr[mt][q], Fkh[q], a);
-          a = mma(kTr[mt][q], Fkl[q], a);
+          a = mma<T>(kTr[mt][q], Fkh[q], a);
+          a = mma<T>(kTr[mt][q], Fkl[q], a);
         }
         dS[mt] = a;
       }
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           for (int v = 0; v < 4; ++v)
             *reinterpret_cast<f32x4 *>(dv + 4 * v) = f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
         } else {
-          bf16 *dv = static_cast<bf16 *>(p.dvv) + o;
+          T *dv = static_cast<T *>(p.dvv) + o;
 #pragma unroll
           for (int v = 0; v < 4; ++v)
             *reinterpret_cast<v4 *>(dv + 4 * v) =
@@ -350,8 +351,8 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
             const int f = up_frag(mt, q);
             const f8 ph = *reinterpret_cast<const f8 *>(rec + kDsPH + f * 1024 + lane * 16);
             const f8 pl = *reinterpret_cast<const f8 *>(rec + kDsPL + f * 1024 + lane * 16);
-            a = mma(ph, Bo[q], a);
-            a = mma(pl, Bo[q], a);
+            a = mma<T>(ph, Bo[q], a);
+            a = mma<T>(pl, Bo[q], a);
           }
           *reinterpret_cast<f32x4 *>(&sm.gg[(mt * 64 + lane) * 4]) = a;
         }
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           xq[e] = fq0[e] * f(Bo[q][e]);
           xq[4 + e] = fq1[e] * f(Bo[q][4 + e]);
         }
-        split8(xq, Fqh[q], Fql[q]);
+        split8<T>(xq, Fqh[q], Fql[q]);
       }
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
@@ -380,9 +381,9 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
           const unsigned char *qa1 = qt + trc[mt] + (32 * q) * RB, *qa2 = qt + trc[mt] + (32 * q + 16) * RB;
           const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(qa1));
           const s16x4 q2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(qa2));
-          const f8 qT = cat8<bf16>(__builtin_bit_cast(v4, q1), __builtin_bit_cast(v4, q2));
-          a = mma(qT, Fqh[q], a);
-          a = mma(qT, Fql[q], a);
+          const f8 qT = cat8<T>(__builtin_bit_cast(v4, q1), __builtin_bit_cast(v4, q2));
+          a = mma<T>(qT, Fqh[q], a);
+          a = mma<T>(qT, Fql[q], a);
         }
         *reinterpret_cast<f32x4 *>(&sm.hq[(mt * 64 + lane) * 4]) = a;
       }
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
       const bool isk = role < 2;
       const int i0 = (role & 1) * NH;
       const int64_t st = isk ? p.sk_t : p.sq_t;
-      const bf16 *xb = static_cast<const bf16 *>(isk ? p.k : p.q) + brow * (isk ? p.sk_b : p.sq_b) +
+      const T *xb = static_cast<const T *>(isk ? p.k : p.q) + brow * (isk ? p.sk_b : p.sq_b) +
                        hk * (isk ? p.sk_h : p.sq_h) + bos * st;
       uint32_t xoff[NH];
 #pragma unroll
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
     } else {
       constexpr int NRH = NR / 2;
       const int half = role - 4;
-      const bf16 *ob = static_cast<const bf16 *>(p.d_o) + brow * p.sdo_b + h * p.sdo_h + j0 + bos * p.sdo_t;
+      const T *ob = static_cast<const T *>(p.d_o) + brow * p.sdo_b + h * p.sdo_h + j0 + bos * p.sdo_t;
       for_steps2(Nc - 1, [&](int s, auto SL) {
         lds_barrier();
         constexpr int sl = (decltype(SL)::v + 1) % 2;
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
 // ---------------------------------------------------------------------------
 // Forward-state pass: per (sequence, value head, 16 value rows), serial over
 // the chunks in order, the state S (16 x dk) is carried in FP32 MFMA
-// accumulators and each chunk gives (raw BF16 k rows, factors from the
+// accumulators and each chunk gives (raw 16-bit k rows, factors from the
 // record)
 //
 //   U = K S^T,   R = V - (e^gamma rk) (.) U,   Delta = M (beta (.) R)
@@ -484,12 +485,12 @@ __global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
 // 2-7 copy the k tile, the v slice and the record's [0, kBrMtH) part of the
 // chunk two steps ahead into a three-slot ring (one barrier per step).
 // ---------------------------------------------------------------------------
-template <int DK>
+template <typename T, int DK>
 struct StLds {
   static constexpr int RB = DK * 2;
   static constexpr int TILE = BT * RB;
   alignas(16) unsigned char k[3][TILE];
-  alignas(16) bf16 v[3][BT * DVT];
+  alignas(16) T v[3][BT * DVT];
   alignas(16) unsigned char rec[3][kBrMtH];
   alignas(16) float stage[2][2 * 4 * 64 * 4];  // R, then Delta, [mt][lane][4]
 };
@@ -504,9 +505,11 @@ __device__ __forceinline__ void for_steps3(int last, F &&body) {
   }
 }
 
-template <int DK>
+template <typename T, int DK>
 __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
-  using SM = StLds<DK>;
+  using SM = StLds<T, DK>;
+  using f8 = typename M2<T>::f8;
+  using v4 = typename M2<T>::v4;
   constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB;
   constexpr int NI = SM::TILE / 1024;        // 1 KB copies per k tile
   constexpr int NR = (int)(kBrMtH / 1024);   // 1 KB copies per record part
@@ -578,14 +581,14 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
           for (int pp = 0; pp < KT; ++pp) kfr[mt][pp] = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
         f8 Sh[KT], Sl[KT];
 #pragma unroll
-        for (int pp = 0; pp < KT; ++pp) split2x4(S[2 * pp], S[2 * pp + 1], Sh[pp], Sl[pp]);
+        for (int pp = 0; pp < KT; ++pp) split2x4<T>(S[2 * pp], S[2 * pp + 1], Sh[pp], Sl[pp]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           f32x4 u = zero4;
 #pragma unroll
           for (int pp = 0; pp < KT; ++pp) {
-            u = mma(kfr[mt][pp], Sh[pp], u);
-            u = mma(kfr[mt][pp], Sl[pp], u);
+            u = mma<T>(kfr[mt][pp], Sh[pp], u);
+            u = mma<T>(kfr[mt][pp], Sl[pp], u);
           }
           U[mt] = u;
         }
@@ -604,7 +607,7 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
           const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
           const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
           const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
-          kTr[mt][q] = cat8<bf16>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
+          kTr[mt][q] = cat8<T>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
         }
       {  // S0 to the workspace ([dv][dk]), after the products (the stores do
          // not wait behind the step's copies)
@@ -620,7 +623,7 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
         const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb));
         const s16x4 r1 =
             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb + 16 * DVT * 2));
-        Bv[q] = cat8<bf16>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
+        Bv[q] = cat8<T>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
       }
       float *stg = sm.stage[s & 1];
       f32x4 X[4];
@@ -640,7 +643,7 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
       {
         f8 Xh[2], Xl[2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) split2x4(X[2 * q], X[2 * q + 1], Xh[q], Xl[q]);
+        for (int q = 0; q < 2; ++q) split2x4<T>(X[2 * q], X[2 * q + 1], Xh[q], Xl[q]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           f32x4 d = zero4;
@@ -648,9 +651,9 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
           for (int q = 0; q < 2; ++q) {
             if (q == 1 && mt < 2) continue;
             const int fi = q == 0 ? mt : 2 + mt;
-            d = mma(mfh[fi], Xh[q], d);
-            d = mma(mfh[fi], Xl[q], d);
-            d = mma(mfl[fi], Xh[q], d);
+            d = mma<T>(mfh[fi], Xh[q], d);
+            d = mma<T>(mfh[fi], Xl[q], d);
+            d = mma<T>(mfl[fi], Xh[q], d);
           }
           Dl4[mt] = d;
           *reinterpret_cast<f32x4 *>(&stg[((4 + mt) * 64 + lane) * 4]) = d;
@@ -662,7 +665,7 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
       for (int q = 0; q < 2; ++q) {
         const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 32 * q + 4 * g]);
         const f32x4 c1 = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 32 * q + 16 + 4 * g]);
-        split2x4(c0 * Dl4[2 * q], c1 * Dl4[2 * q + 1], Bwh[q], Bwl[q]);
+        split2x4<T>(c0 * Dl4[2 * q], c1 * Dl4[2 * q + 1], Bwh[q], Bwl[q]);
       }
       const float eC = fa[5 * BT];
 #pragma unroll
@@ -670,8 +673,8 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
         f32x4 a = S[mt] * eC;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          a = mma(kTr[mt][q], Bwh[q], a);
-          a = mma(kTr[mt][q], Bwl[q], a);
+          a = mma<T>(kTr[mt][q], Bwh[q], a);
+          a = mma<T>(kTr[mt][q], Bwl[q], a);
         }
         S[mt] = a;
       }
@@ -704,7 +707,7 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
     if (role < 4) {
       constexpr int NQ = NI / 4;
       const int i0 = role * NQ;
-      const bf16 *xb = static_cast<const bf16 *>(p.k) + brow * p.sk_b + hk * p.sk_h + bos * p.sk_t;
+      const T *xb = static_cast<const T *>(p.k) + brow * p.sk_b + hk * p.sk_h + bos * p.sk_t;
       uint32_t xoff[NQ];
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {
@@ -743,7 +746,7 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
     } else {
       constexpr int NRH = NR / 2;
       const int half = role - 4;
-      const bf16 *vb = static_cast<const bf16 *>(p.v) + brow * p.sv_b + h * p.sv_h + j0 + bos * p.sv_t;
+      const T *vb = static_cast<const T *>(p.v) + brow * p.sv_b + h * p.sv_h + j0 + bos * p.sv_t;
       for_steps3(Nc, [&](int s, auto SL) {
         lds_barrier();
         constexpr int sl = (decltype(SL)::v + 2) % 3;
@@ -766,26 +769,26 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
   }
 }
 
-template <int DK>
+template <typename T, int DK>
 hipError_t launch_st(const ChunkBwdArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(a.dv / DVT), (unsigned)a.Hv, (unsigned)a.n_seqs);
-  hipLaunchKernelGGL((bwd_states_mma_kernel<DK>), grid, dim3(kThr), 0, s, a);
+  hipLaunchKernelGGL((bwd_states_mma_kernel<T, DK>), grid, dim3(kThr), 0, s, a);
   return hipGetLastError();
 }
 
-template <int DK>
+template <typename T, int DK>
 hipError_t launch_ds(const ChunkBwdArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(a.dv / DVT), (unsigned)a.Hv, (unsigned)a.n_seqs);
-  hipLaunchKernelGGL((bwd_dstate_mma_kernel<DK>), grid, dim3(kThr), 0, s, a);
+  hipLaunchKernelGGL((bwd_dstate_mma_kernel<T, DK>), grid, dim3(kThr), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// BF16 activations, dk 64 or 128, dv a multiple of 16; q, k, v and d_o rows
-// 16-byte aligned (LDS DMA copies), dv rows aligned to 4 elements.
+// BF16 or FP16 activations, dk 64 or 128, dv a multiple of 16; q, k, v and
+// d_o rows 16-byte aligned (LDS DMA copies), dv rows aligned to 4 elements.
 bool chunk_bwd_state_mma_supported(const ChunkBwdArgs &a) {
-  if (a.act != kBF16 || !(a.dk == 64 || a.dk == 128) || a.dv % 16 != 0) return false;
+  if ((a.act != kBF16 && a.act != kF16) || !(a.dk == 64 || a.dk == 128) || a.dv % 16 != 0) return false;
   const uint64_t vva = (uint64_t)(uintptr_t)a.v | (uint64_t)(a.sv_b * 2) | (uint64_t)(a.sv_t * 2) | (uint64_t)(a.sv_h * 2);
   if (align_of_host(vva) < 16) return false;
   const uint64_t qa = (uint64_t)(uintptr_t)a.q | (uint64_t)(a.sq_b * 2) | (uint64_t)(a.sq_t * 2) | (uint64_t)(a.sq_h * 2);
@@ -799,11 +802,13 @@ bool chunk_bwd_state_mma_supported(const ChunkBwdArgs &a) {
 }
 
 hipError_t launch_chunk_bwd_dstate_mma(const ChunkBwdArgs &a, hipStream_t s) {
-  return a.dk == 64 ? launch_ds<64>(a, s) : launch_ds<128>(a, s);
+  if (a.act == kF16) return a.dk == 64 ? launch_ds<f16, 64>(a, s) : launch_ds<f16, 128>(a, s);
+  return a.dk == 64 ? launch_ds<bf16, 64>(a, s) : launch_ds<bf16, 128>(a, s);
 }
 
 hipError_t launch_chunk_bwd_states_mma(const ChunkBwdArgs &a, hipStream_t s) {
-  return a.dk == 64 ? launch_st<64>(a, s) : launch_st<128>(a, s);
+  if (a.act == kF16) return a.dk == 64 ? launch_st<f16, 64>(a, s) : launch_st<f16, 128>(a, s);
+  return a.dk == 64 ? launch_st<bf16, 64>(a, s) : launch_st<bf16, 128>(a, s);
 }
 
 }  // namespace gdn

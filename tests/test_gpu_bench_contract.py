@@ -42,4 +42,4 @@ def test_bench_emits_one_json_line_with_roofline_and_cpu_baseline():
         assert other[st]["hbm_frac"] > 0 and other[st]["ms"]["median"] > 0
     rb = out["backward"]["chunk_rule_bwd"]
     assert rb["ms"] > 0 and 0 < rb["frac"] <= 1 and 0 < rb["fp32_vector_frac"]
-    assert rb["arith"] in ("bf16 mfma, split operands", "f32 vector")
+    assert rb["arith"] in ("bf16 mfma, split operands", "f16 mfma, split operands", "f32 vector")

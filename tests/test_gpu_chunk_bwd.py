@@ -119,9 +119,10 @@ def test_chunk_rule_bwd_strided_views_equal_contiguous():
             assert torch.equal(x, y), n
 
 
-# BF16 workloads run matrix-core kernels where their operand rows allow: the
-# two state passes need 16-byte q, k, v and d_o rows, the gradient kernel
-# dv a multiple of 32 and 8-byte d_o rows. These cases pick each mix.
+# 16-bit workloads (BF16 and FP16) run matrix-core kernels where their
+# operand rows allow: the two state passes need 16-byte q, k, v and d_o rows,
+# the gradient kernel dv a multiple of 32 and 8-byte d_o rows. These cases
+# pick each mix, in both 16-bit types.
 MIXES = [
     # name, dv, d_o row pitch (elements past dv)
     ("states-mma-grad-fp32-dv16", 16, 0),
@@ -130,9 +131,10 @@ MIXES = [
 ]
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
 @pytest.mark.parametrize("name,dv,pad", MIXES, ids=[m[0] for m in MIXES])
-def test_chunk_rule_bwd_kernel_mixes(name, dv, pad):
-    s, q, k, v, g, beta, cu = _inputs(2, {"T": 130, "Hqk": 1, "Hv": 2, "dk": 64, "dv": dv, "B": 1})
+def test_chunk_rule_bwd_kernel_mixes(name, dv, pad, act):
+    s, q, k, v, g, beta, cu = _inputs(2, {"act": act, "T": 130, "Hqk": 1, "Hv": 2, "dk": 64, "dv": dv, "B": 1})
     (qd, kd, vd, gd, bd), cud = _dev(s, (q, k, v, g, beta), cu)
     buf = synth.randn((s.B, s.T, s.Hv, dv + pad), s.act, 450).cuda()
     do = buf[..., :dv]
@@ -141,13 +143,15 @@ def test_chunk_rule_bwd_kernel_mixes(name, dv, pad):
     got = gdn.gdn_chunk_rule_bwd(qd, kd, vd, gd, bd, do, 0.125, True, 1e-6, None, h0, dht, want_d_initial_state=True)
     torch.cuda.synchronize()
     ref = OB.chunk_rule_bwd(q, k, v, g, beta, f64(do), 0.125, True, 1e-6, None, f64(h0), f64(dht))
-    _check(got, ref, TAU["bf16"])
+    _check(got, ref, TAU[act])
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
 @pytest.mark.parametrize("where", ["tail", "mid"])
-def test_chunk_rule_bwd_full_size_window(where):
+def test_chunk_rule_bwd_full_size_window(where, act):
     """The 131072-token workload's shape (16 q/k heads, 32 value heads, dk = dv
-    = 128, BF16) in one call, with d_o zero except on a window of 150 tokens:
+    = 128; BF16, and the same shape in FP16) in one call, with d_o zero except
+    on a window of 150 tokens:
     the sequence's last 150 tokens, or 150 tokens from 70037 (not a multiple
     of the 64-token chunk). Every token of every head is checked:
       * tokens [start - 100, end): all five gradients against the oracle
@@ -165,10 +169,10 @@ def test_chunk_rule_bwd_full_size_window(where):
     beta ~ U(0.05, 1))."""
     s = synth.spec(3)
     B, T, Hqk, dk, Hv, dv = s.B, s.T, s.Hqk, s.dk, s.Hv, s.dv
-    print(f"[bwd full size] window {where}", flush=True)
-    q = synth.randn((B, T, Hqk, dk), "bf16", 500)
-    k = synth.randn((B, T, Hqk, dk), "bf16", 501)
-    v = synth.randn((B, T, Hv, dv), "bf16", 502)
+    print(f"[bwd full size] window {where} {act}", flush=True)
+    q = synth.randn((B, T, Hqk, dk), act, 500)
+    k = synth.randn((B, T, Hqk, dk), act, 501)
+    v = synth.randn((B, T, Hv, dv), act, 502)
     g = O.round_to(-synth.uniform((B, T, Hv), 0.01, 0.5, 503), "f32")
     beta = O.round_to(synth.uniform((B, T, Hv), 0.05, 1.0, 504), "f32")
     W, W1, LEAD = 150, 100, 256
@@ -176,8 +180,8 @@ def test_chunk_rule_bwd_full_size_window(where):
     end = start + W
     assert where == "tail" or start % 64 != 0
     t1, t0 = start - W1, start - W1 - LEAD
-    do = torch.zeros((B, T, Hv, dv), dtype=torch.bfloat16)
-    do[:, start:end] = synth.randn((B, W, Hv, dv), "bf16", 505)
+    do = torch.zeros((B, T, Hv, dv), dtype=synth.TORCH_DTYPE[act])
+    do[:, start:end] = synth.randn((B, W, Hv, dv), act, 505)
     scale = dk ** -0.5
     got = gdn.gdn_chunk_rule_bwd(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(g).float().cuda(),
                                  torch.from_numpy(beta).float().cuda(), do.cuda(), scale)
@@ -194,7 +198,7 @@ def test_chunk_rule_bwd_full_size_window(where):
     assert float(lead.max()) < 1e-12, lead.max()
     ref = OB.chunk_rule_bwd(f64(q[:, t0:end]), f64(k[:, t0:end]), f64(v[:, t0:end]), g[:, t0:end],
                             beta[:, t0:end], f64(do[:, t0:end]), scale)
-    tau = TAU["bf16"]
+    tau = TAU[act]
     w = slice(t1 - t0, end - t0)
     for n, x, r in zip(NAMES, (dq, dkk, dvv, dg, db), ref[:5]):
         H.assert_close(f64(x[:, t1:end]), r[:, w], tau, n)
@@ -211,3 +215,29 @@ def test_chunk_rule_bwd_full_size_window(where):
         before = x[:, :t1].float().abs()
         worst = float(before.max()) if before.numel() else 0.0
         assert worst <= bound * big, (n, worst, bound * big)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_chunk_rule_bwd_slow_decay(act):
+    """Slow decay (g ~ -U(1e-4, 2e-3), the state carried across 2048 tokens
+    with little loss) at dk = dv = 128, one q/k head and its two value heads,
+    a random initial state and a final-state gradient: the matrix-core
+    passes carry the states and their gradients as split 16-bit operands, and
+    this is where they grow largest; FP16 halves have the narrower range.
+    Every gradient against the oracle at the 16-bit bar."""
+    B, T, Hqk, dk, Hv, dv = 1, 2048, 1, 128, 2, 128
+    q = synth.randn((B, T, Hqk, dk), act, 520)
+    k = synth.randn((B, T, Hqk, dk), act, 521)
+    v = synth.randn((B, T, Hv, dv), act, 522)
+    g = O.round_to(-synth.uniform((B, T, Hv), 1e-4, 2e-3, 523), "f32")
+    beta = O.round_to(synth.uniform((B, T, Hv), 0.05, 1.0, 524), "f32")
+    do = synth.randn((B, T, Hv, dv), act, 525)
+    h0 = synth.randn((1, Hv, dv, dk), "f32", 526)
+    dht = synth.randn((1, Hv, dv, dk), "f32", 527)
+    scale = dk ** -0.5
+    got = gdn.gdn_chunk_rule_bwd(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(g).float().cuda(),
+                                 torch.from_numpy(beta).float().cuda(), do.cuda(), scale, True, 1e-6, None,
+                                 h0.cuda(), dht.cuda(), want_d_initial_state=True)
+    torch.cuda.synchronize()
+    ref = OB.chunk_rule_bwd(f64(q), f64(k), f64(v), g, beta, f64(do), scale, True, 1e-6, None, f64(h0), f64(dht))
+    _check(got, ref, TAU[act])
