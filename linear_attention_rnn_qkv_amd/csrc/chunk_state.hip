@@ -381,6 +381,294 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Four-slice variant, for launches with many (sequence, head) pairs (packed
+// or batched sequences): one workgroup = (sequence, value head, 64 rows of
+// dv). The step of chunk_state_kernel is bound by the bytes a CU moves, and
+// its k, q and record copies serve one 16-row slice; here one copy of them
+// serves four. Waves 0-3 each own a 16-row slice and run the whole step for
+// it (chain and output: X and Z = S0 Q^T from the same state fragments,
+// U, Vn, O, the state update), with no LDS hand-off; waves 4-7 copy the k
+// tile, the q tile, the record and the [64][64] v tile of chunk s + 1 into
+// two-slot rings during step s (complete before the barrier that starts step
+// s + 1). LDS: 108 KB at dk 128, one workgroup per CU.
+// ---------------------------------------------------------------------------
+constexpr int kQuadSlices = 4;
+
+template <typename T, int DK>
+struct QuadLds {
+  static constexpr int RB = DK * 2;
+  static constexpr int TILE = BT * RB;
+  static constexpr int VB = kQuadSlices * DVT * 2;  // bytes per v row
+  alignas(16) unsigned char k[2][TILE];
+  alignas(16) unsigned char q[2][TILE];
+  alignas(16) unsigned char v[2][BT * VB];
+  alignas(16) unsigned char rec[2][kRecBytes];
+};
+
+// Runs body(s, Slot<s mod 2>) for s = -1 .. last - 1 in order.
+template <typename F>
+__device__ __forceinline__ void for_steps2(int last, F &&body) {
+  for (int base = -2; base < last; base += 2) {
+    if (base >= -1) body(base, Slot<0>{});
+    if (base + 1 < last) body(base + 1, Slot<1>{});
+  }
+}
+
+template <typename T, int DK>
+__global__ __launch_bounds__(kStateThreads) void chunk_state_quad_kernel(ChunkArgs p) {
+  using MF = M2<T>;
+  using f8 = typename MF::f8;
+  using v4 = typename MF::v4;
+  using SM = QuadLds<T, DK>;
+  constexpr int KT = DK / 32;
+  constexpr int NT = DK / 16;
+  constexpr int RB = SM::RB;
+  constexpr int VB = SM::VB;
+  constexpr int NI = SM::TILE / 1024;          // 1 KB copies per q/k tile
+  constexpr int NR = (int)(kRecBytes / 1024);  // 1 KB copies per record
+  constexpr int NV = BT * VB / 1024;           // 1 KB copies per v tile
+  static_assert(NI <= 16 && NR <= 16 && NV <= 16, "copies per loader wave");
+  __shared__ SM sm;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
+  const int64_t jg = (lid % ntile) * (kQuadSlices * DVT);  // first value row of the workgroup
+  const int64_t h = (lid / ntile) % gridDim.y;
+  const int64_t n = lid / (ntile * gridDim.y);
+  const int64_t hk = h / (p.Hv / p.Hqk);
+  int64_t bos, eos, brow, cbase;
+  if (p.cu_seqlens) {
+    bos = p.cu_seqlens[n];
+    eos = p.cu_seqlens[n + 1];
+    brow = 0;
+    cbase = p.cu_chunks[n];
+  } else {
+    bos = 0;
+    eos = p.T;
+    brow = n;
+    cbase = n * ((p.T + BT - 1) / BT);
+  }
+  const int64_t L = eos - bos;
+  const int Nc = (int)((L + BT - 1) / BT);
+  auto rows_of = [&](int ch) -> int {
+    const int64_t r = L - (int64_t)ch * BT;
+    return (int)(r < BT ? r : BT);
+  };
+
+  if (wave < kQuadSlices) {
+    // ------------------------------------------- one 16-row slice, whole step
+    const int64_t j0 = jg + DVT * wave;
+    T *ob = static_cast<T *>(p.o) + brow * p.so_b + h * p.so_h + j0 + bos * p.so_t;
+    const int64_t st_base = ((n * p.Hv + h) * p.dv + j0) * DK;
+    int fo[KT];  // row c of a 16-row tile, dk 32 pp + 8 g .. + 7
+#pragma unroll
+    for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
+    const int yrow = 4 * g + (c >> 2);
+    int trc[NT];  // transposing reads of K^T fragments (as in chunk_state_kernel)
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+      trc[mt] = yrow * RB + (((4 * (mt >> 1) + (c & 3)) ^ kswz<DK>(yrow)) << 4) + 8 * (mt & 1);
+    // V fragments by transposing reads of this slice's 16 columns of the
+    // [64][64] v tile
+    const int vtr = (4 * g + (c >> 2)) * VB + 2 * DVT * wave + 8 * (c & 3);
+    f32x4 S[NT];  // S[mt][i] = S[dv row c][dk dk_of(mt, 4 g + i)]
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[mt][i] = p.init_state ? p.init_state[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] : 0.f;
+    f8 Sf[KT];
+#pragma unroll
+    for (int pp = 0; pp < KT; ++pp) Sf[pp] = cat8<T>(cvt4<T>(S[2 * pp]), cvt4<T>(S[2 * pp + 1]));
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    for_steps2(Nc, [&](int s, auto SL) {
+      lds_barrier();
+      if (s < 0) return;
+      constexpr int sl = decltype(SL)::v;
+      const unsigned char *kt = sm.k[sl], *qt = sm.q[sl], *rec = sm.rec[sl], *vt = sm.v[sl];
+      const float *fa = reinterpret_cast<const float *>(rec + kRecF);
+      // X = K S0^T
+      f32x4 X[4];
+      {
+        f8 kf[4][KT];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int pp = 0; pp < KT; ++pp) kf[mt][pp] = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) X[mt] = zero4;
+#pragma unroll
+        for (int pp = 0; pp < KT; ++pp)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) X[mt] = MF::k32(kf[mt][pp], Sf[pp], X[mt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Z^T = S0 Q^T (lane (g, c) holds Z[16 mt + c][dv 4 g + i]), scaled by zc
+      f32x4 Zc[4];
+      {
+        f8 qf[4][KT];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int pp = 0; pp < KT; ++pp) qf[mt][pp] = *reinterpret_cast<const f8 *>(qt + mt * 16 * RB + fo[pp]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Zc[mt] = zero4;
+#pragma unroll
+        for (int pp = 0; pp < KT; ++pp)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) Zc[mt] = MF::k32(Sf[pp], qf[mt][pp], Zc[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Zc[mt] = Zc[mt] * fa[2 * BT + 16 * mt + c];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // U = T' V, Vn = U - T' (aa (.) X)
+      f32x4 Vn[4];
+      {
+        f8 Tf[6];
+#pragma unroll
+        for (int f = 0; f < 6; ++f) Tf[f] = *reinterpret_cast<const f8 *>(rec + kRecT + f * 1024 + lane * 16);
+        f8 Bv[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const unsigned char *vb8 = vt + vtr + 32 * q * VB;
+          const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb8));
+          const s16x4 r1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb8 + 16 * VB));
+          Bv[q] = cat8<T>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
+        }
+        f8 Rf[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&fa[0 * BT + 32 * q + 4 * g]);
+          const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&fa[0 * BT + 32 * q + 16 + 4 * g]);
+          Rf[q] = cat8<T>(cvt4<T>(a0 * X[2 * q]), cvt4<T>(a1 * X[2 * q + 1]));
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 u = MF::k32(Tf[frag_id(mt, 0)], Bv[0], zero4);
+          f32x4 y = MF::k32(Tf[frag_id(mt, 0)], Rf[0], zero4);
+          if (mt >= 2) {
+            u = MF::k32(Tf[frag_id(mt, 1)], Bv[1], u);
+            y = MF::k32(Tf[frag_id(mt, 1)], Rf[1], y);
+          }
+          Vn[mt] = u - y;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // o = zc (.) (Q S0^T) + P Vn, transposed: O^T = Zc^T + Vn^T P^T
+      {
+        f8 Wf[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) Wf[q] = cat8<T>(cvt4<T>(Vn[2 * q]), cvt4<T>(Vn[2 * q + 1]));
+        const int nr = rows_of(s);
+        T *orow = ob + (int64_t)s * BT * p.so_t;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 o = MF::k32(Wf[0], *reinterpret_cast<const f8 *>(rec + kRecP + frag_id(mt, 0) * 1024 + lane * 16), Zc[mt]);
+          if (mt >= 2)
+            o = MF::k32(Wf[1], *reinterpret_cast<const f8 *>(rec + kRecP + frag_id(mt, 1) * 1024 + lane * 16), o);
+          const int r = 16 * mt + c;
+          if (r < nr) *reinterpret_cast<v4 *>(orow + (int64_t)r * p.so_t + 4 * g) = cvt4<T>(o);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // S = e^{gamma_C} S0 + K^T (cw (.) Vn)
+      {
+        f8 Bw[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 32 * q + 4 * g]);
+          const f32x4 c1 = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 32 * q + 16 + 4 * g]);
+          Bw[q] = cat8<T>(cvt4<T>(c0 * Vn[2 * q]), cvt4<T>(c1 * Vn[2 * q + 1]));
+        }
+        const float eC = fa[4 * BT];
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+          f32x4 a = S[mt] * eC;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const unsigned char *a1 = kt + trc[mt] + (32 * q) * RB;
+            const unsigned char *a2 = kt + trc[mt] + (32 * q + 16) * RB;
+            const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(a1));
+            const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(a2));
+            a = MF::k32(cat8<T>(__builtin_bit_cast(v4, r1), __builtin_bit_cast(v4, r2)), Bw[q], a);
+          }
+          S[mt] = a;
+        }
+#pragma unroll
+        for (int pp = 0; pp < KT; ++pp) Sf[pp] = cat8<T>(cvt4<T>(S[2 * pp]), cvt4<T>(S[2 * pp + 1]));
+      }
+    });
+    if (p.final_state) {
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p.final_state[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] = S[mt][i];
+    }
+  } else {
+    // ------------------------------------------------------------- loads
+    // wave 4: the k tile; 5: the q tile; 6: the record; 7: the v tile; for
+    // chunk s + 1, complete before the next barrier
+    const int role = wave - kQuadSlices;
+    const bool isx = role < 2;
+    const int64_t st = role == 0 ? p.sk_t : p.sq_t;
+    const T *xb = (role == 0 ? static_cast<const T *>(p.k) + brow * p.sk_b + hk * p.sk_h + bos * p.sk_t
+                             : static_cast<const T *>(p.q) + brow * p.sq_b + hk * p.sq_h + bos * p.sq_t);
+    const T *vb = static_cast<const T *>(p.v) + brow * p.sv_b + h * p.sv_h + jg + bos * p.sv_t;
+    const unsigned char *recb = p.ws_rec + (cbase * p.Hv + h) * kRecBytes;
+    const int64_t rec_stride = p.Hv * kRecBytes;
+    for_steps2(Nc, [&](int s, auto SL) {
+      lds_barrier();
+      constexpr int sl = (decltype(SL)::v + 1) % 2;  // slot of chunk s + 1
+      const int cl = s + 1;
+      if (cl < Nc) {
+        const int nr = rows_of(cl);
+        const int64_t t0 = (int64_t)cl * BT;
+        if (isx) {
+          unsigned char *xt = role == 0 ? sm.k[sl] : sm.q[sl];
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            const int b = 1024 * i + 16 * lane;
+            const int r = b / RB, jp = (b % RB) >> 4;
+            const int j = jp ^ kswz<DK>(r);
+            const int rr = r < nr ? r : nr - 1;  // rows past the chunk's end repeat its last row
+            g2l16(xb + (t0 + rr) * st + 8 * j, xt + 1024 * i);
+          }
+        } else if (role == 2) {
+          const unsigned char *rg = recb + (int64_t)cl * rec_stride;
+#pragma unroll
+          for (int i = 0; i < NR; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * i);
+        } else {
+          // copy i: rows 8 i + lane / 8, 16 bytes at column 8 (lane % 8)
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            const int rr = r < nr ? r : nr - 1;
+            g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane & 7), sm.v[sl] + 1024 * i);
+          }
+        }
+      }
+      wait_vm<0>();
+    });
+  }
+}
+
+template <typename T, int DK>
+hipError_t launch_quad(const ChunkArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)(a.dv / (kQuadSlices * DVT)), (unsigned)a.Hv, (unsigned)a.n_seqs);
+  hipLaunchKernelGGL((chunk_state_quad_kernel<T, DK>), grid, dim3(kStateThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// The four-slice kernel when its launch has at least this many workgroups
+// (half the CUs): below that, four times as many one-slice workgroups run
+// more chunks at once than it saves per chunk.
+constexpr int64_t kQuadMinWorkgroups = 128;
+
 template <typename T, int DK>
 hipError_t launch_dk(const ChunkArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(a.dv / DVT), (unsigned)a.Hv, (unsigned)a.n_seqs);
@@ -406,6 +694,10 @@ hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s) {
   hipError_t e = launch_chunk_prep(a, s);
   if (e != hipSuccess) return e;
   if (a.dk == 256) return launch_chunk_state_wide(a, s);
+  if (a.dv % (kQuadSlices * DVT) == 0 && a.n_seqs * a.Hv * (a.dv / (kQuadSlices * DVT)) >= kQuadMinWorkgroups) {
+    if (a.act == kBF16) return a.dk == 64 ? launch_quad<bf16, 64>(a, s) : launch_quad<bf16, 128>(a, s);
+    if (a.act == kF16) return a.dk == 64 ? launch_quad<f16, 64>(a, s) : launch_quad<f16, 128>(a, s);
+  }
   if (a.act == kBF16) return a.dk == 64 ? launch_dk<bf16, 64>(a, s) : launch_dk<bf16, 128>(a, s);
   if (a.act == kF16) return a.dk == 64 ? launch_dk<f16, 64>(a, s) : launch_dk<f16, 128>(a, s);
   return hipErrorInvalidValue;
