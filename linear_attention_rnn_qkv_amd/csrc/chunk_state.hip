@@ -382,24 +382,23 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_kernel(ChunkArgs p)
 }
 
 // ---------------------------------------------------------------------------
-// Four-slice variant, for launches with many (sequence, head) pairs (packed
-// or batched sequences): one workgroup = (sequence, value head, 64 rows of
-// dv). The step of chunk_state_kernel is bound by the bytes a CU moves, and
-// its k, q and record copies serve one 16-row slice; here one copy of them
-// serves four. Waves 0-3 each own a 16-row slice and run the whole step for
-// it (chain and output: X and Z = S0 Q^T from the same state fragments,
-// U, Vn, O, the state update), with no LDS hand-off; waves 4-7 copy the k
-// tile, the q tile, the record and the [64][64] v tile of chunk s + 1 into
-// two-slot rings during step s (complete before the barrier that starts step
-// s + 1). LDS: 108 KB at dk 128, one workgroup per CU.
+// Multi-slice variant, for launches with many (sequence, head) pairs (packed
+// or batched sequences): one workgroup = (sequence, value head, NS * 16 rows
+// of dv), NS = 4 or 8. The step of chunk_state_kernel is bound by the bytes a
+// CU moves, and its k, q and record copies serve one 16-row slice; here one
+// copy of them serves NS. Waves 0 .. NS - 1 each own a 16-row slice and run
+// the whole step for it (chain and output: X and Z = S0 Q^T from the same
+// state fragments, U, Vn, O, the state update), with no LDS hand-off; the
+// four waves after them copy the k tile, the q tile, the record and the
+// [64][16 NS] v tile of chunk s + 1 into two-slot rings during step s
+// (complete before the barrier that starts step s + 1). LDS at dk 128: 108 KB
+// (NS 4) or 124 KB (NS 8), one workgroup per CU.
 // ---------------------------------------------------------------------------
-constexpr int kQuadSlices = 4;
-
-template <typename T, int DK>
+template <typename T, int DK, int NS>
 struct QuadLds {
   static constexpr int RB = DK * 2;
   static constexpr int TILE = BT * RB;
-  static constexpr int VB = kQuadSlices * DVT * 2;  // bytes per v row
+  static constexpr int VB = NS * DVT * 2;  // bytes per v row
   alignas(16) unsigned char k[2][TILE];
   alignas(16) unsigned char q[2][TILE];
   alignas(16) unsigned char v[2][BT * VB];
@@ -415,12 +414,12 @@ __device__ __forceinline__ void for_steps2(int last, F &&body) {
   }
 }
 
-template <typename T, int DK>
-__global__ __launch_bounds__(kStateThreads) void chunk_state_quad_kernel(ChunkArgs p) {
+template <typename T, int DK, int NS>
+__global__ __launch_bounds__((NS + 4) * 64) void chunk_state_quad_kernel(ChunkArgs p) {
   using MF = M2<T>;
   using f8 = typename MF::f8;
   using v4 = typename MF::v4;
-  using SM = QuadLds<T, DK>;
+  using SM = QuadLds<T, DK, NS>;
   constexpr int KT = DK / 32;
   constexpr int NT = DK / 16;
   constexpr int RB = SM::RB;
@@ -428,6 +427,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_quad_kernel(ChunkAr
   constexpr int NI = SM::TILE / 1024;          // 1 KB copies per q/k tile
   constexpr int NR = (int)(kRecBytes / 1024);  // 1 KB copies per record
   constexpr int NV = BT * VB / 1024;           // 1 KB copies per v tile
+  constexpr int LV = VB / 16;                   // lanes per v row in a copy
   static_assert(NI <= 16 && NR <= 16 && NV <= 16, "copies per loader wave");
   __shared__ SM sm;
 
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_quad_kernel(ChunkAr
   const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
   int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
   if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
-  const int64_t jg = (lid % ntile) * (kQuadSlices * DVT);  // first value row of the workgroup
+  const int64_t jg = (lid % ntile) * (NS * DVT);  // first value row of the workgroup
   const int64_t h = (lid / ntile) % gridDim.y;
   const int64_t n = lid / (ntile * gridDim.y);
   const int64_t hk = h / (p.Hv / p.Hqk);
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_quad_kernel(ChunkAr
     return (int)(r < BT ? r : BT);
   };
 
-  if (wave < kQuadSlices) {
+  if (wave < NS) {
     // ------------------------------------------- one 16-row slice, whole step
     const int64_t j0 = jg + DVT * wave;
     T *ob = static_cast<T *>(p.o) + brow * p.so_b + h * p.so_h + j0 + bos * p.so_t;
@@ -611,9 +611,9 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_quad_kernel(ChunkAr
     }
   } else {
     // ------------------------------------------------------------- loads
-    // wave 4: the k tile; 5: the q tile; 6: the record; 7: the v tile; for
-    // chunk s + 1, complete before the next barrier
-    const int role = wave - kQuadSlices;
+    // wave NS: the k tile; NS + 1: the q tile; NS + 2: the record; NS + 3:
+    // the v tile; for chunk s + 1, complete before the next barrier
+    const int role = wave - NS;
     const bool isx = role < 2;
     const int64_t st = role == 0 ? p.sk_t : p.sq_t;
     const T *xb = (role == 0 ? static_cast<const T *>(p.k) + brow * p.sk_b + hk * p.sk_h + bos * p.sk_t
@@ -643,12 +643,12 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_quad_kernel(ChunkAr
 #pragma unroll
           for (int i = 0; i < NR; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * i);
         } else {
-          // copy i: rows 8 i + lane / 8, 16 bytes at column 8 (lane % 8)
+          // copy i: rows (64 / LV) i + lane / LV, 16 bytes at column 8 (lane % LV)
 #pragma unroll
           for (int i = 0; i < NV; ++i) {
-            const int r = 8 * i + (lane >> 3);
+            const int r = (64 / LV) * i + lane / LV;
             const int rr = r < nr ? r : nr - 1;
-            g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane & 7), sm.v[sl] + 1024 * i);
+            g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane % LV), sm.v[sl] + 1024 * i);
           }
         }
       }
@@ -657,17 +657,27 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_quad_kernel(ChunkAr
   }
 }
 
-template <typename T, int DK>
+template <typename T, int DK, int NS>
 hipError_t launch_quad(const ChunkArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)(a.dv / (kQuadSlices * DVT)), (unsigned)a.Hv, (unsigned)a.n_seqs);
-  hipLaunchKernelGGL((chunk_state_quad_kernel<T, DK>), grid, dim3(kStateThreads), 0, s, a);
+  dim3 grid((unsigned)(a.dv / (NS * DVT)), (unsigned)a.Hv, (unsigned)a.n_seqs);
+  hipLaunchKernelGGL((chunk_state_quad_kernel<T, DK, NS>), grid, dim3((NS + 4) * 64), 0, s, a);
   return hipGetLastError();
 }
 
-// The four-slice kernel when its launch has at least this many workgroups
-// (half the CUs): below that, four times as many one-slice workgroups run
+// A multi-slice kernel when its launch has at least this many workgroups
+// (half the CUs): below that, the NS times as many one-slice workgroups run
 // more chunks at once than it saves per chunk.
 constexpr int64_t kQuadMinWorkgroups = 128;
+
+template <typename T, int DK>
+hipError_t launch_multi(const ChunkArgs &a, hipStream_t s, bool &done) {
+  done = true;
+  const int64_t pairs = a.n_seqs * a.Hv;
+  if (a.dv % (8 * DVT) == 0 && pairs * (a.dv / (8 * DVT)) >= kQuadMinWorkgroups) return launch_quad<T, DK, 8>(a, s);
+  if (a.dv % (4 * DVT) == 0 && pairs * (a.dv / (4 * DVT)) >= kQuadMinWorkgroups) return launch_quad<T, DK, 4>(a, s);
+  done = false;
+  return hipSuccess;
+}
 
 template <typename T, int DK>
 hipError_t launch_dk(const ChunkArgs &a, hipStream_t s) {
@@ -694,9 +704,11 @@ hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s) {
   hipError_t e = launch_chunk_prep(a, s);
   if (e != hipSuccess) return e;
   if (a.dk == 256) return launch_chunk_state_wide(a, s);
-  if (a.dv % (kQuadSlices * DVT) == 0 && a.n_seqs * a.Hv * (a.dv / (kQuadSlices * DVT)) >= kQuadMinWorkgroups) {
-    if (a.act == kBF16) return a.dk == 64 ? launch_quad<bf16, 64>(a, s) : launch_quad<bf16, 128>(a, s);
-    if (a.act == kF16) return a.dk == 64 ? launch_quad<f16, 64>(a, s) : launch_quad<f16, 128>(a, s);
+  {
+    bool done = false;
+    if (a.act == kBF16) e = a.dk == 64 ? launch_multi<bf16, 64>(a, s, done) : launch_multi<bf16, 128>(a, s, done);
+    else if (a.act == kF16) e = a.dk == 64 ? launch_multi<f16, 64>(a, s, done) : launch_multi<f16, 128>(a, s, done);
+    if (done) return e;
   }
   if (a.act == kBF16) return a.dk == 64 ? launch_dk<bf16, 64>(a, s) : launch_dk<bf16, 128>(a, s);
   if (a.act == kF16) return a.dk == 64 ? launch_dk<f16, 64>(a, s) : launch_dk<f16, 128>(a, s);

@@ -151,6 +151,54 @@ def test_chunk_rule_state_in_out_slow_decay(act_cfg, path):
     H.assert_close(f64(f2), rfin, tau, "final state (hand-off)")
 
 
+# The split path's state kernel has three forms: one 16-row value slice per
+# workgroup, and 4 or 8 slices per workgroup sharing one copy of the k, q and
+# record tiles, taken when the launch has at least 128 such workgroups
+# (packed or batched sequences). These cases reach each multi-slice form
+# (8 sequences x 32 heads at dv 128: 8 slices; 3 x 32 at dv 128 and
+# 8 x 32 at dv 64: 4 slices; 8 batch rows: 8 slices over batch rows), with an
+# initial state and the final state out, against the oracle and, bit for bit,
+# against per-sequence calls, which run the one-slice kernel.
+MULTI = [
+    ("slices8-packed-fp16", 4, {"lengths": (1, 63, 64, 65, 130, 2, 3, 200)}),
+    ("slices4-packed-fp16-3seq", 4, {"lengths": (100, 130, 64)}),
+    ("slices4-packed-fp16-dv64", 4, {"lengths": (1, 63, 64, 65, 130, 2, 3, 200), "dv": 64}),
+    ("slices8-batched-bf16-B8", 2, {"B": 8, "T": 100}),
+]
+
+
+@pytest.mark.parametrize("name,cfg,over", MULTI, ids=[m[0] for m in MULTI])
+def test_chunk_rule_multi_slice_state_kernels(name, cfg, over):
+    s, x, qkv, g, beta = _stress_inputs(cfg, over, 0)
+    q, k, v = H.split_qkv(qkv, s)
+    cu = H.cu_of(x)
+    qd, kd, vd, gd, bd, cud = _gpu_stage_inputs(s, qkv, g, beta, cu)
+    N = s.B if cu is None else len(cu) - 1
+    S0 = synth.randn((N, s.Hv, s.dv, s.dk), "f32", 78).cuda() * 0.5
+    scale = s.dk ** -0.5
+    o, fin = gdn.gdn_chunk_rule_fwd(qd, kd, vd, gd, bd, scale, True, 1e-6, cud, S0, output_final_state=True)
+    torch.cuda.synchronize()
+    ro, rfin = O.gated_delta_rule(q, k, v, g, beta, scale=scale, cu_seqlens=cu, initial_state=f64(S0),
+                                  output_final_state=True)
+    tau = TAU[s.act]
+    H.assert_close(f64(o), O.round_to(ro, s.act), tau, "o")
+    H.assert_close(f64(fin), rfin, tau, "final state")
+    for i in range(N):
+        if cu is None:
+            sl, rows = (slice(i, i + 1), slice(None)), slice(i, i + 1)
+            oi, fi = gdn.gdn_chunk_rule_fwd(qd[sl], kd[sl], vd[sl], gd[sl], bd[sl], scale, True, 1e-6, None,
+                                            S0[i:i + 1], output_final_state=True)
+            torch.cuda.synchronize()
+            assert torch.equal(oi, o[rows]), i
+        else:
+            a, b = int(cu[i]), int(cu[i + 1])
+            oi, fi = gdn.gdn_chunk_rule_fwd(qd[:, a:b], kd[:, a:b], vd[:, a:b], gd[:, a:b], bd[:, a:b], scale, True,
+                                            1e-6, None, S0[i:i + 1], output_final_state=True)
+            torch.cuda.synchronize()
+            assert torch.equal(oi, o[:, a:b]), i
+        assert torch.equal(fi[0], fin[i]), i
+
+
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("cfg", [0, 3])
 def test_chunk_rule_no_decay(cfg, path):
