@@ -566,12 +566,15 @@ gdn_status plan_norm_bwd(const gdn_tensor *o, const gdn_tensor *gate, const gdn_
   return GDN_OK;
 }
 
-// Tokens per tile of the prologue backward: 256, halved down to 32 while the
+// Tokens per tile of the prologue backward: 128, halved down to 32 while the
 // conv launch (one 256-thread block per 1024 channels and tile) would have
-// fewer than 2048 blocks, eight per CU.
+// fewer than 2048 blocks, eight per CU. Measured at 131072 tokens of 16 + 16 +
+// 32 heads (C = 8192): 512-token tiles 2.04 ms, 256 1.77 ms, 128 1.62 ms, 64
+// 1.63 ms, 32 1.82 ms (more, shorter blocks keep more loads in flight until
+// the partial sums, one [C][5] row per tile, start to cost).
 int64_t prologue_bwd_tile(int64_t ntok, int64_t C) {
   const int64_t chb = (C / 4 + 255) / 256;
-  int64_t tile = 256;
+  int64_t tile = 128;
   while (tile > 32 && ((ntok + tile - 1) / tile) * chb < 2048) tile /= 2;
   return tile;
 }

@@ -238,17 +238,17 @@ def test_backward_workspace_bytes_and_rejections():
     assert gdn.lib().gdn_gated_norm_bwd_workspace_bytes(1, 1 << 20, 32, 128) == 8192 * 128 * 4 + 32 * 128 * 4
     assert gdn.lib().gdn_gated_norm_bwd_workspace_bytes(1, 10, 2, 96) == 0
     # prologue: [token tiles][C][4] and [token tiles][C], [head tiles of 4096 / Hv tokens][Hv] twice,
-    # then the reduction scratch [32][C * 4], all FP32. Tiles are 256 tokens, halved down to 32 while
+    # then the reduction scratch [32][C * 4], all FP32. Tiles are 128 tokens, halved down to 32 while
     # the conv launch (one block per 1024 channels and tile) would have fewer than 2048 blocks: here
     # C = 512 gives one block per tile, so 600 tokens use 32-token tiles (19 of them)
     gd = gdn.dims_of(2, 64, 4, 64)
     C = 2 * 128 + 256
     assert gdn.lib().gdn_prologue_bwd_workspace_bytes(1, 600, gd) == (a256(19 * C * 16) + a256(19 * C * 4) +
                                                                       2 * a256(1 * 4 * 4) + a256(32 * C * 16))
-    # 131072 tokens of the 16 -> 32 head geometry (C = 8192, 8 blocks per tile) keep 256-token tiles
+    # 131072 tokens of the 16 -> 32 head geometry (C = 8192, 8 blocks per tile) keep 128-token tiles
     gd3 = gdn.dims_of(16, 128, 32, 128)
     assert gdn.lib().gdn_prologue_bwd_workspace_bytes(1, 131072, gd3) == (
-        a256(512 * 8192 * 16) + a256(512 * 8192 * 4) + 2 * a256(1024 * 32 * 4) + a256(32 * 8192 * 16))
+        a256(1024 * 8192 * 16) + a256(1024 * 8192 * 4) + 2 * a256(1024 * 32 * 4) + a256(32 * 8192 * 16))
     o = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
     w = torch.ones(64, dtype=torch.bfloat16)
     _expect(INVALID, "dout: dtype", gdn.gdn_gated_norm_bwd, o, o.clone(), w, o.half())
@@ -353,7 +353,7 @@ def test_noalloc_rejects_inputs_beyond_the_static_scratch():
 
 
 def test_prologue_bwd_token_tile_per_size():
-    """The prologue backward's token tile (256 tokens, halved down to 32 while
+    """The prologue backward's token tile (128 tokens, halved down to 32 while
     its conv launch would have fewer than 2048 blocks) read back from the
     workspace it asks for: per tile, [C][4] and [C] FP32 partial sums."""
     def a256(x):
@@ -366,6 +366,6 @@ def test_prologue_bwd_token_tile_per_size():
         head_tile = 4096 // 32
         nh = (T + head_tile - 1) // head_tile
         return a256(nt * C * 16) + a256(nt * C * 4) + 2 * a256(nh * 32 * 4) + a256(32 * C * 16)
-    for T, tile in [(8192, 32), (16384, 64), (32768, 128), (65536, 256), (131072, 256), (100, 32)]:
+    for T, tile in [(8192, 32), (16384, 64), (32768, 128), (65536, 128), (131072, 128), (100, 32)]:
         got = gdn.lib().gdn_prologue_bwd_workspace_bytes(1, T, ctypes.byref(gdn.dims_of(*dims)))
         assert got == expect(T, tile), (T, tile, got)
