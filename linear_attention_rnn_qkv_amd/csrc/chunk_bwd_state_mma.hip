@@ -769,6 +769,266 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Multi-slice forward-state pass, for launches with many (sequence, head)
+// pairs: one workgroup = (sequence, value head, NS * 16 value rows). One
+// copy of the k tile and of the record's [0, kBrMtH) part serves NS chains;
+// waves 0 .. NS - 1 each carry one 16-row slice through the chain of
+// bwd_states_mma_kernel (the same products in the same order) and store its
+// S0, R and Delta themselves; the four waves after them copy the halves of
+// the k tile, the record part and the [64][16 NS] v tile of the next chunk
+// into two-slot rings (one barrier per step; a chain step is longer than the
+// copies' latency, so one step of look-ahead suffices, and the rings stay
+// small enough for LDS offsets without extra address registers). NS = 8 at
+// dk 64 and 4 at dk 128: eight dk-128 chains need more registers than twelve
+// waves leave.
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int NS>
+struct StMLds {
+  static constexpr int RB = DK * 2;
+  static constexpr int TILE = BT * RB;
+  static constexpr int VB = NS * DVT * 2;  // bytes per v row
+  alignas(16) unsigned char k[2][TILE];
+  alignas(16) unsigned char v[2][BT * VB];
+  alignas(16) unsigned char rec[2][kBrMtH];
+};
+
+template <typename T, int DK, int NS>
+__global__ __launch_bounds__((NS + 4) * 64) void bwd_states_multi_kernel(ChunkBwdArgs p) {
+  using SM = StMLds<T, DK, NS>;
+  using f8 = typename M2<T>::f8;
+  using v4 = typename M2<T>::v4;
+  constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB, VB = SM::VB;
+  constexpr int NI = SM::TILE / 1024;        // 1 KB copies per k tile
+  constexpr int NR = (int)(kBrMtH / 1024);   // 1 KB copies per record part
+  constexpr int NV = BT * VB / 1024;         // 1 KB copies per v tile
+  constexpr int LV = VB / 16;                // lanes per v row in a copy
+  static_assert(NI % 2 == 0 && NI / 2 <= 16 && NR <= 16 && NV <= 16, "copies per loader wave");
+  __shared__ SM sm;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
+  const int64_t jg = (lid % ntile) * (NS * DVT);
+  const int64_t h = (lid / ntile) % gridDim.y;
+  const int64_t n = lid / (ntile * gridDim.y);
+  const int64_t hk = h / (p.Hv / p.Hqk);
+  int64_t brow, bos, L, gc0;
+  if (p.cu_seqlens) {
+    brow = 0;
+    bos = p.cu_seqlens[n];
+    L = p.cu_seqlens[n + 1] - bos;
+    gc0 = p.cu_chunks[n];
+  } else {
+    brow = n;
+    bos = 0;
+    L = p.T;
+    gc0 = n * ((p.T + BT - 1) / BT);
+  }
+  const int Nc = (int)((L + BT - 1) / BT);
+  auto rows_of = [&](int ch) -> int {
+    const int64_t r = L - (int64_t)ch * BT;
+    return (int)(r < BT ? r : BT);
+  };
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  if (wave < NS) {
+    // ------------------------------------------------ the chain of one slice
+    const int64_t j0 = jg + DVT * wave;
+    const int64_t st_base = ((n * p.Hv + h) * p.dv + j0) * DK;
+    int fo[KT];
+#pragma unroll
+    for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
+    const int yrow = 4 * g + (c >> 2);
+    int trc[NT];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+      trc[mt] = yrow * RB + (((4 * (mt >> 1) + (c & 3)) ^ kswz<DK>(yrow)) << 4) + 8 * (mt & 1);
+    const int vtr = (4 * g + (c >> 2)) * VB + 2 * DVT * wave + 8 * (c & 3);
+    f32x4 S[NT];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[mt][i] = p.init_state ? p.init_state[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] : 0.f;
+    for_steps2(Nc - 1, [&](int s, auto SL) {
+      lds_barrier();
+      if (s < 0) return;
+      constexpr int sl = decltype(SL)::v;
+      const int64_t gc = gc0 + s;
+      const unsigned char *kt = sm.k[sl], *rec = sm.rec[sl];
+      const float *fa = reinterpret_cast<const float *>(rec + kBrF);
+      // U = K S^T
+      f32x4 U[4];
+      {
+        f8 kfr[4][KT];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int pp = 0; pp < KT; ++pp) kfr[mt][pp] = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
+        f8 Sh[KT], Sl[KT];
+#pragma unroll
+        for (int pp = 0; pp < KT; ++pp) split2x4<T>(S[2 * pp], S[2 * pp + 1], Sh[pp], Sl[pp]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 u = zero4;
+#pragma unroll
+          for (int pp = 0; pp < KT; ++pp) {
+            u = mma<T>(kfr[mt][pp], Sh[pp], u);
+            u = mma<T>(kfr[mt][pp], Sl[pp], u);
+          }
+          U[mt] = u;
+        }
+      }
+      f8 mfh[6], mfl[6], kTr[NT][2];
+#pragma unroll
+      for (int fi = 0; fi < 6; ++fi) {
+        mfh[fi] = *reinterpret_cast<const f8 *>(rec + kBrMH + fi * 1024 + lane * 16);
+        mfl[fi] = *reinterpret_cast<const f8 *>(rec + kBrML + fi * 1024 + lane * 16);
+      }
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
+          const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
+          const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
+          kTr[mt][q] = cat8<T>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
+        }
+      {  // S0 to the workspace ([dv][dk])
+        float *sw = p.s0 + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(sw + dk_of(mt, 4 * g)) = S[mt];
+      }
+      // R = V - e^gamma rk (.) U; X = beta (.) R
+      f8 Bv[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const unsigned char *vb = sm.v[sl] + vtr + 32 * q * VB;
+        const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb));
+        const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(vb + 16 * VB));
+        Bv[q] = cat8<T>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
+      }
+      // R and Delta rows of this slice: lane (g, c) holds rows 16 mt + 4 g + i
+      // of column c; each store writes 64 contiguous bytes per row. The row
+      // offsets (16 mt + i) dv are uniform, the lane's 4 g dv part is in its
+      // base pointer (no per-row addresses held across steps).
+      const int64_t dvs = p.dv;
+      float *rrow = p.rr + ((gc * p.Hv + h) * BT + 4 * g) * dvs + j0 + c;
+      float *drow = p.del + ((gc * p.Hv + h) * BT + 4 * g) * dvs + j0 + c;
+      f32x4 X[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 er = *reinterpret_cast<const f32x4 *>(&fa[6 * BT + 16 * mt + 4 * g]);
+        const f32x4 bt = *reinterpret_cast<const f32x4 *>(&fa[2 * BT + 16 * mt + 4 * g]);
+        f32x4 vv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[i] = f(Bv[mt >> 1][4 * (mt & 1) + i]);
+        const f32x4 r = vv - er * U[mt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rrow[(16 * mt + i) * dvs] = r[i];
+        X[mt] = bt * r;
+      }
+      // Delta = M X
+      f32x4 Dl4[4];
+      {
+        f8 Xh[2], Xl[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) split2x4<T>(X[2 * q], X[2 * q + 1], Xh[q], Xl[q]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 d = zero4;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            if (q == 1 && mt < 2) continue;
+            const int fi = q == 0 ? mt : 2 + mt;
+            d = mma<T>(mfh[fi], Xh[q], d);
+            d = mma<T>(mfh[fi], Xl[q], d);
+            d = mma<T>(mfl[fi], Xh[q], d);
+          }
+          Dl4[mt] = d;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) drow[(16 * mt + i) * dvs] = d[i];
+        }
+      }
+      // S = e^{gamma_C} S + K^T (cw rk (.) Delta)
+      f8 Bwh[2], Bwl[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 32 * q + 4 * g]);
+        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 32 * q + 16 + 4 * g]);
+        split2x4<T>(c0 * Dl4[2 * q], c1 * Dl4[2 * q + 1], Bwh[q], Bwl[q]);
+      }
+      const float eC = fa[5 * BT];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        f32x4 a = S[mt] * eC;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          a = mma<T>(kTr[mt][q], Bwh[q], a);
+          a = mma<T>(kTr[mt][q], Bwl[q], a);
+        }
+        S[mt] = a;
+      }
+    });
+  } else {
+    // ------------------------------------------------------------- loads
+    // waves NS, NS + 1: halves of the k tile; NS + 2: the record part;
+    // NS + 3: the v tile; for the chunk of step s + 1, complete before the
+    // next barrier
+    const int role = wave - NS;
+    const T *xb = static_cast<const T *>(p.k) + brow * p.sk_b + hk * p.sk_h + bos * p.sk_t;
+    const T *vb = static_cast<const T *>(p.v) + brow * p.sv_b + h * p.sv_h + jg + bos * p.sv_t;
+    for_steps2(Nc - 1, [&](int s, auto SL) {
+      lds_barrier();
+      constexpr int sl = (decltype(SL)::v + 1) % 2;
+      const int cl = s + 1;
+      const bool issue = cl < Nc;
+      if (issue) {
+        const int nr = rows_of(cl);
+        const int64_t t0 = (int64_t)cl * BT;
+        if (role < 2) {
+          constexpr int NH = NI / 2;
+#pragma unroll
+          for (int i = 0; i < NH; ++i) {
+            const int b = 1024 * (role * NH + i) + 16 * lane;
+            const int r = b / RB, jp = (b % RB) >> 4;
+            const int j = jp ^ kswz<DK>(r);
+            const int rr = r < nr ? r : nr - 1;
+            g2l16(xb + (t0 + rr) * p.sk_t + 8 * j, sm.k[sl] + 1024 * (role * NH + i));
+          }
+        } else if (role == 2) {
+          const unsigned char *rg = p.brec + ((gc0 + cl) * p.Hv + h) * kBrBytes;
+#pragma unroll
+          for (int i = 0; i < NR; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * i);
+        } else {
+          // v rows past the chunk's end repeat its last row (beta is 0 there)
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            const int r = (64 / LV) * i + lane / LV;
+            const int rr = r < nr ? r : nr - 1;
+            g2l16(vb + (t0 + rr) * p.sv_t + 8 * (lane % LV), sm.v[sl] + 1024 * i);
+          }
+        }
+      }
+      wait_vm<0>();
+    });
+  }
+}
+
+template <typename T, int DK, int NS>
+hipError_t launch_stm(const ChunkBwdArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)(a.dv / (NS * DVT)), (unsigned)a.Hv, (unsigned)a.n_seqs);
+  hipLaunchKernelGGL((bwd_states_multi_kernel<T, DK, NS>), grid, dim3((NS + 4) * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+// A multi-slice pass when its launch has at least this many workgroups (half
+// the CUs), else the one-slice kernel.
+constexpr int64_t kMultiMinWorkgroups = 128;
+
 template <typename T, int DK>
 hipError_t launch_st(const ChunkBwdArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(a.dv / DVT), (unsigned)a.Hv, (unsigned)a.n_seqs);
@@ -806,9 +1066,21 @@ hipError_t launch_chunk_bwd_dstate_mma(const ChunkBwdArgs &a, hipStream_t s) {
   return a.dk == 64 ? launch_ds<bf16, 64>(a, s) : launch_ds<bf16, 128>(a, s);
 }
 
+namespace {
+template <typename T, int DK>
+hipError_t launch_states(const ChunkBwdArgs &a, hipStream_t s) {
+  const int64_t pairs = a.n_seqs * a.Hv;
+  // eight chains fit twelve waves' registers at dk 64 only
+  if (DK == 64 && a.dv % (8 * DVT) == 0 && pairs * (a.dv / (8 * DVT)) >= kMultiMinWorkgroups)
+    return launch_stm<T, DK, 8>(a, s);
+  if (a.dv % (4 * DVT) == 0 && pairs * (a.dv / (4 * DVT)) >= kMultiMinWorkgroups) return launch_stm<T, DK, 4>(a, s);
+  return launch_st<T, DK>(a, s);
+}
+}  // namespace
+
 hipError_t launch_chunk_bwd_states_mma(const ChunkBwdArgs &a, hipStream_t s) {
-  if (a.act == kF16) return a.dk == 64 ? launch_st<f16, 64>(a, s) : launch_st<f16, 128>(a, s);
-  return a.dk == 64 ? launch_st<bf16, 64>(a, s) : launch_st<bf16, 128>(a, s);
+  if (a.act == kF16) return a.dk == 64 ? launch_states<f16, 64>(a, s) : launch_states<f16, 128>(a, s);
+  return a.dk == 64 ? launch_states<bf16, 64>(a, s) : launch_states<bf16, 128>(a, s);
 }
 
 }  // namespace gdn

@@ -241,3 +241,38 @@ def test_chunk_rule_bwd_slow_decay(act):
     torch.cuda.synchronize()
     ref = OB.chunk_rule_bwd(f64(q), f64(k), f64(v), g, beta, f64(do), scale, True, 1e-6, None, f64(h0), f64(dht))
     _check(got, ref, TAU[act])
+
+
+# The forward-state pass of the matrix-core path carries 4 (dk 128) or 8
+# (dk 64) value slices per workgroup when the launch has at least 128 such
+# workgroups (packed or batched sequences). These cases reach both forms and
+# compare with the oracle and, bit for bit, with per-sequence calls (which
+# run the one-slice pass).
+MULTI = [
+    ("slices4-dk128-fp16-8seq", 4, {"lengths": (1, 63, 64, 65, 130, 2, 3, 100)}),
+    ("slices8-dk64-bf16-8seq", 4, {"act": "bf16", "dk": 64, "lengths": (70, 1, 64, 129, 5, 66, 30, 64)}),
+]
+
+
+@pytest.mark.parametrize("name,cfg,over", MULTI, ids=[m[0] for m in MULTI])
+def test_chunk_rule_bwd_multi_slice_states(name, cfg, over):
+    s, q, k, v, g, beta, cu = _inputs(cfg, over)
+    (qd, kd, vd, gd, bd), cud = _dev(s, (q, k, v, g, beta), cu)
+    N = len(cu) - 1
+    do = synth.randn((s.B, s.T, s.Hv, s.dv), s.act, 460).cuda()
+    h0 = synth.randn((N, s.Hv, s.dv, s.dk), "f32", 461).cuda() * 0.5
+    scale = s.dk ** -0.5
+    got = gdn.gdn_chunk_rule_bwd(qd, kd, vd, gd, bd, do, scale, True, 1e-6, cud, h0, want_d_initial_state=True)
+    torch.cuda.synchronize()
+    ref = OB.chunk_rule_bwd(q, k, v, g, beta, f64(do), scale, True, 1e-6, cu, f64(h0))
+    _check(got, ref, TAU[s.act])
+    for i in range(N):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if a == b:
+            continue
+        one = gdn.gdn_chunk_rule_bwd(qd[:, a:b], kd[:, a:b], vd[:, a:b], gd[:, a:b], bd[:, a:b], do[:, a:b], scale,
+                                     True, 1e-6, None, h0[i:i + 1], want_d_initial_state=True)
+        torch.cuda.synchronize()
+        for n, x, y in zip(NAMES[:5], got[:5], one[:5]):
+            assert torch.equal(x[:, a:b], y), (n, i)
+        assert torch.equal(got[5][i], one[5][0]), ("d_initial_state", i)
