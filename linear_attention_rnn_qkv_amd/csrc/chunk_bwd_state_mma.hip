@@ -1025,6 +1025,408 @@ hipError_t launch_stm(const ChunkBwdArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Multi-slice reverse pass, for launches with many (sequence, head) pairs and
+// for running beside the forward-state pass: one workgroup = (sequence, value
+// head, NS * 16 value rows). One copy of the k and q tiles and of the
+// record's reverse part serves NS slices. Waves 0 .. NS - 1 carry the chain
+// of bwd_dstate_mma_kernel for one slice each (the same products in the same
+// order), waves NS .. 2 NS - 1 are their helpers (G = P'^T dO, the q term,
+// the dR' and dv stores); the last four waves copy the k tile, the q tile and
+// the halves of the record part and of the [64][16 NS] dO tile of the next
+// chunk into two-slot rings. Two barriers per step as in the one-slice
+// kernel. The dR' hand-off has one slot per slice: a helper reads the
+// previous step's stage before the middle barrier, after which its chain
+// writes the next one.
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int NS>
+struct DsMLds {
+  static constexpr int RB = DK * 2;
+  static constexpr int TILE = BT * RB;
+  static constexpr int VB = NS * DVT * 2;  // bytes per dO row
+  alignas(16) unsigned char k[2][TILE];
+  alignas(16) unsigned char q[2][TILE];
+  alignas(16) unsigned char o[2][BT * VB];
+  alignas(16) unsigned char rec[2][kDsRec];
+  alignas(16) float gg[NS][4 * 64 * 4];        // G of each slice, [mt][lane][4]
+  alignas(16) float hq[NS][DK / 16 * 64 * 4];  // q term of each slice, [mt][lane][4]
+  alignas(16) float stage[NS][4 * 64 * 4 + 64];  // dR' [mt][lane][4], then beta
+};
+
+template <typename T, int DK, int NS>
+__global__ __launch_bounds__((2 * NS + 4) * 64) void bwd_dstate_multi_kernel(ChunkBwdArgs p) {
+  using SM = DsMLds<T, DK, NS>;
+  using f8 = typename M2<T>::f8;
+  using v4 = typename M2<T>::v4;
+  constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB, VB = SM::VB;
+  constexpr int NI = SM::TILE / 1024;       // 1 KB copies per q/k tile
+  constexpr int NR = (int)(kDsRec / 1024);  // 1 KB copies per record part
+  constexpr int NO = BT * VB / 1024;        // 1 KB copies per dO tile
+  constexpr int LV = VB / 16;               // lanes per dO row in a copy
+  static_assert(NI <= 31 && NR % 2 == 0 && NO % 2 == 0 && NR / 2 + NO / 2 <= 31, "copies per loader wave");
+  static_assert(sizeof(SM) <= 160 * 1024, "LDS");
+  __shared__ SM sm;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
+  const int64_t jg = (lid % ntile) * (NS * DVT);
+  const int64_t h = (lid / ntile) % gridDim.y;
+  const int64_t n = lid / (ntile * gridDim.y);
+  const int64_t hk = h / (p.Hv / p.Hqk);
+  int64_t brow, bos, L, gc0;
+  if (p.cu_seqlens) {
+    brow = 0;
+    bos = p.cu_seqlens[n];
+    L = p.cu_seqlens[n + 1] - bos;
+    gc0 = p.cu_chunks[n];
+  } else {
+    brow = n;
+    bos = 0;
+    L = p.T;
+    gc0 = n * ((p.T + BT - 1) / BT);
+  }
+  const int Nc = (int)((L + BT - 1) / BT);
+  // step s works on chunk Nc - 1 - s
+  auto rows_of = [&](int ch) -> int {
+    const int64_t r = L - (int64_t)ch * BT;
+    return (int)(r < BT ? r : BT);
+  };
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  if (wave < 2 * NS) {
+    const int sw = wave < NS ? wave : wave - NS;  // the slice of this wave
+    const int64_t j0 = jg + DVT * sw;
+    const int64_t st_base = ((n * p.Hv + h) * p.dv + j0) * DK;
+    float *const gq = sm.gg[sw];
+    float *const hq = sm.hq[sw];
+    float *const stg = sm.stage[sw];
+    const int yrow = 4 * g + (c >> 2);
+    int trc[NT];
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt)
+      trc[mt] = yrow * RB + (((4 * (mt >> 1) + (c & 3)) ^ kswz<DK>(yrow)) << 4) + 8 * (mt & 1);
+    if (wave < NS) {
+      // -------------------------------------------------------------- chain
+      int fo[KT];
+#pragma unroll
+      for (int pp = 0; pp < KT; ++pp) fo[pp] = c * RB + (((4 * pp + g) ^ kswz<DK>(c)) << 4);
+      f32x4 dS[NT];  // dS[mt][i] = dS[dv row c][dk dk_of(mt, 4 g + i)]
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dS[mt][i] = p.d_final ? p.d_final[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] : 0.f;
+
+      for_steps2(Nc - 1, [&](int s, auto SL) {
+        lds_barrier();  // B0
+        constexpr int sl = decltype(SL)::v;
+        const int ch = Nc - 1 - s;
+        const int64_t gc = gc0 + ch;
+        const unsigned char *kt = sm.k[sl], *rec = sm.rec[sl];
+        const float *fa = reinterpret_cast<const float *>(rec + kDsF);
+        f32x4 U[4];
+        f8 mth[6], mtl[6], kTr[NT][2];
+        if (s >= 0) {
+          // U = K dS^T, with the q term of the previous step added first
+          f8 kfr[4][KT];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int pp = 0; pp < KT; ++pp) kfr[mt][pp] = *reinterpret_cast<const f8 *>(kt + mt * 16 * RB + fo[pp]);
+          if (s > 0) {
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt) dS[mt] += *reinterpret_cast<const f32x4 *>(&hq[(mt * 64 + lane) * 4]);
+          }
+          f8 Sh[KT], Sl[KT];
+#pragma unroll
+          for (int pp = 0; pp < KT; ++pp) split2x4<T>(dS[2 * pp], dS[2 * pp + 1], Sh[pp], Sl[pp]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            f32x4 u = zero4;
+#pragma unroll
+            for (int pp = 0; pp < KT; ++pp) {
+              u = mma<T>(kfr[mt][pp], Sh[pp], u);
+              u = mma<T>(kfr[mt][pp], Sl[pp], u);
+            }
+            U[mt] = u;
+          }
+#pragma unroll
+          for (int f = 0; f < 6; ++f) {
+            mth[f] = *reinterpret_cast<const f8 *>(rec + kDsMtH + f * 1024 + lane * 16);
+            mtl[f] = *reinterpret_cast<const f8 *>(rec + kDsMtL + f * 1024 + lane * 16);
+          }
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const unsigned char *ka1 = kt + trc[mt] + (32 * q) * RB, *ka2 = kt + trc[mt] + (32 * q + 16) * RB;
+              const s16x4 k1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka1));
+              const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
+              kTr[mt][q] = cat8<T>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
+            }
+          // dS_C to the workspace (as [dv][dk])
+          float *dsw = p.ds + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
+#pragma unroll
+          for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(dsw + dk_of(mt, 4 * g)) = dS[mt];
+        }
+        lds_barrier();  // B1: G of this chunk is in LDS, the stage has been read
+        if (s < 0) return;
+        f32x4 dD[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const f32x4 cr = *reinterpret_cast<const f32x4 *>(&fa[1 * BT + 16 * mt + 4 * g]);
+          dD[mt] = U[mt] * cr + *reinterpret_cast<const f32x4 *>(&gq[(mt * 64 + lane) * 4]);
+        }
+        f32x4 dR[4];
+        {
+          f8 Dh[2], Dl[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) split2x4<T>(dD[2 * q], dD[2 * q + 1], Dh[q], Dl[q]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            f32x4 r = zero4;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              if (q == 0 && mt >= 2) continue;
+              const int f = up_frag(mt, q);
+              r = mma<T>(mth[f], Dh[q], r);
+              r = mma<T>(mth[f], Dl[q], r);
+              r = mma<T>(mtl[f], Dh[q], r);
+            }
+            dR[mt] = r;
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4 *>(&stg[(mt * 64 + lane) * 4]) = dR[mt];
+        stg[4 * 64 * 4 + lane] = fa[2 * BT + lane];
+        f8 Fkh[2], Fkl[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4 fk0 = *reinterpret_cast<const f32x4 *>(&fa[4 * BT + 32 * q + 4 * g]);
+          const f32x4 fk1 = *reinterpret_cast<const f32x4 *>(&fa[4 * BT + 32 * q + 16 + 4 * g]);
+          split2x4<T>(fk0 * dR[2 * q], fk1 * dR[2 * q + 1], Fkh[q], Fkl[q]);
+        }
+        const float eC = fa[5 * BT];
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+          f32x4 a = dS[mt] * eC;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            a = mma<T>(kTr[mt][q], Fkh[q], a);
+            a = mma<T>(kTr[mt][q], Fkl[q], a);
+          }
+          dS[mt] = a;
+        }
+      });
+      lds_barrier();  // the last q term is in LDS
+      if (Nc > 0) {
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) dS[mt] += *reinterpret_cast<const f32x4 *>(&hq[(mt * 64 + lane) * 4]);
+      }
+      if (p.d_init) {
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+          *reinterpret_cast<f32x4 *>(p.d_init + st_base + (int64_t)c * DK + dk_of(mt, 4 * g)) = dS[mt];
+      }
+    } else {
+      // ---------------------------------------------------------- helper
+      // the stage (dR' of the previous step in accumulator layout, then
+      // beta) as lane t's row t: x[cc] = dR'[t][j0 + cc]
+      auto load_stage = [&](float (&x)[16], float &bt) {
+        const int t = lane, mt = t >> 4, gr = (t >> 2) & 3, i = t & 3;
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) x[cc] = stg[(mt * 64 + 16 * gr + cc) * 4 + i];
+        bt = stg[4 * 64 * 4 + t];
+      };
+      // dR' (FP32) and dv = beta dR' of step s2 (chunk Nc - 1 - s2)
+      auto store_rows = [&](int s2, float (&x)[16], float bt) {
+        const int ch = Nc - 1 - s2;
+        const int64_t gc = gc0 + ch, t0 = bos + (int64_t)ch * BT;
+        const int nr = rows_of(ch);
+        const int t = lane;
+        float *dr = p.drp + ((gc * p.Hv + h) * BT + t) * p.dv + j0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          *reinterpret_cast<f32x4 *>(dr + 4 * v) = f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
+        if (t < nr) {
+          const int64_t o = brow * p.sdv_b + (t0 + t) * p.sdv_t + h * p.dv + j0;
+#pragma unroll
+          for (int cc = 0; cc < 16; ++cc) x[cc] *= bt;
+          if (p.grad_dtype == kF32) {
+            float *dv = static_cast<float *>(p.dvv) + o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              *reinterpret_cast<f32x4 *>(dv + 4 * v) = f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
+          } else {
+            T *dv = static_cast<T *>(p.dvv) + o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              *reinterpret_cast<v4 *>(dv + 4 * v) =
+                  __builtin_convertvector(f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]}, v4);
+          }
+        }
+      };
+      const int otr = (4 * g + (c >> 2)) * VB + 2 * DVT * sw + 8 * (c & 3);
+      for_steps2(Nc - 1, [&](int s, auto SL) {
+        lds_barrier();  // B0
+        constexpr int sl = decltype(SL)::v;
+        const unsigned char *qt = sm.q[sl], *rec = sm.rec[sl];
+        const float *fa = reinterpret_cast<const float *>(rec + kDsF);
+        f8 Bo[2];
+        float x[16], bt = 0.f;
+        if (s >= 1) load_stage(x, bt);
+        if (s >= 0) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const unsigned char *ob = sm.o[sl] + otr + 32 * q * VB;
+            const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ob));
+            const s16x4 r1 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ob + 16 * VB));
+            Bo[q] = cat8<T>(__builtin_bit_cast(v4, r0), __builtin_bit_cast(v4, r1));
+          }
+          // G = P'^T dO in the accumulator layout of dDelta
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            f32x4 a = zero4;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              if (q == 0 && mt >= 2) continue;
+              const int f = up_frag(mt, q);
+              const f8 ph = *reinterpret_cast<const f8 *>(rec + kDsPH + f * 1024 + lane * 16);
+              const f8 pl = *reinterpret_cast<const f8 *>(rec + kDsPL + f * 1024 + lane * 16);
+              a = mma<T>(ph, Bo[q], a);
+              a = mma<T>(pl, Bo[q], a);
+            }
+            *reinterpret_cast<f32x4 *>(&gq[(mt * 64 + lane) * 4]) = a;
+          }
+        }
+        lds_barrier();  // B1
+        if (s < 0) return;
+        // q term Q^T (fq (.) dO), added to dS by the chain at the next step
+        f8 Fqh[2], Fql[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4 fq0 = *reinterpret_cast<const f32x4 *>(&fa[3 * BT + 32 * q + 4 * g]);
+          const f32x4 fq1 = *reinterpret_cast<const f32x4 *>(&fa[3 * BT + 32 * q + 16 + 4 * g]);
+          float xq[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xq[e] = fq0[e] * f(Bo[q][e]);
+            xq[4 + e] = fq1[e] * f(Bo[q][4 + e]);
+          }
+          split8<T>(xq, Fqh[q], Fql[q]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+          f32x4 a = zero4;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const unsigned char *qa1 = qt + trc[mt] + (32 * q) * RB, *qa2 = qt + trc[mt] + (32 * q + 16) * RB;
+            const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(qa1));
+            const s16x4 q2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(qa2));
+            const f8 qT = cat8<T>(__builtin_bit_cast(v4, q1), __builtin_bit_cast(v4, q2));
+            a = mma<T>(qT, Fqh[q], a);
+            a = mma<T>(qT, Fql[q], a);
+          }
+          *reinterpret_cast<f32x4 *>(&hq[(mt * 64 + lane) * 4]) = a;
+        }
+        if (s >= 1) store_rows(s - 1, x, bt);
+      });
+      lds_barrier();  // the last stage is in LDS
+      if (Nc > 0) {
+        float x[16], bt;
+        load_stage(x, bt);
+        store_rows(Nc - 1, x, bt);
+      }
+    }
+  } else {
+    // ------------------------------------------------------------- loads
+    // role 0 the k tile, 1 the q tile, 2 and 3 the halves of the record part
+    // and of the dO tile, for the chunk of step s + 1; complete before the
+    // barrier that ends step s
+    const int role = wave - 2 * NS;
+    if (role < 2) {
+      const bool isk = role == 0;
+      const int64_t st = isk ? p.sk_t : p.sq_t;
+      const T *xb = static_cast<const T *>(isk ? p.k : p.q) + brow * (isk ? p.sk_b : p.sq_b) +
+                    hk * (isk ? p.sk_h : p.sq_h) + bos * st;
+      uint32_t xoff[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int b = 1024 * i + 16 * lane;
+        const int r = b / RB, jp = (b % RB) >> 4;
+        const int j = jp ^ kswz<DK>(r);
+        xoff[i] = (uint32_t)(((int64_t)r * st + 8 * j) * 2);
+      }
+      for_steps2(Nc - 1, [&](int s, auto SL) {
+        lds_barrier();
+        constexpr int sl = (decltype(SL)::v + 1) % 2;  // slot of step s + 1
+        if (s + 1 < Nc) {
+          const int ch = Nc - 2 - s;
+          const int nr = rows_of(ch);
+          const int64_t t0 = (int64_t)ch * BT;
+          unsigned char *xt = isk ? sm.k[sl] : sm.q[sl];
+          if (nr == BT) {
+            const unsigned char *xg = reinterpret_cast<const unsigned char *>(xb + t0 * st);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) g2l16(xg + xoff[i], xt + 1024 * i);
+          } else {
+            // partial chunk: rows past its end repeat its last row
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+              const int b = 1024 * i + 16 * lane;
+              const int r = b / RB, jp = (b % RB) >> 4;
+              const int j = jp ^ kswz<DK>(r);
+              const int rr = r < nr ? r : nr - 1;
+              g2l16(xb + (t0 + rr) * st + 8 * j, xt + 1024 * i);
+            }
+          }
+        }
+        lds_barrier();  // B1
+        wait_vm<0>();
+      });
+      lds_barrier();
+    } else {
+      constexpr int NRH = NR / 2, NOH = NO / 2;
+      const int half = role - 2;
+      const T *ob = static_cast<const T *>(p.d_o) + brow * p.sdo_b + h * p.sdo_h + jg + bos * p.sdo_t;
+      for_steps2(Nc - 1, [&](int s, auto SL) {
+        lds_barrier();
+        constexpr int sl = (decltype(SL)::v + 1) % 2;
+        if (s + 1 < Nc) {
+          const int ch = Nc - 2 - s;
+          const int nr = rows_of(ch);
+          const int64_t t0 = (int64_t)ch * BT;
+          const unsigned char *rg = p.brec + ((gc0 + ch) * p.Hv + h) * kBrBytes + kBrF + 1024 * NRH * half;
+#pragma unroll
+          for (int i = 0; i < NRH; ++i) g2l16(rg + 1024 * i + 16 * lane, sm.rec[sl] + 1024 * (NRH * half + i));
+          // dO rows past the chunk's end repeat its last row (their factors are 0)
+#pragma unroll
+          for (int i = 0; i < NOH; ++i) {
+            const int ci = NOH * half + i;
+            const int r = (64 / LV) * ci + lane / LV;
+            const int rr = r < nr ? r : nr - 1;
+            g2l16(ob + (t0 + rr) * p.sdo_t + 8 * (lane % LV), sm.o[sl] + 1024 * ci);
+          }
+        }
+        lds_barrier();  // B1
+        wait_vm<0>();
+      });
+      lds_barrier();
+    }
+  }
+}
+
+template <typename T, int DK, int NS>
+hipError_t launch_dsm(const ChunkBwdArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)(a.dv / (NS * DVT)), (unsigned)a.Hv, (unsigned)a.n_seqs);
+  hipLaunchKernelGGL((bwd_dstate_multi_kernel<T, DK, NS>), grid, dim3((2 * NS + 4) * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 // A multi-slice pass when its launch has at least this many workgroups (half
 // the CUs), else the one-slice kernel.
 constexpr int64_t kMultiMinWorkgroups = 128;
@@ -1061,9 +1463,21 @@ bool chunk_bwd_state_mma_supported(const ChunkBwdArgs &a) {
          align_of_host(va) >= (int)(4 * es > 16 ? 16 : 4 * es);
 }
 
+namespace {
+template <typename T, int DK>
+hipError_t launch_dstate(const ChunkBwdArgs &a, hipStream_t s) {
+  const int64_t pairs = a.n_seqs * a.Hv;
+  // four slices (twelve waves) fit LDS at dk 64 only
+  if constexpr (DK == 64)
+    if (a.dv % (4 * DVT) == 0 && pairs * (a.dv / (4 * DVT)) >= kMultiMinWorkgroups) return launch_dsm<T, DK, 4>(a, s);
+  if (a.dv % (2 * DVT) == 0 && pairs * (a.dv / (2 * DVT)) >= kMultiMinWorkgroups) return launch_dsm<T, DK, 2>(a, s);
+  return launch_ds<T, DK>(a, s);
+}
+}  // namespace
+
 hipError_t launch_chunk_bwd_dstate_mma(const ChunkBwdArgs &a, hipStream_t s) {
-  if (a.act == kF16) return a.dk == 64 ? launch_ds<f16, 64>(a, s) : launch_ds<f16, 128>(a, s);
-  return a.dk == 64 ? launch_ds<bf16, 64>(a, s) : launch_ds<bf16, 128>(a, s);
+  if (a.act == kF16) return a.dk == 64 ? launch_dstate<f16, 64>(a, s) : launch_dstate<f16, 128>(a, s);
+  return a.dk == 64 ? launch_dstate<bf16, 64>(a, s) : launch_dstate<bf16, 128>(a, s);
 }
 
 namespace {
@@ -1074,6 +1488,7 @@ hipError_t launch_states(const ChunkBwdArgs &a, hipStream_t s) {
   if (DK == 64 && a.dv % (8 * DVT) == 0 && pairs * (a.dv / (8 * DVT)) >= kMultiMinWorkgroups)
     return launch_stm<T, DK, 8>(a, s);
   if (a.dv % (4 * DVT) == 0 && pairs * (a.dv / (4 * DVT)) >= kMultiMinWorkgroups) return launch_stm<T, DK, 4>(a, s);
+  if (a.dv % (2 * DVT) == 0 && pairs * (a.dv / (2 * DVT)) >= kMultiMinWorkgroups) return launch_stm<T, DK, 2>(a, s);
   return launch_st<T, DK>(a, s);
 }
 }  // namespace

@@ -251,6 +251,11 @@ def test_chunk_rule_bwd_slow_decay(act):
 MULTI = [
     ("slices4-dk128-fp16-8seq", 4, {"lengths": (1, 63, 64, 65, 130, 2, 3, 100)}),
     ("slices8-dk64-bf16-8seq", 4, {"act": "bf16", "dk": 64, "lengths": (70, 1, 64, 129, 5, 66, 30, 64)}),
+    # 16 sequences of 8 value heads: the packed call takes the multi-slice
+    # forms of both passes, each per-sequence call (8 pairs) the one-slice ones
+    ("multi-vs-one-slice-dk128-bf16-16seq", 4,
+     {"act": "bf16", "Hqk": 4, "Hv": 8,
+      "lengths": (65, 1, 130, 64, 0, 200, 3, 127, 64, 66, 10, 129, 2, 70, 191, 33)}),
 ]
 
 
@@ -276,3 +281,41 @@ def test_chunk_rule_bwd_multi_slice_states(name, cfg, over):
         for n, x, y in zip(NAMES[:5], got[:5], one[:5]):
             assert torch.equal(x[:, a:b], y), (n, i)
         assert torch.equal(got[5][i], one[5][0]), ("d_initial_state", i)
+
+
+def test_chunk_rule_bwd_back_to_back_on_a_stream():
+    """Two calls in a row on a non-default stream with one workspace: the
+    forward-state pass runs on the library's second stream and is joined back
+    before the gradient kernel, so the second call's prep cannot overwrite
+    records the first call's passes still read. Both results equal the same
+    calls made one at a time on the default stream."""
+    s = synth.spec(3).replace(T=640, Hqk=16, Hv=32)
+    dt = synth.TORCH_DTYPE[s.act]
+    ins = []
+    for seed in (0, 1):
+        q = synth.randn((1, s.T, s.Hqk, s.dk), s.act, 480 + 10 * seed).cuda()
+        k = synth.randn((1, s.T, s.Hqk, s.dk), s.act, 481 + 10 * seed).cuda()
+        v = synth.randn((1, s.T, s.Hv, s.dv), s.act, 482 + 10 * seed).cuda()
+        g = -torch.rand(1, s.T, s.Hv, generator=torch.Generator().manual_seed(483 + seed)).cuda() * 0.3
+        b = torch.rand(1, s.T, s.Hv, generator=torch.Generator().manual_seed(484 + seed)).cuda()
+        do = synth.randn((1, s.T, s.Hv, s.dv), s.act, 485 + 10 * seed).cuda()
+        ins.append((q, k, v, g, b, do))
+    ws = torch.empty(gdn.gdn_chunk_rule_bwd_workspace_bytes(1, s.T, (s.Hqk, s.dk, s.Hv, s.dv)), dtype=torch.uint8,
+                     device="cuda")
+    scale = s.dk ** -0.5
+    ref = []
+    for x in ins:
+        ref.append([t.clone() for t in gdn.gdn_chunk_rule_bwd(*x[:5], x[5], scale, True, 1e-6, workspace=ws)
+                    if t is not None])
+        torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        got = [[t for t in gdn.gdn_chunk_rule_bwd(*x[:5], x[5], scale, True, 1e-6, workspace=ws) if t is not None]
+               for x in ins]
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    assert dt in (torch.bfloat16, torch.float16)
+    for i in range(2):
+        for j, (a, r) in enumerate(zip(got[i], ref[i])):
+            assert torch.equal(a, r), (i, NAMES[j])

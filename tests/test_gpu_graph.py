@@ -98,8 +98,9 @@ def test_decode_graph_replays_advance_the_state():
 
 
 @pytest.mark.parametrize("cfg,over", [(2, {"T": 150, "Hqk": 1, "Hv": 2}), (4, {"lengths": (5, 70, 1, 64),
-                                                                             "Hqk": 1, "Hv": 2})],
-                         ids=["bf16-gqa", "fp16-packed"])
+                                                                             "Hqk": 1, "Hv": 2}),
+                                      (2, {"T": 200})],
+                         ids=["bf16-gqa", "fp16-packed", "bf16-two-slice-state-passes"])
 def test_layer_bwd_graph_replays_equal_eager(cfg, over):
     """The whole layer-core backward (its forward recomputed, then the three
     backward stages, every partial sum in the caller's workspace) captured
