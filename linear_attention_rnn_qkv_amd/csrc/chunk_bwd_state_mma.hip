@@ -853,6 +853,11 @@ __global__ __launch_bounds__((NS + 4) * 64) void bwd_states_multi_kernel(ChunkBw
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         S[mt][i] = p.init_state ? p.init_state[st_base + (int64_t)c * DK + dk_of(mt, 4 * g + i)] : 0.f;
+    if (Nc > 0) {  // S0 of the first chunk
+      float *sw = p.s0 + ((gc0 * p.Hv + h) * p.dv + j0 + c) * DK;
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(sw + dk_of(mt, 4 * g)) = S[mt];
+    }
     for_steps2(Nc - 1, [&](int s, auto SL) {
       lds_barrier();
       if (s < 0) return;
@@ -897,11 +902,6 @@ __global__ __launch_bounds__((NS + 4) * 64) void bwd_states_multi_kernel(ChunkBw
           const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
           kTr[mt][q] = cat8<T>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
         }
-      {  // S0 to the workspace ([dv][dk])
-        float *sw = p.s0 + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
-#pragma unroll
-        for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(sw + dk_of(mt, 4 * g)) = S[mt];
-      }
       // R = V - e^gamma rk (.) U; X = beta (.) R
       f8 Bv[2];
 #pragma unroll
@@ -971,6 +971,14 @@ __global__ __launch_bounds__((NS + 4) * 64) void bwd_states_multi_kernel(ChunkBw
           a = mma<T>(kTr[mt][q], Bwl[q], a);
         }
         S[mt] = a;
+      }
+      // the state just formed is S0 of the next chunk: stored at the end of
+      // the step, after the step's copies have drained from the CU's memory
+      // queue
+      if (s + 1 < Nc) {
+        float *sw = p.s0 + (((gc + 1) * p.Hv + h) * p.dv + j0 + c) * DK;
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(sw + dk_of(mt, 4 * g)) = S[mt];
       }
     });
   } else {
@@ -1167,13 +1175,16 @@ __global__ __launch_bounds__((2 * NS + 4) * 64) void bwd_dstate_multi_kernel(Chu
               const s16x4 k2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<unsigned char *>(ka2));
               kTr[mt][q] = cat8<T>(__builtin_bit_cast(v4, k1), __builtin_bit_cast(v4, k2));
             }
-          // dS_C to the workspace (as [dv][dk])
+        }
+        lds_barrier();  // B1: G of this chunk is in LDS, the stage has been read
+        if (s < 0) return;
+        {  // dS_C to the workspace (as [dv][dk]); issued after the middle
+           // barrier, when the step's copies no longer fill the CU's memory
+           // queue that the stores would wait behind
           float *dsw = p.ds + ((gc * p.Hv + h) * p.dv + j0 + c) * DK;
 #pragma unroll
           for (int mt = 0; mt < NT; ++mt) *reinterpret_cast<f32x4 *>(dsw + dk_of(mt, 4 * g)) = dS[mt];
         }
-        lds_barrier();  // B1: G of this chunk is in LDS, the stage has been read
-        if (s < 0) return;
         f32x4 dD[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
