@@ -77,6 +77,34 @@ def test_prologue_parity(name, cfg, over):
     H.assert_close(f64(beta), rb, 1e-5, "beta")
 
 
+# The prologue over every token of longer inputs against the oracle: 8192
+# dense tokens (one 128-token tile per block and CU), 16383 and 33000 packed
+# tokens (two and four blocks per CU, sequence boundaries inside tiles and a
+# partial last tile).
+DEEP = [
+    ("gqa-bf16-T8192", 2, {}),
+    ("varlen-fp16-16383-16seq", 4,
+     {"lengths": (1, 700, 64, 65, 3000, 2, 129, 4096, 63, 2500, 1, 1500, 2000, 200, 1000, 1062)}),
+    ("varlen-fp16-33000-9seq", 4,
+     {"lengths": (5000, 1, 8191, 64, 12000, 3, 7000, 130, 611)}),
+]
+
+
+@pytest.mark.parametrize("name,cfg,over", DEEP, ids=[d[0] for d in DEEP])
+def test_prologue_parity_launch_shapes(name, cfg, over):
+    s = _spec(cfg, over)
+    assert s.T == (8192 if cfg == 2 else sum(over["lengths"]))
+    x = synth.make_inputs(s)
+    xd = H.to_dev(x)
+    qkv, g, beta = gdn.gdn_prologue_fwd(xd["x_q"], xd["x_k"], xd["x_v"], xd["conv_w"], None, xd["a"],
+                                        xd["b"], xd["A_log"], xd["dt_bias"], xd["cu_seqlens"], _dims(s))
+    torch.cuda.synchronize()
+    rq, rg, rb = H.oracle_prologue(x, s)
+    H.assert_close(f64(qkv), rq, TAU[s.act], "qkv")
+    H.assert_close(f64(g), rg, 1e-5, "g")
+    H.assert_close(f64(beta), rb, 1e-5, "beta")
+
+
 @pytest.mark.parametrize("name,cfg,over", [SMALL[0], SMALL[2], SMALL[5]], ids=[IDS[0], IDS[2], IDS[5]])
 def test_prologue_caller_side_l2norm(name, cfg, over):
     s = _spec(cfg, over)
