@@ -64,6 +64,16 @@ __device__ __forceinline__ void split4(f32x4 x, V &hi, V &lo) {
   lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4), V);
 }
 
+// threadIdx.x through an empty asm statement: LDS addresses derived from it
+// inside the value-head loop are computed there, at their use, instead of
+// being kept live from the kernel's start (at 256 VGPRs the compiler spills
+// such addresses and every reload waits for all loads in flight)
+__device__ __forceinline__ int fresh_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 template <typename T, int DK>
 struct GradLds {
   static constexpr int RB = DK * 2;  // bytes per row of a dk-wide BF16 tile
@@ -306,9 +316,11 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
       float rz[4] = {0.f, 0.f, 0.f, 0.f}, rw[4] = {0.f, 0.f, 0.f, 0.f}, cz[2] = {0.f, 0.f};
       // the lane's row and column factors, read once (the stores below would
       // otherwise order every factor read behind them)
-      const f32x4 gtv = *reinterpret_cast<const f32x4 *>(&sm.gam[16 * tt + 4 * g]);
-      const f32x4 btv = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * tt + 4 * g]);
-      const float gsv[2] = {sm.gam[32 * jh + c], sm.gam[32 * jh + 16 + c]};
+      const int ft = fresh_tid(), fw = ft >> 6, frow = 16 * (fw & 3) + 4 * ((ft & 63) >> 4);
+      const int fcol = 32 * (fw >> 2) + (ft & 15);
+      const f32x4 gtv = *reinterpret_cast<const f32x4 *>(&sm.gam[frow]);
+      const f32x4 btv = *reinterpret_cast<const f32x4 *>(&sm.beta[frow]);
+      const float gsv[2] = {sm.gam[fcol], sm.gam[fcol + 16]};
       float z1v[2][4], z2v[2][4];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -339,17 +351,23 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
         rz[i] = lane_sum<16>(rz[i]);
         rw[i] = lane_sum<16>(rw[i]);
       }
-      if (c == 0)
+      if (c == 0) {
+        const int ft = fresh_tid(), fw = ft >> 6, r0 = 16 * (fw & 3) + 4 * ((ft & 63) >> 4);
+        float *zr = &sm.rowz[fw >> 2][r0], *wr = &sm.roww[fw >> 2][r0];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sm.rowz[jh][16 * tt + 4 * g + i] = rz[i];
-          sm.roww[jh][16 * tt + 4 * g + i] = rw[i];
+          zr[i] = rz[i];
+          wr[i] = rw[i];
         }
+      }
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         cz[a] += __shfl_xor(cz[a], 16, 64);
         cz[a] += __shfl_xor(cz[a], 32, 64);
-        if (g == 0) sm.colz[tt][16 * (2 * jh + a) + c] = cz[a];
+        if (g == 0) {
+          const int ft = fresh_tid(), fw = ft >> 6;
+          sm.colz[fw & 3][16 * (2 * (fw >> 2) + a) + (ft & 15)] = cz[a];
+        }
       }
     }
     // row dots q_t . k1_t, k_t . k3_t, k_t . k2_t (raw rows) over this wave's
@@ -377,9 +395,10 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
         mm += __shfl_xor(mm, off, 64);
       }
       if (g == 0) {
-        sm.pa[jh][t] = a;
-        sm.pb[jh][t] = b;
-        sm.pm[jh][t] = mm;
+        const int ft = fresh_tid(), fw = ft >> 6, ftt = 16 * (fw & 3) + (ft & 15);
+        sm.pa[fw >> 2][ftt] = a;
+        sm.pb[fw >> 2][ftt] = b;
+        sm.pm[fw >> 2][ftt] = mm;
       }
 #pragma unroll
       for (int m = 0; m < NJW; ++m)
@@ -391,9 +410,9 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
     }
     {
       dbp = lane_sum<8>(dbp);
-      if ((tid & 7) == 0) sm.db[st_t] = dbp;
+      if ((tid & 7) == 0) sm.db[fresh_tid() >> 3] = dbp;
       sdp = lane_sum<64>(sdp);
-      if (lane == 0) sm.sdot[wave] = sdp;
+      if (lane == 0) sm.sdot[fresh_tid() >> 6] = sdp;
     }
     __syncthreads();
 

@@ -1496,8 +1496,8 @@ template <typename T, int DK>
 hipError_t launch_states(const ChunkBwdArgs &a, hipStream_t s) {
   const int64_t pairs = a.n_seqs * a.Hv;
   // eight chains fit twelve waves' registers at dk 64 only
-  if (DK == 64 && a.dv % (8 * DVT) == 0 && pairs * (a.dv / (8 * DVT)) >= kMultiMinWorkgroups)
-    return launch_stm<T, DK, 8>(a, s);
+  if constexpr (DK == 64)
+    if (a.dv % (8 * DVT) == 0 && pairs * (a.dv / (8 * DVT)) >= kMultiMinWorkgroups) return launch_stm<T, DK, 8>(a, s);
   if (a.dv % (4 * DVT) == 0 && pairs * (a.dv / (4 * DVT)) >= kMultiMinWorkgroups) return launch_stm<T, DK, 4>(a, s);
   if (a.dv % (2 * DVT) == 0 && pairs * (a.dv / (2 * DVT)) >= kMultiMinWorkgroups) return launch_stm<T, DK, 2>(a, s);
   return launch_st<T, DK>(a, s);

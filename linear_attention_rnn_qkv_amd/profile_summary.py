@@ -69,6 +69,12 @@ KERNELS = {
                                                         "mfma_tiles.h", "device_common.h", "gdn_internal.h"]),
     "bwd_grad_mma_kernel": ("bwd_grad_mma_kernel", ["chunk_bwd_mma.hip", "chunk_bwd_common.h", "mfma_tiles.h",
                                                     "device_common.h", "gdn_internal.h"]),
+    "bwd_states_multi_kernel": ("bwd_states_multi_kernel", ["chunk_bwd_state_mma.hip", "chunk_bwd_common.h",
+                                                            "mfma_tiles.h", "device_common.h", "gdn_internal.h"]),
+    "bwd_dstate_multi_kernel": ("bwd_dstate_multi_kernel", ["chunk_bwd_state_mma.hip", "chunk_bwd_common.h",
+                                                            "mfma_tiles.h", "device_common.h", "gdn_internal.h"]),
+    "chunk_state_quad_kernel": ("chunk_state_quad_kernel", ["chunk_state.hip", "mfma_tiles.h", "device_common.h",
+                                                            "gdn_internal.h"]),
 }
 
 
