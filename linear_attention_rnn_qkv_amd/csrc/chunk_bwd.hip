@@ -27,7 +27,12 @@
 //   bwd_grad_kernel    per (chunk, q/k head), the value heads of the group
 //                      in turn: dq, dk (through the L2 fold), dg, dbeta
 // Products run in FP32 on the vector ALU from LDS tiles; the forward's MFMA
-// records (BF16 fragments of M diag(beta), not M) are not reused.
+// records (BF16 fragments of M diag(beta), not M) are not reused. For BF16
+// and FP16 activations at dk 64/128 the prep also writes matrix-core records
+// and the state passes and the gradients run on the matrix cores
+// (chunk_bwd_state_mma.hip, chunk_bwd_mma.hip); the two state passes are
+// independent of each other, and there the forward-state pass runs on a
+// second stream beside the reverse pass (launch_state_passes_mma).
 #include <mutex>
 #include <type_traits>
 
