@@ -266,17 +266,20 @@ def test_chunk_rule_bwd_multi_slice_states(name, cfg, over):
     N = len(cu) - 1
     do = synth.randn((s.B, s.T, s.Hv, s.dv), s.act, 460).cuda()
     h0 = synth.randn((N, s.Hv, s.dv, s.dk), "f32", 461).cuda() * 0.5
+    dfin = synth.randn((N, s.Hv, s.dv, s.dk), "f32", 462).cuda() * 0.5
     scale = s.dk ** -0.5
-    got = gdn.gdn_chunk_rule_bwd(qd, kd, vd, gd, bd, do, scale, True, 1e-6, cud, h0, want_d_initial_state=True)
+    got = gdn.gdn_chunk_rule_bwd(qd, kd, vd, gd, bd, do, scale, True, 1e-6, cud, h0, dfin,
+                                 want_d_initial_state=True)
     torch.cuda.synchronize()
-    ref = OB.chunk_rule_bwd(q, k, v, g, beta, f64(do), scale, True, 1e-6, cu, f64(h0))
+    ref = OB.chunk_rule_bwd(q, k, v, g, beta, f64(do), scale, True, 1e-6, cu, f64(h0), f64(dfin))
     _check(got, ref, TAU[s.act])
     for i in range(N):
         a, b = int(cu[i]), int(cu[i + 1])
         if a == b:
+            assert torch.equal(got[5][i], dfin[i]), ("d_initial_state of an empty sequence", i)
             continue
         one = gdn.gdn_chunk_rule_bwd(qd[:, a:b], kd[:, a:b], vd[:, a:b], gd[:, a:b], bd[:, a:b], do[:, a:b], scale,
-                                     True, 1e-6, None, h0[i:i + 1], want_d_initial_state=True)
+                                     True, 1e-6, None, h0[i:i + 1], dfin[i:i + 1], want_d_initial_state=True)
         torch.cuda.synchronize()
         for n, x, y in zip(NAMES[:5], got[:5], one[:5]):
             assert torch.equal(x[:, a:b], y), (n, i)
