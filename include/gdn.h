@@ -38,9 +38,12 @@
  *     read in place, never copied) except that the innermost (channel /
  *     head-dim) stride must be 1. Outputs that this ABI calls "contiguous"
  *     must have row-major strides.
- *   - All memory is owned by the caller. The library never allocates, frees
- *     or synchronises; every call only enqueues kernels on `stream` (a
- *     hipStream_t; NULL is the legacy default stream) and returns.
+ *   - All memory is owned by the caller. The library never allocates device
+ *     memory, frees or synchronises; every call only enqueues work ordered on
+ *     `stream` (a hipStream_t; NULL is the legacy default stream) and
+ *     returns. gdn_chunk_rule_bwd and gdn_layer_bwd fork part of their work
+ *     onto a second stream the library keeps per device and join it back
+ *     (see gdn_chunk_rule_bwd).
  *   - Every argument is checked from host metadata alone (shapes, strides,
  *     dtypes, pointer alignment and overlap) before anything is launched, so
  *     a call that returns an error has had no effect ([P2] Post-GDR
