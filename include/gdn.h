@@ -38,12 +38,9 @@
  *     read in place, never copied) except that the innermost (channel /
  *     head-dim) stride must be 1. Outputs that this ABI calls "contiguous"
  *     must have row-major strides.
- *   - All memory is owned by the caller. The library never allocates device
- *     memory, frees or synchronises; every call only enqueues work ordered on
- *     `stream` (a hipStream_t; NULL is the legacy default stream) and
- *     returns. gdn_chunk_rule_bwd and gdn_layer_bwd fork part of their work
- *     onto a second stream the library keeps per device and join it back
- *     (see gdn_chunk_rule_bwd).
+ *   - All memory is owned by the caller. The library never allocates, frees
+ *     or synchronises; every call only enqueues kernels on `stream` (a
+ *     hipStream_t; NULL is the legacy default stream) and returns.
  *   - Every argument is checked from host metadata alone (shapes, strides,
  *     dtypes, pointer alignment and overlap) before anything is launched, so
  *     a call that returns an error has had no effect ([P2] Post-GDR
@@ -435,13 +432,6 @@ gdn_status gdn_prologue_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
  *                   this call's work on `stream` is done
  * Outputs must not overlap inputs or each other. Supported: dk 64, 128 or
  * 256, dv a multiple of 16 (GDN_ERR_NOT_SUPPORTED otherwise).
- * Streams: with BF16/FP16 activations and dk 64/128 the forward-state pass
- * runs on a second stream the library keeps per device (created on the
- * first such call, default priority, never destroyed), forked from `stream`
- * by an event and joined back before the last kernel, so all of the call's
- * work is ordered on `stream` as usual and a capture of `stream` captures
- * both branches. The first such call on a device should not itself be under
- * stream capture (it creates that stream and two events).
  */
 gdn_status gdn_chunk_rule_bwd(const gdn_tensor *q, const gdn_tensor *k,
                               const gdn_tensor *v, const gdn_tensor *g,
@@ -488,7 +478,7 @@ size_t gdn_chunk_rule_bwd_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs,
  *                   aligned, owned by the caller and not used by any other
  *                   call until this call's work on `stream` is done
  * Outputs must not overlap inputs, each other or the workspace. Supported:
- * the geometries of gdn_chunk_rule_bwd, whose note on streams applies.
+ * the geometries of gdn_chunk_rule_bwd.
  */
 gdn_status gdn_layer_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
                          const gdn_tensor *x_v, const gdn_tensor *conv_w,

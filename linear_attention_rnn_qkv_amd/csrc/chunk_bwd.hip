@@ -31,9 +31,7 @@
 // and FP16 activations at dk 64/128 the prep also writes matrix-core records
 // and the state passes and the gradients run on the matrix cores
 // (chunk_bwd_state_mma.hip, chunk_bwd_mma.hip); the two state passes are
-// independent of each other, and there the forward-state pass runs on a
-// second stream beside the reverse pass (launch_state_passes_mma).
-#include <mutex>
+// independent of each other and run side by side in one launch there.
 #include <type_traits>
 
 #include "chunk_bwd_common.h"
@@ -1117,71 +1115,6 @@ __global__ __launch_bounds__(grad_threads<DK>()) void bwd_grad_kernel(ChunkBwdAr
   }
 }
 
-// A second stream per device (created on the first call that uses it, with
-// the default priority, kept until the process ends) and the two events that
-// fork work onto it from the caller's stream and join it back. The mutex makes
-// each fork .. join sequence atomic across host threads.
-constexpr int kMaxDevices = 64;
-struct SideStream {
-  hipStream_t st = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-
-// the side stream of the device that owns stream s (call with g_side_mu held)
-hipError_t side_stream_of(hipStream_t s, SideStream *&out) {
-  hipDevice_t dev = -1;
-  hipError_t e = hipStreamGetDevice(s, &dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  SideStream &sd = g_side[dev];
-  if (!sd.st) {
-    int cur = -1;
-    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
-    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
-    SideStream n;
-    e = hipStreamCreateWithFlags(&n.st, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      if (n.join) (void)hipEventDestroy(n.join);
-      if (n.fork) (void)hipEventDestroy(n.fork);
-      if (n.st) (void)hipStreamDestroy(n.st);
-    } else {
-      sd = n;
-    }
-    if (cur != dev) {
-      const hipError_t e2 = hipSetDevice(cur);
-      if (e == hipSuccess) e = e2;
-    }
-    if (e != hipSuccess) return e;
-  }
-  out = &sd;
-  return hipSuccess;
-}
-
-// The matrix-core forward-state and reverse passes read only the inputs and
-// the records and write disjoint workspace arrays, so the first runs on the
-// side stream while the second runs on s; s waits for both before the
-// gradient kernel. With few (sequence, head) pairs each pass takes the
-// two-slice form on half of the CUs, and the two chains run side by side.
-hipError_t launch_state_passes_mma(const ChunkBwdArgs &a, hipStream_t s) {
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream *sd = nullptr;
-  hipError_t e = side_stream_of(s, sd);
-  if (e != hipSuccess) return e;
-  if ((e = hipEventRecord(sd->fork, s)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(sd->st, sd->fork, 0)) != hipSuccess) return e;
-  const hipError_t e_states = launch_chunk_bwd_states_mma(a, sd->st);
-  const hipError_t e_join = hipEventRecord(sd->join, sd->st);
-  const hipError_t e_rev = launch_chunk_bwd_dstate_mma(a, s);
-  const hipError_t e_wait = e_join == hipSuccess ? hipStreamWaitEvent(s, sd->join, 0) : e_join;
-  for (const hipError_t x : {e_states, e_join, e_rev, e_wait})
-    if (x != hipSuccess) return x;
-  return hipSuccess;
-}
-
 template <typename T, int DK>
 hipError_t launch_t(const ChunkBwdArgs &a0, hipStream_t s) {
   // The matrix-core state passes read the records the prep writes, and no
@@ -1210,7 +1143,7 @@ hipError_t launch_t(const ChunkBwdArgs &a0, hipStream_t s) {
   if (e != hipSuccess) return e;
   const dim3 sg((unsigned)(a.dv / 16), (unsigned)a.Hv, (unsigned)N);
   if (ds_mma) {
-    e = launch_state_passes_mma(a, s);
+    e = launch_chunk_bwd_state_passes_mma(a, s);
   } else {
     hipLaunchKernelGGL((bwd_states_kernel<T, DK>), sg, dim3(kSer), 0, s, a);
     e = hipGetLastError();

@@ -1,5 +1,10 @@
-// Reverse state pass of the chunk-rule backward on the 16-bit matrix cores,
-// for BF16 or FP16 activations with dk 64 or 128: per (sequence, value head, 16 value
+// The two serial state passes of the chunk-rule backward on the 16-bit
+// matrix cores, for BF16 or FP16 activations with dk 64 or 128, run by one
+// launch (bwd_state_passes_kernel at the end of this file): its first
+// workgroups run the forward-state pass, the rest the reverse pass, each in
+// a one-slice or a multi-slice form.
+//
+// Reverse pass: per (sequence, value head, 16 value
 // rows), serial over the chunks from the last to the first, the gradient dS
 // of the state leaving each chunk is carried in FP32 MFMA accumulators and
 // each chunk gives (unit q, k rows q^, k^; the algebra is written out at the
@@ -30,12 +35,19 @@
 //              two-slot LDS stage, so that the chain issues only dS_C's;
 //   waves 2-7  copies (global_load_lds) of the k and q tiles, the dO slice
 //              and the record of the next chunk into a two-slot LDS ring.
+#include <atomic>
+#include <type_traits>
+
 #include "chunk_bwd_common.h"
 #include "gdn_internal.h"
 #include "mfma_tiles.h"
 
 namespace gdn {
 namespace {
+
+// LDS of the state passes: one dynamic allocation of the launch's size, read
+// by whichever pass a workgroup runs (each body views it as its own layout)
+extern __shared__ __attribute__((aligned(16))) unsigned char g_pass_lds[];
 
 constexpr int kThr = 512;
 constexpr int BT = 64;
@@ -102,25 +114,25 @@ __device__ __forceinline__ void for_steps2(int last, F &&body) {
 }
 
 template <typename T, int DK>
-__global__ __launch_bounds__(kThr) void bwd_dstate_mma_kernel(ChunkBwdArgs p) {
+__device__ __forceinline__ void dstate_pass(const ChunkBwdArgs &p, int64_t bid) {
   using SM = DsLds<T, DK>;
+  SM &sm = *reinterpret_cast<SM *>(g_pass_lds);
   using f8 = typename M2<T>::f8;
   using v4 = typename M2<T>::v4;
   constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB;
   constexpr int NI = SM::TILE / 1024;           // 1 KB copies per q/k tile
   constexpr int NR = (int)(kDsRec / 1024);      // 1 KB copies per record
   static_assert(NI % 2 == 0 && NR % 2 == 0 && NI / 2 <= 31 && NR / 2 + 1 <= 31, "copy split");
-  __shared__ SM sm;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   // slices of one head (which read the same tiles and records) on one XCD
-  const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
-  int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t ntile = p.dv / DVT, nwg = ntile * p.Hv * p.n_seqs;
+  int64_t lid = bid;
   if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
   const int64_t j0 = (lid % ntile) * DVT;
-  const int64_t h = (lid / ntile) % gridDim.y;
-  const int64_t n = lid / (ntile * gridDim.y);
+  const int64_t h = (lid / ntile) % p.Hv;
+  const int64_t n = lid / (ntile * p.Hv);
   const int64_t hk = h / (p.Hv / p.Hqk);
   int64_t brow, bos, L, gc0;
   if (p.cu_seqlens) {
@@ -506,24 +518,24 @@ __device__ __forceinline__ void for_steps3(int last, F &&body) {
 }
 
 template <typename T, int DK>
-__global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
+__device__ __forceinline__ void states_pass(const ChunkBwdArgs &p, int64_t bid) {
   using SM = StLds<T, DK>;
+  SM &sm = *reinterpret_cast<SM *>(g_pass_lds);
   using f8 = typename M2<T>::f8;
   using v4 = typename M2<T>::v4;
   constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB;
   constexpr int NI = SM::TILE / 1024;        // 1 KB copies per k tile
   constexpr int NR = (int)(kBrMtH / 1024);   // 1 KB copies per record part
   static_assert(NI % 4 == 0 && NR % 2 == 0, "copy split");
-  __shared__ SM sm;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
-  int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t ntile = p.dv / DVT, nwg = ntile * p.Hv * p.n_seqs;
+  int64_t lid = bid;
   if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
   const int64_t j0 = (lid % ntile) * DVT;
-  const int64_t h = (lid / ntile) % gridDim.y;
-  const int64_t n = lid / (ntile * gridDim.y);
+  const int64_t h = (lid / ntile) % p.Hv;
+  const int64_t n = lid / (ntile * p.Hv);
   const int64_t hk = h / (p.Hv / p.Hqk);
   int64_t brow, bos, L, gc0;
   if (p.cu_seqlens) {
@@ -774,14 +786,14 @@ __global__ __launch_bounds__(kThr) void bwd_states_mma_kernel(ChunkBwdArgs p) {
 // pairs: one workgroup = (sequence, value head, NS * 16 value rows). One
 // copy of the k tile and of the record's [0, kBrMtH) part serves NS chains;
 // waves 0 .. NS - 1 each carry one 16-row slice through the chain of
-// bwd_states_mma_kernel (the same products in the same order) and store its
+// the one-slice pass, states_pass (the same products in the same order), and store its
 // S0, R and Delta themselves; the four waves after them copy the halves of
 // the k tile, the record part and the [64][16 NS] v tile of the next chunk
 // into two-slot rings (one barrier per step; a chain step is longer than the
 // copies' latency, so one step of look-ahead suffices, and the rings stay
-// small enough for LDS offsets without extra address registers). NS = 8 at
-// dk 64 and 4 at dk 128: eight dk-128 chains need more registers than twelve
-// waves leave.
+// small enough for LDS offsets without extra address registers). NS is 2
+// or 4; waves past NS + 4 (the launch's workgroups are sized for the reverse
+// pass) only take part in the barriers.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int NS>
 struct StMLds {
@@ -794,8 +806,9 @@ struct StMLds {
 };
 
 template <typename T, int DK, int NS>
-__global__ __launch_bounds__((NS + 4) * 64) void bwd_states_multi_kernel(ChunkBwdArgs p) {
+__device__ __forceinline__ void states_multi_pass(const ChunkBwdArgs &p, int64_t bid) {
   using SM = StMLds<T, DK, NS>;
+  SM &sm = *reinterpret_cast<SM *>(g_pass_lds);
   using f8 = typename M2<T>::f8;
   using v4 = typename M2<T>::v4;
   constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB, VB = SM::VB;
@@ -804,16 +817,15 @@ __global__ __launch_bounds__((NS + 4) * 64) void bwd_states_multi_kernel(ChunkBw
   constexpr int NV = BT * VB / 1024;         // 1 KB copies per v tile
   constexpr int LV = VB / 16;                // lanes per v row in a copy
   static_assert(NI % 2 == 0 && NI / 2 <= 16 && NR <= 16 && NV <= 16, "copies per loader wave");
-  __shared__ SM sm;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
-  int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t ntile = p.dv / (NS * DVT), nwg = ntile * p.Hv * p.n_seqs;
+  int64_t lid = bid;
   if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
   const int64_t jg = (lid % ntile) * (NS * DVT);
-  const int64_t h = (lid / ntile) % gridDim.y;
-  const int64_t n = lid / (ntile * gridDim.y);
+  const int64_t h = (lid / ntile) % p.Hv;
+  const int64_t n = lid / (ntile * p.Hv);
   const int64_t hk = h / (p.Hv / p.Hqk);
   int64_t brow, bos, L, gc0;
   if (p.cu_seqlens) {
@@ -834,6 +846,12 @@ __global__ __launch_bounds__((NS + 4) * 64) void bwd_states_multi_kernel(ChunkBw
   };
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
+  if (wave >= NS + 4) {
+    // waves beyond this pass's own (the launch's block also serves the
+    // reverse pass): they only take part in the barriers
+    for_steps2(Nc - 1, [&](int, auto) { lds_barrier(); });
+    return;
+  }
   if (wave < NS) {
     // ------------------------------------------------ the chain of one slice
     const int64_t j0 = jg + DVT * wave;
@@ -1026,19 +1044,12 @@ __global__ __launch_bounds__((NS + 4) * 64) void bwd_states_multi_kernel(ChunkBw
   }
 }
 
-template <typename T, int DK, int NS>
-hipError_t launch_stm(const ChunkBwdArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)(a.dv / (NS * DVT)), (unsigned)a.Hv, (unsigned)a.n_seqs);
-  hipLaunchKernelGGL((bwd_states_multi_kernel<T, DK, NS>), grid, dim3((NS + 4) * 64), 0, s, a);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // Multi-slice reverse pass, for launches with many (sequence, head) pairs and
 // for running beside the forward-state pass: one workgroup = (sequence, value
 // head, NS * 16 value rows). One copy of the k and q tiles and of the
 // record's reverse part serves NS slices. Waves 0 .. NS - 1 carry the chain
-// of bwd_dstate_mma_kernel for one slice each (the same products in the same
+// of the one-slice pass, dstate_pass, for one slice each (the same products in the same
 // order), waves NS .. 2 NS - 1 are their helpers (G = P'^T dO, the q term,
 // the dR' and dv stores); the last four waves copy the k tile, the q tile and
 // the halves of the record part and of the [64][16 NS] dO tile of the next
@@ -1062,8 +1073,9 @@ struct DsMLds {
 };
 
 template <typename T, int DK, int NS>
-__global__ __launch_bounds__((2 * NS + 4) * 64) void bwd_dstate_multi_kernel(ChunkBwdArgs p) {
+__device__ __forceinline__ void dstate_multi_pass(const ChunkBwdArgs &p, int64_t bid) {
   using SM = DsMLds<T, DK, NS>;
+  SM &sm = *reinterpret_cast<SM *>(g_pass_lds);
   using f8 = typename M2<T>::f8;
   using v4 = typename M2<T>::v4;
   constexpr int KT = DK / 32, NT = DK / 16, RB = SM::RB, VB = SM::VB;
@@ -1073,16 +1085,15 @@ __global__ __launch_bounds__((2 * NS + 4) * 64) void bwd_dstate_multi_kernel(Chu
   constexpr int LV = VB / 16;               // lanes per dO row in a copy
   static_assert(NI <= 31 && NR % 2 == 0 && NO % 2 == 0 && NR / 2 + NO / 2 <= 31, "copies per loader wave");
   static_assert(sizeof(SM) <= 160 * 1024, "LDS");
-  __shared__ SM sm;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t ntile = gridDim.x, nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
-  int64_t lid = blockIdx.x + ntile * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t ntile = p.dv / (NS * DVT), nwg = ntile * p.Hv * p.n_seqs;
+  int64_t lid = bid;
   if (nwg % 8 == 0) lid = (lid % 8) * (nwg / 8) + lid / 8;
   const int64_t jg = (lid % ntile) * (NS * DVT);
-  const int64_t h = (lid / ntile) % gridDim.y;
-  const int64_t n = lid / (ntile * gridDim.y);
+  const int64_t h = (lid / ntile) % p.Hv;
+  const int64_t n = lid / (ntile * p.Hv);
   const int64_t hk = h / (p.Hv / p.Hqk);
   int64_t brow, bos, L, gc0;
   if (p.cu_seqlens) {
@@ -1431,28 +1442,72 @@ __global__ __launch_bounds__((2 * NS + 4) * 64) void bwd_dstate_multi_kernel(Chu
   }
 }
 
-template <typename T, int DK, int NS>
-hipError_t launch_dsm(const ChunkBwdArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)(a.dv / (NS * DVT)), (unsigned)a.Hv, (unsigned)a.n_seqs);
-  hipLaunchKernelGGL((bwd_dstate_multi_kernel<T, DK, NS>), grid, dim3((2 * NS + 4) * 64), 0, s, a);
-  return hipGetLastError();
-}
-
 // A multi-slice pass when its launch has at least this many workgroups (half
 // the CUs), else the one-slice kernel.
 constexpr int64_t kMultiMinWorkgroups = 128;
 
-template <typename T, int DK>
-hipError_t launch_st(const ChunkBwdArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)(a.dv / DVT), (unsigned)a.Hv, (unsigned)a.n_seqs);
-  hipLaunchKernelGGL((bwd_states_mma_kernel<T, DK>), grid, dim3(kThr), 0, s, a);
-  return hipGetLastError();
+// One launch runs both passes: blocks [0, nst) the forward-state pass, the
+// rest the reverse pass. The two read only the inputs and the records and
+// write disjoint workspace arrays, so they run side by side; with few
+// (sequence, head) pairs each takes half of the CUs. NSS / NSR: slices per
+// workgroup of each pass (1 = the one-slice kernel's body).
+template <int NS> constexpr int states_waves() { return NS == 1 ? kThr / 64 : NS + 4; }
+template <int NS> constexpr int reverse_waves() { return NS == 1 ? kThr / 64 : 2 * NS + 4; }
+template <int NSS, int NSR> constexpr int pair_waves() {
+  return states_waves<NSS>() > reverse_waves<NSR>() ? states_waves<NSS>() : reverse_waves<NSR>();
+}
+template <typename T, int DK, int NS> struct StatesLds { using type = StMLds<T, DK, NS>; };
+template <typename T, int DK> struct StatesLds<T, DK, 1> { using type = StLds<T, DK>; };
+template <typename T, int DK, int NS> struct ReverseLds { using type = DsMLds<T, DK, NS>; };
+template <typename T, int DK> struct ReverseLds<T, DK, 1> { using type = DsLds<T, DK>; };
+
+template <typename T, int DK, int NSS, int NSR>
+__global__ __launch_bounds__((pair_waves<NSS, NSR>() * 64)) void bwd_state_passes_kernel(ChunkBwdArgs p, int64_t nst) {
+  // only the forward-state pass may have spare waves (its barrier-only waves)
+  static_assert(reverse_waves<NSR>() == pair_waves<NSS, NSR>(), "reverse pass sets the block size");
+  static_assert(NSS > 1 || states_waves<NSS>() == pair_waves<NSS, NSR>(), "one-slice state pass: no spare waves");
+  // blocks [0, nst) run the forward-state pass, the rest the reverse pass;
+  // nst is a multiple of 8 whenever Hv is, so each pass's workgroup index
+  // keeps its block's XCD (index mod 8 = block mod 8)
+  const int64_t b = blockIdx.x;
+  const bool states = b < nst;
+  const int64_t idx = states ? b : b - nst;
+  if (states) {
+    if constexpr (NSS == 1) states_pass<T, DK>(p, idx);
+    else states_multi_pass<T, DK, NSS>(p, idx);
+  } else {
+    if constexpr (NSR == 1) dstate_pass<T, DK>(p, idx);
+    else dstate_multi_pass<T, DK, NSR>(p, idx);
+  }
 }
 
-template <typename T, int DK>
-hipError_t launch_ds(const ChunkBwdArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)(a.dv / DVT), (unsigned)a.Hv, (unsigned)a.n_seqs);
-  hipLaunchKernelGGL((bwd_dstate_mma_kernel<T, DK>), grid, dim3(kThr), 0, s, a);
+// A kernel whose dynamic LDS exceeds 64 KB states its size as a function
+// attribute (no allocation), once per kernel instance and device.
+constexpr int kMaxDevices = 64;
+template <typename K>
+hipError_t lds_limit(K kernel, size_t bytes) {
+  static std::atomic<bool> set[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (set[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)bytes);
+  if (e == hipSuccess) set[dev].store(true, std::memory_order_release);
+  return e;
+}
+
+template <typename T, int DK, int NSS, int NSR>
+hipError_t launch_pair(const ChunkBwdArgs &a, hipStream_t s) {
+  const int64_t pairs = a.n_seqs * a.Hv;
+  const int64_t nst = pairs * (a.dv / (NSS * DVT)), nrv = pairs * (a.dv / (NSR * DVT));
+  constexpr size_t bs = sizeof(typename StatesLds<T, DK, NSS>::type), br = sizeof(typename ReverseLds<T, DK, NSR>::type);
+  constexpr size_t bytes = bs > br ? bs : br;
+  const hipError_t e = lds_limit(bwd_state_passes_kernel<T, DK, NSS, NSR>, bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_state_passes_kernel<T, DK, NSS, NSR>), dim3((unsigned)(nst + nrv)),
+                     dim3(pair_waves<NSS, NSR>() * 64), bytes, s, a, nst);
   return hipGetLastError();
 }
 
@@ -1475,38 +1530,24 @@ bool chunk_bwd_state_mma_supported(const ChunkBwdArgs &a) {
 }
 
 namespace {
+// Slices per workgroup: a multi-slice form when its launch has at least
+// kMultiMinWorkgroups workgroups (with W(n) = pairs * dv / (16 n)): the
+// forward-state pass takes 4 or 2, the reverse pass 2. Every pair runs in
+// eight-wave workgroups, which leave each wave 256 VGPRs; twelve-wave pairs
+// (eight state chains or four reverse chains at dk 64) would leave 170.
 template <typename T, int DK>
-hipError_t launch_dstate(const ChunkBwdArgs &a, hipStream_t s) {
+hipError_t launch_passes(const ChunkBwdArgs &a, hipStream_t s) {
   const int64_t pairs = a.n_seqs * a.Hv;
-  // four slices (twelve waves) fit LDS at dk 64 only
-  if constexpr (DK == 64)
-    if (a.dv % (4 * DVT) == 0 && pairs * (a.dv / (4 * DVT)) >= kMultiMinWorkgroups) return launch_dsm<T, DK, 4>(a, s);
-  if (a.dv % (2 * DVT) == 0 && pairs * (a.dv / (2 * DVT)) >= kMultiMinWorkgroups) return launch_dsm<T, DK, 2>(a, s);
-  return launch_ds<T, DK>(a, s);
+  auto fits = [&](int ns) { return a.dv % (ns * DVT) == 0 && pairs * (a.dv / (ns * DVT)) >= kMultiMinWorkgroups; };
+  if (fits(4)) return launch_pair<T, DK, 4, 2>(a, s);
+  if (fits(2)) return launch_pair<T, DK, 2, 2>(a, s);
+  return launch_pair<T, DK, 1, 1>(a, s);
 }
 }  // namespace
 
-hipError_t launch_chunk_bwd_dstate_mma(const ChunkBwdArgs &a, hipStream_t s) {
-  if (a.act == kF16) return a.dk == 64 ? launch_dstate<f16, 64>(a, s) : launch_dstate<f16, 128>(a, s);
-  return a.dk == 64 ? launch_dstate<bf16, 64>(a, s) : launch_dstate<bf16, 128>(a, s);
-}
-
-namespace {
-template <typename T, int DK>
-hipError_t launch_states(const ChunkBwdArgs &a, hipStream_t s) {
-  const int64_t pairs = a.n_seqs * a.Hv;
-  // eight chains fit twelve waves' registers at dk 64 only
-  if constexpr (DK == 64)
-    if (a.dv % (8 * DVT) == 0 && pairs * (a.dv / (8 * DVT)) >= kMultiMinWorkgroups) return launch_stm<T, DK, 8>(a, s);
-  if (a.dv % (4 * DVT) == 0 && pairs * (a.dv / (4 * DVT)) >= kMultiMinWorkgroups) return launch_stm<T, DK, 4>(a, s);
-  if (a.dv % (2 * DVT) == 0 && pairs * (a.dv / (2 * DVT)) >= kMultiMinWorkgroups) return launch_stm<T, DK, 2>(a, s);
-  return launch_st<T, DK>(a, s);
-}
-}  // namespace
-
-hipError_t launch_chunk_bwd_states_mma(const ChunkBwdArgs &a, hipStream_t s) {
-  if (a.act == kF16) return a.dk == 64 ? launch_states<f16, 64>(a, s) : launch_states<f16, 128>(a, s);
-  return a.dk == 64 ? launch_states<bf16, 64>(a, s) : launch_states<bf16, 128>(a, s);
+hipError_t launch_chunk_bwd_state_passes_mma(const ChunkBwdArgs &a, hipStream_t s) {
+  if (a.act == kF16) return a.dk == 64 ? launch_passes<f16, 64>(a, s) : launch_passes<f16, 128>(a, s);
+  return a.dk == 64 ? launch_passes<bf16, 64>(a, s) : launch_passes<bf16, 128>(a, s);
 }
 
 }  // namespace gdn

@@ -260,15 +260,16 @@ hipError_t launch_chunk_split(const ChunkArgs &a, hipStream_t s);
 // Backward of the chunk rule (dk 64, 128 or 256, dv a multiple of 16).
 bool chunk_bwd_supported(int64_t dk, int64_t dv);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t s);
-// Its gradient kernel on the BF16 matrix cores (BF16 activations, dk 64 or
-// 128, dv a multiple of 32, aligned rows); the FP32 kernel serves the rest.
+// Its gradient kernel on the 16-bit matrix cores (BF16 or FP16 activations,
+// dk 64 or 128, dv a multiple of 32, aligned rows); the FP32 kernel serves the
+// rest.
 bool chunk_bwd_grad_mma_supported(const ChunkBwdArgs &a);
 hipError_t launch_chunk_bwd_grad_mma(const ChunkBwdArgs &a, hipStream_t s);
-// Its reverse state pass on the BF16 matrix cores (BF16 activations, dk 64 or
-// 128, 16-byte aligned q, k and d_o rows); needs a.brec written by the prep.
+// Its forward-state and reverse state passes on the 16-bit matrix cores (BF16
+// or FP16 activations, dk 64 or 128, 16-byte aligned q, k, v and d_o rows), in
+// one launch; they need a.brec written by the prep.
 bool chunk_bwd_state_mma_supported(const ChunkBwdArgs &a);
-hipError_t launch_chunk_bwd_dstate_mma(const ChunkBwdArgs &a, hipStream_t s);
-hipError_t launch_chunk_bwd_states_mma(const ChunkBwdArgs &a, hipStream_t s);
+hipError_t launch_chunk_bwd_state_passes_mma(const ChunkBwdArgs &a, hipStream_t s);
 
 // Device address of the static chunk scratch (GDN_NOALLOC_SCRATCH_BYTES) on
 // the current device; looked up once per device.

@@ -63,15 +63,9 @@ KERNELS = {
                                                 "device_common.h", "gdn_internal.h"]),
     "bwd_grad_kernel": ("bwd_grad_kernel", ["chunk_bwd.hip", "chunk_bwd_common.h", "mfma_tiles.h",
                                             "device_common.h", "gdn_internal.h"]),
-    "bwd_states_mma_kernel": ("bwd_states_mma_kernel", ["chunk_bwd_state_mma.hip", "chunk_bwd_common.h",
-                                                        "mfma_tiles.h", "device_common.h", "gdn_internal.h"]),
-    "bwd_dstate_mma_kernel": ("bwd_dstate_mma_kernel", ["chunk_bwd_state_mma.hip", "chunk_bwd_common.h",
-                                                        "mfma_tiles.h", "device_common.h", "gdn_internal.h"]),
     "bwd_grad_mma_kernel": ("bwd_grad_mma_kernel", ["chunk_bwd_mma.hip", "chunk_bwd_common.h", "mfma_tiles.h",
                                                     "device_common.h", "gdn_internal.h"]),
-    "bwd_states_multi_kernel": ("bwd_states_multi_kernel", ["chunk_bwd_state_mma.hip", "chunk_bwd_common.h",
-                                                            "mfma_tiles.h", "device_common.h", "gdn_internal.h"]),
-    "bwd_dstate_multi_kernel": ("bwd_dstate_multi_kernel", ["chunk_bwd_state_mma.hip", "chunk_bwd_common.h",
+    "bwd_state_passes_kernel": ("bwd_state_passes_kernel", ["chunk_bwd_state_mma.hip", "chunk_bwd_common.h",
                                                             "mfma_tiles.h", "device_common.h", "gdn_internal.h"]),
     "chunk_state_quad_kernel": ("chunk_state_quad_kernel", ["chunk_state.hip", "mfma_tiles.h", "device_common.h",
                                                             "gdn_internal.h"]),

@@ -287,11 +287,11 @@ def test_chunk_rule_bwd_multi_slice_states(name, cfg, over):
 
 
 def test_chunk_rule_bwd_back_to_back_on_a_stream():
-    """Two calls in a row on a non-default stream with one workspace: the
-    forward-state pass runs on the library's second stream and is joined back
-    before the gradient kernel, so the second call's prep cannot overwrite
-    records the first call's passes still read. Both results equal the same
-    calls made one at a time on the default stream."""
+    """Two calls in a row on a non-default stream with one workspace (the
+    two-slice state passes, launched together): every kernel of a call is
+    ordered on the caller's stream, so the second call's prep cannot
+    overwrite records the first call's passes still read. Both results equal
+    the same calls made one at a time on the default stream."""
     s = synth.spec(3).replace(T=640, Hqk=16, Hv=32)
     dt = synth.TORCH_DTYPE[s.act]
     ins = []
