@@ -36,7 +36,6 @@
 //   waves 2-7  copies (global_load_lds) of the k and q tiles, the dO slice
 //              and the record of the next chunk into a two-slot LDS ring.
 #include <atomic>
-#include <type_traits>
 
 #include "chunk_bwd_common.h"
 #include "gdn_internal.h"
@@ -1442,8 +1441,8 @@ __device__ __forceinline__ void dstate_multi_pass(const ChunkBwdArgs &p, int64_t
   }
 }
 
-// A multi-slice pass when its launch has at least this many workgroups (half
-// the CUs), else the one-slice kernel.
+// A multi-slice form when its pass has at least this many workgroups (half
+// the CUs), else the one-slice form.
 constexpr int64_t kMultiMinWorkgroups = 128;
 
 // One launch runs both passes: blocks [0, nst) the forward-state pass, the
