@@ -243,14 +243,16 @@ def test_chunk_rule_bwd_slow_decay(act):
     _check(got, ref, TAU[act])
 
 
-# The forward-state pass of the matrix-core path carries 4 (dk 128) or 8
-# (dk 64) value slices per workgroup when the launch has at least 128 such
-# workgroups (packed or batched sequences). These cases reach both forms and
-# compare with the oracle and, bit for bit, with per-sequence calls (which
-# run the one-slice pass).
+# The matrix-core state passes run in one launch, each in a one-slice or a
+# multi-slice form (the forward-state pass 4 or 2 value slices per
+# workgroup, the reverse pass 2) chosen by the workgroup count of each form.
+# These cases reach the multi-slice forms in the packed call and other forms
+# in the per-sequence calls, and compare with the oracle and, bit for bit,
+# across the two.
 MULTI = [
     ("slices4-dk128-fp16-8seq", 4, {"lengths": (1, 63, 64, 65, 130, 2, 3, 100)}),
-    ("slices8-dk64-bf16-8seq", 4, {"act": "bf16", "dk": 64, "lengths": (70, 1, 64, 129, 5, 66, 30, 64)}),
+    ("slices4-dk64-bf16-8seq", 4, {"act": "bf16", "dk": 64, "lengths": (70, 1, 64, 129, 5, 66, 30, 64)}),
+    ("slices4-dk64-fp16-8seq", 4, {"dk": 64, "lengths": (3, 130, 64, 1, 65, 200, 63, 2)}),
     # 16 sequences of 8 value heads: the packed call takes the multi-slice
     # forms of both passes, each per-sequence call (8 pairs) the one-slice ones
     ("multi-vs-one-slice-dk128-bf16-16seq", 4,
