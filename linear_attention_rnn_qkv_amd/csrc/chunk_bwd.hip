@@ -1119,12 +1119,13 @@ template <typename T, int DK>
 hipError_t launch_t(const ChunkBwdArgs &a0, hipStream_t s) {
   // The matrix-core state passes read the records the prep writes, and no
   // (I + A)^-1 or P in FP32; with the matrix-core gradient kernel as well,
-  // nothing reads the unit q, k rows. The prep skips what is not read.
+  // nothing reads the unit q, k rows, and R is recomputed there instead of
+  // stored. The prep and the state passes skip what is not read.
   ChunkBwdArgs a = a0;
   const bool ds_mma = chunk_bwd_state_mma_supported(a), grad_mma = chunk_bwd_grad_mma_supported(a);
   if (!ds_mma) a.brec = nullptr;
   if (ds_mma) a.mm = a.pp = nullptr;
-  if (ds_mma && grad_mma) a.qn = a.kn = nullptr;
+  if (ds_mma && grad_mma) a.qn = a.kn = a.rr = nullptr;
   const int64_t N = a.n_seqs;
   // the matrix-core prep serves the all-matrix-core path (BF16 or FP16, dk
   // 64/128)
@@ -1152,7 +1153,7 @@ hipError_t launch_t(const ChunkBwdArgs &a0, hipStream_t s) {
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  if (chunk_bwd_grad_mma_supported(a)) return launch_chunk_bwd_grad_mma(a, s);
+  if (grad_mma) return launch_chunk_bwd_grad_mma(a, s);
   hipLaunchKernelGGL((bwd_grad_kernel<T, DK>), dim3((unsigned)a.chunk_bound, (unsigned)a.Hqk),
                      dim3(grad_threads<DK>()), 0, s, a);
   return hipGetLastError();

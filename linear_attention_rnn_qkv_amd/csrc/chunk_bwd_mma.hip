@@ -3,8 +3,11 @@
 // L2 fold), dg and dbeta per (chunk, q/k head), the value heads of the GQA
 // group in turn, for BF16 or FP16 activations with dk 64 or 128 and dv a
 // multiple of 32. It computes what the FP32 gradient kernel of chunk_bwd.hip
-// computes, from the same workspace arrays (gamma, inverse norms, R, Delta,
-// M^T dDelta and the states S0, dS_C); the forward and backward algebra is
+// computes, from the same workspace arrays (gamma, inverse norms, Delta,
+// M^T dDelta and the states S0, dS_C) and v in place of the corrected values
+// R = V - e^gamma rk (.) (K S0^T), which dbeta needs only through the row sums
+// sum_i dR' R = sum_i dR' V - e^gamma rk (k . (S0^T dR'^T)), and the row dot
+// k . k3 on the right is formed for dk anyway; the forward and backward algebra is
 // written out at the top of chunk_bwd.hip (gated delta rule of Gated
 // DeltaNet in the chunked form of the flash-linear-attention and Megatron-LM
 // pull requests; first-order autograd as in Megatron Core "GDN Elementwise
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
   const int nslab = (int)(dvn / 32);
 
   // staging of a slab: thread tid holds row tid / 8, value columns
-  // 4 (tid % 8) .. + 3 of d_o, Delta, dR', R, and S4 float4 of S0, dS.
+  // 4 (tid % 8) .. + 3 of d_o, Delta, dR', v, and S4 float4 of S0, dS.
   // Slab `it` of the flattened (value head, slab) order is fetched into
   // registers while slab it - 1 is multiplied (the first slab of a value
   // head while the previous head's dq, dk products run). Loads are never under a
@@ -134,7 +137,8 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
   const int st_t = tid >> 3, st_c = 4 * (tid & 7);
   const int st_tc = st_t < nr ? st_t : nr - 1;
   uint2 so;
-  f32x4 sd4, sr4, sq4, s04[S4], sds4[S4];
+  uint2 sv;
+  f32x4 sd4, sr4, s04[S4], sds4[S4];
   auto fetch = [&](int it) {
     const int64_t h = hk * G + it / nslab, i0 = 32 * (int64_t)(it % nslab);
     so = *reinterpret_cast<const uint2 *>(static_cast<const T *>(p.d_o) + cp.brow * p.sdo_b +
@@ -142,7 +146,8 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
     const int64_t wo = ((gc * p.Hv + h) * BT + st_t) * dvn + i0 + st_c;
     sd4 = *reinterpret_cast<const f32x4 *>(p.del + wo);
     sr4 = *reinterpret_cast<const f32x4 *>(p.drp + wo);
-    sq4 = *reinterpret_cast<const f32x4 *>(p.rr + wo);
+    sv = *reinterpret_cast<const uint2 *>(static_cast<const T *>(p.v) + cp.brow * p.sv_b +
+                                         (cp.t0 + st_tc) * p.sv_t + h * p.sv_h + i0 + st_c);
 #pragma unroll
     for (int m = 0; m < S4; ++m) {
       const int64_t e = ((gc * p.Hv + h) * dvn + i0) * DK + 4 * (tid + kThr * m);
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
     for (int a = 0; a < 2; ++a) c1[a] = c2[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < NJW; ++m) k1[m] = k2[m] = k3[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dbp = 0.f, sdp = 0.f;  // this thread's part of sum_i dR' R (row st_t) and of <S0, dS>
+    float dbp = 0.f, sdp = 0.f;  // this thread's part of sum_i dR' V (row st_t) and of <S0, dS>
 
     for (int sl = 0; sl < nslab; ++sl) {
       __syncthreads();  // the previous slab (or value head) is done with the union
@@ -235,8 +240,9 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
         split4(sr4, hi, lo);
         *reinterpret_cast<v4 *>(&sm.u.s.rh[st_t * SP + st_c]) = hi;
         *reinterpret_cast<v4 *>(&sm.u.s.rl[st_t * SP + st_c]) = lo;
+        const v4 vv = __builtin_bit_cast(v4, sv);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) dbp = fmaf(sr4[q], sq4[q], dbp);
+        for (int q = 0; q < 4; ++q) dbp = fmaf(sr4[q], f(vv[q]), dbp);
 #pragma unroll
         for (int m = 0; m < S4; ++m) {
           const int e = 4 * (tid + kThr * m), i = e / DK, j = e % DK;
@@ -301,14 +307,19 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
         qk[a] = mma<T>(qt, ks, qk[a]);
       }
     }
+    {
+      // (addresses from fresh_tid: computed here, not held across the loop)
+      const int ft = fresh_tid(), fw = ft >> 6, t0 = 16 * (fw & 3) + 4 * ((ft >> 4) & 3);
+      const int s0 = 32 * (fw >> 2) + (ft & 15);
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * tt + 4 * g + i, s = 16 * (2 * jh + a) + c;
-        gg[a][i] *= sm.rk[t] * sm.rk[s];
-        qk[a][i] *= sm.rq[t] * sm.rk[s];
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + i, s = s0 + 16 * a;
+          gg[a][i] *= sm.rk[t] * sm.rk[s];
+          qk[a][i] *= sm.rq[t] * sm.rk[s];
+        }
+    }
 
     // elementwise on the c tiles; row sums of z and of dA o E o gg, column
     // sums of z
@@ -469,7 +480,7 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
       if (t < nr) {
         const int64_t o = (cp.brow * p.T + cp.t0 + t) * p.Hv + h;
         p.dg[o] = dgam;
-        p.dbeta[o] = sm.db[t] + sm.roww[0][t] + sm.roww[1][t];
+        p.dbeta[o] = (sm.db[t] - sm.eg[t] * bt) + sm.roww[0][t] + sm.roww[1][t];
       }
     }
     __syncthreads();
@@ -576,7 +587,8 @@ bool chunk_bwd_grad_mma_supported(const ChunkBwdArgs &a) {
   const int64_t es = a.grad_dtype == kF32 ? 4 : 2;
   const uint64_t ga = (uint64_t)(uintptr_t)a.dqq | (uint64_t)(uintptr_t)a.dkk | (uint64_t)(a.sdq_b * es) |
                       (uint64_t)(a.sdq_t * es) | (uint64_t)(a.sdk_b * es) | (uint64_t)(a.sdk_t * es);
-  return align_of_host(qa) >= 16 && align_of_host(ka) >= 16 && align_of_host(oa) >= 8 &&
+  const uint64_t va = (uint64_t)(uintptr_t)a.v | (uint64_t)(a.sv_b * 2) | (uint64_t)(a.sv_t * 2) | (uint64_t)(a.sv_h * 2);
+  return align_of_host(qa) >= 16 && align_of_host(ka) >= 16 && align_of_host(oa) >= 8 && align_of_host(va) >= 8 &&
          align_of_host(ga) >= (int)(4 * es > 16 ? 16 : 4 * es);
 }
 

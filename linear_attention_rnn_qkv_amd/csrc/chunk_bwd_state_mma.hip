@@ -701,6 +701,7 @@ __device__ __forceinline__ void states_pass(const ChunkBwdArgs &p, int64_t bid) 
       const int t = lane, mt = t >> 4, gg = (t >> 2) & 3, i = t & 3;
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
+        if (a == 0 && p.rr == nullptr) continue;  // R not kept (the gradient kernel recomputes it)
         float x[16];
 #pragma unroll
         for (int cc = 0; cc < 16; ++cc) x[cc] = stg[((4 * a + mt) * 64 + 16 * gg + cc) * 4 + i];
@@ -944,8 +945,10 @@ __device__ __forceinline__ void states_multi_pass(const ChunkBwdArgs &p, int64_t
 #pragma unroll
         for (int i = 0; i < 4; ++i) vv[i] = f(Bv[mt >> 1][4 * (mt & 1) + i]);
         const f32x4 r = vv - er * U[mt];
+        if (p.rr != nullptr) {  // R kept only for the FP32 gradient kernel
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rrow[(16 * mt + i) * dvs] = r[i];
+          for (int i = 0; i < 4; ++i) rrow[(16 * mt + i) * dvs] = r[i];
+        }
         X[mt] = bt * r;
       }
       // Delta = M X

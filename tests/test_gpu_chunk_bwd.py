@@ -121,7 +121,7 @@ def test_chunk_rule_bwd_strided_views_equal_contiguous():
 
 # 16-bit workloads (BF16 and FP16) run matrix-core kernels where their
 # operand rows allow: the two state passes need 16-byte q, k, v and d_o rows,
-# the gradient kernel dv a multiple of 32 and 8-byte d_o rows. These cases
+# the gradient kernel dv a multiple of 32 and 8-byte d_o and v rows. These cases
 # pick each mix, in both 16-bit types.
 MIXES = [
     # name, dv, d_o row pitch (elements past dv)
