@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
   // 4 (tid % 8) .. + 3 of d_o, Delta, dR', v, and S4 float4 of S0, dS.
   // Slab `it` of the flattened (value head, slab) order is fetched into
   // registers while slab it - 1 is multiplied (the first slab of a value
-  // head while the previous head's dq, dk products run). Loads are never under a
+  // head during the previous head's tail). Loads are never under a
   // branch (rows past the chunk's end read its last row and are zeroed when
   // stored), so that they stay in flight.
   const int st_t = tid >> 3, st_c = 4 * (tid & 7);
@@ -291,6 +291,9 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
       }
     }
     __syncthreads();  // the slab tiles are dead: the union now holds Z1, Z2, z
+    // the next value head's first slab: its loads overlap this head's tail
+    // (which holds no spilled values whose reloads would wait for them)
+    if (vh + 1 < G) fetch((int)(vh + 1) * nslab);
 
     // gg = K^ K^T and qk = Q^ K^T on tiles (tt, 2 jh + a): lane holds rows
     // t = 16 tt + 4 g + i, column s = 16 (2 jh + a) + c
@@ -484,10 +487,6 @@ __global__ __launch_bounds__(kThr) void bwd_grad_mma_kernel(ChunkBwdArgs p) {
       }
     }
     __syncthreads();
-    // the next value head's first slab: its loads overlap the products below
-    // (issued only now, so that no load is in flight during the tail above,
-    // whose register reloads would wait for it)
-    if (vh + 1 < G) fetch((int)(vh + 1) * nslab);
     // dq^T += K^T W1^T, dk^T += K^T W2^T + Q^T W3^T (contraction over s)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
