@@ -55,6 +55,7 @@ CASES = [
     ("bf16-dk64-dv256-T200", 0, {"act": "bf16", "T": 200, "Hqk": 1, "Hv": 1, "dv": 256}, True, True),
     ("fp32-no-l2-T90", 0, {"T": 90, "Hqk": 1, "Hv": 2, "dv": 64}, False, False),
     ("bf16-group4-T129", 2, {"T": 129, "Hqk": 2, "Hv": 8, "dv": 64}, True, True),
+    ("fp16-group3-T150", 4, {"T": 150, "lengths": None, "Hqk": 2, "Hv": 6, "dv": 64}, True, True),
     ("bf16-dk256-dv512-T130", 1, {"T": 130, "B": 1, "Hqk": 1, "Hv": 1}, True, True),
     ("fp32-dk256-gqa-T70", 0, {"T": 70, "dk": 256, "dv": 64, "Hqk": 1, "Hv": 2}, True, True),
 ]

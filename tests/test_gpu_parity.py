@@ -31,6 +31,9 @@ SMALL = [
     ("gqa-bf16-T300-fp32gate", 2, {"T": 300}),
     ("long-bf16-T200", 3, {"T": 200}),
     ("varlen-fp16-8seq", 4, {"lengths": (1, 63, 64, 65, 130, 2, 3, 200)}),
+    # an odd GQA group (3 value heads per q/k head): the prep kernels then
+    # take one value head per workgroup
+    ("gqa3-bf16-T200", 3, {"T": 200, "Hqk": 2, "Hv": 6}),
 ]
 IDS = [c[0] for c in SMALL]
 # The recurrence runs as two kernels (chunk prep + chunk state) when given a
