@@ -387,7 +387,35 @@ def backward_leg(gdn, synth, torch, s, d, o, dims, steps, warmup, rule=None, lay
         e1.record(stream)
         torch.cuda.synchronize()
         out["layer_core_bwd_ms"] = e0.elapsed_time(e1) / steps
-        del lws
+
+        # a training step of the core that keeps the forward's activations:
+        # gdn_layer_fwd into the backward's workspace, then gdn_layer_bwd_saved
+        # (no forward recompute); and that backward alone
+        lo = torch.empty((s.B, s.T, s.Hv, s.dv), dtype=dout.dtype, device="cuda")
+        fargs = (d["x_q"], d["x_k"], d["x_v"], d["conv_w"], None, d["a"], d["b"], d["A_log"], d["dt_bias"],
+                 d["gate"], d["norm_w"], d["cu_seqlens"], dims, scale)
+
+        def layer_f():
+            gdn.gdn_layer_fwd(*fargs, workspace=lws, out=lo)
+
+        def layer_bs():
+            gdn.gdn_layer_bwd_saved(*fargs, dout, lws)
+
+        for name, fns in (("layer_core_fwd_bwd_saved_ms", (layer_f, layer_bs)), ("layer_core_bwd_saved_ms",
+                                                                                 (layer_bs,))):
+            layer_f()
+            for _ in range(warmup):
+                for fn in fns:
+                    fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(steps):
+                for fn in fns:
+                    fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out[name] = e0.elapsed_time(e1) / steps
+        del lws, lo
     return out
 
 

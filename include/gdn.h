@@ -19,6 +19,8 @@
  *                       prologue and of the chunked gated delta rule
  *   gdn_layer_bwd       the gradients of gdn_layer_fwd: the forward stages
  *                       recomputed, then the three backward stages
+ *   gdn_layer_bwd_saved the same gradients from the activations a
+ *                       gdn_layer_fwd call left in the workspace
  *
  * Sources (web pages):
  *   [P1] Megatron-LM pull request "perf(gated_delta_net): fold q/k L2-norm
@@ -498,6 +500,38 @@ gdn_status gdn_layer_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k,
                          const gdn_tensor *d_gate, const gdn_tensor *d_norm_w,
                          void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/*
+ * gdn_layer_bwd_saved - gdn_layer_bwd for callers that keep the forward's
+ * activations (the same gradients, [P2] Execution and numerical behavior):
+ * the prologue and the chunk rule are not recomputed. `workspace` must hold
+ * what a gdn_layer_fwd call with the same inputs and arguments wrote into
+ * its first gdn_layer_workspace_bytes(...) bytes (qkv, g, beta and o sit at
+ * the same offsets in both layouts), and nothing may have written to it
+ * since; it is gdn_layer_bwd_workspace_bytes(...) bytes, so the forward call
+ * is given the same buffer. The outputs are then bit for bit those of
+ * gdn_layer_bwd (the kernels are deterministic); with other contents they are
+ * the gradients at whatever the workspace holds, and no error is reported.
+ * Arguments, validation and errors otherwise as gdn_layer_bwd.
+ */
+gdn_status gdn_layer_bwd_saved(const gdn_tensor *x_q, const gdn_tensor *x_k,
+                               const gdn_tensor *x_v, const gdn_tensor *conv_w,
+                               const gdn_tensor *conv_b, const gdn_tensor *a,
+                               const gdn_tensor *b, const gdn_tensor *A_log,
+                               const gdn_tensor *dt_bias, const gdn_tensor *gate,
+                               const gdn_tensor *norm_w,
+                               const gdn_tensor *cu_seqlens, const gdn_dims *dims,
+                               float scale, int32_t use_qk_l2norm_in_kernel,
+                               float l2_eps, float rms_eps,
+                               const gdn_tensor *d_out, const gdn_tensor *dx_q,
+                               const gdn_tensor *dx_k, const gdn_tensor *dx_v,
+                               const gdn_tensor *d_conv_w,
+                               const gdn_tensor *d_conv_b, const gdn_tensor *d_a,
+                               const gdn_tensor *d_b, const gdn_tensor *d_A_log,
+                               const gdn_tensor *d_dt_bias,
+                               const gdn_tensor *d_gate, const gdn_tensor *d_norm_w,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 /* Bytes of workspace gdn_layer_bwd needs (n_seqs as in
  * gdn_layer_workspace_bytes): the forward stage outputs and the chunk

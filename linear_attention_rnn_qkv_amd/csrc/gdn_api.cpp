@@ -993,6 +993,101 @@ LayerBwdWs layer_bwd_layout(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims
   return w;
 }
 
+// The layer backward; with recompute false the workspace already holds the
+// forward stage outputs (qkv, g, beta, o) that gdn_layer_fwd wrote at the
+// same offsets, and the prologue and chunk rule are planned (validated) but
+// not launched.
+gdn_status layer_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
+                     const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *a, const gdn_tensor *b,
+                     const gdn_tensor *A_log, const gdn_tensor *dt_bias, const gdn_tensor *gate,
+                     const gdn_tensor *norm_w, const gdn_tensor *cu_seqlens, const gdn_dims *dims, float scale,
+                     int32_t use_qk_l2norm_in_kernel, float l2_eps, float rms_eps, const gdn_tensor *d_out,
+                     const gdn_tensor *dx_q, const gdn_tensor *dx_k, const gdn_tensor *dx_v,
+                     const gdn_tensor *d_conv_w, const gdn_tensor *d_conv_b, const gdn_tensor *d_a,
+                     const gdn_tensor *d_b, const gdn_tensor *d_A_log, const gdn_tensor *d_dt_bias,
+                     const gdn_tensor *d_gate, const gdn_tensor *d_norm_w, void *workspace, size_t workspace_bytes,
+                     void *stream, bool recompute) {
+  g_error.clear();
+  TRY(check_dims(dims));
+  if (!x_q || x_q->ndim != 3) return fail(GDN_ERR_INVALID_VALUE, "x_q: expected [B, T, Hqk*dk]");
+  const int64_t B = x_q->shape[0], T = x_q->shape[1];
+  const int32_t act = x_q->dtype;
+  if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "x_q: dtype must be F32, BF16 or F16");
+  if (B * T == 0) return fail(GDN_ERR_INVALID_VALUE, "empty input (B*T == 0)");
+  int64_t n_seqs = 0;
+  if (cu_seqlens) {
+    if (cu_seqlens->ndim != 1 || cu_seqlens->shape[0] < 1)
+      return fail(GDN_ERR_INVALID_VALUE, "cu_seqlens: expected [N+1]");
+    n_seqs = cu_seqlens->shape[0] - 1;
+  }
+  if (!gdn::chunk_bwd_supported(dims->dk, dims->dv))
+    return fail(GDN_ERR_NOT_SUPPORTED, "layer backward: dk=%lld dv=%lld is not instantiated", (long long)dims->dk,
+                (long long)dims->dv);
+  const LayerBwdWs L = layer_bwd_layout(B, T, n_seqs, dims, act);
+  if (!workspace) return fail(GDN_ERR_INVALID_VALUE, "workspace is NULL");
+  if (workspace_bytes < L.total)
+    return fail(GDN_ERR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+  if ((uintptr_t)workspace % 256) return fail(GDN_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+
+  const int64_t Hqk = dims->Hqk, dk = dims->dk, Hv = dims->Hv, dv = dims->dv;
+  const int64_t nq = Hqk * dk, C = 2 * nq + Hv * dv, es = elem_size(act);
+  char *w = static_cast<char *>(workspace);
+  gdn_tensor qkv = {w + L.qkv, act, 3, {B, T, C}, {T * C, C, 1}};
+  gdn_tensor gt = {w + L.g, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
+  gdn_tensor bt = {w + L.beta, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
+  gdn_tensor ot = {w + L.o, act, 4, {B, T, Hv, dv}, {T * Hv * dv, Hv * dv, dv, 1}};
+  gdn_tensor dot = {w + L.d_o, act, 4, {B, T, Hv, dv}, {T * Hv * dv, Hv * dv, dv, 1}};
+  gdn_tensor dqkv = {w + L.dqkv, GDN_F32, 3, {B, T, C}, {T * C, C, 1}};
+  gdn_tensor dgt = {w + L.dg, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
+  gdn_tensor dbt = {w + L.dbeta, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
+  char *qb = w + L.qkv, *db = w + L.dqkv;
+  gdn_tensor qv = {qb, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor kv = {qb + nq * es, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor vv = {qb + 2 * nq * es, act, 4, {B, T, Hv, dv}, {T * C, C, dv, 1}};
+  gdn_tensor dqv = {db, GDN_F32, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor dkv = {db + nq * 4, GDN_F32, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor dvv = {db + 2 * nq * 4, GDN_F32, 4, {B, T, Hv, dv}, {T * C, C, dv, 1}};
+  gdn_tensor wsd = {workspace, GDN_BF16, 1, {(int64_t)(L.total / 2)}, {1}};
+
+  // Plan every stage before launching anything.
+  gdn::PrologueArgs PP;
+  gdn::ChunkArgs PC;
+  gdn::NormBwdArgs PN;
+  gdn::ChunkBwdArgs PB;
+  gdn::PrologueBwdArgs PR;
+  TRY(plan_prologue(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, dims, 0, l2_eps, &qkv, &gt,
+                    &bt, &PP));
+  TRY(plan_chunk(&qv, &kv, &vv, &gt, &bt, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, nullptr, &ot,
+                 nullptr, &PC));
+  TRY(attach_chunk_ws(&PC, L.cfw_n ? w + L.cfw : nullptr, L.cfw_n));
+  TRY(plan_norm_bwd(&ot, gate, norm_w, rms_eps, d_out, &dot, d_gate, d_norm_w, w + L.nbw, L.nbw_n, &PN));
+  TRY(plan_chunk_bwd(&qv, &kv, &vv, &gt, &bt, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, nullptr, &dot,
+                     nullptr, &dqv, &dkv, &dvv, &dgt, &dbt, nullptr, w + L.cbw, L.cbw_n, &PB, true));
+  TRY(plan_prologue_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, dims, &dqkv, &dgt, &dbt,
+                        dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b, d_A_log, d_dt_bias, w + L.pbw, L.pbw_n,
+                        &PR));
+  const gdn_tensor *ins[] = {x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens, d_out};
+  const gdn_tensor *outs[] = {dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b, d_A_log, d_dt_bias, d_gate, d_norm_w};
+  for (auto *t : ins)
+    if (overlaps(&wsd, t)) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps an input");
+  for (size_t i = 0; i < sizeof outs / sizeof outs[0]; ++i) {
+    if (overlaps(&wsd, outs[i])) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps an output");
+    for (auto *t : ins)
+      if (overlaps(outs[i], t)) return fail(GDN_ERR_INVALID_VALUE, "an output overlaps an input");
+    for (size_t j = i + 1; j < sizeof outs / sizeof outs[0]; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(GDN_ERR_INVALID_VALUE, "two outputs overlap");
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  if (recompute) {
+    TRY(launched(gdn::launch_prologue(PP, s), "prologue"));
+    TRY(launched(gdn::launch_chunk_rule(PC, s), "chunk rule"));
+  }
+  TRY(launched(gdn::launch_gated_norm_bwd(PN, s), "gated norm backward"));
+  TRY(launched(gdn::launch_chunk_bwd(PB, s), "chunk rule backward"));
+  return launched(gdn::launch_prologue_bwd(PR, s), "prologue backward");
+}
+
 }  // namespace
 
 extern "C" {
@@ -1163,83 +1258,25 @@ gdn_status gdn_layer_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn
                          const gdn_tensor *d_a, const gdn_tensor *d_b, const gdn_tensor *d_A_log,
                          const gdn_tensor *d_dt_bias, const gdn_tensor *d_gate, const gdn_tensor *d_norm_w,
                          void *workspace, size_t workspace_bytes, void *stream) {
-  g_error.clear();
-  TRY(check_dims(dims));
-  if (!x_q || x_q->ndim != 3) return fail(GDN_ERR_INVALID_VALUE, "x_q: expected [B, T, Hqk*dk]");
-  const int64_t B = x_q->shape[0], T = x_q->shape[1];
-  const int32_t act = x_q->dtype;
-  if (!is_act(act)) return fail(GDN_ERR_INVALID_VALUE, "x_q: dtype must be F32, BF16 or F16");
-  if (B * T == 0) return fail(GDN_ERR_INVALID_VALUE, "empty input (B*T == 0)");
-  int64_t n_seqs = 0;
-  if (cu_seqlens) {
-    if (cu_seqlens->ndim != 1 || cu_seqlens->shape[0] < 1)
-      return fail(GDN_ERR_INVALID_VALUE, "cu_seqlens: expected [N+1]");
-    n_seqs = cu_seqlens->shape[0] - 1;
-  }
-  if (!gdn::chunk_bwd_supported(dims->dk, dims->dv))
-    return fail(GDN_ERR_NOT_SUPPORTED, "layer backward: dk=%lld dv=%lld is not instantiated", (long long)dims->dk,
-                (long long)dims->dv);
-  const LayerBwdWs L = layer_bwd_layout(B, T, n_seqs, dims, act);
-  if (!workspace) return fail(GDN_ERR_INVALID_VALUE, "workspace is NULL");
-  if (workspace_bytes < L.total)
-    return fail(GDN_ERR_INVALID_VALUE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
-  if ((uintptr_t)workspace % 256) return fail(GDN_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  return layer_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens, dims, scale,
+                   use_qk_l2norm_in_kernel, l2_eps, rms_eps, d_out, dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b,
+                   d_A_log, d_dt_bias, d_gate, d_norm_w, workspace, workspace_bytes, stream, true);
+}
 
-  const int64_t Hqk = dims->Hqk, dk = dims->dk, Hv = dims->Hv, dv = dims->dv;
-  const int64_t nq = Hqk * dk, C = 2 * nq + Hv * dv, es = elem_size(act);
-  char *w = static_cast<char *>(workspace);
-  gdn_tensor qkv = {w + L.qkv, act, 3, {B, T, C}, {T * C, C, 1}};
-  gdn_tensor gt = {w + L.g, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
-  gdn_tensor bt = {w + L.beta, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
-  gdn_tensor ot = {w + L.o, act, 4, {B, T, Hv, dv}, {T * Hv * dv, Hv * dv, dv, 1}};
-  gdn_tensor dot = {w + L.d_o, act, 4, {B, T, Hv, dv}, {T * Hv * dv, Hv * dv, dv, 1}};
-  gdn_tensor dqkv = {w + L.dqkv, GDN_F32, 3, {B, T, C}, {T * C, C, 1}};
-  gdn_tensor dgt = {w + L.dg, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
-  gdn_tensor dbt = {w + L.dbeta, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
-  char *qb = w + L.qkv, *db = w + L.dqkv;
-  gdn_tensor qv = {qb, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
-  gdn_tensor kv = {qb + nq * es, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
-  gdn_tensor vv = {qb + 2 * nq * es, act, 4, {B, T, Hv, dv}, {T * C, C, dv, 1}};
-  gdn_tensor dqv = {db, GDN_F32, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
-  gdn_tensor dkv = {db + nq * 4, GDN_F32, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
-  gdn_tensor dvv = {db + 2 * nq * 4, GDN_F32, 4, {B, T, Hv, dv}, {T * C, C, dv, 1}};
-  gdn_tensor wsd = {workspace, GDN_BF16, 1, {(int64_t)(L.total / 2)}, {1}};
-
-  // Plan every stage before launching anything.
-  gdn::PrologueArgs PP;
-  gdn::ChunkArgs PC;
-  gdn::NormBwdArgs PN;
-  gdn::ChunkBwdArgs PB;
-  gdn::PrologueBwdArgs PR;
-  TRY(plan_prologue(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, dims, 0, l2_eps, &qkv, &gt,
-                    &bt, &PP));
-  TRY(plan_chunk(&qv, &kv, &vv, &gt, &bt, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, nullptr, &ot,
-                 nullptr, &PC));
-  TRY(attach_chunk_ws(&PC, L.cfw_n ? w + L.cfw : nullptr, L.cfw_n));
-  TRY(plan_norm_bwd(&ot, gate, norm_w, rms_eps, d_out, &dot, d_gate, d_norm_w, w + L.nbw, L.nbw_n, &PN));
-  TRY(plan_chunk_bwd(&qv, &kv, &vv, &gt, &bt, scale, use_qk_l2norm_in_kernel, l2_eps, cu_seqlens, nullptr, &dot,
-                     nullptr, &dqv, &dkv, &dvv, &dgt, &dbt, nullptr, w + L.cbw, L.cbw_n, &PB, true));
-  TRY(plan_prologue_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens, dims, &dqkv, &dgt, &dbt,
-                        dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b, d_A_log, d_dt_bias, w + L.pbw, L.pbw_n,
-                        &PR));
-  const gdn_tensor *ins[] = {x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens, d_out};
-  const gdn_tensor *outs[] = {dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b, d_A_log, d_dt_bias, d_gate, d_norm_w};
-  for (auto *t : ins)
-    if (overlaps(&wsd, t)) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps an input");
-  for (size_t i = 0; i < sizeof outs / sizeof outs[0]; ++i) {
-    if (overlaps(&wsd, outs[i])) return fail(GDN_ERR_INVALID_VALUE, "workspace overlaps an output");
-    for (auto *t : ins)
-      if (overlaps(outs[i], t)) return fail(GDN_ERR_INVALID_VALUE, "an output overlaps an input");
-    for (size_t j = i + 1; j < sizeof outs / sizeof outs[0]; ++j)
-      if (overlaps(outs[i], outs[j])) return fail(GDN_ERR_INVALID_VALUE, "two outputs overlap");
-  }
-
-  hipStream_t s = (hipStream_t)stream;
-  TRY(launched(gdn::launch_prologue(PP, s), "prologue"));
-  TRY(launched(gdn::launch_chunk_rule(PC, s), "chunk rule"));
-  TRY(launched(gdn::launch_gated_norm_bwd(PN, s), "gated norm backward"));
-  TRY(launched(gdn::launch_chunk_bwd(PB, s), "chunk rule backward"));
-  return launched(gdn::launch_prologue_bwd(PR, s), "prologue backward");
+gdn_status gdn_layer_bwd_saved(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_tensor *x_v,
+                               const gdn_tensor *conv_w, const gdn_tensor *conv_b, const gdn_tensor *a,
+                               const gdn_tensor *b, const gdn_tensor *A_log, const gdn_tensor *dt_bias,
+                               const gdn_tensor *gate, const gdn_tensor *norm_w, const gdn_tensor *cu_seqlens,
+                               const gdn_dims *dims, float scale, int32_t use_qk_l2norm_in_kernel, float l2_eps,
+                               float rms_eps, const gdn_tensor *d_out, const gdn_tensor *dx_q,
+                               const gdn_tensor *dx_k, const gdn_tensor *dx_v, const gdn_tensor *d_conv_w,
+                               const gdn_tensor *d_conv_b, const gdn_tensor *d_a, const gdn_tensor *d_b,
+                               const gdn_tensor *d_A_log, const gdn_tensor *d_dt_bias, const gdn_tensor *d_gate,
+                               const gdn_tensor *d_norm_w, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  return layer_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens, dims, scale,
+                   use_qk_l2norm_in_kernel, l2_eps, rms_eps, d_out, dx_q, dx_k, dx_v, d_conv_w, d_conv_b, d_a, d_b,
+                   d_A_log, d_dt_bias, d_gate, d_norm_w, workspace, workspace_bytes, stream, false);
 }
 
 size_t gdn_layer_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims *dims,

@@ -83,9 +83,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_layer_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_layer_bwd.argtypes = ([P] * 12 + [ctypes.POINTER(GdnDims), f32, i32, f32, f32] + [P] * 12 +
                                     [vp, ctypes.c_size_t, vp])
+        L.gdn_layer_bwd_saved.argtypes = L.gdn_layer_bwd.argtypes
         for name in ("gdn_prologue_fwd", "gdn_chunk_rule_fwd", "gdn_gated_norm_fwd", "gdn_layer_fwd",
                      "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_prologue_bwd", "gdn_chunk_rule_bwd",
-                     "gdn_layer_bwd"):
+                     "gdn_layer_bwd", "gdn_layer_bwd_saved"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -352,6 +353,12 @@ def gdn_layer_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, nor
                   l2_eps: float = 1e-6, rms_eps: float = 1e-5, workspace=None):
     """Gradients of gdn_layer_fwd. Returns (dx_q, dx_k, dx_v, d_conv_w, d_conv_b or None, d_a, d_b,
     d_A_log, d_dt_bias, d_gate, d_norm_w)."""
+    return _layer_bwd(lib().gdn_layer_bwd, x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w,
+                      cu_seqlens, dims, scale, d_out, use_qk_l2norm_in_kernel, l2_eps, rms_eps, workspace)
+
+
+def _layer_bwd(fn, x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens, dims, scale,
+               d_out, use_qk_l2norm_in_kernel, l2_eps, rms_eps, workspace):
     Hqk, dk, Hv, dv = dims
     B, T = x_q.shape[0], x_q.shape[1]
     C = 2 * Hqk * dk + Hv * dv
@@ -370,11 +377,21 @@ def gdn_layer_bwd(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, nor
     gd = dims_of(Hqk, dk, Hv, dv)
     D = [desc(t) for t in (x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens)]
     E = [desc(t) for t in (d_out, dxq, dxk, dxv, dw, dbias, da, db, dal, ddt, dgate, dnw)]
-    _check(lib().gdn_layer_bwd(*[_p(d) for d in D], ctypes.byref(gd), float(scale),
+    _check(fn(*[_p(d) for d in D], ctypes.byref(gd), float(scale),
                                int(bool(use_qk_l2norm_in_kernel)), float(l2_eps), float(rms_eps),
                                *[_p(d) for d in E], ctypes.c_void_p(workspace.data_ptr()),
                                ctypes.c_size_t(workspace.numel()), _stream(x_q)))
     return dxq, dxk, dxv, dw, dbias, da, db, dal, ddt, dgate, dnw
+
+
+def gdn_layer_bwd_saved(x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate, norm_w, cu_seqlens,
+                        dims: Sequence[int], scale: float, d_out, workspace, use_qk_l2norm_in_kernel: bool = True,
+                        l2_eps: float = 1e-6, rms_eps: float = 1e-5):
+    """gdn_layer_bwd from the activations a gdn_layer_fwd call with the same
+    arguments left in `workspace` (gdn_layer_bwd_workspace_bytes bytes, given
+    to that forward call). Returns what gdn_layer_bwd returns."""
+    return _layer_bwd(lib().gdn_layer_bwd_saved, x_q, x_k, x_v, conv_w, conv_b, a, b, A_log, dt_bias, gate,
+                      norm_w, cu_seqlens, dims, scale, d_out, use_qk_l2norm_in_kernel, l2_eps, rms_eps, workspace)
 
 
 def dtype_name(t: torch.dtype) -> str:

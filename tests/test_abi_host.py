@@ -24,7 +24,8 @@ def test_exports_every_declared_symbol():
                      "gdn_chunk_rule_workspace_bytes", "gdn_gated_norm_fwd", "gdn_layer_workspace_bytes",
                      "gdn_layer_fwd", "gdn_decode_fwd", "gdn_gated_norm_bwd", "gdn_gated_norm_bwd_workspace_bytes",
                      "gdn_prologue_bwd", "gdn_prologue_bwd_workspace_bytes", "gdn_chunk_rule_bwd",
-                     "gdn_chunk_rule_bwd_workspace_bytes", "gdn_layer_bwd", "gdn_layer_bwd_workspace_bytes",
+                     "gdn_chunk_rule_bwd_workspace_bytes", "gdn_layer_bwd", "gdn_layer_bwd_saved",
+                     "gdn_layer_bwd_workspace_bytes",
                      "gdn_chunk_rule_fwd_noalloc"}
     L = gdn.lib()
     for n in names:
@@ -319,6 +320,13 @@ def test_layer_bwd_workspace_bytes_and_rejections():
     off = (-raw.data_ptr()) % 256
     _expect(INVALID, "dout: dtype", gdn.gdn_layer_bwd, *args, gate, nw, x["cu_seqlens"], x["dims"], 0.125,
             d_out.half(), workspace=raw[off:off + nb])
+    # the variant that reuses the forward's activations validates the same
+    # way, and the forward's workspace layout is a prefix of the backward's
+    _expect(INVALID, "workspace too small", gdn.gdn_layer_bwd_saved, *args, gate, nw, x["cu_seqlens"], x["dims"],
+            0.125, d_out, torch.zeros(16, dtype=torch.uint8))
+    _expect(INVALID, "dout: dtype", gdn.gdn_layer_bwd_saved, *args, gate, nw, x["cu_seqlens"], x["dims"], 0.125,
+            d_out.half(), raw[off:off + nb])
+    assert gdn.gdn_layer_workspace_bytes(B, T, x["dims"], torch.bfloat16) <= nb
 
 
 def test_bench_refuses_more_than_one_gpu():

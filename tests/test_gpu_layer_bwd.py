@@ -68,3 +68,35 @@ def test_layer_bwd_parity(name, cfg, over, bias):
     for n, a_, b_ in zip(names, got, again):
         if a_ is not None:
             assert torch.equal(a_, b_), f"{n} differs between calls"
+
+
+@pytest.mark.parametrize("name,cfg,over,bias", CASES, ids=[c[0] for c in CASES])
+def test_layer_bwd_saved_equals_recomputed(name, cfg, over, bias):
+    """gdn_layer_bwd_saved after a gdn_layer_fwd into the same workspace gives
+    gdn_layer_bwd's outputs bit for bit (the forward's qkv, g, beta and o are
+    what the recompute would write; the kernels are deterministic)."""
+    s = synth.spec(cfg).replace(**over)
+    x = H.to_dev(synth.make_inputs(s))
+    if bias:
+        x["conv_b"] = (0.1 * synth.randn((s.C,), "f32", 56)).cuda()
+    dims = (s.Hqk, s.dk, s.Hv, s.dv)
+    scale = s.dk ** -0.5
+    d_out = synth.randn((s.B, s.T, s.Hv, s.dv), s.act, 610 + cfg).cuda()
+    ins = (x["x_q"], x["x_k"], x["x_v"], x["conv_w"], x["conv_b"], x["a"], x["b"], x["A_log"], x["dt_bias"],
+           x["gate"], x["norm_w"], x["cu_seqlens"], dims, scale)
+    n_seqs = 0 if x["cu_seqlens"] is None else x["cu_seqlens"].shape[0] - 1
+    nb = gdn.gdn_layer_bwd_workspace_bytes(s.B, s.T, dims, x["x_q"].dtype, n_seqs)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = gdn.gdn_layer_fwd(*ins, workspace=ws)
+    saved = gdn.gdn_layer_bwd_saved(*ins, d_out, ws)
+    ref_out = gdn.gdn_layer_fwd(*ins)
+    ref = gdn.gdn_layer_bwd(*ins, d_out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    names = ("dx_q", "dx_k", "dx_v", "d_conv_w", "d_conv_b", "d_a", "d_b", "d_A_log", "d_dt_bias", "d_gate",
+             "d_norm_w")
+    for n, a_, b_ in zip(names, saved, ref):
+        if b_ is None:
+            assert a_ is None, n
+        else:
+            assert torch.equal(a_, b_), f"{n} differs from the recomputing backward"
