@@ -466,8 +466,8 @@ size_t gdn_chunk_rule_bwd_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs,
  * parameter of gdn_layer_fwd. On `stream`, in a caller workspace: the
  * prologue and the chunk rule are recomputed (qkv, g, beta and o as
  * gdn_layer_fwd materialises them), then gdn_gated_norm_bwd (d_o in the act
- * dtype), gdn_chunk_rule_bwd (dq, dk, dv into one FP32 [B, T, C] buffer,
- * dg, dbeta) and gdn_prologue_bwd run. Each stage's gradient is evaluated at
+ * dtype), gdn_chunk_rule_bwd (dq, dk, dv into one [B, T, C] buffer of the
+ * act dtype, dg, dbeta) and gdn_prologue_bwd run. Each stage's gradient is evaluated at
  * the stored values of its inputs, the roundings taken as the identity.
  *
  *   inputs          as in gdn_layer_fwd (initial state: none)
@@ -535,7 +535,7 @@ gdn_status gdn_layer_bwd_saved(const gdn_tensor *x_q, const gdn_tensor *x_k,
 
 /* Bytes of workspace gdn_layer_bwd needs (n_seqs as in
  * gdn_layer_workspace_bytes): the forward stage outputs and the chunk
- * forward's workspace, d_o, d_qkv (FP32), dg and dbeta, and the three
+ * forward's workspace, d_o, d_qkv (act dtype), dg and dbeta, and the three
  * backward stages' workspaces, each 256-byte aligned. 0 for invalid or
  * unsupported geometry. */
 size_t gdn_layer_bwd_workspace_bytes(int64_t B, int64_t T, int64_t n_seqs,

@@ -956,7 +956,7 @@ gdn_status plan_chunk_bwd(const gdn_tensor *q, const gdn_tensor *k, const gdn_te
 
 // Workspace of the layer backward (byte offsets, each 256-aligned): the
 // recomputed forward stage outputs, the chunk forward's workspace, d_o and the
-// gated-norm backward's partials, d_qkv (FP32) with dg and dbeta, then the
+// gated-norm backward's partials, d_qkv (activation dtype) with dg and dbeta, then the
 // chunk-rule and prologue backward workspaces.
 struct LayerBwdWs {
   size_t qkv, g, beta, o, cfw, d_o, nbw, dqkv, dg, dbeta, cbw, pbw, total;
@@ -984,7 +984,7 @@ LayerBwdWs layer_bwd_layout(int64_t B, int64_t T, int64_t n_seqs, const gdn_dims
   w.cfw = take(w.cfw_n);
   w.d_o = take(n * HD * es);
   w.nbw = take(w.nbw_n);
-  w.dqkv = take(n * C * 4);
+  w.dqkv = take(n * C * es);
   w.dg = take(n * Hv * 4);
   w.dbeta = take(n * Hv * 4);
   w.cbw = take(w.cbw_n);
@@ -1037,16 +1037,16 @@ gdn_status layer_bwd(const gdn_tensor *x_q, const gdn_tensor *x_k, const gdn_ten
   gdn_tensor bt = {w + L.beta, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
   gdn_tensor ot = {w + L.o, act, 4, {B, T, Hv, dv}, {T * Hv * dv, Hv * dv, dv, 1}};
   gdn_tensor dot = {w + L.d_o, act, 4, {B, T, Hv, dv}, {T * Hv * dv, Hv * dv, dv, 1}};
-  gdn_tensor dqkv = {w + L.dqkv, GDN_F32, 3, {B, T, C}, {T * C, C, 1}};
+  gdn_tensor dqkv = {w + L.dqkv, act, 3, {B, T, C}, {T * C, C, 1}};
   gdn_tensor dgt = {w + L.dg, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
   gdn_tensor dbt = {w + L.dbeta, GDN_F32, 3, {B, T, Hv}, {T * Hv, Hv, 1}};
   char *qb = w + L.qkv, *db = w + L.dqkv;
   gdn_tensor qv = {qb, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
   gdn_tensor kv = {qb + nq * es, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
   gdn_tensor vv = {qb + 2 * nq * es, act, 4, {B, T, Hv, dv}, {T * C, C, dv, 1}};
-  gdn_tensor dqv = {db, GDN_F32, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
-  gdn_tensor dkv = {db + nq * 4, GDN_F32, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
-  gdn_tensor dvv = {db + 2 * nq * 4, GDN_F32, 4, {B, T, Hv, dv}, {T * C, C, dv, 1}};
+  gdn_tensor dqv = {db, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor dkv = {db + nq * es, act, 4, {B, T, Hqk, dk}, {T * C, C, dk, 1}};
+  gdn_tensor dvv = {db + 2 * nq * es, act, 4, {B, T, Hv, dv}, {T * C, C, dv, 1}};
   gdn_tensor wsd = {workspace, GDN_BF16, 1, {(int64_t)(L.total / 2)}, {1}};
 
   // Plan every stage before launching anything.

@@ -302,7 +302,7 @@ def test_chunk_rule_bwd_workspace_bytes_and_rejections():
 
 def test_layer_bwd_workspace_bytes_and_rejections():
     # the layer backward holds the forward's stage outputs, the chunk forward's
-    # workspace, d_o, d_qkv (FP32), dg, dbeta and the three backward workspaces
+    # workspace, d_o, d_qkv (act dtype), dg, dbeta and the three backward workspaces
     dims = (2, 64, 4, 64)
     n = gdn.gdn_layer_bwd_workspace_bytes(1, 100, dims, torch.bfloat16)
     assert n > gdn.gdn_chunk_rule_bwd_workspace_bytes(1, 100, dims) + 100 * (2 * 128 + 256) * 4
