@@ -33,7 +33,10 @@ def test_bench_emits_one_json_line_with_roofline_and_cpu_baseline():
     cpu = out["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
     assert out["decode"]["seqs"] == 8 and out["decode"]["GB/s"] > 0
-    assert set(out["backward"]) == {"gated_norm_bwd", "prologue_bwd", "chunk_rule_bwd", "layer_core_bwd_ms"}
+    assert set(out["backward"]) == {"gated_norm_bwd", "prologue_bwd", "chunk_rule_bwd", "layer_core_bwd_ms",
+                                    "layer_core_bwd_saved_ms", "layer_core_fwd_bwd_saved_ms"}
+    for key in ("layer_core_bwd_ms", "layer_core_bwd_saved_ms", "layer_core_fwd_bwd_saved_ms"):
+        assert out["backward"][key] > 0, key
     q = out["ms_per_step_q"]
     assert 0 < q["p20"] <= q["median"] <= q["p80"]
     (other,) = out["other_workloads"]
