@@ -139,3 +139,44 @@ def test_layer_bwd_graph_replays_equal_eager(cfg, over):
             assert torch.equal(a, b), f"replay {i}: gradient {j} differs from the eager call"
         run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_layer_fwd_then_saved_bwd_graph_replays_equal_eager():
+    """A training step of the layer core that keeps its activations:
+    gdn_layer_fwd into the backward's workspace, then gdn_layer_bwd_saved on
+    it, captured once and replayed; the output and every gradient of every
+    replay equal the eager calls."""
+    s = synth.spec(2).replace(T=150, Hqk=1, Hv=2)
+    x = H.to_dev(synth.make_inputs(s))
+    dims = (s.Hqk, s.dk, s.Hv, s.dv)
+    dt = synth.TORCH_DTYPE[s.act]
+    ws = torch.empty(gdn.gdn_layer_bwd_workspace_bytes(s.B, s.T, dims, dt, 0), dtype=torch.uint8, device="cuda")
+    d_out = synth.randn((s.B, s.T, s.Hv, s.dv), s.act, 720).cuda()
+    ins = (x["x_q"], x["x_k"], x["x_v"], x["conv_w"], None, x["a"], x["b"], x["A_log"], x["dt_bias"], x["gate"],
+           x["norm_w"], None, dims, s.dk ** -0.5)
+
+    def run():
+        out = gdn.gdn_layer_fwd(*ins, workspace=ws)
+        return [out] + [t for t in gdn.gdn_layer_bwd_saved(*ins, d_out, ws) if t is not None]
+
+    eager = [t.clone() for t in run()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = run()
+    for i in range(3):
+        for t in outs:
+            t.zero_()
+        ws.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), f"replay {i}: tensor {j} differs from the eager calls"
+        run()  # eager work between replays
+        torch.cuda.synchronize()
